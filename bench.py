@@ -1,0 +1,247 @@
+"""Decode-attention benchmark: one step = score_pages + select_pages + sparse_decode_attn for the
+whole batch (every head, one query token per sequence, one layer), inputs resident in HBM.
+
+Prints ONE JSON line (rank 0): steps/s, ms/step, achieved HBM GB/s on the step's algorithmic
+bytes, a roofline record for the dominant kernel (timed live with HIP events on the stream it
+runs on) and the float64 oracle timed on a bounded sample on the host cores.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload token128k] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sparse_kv_cache_build_amd as skv  # noqa: E402
+import workloads as W  # noqa: E402
+
+METRIC = "decode attn steps/sec and achieved HBM GB/s (% of peak) at 128K ctx, 1 GPU"
+PEAK_GBPS = 8000.0          # MI355X HBM3E
+MALL_BYTES = 256 << 20      # Infinity Cache: rotate buffer sets so a round touches > 2x this
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Step:
+    """Preallocated buffers of one decode step on one buffer set."""
+
+    def __init__(self, w: W.Workload, alpha: float, split: int = 0):
+        cfg = w.cfg
+        self.w, self.alpha = w, alpha
+        self.kind = cfg["score"]
+        self.cache = skv.PagedCache(w.k, w.v, w.block_table, w.seq_lens, w.Hq)
+        t0 = time.time()
+        self.meta = skv.build_page_meta(self.cache, (self.kind,), proj=w.proj)
+        torch.cuda.synchronize()
+        self.meta_s = time.time() - t0
+        self.scores = skv.ScoreBuffers(self.cache, self.kind)
+        p = skv.select_params(cfg["policy"], k=cfg.get("k", 0), budget_pct=cfg.get("pct", 0),
+                              alpha=cfg.get("sel_alpha", 1.5), delta=cfg.get("delta", 0.0),
+                              tokens=1 if self.kind == "proj" else 0)
+        self.sel = skv.Selection(self.cache, p)
+        self.attn = skv.AttnBuffers(self.cache, skv.attn_params(self.cache, alpha, None, self.sel.granularity, split),
+                                    self.sel.cap)
+
+    def score(self):
+        skv.score_pages(self.cache, self.meta, self.w.q, self.kind, out=self.scores)
+
+    def rest(self):
+        skv.select_pages(self.cache, self.scores, None, out=self.sel)
+        skv.sparse_decode_attn(self.cache, self.w.q, self.sel, out=self.attn)
+
+    def run(self):
+        self.score()
+        self.rest()
+
+
+def step_bytes(st: Step):
+    """Algorithmic bytes of one step: metadata read + K of the selected rows + V of the rows that
+    carry weight + q + out. Returns (total, score_kernel_bytes, details)."""
+    w = st.w
+    e = 2 if w.dtype == torch.bfloat16 else 4
+    d, S, G = w.d, w.S, w.G
+    lens = np.array(w.lens)
+    P = (lens + S - 1) // S
+    cnt = st.sel.count.cpu().numpy().astype(np.int64)
+    if st.kind == "box":
+        meta = int(P.sum()) * w.Hkv * 2 * d * e
+        keys_out = w.B * w.Hkv * w.maxP * 4
+    elif st.kind == "gauss":
+        meta = int(P.sum()) * w.Hkv * 2 * d * 4
+        keys_out = 3 * w.B * w.Hq * w.maxP * 4
+    else:
+        r = w.proj.shape[0]
+        meta = int(lens.sum()) * w.Hkv * r * 2
+        keys_out = w.B * w.Hkv * w.maxP * S * 4
+    if st.sel.granularity:
+        k_rows = int(cnt.sum())
+    else:
+        idx = st.sel.idx.cpu().numpy()
+        k_rows = 0
+        for b in range(w.B):
+            for g in range(w.Hkv):
+                pg = idx[b, g, :cnt[b, g]].astype(np.int64)
+                k_rows += int(np.minimum(S, lens[b] - pg * S).sum())
+    kv_row = d * e
+    v_rows = k_rows   # softmax weights every selected row; entmax reads fewer (reported as an upper bound)
+    q_out = w.B * w.Hq * d * (e + 4)
+    total = meta + k_rows * kv_row + v_rows * kv_row + q_out
+    return total, meta + keys_out, dict(meta=meta, k_rows=k_rows, v_rows=v_rows, q_out=q_out, keys_out=keys_out)
+
+
+def cpu_baseline(name: str, over: dict, alpha: float, budget_s: float = 20.0):
+    """The float64 oracle (unchanged) on a bounded sample: units (sequence, KV head) drawn on the
+    CPU with the workload's shapes, run in parallel threads, one unit per task. Metadata is built
+    first (prefill work, not timed); score + select + attention of the sampled units is timed and
+    scaled to whole steps."""
+    import oracle
+    from oracle import pipeline
+
+    cores = len(os.sched_getaffinity(0))
+    threads = max(1, min(cores, 16))
+    w = W.make(name, device="cpu", **dict(over, B=1))
+    spec = pipeline.Spec(score=w.cfg["score"], policy=w.cfg["policy"], k=w.cfg.get("k", 0), pct=w.cfg.get("pct", 0),
+                         sel_alpha=w.cfg.get("sel_alpha", 1.5), delta=w.cfg.get("delta", 0.0), alphas=(alpha,),
+                         proj=w.proj.numpy() if w.proj is not None else None)
+    h = W.host_arrays(w)
+    n_units = min(w.Hkv, threads)
+    caches = []
+    for g in range(n_units):   # one KV head per sub-cache (exact bytes of that head)
+        G = w.G
+        caches.append(oracle.Cache(q=np.ascontiguousarray(h["q"][:, g * G:(g + 1) * G]),
+                                   k=np.ascontiguousarray(h["k"][:, g:g + 1]),
+                                   v=np.ascontiguousarray(h["v"][:, g:g + 1]),
+                                   block_table=h["block_table"], seq_lens=h["seq_lens"]))
+    with cf.ThreadPoolExecutor(threads) as ex:
+        mds = list(ex.map(lambda c: pipeline.build_metadata(c, spec), caches))
+
+    def one(i):
+        c, md = caches[i], mds[i]
+        sc = pipeline.compute_scores(c, spec, md)
+        r = pipeline.run_unit(c, spec, sc, 0, 0)
+        return len(r.sel)
+
+    reps, t = 0, 0.0
+    with cf.ThreadPoolExecutor(threads) as ex:
+        while t < 2.0 and reps < 50:
+            t0 = time.perf_counter()
+            list(ex.map(one, range(n_units)))
+            t += time.perf_counter() - t0
+            reps += 1
+    per_round = t / reps
+    units_total = W.CONFIGS[name]["B"] * W.CONFIGS[name]["Hkv"] if "B" not in over else over["B"] * w.Hkv
+    steps_per_s = (n_units / units_total) / per_round
+    return dict(value=steps_per_s, unit="steps/s", cores=threads, kind="oracle",
+                sample=f"{n_units} units (1 sequence x {n_units} KV heads, {w.G} query heads each) of {name} at full "
+                       f"context ({w.lens[0]} tokens), metadata prebuilt; score+select+attention timed over {reps} "
+                       f"round(s), {per_round:.3f} s per round, scaled by {units_total} units per step")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="token128k", choices=list(W.CONFIGS))
+    ap.add_argument("--alpha", type=float, default=None)
+    ap.add_argument("--split", type=int, default=0)
+    ap.add_argument("--sets", type=int, default=0, help="buffer sets rotated per step (0: enough to exceed 2x MALL)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the decode path has no multi-GPU mode "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    name = args.workload
+    cfg = W.CONFIGS[name]
+    alpha = args.alpha if args.alpha is not None else cfg["alphas"][0]
+
+    log(f"[bench] drawing {name} on {dev}")
+    sets = [Step(W.make(name, device=dev), alpha, args.split)]
+    sets[0].run()
+    torch.cuda.synchronize()
+    total, score_bytes, det = step_bytes(sets[0])
+    n_sets = args.sets or max(1, math.ceil(2 * MALL_BYTES / max(total, 1)))
+    for i in range(1, n_sets):
+        log(f"[bench] buffer set {i + 1}/{n_sets}")
+        sets.append(Step(W.make(name, device=dev, seed=cfg["seed"] + 100 * i), alpha, args.split))
+    meta_s = sets[0].meta_s
+
+    log(f"[bench] warmup {args.warmup}")
+    for i in range(args.warmup):
+        sets[i % n_sets].run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        s = sets[i % n_sets]
+        ev[i][0].record(stream)
+        s.score()
+        ev[i][1].record(stream)
+        s.rest()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    score_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    sps = 1000.0 / ms
+    gbps = total / (ms * 1e-3) / 1e9
+    score_gbps = score_bytes / (score_ms * 1e-3) / 1e9
+    log(f"[bench] {ms * 1e3:.1f} us/step, score stage {score_ms * 1e3:.1f} us")
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        cpu = cpu_baseline(name, {}, alpha)
+
+    sel_desc = {"topk": f"top-{cfg.get('k')} pages by box bound", "budget": f"{cfg.get('pct')}% page budget by box bound",
+                "thresh": f"Gaussian entmax threshold (alpha {cfg.get('sel_alpha')}, Delta {cfg.get('delta')})",
+                "token_topk": f"top-{cfg.get('k')} tokens per KV head, rank-{cfg.get('proj_rank')} projection"}
+    w0 = sets[0].w
+    line = {
+        "metric": METRIC,
+        "value": round(sps, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": name, "batch": w0.B, "ctx": int(max(w0.lens)), "mean_ctx": float(np.mean(w0.lens)),
+                   "q_heads": w0.Hq, "kv_heads": w0.Hkv, "head_dim": w0.d, "page": w0.S, "kv_dtype": "bf16"
+                   if w0.dtype == torch.bfloat16 else "f32", "select": sel_desc[cfg["policy"]],
+                   "attn": "softmax" if alpha == 1.0 else f"{alpha}-entmax", "bytes_per_step": int(total),
+                   "achieved_GBps": round(gbps, 1), "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
+                   "buffer_sets": n_sets, "meta_build_s": round(meta_s, 4), "bytes_detail": det},
+        "roofline": {"bound": "hbm", "kernel": f"score_pages[{sets[0].kind}]", "achieved": round(score_gbps, 1),
+                     "peak": PEAK_GBPS, "unit": "GB/s", "frac": round(score_gbps / PEAK_GBPS, 4), "traffic": None,
+                     "avg_us": round(score_ms * 1e3, 2), "bytes_per_launch": int(score_bytes)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

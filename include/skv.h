@@ -1,0 +1,212 @@
+/*
+ * skv.h -- C ABI of libskv.so: query-aware sparse decode attention over a paged
+ * grouped-query (GQA) KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The calls follow the pipeline the pages describe for one decode step:
+ *   skv_build_page_meta    per-page metadata, once per page at prefill/append time
+ *                          ("EntmaxKV" summary, s2.A: box bounds k_min/k_max and Gaussian
+ *                          moments stored per page; "Joint Subspace Sparse Attention" abstract:
+ *                          keys cached in a shared low-dimensional subspace)
+ *   skv_score_pages        query-aware page (or token) scores from the metadata ("EntmaxKV" s2.A)
+ *   skv_select_pages       candidate selection: top-k pages, a page budget, the Gaussian-aware
+ *                          entmax threshold tau_hat with margin Delta ("EntmaxKV" s2.B), or
+ *                          top-k tokens per KV head ("Joint Subspace Sparse Attention" abstract;
+ *                          "SOCKET" summary, Methodology step 4)
+ *   skv_sparse_decode_attn softmax or alpha-entmax attention over the selected KV only
+ *                          ("EntmaxKV" s2.C; softmax is the comparator of s1 and s3)
+ *
+ * Conventions shared by every call
+ *   - Memory: every pointer in a struct or argument is a device pointer unless stated
+ *     otherwise; the caller owns all memory, including workspaces (size them with
+ *     skv_workspace_bytes). The library never allocates, frees or keeps caller memory.
+ *   - Streams: `stream` is a hipStream_t (NULL = the null stream). Every call only enqueues
+ *     work on it and returns; nothing is synchronised. Results are valid once the stream
+ *     reaches the enqueued work.
+ *   - Errors: arguments are validated on the host before anything is enqueued; on any error
+ *     nothing is enqueued and a non-zero skv_status is returned. A launch failure reported by
+ *     the HIP runtime returns SKV_ERR_HIP. Device-side data (seq_lens, block_table, counts)
+ *     cannot be validated on the host: seq_lens are clamped to [0, max_pages * page_size],
+ *     block_table entries of pages below the clamped length must lie in [0, num_phys_pages),
+ *     sel_count entries are clamped to [0, cap].
+ *   - Threading: calls are reentrant; concurrent calls must not share output or workspace
+ *     buffers.
+ *   - Determinism: for a fixed input, launch configuration and device, outputs are bitwise
+ *     reproducible (no floating-point atomics).
+ *
+ * Cache layout ("Joint Subspace Sparse Attention" abstract: the standard GQA paged layout)
+ *   k, v        [num_phys_pages, num_kv_heads, page_size, head_dim], dtype `dtype`
+ *   block_table [batch, max_pages] int32: logical page p of sequence b -> physical page
+ *   seq_lens    [batch] int32
+ *   q           [batch, num_q_heads, head_dim], dtype `dtype`
+ *   Query head h reads KV head h / G, G = num_q_heads / num_kv_heads. Page p of sequence b holds
+ *   tokens [p*S, min(p*S + S, L_b)). A physical page is referenced by at most one
+ *   (sequence, logical page).
+ * Supported: head_dim 64 or 128; page_size 1..1024; G in {1, 2, 4, 8}; dtype f32 or bf16.
+ */
+#ifndef SKV_H
+#define SKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum skv_status {
+  SKV_OK = 0,
+  SKV_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent dimensions */
+  SKV_ERR_UNSUPPORTED = 2, /* valid but outside the supported set above */
+  SKV_ERR_CAPACITY = 3,    /* an output capacity (cap) is too small for the policy */
+  SKV_ERR_WORKSPACE = 4,   /* workspace missing or smaller than skv_workspace_bytes */
+  SKV_ERR_HIP = 5          /* the HIP runtime reported an error */
+} skv_status;
+
+enum { SKV_DTYPE_F32 = 0, SKV_DTYPE_BF16 = 1 };
+
+typedef struct skv_cache {
+  int32_t batch;          /* B */
+  int32_t num_q_heads;    /* Hq */
+  int32_t num_kv_heads;   /* Hkv; Hq must be a multiple */
+  int32_t head_dim;       /* d */
+  int32_t page_size;      /* S (tokens per page) */
+  int32_t max_pages;      /* columns of block_table */
+  int32_t num_phys_pages; /* rows of k and v */
+  int32_t dtype;          /* SKV_DTYPE_* of k, v, q and the box metadata */
+  const void *k;
+  const void *v;
+  const int32_t *block_table;
+  const int32_t *seq_lens;
+} skv_cache;
+
+/* ------------------------------------------------------------------ page metadata */
+
+enum { SKV_META_BOX = 1, SKV_META_GAUSS = 2, SKV_META_PROJ = 4 };
+
+typedef struct skv_meta {
+  uint32_t kinds;     /* OR of SKV_META_* to build (build_page_meta) / available (score) */
+  void *box;          /* BOX:   [Nphys, Hkv, 2, d] cache dtype: row 0 k_min, row 1 k_max */
+  float *gauss;       /* GAUSS: [Nphys, Hkv, 2, d] float32: row 0 mean, row 1 variance */
+  int32_t proj_rank;  /* PROJ:  r, 1..64 */
+  const float *proj;  /* PROJ:  [r, d] float32 projection shared by queries and keys */
+  uint16_t *kproj;    /* PROJ:  [Nphys, Hkv, S, r] bf16 bit patterns */
+} skv_meta;
+
+/* Builds the requested metadata of every page in use (p < ceil(L_b / S)) from the valid tokens
+ * of the page ("EntmaxKV" s2.A; "Joint Subspace Sparse Attention" abstract).
+ *   BOX:   coordinate-wise min and max of the keys (exact, stored in the cache dtype).
+ *   GAUSS: per-coordinate mean and population variance, computed in float64 (mean first, then
+ *          mean squared deviation) and rounded once to float32.
+ *   PROJ:  k~_t[i] = RN_bf16(sum_j proj[i][j] k_t[j]), the sum in float64 over j ascending.
+ * Rows of metadata of unused physical pages, and kproj rows of tokens past L_b, are not
+ * written. Errors: SKV_ERR_INVALID_ARG for null or inconsistent arguments or a missing output
+ * of a requested kind; SKV_ERR_UNSUPPORTED outside the supported set. */
+skv_status skv_build_page_meta(const skv_cache *c, const skv_meta *m, void *stream);
+
+/* ------------------------------------------------------------------ scores */
+
+enum { SKV_SCORE_BOX = 0, SKV_SCORE_GAUSS = 1, SKV_SCORE_PROJ = 2 };
+
+typedef struct skv_scores {
+  float *key;   /* BOX: [B, Hkv, max_pages]; PROJ: [B, Hkv, max_pages * S] */
+  float *m;     /* GAUSS: [B, Hq, max_pages] Gaussian mean of the scaled scores of the page */
+  float *s;     /* GAUSS: [B, Hq, max_pages] its standard deviation */
+  float *shat;  /* GAUSS: [B, Hq, max_pages] estimated maximum m + s sqrt(2 ln n_p) */
+} skv_scores;
+
+/* Query-aware scores ("EntmaxKV" s2.A; "Joint Subspace Sparse Attention" abstract).
+ *   BOX:   key[b][g][p] = RN_f32(max over the G query heads h of g of
+ *          U_h(p) = sum_j max(q_hj k_min_j, q_hj k_max_j)), the upper bound of q_h . k over the
+ *          page's box; float64 sum over j ascending (products are exact), unscaled.
+ *   GAUSS: per query head, m = sm_scale sum_j q_j mean_j, s = sm_scale sqrt(sum_j q_j^2 var_j),
+ *          shat = m + s sqrt(2 ln n_p) (n_p valid tokens of the page; shat = m for n_p = 1).
+ *   PROJ:  q~_h = RN_f32(proj q_h) (float64 sum), u_h(t) = sum_i q~_h[i] k~_t[i] (float64 sum,
+ *          i ascending), key[b][g][t] = RN_f32(max over the G heads of g of u_h(t)).
+ * Entries past the sequence (p >= ceil(L_b / S), or t >= L_b) are -inf (BOX, PROJ) or NaN
+ * (GAUSS). `q` is [B, Hq, d] in the cache dtype. `workspace` must hold
+ * skv_workspace_bytes(c, SKV_OP_SCORE, &kind, 0) bytes (256-byte aligned).
+ * Errors: SKV_ERR_INVALID_ARG (null pointers, kind not in m->kinds, bad sm_scale),
+ * SKV_ERR_WORKSPACE, SKV_ERR_UNSUPPORTED, SKV_ERR_HIP. */
+skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q, int32_t kind, float sm_scale,
+                           const skv_scores *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------ selection */
+
+enum {
+  SKV_SEL_TOPK = 0,         /* the k pages with the largest BOX key */
+  SKV_SEL_BUDGET = 1,       /* the ceil(budget_pct * P_b / 100) pages (at least 1) with the largest BOX key */
+  SKV_SEL_THRESH_GAUSS = 2, /* Gaussian-aware entmax threshold (GAUSS scores) */
+  SKV_SEL_TOKEN_TOPK = 3,   /* the k tokens with the largest PROJ key */
+  SKV_SEL_ALL = 4           /* every page (tokens == 0) or every token (tokens == 1): full cache */
+};
+
+typedef struct skv_select_params {
+  int32_t policy;     /* SKV_SEL_* */
+  int32_t k;          /* TOPK, TOKEN_TOPK: k >= 1 */
+  int32_t budget_pct; /* BUDGET: 1..100 */
+  float alpha;        /* THRESH_GAUSS: 1.5 or 2 */
+  float delta;        /* THRESH_GAUSS: safety margin Delta >= 0, in units of tau */
+  int32_t tokens;     /* ALL: 0 pages, 1 tokens */
+} skv_select_params;
+
+/* Candidate selection, one selection per (sequence, KV head) shared by its G query heads
+ * ("Joint Subspace Sparse Attention" abstract: distinct selection per KV head).
+ *   TOPK / BUDGET / TOKEN_TOPK: order candidates by (key descending, index ascending) and keep
+ *     the first min(k, n); ties go to the lower index ("EntmaxKV" s2.B policy 1).
+ *   THRESH_GAUSS ("EntmaxKV" s2.B policy 2): per query head, tau_hat solves
+ *     sum_p n_p E[((alpha-1) Z_p - tau)_+^(1/(alpha-1))] = 1 with Z_p ~ N(m_p, s_p^2); a page is
+ *     kept iff some head h of the group has (alpha-1) shat_h(p) > tau_hat_h - delta.
+ *     tau_hat [B, Hq] float32 receives the thresholds (unused pointer otherwise).
+ * Output: sel_idx [B, Hkv, cap] int32 holds the kept logical page (or token) indices in
+ * ascending order, sel_count [B, Hkv] int32 their number; entries past the count are not
+ * written. cap must be >= k (TOPK, TOKEN_TOPK), >= max_pages (BUDGET, THRESH_GAUSS, ALL pages)
+ * or >= max_pages * S (ALL tokens), else SKV_ERR_CAPACITY. workspace: skv_workspace_bytes(c,
+ * SKV_OP_SELECT, p, cap). The scores are those written by skv_score_pages for the same cache. */
+skv_status skv_select_pages(const skv_cache *c, const skv_scores *sc, const skv_select_params *p,
+                            int32_t *sel_idx, int32_t *sel_count, int32_t cap, float *tau_hat, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------ attention */
+
+typedef struct skv_attn_params {
+  float alpha;         /* 1 = softmax; 1 < alpha <= 2 = alpha-entmax (2 = sparsemax) */
+  float sm_scale;      /* logit scale c: z_t = c q_h . k_t (c > 0, finite) */
+  int32_t granularity; /* 0: sel_idx holds logical pages; 1: sel_idx holds token positions */
+  int32_t split;       /* selected items (pages or tokens) per split-K partition; 0 = automatic */
+} skv_attn_params;
+
+/* Attention of every query head over the KV rows its KV head selected ("EntmaxKV" s2.C; the
+ * token-granular form reads the rows in place through block_table with no gathered copy,
+ * "Joint Subspace Sparse Attention" abstract).
+ *   z_t = sm_scale q_h . k_t (float32 accumulation), p = softmax(z) (alpha = 1) or
+ *   p = [(alpha-1) z - tau]_+^(1/(alpha-1)) with sum p = 1 (entmax), out_h = sum_t p_t v_t.
+ * Softmax runs as a split-K flash-decode (online max/sum per partition, fixed-order
+ * log-sum-exp combine). Entmax runs in two passes: logits of each partition are filtered to
+ * those within reach of the threshold ((alpha-1) z > (alpha-1) max z - 1), tau is solved per
+ * head over the survivors (bisection, then the closed form on the support for alpha 1.5 and
+ * 2), and V is read only for rows with p > 0.
+ * sel_idx / sel_count / cap are as written by skv_select_pages (indices ascending, within the
+ * sequence; others are skipped). out [B, Hq, d] float32; an empty selection gives zeros.
+ * workspace: skv_workspace_bytes(c, SKV_OP_ATTN, p, cap). Errors: SKV_ERR_INVALID_ARG,
+ * SKV_ERR_UNSUPPORTED, SKV_ERR_WORKSPACE, SKV_ERR_HIP. */
+skv_status skv_sparse_decode_attn(const skv_cache *c, const void *q, const int32_t *sel_idx,
+                                  const int32_t *sel_count, int32_t cap, const skv_attn_params *p, float *out,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------ utilities */
+
+enum { SKV_OP_SCORE = 0, SKV_OP_SELECT = 1, SKV_OP_ATTN = 2 };
+
+/* Workspace bytes the call `op` needs for this cache: params points to an int32_t score kind
+ * (SCORE), a skv_select_params (SELECT) or a skv_attn_params (ATTN); cap as passed to that call.
+ * Host-only; enqueues nothing. Writes *bytes; SKV_ERR_INVALID_ARG on bad arguments. */
+skv_status skv_workspace_bytes(const skv_cache *c, int32_t op, const void *params, int32_t cap, size_t *bytes);
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char *skv_status_str(skv_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKV_H */

@@ -1,0 +1,13 @@
+"""Query-aware sparse decode attention over a paged GQA KV cache, for AMD MI355X (gfx950).
+
+The compute path is libskv.so (hand-written HIP kernels behind the C ABI of include/skv.h);
+this package is its thin ctypes binding. The library loads on first use and the calls raise if
+it is missing: there is no CPU fallback.
+"""
+from ._binding import (AttnBuffers, AttnParams, PagedCache, PageMeta, ScoreBuffers, Selection, SelectParams,
+                       SkvError, attn_params, build_page_meta, lib, score_pages, select_cap, select_pages,
+                       select_params, sparse_decode_attn, status_str, workspace_bytes)
+
+__all__ = ["AttnBuffers", "AttnParams", "PagedCache", "PageMeta", "ScoreBuffers", "Selection", "SelectParams",
+           "SkvError", "attn_params", "build_page_meta", "lib", "score_pages", "select_cap", "select_pages",
+           "select_params", "sparse_decode_attn", "status_str", "workspace_bytes"]

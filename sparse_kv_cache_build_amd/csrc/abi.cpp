@@ -1,0 +1,292 @@
+// C ABI of libskv: synchronous host-side validation, workspace planning and kernel dispatch.
+// Nothing is enqueued unless every argument checks out. See include/skv.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "launch.hpp"
+#include "skv.h"
+
+namespace {
+
+using skv::CacheView;
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+skv_status check_cache(const skv_cache *c) {
+  if (!c || !c->k || !c->v || !c->block_table || !c->seq_lens) return SKV_ERR_INVALID_ARG;
+  if (c->batch < 1 || c->num_q_heads < 1 || c->num_kv_heads < 1 || c->head_dim < 1 || c->page_size < 1 ||
+      c->max_pages < 1 || c->num_phys_pages < 1)
+    return SKV_ERR_INVALID_ARG;
+  if (c->num_q_heads % c->num_kv_heads) return SKV_ERR_INVALID_ARG;
+  if (c->dtype != SKV_DTYPE_F32 && c->dtype != SKV_DTYPE_BF16) return SKV_ERR_INVALID_ARG;
+  const int G = c->num_q_heads / c->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return SKV_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return SKV_ERR_UNSUPPORTED;
+  if (c->page_size > 1024) return SKV_ERR_UNSUPPORTED;
+  if ((int64_t)c->max_pages * c->page_size > INT32_MAX) return SKV_ERR_UNSUPPORTED;
+  if ((int64_t)c->batch * c->num_kv_heads > 65535 || c->batch > 65535) return SKV_ERR_UNSUPPORTED;
+  if (!aligned(c->k, 16) || !aligned(c->v, 16)) return SKV_ERR_INVALID_ARG;
+  return SKV_OK;
+}
+
+CacheView view(const skv_cache *c) {
+  CacheView v;
+  v.B = c->batch;
+  v.Hq = c->num_q_heads;
+  v.Hkv = c->num_kv_heads;
+  v.D = c->head_dim;
+  v.S = c->page_size;
+  v.maxP = c->max_pages;
+  v.Nphys = c->num_phys_pages;
+  v.G = c->num_q_heads / c->num_kv_heads;
+  v.k = c->k;
+  v.v = c->v;
+  v.bt = c->block_table;
+  v.lens = c->seq_lens;
+  return v;
+}
+
+skv_status hip_status(hipError_t e) { return e == hipSuccess ? SKV_OK : SKV_ERR_HIP; }
+
+bool rank_ok(int r) { return r == 16 || r == 32 || r == 64; }
+
+size_t score_ws(const skv_cache *c, int kind, int r) {
+  if (kind == SKV_SCORE_PROJ) return round_up(sizeof(double) * (size_t)c->batch * c->num_q_heads * r);
+  return round_up(sizeof(double) * 2 * (size_t)c->batch * c->num_q_heads * c->head_dim);
+}
+
+// Split-K plan of the attention call.
+struct AttnPlan {
+  int spi = 1, nsplit = 1, rps = 1;
+  size_t part = 0, cand = 0, cnt = 0, mx = 0, total = 0;
+};
+
+skv_status attn_plan(const skv_cache *c, const skv_attn_params *p, int cap, AttnPlan *out) {
+  const int G = c->num_q_heads / c->num_kv_heads;
+  const int rows_per_item = p->granularity ? 1 : c->page_size;
+  const bool entmax = p->alpha != 1.0f;
+  const int64_t U = (int64_t)c->batch * c->num_kv_heads;
+  const int rmax = entmax ? 512 : 1024;   // rows per partition
+  int64_t spi = p->split;
+  if (spi <= 0) {
+    spi = ((int64_t)cap * U + 2047) / 2048;   // about 2048 partitions in total
+    spi = std::max<int64_t>(1, std::min<int64_t>(spi, std::max(1, rmax / rows_per_item)));
+  }
+  spi = std::min<int64_t>(spi, cap);
+  const int64_t nsplit = (cap + spi - 1) / spi;
+  const int64_t rps = spi * rows_per_item;
+  if (nsplit > 65535) return SKV_ERR_UNSUPPORTED;
+  if (entmax && (int64_t)G * rps * 4 > 65536) return SKV_ERR_UNSUPPORTED;   // LDS of the logits pass
+  out->spi = (int)spi;
+  out->nsplit = (int)nsplit;
+  out->rps = (int)rps;
+  if (!entmax) {
+    out->part = nsplit > 1 ? round_up(sizeof(float) * (size_t)U * nsplit * G * (c->head_dim + 2)) : 0;
+  } else {
+    out->cand = round_up(sizeof(float) * 2 * (size_t)U * G * nsplit * rps);
+    out->cnt = round_up(sizeof(int32_t) * (size_t)U * G * nsplit);
+    out->mx = round_up(sizeof(float) * (size_t)U * G * nsplit);
+  }
+  out->total = out->part + out->cand + out->cnt + out->mx;
+  return SKV_OK;
+}
+
+skv_status check_attn_params(const skv_attn_params *p) {
+  if (!p) return SKV_ERR_INVALID_ARG;
+  if (!std::isfinite(p->alpha) || !(p->alpha == 1.0f || (p->alpha > 1.0f && p->alpha <= 2.0f)))
+    return SKV_ERR_INVALID_ARG;
+  if (!std::isfinite(p->sm_scale) || !(p->sm_scale > 0.0f)) return SKV_ERR_INVALID_ARG;
+  if (p->granularity != 0 && p->granularity != 1) return SKV_ERR_INVALID_ARG;
+  if (p->split < 0) return SKV_ERR_INVALID_ARG;
+  return SKV_OK;
+}
+
+int budget_cap(int maxP, int pct) {
+  const int64_t k = ((int64_t)pct * maxP + 99) / 100;
+  return (int)std::max<int64_t>(1, k);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *skv_status_str(skv_status s) {
+  switch (s) {
+    case SKV_OK: return "SKV_OK";
+    case SKV_ERR_INVALID_ARG: return "SKV_ERR_INVALID_ARG";
+    case SKV_ERR_UNSUPPORTED: return "SKV_ERR_UNSUPPORTED";
+    case SKV_ERR_CAPACITY: return "SKV_ERR_CAPACITY";
+    case SKV_ERR_WORKSPACE: return "SKV_ERR_WORKSPACE";
+    case SKV_ERR_HIP: return "SKV_ERR_HIP";
+  }
+  return "SKV_ERR_UNKNOWN";
+}
+
+skv_status skv_workspace_bytes(const skv_cache *c, int32_t op, const void *params, int32_t cap, size_t *bytes) {
+  if (!bytes || !params) return SKV_ERR_INVALID_ARG;
+  skv_status st = check_cache(c);
+  if (st != SKV_OK) return st;
+  if (op == SKV_OP_SCORE) {
+    const int kind = *static_cast<const int32_t *>(params);
+    if (kind < SKV_SCORE_BOX || kind > SKV_SCORE_PROJ) return SKV_ERR_INVALID_ARG;
+    *bytes = score_ws(c, kind, 64);
+    return SKV_OK;
+  }
+  if (op == SKV_OP_SELECT) {
+    *bytes = 0;
+    return SKV_OK;
+  }
+  if (op == SKV_OP_ATTN) {
+    const skv_attn_params *p = static_cast<const skv_attn_params *>(params);
+    if ((st = check_attn_params(p)) != SKV_OK) return st;
+    if (cap < 1) return SKV_ERR_INVALID_ARG;
+    AttnPlan plan;
+    if ((st = attn_plan(c, p, cap, &plan)) != SKV_OK) return st;
+    *bytes = plan.total;
+    return SKV_OK;
+  }
+  return SKV_ERR_INVALID_ARG;
+}
+
+skv_status skv_build_page_meta(const skv_cache *c, const skv_meta *m, void *stream) {
+  skv_status st = check_cache(c);
+  if (st != SKV_OK) return st;
+  if (!m || m->kinds == 0 || (m->kinds & ~(uint32_t)(SKV_META_BOX | SKV_META_GAUSS | SKV_META_PROJ)))
+    return SKV_ERR_INVALID_ARG;
+  const bool box = m->kinds & SKV_META_BOX, gauss = m->kinds & SKV_META_GAUSS, proj = m->kinds & SKV_META_PROJ;
+  if ((box && !m->box) || (gauss && !m->gauss)) return SKV_ERR_INVALID_ARG;
+  if (box && !aligned(m->box, 16)) return SKV_ERR_INVALID_ARG;
+  if (gauss && !aligned(m->gauss, 16)) return SKV_ERR_INVALID_ARG;
+  if (proj) {
+    if (!m->proj || !m->kproj) return SKV_ERR_INVALID_ARG;
+    if (!rank_ok(m->proj_rank)) return SKV_ERR_UNSUPPORTED;
+    const size_t lds = sizeof(float) * ((size_t)m->proj_rank * (c->head_dim + 1) + (size_t)c->page_size * c->head_dim);
+    if (lds > 65536) return SKV_ERR_UNSUPPORTED;
+  }
+  (void)hipGetLastError();
+  const hipError_t e = skv::launch_build_meta(view(c), c->dtype, box ? m->box : nullptr, gauss ? m->gauss : nullptr,
+                                              m->proj_rank, proj ? m->proj : nullptr, proj ? m->kproj : nullptr,
+                                              static_cast<hipStream_t>(stream));
+  return hip_status(e);
+}
+
+skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q, int32_t kind, float sm_scale,
+                           const skv_scores *out, void *workspace, size_t workspace_bytes, void *stream) {
+  skv_status st = check_cache(c);
+  if (st != SKV_OK) return st;
+  if (!m || !q || !out) return SKV_ERR_INVALID_ARG;
+  if (!aligned(q, 16)) return SKV_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const CacheView v = view(c);
+  if (kind == SKV_SCORE_BOX) {
+    if (!(m->kinds & SKV_META_BOX) || !m->box || !out->key || !aligned(m->box, 16)) return SKV_ERR_INVALID_ARG;
+  } else if (kind == SKV_SCORE_GAUSS) {
+    if (!(m->kinds & SKV_META_GAUSS) || !m->gauss || !out->m || !out->s || !out->shat || !aligned(m->gauss, 16))
+      return SKV_ERR_INVALID_ARG;
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SKV_ERR_INVALID_ARG;
+  } else if (kind == SKV_SCORE_PROJ) {
+    if (!(m->kinds & SKV_META_PROJ) || !m->kproj || !m->proj || !out->key) return SKV_ERR_INVALID_ARG;
+    if (!rank_ok(m->proj_rank)) return SKV_ERR_UNSUPPORTED;
+    if (!aligned(m->kproj, 16)) return SKV_ERR_INVALID_ARG;
+  } else {
+    return SKV_ERR_INVALID_ARG;
+  }
+  const size_t need = score_ws(c, kind, m->proj_rank);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 8)) return SKV_ERR_WORKSPACE;
+  double *ws = static_cast<double *>(workspace);
+  (void)hipGetLastError();
+  hipError_t e;
+  if (kind == SKV_SCORE_BOX)
+    e = skv::launch_score_box(v, c->dtype, q, m->box, out->key, ws, s);
+  else if (kind == SKV_SCORE_GAUSS)
+    e = skv::launch_score_gauss(v, c->dtype, q, m->gauss, (double)sm_scale, out->m, out->s, out->shat, ws, s);
+  else
+    e = skv::launch_score_proj(v, c->dtype, q, m->proj_rank, m->proj, m->kproj, out->key, ws, s);
+  return hip_status(e);
+}
+
+skv_status skv_select_pages(const skv_cache *c, const skv_scores *sc, const skv_select_params *p, int32_t *sel_idx,
+                            int32_t *sel_count, int32_t cap, float *tau_hat, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  skv_status st = check_cache(c);
+  if (st != SKV_OK) return st;
+  if (!sc || !p || !sel_idx || !sel_count || cap < 1) return SKV_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const CacheView v = view(c);
+  const int maxP = c->max_pages, Lmax = c->max_pages * c->page_size;
+  (void)hipGetLastError();
+  switch (p->policy) {
+    case SKV_SEL_TOPK:
+    case SKV_SEL_TOKEN_TOPK: {
+      if (p->k < 1 || !sc->key) return SKV_ERR_INVALID_ARG;
+      if (cap < p->k) return SKV_ERR_CAPACITY;
+      const int stride = p->policy == SKV_SEL_TOPK ? maxP : Lmax;
+      return hip_status(skv::launch_select_topk(v, sc->key, stride, p->policy, p->k, 0, sel_idx, sel_count, cap, s));
+    }
+    case SKV_SEL_BUDGET: {
+      if (p->budget_pct < 1 || p->budget_pct > 100 || !sc->key) return SKV_ERR_INVALID_ARG;
+      if (cap < budget_cap(maxP, p->budget_pct)) return SKV_ERR_CAPACITY;
+      return hip_status(
+          skv::launch_select_topk(v, sc->key, maxP, p->policy, 0, p->budget_pct, sel_idx, sel_count, cap, s));
+    }
+    case SKV_SEL_THRESH_GAUSS: {
+      if (!sc->m || !sc->s || !sc->shat || !tau_hat) return SKV_ERR_INVALID_ARG;
+      if (!std::isfinite(p->delta) || p->delta < 0.0f) return SKV_ERR_INVALID_ARG;
+      if (!std::isfinite(p->alpha) || !(p->alpha > 1.0f && p->alpha <= 2.0f)) return SKV_ERR_INVALID_ARG;
+      if (p->alpha != 1.5f && p->alpha != 2.0f) return SKV_ERR_UNSUPPORTED;
+      if (cap < maxP) return SKV_ERR_CAPACITY;
+      return hip_status(skv::launch_select_thresh(v, sc->m, sc->s, sc->shat, p->alpha, p->delta, tau_hat, sel_idx,
+                                                  sel_count, cap, s));
+    }
+    case SKV_SEL_ALL: {
+      if (p->tokens != 0 && p->tokens != 1) return SKV_ERR_INVALID_ARG;
+      if (cap < (p->tokens ? Lmax : maxP)) return SKV_ERR_CAPACITY;
+      return hip_status(skv::launch_select_all(v, p->tokens, sel_idx, sel_count, cap, s));
+    }
+    default:
+      return SKV_ERR_INVALID_ARG;
+  }
+}
+
+skv_status skv_sparse_decode_attn(const skv_cache *c, const void *q, const int32_t *sel_idx, const int32_t *sel_count,
+                                  int32_t cap, const skv_attn_params *p, float *out, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+  skv_status st = check_cache(c);
+  if (st != SKV_OK) return st;
+  if (!q || !sel_idx || !sel_count || !out || cap < 1) return SKV_ERR_INVALID_ARG;
+  if (!aligned(q, 16)) return SKV_ERR_INVALID_ARG;
+  if ((st = check_attn_params(p)) != SKV_OK) return st;
+  AttnPlan plan;
+  if ((st = attn_plan(c, p, cap, &plan)) != SKV_OK) return st;
+  if (plan.total && (!workspace || workspace_bytes < plan.total || !aligned(workspace, 16))) return SKV_ERR_WORKSPACE;
+  char *ws = static_cast<char *>(workspace);
+  skv::AttnArgs a;
+  a.c = view(c);
+  a.dtype = c->dtype;
+  a.q = q;
+  a.sel_idx = sel_idx;
+  a.sel_count = sel_count;
+  a.cap = cap;
+  a.gran = p->granularity;
+  a.spi = plan.spi;
+  a.nsplit = plan.nsplit;
+  a.alpha = p->alpha;
+  a.sm_scale = p->sm_scale;
+  a.out = out;
+  a.part = plan.part ? reinterpret_cast<float *>(ws) : nullptr;
+  a.cand = plan.cand ? reinterpret_cast<float2 *>(ws) : nullptr;
+  a.cand_cnt = plan.cnt ? reinterpret_cast<int32_t *>(ws + plan.cand) : nullptr;
+  a.cand_max = plan.mx ? reinterpret_cast<float *>(ws + plan.cand + plan.cnt) : nullptr;
+  (void)hipGetLastError();
+  return hip_status(skv::launch_attn(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,208 @@
+// Device-side helpers shared by the kernels of libskv (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+namespace skv {
+
+constexpr int kWave = 64;
+
+// Plain view of the paged cache passed by value to kernels.
+struct CacheView {
+  int32_t B, Hq, Hkv, D, S, maxP, Nphys, G;
+  const void *k;
+  const void *v;
+  const int32_t *bt;    // [B, maxP]
+  const int32_t *lens;  // [B]
+};
+
+// Valid length of sequence b, clamped to [0, maxP * S].
+__device__ __forceinline__ int seq_len(const CacheView &c, int b) {
+  int L = c.lens[b];
+  int cap = c.maxP * c.S;
+  return L < 0 ? 0 : (L > cap ? cap : L);
+}
+
+__device__ __forceinline__ int num_pages(const CacheView &c, int L) { return (L + c.S - 1) / c.S; }
+
+// ---------------------------------------------------------------- element access
+// Cache elements are float or bf16 (stored as uint16_t bit patterns). bf16 widens to f32 by a
+// 16-bit shift, which is exact.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+  static __device__ __forceinline__ float get(const float *p, size_t i) { return p[i]; }
+  // 8 consecutive elements (32-byte aligned)
+  static __device__ __forceinline__ void load8(const float *p, float (&x)[8]) {
+    float4 a = *reinterpret_cast<const float4 *>(p);
+    float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+};
+
+template <>
+struct Elem<uint16_t> {
+  static __device__ __forceinline__ float get(const uint16_t *p, size_t i) { return bf16_f32(p[i]); }
+  // 8 consecutive elements (16-byte aligned)
+  static __device__ __forceinline__ void load8(const uint16_t *p, float (&x)[8]) {
+    uint4 w = *reinterpret_cast<const uint4 *>(p);
+    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+  }
+};
+
+// Round a double to bf16, nearest-even. Normal range: round to odd at binary32 (truncate,
+// then set the last bit when inexact) and round that to nearest-even at 8 significant bits;
+// a round-to-odd intermediate with at least two extra bits makes the second rounding equal
+// to a single one. Below 2^-126 bf16 is subnormal with quantum 2^-133: round |x| * 2^133 to an
+// integer directly (it is the fraction field, and 128 carries into the smallest normal).
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  if (x != x) return 0x7fc0;
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  double ax = fabs(x);
+  if (ax < 0x1p-126) return sign | (uint16_t)rint(ax * 0x1p133);
+  float f = (float)ax;  // round to nearest even
+  uint32_t u = __float_as_uint(f);
+  double back = (double)f;
+  if (back != ax) {
+    if (back > ax) u -= 1;  // rounded up: step back to the truncated value
+    u |= 1u;                // sticky bit
+  }
+  if ((u & 0x7f800000u) == 0x7f800000u) return sign | 0x7f80;  // +inf
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return sign | (uint16_t)(u >> 16);
+}
+
+// Order-preserving map float -> uint32 (larger float, larger key); -0 and +0 map alike.
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u << 1) == 0) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- wave / block reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ double wave_max(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Block-wide exclusive prefix sum for blocks of NT threads (NT a multiple of 64, <= 1024).
+// `scratch` holds NT/64 + 1 ints of shared memory. Returns the exclusive prefix; *total gets the
+// block sum. Contains __syncthreads: every thread of the block must call it.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int *scratch, int *total) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  int incl = wave_incl_scan(v);
+  if (lane == kWave - 1) scratch[w] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < NW; ++i) {
+      int t = scratch[i];
+      scratch[i] = run;
+      run += t;
+    }
+    scratch[NW] = run;
+  }
+  __syncthreads();
+  int res = scratch[w] + incl - v;
+  *total = scratch[NW];
+  __syncthreads();
+  return res;
+}
+
+template <int NT>
+__device__ __forceinline__ float block_max(float v, float *scratch) {
+  constexpr int NW = NT / kWave;
+  v = wave_max(v);
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[threadIdx.x / kWave] = v;
+  __syncthreads();
+  float r = scratch[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = fmaxf(r, scratch[i]);
+  __syncthreads();
+  return r;
+}
+
+template <int NT>
+__device__ __forceinline__ double block_sum(double v, double *scratch) {
+  constexpr int NW = NT / kWave;
+  v = wave_sum(v);
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[threadIdx.x / kWave] = v;
+  __syncthreads();
+  double r = scratch[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r += scratch[i];
+  __syncthreads();
+  return r;
+}
+
+template <int NT>
+__device__ __forceinline__ double block_max(double v, double *scratch) {
+  constexpr int NW = NT / kWave;
+  v = wave_max(v);
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[threadIdx.x / kWave] = v;
+  __syncthreads();
+  double r = scratch[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = fmax(r, scratch[i]);
+  __syncthreads();
+  return r;
+}
+
+// Sum over the `width` consecutive lanes of an aligned lane group (width 8 or 16) with DPP moves:
+// quad_perm [1,0,3,2] and [2,3,0,1] sum a quad, row_half_mirror pairs the two quads of 8 lanes,
+// row_mirror the two halves of a 16-lane row. Every lane of the group gets the group sum.
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(WIDTH == 8 || WIDTH == 16, "lane group of 8 or 16");
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+  if (WIDTH == 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+}  // namespace skv

@@ -1,0 +1,42 @@
+// Internal launchers of libskv (host functions defined next to their kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace skv {
+
+struct AttnArgs {
+  CacheView c;
+  int dtype;
+  const void *q;
+  const int32_t *sel_idx;
+  const int32_t *sel_count;
+  int cap, gran, spi, nsplit;
+  float alpha, sm_scale;
+  float *out;
+  float *part;       // softmax split partials [U, nsplit, G, D + 2]
+  float2 *cand;      // entmax (z', slot) pairs [U, G, nsplit, rps]
+  int32_t *cand_cnt; // [U, G, nsplit]
+  float *cand_max;   // [U, G, nsplit]
+};
+
+hipError_t launch_build_meta(const CacheView &c, int dtype, void *box, float *gauss, int r, const float *proj,
+                             uint16_t *kproj, hipStream_t st);
+hipError_t launch_score_box(const CacheView &c, int dtype, const void *q, const void *box, float *key, double *ws,
+                            hipStream_t st);
+hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, const float *gauss, double scale, float *m,
+                              float *s, float *shat, double *ws, hipStream_t st);
+hipError_t launch_score_proj(const CacheView &c, int dtype, const void *q, int r, const float *proj,
+                             const uint16_t *kproj, float *key, double *ws, hipStream_t st);
+hipError_t launch_select_topk(const CacheView &c, const float *key, int key_stride, int policy, int k, int pct,
+                              int32_t *sel_idx, int32_t *sel_count, int cap, hipStream_t st);
+hipError_t launch_select_all(const CacheView &c, int tokens, int32_t *sel_idx, int32_t *sel_count, int cap,
+                             hipStream_t st);
+hipError_t launch_select_thresh(const CacheView &c, const float *m, const float *s, const float *shat, float alpha,
+                                float delta, float *tau, int32_t *sel_idx, int32_t *sel_count, int cap, hipStream_t st);
+hipError_t launch_attn(const AttnArgs &a, hipStream_t st);
+
+}  // namespace skv

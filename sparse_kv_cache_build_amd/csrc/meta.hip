@@ -1,0 +1,103 @@
+// Page metadata builder ("EntmaxKV" summary s2.A: per-page box bounds and Gaussian moments;
+// "Joint Subspace Sparse Attention" abstract: keys cached in a shared low-dimensional subspace).
+// Runs once per page at prefill / append time, off the per-step path.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace skv {
+
+// One workgroup per logical page (p, b); threads sweep (KV head, coordinate) pairs so that each
+// token row is read with consecutive coordinates across consecutive threads.
+//   box:   exact min / max over the valid tokens, stored as the original element bits.
+//   gauss: float64 mean (sum over t ascending, divided by n), then float64 mean squared
+//          deviation, each rounded once to float32.
+template <typename T>
+__global__ __launch_bounds__(256) void meta_box_gauss_kernel(CacheView c, T *__restrict__ box,
+                                                             float *__restrict__ gauss) {
+  const int p = blockIdx.x, b = blockIdx.y;
+  const int L = seq_len(c, b);
+  if (p >= num_pages(c, L)) return;
+  const int n = min(c.S, L - p * c.S);
+  const int phys = c.bt[(size_t)b * c.maxP + p];
+  const T *K = static_cast<const T *>(c.k);
+  for (int idx = threadIdx.x; idx < c.Hkv * c.D; idx += blockDim.x) {
+    const int g = idx / c.D, j = idx - g * c.D;
+    const size_t base = ((size_t)phys * c.Hkv + g) * c.S * c.D + j;
+    const size_t mo = ((size_t)phys * c.Hkv + g) * 2 * c.D + j;
+    if (box) {
+      T lo = K[base], hi = K[base];
+      float flo = Elem<T>::get(K, base), fhi = flo;
+      for (int t = 1; t < n; ++t) {
+        T x = K[base + (size_t)t * c.D];
+        float fx = Elem<T>::get(K, base + (size_t)t * c.D);
+        if (fx < flo) { flo = fx; lo = x; }
+        if (fx > fhi) { fhi = fx; hi = x; }
+      }
+      box[mo] = lo;
+      box[mo + c.D] = hi;
+    }
+    if (gauss) {
+      double sum = 0.0;
+      for (int t = 0; t < n; ++t) sum += (double)Elem<T>::get(K, base + (size_t)t * c.D);
+      const double mu = sum / n;
+      double ss = 0.0;
+      for (int t = 0; t < n; ++t) {
+        const double dv = (double)Elem<T>::get(K, base + (size_t)t * c.D) - mu;
+        ss += dv * dv;
+      }
+      gauss[mo] = (float)mu;
+      gauss[mo + c.D] = (float)(ss / n);
+    }
+  }
+}
+
+// Projected keys k~_t[i] = RN_bf16(sum_j P[i][j] k_t[j]) (float64, j ascending). One workgroup
+// per (logical page, KV head): the page's keys and P are staged in LDS as float (exact), then
+// each thread owns (token, i) pairs.
+template <typename T>
+__global__ __launch_bounds__(256) void meta_proj_kernel(CacheView c, int r, const float *__restrict__ proj,
+                                                        uint16_t *__restrict__ kproj) {
+  extern __shared__ float smem[];
+  const int p = blockIdx.x, b = blockIdx.y / c.Hkv, g = blockIdx.y % c.Hkv;
+  const int L = seq_len(c, b);
+  if (p >= num_pages(c, L)) return;
+  const int n = min(c.S, L - p * c.S);
+  const int phys = c.bt[(size_t)b * c.maxP + p];
+  const int ldp = c.D + 1;  // padded row stride of P (bank spread across i)
+  float *Ps = smem;                     // [r][D+1]
+  float *Ks = smem + (size_t)r * ldp;   // [n][D]
+  const T *K = static_cast<const T *>(c.k) + ((size_t)phys * c.Hkv + g) * c.S * c.D;
+  for (int i = threadIdx.x; i < r * c.D; i += blockDim.x) Ps[(i / c.D) * ldp + i % c.D] = proj[i];
+  for (int i = threadIdx.x; i < n * c.D; i += blockDim.x) Ks[i] = Elem<T>::get(K, i);
+  __syncthreads();
+  uint16_t *out = kproj + ((size_t)phys * c.Hkv + g) * c.S * r;
+  for (int pair = threadIdx.x; pair < n * r; pair += blockDim.x) {
+    const int t = pair / r, i = pair - t * r;
+    const float *pr = Ps + i * ldp, *kr = Ks + t * c.D;
+    double acc = 0.0;
+    for (int j = 0; j < c.D; ++j) acc = fma((double)pr[j], (double)kr[j], acc);
+    out[(size_t)t * r + i] = f64_to_bf16(acc);
+  }
+}
+
+hipError_t launch_build_meta(const CacheView &c, int dtype, void *box, float *gauss, int r, const float *proj,
+                             uint16_t *kproj, hipStream_t st) {
+  const dim3 grid(c.maxP, c.B);
+  if (box || gauss) {
+    if (dtype == 0)
+      meta_box_gauss_kernel<float><<<grid, 256, 0, st>>>(c, static_cast<float *>(box), gauss);
+    else
+      meta_box_gauss_kernel<uint16_t><<<grid, 256, 0, st>>>(c, static_cast<uint16_t *>(box), gauss);
+  }
+  if (kproj) {
+    const size_t lds = sizeof(float) * ((size_t)r * (c.D + 1) + (size_t)c.S * c.D);
+    const dim3 g2(c.maxP, c.B * c.Hkv);
+    if (dtype == 0)
+      meta_proj_kernel<float><<<g2, 256, lds, st>>>(c, r, proj, kproj);
+    else
+      meta_proj_kernel<uint16_t><<<g2, 256, lds, st>>>(c, r, proj, kproj);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace skv

@@ -1,0 +1,245 @@
+// Query-aware page / token scores ("EntmaxKV" summary s2.A; "Joint Subspace Sparse Attention"
+// abstract for token scores in the shared subspace).
+//
+// Exactness: every score sum runs in float64 over the coordinate index in ascending order, one
+// lane per page (or token), so that the float32 key is the rounding of the same float64 value
+// a plain sequential loop produces; all products involved are exact in float64. The query terms
+// are staged once per step in a float64 workspace, read by uniform (scalar) loads.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace skv {
+
+// Per query head and coordinate, two float64 terms:
+//   BOX:   (max(q_j, 0), min(q_j, 0)), so that max(q kmin, q kmax) = q+ kmax + q- kmin term by term
+//   GAUSS: (q_j, q_j^2)
+// Layout [B, Hq, D, 2].
+template <typename T>
+__global__ void qprep_pair_kernel(const T *__restrict__ q, int n, int gauss, double *__restrict__ out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const double x = (double)Elem<T>::get(q, i);
+  out[2 * i] = gauss ? x : fmax(x, 0.0);
+  out[2 * i + 1] = gauss ? x * x : fmin(x, 0.0);
+}
+
+// PROJ: q~_h[i] = RN_f32(sum_j P[i][j] q_hj) (float64 sum, j ascending), stored as float64 values.
+// Layout [B, Hq, r].
+template <typename T>
+__global__ void qprep_proj_kernel(const T *__restrict__ q, int BH, int D, int r, const float *__restrict__ proj,
+                                  double *__restrict__ out) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= BH * r) return;
+  const int bh = idx / r, i = idx - bh * r;
+  const T *qh = q + (size_t)bh * D;
+  double acc = 0.0;
+  for (int j = 0; j < D; ++j) acc = fma((double)proj[(size_t)i * D + j], (double)Elem<T>::get(qh, j), acc);
+  out[idx] = (double)(float)acc;
+}
+
+// BOX key: one lane per page. key[b][g][p] = RN_f32(max_h sum_j (q+_hj kmax_j + q-_hj kmin_j)).
+// For each coordinate exactly one of the two products is nonzero (or both are zero), so the
+// float64 running sum equals sum_j max(q_hj kmin_j, q_hj kmax_j) accumulated in order.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void score_box_kernel(CacheView c, const T *__restrict__ box,
+                                                        const double *__restrict__ qpm, float *__restrict__ key) {
+  const int unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= c.maxP) return;
+  float *out = key + (size_t)unit * c.maxP + p;
+  const int P = num_pages(c, seq_len(c, b));
+  if (p >= P) {
+    *out = -INFINITY;
+    return;
+  }
+  const int phys = c.bt[(size_t)b * c.maxP + p];
+  const T *lo = box + ((size_t)phys * c.Hkv + g) * 2 * D;
+  const T *hi = lo + D;
+  const double *qq = qpm + (size_t)(b * c.Hq + g * G) * D * 2;
+  double acc[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) acc[h] = 0.0;
+#pragma unroll
+  for (int j0 = 0; j0 < D; j0 += 8) {
+    float xl[8], xh[8];
+    Elem<T>::load8(lo + j0, xl);
+    Elem<T>::load8(hi + j0, xh);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const double dl = xl[jj], dh = xh[jj];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        acc[h] = fma(qq[((size_t)h * D + j0 + jj) * 2], dh, acc[h]);
+        acc[h] = fma(qq[((size_t)h * D + j0 + jj) * 2 + 1], dl, acc[h]);
+      }
+    }
+  }
+  double best = acc[0];
+#pragma unroll
+  for (int h = 1; h < G; ++h) best = fmax(best, acc[h]);
+  *out = (float)best;
+}
+
+// GAUSS scores: one lane per page, G heads. m = scale sum_j q_j mean_j, s = scale sqrt(sum_j
+// q_j^2 var_j) (float64), shat = m + s sqrt(2 ln n_p). Outputs [B, Hq, maxP].
+template <int D, int G>
+__global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const float *__restrict__ gauss,
+                                                          const double *__restrict__ qpm, double scale,
+                                                          float *__restrict__ m_out, float *__restrict__ s_out,
+                                                          float *__restrict__ shat_out) {
+  const int unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= c.maxP) return;
+  const int L = seq_len(c, b);
+  const size_t o0 = (size_t)(b * c.Hq + g * G) * c.maxP + p;
+  if (p >= num_pages(c, L)) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) m_out[o0 + (size_t)h * c.maxP] = s_out[o0 + (size_t)h * c.maxP] =
+        shat_out[o0 + (size_t)h * c.maxP] = NAN;
+    return;
+  }
+  const int n = min(c.S, L - p * c.S);
+  const int phys = c.bt[(size_t)b * c.maxP + p];
+  const float *mu = gauss + ((size_t)phys * c.Hkv + g) * 2 * D;
+  const float *var = mu + D;
+  const double *qq = qpm + (size_t)(b * c.Hq + g * G) * D * 2;
+  double sm[G], sv[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) sm[h] = sv[h] = 0.0;
+#pragma unroll
+  for (int j0 = 0; j0 < D; j0 += 8) {
+    float xm[8], xv[8];
+    Elem<float>::load8(mu + j0, xm);
+    Elem<float>::load8(var + j0, xv);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const double dm = xm[jj], dv = xv[jj];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        sm[h] = fma(qq[((size_t)h * D + j0 + jj) * 2], dm, sm[h]);
+        sv[h] = fma(qq[((size_t)h * D + j0 + jj) * 2 + 1], dv, sv[h]);
+      }
+    }
+  }
+  const double lg = sqrt(2.0 * log((double)n));
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const double m = scale * sm[h], s = scale * sqrt(sv[h]);
+    m_out[o0 + (size_t)h * c.maxP] = (float)m;
+    s_out[o0 + (size_t)h * c.maxP] = (float)s;
+    shat_out[o0 + (size_t)h * c.maxP] = (float)(m + s * lg);
+  }
+}
+
+// PROJ key: one lane per token t. u_h(t) = sum_i q~_h[i] k~_t[i] (float64, i ascending; the
+// products of a float32 and a bf16 value are exact), key = RN_f32(max_h u_h(t)).
+template <int R, int G>
+__global__ __launch_bounds__(256) void score_proj_kernel(CacheView c, const uint16_t *__restrict__ kproj,
+                                                         const double *__restrict__ qt, float *__restrict__ key) {
+  const int unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int Lmax = c.maxP * c.S;
+  if (t >= Lmax) return;
+  float *out = key + (size_t)unit * Lmax + t;
+  if (t >= seq_len(c, b)) {
+    *out = -INFINITY;
+    return;
+  }
+  const int phys = c.bt[(size_t)b * c.maxP + t / c.S];
+  const uint16_t *row = kproj + (((size_t)phys * c.Hkv + g) * c.S + t % c.S) * R;
+  const double *qq = qt + (size_t)(b * c.Hq + g * G) * R;
+  double acc[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) acc[h] = 0.0;
+#pragma unroll
+  for (int i0 = 0; i0 < R; i0 += 8) {
+    float x[8];
+    Elem<uint16_t>::load8(row + i0, x);
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) {
+      const double dx = x[ii];
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc[h] = fma(qq[(size_t)h * R + i0 + ii], dx, acc[h]);
+    }
+  }
+  double best = acc[0];
+#pragma unroll
+  for (int h = 1; h < G; ++h) best = fmax(best, acc[h]);
+  *out = (float)best;
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <typename T>
+static hipError_t qprep_pair(const void *q, int n, int gauss, double *ws, hipStream_t st) {
+  qprep_pair_kernel<T><<<(n + 255) / 256, 256, 0, st>>>(static_cast<const T *>(q), n, gauss, ws);
+  return hipGetLastError();
+}
+
+#define SKV_DISPATCH_G(G, ...)                      \
+  switch (G) {                                      \
+    case 1: { constexpr int GG = 1; __VA_ARGS__; } break; \
+    case 2: { constexpr int GG = 2; __VA_ARGS__; } break; \
+    case 4: { constexpr int GG = 4; __VA_ARGS__; } break; \
+    case 8: { constexpr int GG = 8; __VA_ARGS__; } break; \
+    default: return hipErrorInvalidValue;           \
+  }
+
+template <typename T, int D>
+static hipError_t box_d(const CacheView &c, const void *box, const double *qpm, float *key, hipStream_t st) {
+  const dim3 grid((c.maxP + 255) / 256, c.B * c.Hkv);
+  SKV_DISPATCH_G(c.G, score_box_kernel<T, D, GG><<<grid, 256, 0, st>>>(c, static_cast<const T *>(box), qpm, key))
+  return hipGetLastError();
+}
+
+hipError_t launch_score_box(const CacheView &c, int dtype, const void *q, const void *box, float *key, double *ws,
+                            hipStream_t st) {
+  const int n = c.B * c.Hq * c.D;
+  hipError_t e = dtype == 0 ? qprep_pair<float>(q, n, 0, ws, st) : qprep_pair<uint16_t>(q, n, 0, ws, st);
+  if (e != hipSuccess) return e;
+  if (c.D == 64) return dtype == 0 ? box_d<float, 64>(c, box, ws, key, st) : box_d<uint16_t, 64>(c, box, ws, key, st);
+  return dtype == 0 ? box_d<float, 128>(c, box, ws, key, st) : box_d<uint16_t, 128>(c, box, ws, key, st);
+}
+
+template <int D>
+static hipError_t gauss_d(const CacheView &c, const float *gauss, const double *qpm, double scale, float *m, float *s,
+                          float *shat, hipStream_t st) {
+  const dim3 grid((c.maxP + 255) / 256, c.B * c.Hkv);
+  SKV_DISPATCH_G(c.G, score_gauss_kernel<D, GG><<<grid, 256, 0, st>>>(c, gauss, qpm, scale, m, s, shat))
+  return hipGetLastError();
+}
+
+hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, const float *gauss, double scale, float *m,
+                              float *s, float *shat, double *ws, hipStream_t st) {
+  const int n = c.B * c.Hq * c.D;
+  hipError_t e = dtype == 0 ? qprep_pair<float>(q, n, 1, ws, st) : qprep_pair<uint16_t>(q, n, 1, ws, st);
+  if (e != hipSuccess) return e;
+  return c.D == 64 ? gauss_d<64>(c, gauss, ws, scale, m, s, shat, st) : gauss_d<128>(c, gauss, ws, scale, m, s, shat, st);
+}
+
+template <int R>
+static hipError_t proj_r(const CacheView &c, const uint16_t *kproj, const double *qt, float *key, hipStream_t st) {
+  const dim3 grid((c.maxP * c.S + 255) / 256, c.B * c.Hkv);
+  SKV_DISPATCH_G(c.G, score_proj_kernel<R, GG><<<grid, 256, 0, st>>>(c, kproj, qt, key))
+  return hipGetLastError();
+}
+
+hipError_t launch_score_proj(const CacheView &c, int dtype, const void *q, int r, const float *proj,
+                             const uint16_t *kproj, float *key, double *ws, hipStream_t st) {
+  const int BH = c.B * c.Hq;
+  if (dtype == 0)
+    qprep_proj_kernel<float><<<(BH * r + 255) / 256, 256, 0, st>>>(static_cast<const float *>(q), BH, c.D, r, proj, ws);
+  else
+    qprep_proj_kernel<uint16_t><<<(BH * r + 255) / 256, 256, 0, st>>>(static_cast<const uint16_t *>(q), BH, c.D, r,
+                                                                        proj, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (r) {
+    case 16: return proj_r<16>(c, kproj, ws, key, st);
+    case 32: return proj_r<32>(c, kproj, ws, key, st);
+    case 64: return proj_r<64>(c, kproj, ws, key, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace skv

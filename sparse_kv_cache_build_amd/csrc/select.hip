@@ -1,0 +1,257 @@
+// Candidate selection ("EntmaxKV" summary s2.B: top-k pages by bound, Gaussian-aware entmax
+// threshold; "Joint Subspace Sparse Attention" abstract: top-k tokens per KV head).
+// One selection per (sequence, KV head); indices are emitted in ascending order.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace skv {
+
+constexpr int kSelThreads = 512;
+constexpr int kSelLds = 16384;   // keys held in LDS when n <= kSelLds (64 KiB)
+
+// Number of candidates and how many to keep for unit (b, g).
+struct SelSize {
+  int n, k;
+};
+
+__device__ __forceinline__ SelSize sel_size(const CacheView &c, int b, int policy, int k, int pct) {
+  const int L = seq_len(c, b);
+  const int P = num_pages(c, L);
+  SelSize s;
+  if (policy == 3) {  // TOKEN_TOPK
+    s.n = L;
+    s.k = min(k, L);
+  } else if (policy == 1) {  // BUDGET: ceil(pct * P / 100), at least 1
+    s.n = P;
+    const long long kb = ((long long)pct * P + 99) / 100;
+    s.k = P == 0 ? 0 : (int)min((long long)P, max(1LL, kb));
+  } else {  // TOPK
+    s.n = P;
+    s.k = min(k, P);
+  }
+  return s;
+}
+
+// Radix selection of the k largest keys (order: key descending, index ascending), then an
+// ordered compaction. The float keys are mapped to order-preserving uint32; four 8-bit digits,
+// most significant first, find the exact k-th largest key T and how many keys equal to T are
+// needed (the lowest-indexed ones). Integer LDS atomics only, so the result is deterministic.
+__global__ __launch_bounds__(kSelThreads) void select_topk_kernel(CacheView c, const float *__restrict__ key,
+                                                                  int key_stride, int policy, int k, int pct,
+                                                                  int32_t *__restrict__ sel_idx,
+                                                                  int32_t *__restrict__ sel_count, int cap) {
+  __shared__ uint32_t skeys[kSelLds];
+  __shared__ uint32_t hist[256];
+  __shared__ int scan_scratch[kSelThreads / kWave + 1];
+  __shared__ uint32_t s_prefix, s_need;
+  const int unit = blockIdx.x, b = unit / c.Hkv;
+  const SelSize sz = sel_size(c, b, policy, k, pct);
+  const float *kr = key + (size_t)unit * key_stride;
+  int32_t *out = sel_idx + (size_t)unit * cap;
+  const int tid = threadIdx.x;
+  if (tid == 0) sel_count[unit] = sz.k;
+  if (sz.k <= 0) return;
+  if (sz.k >= sz.n) {  // everything is kept
+    for (int i = tid; i < sz.n; i += kSelThreads) out[i] = i;
+    return;
+  }
+  const bool in_lds = sz.n <= kSelLds;
+  if (in_lds)
+    for (int i = tid; i < sz.n; i += kSelThreads) skeys[i] = f32_order_key(kr[i]);
+  __syncthreads();
+
+  uint32_t prefix = 0, mask = 0;
+  uint32_t need = (uint32_t)sz.k;  // keys still to take from those matching prefix
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < sz.n; i += kSelThreads) {
+      const uint32_t u = in_lds ? skeys[i] : f32_order_key(kr[i]);
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 0xffu], 1u);
+    }
+    __syncthreads();
+    // suffix counts: the wanted digit v has count(> v) < need <= count(>= v)
+    if (tid < kWave) {
+      uint32_t c4[4];
+      uint32_t local = 0;
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {  // lane handles digits 4*lane .. 4*lane+3
+        c4[i] = hist[4 * tid + i];
+        local += c4[i];
+      }
+      // exclusive suffix sum over lanes (higher lanes hold larger digits)
+      uint32_t incl = local;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        uint32_t t = __shfl_down(incl, o, kWave);
+        if (tid + o < kWave) incl += t;
+      }
+      uint32_t above = incl - local;  // keys with digit > 4*tid+3
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if (above < need && above + c4[i] >= need) {
+          s_prefix = prefix | ((uint32_t)(4 * tid + i) << shift);
+          s_need = need - above;
+        }
+        above += c4[i];
+      }
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    need = s_need;
+    mask |= 0xffu << shift;
+    __syncthreads();
+  }
+  // prefix == T (the k-th largest key); take keys > T and the first `need` keys == T.
+  const int per = (sz.n + kSelThreads - 1) / kSelThreads;
+  const int i0 = min(sz.n, tid * per), i1 = min(sz.n, i0 + per);
+  int ngt = 0, neq = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t u = in_lds ? skeys[i] : f32_order_key(kr[i]);
+    ngt += u > prefix;
+    neq += u == prefix;
+  }
+  int tot;
+  int gt_before = block_excl_scan<kSelThreads>(ngt, scan_scratch, &tot);
+  int eq_before = block_excl_scan<kSelThreads>(neq, scan_scratch, &tot);
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t u = in_lds ? skeys[i] : f32_order_key(kr[i]);
+    const bool take = u > prefix || (u == prefix && (uint32_t)eq_before < need);
+    if (take) out[gt_before + min((uint32_t)eq_before, need)] = i;
+    gt_before += u > prefix;
+    eq_before += u == prefix;
+  }
+}
+
+// Every page (or token) of the sequence.
+__global__ void select_all_kernel(CacheView c, int tokens, int32_t *__restrict__ sel_idx,
+                                  int32_t *__restrict__ sel_count, int cap) {
+  const int unit = blockIdx.y, b = unit / c.Hkv;
+  const int L = seq_len(c, b);
+  const int n = tokens ? L : num_pages(c, L);
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0) sel_count[unit] = n;
+  if (i < n) sel_idx[(size_t)unit * cap + i] = i;
+}
+
+// ---------------------------------------------------------------- Gaussian-aware threshold
+
+// E[(X - tau)_+^(1/(alpha-1))] and its tau-derivative for X ~ N(mu_x, sd^2), alpha in {1.5, 2}:
+//   alpha = 2:   E = mu Phi(a) + sd phi(a),                 dE/dtau = -Phi(a)
+//   alpha = 1.5: E = (mu^2 + sd^2) Phi(a) + mu sd phi(a),   dE/dtau = -2 (mu Phi(a) + sd phi(a))
+// with mu = mu_x - tau, a = mu / sd; a zero sd gives the point-mass values.
+__device__ __forceinline__ void gauss_moment(float mu, float sd, bool sparsemax, float &E, float &dE) {
+  if (sd <= 0.0f) {
+    const float pos = fmaxf(mu, 0.0f);
+    E = sparsemax ? pos : pos * pos;
+    dE = sparsemax ? -(mu > 0.0f ? 1.0f : 0.0f) : -2.0f * pos;
+    return;
+  }
+  const float a = mu / sd;
+  const float Phi = 0.5f * erfcf(-a * 0.70710678118654752f);
+  const float phi = 0.39894228040143268f * expf(-0.5f * a * a);
+  const float first = mu * Phi + sd * phi;
+  if (sparsemax) {
+    E = first;
+    dE = -Phi;
+  } else {
+    E = (mu * mu + sd * sd) * Phi + mu * sd * phi;
+    dE = -2.0f * first;
+  }
+}
+
+// tau_hat per (sequence, query head): root of F(tau) = sum_p n_p E_p(tau) - 1, which is convex
+// and non-increasing. Newton's method started at tau0 = (alpha-1) max_p m_p - 1, where F >= 0,
+// moves right monotonically without passing the root. Per-page terms in float32, sums in
+// float64. Stops when the step falls below 2^-22 max(1, |tau|) or after 64 steps.
+__global__ __launch_bounds__(256) void tau_hat_kernel(CacheView c, const float *__restrict__ m,
+                                                      const float *__restrict__ s, float alpha,
+                                                      float *__restrict__ tau_out) {
+  __shared__ double red[256 / kWave];
+  __shared__ float redf[256 / kWave];
+  const int bh = blockIdx.x, b = bh / c.Hq;
+  const int L = seq_len(c, b);
+  const int P = num_pages(c, L);
+  const float *mr = m + (size_t)bh * c.maxP, *sr = s + (size_t)bh * c.maxP;
+  if (P == 0) {
+    if (threadIdx.x == 0) tau_out[bh] = NAN;
+    return;
+  }
+  const float am1 = alpha - 1.0f;
+  const bool sparsemax = alpha == 2.0f;
+  float mx = -INFINITY;
+  for (int p = threadIdx.x; p < P; p += 256) mx = fmaxf(mx, mr[p]);
+  mx = block_max<256>(mx, redf);
+  float tau = am1 * mx - 1.0f;
+  for (int it = 0; it < 64; ++it) {
+    double F = 0.0, dF = 0.0;
+    for (int p = threadIdx.x; p < P; p += 256) {
+      const float n = (float)min(c.S, L - p * c.S);
+      float E, dE;
+      gauss_moment(am1 * mr[p] - tau, am1 * sr[p], sparsemax, E, dE);
+      F += (double)(n * E);
+      dF += (double)(n * dE);
+    }
+    F = block_sum<256>(F, red) - 1.0;
+    dF = block_sum<256>(dF, red);
+    if (!(F > 0.0) || !(dF < 0.0)) break;
+    const double step = -F / dF;
+    tau = (float)((double)tau + step);
+    if (step <= 0x1p-22 * fmax(1.0, fabs((double)tau))) break;
+  }
+  if (threadIdx.x == 0) tau_out[bh] = tau;
+}
+
+// Keep page p of unit (b, g) iff some head h of g has (alpha-1) shat_h(p) > tau_h - delta;
+// ordered compaction.
+__global__ __launch_bounds__(256) void select_thresh_kernel(CacheView c, const float *__restrict__ shat,
+                                                            const float *__restrict__ tau, float alpha, float delta,
+                                                            int32_t *__restrict__ sel_idx,
+                                                            int32_t *__restrict__ sel_count, int cap) {
+  __shared__ int scan_scratch[256 / kWave + 1];
+  const int unit = blockIdx.x, b = unit / c.Hkv, g = unit - b * c.Hkv;
+  const int P = num_pages(c, seq_len(c, b));
+  const float am1 = alpha - 1.0f;
+  int32_t *out = sel_idx + (size_t)unit * cap;
+  int base = 0;
+  for (int p0 = 0; p0 < P; p0 += 256) {
+    const int p = p0 + threadIdx.x;
+    int keep = 0;
+    if (p < P)
+      for (int h = 0; h < c.G; ++h) {
+        const int bh = b * c.Hq + g * c.G + h;
+        if (am1 * shat[(size_t)bh * c.maxP + p] > tau[bh] - delta) keep = 1;
+      }
+    int tot;
+    const int pos = block_excl_scan<256>(keep, scan_scratch, &tot);
+    if (keep) out[base + pos] = p;
+    base += tot;
+  }
+  if (threadIdx.x == 0) sel_count[unit] = base;
+}
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_select_topk(const CacheView &c, const float *key, int key_stride, int policy, int k, int pct,
+                              int32_t *sel_idx, int32_t *sel_count, int cap, hipStream_t st) {
+  select_topk_kernel<<<c.B * c.Hkv, kSelThreads, 0, st>>>(c, key, key_stride, policy, k, pct, sel_idx, sel_count, cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_all(const CacheView &c, int tokens, int32_t *sel_idx, int32_t *sel_count, int cap,
+                             hipStream_t st) {
+  const int n = tokens ? c.maxP * c.S : c.maxP;
+  select_all_kernel<<<dim3((n + 255) / 256, c.B * c.Hkv), 256, 0, st>>>(c, tokens, sel_idx, sel_count, cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_thresh(const CacheView &c, const float *m, const float *s, const float *shat, float alpha,
+                                float delta, float *tau, int32_t *sel_idx, int32_t *sel_count, int cap, hipStream_t st) {
+  tau_hat_kernel<<<c.B * c.Hq, 256, 0, st>>>(c, m, s, alpha, tau);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  select_thresh_kernel<<<c.B * c.Hkv, 256, 0, st>>>(c, shat, tau, alpha, delta, sel_idx, sel_count, cap);
+  return hipGetLastError();
+}
+
+}  // namespace skv

@@ -1,0 +1,165 @@
+"""Runs one decode step of a workload through libskv (GPU) and the same step through the float64
+oracle (CPU, raw inputs only) and compares them. Used by the GPU parity tests."""
+from __future__ import annotations
+
+import math
+import sys
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+import oracle
+from oracle import pipeline
+import sparse_kv_cache_build_amd as skv
+import workloads as W
+
+# Output tolerance (bf16 inputs, fp32 accumulation): |gpu - ref| <= ATOL + RTOL |ref|
+RTOL, ATOL = 2e-3, 1e-3
+# tau_hat: the GPU solves in float32 from float32 (m, s); decisions closer than this to the
+# threshold may go either way (certified near-ties)
+TAU_TOL = 1e-4
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def spec_of(w: W.Workload, alphas=None) -> pipeline.Spec:
+    cfg = w.cfg
+    return pipeline.Spec(score=cfg["score"], policy=cfg["policy"], k=cfg.get("k", 0), pct=cfg.get("pct", 0),
+                         sel_alpha=cfg.get("sel_alpha", 1.5), delta=cfg.get("delta", 0.0),
+                         alphas=tuple(alphas or cfg["alphas"]),
+                         proj=w.proj.cpu().numpy() if w.proj is not None else None)
+
+
+@dataclass
+class GpuStep:
+    cache: skv.PagedCache
+    meta: skv.PageMeta
+    scores: skv.ScoreBuffers
+    sel: skv.Selection
+    outs: dict = field(default_factory=dict)
+
+
+def gpu_step(w: W.Workload, alphas=None, split=0, policy=None, cap=None) -> GpuStep:
+    cfg = w.cfg
+    cache = skv.PagedCache(w.k, w.v, w.block_table, w.seq_lens, w.Hq)
+    kind = cfg["score"]
+    meta = skv.build_page_meta(cache, (kind,), proj=w.proj)
+    scores = skv.score_pages(cache, meta, w.q, kind)
+    pol = policy or cfg["policy"]
+    sel = skv.select_pages(cache, scores, pol, k=cfg.get("k", 0), budget_pct=cfg.get("pct", 0),
+                           alpha=cfg.get("sel_alpha", 1.5), delta=cfg.get("delta", 0.0),
+                           tokens=1 if kind == "proj" else 0, cap=cap)
+    st = GpuStep(cache, meta, scores, sel)
+    for a in (alphas or cfg["alphas"]):
+        st.outs[a] = skv.sparse_decode_attn(cache, w.q, sel, alpha=a, split=split).clone()
+    torch.cuda.synchronize()
+    return st
+
+
+def oracle_cache(h) -> oracle.Cache:
+    return oracle.Cache(q=h["q"], k=h["k"], v=h["v"], block_table=h["block_table"], seq_lens=h["seq_lens"])
+
+
+def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+@dataclass
+class Report:
+    units: int = 0
+    near_ties: int = 0
+    max_err: float = 0.0
+    notes: list = field(default_factory=list)
+
+
+def compare(w: W.Workload, st: GpuStep, seqs=None, alphas=None, check_meta=True) -> Report:
+    """Oracle on sequences `seqs` (all if None) from raw inputs; asserts parity. Returns a report."""
+    seqs = list(range(w.B)) if seqs is None else list(seqs)
+    h = W.host_arrays(w, None if seqs == list(range(w.B)) else seqs)
+    c = oracle_cache(h)
+    spec = spec_of(w, alphas)
+    md = pipeline.build_metadata(c, spec)
+    sc = pipeline.compute_scores(c, spec, md)
+    rep = Report()
+    pm = h["phys_map"]
+    G = w.G
+    if check_meta:
+        _compare_meta(w, st, c, md, pm, spec)
+    idx = st.sel.idx.cpu().numpy()
+    cnt = st.sel.count.cpu().numpy()
+    outs = {a: o.cpu().numpy() for a, o in st.outs.items()}
+    gkey = st.scores.key.cpu().numpy() if st.scores.key is not None else None
+    for i, b in enumerate(seqs):
+        for g in range(w.Hkv):
+            rep.units += 1
+            if gkey is not None:
+                n = c.maxP if spec.score == "box" else c.maxP * c.S
+                ok = np.array_equal(gkey[b, g, :n], sc.key[i, g, :n])
+                if not ok:
+                    bad = np.nonzero(gkey[b, g, :n] != sc.key[i, g, :n])[0]
+                    raise AssertionError(f"key mismatch unit ({b},{g}) at {bad[:8]}: gpu {gkey[b, g, bad[:4]]} "
+                                         f"oracle {sc.key[i, g, bad[:4]]}")
+            r = pipeline.select_unit(c, spec, sc, i, g)
+            got = idx[b, g, :cnt[b, g]]
+            same = len(got) == len(r.sel) and np.array_equal(got, r.sel)
+            if spec.policy == "thresh":
+                tau_g = st.sel.tau_hat[b, g * G:(g + 1) * G].cpu().numpy().astype(np.float64)
+                if np.all(np.isnan(r.tau_hat)):          # empty sequence: no threshold
+                    assert np.all(np.isnan(tau_g)) and len(got) == 0, (b, g, tau_g, got)
+                    continue
+                assert np.all(np.abs(tau_g - r.tau_hat) <= TAU_TOL * np.maximum(1.0, np.abs(r.tau_hat))), \
+                    (b, g, tau_g, r.tau_hat)
+                if not same:
+                    diff = np.setxor1d(got, r.sel)
+                    shat = sc.shat[i, g * G:(g + 1) * G, :]
+                    margin = np.max((spec.sel_alpha - 1.0) * shat[:, diff] - (r.tau_hat[:, None] - spec.delta), axis=0)
+                    assert np.all(np.abs(margin) <= TAU_TOL * max(1.0, np.abs(r.tau_hat).max())), (b, g, diff, margin)
+                    rep.near_ties += len(diff)
+            else:
+                assert same, f"selection mismatch unit ({b},{g}): gpu {got[:10]}.. ({len(got)}) oracle " \
+                             f"{r.sel[:10]}.. ({len(r.sel)})"
+            if not same:
+                continue
+            for a in spec.alphas:
+                ref = pipeline.attend_unit(c, spec, i, g, r.sel, a)
+                gpu = outs[a][b, g * G:(g + 1) * G]
+                err = np.abs(gpu - ref)
+                rep.max_err = max(rep.max_err, float((err / (ATOL + RTOL * np.abs(ref))).max()))
+                assert np.all(err <= ATOL + RTOL * np.abs(ref)), \
+                    f"output mismatch unit ({b},{g}) alpha {a}: max abs err {err.max():.3g}"
+    return rep
+
+
+def _compare_meta(w, st, c, md, pm, spec):
+    """Metadata of every page the sampled sequences use: box and kproj bit-exact; Gaussian mean and
+    variance equal the float32 rounding of the float64 values."""
+    used = set()
+    for i in range(c.B):
+        used.update(int(x) for x in c.block_table[i, :c.pages(i)])
+    used = np.array(sorted(used), dtype=np.int64)
+    if len(used) == 0:
+        return
+    gp = torch.from_numpy(pm[used]).to(w.k.device)
+    if spec.score == "box":
+        box = bf16_to_f64(st.meta.box[gp])          # [n, Hkv, 2, d]
+        assert np.array_equal(box[:, :, 0], md.kmin[used]), "kmin mismatch"
+        assert np.array_equal(box[:, :, 1], md.kmax[used]), "kmax mismatch"
+    elif spec.score == "gauss":
+        ga = st.meta.gauss[gp].cpu().numpy()
+        assert np.array_equal(ga[:, :, 0], md.mean[used].astype(np.float32)), "mean mismatch"
+        assert np.array_equal(ga[:, :, 1], md.var[used].astype(np.float32)), "var mismatch"
+    elif spec.score == "proj":
+        kp = st.meta.kproj[gp].cpu().numpy().view(np.uint16)
+        owner = {}
+        for i in range(c.B):
+            for p in range(c.pages(i)):
+                owner[int(c.block_table[i, p])] = c.page_tokens(i, p)
+        for n, pg in enumerate(used):
+            nt = owner[int(pg)]          # only rows of valid tokens are defined
+            assert np.array_equal(kp[n, :, :nt], md.kproj[pg, :, :nt]), f"kproj mismatch page {pg}"

@@ -1,0 +1,152 @@
+"""The C ABI loads and exports every symbol include/skv.h declares; host-side validation
+rejects bad arguments with the documented status before anything touches the GPU.
+No compute call runs here (no GPU needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+
+from sparse_kv_cache_build_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "skv.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libskv.so is not built (run __graft_entry__.build())")
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(skv_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    assert [B.status_str(i) for i in range(6)] == [
+        "SKV_OK", "SKV_ERR_INVALID_ARG", "SKV_ERR_UNSUPPORTED", "SKV_ERR_CAPACITY", "SKV_ERR_WORKSPACE",
+        "SKV_ERR_HIP"]
+    assert B.status_str(99) == "SKV_ERR_UNKNOWN"
+
+
+FAKE = 0x10000   # aligned non-null "device" address: validation never dereferences it
+
+
+def cache(**kw):
+    d = dict(batch=2, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, max_pages=64,
+             num_phys_pages=128, dtype=1, k=FAKE, v=FAKE, block_table=FAKE, seq_lens=FAKE)
+    d.update(kw)
+    return B.Cache(**d)
+
+
+def ws_attn(L, c, **kw):
+    p = B.AttnParams(kw.get("alpha", 1.0), kw.get("sm_scale", 0.088), kw.get("granularity", 0), kw.get("split", 0))
+    n = C.c_size_t(0)
+    st = L.skv_workspace_bytes(C.byref(c), B.OP_ATTN, C.byref(p), kw.get("cap", 64), C.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(), B.SKV_OK),
+    (dict(num_q_heads=30), B.SKV_ERR_INVALID_ARG),          # Hq not a multiple of Hkv
+    (dict(num_q_heads=24), B.SKV_ERR_UNSUPPORTED),          # G = 3
+    (dict(num_q_heads=128), B.SKV_ERR_UNSUPPORTED),         # G = 16
+    (dict(head_dim=96), B.SKV_ERR_UNSUPPORTED),
+    (dict(page_size=0), B.SKV_ERR_INVALID_ARG),
+    (dict(page_size=2048), B.SKV_ERR_UNSUPPORTED),
+    (dict(dtype=7), B.SKV_ERR_INVALID_ARG),
+    (dict(k=0), B.SKV_ERR_INVALID_ARG),
+    (dict(v=FAKE + 2), B.SKV_ERR_INVALID_ARG),              # misaligned
+    (dict(batch=0), B.SKV_ERR_INVALID_ARG),
+    (dict(max_pages=1 << 22, page_size=1024), B.SKV_ERR_UNSUPPORTED),  # max_pages * S > int32
+])
+def test_cache_validation(L, over, status):
+    st, _ = ws_attn(L, cache(**over))
+    assert st == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(alpha=0.5), B.SKV_ERR_INVALID_ARG),
+    (dict(alpha=2.5), B.SKV_ERR_INVALID_ARG),
+    (dict(alpha=float("nan")), B.SKV_ERR_INVALID_ARG),
+    (dict(sm_scale=0.0), B.SKV_ERR_INVALID_ARG),
+    (dict(granularity=2), B.SKV_ERR_INVALID_ARG),
+    (dict(split=-1), B.SKV_ERR_INVALID_ARG),
+    (dict(cap=0), B.SKV_ERR_INVALID_ARG),
+    (dict(alpha=1.5), B.SKV_OK),
+    (dict(alpha=1.25, granularity=1, cap=2048), B.SKV_OK),
+])
+def test_attn_param_validation(L, kw, status):
+    st, n = ws_attn(L, cache(), **kw)
+    assert st == status
+    if st == B.SKV_OK:
+        assert n % 256 == 0
+
+
+def test_workspace_sizes_follow_plan(L):
+    c = cache()
+    st, n_soft = ws_attn(L, c, alpha=1.0, split=8, cap=64)       # 8 splits: partials [U, 8, G, d + 2]
+    assert st == 0 and n_soft == -(-(4 * 16 * 8 * 4 * 130) // 256) * 256
+    st, n_one = ws_attn(L, c, alpha=1.0, split=64, cap=64)       # one split: no partials
+    assert st == 0 and n_one == 0
+    st, n_ent = ws_attn(L, c, alpha=2.0, split=4, cap=64)        # 16 splits of 4 pages x 16 rows
+    cand = 8 * 16 * 4 * 16 * 64
+    assert st == 0 and n_ent >= cand
+
+
+def test_select_capacity_and_policy_checks(L):
+    c = cache()
+    sc = B.Scores(FAKE, FAKE, FAKE, FAKE)
+
+    def sel(policy, cap, **kw):
+        p = B.SelectParams(policy, kw.get("k", 0), kw.get("pct", 0), kw.get("alpha", 1.5), kw.get("delta", 0.5),
+                           kw.get("tokens", 0))
+        return L.skv_select_pages(C.byref(c), C.byref(sc), C.byref(p), C.c_void_p(FAKE), C.c_void_p(FAKE), cap,
+                                  C.c_void_p(FAKE), None, 0, None)
+
+    assert sel(B.SEL_TOPK, 63, k=64) == B.SKV_ERR_CAPACITY
+    assert sel(B.SEL_TOPK, 64, k=0) == B.SKV_ERR_INVALID_ARG
+    assert sel(B.SEL_TOKEN_TOPK, 100, k=2048) == B.SKV_ERR_CAPACITY
+    assert sel(B.SEL_BUDGET, 3, pct=5) == B.SKV_ERR_CAPACITY        # ceil(5% of 64) = 4
+    assert sel(B.SEL_BUDGET, 4, pct=0) == B.SKV_ERR_INVALID_ARG
+    assert sel(B.SEL_THRESH_GAUSS, 63, alpha=1.5) == B.SKV_ERR_CAPACITY
+    assert sel(B.SEL_THRESH_GAUSS, 64, alpha=1.25) == B.SKV_ERR_UNSUPPORTED
+    assert sel(B.SEL_THRESH_GAUSS, 64, alpha=3.0) == B.SKV_ERR_INVALID_ARG
+    assert sel(B.SEL_THRESH_GAUSS, 64, alpha=1.5, delta=-1.0) == B.SKV_ERR_INVALID_ARG
+    assert sel(B.SEL_ALL, 64 * 16 - 1, tokens=1) == B.SKV_ERR_CAPACITY
+    assert sel(9, 64) == B.SKV_ERR_INVALID_ARG
+
+
+def test_score_and_meta_validation(L):
+    c = cache()
+    m = B.Meta(B.META_BOX, FAKE, None, 0, None, None)
+    out = B.Scores(FAKE, None, None, None)
+    st = L.skv_score_pages(C.byref(c), C.byref(m), C.c_void_p(FAKE), B.SCORE_BOX, 0.1, C.byref(out), None, 0, None)
+    assert st == B.SKV_ERR_WORKSPACE
+    st = L.skv_score_pages(C.byref(c), C.byref(m), C.c_void_p(FAKE), B.SCORE_GAUSS, 0.1, C.byref(out),
+                           C.c_void_p(FAKE), 1 << 20, None)
+    assert st == B.SKV_ERR_INVALID_ARG                              # gauss metadata not present
+    mp = B.Meta(B.META_PROJ, None, None, 24, FAKE, FAKE)
+    assert L.skv_build_page_meta(C.byref(c), C.byref(mp), None) == B.SKV_ERR_UNSUPPORTED   # rank 24
+    assert L.skv_build_page_meta(C.byref(c), C.byref(B.Meta(0, None, None, 0, None, None)), None) == \
+        B.SKV_ERR_INVALID_ARG
+    assert L.skv_build_page_meta(C.byref(c), C.byref(B.Meta(B.META_GAUSS, None, None, 0, None, None)), None) == \
+        B.SKV_ERR_INVALID_ARG
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        B.lib()

@@ -1,0 +1,118 @@
+"""GPU parity: libskv (HIP, through the C ABI) against the float64 oracle on the same seeded inputs.
+
+Indices (selected pages / tokens) and box / projected keys and metadata must be bit-exact;
+outputs within 2e-3 relative / 1e-3 absolute; the Gaussian threshold within 1e-4 relative,
+with decisions that close to the threshold counted as certified near-ties.
+Small cases cover every unit and span several tiles with ragged tails; full-size cases run the
+launch configuration the benchmark times and check sampled sequences."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as H
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny": dict(),
+    "gqa32k": dict(B=2, L=3000),
+    "long_gauss": dict(B=2, L=6000),
+    "token128k": dict(B=2, L=5000, k=512),
+    "ragged": dict(B=5, lens=[0, 100, 4500, 20000, 12345]),
+}
+
+FULL_SAMPLE = {"tiny": None, "gqa32k": [0, 5], "long_gauss": [1], "token128k": [3], "ragged": "ends"}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_parity(dev, name):
+    H.log(f"[parity small] {name} {SMALL[name]}")
+    w = W.make(name, device=dev, **SMALL[name])
+    st = H.gpu_step(w)
+    rep = H.compare(w, st)
+    H.log(f"  units={rep.units} near_ties={rep.near_ties} max_err/tol={rep.max_err:.3f}")
+
+
+@pytest.mark.parametrize("name,split", [("gqa32k", 1), ("gqa32k", 3), ("token128k", 7), ("ragged", 1),
+                                        ("ragged", 2), ("tiny", 5), ("long_gauss", 1)])
+def test_explicit_splits_match_oracle(dev, name, split):
+    H.log(f"[parity split] {name} split={split}")
+    w = W.make(name, device=dev, **SMALL[name])
+    st = H.gpu_step(w, split=split)
+    H.compare(w, st, check_meta=False)
+
+
+@pytest.mark.parametrize("name,alphas", [("gqa32k", (1.0, 1.5, 2.0, 1.25)), ("tiny", (1.0, 1.5, 2.0)),
+                                         ("ragged", (1.0, 2.0)), ("token128k", (1.0, 1.5))])
+def test_alphas_over_selection(dev, name, alphas):
+    H.log(f"[parity alphas] {name} {alphas}")
+    w = W.make(name, device=dev, **SMALL[name])
+    st = H.gpu_step(w, alphas=alphas)
+    H.compare(w, st, alphas=alphas, check_meta=False)
+
+
+@pytest.mark.parametrize("name", ["gqa32k", "ragged", "token128k"])
+@pytest.mark.parametrize("alpha", [1.0, 1.5, 2.0])
+def test_full_cache_comparator(dev, name, alpha):
+    """policy 'all' = full-cache decode with the same kernels (the pages' comparator)."""
+    H.log(f"[parity full-cache] {name} alpha={alpha}")
+    w = W.make(name, device=dev, **SMALL[name])
+    w.cfg = dict(w.cfg, policy="all")
+    st = H.gpu_step(w, alphas=(alpha,))
+    H.compare(w, st, alphas=(alpha,), check_meta=False)
+
+
+def test_k_at_least_pages_and_tokens_selects_all(dev):
+    H.log("[edge] k >= P_b, k >= L_b")
+    w = W.make("gqa32k", device=dev, B=2, lens=[700, 33], k=400)
+    st = H.gpu_step(w)
+    cnt = st.sel.count.cpu().numpy()
+    assert np.array_equal(cnt, np.array([[44] * 8, [3] * 8]))
+    H.compare(w, st)
+    w2 = W.make("token128k", device=dev, B=2, lens=[600, 1500], k=1000)
+    st2 = H.gpu_step(w2)
+    assert np.array_equal(st2.sel.count.cpu().numpy(), np.array([[600] * 8, [1000] * 8]))
+    H.compare(w2, st2)
+
+
+def test_empty_sequence_gives_zero_output_and_no_selection(dev):
+    H.log("[edge] empty sequences")
+    for name in ("gqa32k", "long_gauss", "token128k", "ragged"):
+        w = W.make(name, device=dev, B=2, lens=[0, 37 if name != "ragged" else 130])
+        st = H.gpu_step(w)
+        assert np.all(st.sel.count.cpu().numpy()[0] == 0), name
+        for o in st.outs.values():
+            assert torch.all(o[0] == 0).item(), name
+        H.compare(w, st)
+
+
+def test_determinism(dev):
+    H.log("[determinism] gqa32k, ragged")
+    for name in ("gqa32k", "ragged", "long_gauss"):
+        w = W.make(name, device=dev, **SMALL[name])
+        a, b = H.gpu_step(w), H.gpu_step(w)
+        assert torch.equal(a.sel.idx, b.sel.idx) and torch.equal(a.sel.count, b.sel.count)
+        for al in a.outs:
+            assert torch.equal(a.outs[al], b.outs[al]), (name, al)
+
+
+@pytest.mark.parametrize("name", list(FULL_SAMPLE))
+def test_full_size_sampled(dev, name):
+    H.log(f"[parity full size] {name}")
+    w = W.make(name, device=dev)
+    st = H.gpu_step(w)
+    seqs = FULL_SAMPLE[name]
+    if seqs == "ends":
+        order = np.argsort(w.lens)
+        seqs = [int(order[0]), int(order[-1])]
+    rep = H.compare(w, st, seqs=seqs)
+    H.log(f"  sampled seqs={seqs} units={rep.units} near_ties={rep.near_ties} max_err/tol={rep.max_err:.3f}")
+    del st, w
+    torch.cuda.empty_cache()
