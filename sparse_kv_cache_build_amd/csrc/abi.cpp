@@ -75,7 +75,7 @@ skv_status attn_plan(const skv_cache *c, const skv_attn_params *p, int cap, Attn
   const int rmax = entmax ? 512 : 1024;   // rows per partition
   int64_t spi = p->split;
   if (spi <= 0) {
-    spi = ((int64_t)cap * U + 2047) / 2048;   // about 2048 partitions in total
+    spi = ((int64_t)cap * U + 1023) / 1024;   // about 1024 partitions in total
     spi = std::max<int64_t>(1, std::min<int64_t>(spi, std::max(1, rmax / rows_per_item)));
   }
   spi = std::min<int64_t>(spi, cap);
@@ -193,7 +193,7 @@ skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q,
   } else if (kind == SKV_SCORE_PROJ) {
     if (!(m->kinds & SKV_META_PROJ) || !m->kproj || !m->proj || !out->key) return SKV_ERR_INVALID_ARG;
     if (!rank_ok(m->proj_rank)) return SKV_ERR_UNSUPPORTED;
-    if (!aligned(m->kproj, 16)) return SKV_ERR_INVALID_ARG;
+    if (!aligned(m->kproj, 16) || !aligned(m->proj, 16)) return SKV_ERR_INVALID_ARG;
   } else {
     return SKV_ERR_INVALID_ARG;
   }

@@ -95,13 +95,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_softmax_kernel(
     for (int j = 0; j < 8; ++j) acc[h][j] = 0.0f;
   }
   const T *K = static_cast<const T *>(c.k), *V = static_cast<const T *>(c.v);
-  for (int r = rg; r < NR; r += RL::RGB) {
-    const int item = it0 + r / rows_per_item;
-    const long long off = rm.row_offset(item, r - (r / rows_per_item) * rows_per_item);
-    if (off < 0) continue;
-    float kx[8], vx[8];
-    Elem<T>::load8(K + off + lr * 8, kx);
-    Elem<T>::load8(V + off + lr * 8, vx);
+  auto row_off = [&](int r) -> long long {
+    if (r >= NR) return -1;
+    const int it = r / rows_per_item;
+    return rm.row_offset(it0 + it, r - it * rows_per_item);
+  };
+  auto accumulate = [&](const float (&kx)[8], const float (&vx)[8]) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float part_dot = 0.0f;
@@ -120,6 +119,21 @@ __global__ __launch_bounds__(kAttnThreads) void attn_softmax_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(p, vx[j], acc[h][j]);
     }
+  };
+  // two rows per lane group per step: both rows' loads are in flight before either is used
+  for (int r = rg; r < NR; r += 2 * RL::RGB) {
+    const long long o1 = row_off(r), o2 = row_off(r + RL::RGB);
+    float k1[8], v1[8], k2[8], v2[8];
+    if (o1 >= 0) {
+      Elem<T>::load8(K + o1 + lr * 8, k1);
+      Elem<T>::load8(V + o1 + lr * 8, v1);
+    }
+    if (o2 >= 0) {
+      Elem<T>::load8(K + o2 + lr * 8, k2);
+      Elem<T>::load8(V + o2 + lr * 8, v2);
+    }
+    if (o1 >= 0) accumulate(k1, v1);
+    if (o2 >= 0) accumulate(k2, v2);
   }
   // merge the lane groups: common reference per head, then sums
   if (lr == 0)
@@ -171,29 +185,47 @@ __global__ __launch_bounds__(kAttnThreads) void attn_softmax_kernel(
   }
 }
 
-// Fixed-order log-sum-exp combine of the non-empty splits of each query head.
+// Fixed-order log-sum-exp combine of the non-empty splits of each query head. The per-split
+// (max, sum) pairs go through LDS first so that the accumulator loads are independent.
+constexpr int kCombineMax = 1024;   // splits merged per LDS round
 template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(CacheView c, const int32_t *__restrict__ sel_count, int cap,
                                                         int spi, int nsplit, const float *__restrict__ part,
                                                         float *__restrict__ out) {
+  __shared__ float s_w[kCombineMax];
+  __shared__ float s_l[kCombineMax];
+  __shared__ float red[D / kWave];
   const int bh = blockIdx.x, b = bh / c.Hq, h = bh - b * c.Hq, g = h / c.G, hh = h - g * c.G;
   const int unit = b * c.Hkv + g;
   const int count = min(max(sel_count[unit], 0), cap);
   const int ns = min(nsplit, (count + spi - 1) / spi);
   const int j = threadIdx.x;
+  const size_t stride = (size_t)c.G * (D + 2);
+  const float *p0 = part + ((size_t)unit * nsplit * c.G + hh) * (D + 2);
+  // global max over the non-empty splits
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) {
-    const float *pp = part + (((size_t)unit * nsplit + s) * c.G + hh) * (D + 2);
+  for (int s = j; s < ns; s += D) {
+    const float *pp = p0 + s * stride;
     if (pp[1] > 0.0f) M = fmaxf(M, pp[0]);
   }
+  M = block_max<D>(M, red);
   float lsum = 0.0f, a = 0.0f;
-  for (int s = 0; s < ns; ++s) {
-    const float *pp = part + (((size_t)unit * nsplit + s) * c.G + hh) * (D + 2);
-    if (pp[1] > 0.0f) {
-      const float f = exp2f(pp[0] - M);
-      lsum += pp[1] * f;
-      a += pp[2 + j] * f;
+  for (int s0 = 0; s0 < ns; s0 += kCombineMax) {
+    const int n = min(kCombineMax, ns - s0);
+    for (int s = j; s < n; s += D) {
+      const float *pp = p0 + (s0 + s) * stride;
+      const float l = pp[1];
+      s_w[s] = l > 0.0f ? exp2f(pp[0] - M) : 0.0f;
+      s_l[s] = l;
     }
+    __syncthreads();
+#pragma unroll 8
+    for (int s = 0; s < n; ++s) {
+      const float w = s_w[s];
+      lsum += s_l[s] * w;
+      a += (w > 0.0f ? p0[(s0 + s) * stride + 2 + j] : 0.0f) * w;
+    }
+    __syncthreads();
   }
   out[(size_t)bh * D + j] = lsum > 0.0f ? a / lsum : 0.0f;
 }
@@ -228,11 +260,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
     for (int j = 0; j < 8; ++j) qv[h][j] *= zscale;
   }
   const T *K = static_cast<const T *>(c.k);
-  for (int r = rg; r < NR; r += RL::RGB) {
-    const int item = it0 + r / rows_per_item;
-    const long long off = rm.row_offset(item, r - (r / rows_per_item) * rows_per_item);
-    float kx[8];
-    if (off >= 0) Elem<T>::load8(K + off + lr * 8, kx);
+  auto row_off = [&](int r) -> long long {
+    if (r >= NR) return -1;
+    const int it = r / rows_per_item;
+    return rm.row_offset(it0 + it, r - it * rows_per_item);
+  };
+  auto logits = [&](int r, long long off, const float (&kx)[8]) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float part_dot = 0.0f;
@@ -243,6 +276,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
       }
       if (lr == h % RL::LPR) zs[h * rps + r] = off >= 0 ? part_dot : -INFINITY;
     }
+  };
+  for (int r = rg; r < NR; r += 2 * RL::RGB) {
+    const int r2 = r + RL::RGB;
+    const long long o1 = row_off(r), o2 = row_off(r2);
+    float k1[8], k2[8];
+    if (o1 >= 0) Elem<T>::load8(K + o1 + lr * 8, k1);
+    if (o2 >= 0) Elem<T>::load8(K + o2 + lr * 8, k2);
+    logits(r, o1, k1);
+    if (r2 < NR) logits(r2, o2, k2);
   }
   __syncthreads();
   for (int h = 0; h < G; ++h) {

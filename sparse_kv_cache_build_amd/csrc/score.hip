@@ -24,17 +24,25 @@ __global__ void qprep_pair_kernel(const T *__restrict__ q, int n, int gauss, dou
 }
 
 // PROJ: q~_h[i] = RN_f32(sum_j P[i][j] q_hj) (float64 sum, j ascending), stored as float64 values.
-// Layout [B, Hq, r].
-template <typename T>
-__global__ void qprep_proj_kernel(const T *__restrict__ q, int BH, int D, int r, const float *__restrict__ proj,
-                                  double *__restrict__ out) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= BH * r) return;
-  const int bh = idx / r, i = idx - bh * r;
+// One block per query head, thread i owns row i of P: its row is read with independent 16-byte
+// loads while q_h is read with uniform (scalar) loads. Layout [B, Hq, r].
+template <typename T, int D>
+__global__ __launch_bounds__(64) void qprep_proj_kernel(const T *__restrict__ q, int r,
+                                                        const float *__restrict__ proj, double *__restrict__ out) {
+  const int bh = blockIdx.x, i = threadIdx.x;
+  if (i >= r) return;
   const T *qh = q + (size_t)bh * D;
+  const float4 *pr = reinterpret_cast<const float4 *>(proj + (size_t)i * D);
   double acc = 0.0;
-  for (int j = 0; j < D; ++j) acc = fma((double)proj[(size_t)i * D + j], (double)Elem<T>::get(qh, j), acc);
-  out[idx] = (double)(float)acc;
+#pragma unroll
+  for (int j0 = 0; j0 < D; j0 += 4) {
+    const float4 pv = pr[j0 / 4];
+    acc = fma((double)pv.x, (double)Elem<T>::get(qh, j0), acc);
+    acc = fma((double)pv.y, (double)Elem<T>::get(qh, j0 + 1), acc);
+    acc = fma((double)pv.z, (double)Elem<T>::get(qh, j0 + 2), acc);
+    acc = fma((double)pv.w, (double)Elem<T>::get(qh, j0 + 3), acc);
+  }
+  out[(size_t)bh * r + i] = (double)(float)acc;
 }
 
 // BOX key: one lane per page. key[b][g][p] = RN_f32(max_h sum_j (q+_hj kmax_j + q-_hj kmin_j)).
@@ -227,11 +235,17 @@ static hipError_t proj_r(const CacheView &c, const uint16_t *kproj, const double
 hipError_t launch_score_proj(const CacheView &c, int dtype, const void *q, int r, const float *proj,
                              const uint16_t *kproj, float *key, double *ws, hipStream_t st) {
   const int BH = c.B * c.Hq;
-  if (dtype == 0)
-    qprep_proj_kernel<float><<<(BH * r + 255) / 256, 256, 0, st>>>(static_cast<const float *>(q), BH, c.D, r, proj, ws);
-  else
-    qprep_proj_kernel<uint16_t><<<(BH * r + 255) / 256, 256, 0, st>>>(static_cast<const uint16_t *>(q), BH, c.D, r,
-                                                                        proj, ws);
+  if (dtype == 0) {
+    if (c.D == 64)
+      qprep_proj_kernel<float, 64><<<BH, 64, 0, st>>>(static_cast<const float *>(q), r, proj, ws);
+    else
+      qprep_proj_kernel<float, 128><<<BH, 64, 0, st>>>(static_cast<const float *>(q), r, proj, ws);
+  } else {
+    if (c.D == 64)
+      qprep_proj_kernel<uint16_t, 64><<<BH, 64, 0, st>>>(static_cast<const uint16_t *>(q), r, proj, ws);
+    else
+      qprep_proj_kernel<uint16_t, 128><<<BH, 64, 0, st>>>(static_cast<const uint16_t *>(q), r, proj, ws);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (r) {

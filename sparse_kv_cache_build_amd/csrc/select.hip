@@ -7,7 +7,10 @@
 namespace skv {
 
 constexpr int kSelThreads = 512;
-constexpr int kSelLds = 16384;   // keys held in LDS when n <= kSelLds (64 KiB)
+constexpr int kSelLds = 16384;   // page keys held in LDS when n <= kSelLds (64 KiB)
+constexpr int kTokThreads = 1024;
+constexpr int kTokCand = 8192;   // token candidates held in LDS (key + index: 64 KiB)
+constexpr int kTokSample = 8192; // keys sampled to place the candidate threshold
 
 // Number of candidates and how many to keep for unit (b, g).
 struct SelSize {
@@ -32,18 +35,89 @@ __device__ __forceinline__ SelSize sel_size(const CacheView &c, int b, int polic
   return s;
 }
 
-// Radix selection of the k largest keys (order: key descending, index ascending), then an
-// ordered compaction. The float keys are mapped to order-preserving uint32; four 8-bit digits,
-// most significant first, find the exact k-th largest key T and how many keys equal to T are
-// needed (the lowest-indexed ones). Integer LDS atomics only, so the result is deterministic.
+// Radix selection over order keys get(i), i < n: finds the r-th largest key T (1 <= r <= n) and
+// need = r - #(keys > T), i.e. how many keys equal to T belong to the top r. Four 8-bit digits,
+// most significant first; histograms use integer LDS atomics (deterministic). `hist` holds 256
+// words, `bc` 2 words of shared memory. Every thread of the block must call it.
+template <int NT, typename Get>
+__device__ void radix_kth(Get get, int n, uint32_t r, uint32_t *hist, uint32_t *bc, uint32_t &T, uint32_t &need) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, mask = 0;
+  need = r;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+      const uint32_t u = get(i);
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 0xffu], 1u);
+    }
+    __syncthreads();
+    // the wanted digit v has count(> v) < need <= count(>= v); lane l owns digits 4l .. 4l+3
+    if (tid < kWave) {
+      uint32_t c4[4], local = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c4[i] = hist[4 * tid + i];
+        local += c4[i];
+      }
+      uint32_t incl = local;  // inclusive suffix sum over lanes (higher lanes: larger digits)
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t t = __shfl_down(incl, o, kWave);
+        if (tid + o < kWave) incl += t;
+      }
+      uint32_t above = incl - local;
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if (above < need && above + c4[i] >= need) {
+          bc[0] = prefix | ((uint32_t)(4 * tid + i) << shift);
+          bc[1] = need - above;
+        }
+        above += c4[i];
+      }
+    }
+    __syncthreads();
+    prefix = bc[0];
+    need = bc[1];
+    mask |= 0xffu << shift;
+    __syncthreads();
+  }
+  T = prefix;
+}
+
+// Ordered take over i in [0, n): keeps keys > T and the first `need` keys == T (lowest i), and
+// writes out[rank] = idx(i) in increasing i. Each thread walks a contiguous chunk; block scans
+// give the ranks. Every thread of the block must call it.
+template <int NT, typename Get, typename Idx>
+__device__ void ordered_take(Get get, Idx idx, int n, uint32_t T, uint32_t need, int32_t *out, int *scan_scratch) {
+  const int per = (n + NT - 1) / NT;
+  const int i0 = min(n, (int)threadIdx.x * per), i1 = min(n, i0 + per);
+  int ngt = 0, neq = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t u = get(i);
+    ngt += u > T;
+    neq += u == T;
+  }
+  int tot;
+  int gt_before = block_excl_scan<NT>(ngt, scan_scratch, &tot);
+  int eq_before = block_excl_scan<NT>(neq, scan_scratch, &tot);
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t u = get(i);
+    if (u > T || (u == T && (uint32_t)eq_before < need)) out[gt_before + min((uint32_t)eq_before, need)] = idx(i);
+    gt_before += u > T;
+    eq_before += u == T;
+  }
+}
+
+// Page top-k / budget: one block per unit; the unit's page keys sit in LDS when they fit.
 __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(CacheView c, const float *__restrict__ key,
                                                                   int key_stride, int policy, int k, int pct,
                                                                   int32_t *__restrict__ sel_idx,
                                                                   int32_t *__restrict__ sel_count, int cap) {
   __shared__ uint32_t skeys[kSelLds];
   __shared__ uint32_t hist[256];
+  __shared__ uint32_t bc[2];
   __shared__ int scan_scratch[kSelThreads / kWave + 1];
-  __shared__ uint32_t s_prefix, s_need;
   const int unit = blockIdx.x, b = unit / c.Hkv;
   const SelSize sz = sel_size(c, b, policy, k, pct);
   const float *kr = key + (size_t)unit * key_stride;
@@ -55,72 +129,119 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(CacheView c, c
     for (int i = tid; i < sz.n; i += kSelThreads) out[i] = i;
     return;
   }
-  const bool in_lds = sz.n <= kSelLds;
-  if (in_lds)
+  uint32_t T, need;
+  auto ident = [](int i) { return i; };
+  if (sz.n <= kSelLds) {
     for (int i = tid; i < sz.n; i += kSelThreads) skeys[i] = f32_order_key(kr[i]);
-  __syncthreads();
+    __syncthreads();
+    auto get = [&](int i) { return skeys[i]; };
+    radix_kth<kSelThreads>(get, sz.n, (uint32_t)sz.k, hist, bc, T, need);
+    ordered_take<kSelThreads>(get, ident, sz.n, T, need, out, scan_scratch);
+  } else {
+    auto get = [&](int i) { return f32_order_key(kr[i]); };
+    radix_kth<kSelThreads>(get, sz.n, (uint32_t)sz.k, hist, bc, T, need);
+    ordered_take<kSelThreads>(get, ident, sz.n, T, need, out, scan_scratch);
+  }
+}
 
-  uint32_t prefix = 0, mask = 0;
-  uint32_t need = (uint32_t)sz.k;  // keys still to take from those matching prefix
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < sz.n; i += kSelThreads) {
-      const uint32_t u = in_lds ? skeys[i] : f32_order_key(kr[i]);
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 0xffu], 1u);
+// Token top-k over long sequences: one block of 1024 threads per unit.
+//  1. Sample 8192 keys (64 evenly spaced runs of 128) and take the r-th largest sampled key,
+//     r = k * 8192 / n plus a 4-sigma margin, as the candidate bound T_lo.
+//  2. One pass over all keys keeps (key, index) with key >= T_lo in LDS, in index order.
+//  3. If at least k candidates were kept (and they fit), the top k all lie among them (the k-th
+//     largest key is >= T_lo, so every key that ties with it is a candidate too): select exactly
+//     in LDS. Otherwise fall back to the radix selection over all keys in global memory.
+__global__ __launch_bounds__(kTokThreads) void select_topk_large_kernel(CacheView c, const float *__restrict__ key,
+                                                                        int key_stride, int k,
+                                                                        int32_t *__restrict__ sel_idx,
+                                                                        int32_t *__restrict__ sel_count, int cap) {
+  __shared__ uint32_t ckey[kTokCand];
+  __shared__ int32_t cidx[kTokCand];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t bc[2];
+  __shared__ int scan_scratch[kTokThreads / kWave + 1];
+  const int unit = blockIdx.x, b = unit / c.Hkv;
+  const int n = seq_len(c, b);
+  const int kk = min(k, n);
+  const float *kr = key + (size_t)unit * key_stride;
+  int32_t *out = sel_idx + (size_t)unit * cap;
+  const int tid = threadIdx.x;
+  if (tid == 0) sel_count[unit] = kk;
+  if (kk <= 0) return;
+  if (kk >= n) {
+    for (int i = tid; i < n; i += kTokThreads) out[i] = i;
+    return;
+  }
+  uint32_t T, need;
+  auto lget = [&](int i) { return ckey[i]; };
+  auto lidx = [&](int i) { return cidx[i]; };
+  if (n <= kTokCand) {
+    for (int i = tid; i < n; i += kTokThreads) {
+      ckey[i] = f32_order_key(kr[i]);
+      cidx[i] = i;
     }
     __syncthreads();
-    // suffix counts: the wanted digit v has count(> v) < need <= count(>= v)
-    if (tid < kWave) {
-      uint32_t c4[4];
-      uint32_t local = 0;
+    radix_kth<kTokThreads>(lget, n, (uint32_t)kk, hist, bc, T, need);
+    ordered_take<kTokThreads>(lget, lidx, n, T, need, out, scan_scratch);
+    return;
+  }
+  // 1. sample
+  const int run = kTokSample / 64, stride = n / 64;
+  for (int s = tid; s < kTokSample; s += kTokThreads) ckey[s] = f32_order_key(kr[(s / run) * stride + s % run]);
+  __syncthreads();
+  const double expect = (double)kk * kTokSample / n;
+  const double rs = ceil(expect + 4.0 * sqrt(expect) + 16.0);
+  uint32_t Tlo = 0;
+  if (rs < kTokSample) {
+    radix_kth<kTokThreads>(lget, kTokSample, (uint32_t)rs, hist, bc, T, need);
+    Tlo = T;
+  }
+  __syncthreads();
+  // 2. filtered pass in index order, 4 consecutive keys per thread per tile
+  const bool vec = (key_stride & 3) == 0;
+  int base = 0;
+  bool overflow = false;
+  for (int t0 = 0; t0 < n; t0 += 4 * kTokThreads) {
+    const int i = t0 + 4 * tid;
+    uint32_t u[4];
+    if (vec && i + 3 < n) {
+      const float4 f = *reinterpret_cast<const float4 *>(kr + i);
+      u[0] = f32_order_key(f.x);
+      u[1] = f32_order_key(f.y);
+      u[2] = f32_order_key(f.z);
+      u[3] = f32_order_key(f.w);
+    } else {
 #pragma unroll
-      for (int i = 3; i >= 0; --i) {  // lane handles digits 4*lane .. 4*lane+3
-        c4[i] = hist[4 * tid + i];
-        local += c4[i];
-      }
-      // exclusive suffix sum over lanes (higher lanes hold larger digits)
-      uint32_t incl = local;
+      for (int j = 0; j < 4; ++j) u[j] = i + j < n ? f32_order_key(kr[i + j]) : 0u;
+    }
+    int cnt = 0;
 #pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        uint32_t t = __shfl_down(incl, o, kWave);
-        if (tid + o < kWave) incl += t;
-      }
-      uint32_t above = incl - local;  // keys with digit > 4*tid+3
+    for (int j = 0; j < 4; ++j) cnt += (i + j < n) && u[j] >= Tlo;
+    int tot;
+    int pos = base + block_excl_scan<kTokThreads>(cnt, scan_scratch, &tot);
+    if (base + tot > kTokCand) overflow = true;
+    if (!overflow) {
 #pragma unroll
-      for (int i = 3; i >= 0; --i) {
-        if (above < need && above + c4[i] >= need) {
-          s_prefix = prefix | ((uint32_t)(4 * tid + i) << shift);
-          s_need = need - above;
+      for (int j = 0; j < 4; ++j)
+        if ((i + j < n) && u[j] >= Tlo) {
+          ckey[pos] = u[j];
+          cidx[pos] = i + j;
+          ++pos;
         }
-        above += c4[i];
-      }
     }
-    __syncthreads();
-    prefix = s_prefix;
-    need = s_need;
-    mask |= 0xffu << shift;
-    __syncthreads();
+    base += tot;
   }
-  // prefix == T (the k-th largest key); take keys > T and the first `need` keys == T.
-  const int per = (sz.n + kSelThreads - 1) / kSelThreads;
-  const int i0 = min(sz.n, tid * per), i1 = min(sz.n, i0 + per);
-  int ngt = 0, neq = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t u = in_lds ? skeys[i] : f32_order_key(kr[i]);
-    ngt += u > prefix;
-    neq += u == prefix;
+  __syncthreads();
+  if (!overflow && base >= kk) {
+    radix_kth<kTokThreads>(lget, base, (uint32_t)kk, hist, bc, T, need);
+    ordered_take<kTokThreads>(lget, lidx, base, T, need, out, scan_scratch);
+    return;
   }
-  int tot;
-  int gt_before = block_excl_scan<kSelThreads>(ngt, scan_scratch, &tot);
-  int eq_before = block_excl_scan<kSelThreads>(neq, scan_scratch, &tot);
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t u = in_lds ? skeys[i] : f32_order_key(kr[i]);
-    const bool take = u > prefix || (u == prefix && (uint32_t)eq_before < need);
-    if (take) out[gt_before + min((uint32_t)eq_before, need)] = i;
-    gt_before += u > prefix;
-    eq_before += u == prefix;
-  }
+  // 3. fallback: exact radix selection over all keys in global memory
+  auto gget = [&](int i) { return f32_order_key(kr[i]); };
+  auto gidx = [](int i) { return i; };
+  radix_kth<kTokThreads>(gget, n, (uint32_t)kk, hist, bc, T, need);
+  ordered_take<kTokThreads>(gget, gidx, n, T, need, out, scan_scratch);
 }
 
 // Every page (or token) of the sequence.
@@ -234,7 +355,11 @@ __global__ __launch_bounds__(256) void select_thresh_kernel(CacheView c, const f
 
 hipError_t launch_select_topk(const CacheView &c, const float *key, int key_stride, int policy, int k, int pct,
                               int32_t *sel_idx, int32_t *sel_count, int cap, hipStream_t st) {
-  select_topk_kernel<<<c.B * c.Hkv, kSelThreads, 0, st>>>(c, key, key_stride, policy, k, pct, sel_idx, sel_count, cap);
+  if (policy == 3)
+    select_topk_large_kernel<<<c.B * c.Hkv, kTokThreads, 0, st>>>(c, key, key_stride, k, sel_idx, sel_count, cap);
+  else
+    select_topk_kernel<<<c.B * c.Hkv, kSelThreads, 0, st>>>(c, key, key_stride, policy, k, pct, sel_idx, sel_count,
+                                                            cap);
   return hipGetLastError();
 }
 
