@@ -66,6 +66,16 @@ class Step:
         self.score()
         self.rest()
 
+    def capture(self):
+        """Record the two stages as HIP graphs (no allocation happens inside run())."""
+        self.g_score, self.g_rest = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(self.g_score):
+            self.score()
+        with torch.cuda.graph(self.g_rest):
+            self.rest()
+        torch.cuda.synchronize()
+
 
 def step_bytes(st: Step):
     """Algorithmic bytes of one step: metadata read + K of the selected rows + V of the rows that
@@ -96,7 +106,9 @@ def step_bytes(st: Step):
                 pg = idx[b, g, :cnt[b, g]].astype(np.int64)
                 k_rows += int(np.minimum(S, lens[b] - pg * S).sum())
     kv_row = d * e
-    v_rows = k_rows   # softmax weights every selected row; entmax reads fewer (reported as an upper bound)
+    # softmax weights every selected row; entmax reads V only for its (small) support, which is not
+    # counted, so entmax figures are conservative
+    v_rows = k_rows if st.alpha == 1.0 else 0
     q_out = w.B * w.Hq * d * (e + 4)
     total = meta + k_rows * kv_row + v_rows * kv_row + q_out
     return total, meta + keys_out, dict(meta=meta, k_rows=k_rows, v_rows=v_rows, q_out=q_out, keys_out=keys_out)
@@ -160,6 +172,9 @@ def main():
     ap.add_argument("--split", type=int, default=0)
     ap.add_argument("--sets", type=int, default=0, help="buffer sets rotated per step (0: enough to exceed 2x MALL)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--graph", action="store_true", help="replay the stages as HIP graphs instead of launching them")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="after timing, copy a 1 GiB buffer 3 times (reference kernel for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the decode path has no multi-GPU mode "
@@ -181,10 +196,20 @@ def main():
         log(f"[bench] buffer set {i + 1}/{n_sets}")
         sets.append(Step(W.make(name, device=dev, seed=cfg["seed"] + 100 * i), alpha, args.split))
     meta_s = sets[0].meta_s
+    graphs = args.graph
+    if graphs:
+        for st in sets:
+            st.capture()
+        score_fn = [st.g_score.replay for st in sets]
+        rest_fn = [st.g_rest.replay for st in sets]
+    else:
+        score_fn = [st.score for st in sets]
+        rest_fn = [st.rest for st in sets]
 
     log(f"[bench] warmup {args.warmup}")
     for i in range(args.warmup):
-        sets[i % n_sets].run()
+        score_fn[i % n_sets]()
+        rest_fn[i % n_sets]()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -193,11 +218,10 @@ def main():
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        s = sets[i % n_sets]
         ev[i][0].record(stream)
-        s.score()
+        score_fn[i % n_sets]()
         ev[i][1].record(stream)
-        s.rest()
+        rest_fn[i % n_sets]()
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
@@ -206,6 +230,14 @@ def main():
     gbps = total / (ms * 1e-3) / 1e9
     score_gbps = score_bytes / (score_ms * 1e-3) / 1e9
     log(f"[bench] {ms * 1e3:.1f} us/step, score stage {score_ms * 1e3:.1f} us")
+
+    if args.calibrate:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu:
@@ -234,7 +266,8 @@ def main():
                    if w0.dtype == torch.bfloat16 else "f32", "select": sel_desc[cfg["policy"]],
                    "attn": "softmax" if alpha == 1.0 else f"{alpha}-entmax", "bytes_per_step": int(total),
                    "achieved_GBps": round(gbps, 1), "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
-                   "buffer_sets": n_sets, "meta_build_s": round(meta_s, 4), "bytes_detail": det},
+                   "buffer_sets": n_sets, "hip_graphs": graphs, "meta_build_s": round(meta_s, 4),
+                   "bytes_detail": det},
         "roofline": {"bound": "hbm", "kernel": f"score_pages[{sets[0].kind}]", "achieved": round(score_gbps, 1),
                      "peak": PEAK_GBPS, "unit": "GB/s", "frac": round(score_gbps / PEAK_GBPS, 4), "traffic": None,
                      "avg_us": round(score_ms * 1e3, 2), "bytes_per_launch": int(score_bytes)},

@@ -79,9 +79,9 @@ skv_status attn_plan(const skv_cache *c, const skv_attn_params *p, int cap, Attn
     spi = std::max<int64_t>(1, std::min<int64_t>(spi, std::max(1, rmax / rows_per_item)));
   }
   spi = std::min<int64_t>(spi, cap);
+  spi = std::max<int64_t>(spi, (cap + 2047) / 2048);   // at most 2048 partitions per unit
   const int64_t nsplit = (cap + spi - 1) / spi;
   const int64_t rps = spi * rows_per_item;
-  if (nsplit > 65535) return SKV_ERR_UNSUPPORTED;
   if (entmax && (int64_t)G * rps * 4 > 65536) return SKV_ERR_UNSUPPORTED;   // LDS of the logits pass
   out->spi = (int)spi;
   out->nsplit = (int)nsplit;

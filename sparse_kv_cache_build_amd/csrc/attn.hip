@@ -24,7 +24,6 @@
 namespace skv {
 
 constexpr int kAttnThreads = 256;
-constexpr int kCandLds = 8192;  // candidates of one head held in LDS by the solve kernel
 
 template <int D>
 struct RowLayout {
@@ -79,13 +78,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_softmax_kernel(
   const int rows_per_item = gran ? 1 : c.S;
   const int NR = max(0, it1 - it0) * rows_per_item;
 
-  float qv[G][8];
+  Packed8<T> qv[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    Elem<T>::load8(q + ((size_t)b * c.Hq + g * G + h) * D + lr * 8, qv[h]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) qv[h][j] *= scale_log2;
-  }
+  for (int h = 0; h < G; ++h) qv[h].load(q + ((size_t)b * c.Hq + g * G + h) * D + lr * 8);
   float mref[G], l[G], acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -100,13 +95,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_softmax_kernel(
     const int it = r / rows_per_item;
     return rm.row_offset(it0 + it, r - it * rows_per_item);
   };
-  auto accumulate = [&](const float (&kx)[8], const float (&vx)[8]) {
+  auto accumulate = [&](const Packed8<T> &kx, const float (&vx)[8]) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float part_dot = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) part_dot = fmaf(qv[h][j], kx[j], part_dot);
-      const float z = group_sum<RL::LPR>(part_dot);
+      const float z = group_sum<RL::LPR>(qv[h].dot(kx)) * scale_log2;
       if (z > mref[h] + 32.0f) {  // rescale the state to a new reference
         const float corr = exp2f(mref[h] - z);
         l[h] *= corr;
@@ -123,13 +115,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_softmax_kernel(
   // two rows per lane group per step: both rows' loads are in flight before either is used
   for (int r = rg; r < NR; r += 2 * RL::RGB) {
     const long long o1 = row_off(r), o2 = row_off(r + RL::RGB);
-    float k1[8], v1[8], k2[8], v2[8];
+    Packed8<T> k1, k2;
+    float v1[8], v2[8];
     if (o1 >= 0) {
-      Elem<T>::load8(K + o1 + lr * 8, k1);
+      k1.load(K + o1 + lr * 8);
       Elem<T>::load8(V + o1 + lr * 8, v1);
     }
     if (o2 >= 0) {
-      Elem<T>::load8(K + o2 + lr * 8, k2);
+      k2.load(K + o2 + lr * 8);
       Elem<T>::load8(V + o2 + lr * 8, v2);
     }
     if (o1 >= 0) accumulate(k1, v1);
@@ -252,37 +245,29 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
   const int L = seq_len(c, b);
   RowMap rm{sel_idx + (size_t)unit * cap, c.bt + (size_t)b * c.maxP, gran, c.S, c.Hkv, g, D, L, num_pages(c, L)};
 
-  float qv[G][8];
+  Packed8<T> qv[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    Elem<T>::load8(q + ((size_t)b * c.Hq + g * G + h) * D + lr * 8, qv[h]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) qv[h][j] *= zscale;
-  }
+  for (int h = 0; h < G; ++h) qv[h].load(q + ((size_t)b * c.Hq + g * G + h) * D + lr * 8);
   const T *K = static_cast<const T *>(c.k);
   auto row_off = [&](int r) -> long long {
     if (r >= NR) return -1;
     const int it = r / rows_per_item;
     return rm.row_offset(it0 + it, r - it * rows_per_item);
   };
-  auto logits = [&](int r, long long off, const float (&kx)[8]) {
+  auto logits = [&](int r, long long off, const Packed8<T> &kx) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float part_dot = 0.0f;
-      if (off >= 0) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) part_dot = fmaf(qv[h][j], kx[j], part_dot);
-        part_dot = group_sum<RL::LPR>(part_dot);
-      }
-      if (lr == h % RL::LPR) zs[h * rps + r] = off >= 0 ? part_dot : -INFINITY;
+      float z = 0.0f;
+      if (off >= 0) z = group_sum<RL::LPR>(qv[h].dot(kx)) * zscale;
+      if (lr == h % RL::LPR) zs[h * rps + r] = off >= 0 ? z : -INFINITY;
     }
   };
   for (int r = rg; r < NR; r += 2 * RL::RGB) {
     const int r2 = r + RL::RGB;
     const long long o1 = row_off(r), o2 = row_off(r2);
-    float k1[8], k2[8];
-    if (o1 >= 0) Elem<T>::load8(K + o1 + lr * 8, k1);
-    if (o2 >= 0) Elem<T>::load8(K + o2 + lr * 8, k2);
+    Packed8<T> k1, k2;
+    if (o1 >= 0) k1.load(K + o1 + lr * 8);
+    if (o2 >= 0) k2.load(K + o2 + lr * 8);
     logits(r, o1, k1);
     if (r2 < NR) logits(r2, o2, k2);
   }
@@ -313,22 +298,32 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
 
 // ---------------------------------------------------------------- entmax threshold and p V
 
-// ALPHA_KIND: 1 -> alpha = 1.5, 2 -> alpha = 2, 3 -> any alpha in (1, 2)
+// One wave per query head. ALPHA_KIND: 1 -> alpha = 1.5, 2 -> alpha = 2, 3 -> any alpha in (1, 2).
+//  1. max_all = max of the split maxima; only z' > max_all - 1 can carry weight.
+//  2. The per-split pair lists are read as one flat list (split-major, row order) through prefix
+//     offsets in LDS, and the survivors are compacted into LDS in that order (ballots).
+//  3. Bisection on tau over [max_all - 1, max_all - n^(1-alpha)], then the closed form on the
+//     support {z' > tau}, iterated until the support size repeats (alpha = 2: tau = (sum z' - 1) / k;
+//     alpha = 1.5: tau = mean - sqrt((1 - k var) / k), the smaller root of sum (z' - tau)^2 = 1).
+//  4. p = (z' - tau)_+^(1/(alpha-1)) (renormalized for other alpha), out = sum p v over rows with
+//     p > 0, read in place through the selection and block table.
+// When the survivors do not fit in LDS, steps 3-4 read the flat list from global memory instead.
+constexpr int kSolveCap = 1024;     // survivors staged in LDS
+constexpr int kSolveSplits = 2048;  // split offsets staged in LDS (the planner keeps nsplit below)
+
 template <typename T, int D, int ALPHA_KIND>
-__global__ __launch_bounds__(kAttnThreads) void attn_entmax_solve_kernel(
+__global__ __launch_bounds__(kWave) void attn_entmax_solve_kernel(
     CacheView c, const int32_t *__restrict__ sel_idx, const int32_t *__restrict__ sel_count, int cap, int gran,
     int spi, int nsplit, float alpha, const float2 *__restrict__ cand, const int32_t *__restrict__ cand_cnt,
     const float *__restrict__ cand_max, float *__restrict__ out) {
   using RL = RowLayout<D>;
-  __shared__ float cz[kCandLds];
-  __shared__ int cslot[kCandLds];
-  __shared__ int scan_scratch[kAttnThreads / kWave + 1];
-  __shared__ float redf[kAttnThreads / kWave];
-  __shared__ double redd[kAttnThreads / kWave];
-  __shared__ float s_acc[kAttnThreads / kWave][D];
+  constexpr int RG = kWave / RL::LPR;  // row groups in the wave
+  __shared__ float cz[kSolveCap];
+  __shared__ int cslot[kSolveCap];
+  __shared__ int soff[kSolveSplits + 1];
   const int bh = blockIdx.x, b = bh / c.Hq, h = bh - b * c.Hq, g = h / c.G, hh = h - g * c.G;
   const int unit = b * c.Hkv + g;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int lane = threadIdx.x;
   const int count = min(max(sel_count[unit], 0), cap);
   const int rows_per_item = gran ? 1 : c.S;
   const int rps = spi * rows_per_item;
@@ -337,48 +332,60 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_solve_kernel(
   float *o = out + (size_t)bh * D;
 
   float mx = -INFINITY;
-  for (int s = tid; s < ns; s += kAttnThreads) mx = fmaxf(mx, cand_max[lid0 + s]);
-  mx = block_max<kAttnThreads>(mx, redf);
+  for (int s = lane; s < ns; s += kWave) mx = fmaxf(mx, cand_max[lid0 + s]);
+  mx = wave_max(mx);
   if (mx == -INFINITY) {  // nothing selected
-    for (int j = tid; j < D; j += kAttnThreads) o[j] = 0.0f;
+    for (int j = lane; j < D; j += kWave) o[j] = 0.0f;
     return;
   }
   const float lo_bound = mx - 1.0f;
-  // gather the pairs with z' > max - 1 into LDS in (split, row) order
+  // prefix offsets of the split lists (exclusive), 64 splits per step
+  int run = 0;
+  for (int s0 = 0; s0 < ns; s0 += kWave) {
+    const int s = s0 + lane;
+    const int cnt = s < ns ? cand_cnt[lid0 + s] : 0;
+    const int incl = wave_incl_scan(cnt);
+    if (s < ns) soff[s] = run + incl - cnt;
+    run += __shfl(incl, kWave - 1, kWave);
+  }
+  if (lane == 0) soff[ns] = run;
+  __syncthreads();
+  const int nraw = run;
+  // flat entry f -> (split, row) through a binary search of the offsets
+  auto entry = [&](int f) -> float2 {
+    int lo = 0, hi = ns - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (soff[mid] <= f) lo = mid; else hi = mid - 1;
+    }
+    return cand[(lid0 + lo) * rps + (f - soff[lo])];
+  };
+  // survivors into LDS, in flat order; four loads in flight per lane
   int n = 0;
-  bool overflow = false;
-  for (int s0 = 0; s0 < ns; s0 += kAttnThreads) {
-    const int s = s0 + tid;
-    int nk = 0;
-    if (s < ns) {
-      const float2 *cl = cand + (lid0 + s) * rps;
-      const int cnt = cand_cnt[lid0 + s];
-      for (int i = 0; i < cnt; ++i) nk += cl[i].x > lo_bound;
+  for (int f0 = 0; f0 < nraw; f0 += 4 * kWave) {
+    float2 e[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int f = f0 + u * kWave + lane;
+      e[u] = f < nraw ? entry(f) : make_float2(-INFINITY, 0.0f);
     }
-    int tot;
-    int pos = n + block_excl_scan<kAttnThreads>(nk, scan_scratch, &tot);
-    if (n + tot > kCandLds) overflow = true;
-    if (!overflow && s < ns) {
-      const float2 *cl = cand + (lid0 + s) * rps;
-      const int cnt = cand_cnt[lid0 + s];
-      for (int i = 0; i < cnt; ++i) {
-        const float2 e = cl[i];
-        if (e.x > lo_bound) {
-          cz[pos] = e.x;
-          cslot[pos] = __float_as_int(e.y);
-          ++pos;
-        }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool keep = e[u].x > lo_bound;
+      const uint64_t bal = __ballot(keep);
+      const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      if (keep && pos < kSolveCap) {
+        cz[pos] = e[u].x;
+        cslot[pos] = __float_as_int(e[u].y);
       }
+      n += __popcll(bal);
     }
-    n += tot;
   }
   __syncthreads();
-  if (overflow) {
-    // more survivors than LDS holds: not produced by a valid bound; flag with NaN output
-    for (int j = tid; j < D; j += kAttnThreads) o[j] = NAN;
-    return;
-  }
-  // bisection: F(tau) = sum (z' - tau)_+^(1/(alpha-1)) - 1, F(mx - 1) >= 0 >= F(mx - n^(1-alpha))
+  const bool in_lds = n <= kSolveCap;
+  const int nn = in_lds ? n : nraw;   // in global mode the unfiltered list is walked (z' <= max - 1 weighs 0)
+  auto z_at = [&](int i) -> float { return in_lds ? cz[i] : entry(i).x; };
+
   const float am1 = alpha - 1.0f, inv = 1.0f / am1;
   auto pw = [&](float x) -> float {
     if (ALPHA_KIND == 1) return x * x;
@@ -390,33 +397,32 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_solve_kernel(
     const float mid = 0.5f * (lo + hi);
     if (mid <= lo || mid >= hi) break;
     double sum = 0.0;
-    for (int i = tid; i < n; i += kAttnThreads) {
-      const float x = cz[i] - mid;
+    for (int i = lane; i < nn; i += kWave) {
+      const float x = z_at(i) - mid;
       if (x > 0.0f) sum += (double)pw(x);
     }
-    sum = block_sum<kAttnThreads>(sum, redd);
-    if (sum >= 1.0)
+    if (wave_sum(sum) >= 1.0)
       lo = mid;
     else
       hi = mid;
   }
   float tau = lo;
   if (ALPHA_KIND != 3) {
-    // closed form on the support S = {z' > tau}, iterated to a fixed point (shifted by mx)
     int prev = -1;
     for (int it = 0; it < 16; ++it) {
       double k = 0.0, s1 = 0.0, s2 = 0.0;
-      for (int i = tid; i < n; i += kAttnThreads) {
-        if (cz[i] > tau) {
-          const double y = (double)cz[i] - (double)mx;
+      for (int i = lane; i < nn; i += kWave) {
+        const float z = z_at(i);
+        if (z > tau) {
+          const double y = (double)z - (double)mx;
           k += 1.0;
           s1 += y;
           s2 += y * y;
         }
       }
-      k = block_sum<kAttnThreads>(k, redd);
-      s1 = block_sum<kAttnThreads>(s1, redd);
-      s2 = block_sum<kAttnThreads>(s2, redd);
+      k = wave_sum(k);
+      s1 = wave_sum(s1);
+      s2 = wave_sum(s2);
       if (k <= 0.0 || (int)k == prev) break;
       prev = (int)k;
       double ty;
@@ -430,28 +436,38 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_solve_kernel(
       tau = (float)((double)mx + ty);
     }
   }
-  // weights and normalisation (alpha outside {1.5, 2}: renormalise the bisection weights)
-  double psum = 0.0;
-  for (int i = tid; i < n; i += kAttnThreads) {
-    const float x = cz[i] - tau;
-    const float p = x > 0.0f ? pw(x) : 0.0f;
-    cz[i] = p;
-    psum += p;
+  float norm = 1.0f;
+  if (ALPHA_KIND == 3) {
+    double psum = 0.0;
+    for (int i = lane; i < nn; i += kWave) {
+      const float x = z_at(i) - tau;
+      if (x > 0.0f) psum += pw(x);
+    }
+    psum = wave_sum(psum);
+    norm = psum > 0.0 ? (float)(1.0 / psum) : 1.0f;
   }
-  psum = block_sum<kAttnThreads>(psum, redd);
-  const float norm = (ALPHA_KIND == 3 && psum > 0.0) ? (float)(1.0 / psum) : 1.0f;
   // p V over rows with p > 0; row groups take entries round-robin
-  const int lr = lane % RL::LPR, rg = wave * RL::RPW + lane / RL::LPR;
+  const int lr = lane % RL::LPR, rg = lane / RL::LPR;
   const int L = seq_len(c, b);
   RowMap rm{sel_idx + (size_t)unit * cap, c.bt + (size_t)b * c.maxP, gran, c.S, c.Hkv, g, D, L, num_pages(c, L)};
   const T *V = static_cast<const T *>(c.v);
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-  for (int i = rg; i < n; i += RL::RGB) {
-    const float p = cz[i] * norm;
-    if (p <= 0.0f) continue;
-    const int slot = cslot[i];
+  for (int i = rg; i < nn; i += RG) {
+    float z;
+    int slot;
+    if (in_lds) {
+      z = cz[i];
+      slot = cslot[i];
+    } else {
+      const float2 e = entry(i);
+      z = e.x;
+      slot = __float_as_int(e.y);
+    }
+    const float x = z - tau;
+    if (!(x > 0.0f)) continue;
+    const float p = pw(x) * norm;
     const int item = slot / rows_per_item;
     const long long off = rm.row_offset(item, slot - item * rows_per_item);
     if (off < 0) continue;
@@ -469,14 +485,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_solve_kernel(
   }
   if (lane < RL::LPR)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) s_acc[wave][lr * 8 + j] = acc[j];
-  __syncthreads();
-  for (int j = tid; j < D; j += kAttnThreads) {
-    float a = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kAttnThreads / kWave; ++w) a += s_acc[w][j];
-    o[j] = a;
-  }
+    for (int j = 0; j < 8; ++j) o[lr * 8 + j] = acc[j];
 }
 
 // ---------------------------------------------------------------- launchers
@@ -515,15 +524,15 @@ static hipError_t attn_typed(const AttnArgs &a, hipStream_t st) {
   const int kind = a.alpha == 1.5f ? 1 : (a.alpha == 2.0f ? 2 : 3);
   const dim3 g2(c.B * c.Hq);
   if (kind == 1)
-    attn_entmax_solve_kernel<T, D, 1><<<g2, kAttnThreads, 0, st>>>(c, a.sel_idx, a.sel_count, a.cap, a.gran, a.spi,
+    attn_entmax_solve_kernel<T, D, 1><<<g2, kWave, 0, st>>>(c, a.sel_idx, a.sel_count, a.cap, a.gran, a.spi,
                                                                     a.nsplit, a.alpha, a.cand, a.cand_cnt, a.cand_max,
                                                                     a.out);
   else if (kind == 2)
-    attn_entmax_solve_kernel<T, D, 2><<<g2, kAttnThreads, 0, st>>>(c, a.sel_idx, a.sel_count, a.cap, a.gran, a.spi,
+    attn_entmax_solve_kernel<T, D, 2><<<g2, kWave, 0, st>>>(c, a.sel_idx, a.sel_count, a.cap, a.gran, a.spi,
                                                                     a.nsplit, a.alpha, a.cand, a.cand_cnt, a.cand_max,
                                                                     a.out);
   else
-    attn_entmax_solve_kernel<T, D, 3><<<g2, kAttnThreads, 0, st>>>(c, a.sel_idx, a.sel_count, a.cap, a.gran, a.spi,
+    attn_entmax_solve_kernel<T, D, 3><<<g2, kWave, 0, st>>>(c, a.sel_idx, a.sel_count, a.cap, a.gran, a.spi,
                                                                     a.nsplit, a.alpha, a.cand, a.cand_cnt, a.cand_max,
                                                                     a.out);
   return hipGetLastError();

@@ -60,6 +60,40 @@ struct Elem<uint16_t> {
   }
 };
 
+// 8 consecutive elements kept packed for the dot-product path: bf16 pairs as they are stored,
+// float as is. dot8(q, k) = sum of the 8 products, accumulated in float32 (for bf16 with
+// v_dot2c_f32_bf16: the bf16 x bf16 products are exact).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <typename T>
+struct Packed8;
+
+template <>
+struct Packed8<uint16_t> {
+  uint4 w;
+  __device__ __forceinline__ void load(const uint16_t *p) { w = *reinterpret_cast<const uint4 *>(p); }
+  __device__ __forceinline__ float dot(const Packed8 &k) const {
+    float acc = 0.0f;
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, k.w.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), __builtin_bit_cast(bf16x2_t, k.w.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), __builtin_bit_cast(bf16x2_t, k.w.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), __builtin_bit_cast(bf16x2_t, k.w.w), acc, false);
+    return acc;
+  }
+};
+
+template <>
+struct Packed8<float> {
+  float x[8];
+  __device__ __forceinline__ void load(const float *p) { Elem<float>::load8(p, x); }
+  __device__ __forceinline__ float dot(const Packed8 &k) const {
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = fmaf(x[j], k.x[j], acc);
+    return acc;
+  }
+};
+
 // Round a double to bf16, nearest-even. Normal range: round to odd at binary32 (truncate,
 // then set the last bit when inexact) and round that to nearest-even at 8 significant bits;
 // a round-to-odd intermediate with at least two extra bits makes the second rounding equal

@@ -140,40 +140,54 @@ __global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const flo
 }
 
 // PROJ key: one lane per token t. u_h(t) = sum_i q~_h[i] k~_t[i] (float64, i ascending; the
-// products of a float32 and a bf16 value are exact), key = RN_f32(max_h u_h(t)).
+// products of a float32 and a bf16 value are exact), key = RN_f32(max_h u_h(t)). Each thread
+// scores TPT tokens (t, t + 256, ...) with all their row loads issued before the arithmetic.
+constexpr int kProjTPT = 2;
 template <int R, int G>
 __global__ __launch_bounds__(256) void score_proj_kernel(CacheView c, const uint16_t *__restrict__ kproj,
                                                          const double *__restrict__ qt, float *__restrict__ key) {
   const int unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  const int Lmax = c.maxP * c.S;
-  if (t >= Lmax) return;
-  float *out = key + (size_t)unit * Lmax + t;
-  if (t >= seq_len(c, b)) {
-    *out = -INFINITY;
-    return;
-  }
-  const int phys = c.bt[(size_t)b * c.maxP + t / c.S];
-  const uint16_t *row = kproj + (((size_t)phys * c.Hkv + g) * c.S + t % c.S) * R;
+  const int Lmax = c.maxP * c.S, L = seq_len(c, b);
+  const int t0 = blockIdx.x * (256 * kProjTPT) + threadIdx.x;
   const double *qq = qt + (size_t)(b * c.Hq + g * G) * R;
-  double acc[G];
+  uint4 w[kProjTPT][R / 8];
 #pragma unroll
-  for (int h = 0; h < G; ++h) acc[h] = 0.0;
+  for (int u = 0; u < kProjTPT; ++u) {
+    const int t = t0 + u * 256;
+    if (t < L) {
+      const int phys = c.bt[(size_t)b * c.maxP + t / c.S];
+      const uint4 *row = reinterpret_cast<const uint4 *>(kproj + (((size_t)phys * c.Hkv + g) * c.S + t % c.S) * R);
 #pragma unroll
-  for (int i0 = 0; i0 < R; i0 += 8) {
-    float x[8];
-    Elem<uint16_t>::load8(row + i0, x);
-#pragma unroll
-    for (int ii = 0; ii < 8; ++ii) {
-      const double dx = x[ii];
-#pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = fma(qq[(size_t)h * R + i0 + ii], dx, acc[h]);
+      for (int i = 0; i < R / 8; ++i) w[u][i] = row[i];
     }
   }
-  double best = acc[0];
 #pragma unroll
-  for (int h = 1; h < G; ++h) best = fmax(best, acc[h]);
-  *out = (float)best;
+  for (int u = 0; u < kProjTPT; ++u) {
+    const int t = t0 + u * 256;
+    if (t >= Lmax) break;
+    float *out = key + (size_t)unit * Lmax + t;
+    if (t >= L) {
+      *out = -INFINITY;
+      continue;
+    }
+    double acc[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) acc[h] = 0.0;
+#pragma unroll
+    for (int i0 = 0; i0 < R / 8; ++i0) {
+      const uint32_t ww[4] = {w[u][i0].x, w[u][i0].y, w[u][i0].z, w[u][i0].w};
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) {
+        const double dx = (ii & 1) ? bf16_hi(ww[ii / 2]) : bf16_lo(ww[ii / 2]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h] = fma(qq[(size_t)h * R + i0 * 8 + ii], dx, acc[h]);
+      }
+    }
+    double best = acc[0];
+#pragma unroll
+    for (int h = 1; h < G; ++h) best = fmax(best, acc[h]);
+    *out = (float)best;
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -227,7 +241,7 @@ hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, cons
 
 template <int R>
 static hipError_t proj_r(const CacheView &c, const uint16_t *kproj, const double *qt, float *key, hipStream_t st) {
-  const dim3 grid((c.maxP * c.S + 255) / 256, c.B * c.Hkv);
+  const dim3 grid((c.maxP * c.S + 256 * kProjTPT - 1) / (256 * kProjTPT), c.B * c.Hkv);
   SKV_DISPATCH_G(c.G, score_proj_kernel<R, GG><<<grid, 256, 0, st>>>(c, kproj, qt, key))
   return hipGetLastError();
 }

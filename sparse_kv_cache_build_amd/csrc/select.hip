@@ -37,19 +37,26 @@ __device__ __forceinline__ SelSize sel_size(const CacheView &c, int b, int polic
 
 // Radix selection over order keys get(i), i < n: finds the r-th largest key T (1 <= r <= n) and
 // need = r - #(keys > T), i.e. how many keys equal to T belong to the top r. Four 8-bit digits,
-// most significant first; histograms use integer LDS atomics (deterministic). `hist` holds 256
-// words, `bc` 2 words of shared memory. Every thread of the block must call it.
+// most significant first. Each wave counts into its own 256-bin LDS histogram (the leading digits
+// of float keys fall into few bins, so one shared histogram would serialize the atomics); the
+// wave histograms are then summed. Integer atomics only, so the result is deterministic.
+// `hist` holds NT/64 * 256 words, `bc` 2 words of shared memory. Every thread must call it.
+// With digits < 4 only the leading digits are resolved: T then has its low bits cleared, which
+// makes it a lower bound of the r-th largest key with at least r keys >= T.
 template <int NT, typename Get>
-__device__ void radix_kth(Get get, int n, uint32_t r, uint32_t *hist, uint32_t *bc, uint32_t &T, uint32_t &need) {
+__device__ void radix_kth(Get get, int n, uint32_t r, uint32_t *hist, uint32_t *bc, uint32_t &T, uint32_t &need,
+                          int digits = 4) {
+  constexpr int NW = NT / kWave;
   const int tid = threadIdx.x;
+  uint32_t *mine = hist + (tid / kWave) * 256;
   uint32_t prefix = 0, mask = 0;
   need = r;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += NT) hist[i] = 0;
+  for (int shift = 24; shift >= 32 - 8 * digits; shift -= 8) {
+    for (int i = tid; i < NW * 256; i += NT) hist[i] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += NT) {
       const uint32_t u = get(i);
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 0xffu], 1u);
+      if ((u & mask) == prefix) atomicAdd(&mine[(u >> shift) & 0xffu], 1u);
     }
     __syncthreads();
     // the wanted digit v has count(> v) < need <= count(>= v); lane l owns digits 4l .. 4l+3
@@ -57,8 +64,11 @@ __device__ void radix_kth(Get get, int n, uint32_t r, uint32_t *hist, uint32_t *
       uint32_t c4[4], local = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        c4[i] = hist[4 * tid + i];
-        local += c4[i];
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) cnt += hist[w * 256 + 4 * tid + i];
+        c4[i] = cnt;
+        local += cnt;
       }
       uint32_t incl = local;  // inclusive suffix sum over lanes (higher lanes: larger digits)
 #pragma unroll
@@ -115,7 +125,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(CacheView c, c
                                                                   int32_t *__restrict__ sel_idx,
                                                                   int32_t *__restrict__ sel_count, int cap) {
   __shared__ uint32_t skeys[kSelLds];
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[kSelThreads / kWave * 256];
   __shared__ uint32_t bc[2];
   __shared__ int scan_scratch[kSelThreads / kWave + 1];
   const int unit = blockIdx.x, b = unit / c.Hkv;
@@ -147,25 +157,32 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(CacheView c, c
 // Token top-k over long sequences: one block of 1024 threads per unit.
 //  1. Sample 8192 keys (64 evenly spaced runs of 128) and take the r-th largest sampled key,
 //     r = k * 8192 / n plus a 4-sigma margin, as the candidate bound T_lo.
-//  2. One pass over all keys keeps (key, index) with key >= T_lo in LDS, in index order.
-//  3. If at least k candidates were kept (and they fit), the top k all lie among them (the k-th
-//     largest key is >= T_lo, so every key that ties with it is a candidate too): select exactly
-//     in LDS. Otherwise fall back to the radix selection over all keys in global memory.
+//  2. One pass over all keys keeps (key, index) with key >= T_lo in LDS, in index order: wave w
+//     scans the w-th contiguous sixteenth of the keys and compacts into its own LDS segment with
+//     ballots (no block barrier per tile); the next tile's loads are issued before the current
+//     tile is compacted.
+//  3. If at least k candidates were kept (and every segment fit), the top k all lie among them (the
+//     k-th largest key is >= T_lo, so every key that ties with it is a candidate too): select
+//     exactly in LDS. Otherwise fall back to the radix selection over all keys in global memory.
+constexpr int kTokWaves = kTokThreads / kWave;
+constexpr int kTokSeg = kTokCand / kTokWaves;   // candidates per wave segment
+
 __global__ __launch_bounds__(kTokThreads) void select_topk_large_kernel(CacheView c, const float *__restrict__ key,
                                                                         int key_stride, int k,
                                                                         int32_t *__restrict__ sel_idx,
                                                                         int32_t *__restrict__ sel_count, int cap) {
   __shared__ uint32_t ckey[kTokCand];
   __shared__ int32_t cidx[kTokCand];
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[kTokWaves * 256];
   __shared__ uint32_t bc[2];
-  __shared__ int scan_scratch[kTokThreads / kWave + 1];
+  __shared__ int scan_scratch[kTokWaves + 1];
+  __shared__ int seg_cnt[kTokWaves];
   const int unit = blockIdx.x, b = unit / c.Hkv;
   const int n = seq_len(c, b);
   const int kk = min(k, n);
   const float *kr = key + (size_t)unit * key_stride;
   int32_t *out = sel_idx + (size_t)unit * cap;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   if (tid == 0) sel_count[unit] = kk;
   if (kk <= 0) return;
   if (kk >= n) {
@@ -193,48 +210,95 @@ __global__ __launch_bounds__(kTokThreads) void select_topk_large_kernel(CacheVie
   const double rs = ceil(expect + 4.0 * sqrt(expect) + 16.0);
   uint32_t Tlo = 0;
   if (rs < kTokSample) {
-    radix_kth<kTokThreads>(lget, kTokSample, (uint32_t)rs, hist, bc, T, need);
+    radix_kth<kTokThreads>(lget, kTokSample, (uint32_t)rs, hist, bc, T, need, 2);   // a lower bound suffices
     Tlo = T;
   }
   __syncthreads();
-  // 2. filtered pass in index order, 4 consecutive keys per thread per tile
+  // 2. filtered pass: wave w owns keys [w * span, (w + 1) * span). Per step a wave covers kSub
+  //    tiles of 256 keys (4 consecutive keys per lane per tile), all loads issued up front.
+  constexpr int kSub = 8;
+  const int span = ((n + kTokWaves - 1) / kTokWaves + 255) / 256 * 256;
+  const int w0 = min(n, wave * span), w1 = min(n, w0 + span);
   const bool vec = (key_stride & 3) == 0;
-  int base = 0;
-  bool overflow = false;
-  for (int t0 = 0; t0 < n; t0 += 4 * kTokThreads) {
-    const int i = t0 + 4 * tid;
-    uint32_t u[4];
-    if (vec && i + 3 < n) {
-      const float4 f = *reinterpret_cast<const float4 *>(kr + i);
-      u[0] = f32_order_key(f.x);
-      u[1] = f32_order_key(f.y);
-      u[2] = f32_order_key(f.z);
-      u[3] = f32_order_key(f.w);
-    } else {
+  uint32_t *sk = ckey + wave * kTokSeg;
+  int32_t *si = cidx + wave * kTokSeg;
+  int cnt = 0;   // candidates of this wave (uniform across the wave)
+  for (int t0 = w0; t0 < w1; t0 += kSub * 4 * kWave) {
+    uint32_t u[kSub][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) u[j] = i + j < n ? f32_order_key(kr[i + j]) : 0u;
+    for (int j = 0; j < kSub; ++j) {
+      const int i = t0 + j * 4 * kWave + 4 * lane;
+      if (vec && i + 3 < w1) {
+        const float4 f = *reinterpret_cast<const float4 *>(kr + i);
+        u[j][0] = f32_order_key(f.x);
+        u[j][1] = f32_order_key(f.y);
+        u[j][2] = f32_order_key(f.z);
+        u[j][3] = f32_order_key(f.w);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[j][e] = i + e < w1 ? f32_order_key(kr[i + e]) : 0u;
+      }
     }
-    int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) cnt += (i + j < n) && u[j] >= Tlo;
-    int tot;
-    int pos = base + block_excl_scan<kTokThreads>(cnt, scan_scratch, &tot);
-    if (base + tot > kTokCand) overflow = true;
-    if (!overflow) {
+    for (int j = 0; j < kSub; ++j) {
+      const int i = t0 + j * 4 * kWave + 4 * lane;
+      bool f[4];
+      uint64_t bal[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if ((i + j < n) && u[j] >= Tlo) {
-          ckey[pos] = u[j];
-          cidx[pos] = i + j;
+      for (int e = 0; e < 4; ++e) {
+        f[e] = (i + e < w1) && u[j][e] >= Tlo;
+        bal[e] = __ballot(f[e]);
+      }
+      // index order is lane-major within a tile: rank = keys of lower lanes + lower e in this lane
+      int pos = cnt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        pos += __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal[e], 0u));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (f[e]) {
+          if (pos < kTokSeg) {
+            sk[pos] = u[j][e];
+            si[pos] = i + e;
+          }
           ++pos;
         }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cnt += __popcll(bal[e]);
     }
-    base += tot;
   }
+  if (lane == 0) seg_cnt[wave] = cnt;
   __syncthreads();
-  if (!overflow && base >= kk) {
-    radix_kth<kTokThreads>(lget, base, (uint32_t)kk, hist, bc, T, need);
-    ordered_take<kTokThreads>(lget, lidx, base, T, need, out, scan_scratch);
+  int total = 0;
+  bool overflow = false;
+  for (int w = 0; w < kTokWaves; ++w) {
+    total += seg_cnt[w];
+    overflow |= seg_cnt[w] > kTokSeg;
+  }
+  if (!overflow && total >= kk) {
+    // gather the segments into one contiguous list (in place, front to back) so the list is
+    // ordered by index; wave w's entries move to the prefix of the earlier segments
+    int off = 0;
+    for (int w = 0; w < kTokWaves; ++w) {
+      const int m = seg_cnt[w];
+      uint32_t tk = 0;
+      int32_t ti = 0;
+      const bool has = tid < m;
+      if (has) {
+        tk = ckey[w * kTokSeg + tid];
+        ti = cidx[w * kTokSeg + tid];
+      }
+      __syncthreads();
+      if (has) {
+        ckey[off + tid] = tk;
+        cidx[off + tid] = ti;
+      }
+      __syncthreads();
+      off += m;
+    }
+    radix_kth<kTokThreads>(lget, total, (uint32_t)kk, hist, bc, T, need);
+    ordered_take<kTokThreads>(lget, lidx, total, T, need, out, scan_scratch);
     return;
   }
   // 3. fallback: exact radix selection over all keys in global memory

@@ -1,0 +1,40 @@
+"""The decode step captured as a HIP graph replays to the same bits as eager launches, replay after
+replay, with eager work and synchronisations in between (no memset nodes are recorded)."""
+import numpy as np
+import pytest
+import torch
+
+import bench
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name,over", [("gqa32k", dict(B=2, L=3000)), ("token128k", dict(B=2, L=5000, k=512)),
+                                       ("ragged", dict(B=4, lens=[100, 4500, 20000, 12345])),
+                                       ("long_gauss", dict(B=2, L=6000))])
+def test_graph_replays_match_eager(name, over):
+    print(f"[graph] {name} {over}", flush=True)
+    w = W.make(name, device="cuda:0", **over)
+    st = bench.Step(w, W.CONFIGS[name]["alphas"][0])
+    st.run()
+    torch.cuda.synchronize()
+    ref_out = st.attn.out.clone()
+    ref_cnt = st.sel.count.clone()
+    cnt = ref_cnt.cpu().numpy()
+    ref_idx = st.sel.idx.cpu().numpy()
+    st.capture()
+    for rep in range(3):
+        st.attn.out.zero_()
+        st.sel.count.zero_()
+        st.g_score.replay()
+        st.g_rest.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.sel.count, ref_cnt), rep
+        idx = st.sel.idx.cpu().numpy()
+        for u, n in np.ndenumerate(cnt):
+            assert np.array_equal(idx[u][:n], ref_idx[u][:n]), (rep, u)
+        assert torch.equal(st.attn.out, ref_out), rep
+        st.run()                      # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(st.attn.out, ref_out)
