@@ -114,6 +114,22 @@ def step_bytes(st: Step):
     return total, meta + keys_out, dict(meta=meta, k_rows=k_rows, v_rows=v_rows, q_out=q_out, keys_out=keys_out)
 
 
+def recorded_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of the dominant kernel from the committed PMC record (profiles/), or None
+    when there is no record or the kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_score_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, rec["source"])
+    if rec.get("kernel") != kernel or not os.path.exists(src):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return int(rec["traffic_bytes"])
+
+
 def cpu_baseline(name: str, over: dict, alpha: float, budget_s: float = 20.0):
     """The float64 oracle (unchanged) on a bounded sample: units (sequence, KV head) drawn on the
     CPU with the workload's shapes, run in parallel threads, one unit per task. Metadata is built
@@ -269,7 +285,8 @@ def main():
                    "buffer_sets": n_sets, "hip_graphs": graphs, "meta_build_s": round(meta_s, 4),
                    "bytes_detail": det},
         "roofline": {"bound": "hbm", "kernel": f"score_pages[{sets[0].kind}]", "achieved": round(score_gbps, 1),
-                     "peak": PEAK_GBPS, "unit": "GB/s", "frac": round(score_gbps / PEAK_GBPS, 4), "traffic": None,
+                     "peak": PEAK_GBPS, "unit": "GB/s", "frac": round(score_gbps / PEAK_GBPS, 4),
+                     "traffic": recorded_traffic(name, f"score_pages[{sets[0].kind}]"),
                      "avg_us": round(score_ms * 1e3, 2), "bytes_per_launch": int(score_bytes)},
         "cpu_baseline": cpu,
     }
