@@ -47,7 +47,9 @@ class Step:
         self.meta = skv.build_page_meta(self.cache, (self.kind,), proj=w.proj)
         torch.cuda.synchronize()
         self.meta_s = time.time() - t0
-        self.scores = skv.ScoreBuffers(self.cache, self.kind)
+        # token top-k: keep only the candidate set of the selection (fused scoring, no dense keys)
+        self.fused = cfg["policy"] == "token_topk"
+        self.scores = skv.ScoreBuffers(self.cache, self.kind, cfg.get("k", 0) if self.fused else 0)
         p = skv.select_params(cfg["policy"], k=cfg.get("k", 0), budget_pct=cfg.get("pct", 0),
                               alpha=cfg.get("sel_alpha", 1.5), delta=cfg.get("delta", 0.0),
                               tokens=1 if self.kind == "proj" else 0)
@@ -95,7 +97,7 @@ def step_bytes(st: Step):
     else:
         r = w.proj.shape[0]
         meta = int(lens.sum()) * w.Hkv * r * 2
-        keys_out = w.B * w.Hkv * w.maxP * S * 4
+        keys_out = 0 if st.fused else w.B * w.Hkv * w.maxP * S * 4   # fused: only a small candidate set
     if st.sel.granularity:
         k_rows = int(cnt.sum())
     else:

@@ -112,6 +112,13 @@ typedef struct skv_scores {
   float *m;     /* GAUSS: [B, Hq, max_pages] Gaussian mean of the scaled scores of the page */
   float *s;     /* GAUSS: [B, Hq, max_pages] its standard deviation */
   float *shat;  /* GAUSS: [B, Hq, max_pages] estimated maximum m + s sqrt(2 ln n_p) */
+  int32_t token_k; /* PROJ only. 0: write every key into `key`. k > 0: write only the token candidates
+                      a top-k selection can need into `cand` (key is unused); select them with
+                      SKV_SEL_TOKEN_TOPK and the same k */
+  void *cand;      /* PROJ with token_k > 0: opaque candidate set, skv_workspace_bytes(c,
+                      SKV_OP_CANDIDATES, &token_k, 0) bytes, 256-byte aligned. The selection that
+                      consumes it also reads the projected keys (meta->kproj), which must still hold
+                      the same values */
 } skv_scores;
 
 /* Query-aware scores ("EntmaxKV" s2.A; "Joint Subspace Sparse Attention" abstract).
@@ -195,10 +202,11 @@ skv_status skv_sparse_decode_attn(const skv_cache *c, const void *q, const int32
 
 /* ------------------------------------------------------------------ utilities */
 
-enum { SKV_OP_SCORE = 0, SKV_OP_SELECT = 1, SKV_OP_ATTN = 2 };
+enum { SKV_OP_SCORE = 0, SKV_OP_SELECT = 1, SKV_OP_ATTN = 2, SKV_OP_CANDIDATES = 3 };
 
 /* Workspace bytes the call `op` needs for this cache: params points to an int32_t score kind
- * (SCORE), a skv_select_params (SELECT) or a skv_attn_params (ATTN); cap as passed to that call.
+ * (SCORE), a skv_select_params (SELECT), a skv_attn_params (ATTN) or the int32_t token_k of a
+ * candidate set (CANDIDATES: the size of skv_scores.cand); cap as passed to that call.
  * Host-only; enqueues nothing. Writes *bytes; SKV_ERR_INVALID_ARG on bad arguments. */
 skv_status skv_workspace_bytes(const skv_cache *c, int32_t op, const void *params, int32_t cap, size_t *bytes);
 

@@ -22,7 +22,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 META_BOX, META_GAUSS, META_PROJ = 1, 2, 4
 SCORE_BOX, SCORE_GAUSS, SCORE_PROJ = 0, 1, 2
 SEL_TOPK, SEL_BUDGET, SEL_THRESH_GAUSS, SEL_TOKEN_TOPK, SEL_ALL = range(5)
-OP_SCORE, OP_SELECT, OP_ATTN = 0, 1, 2
+OP_SCORE, OP_SELECT, OP_ATTN, OP_CANDIDATES = 0, 1, 2, 3
 
 EXPORTS = ("skv_build_page_meta", "skv_score_pages", "skv_select_pages", "skv_sparse_decode_attn",
            "skv_workspace_bytes", "skv_status_str")
@@ -47,7 +47,8 @@ class Meta(C.Structure):
 
 
 class Scores(C.Structure):
-    _fields_ = [("key", C.c_void_p), ("m", C.c_void_p), ("s", C.c_void_p), ("shat", C.c_void_p)]
+    _fields_ = [("key", C.c_void_p), ("m", C.c_void_p), ("s", C.c_void_p), ("shat", C.c_void_p),
+                ("token_k", C.c_int32), ("cand", C.c_void_p)]
 
 
 class SelectParams(C.Structure):
@@ -179,21 +180,27 @@ _KIND = {"box": SCORE_BOX, "gauss": SCORE_GAUSS, "proj": SCORE_PROJ}
 
 
 class ScoreBuffers:
-    """Output tensors of skv_score_pages for one score kind."""
+    """Output tensors of skv_score_pages for one score kind. For "proj" with token_k > 0 the
+    scores are kept as the candidate set of a top-token_k selection instead of dense keys."""
 
-    def __init__(self, cache: PagedCache, kind: str):
+    def __init__(self, cache: PagedCache, kind: str, token_k: int = 0):
         dev, B, Hq, Hkv, maxP, S = cache.device, cache.B, cache.Hq, cache.Hkv, cache.maxP, cache.S
         self.kind = kind
-        self.key = self.m = self.s = self.shat = None
+        self.token_k = int(token_k) if kind == "proj" else 0
+        self.key = self.m = self.s = self.shat = self.cand = None
         if kind == "box":
             self.key = torch.empty((B, Hkv, maxP), dtype=torch.float32, device=dev)
+        elif kind == "proj" and self.token_k > 0:
+            n = workspace_bytes(cache, OP_CANDIDATES, C.c_int32(self.token_k))
+            self.cand = torch.empty(n, dtype=torch.uint8, device=dev)
         elif kind == "proj":
             self.key = torch.empty((B, Hkv, maxP * S), dtype=torch.float32, device=dev)
         elif kind == "gauss":
             self.m, self.s, self.shat = (torch.empty((B, Hq, maxP), dtype=torch.float32, device=dev) for _ in range(3))
         else:
             raise ValueError(kind)
-        self.sc = Scores(*(t.data_ptr() if t is not None else None for t in (self.key, self.m, self.s, self.shat)))
+        ptrs = [t.data_ptr() if t is not None else None for t in (self.key, self.m, self.s, self.shat)]
+        self.sc = Scores(*ptrs, self.token_k, self.cand.data_ptr() if self.cand is not None else None)
         kind_i = C.c_int32(_KIND[kind])
         self.ws = _workspace(cache, workspace_bytes(cache, OP_SCORE, kind_i))
 
@@ -203,9 +210,9 @@ class ScoreBuffers:
 
 
 def score_pages(cache: PagedCache, meta: PageMeta, q, kind: str, sm_scale=None, out: ScoreBuffers | None = None,
-                stream=None) -> ScoreBuffers:
+                token_k: int = 0, stream=None) -> ScoreBuffers:
     assert q.dtype == cache.dtype and q.is_contiguous() and tuple(q.shape) == (cache.B, cache.Hq, cache.d)
-    out = out or ScoreBuffers(cache, kind)
+    out = out or ScoreBuffers(cache, kind, token_k)
     scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(cache.d)
     _check(lib().skv_score_pages(cache.ref, meta.ref, _ptr(q), _KIND[kind], scale, out.ref, _ptr(out.ws),
                                  out.ws.numel(), _stream(stream)), "skv_score_pages")

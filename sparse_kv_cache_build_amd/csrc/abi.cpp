@@ -82,7 +82,9 @@ skv_status attn_plan(const skv_cache *c, const skv_attn_params *p, int cap, Attn
   spi = std::max<int64_t>(spi, (cap + 2047) / 2048);   // at most 2048 partitions per unit
   const int64_t nsplit = (cap + spi - 1) / spi;
   const int64_t rps = spi * rows_per_item;
-  if (entmax && (int64_t)G * rps * 4 > 65536) return SKV_ERR_UNSUPPORTED;   // LDS of the logits pass
+  // LDS of a partition: logits (entmax) and row offsets
+  if (entmax && (int64_t)G * rps * 4 + rps * 8 + 8 > 65536) return SKV_ERR_UNSUPPORTED;
+  if (!entmax && rps * 8 > 32768) return SKV_ERR_UNSUPPORTED;
   out->spi = (int)spi;
   out->nsplit = (int)nsplit;
   out->rps = (int)rps;
@@ -142,6 +144,13 @@ skv_status skv_workspace_bytes(const skv_cache *c, int32_t op, const void *param
     *bytes = 0;
     return SKV_OK;
   }
+  if (op == SKV_OP_CANDIDATES) {
+    if (*static_cast<const int32_t *>(params) < 1) return SKV_ERR_INVALID_ARG;
+    const skv::CandLayout lay(c->batch, c->num_q_heads, c->num_kv_heads, c->max_pages * c->page_size, 64);
+    if (lay.nb > 8192) return SKV_ERR_UNSUPPORTED;
+    *bytes = lay.total;
+    return SKV_OK;
+  }
   if (op == SKV_OP_ATTN) {
     const skv_attn_params *p = static_cast<const skv_attn_params *>(params);
     if ((st = check_attn_params(p)) != SKV_OK) return st;
@@ -191,9 +200,21 @@ skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q,
       return SKV_ERR_INVALID_ARG;
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SKV_ERR_INVALID_ARG;
   } else if (kind == SKV_SCORE_PROJ) {
-    if (!(m->kinds & SKV_META_PROJ) || !m->kproj || !m->proj || !out->key) return SKV_ERR_INVALID_ARG;
+    if (!(m->kinds & SKV_META_PROJ) || !m->kproj || !m->proj) return SKV_ERR_INVALID_ARG;
     if (!rank_ok(m->proj_rank)) return SKV_ERR_UNSUPPORTED;
     if (!aligned(m->kproj, 16) || !aligned(m->proj, 16)) return SKV_ERR_INVALID_ARG;
+    if (out->token_k < 0) return SKV_ERR_INVALID_ARG;
+    if (out->token_k > 0) {
+      if (!out->cand || !aligned(out->cand, 256)) return SKV_ERR_INVALID_ARG;
+      const skv::CandLayout lay(c->batch, c->num_q_heads, c->num_kv_heads, c->max_pages * c->page_size, 64);
+      if (lay.nb > 8192) return SKV_ERR_UNSUPPORTED;
+      (void)hipGetLastError();
+      hipError_t e = skv::launch_token_bound(v, c->dtype, q, out->token_k, m->proj_rank, m->proj, m->kproj,
+                                             static_cast<char *>(out->cand), s);
+      if (e == hipSuccess) e = skv::launch_score_proj_cand(v, m->proj_rank, m->kproj, static_cast<char *>(out->cand), s);
+      return hip_status(e);
+    }
+    if (!out->key) return SKV_ERR_INVALID_ARG;
   } else {
     return SKV_ERR_INVALID_ARG;
   }
@@ -226,6 +247,14 @@ skv_status skv_select_pages(const skv_cache *c, const skv_scores *sc, const skv_
   switch (p->policy) {
     case SKV_SEL_TOPK:
     case SKV_SEL_TOKEN_TOPK: {
+      if (p->policy == SKV_SEL_TOKEN_TOPK && sc->token_k > 0) {   // candidate set of a fused scoring
+        if (p->k != sc->token_k || !sc->cand || !aligned(sc->cand, 256)) return SKV_ERR_INVALID_ARG;
+        if (cap < p->k) return SKV_ERR_CAPACITY;
+        const skv::CandLayout lay(c->batch, c->num_q_heads, c->num_kv_heads, c->max_pages * c->page_size, 64);
+        if (lay.nb > 8192) return SKV_ERR_UNSUPPORTED;
+        return hip_status(skv::launch_select_token_cand(v, p->k, 64, static_cast<const char *>(sc->cand), sel_idx,
+                                                        sel_count, cap, s));
+      }
       if (p->k < 1 || !sc->key) return SKV_ERR_INVALID_ARG;
       if (cap < p->k) return SKV_ERR_CAPACITY;
       const int stride = p->policy == SKV_SEL_TOPK ? maxP : Lmax;

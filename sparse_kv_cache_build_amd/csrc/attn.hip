@@ -63,9 +63,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_softmax_kernel(
     CacheView c, const T *__restrict__ q, const int32_t *__restrict__ sel_idx, const int32_t *__restrict__ sel_count,
     int cap, int gran, int spi, int nsplit, float scale_log2, float *__restrict__ part, float *__restrict__ out) {
   using RL = RowLayout<D>;
+  constexpr int UNR = G <= 4 ? 4 : 2;   // rows per lane group in flight
   __shared__ float s_m[G][RL::RGB];
   __shared__ float s_l[G][RL::RGB];
   __shared__ float s_acc[kAttnThreads / kWave][G][D];
+  extern __shared__ long long roff[];   // element offset of each row of the partition, -1 if none
   const int split = blockIdx.x, unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
   const int count = min(max(sel_count[unit], 0), cap);
   const int it0 = split * spi;
@@ -112,21 +114,26 @@ __global__ __launch_bounds__(kAttnThreads) void attn_softmax_kernel(
       for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(p, vx[j], acc[h][j]);
     }
   };
-  // two rows per lane group per step: both rows' loads are in flight before either is used
-  for (int r = rg; r < NR; r += 2 * RL::RGB) {
-    const long long o1 = row_off(r), o2 = row_off(r + RL::RGB);
-    Packed8<T> k1, k2;
-    float v1[8], v2[8];
-    if (o1 >= 0) {
-      k1.load(K + o1 + lr * 8);
-      Elem<T>::load8(V + o1 + lr * 8, v1);
+  // row offsets first (selection entry -> block table -> row), then UNR rows per lane group per
+  // step with all their loads in flight before any is used
+  for (int r = tid; r < NR; r += kAttnThreads) roff[r] = row_off(r);
+  __syncthreads();
+  for (int r = rg; r < NR; r += UNR * RL::RGB) {
+    long long o[UNR];
+    Packed8<T> kx[UNR];
+    float vx[UNR][8];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int ru = r + u * RL::RGB;
+      o[u] = ru < NR ? roff[ru] : -1;
+      if (o[u] >= 0) {
+        kx[u].load(K + o[u] + lr * 8);
+        Elem<T>::load8(V + o[u] + lr * 8, vx[u]);
+      }
     }
-    if (o2 >= 0) {
-      k2.load(K + o2 + lr * 8);
-      Elem<T>::load8(V + o2 + lr * 8, v2);
-    }
-    if (o1 >= 0) accumulate(k1, v1);
-    if (o2 >= 0) accumulate(k2, v2);
+#pragma unroll
+    for (int u = 0; u < UNR; ++u)
+      if (o[u] >= 0) accumulate(kx[u], vx[u]);
   }
   // merge the lane groups: common reference per head, then sums
   if (lr == 0)
@@ -231,7 +238,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
     int cap, int gran, int spi, int nsplit, float zscale, float2 *__restrict__ cand, int32_t *__restrict__ cand_cnt,
     float *__restrict__ cand_max) {
   using RL = RowLayout<D>;
-  extern __shared__ float zs[];  // [G][rps]
+  extern __shared__ float zs[];  // [G][rps] logits, then [rps] row offsets (8-byte aligned)
   __shared__ int scan_scratch[kAttnThreads / kWave + 1];
   __shared__ float redf[kAttnThreads / kWave];
   const int split = blockIdx.x, unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
@@ -262,14 +269,22 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
       if (lr == h % RL::LPR) zs[h * rps + r] = off >= 0 ? z : -INFINITY;
     }
   };
-  for (int r = rg; r < NR; r += 2 * RL::RGB) {
-    const int r2 = r + RL::RGB;
-    const long long o1 = row_off(r), o2 = row_off(r2);
-    Packed8<T> k1, k2;
-    if (o1 >= 0) k1.load(K + o1 + lr * 8);
-    if (o2 >= 0) k2.load(K + o2 + lr * 8);
-    logits(r, o1, k1);
-    if (r2 < NR) logits(r2, o2, k2);
+  long long *roff = reinterpret_cast<long long *>(zs + ((G * rps + 1) & ~1));
+  for (int r = tid; r < NR; r += kAttnThreads) roff[r] = row_off(r);
+  __syncthreads();
+  constexpr int UNR = 4;
+  for (int r = rg; r < NR; r += UNR * RL::RGB) {
+    long long o[UNR];
+    Packed8<T> kx[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int ru = r + u * RL::RGB;
+      o[u] = ru < NR ? roff[ru] : -1;
+      if (o[u] >= 0) kx[u].load(K + o[u] + lr * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u)
+      if (r + u * RL::RGB < NR) logits(r + u * RL::RGB, o[u], kx[u]);
   }
   __syncthreads();
   for (int h = 0; h < G; ++h) {
@@ -506,7 +521,9 @@ static hipError_t attn_typed(const AttnArgs &a, hipStream_t st) {
   const dim3 grid(a.nsplit, c.B * c.Hkv);
   if (a.alpha == 1.0f) {
     const float scale_log2 = a.sm_scale * 1.4426950408889634f;
-    SKV_ATTN_DISPATCH_G(c.G, attn_softmax_kernel<T, D, GG><<<grid, kAttnThreads, 0, st>>>(
+    const int rps_s = a.spi * (a.gran ? 1 : c.S);
+    const size_t lds_s = sizeof(long long) * (size_t)rps_s;
+    SKV_ATTN_DISPATCH_G(c.G, attn_softmax_kernel<T, D, GG><<<grid, kAttnThreads, lds_s, st>>>(
                                  c, q, a.sel_idx, a.sel_count, a.cap, a.gran, a.spi, a.nsplit, scale_log2, a.part, a.out))
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
@@ -514,7 +531,7 @@ static hipError_t attn_typed(const AttnArgs &a, hipStream_t st) {
     return hipGetLastError();
   }
   const int rps = a.spi * (a.gran ? 1 : c.S);
-  const size_t lds = sizeof(float) * (size_t)c.G * rps;
+  const size_t lds = sizeof(float) * (size_t)((c.G * rps + 1) & ~1) + sizeof(long long) * (size_t)rps;
   const float zscale = a.sm_scale * (a.alpha - 1.0f);
   SKV_ATTN_DISPATCH_G(c.G, attn_entmax_logits_kernel<T, D, GG><<<grid, kAttnThreads, lds, st>>>(
                                c, q, a.sel_idx, a.sel_count, a.cap, a.gran, a.spi, a.nsplit, zscale, a.cand,

@@ -123,6 +123,65 @@ __device__ __forceinline__ uint32_t f32_order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Key of one projected-key row (R bf16 values, as R/8 16-byte words) for the G query heads of a
+// unit: RN_f32(max_h sum_i q~_h[i] k~[i]), each sum in float64 over i ascending. The products of
+// q~ (a float32 value held in float64) and a bf16 value are exact, so every kernel that calls
+// this gets the same bits for the same token. qq points to q~ of the G heads, [G][R].
+template <int R, int G, typename QP>
+__device__ __forceinline__ float proj_row_key(const uint4 (&w)[R / 8], QP qq) {
+  double acc[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) acc[h] = 0.0;
+#pragma unroll
+  for (int i0 = 0; i0 < R / 8; ++i0) {
+    const uint32_t ww[4] = {w[i0].x, w[i0].y, w[i0].z, w[i0].w};
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) {
+      const double dx = (ii & 1) ? bf16_hi(ww[ii / 2]) : bf16_lo(ww[ii / 2]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc[h] = fma(qq[h * R + i0 * 8 + ii], dx, acc[h]);
+    }
+  }
+  double best = acc[0];
+#pragma unroll
+  for (int h = 1; h < G; ++h) best = fmax(best, acc[h]);
+  return (float)best;
+}
+
+// Projected-key row of token t of unit (b, g) (t < L): R/8 16-byte loads through the block table.
+template <int R>
+__device__ __forceinline__ void proj_row_load(const CacheView &c, const uint16_t *kproj, int b, int g, int t,
+                                              uint4 (&w)[R / 8]) {
+  const int phys = c.bt[(size_t)b * c.maxP + t / c.S];
+  const uint4 *row = reinterpret_cast<const uint4 *>(kproj + (((size_t)phys * c.Hkv + g) * c.S + t % c.S) * R);
+#pragma unroll
+  for (int i = 0; i < R / 8; ++i) w[i] = row[i];
+}
+
+// Layout of the token candidate set that the fused projected scoring writes and the token top-k
+// selection reads (one buffer, regions 256-byte aligned):
+//   hdr   kproj pointer (8 bytes) and the rank R (4 bytes), for the exact fallback of the selection
+//   bound [U] uint32     order key T_lo of each unit (candidates are the tokens with key >= T_lo)
+//   qt    [B*Hq*R] f64   projected queries q~
+//   count [U][NB] int32  candidates of each segment (NB = segments of kCandSegTokens tokens)
+//   seg   [U][NB][kCandSegTokens] float2 (key, token index bits), in token order
+constexpr int kCandSegTokens = 128;
+struct CandLayout {
+  size_t hdr, bound, qt, count, seg, total;
+  int nb;
+  __host__ __device__ static size_t align(size_t x) { return (x + 255) / 256 * 256; }
+  __host__ __device__ CandLayout(int B, int Hq, int Hkv, int Lmax, int R) {
+    const size_t U = (size_t)B * Hkv;
+    nb = (Lmax + kCandSegTokens - 1) / kCandSegTokens;
+    hdr = 0;
+    bound = align(hdr + 16);
+    qt = align(bound + sizeof(uint32_t) * U);
+    count = align(qt + sizeof(double) * (size_t)B * Hq * R);
+    seg = align(count + sizeof(int32_t) * U * nb);
+    total = align(seg + sizeof(float2) * U * nb * kCandSegTokens);
+  }
+};
+
 // ---------------------------------------------------------------- wave / block reductions
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

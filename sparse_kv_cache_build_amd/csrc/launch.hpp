@@ -31,6 +31,11 @@ hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, cons
                               float *s, float *shat, double *ws, hipStream_t st);
 hipError_t launch_score_proj(const CacheView &c, int dtype, const void *q, int r, const float *proj,
                              const uint16_t *kproj, float *key, double *ws, hipStream_t st);
+hipError_t launch_score_proj_cand(const CacheView &c, int r, const uint16_t *kproj, char *cand, hipStream_t st);
+hipError_t launch_token_bound(const CacheView &c, int dtype, const void *q, int k, int r, const float *proj,
+                              const uint16_t *kproj, char *cand, hipStream_t st);
+hipError_t launch_select_token_cand(const CacheView &c, int k, int r, const char *cand, int32_t *sel_idx,
+                                    int32_t *sel_count, int cap, hipStream_t st);
 hipError_t launch_select_topk(const CacheView &c, const float *key, int key_stride, int policy, int k, int pct,
                               int32_t *sel_idx, int32_t *sel_count, int cap, hipStream_t st);
 hipError_t launch_select_all(const CacheView &c, int tokens, int32_t *sel_idx, int32_t *sel_count, int cap,

@@ -152,42 +152,53 @@ __global__ __launch_bounds__(256) void score_proj_kernel(CacheView c, const uint
   const double *qq = qt + (size_t)(b * c.Hq + g * G) * R;
   uint4 w[kProjTPT][R / 8];
 #pragma unroll
-  for (int u = 0; u < kProjTPT; ++u) {
-    const int t = t0 + u * 256;
-    if (t < L) {
-      const int phys = c.bt[(size_t)b * c.maxP + t / c.S];
-      const uint4 *row = reinterpret_cast<const uint4 *>(kproj + (((size_t)phys * c.Hkv + g) * c.S + t % c.S) * R);
-#pragma unroll
-      for (int i = 0; i < R / 8; ++i) w[u][i] = row[i];
-    }
-  }
+  for (int u = 0; u < kProjTPT; ++u)
+    if (t0 + u * 256 < L) proj_row_load<R>(c, kproj, b, g, t0 + u * 256, w[u]);
 #pragma unroll
   for (int u = 0; u < kProjTPT; ++u) {
     const int t = t0 + u * 256;
     if (t >= Lmax) break;
-    float *out = key + (size_t)unit * Lmax + t;
-    if (t >= L) {
-      *out = -INFINITY;
-      continue;
-    }
-    double acc[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = 0.0;
-#pragma unroll
-    for (int i0 = 0; i0 < R / 8; ++i0) {
-      const uint32_t ww[4] = {w[u][i0].x, w[u][i0].y, w[u][i0].z, w[u][i0].w};
-#pragma unroll
-      for (int ii = 0; ii < 8; ++ii) {
-        const double dx = (ii & 1) ? bf16_hi(ww[ii / 2]) : bf16_lo(ww[ii / 2]);
-#pragma unroll
-        for (int h = 0; h < G; ++h) acc[h] = fma(qq[(size_t)h * R + i0 * 8 + ii], dx, acc[h]);
-      }
-    }
-    double best = acc[0];
-#pragma unroll
-    for (int h = 1; h < G; ++h) best = fmax(best, acc[h]);
-    *out = (float)best;
+    key[(size_t)unit * Lmax + t] = t < L ? proj_row_key<R, G>(w[u], qq) : -INFINITY;
   }
+}
+
+// Fused PROJ scoring for a token top-k: the same keys, but only tokens whose order key is >= the
+// unit's bound T_lo are written, as (key, token) pairs in token order into a candidate segment,
+// with the segment's count. Each wave owns one segment of kCandSegTokens consecutive tokens
+// (lane and lane + 64), compacts with ballots and needs no barrier.
+template <int R, int G>
+__global__ __launch_bounds__(256) void score_proj_cand_kernel(CacheView c, const uint16_t *__restrict__ kproj,
+                                                              const double *__restrict__ qt,
+                                                              const uint32_t *__restrict__ bound,
+                                                              int32_t *__restrict__ count, float2 *__restrict__ segs,
+                                                              int nb) {
+  static_assert(2 * kWave == kCandSegTokens, "a wave covers one candidate segment");
+  const int unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
+  const int L = seq_len(c, b);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int sid = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;   // segment of this wave
+  const int ts = sid * kCandSegTokens;
+  if (ts >= L || sid >= nb) return;
+  const double *qq = qt + (size_t)(b * c.Hq + g * G) * R;
+  const uint32_t Tlo = bound[unit];
+  uint4 w[2][R / 8];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (ts + u * kWave + lane < L) proj_row_load<R>(c, kproj, b, g, ts + u * kWave + lane, w[u]);
+  float2 *seg = segs + ((size_t)unit * nb + sid) * kCandSegTokens;
+  int base = 0;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int t = ts + u * kWave + lane;
+    const float kv = t < L ? proj_row_key<R, G>(w[u], qq) : 0.0f;
+    const bool keep = t < L && f32_order_key(kv) >= Tlo;
+    const uint64_t bal = __ballot(keep);
+    if (keep)
+      seg[base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] =
+          make_float2(kv, __int_as_float(t));
+    base += __popcll(bal);
+  }
+  if (lane == 0) count[(size_t)unit * nb + sid] = base;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -244,6 +255,28 @@ static hipError_t proj_r(const CacheView &c, const uint16_t *kproj, const double
   const dim3 grid((c.maxP * c.S + 256 * kProjTPT - 1) / (256 * kProjTPT), c.B * c.Hkv);
   SKV_DISPATCH_G(c.G, score_proj_kernel<R, GG><<<grid, 256, 0, st>>>(c, kproj, qt, key))
   return hipGetLastError();
+}
+
+template <int R>
+static hipError_t proj_cand_r(const CacheView &c, const uint16_t *kproj, char *cand, const CandLayout &lay,
+                              hipStream_t st) {
+  const dim3 grid((lay.nb + 3) / 4, c.B * c.Hkv);
+  SKV_DISPATCH_G(c.G, score_proj_cand_kernel<R, GG><<<grid, 256, 0, st>>>(
+                          c, kproj, reinterpret_cast<const double *>(cand + lay.qt),
+                          reinterpret_cast<const uint32_t *>(cand + lay.bound),
+                          reinterpret_cast<int32_t *>(cand + lay.count), reinterpret_cast<float2 *>(cand + lay.seg),
+                          lay.nb))
+  return hipGetLastError();
+}
+
+hipError_t launch_score_proj_cand(const CacheView &c, int r, const uint16_t *kproj, char *cand, hipStream_t st) {
+  const CandLayout lay(c.B, c.Hq, c.Hkv, c.maxP * c.S, 64);   // layout independent of the rank
+  switch (r) {
+    case 16: return proj_cand_r<16>(c, kproj, cand, lay, st);
+    case 32: return proj_cand_r<32>(c, kproj, cand, lay, st);
+    case 64: return proj_cand_r<64>(c, kproj, cand, lay, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_score_proj(const CacheView &c, int dtype, const void *q, int r, const float *proj,

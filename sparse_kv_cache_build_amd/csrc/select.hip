@@ -308,6 +308,174 @@ __global__ __launch_bounds__(kTokThreads) void select_topk_large_kernel(CacheVie
   ordered_take<kTokThreads>(gget, gidx, n, T, need, out, scan_scratch);
 }
 
+// ---------------------------------------------------------------- fused token top-k
+
+constexpr int kBoundSample = 2048;   // tokens scored per unit to place the candidate bound
+constexpr int kMaxCandBlocks = 8192; // candidate segments per unit the selection can gather (1M tokens)
+
+// Step 1 of the fused token top-k, one block per unit:
+//  - q~ of the unit's G heads (the same float64 sums as the projected-query prep), into the
+//    candidate set and LDS;
+//  - keys of 2048 sampled tokens (64 evenly spaced runs of 32), with the scorer's exact arithmetic;
+//  - T_lo = the r-th largest sampled key with its low 16 bits cleared (a lower bound),
+//    r = k * 2048 / L plus a 4-sigma margin. Short sequences (L <= 8192) or k >= L keep every token.
+template <typename T, int D, int R, int G>
+__global__ __launch_bounds__(256) void token_bound_kernel(CacheView c, const T *__restrict__ q, int k,
+                                                          const float *__restrict__ proj,
+                                                          const uint16_t *__restrict__ kproj, char *__restrict__ cand,
+                                                          CandLayout lay) {
+  constexpr int PER = kBoundSample / 256;   // sampled tokens per thread
+  __shared__ float ps[R][D + 1];            // P, padded rows
+  __shared__ float qf[G][D];
+  __shared__ double qs[G * R];
+  __shared__ uint32_t sk[kBoundSample];
+  __shared__ uint32_t hist[256 / kWave * 256];
+  __shared__ uint32_t bc[2];
+  const int unit = blockIdx.x, b = unit / c.Hkv, g = unit - b * c.Hkv;
+  const int tid = threadIdx.x;
+  if (unit == 0 && tid == 0) {
+    *reinterpret_cast<const uint16_t **>(cand + lay.hdr) = kproj;
+    *reinterpret_cast<int32_t *>(cand + lay.hdr + 8) = R;
+  }
+  const int L = seq_len(c, b);
+  const int kk = min(k, L);
+  const bool sample = !(kk >= L || L <= kTokCand);
+  // issue the sampled rows' loads first; they are used after q~ is ready
+  const int run = kBoundSample / 64, stride = L / 64;
+  uint4 w[PER][R / 8];
+  if (sample)
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int s = u * 256 + tid;
+      proj_row_load<R>(c, kproj, b, g, (s / run) * stride + s % run, w[u]);
+    }
+  for (int i = tid; i < R * D; i += 256) ps[i / D][i % D] = proj[i];
+  for (int i = tid; i < G * D; i += 256) qf[i / D][i % D] = Elem<T>::get(q + ((size_t)b * c.Hq + g * G) * D, i);
+  __syncthreads();
+  // q~ of the unit's G heads: the float64 sum over j ascending of P[i][j] q[j]
+  double *qt = reinterpret_cast<double *>(cand + lay.qt) + (size_t)(b * c.Hq + g * G) * R;
+  for (int i = tid; i < G * R; i += 256) {
+    const int h = i / R, ii = i - h * R;
+    double acc = 0.0;
+#pragma unroll 8
+    for (int j = 0; j < D; ++j) acc = fma((double)ps[ii][j], (double)qf[h][j], acc);
+    const double qd = (double)(float)acc;
+    qs[i] = qd;
+    qt[i] = qd;
+  }
+  __syncthreads();
+  uint32_t *bound = reinterpret_cast<uint32_t *>(cand + lay.bound);
+  if (!sample) {
+    if (tid == 0) bound[unit] = 0u;
+    return;
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    int zero = 0;
+    asm volatile("" : "+s"(zero));   // keeps the q~ reads from LDS per token (no hoisting)
+    sk[u * 256 + tid] = f32_order_key(proj_row_key<R, G>(w[u], qs + zero));
+  }
+  __syncthreads();
+  const double expect = (double)kk * kBoundSample / L;
+  const double rs = ceil(expect + 4.0 * sqrt(expect) + 16.0);
+  uint32_t Tlo = 0, need;
+  if (rs < kBoundSample) {
+    auto get = [&](int i) { return sk[i]; };
+    radix_kth<256>(get, kBoundSample, (uint32_t)rs, hist, bc, Tlo, need, 2);
+  }
+  if (tid == 0) bound[unit] = Tlo;
+}
+
+// Step 3 of the fused token top-k, one block per unit: gather the unit's candidate segments in
+// segment order (so in token order) into LDS and select exactly there.
+// When fewer than k candidates arrived, or more than LDS holds, every key of the unit is
+// recomputed from the projected keys (same arithmetic) and selected by radix over global memory.
+template <int G>
+__global__ __launch_bounds__(kTokThreads) void select_token_cand_kernel(CacheView c, int k,
+                                                                        const char *__restrict__ cand, CandLayout lay,
+                                                                        int32_t *__restrict__ sel_idx,
+                                                                        int32_t *__restrict__ sel_count, int cap) {
+  __shared__ uint32_t ckey[kTokCand];
+  __shared__ int32_t cidx[kTokCand];
+  __shared__ int soff[kMaxCandBlocks + 1];
+  __shared__ uint32_t hist[kTokWaves * 256];
+  __shared__ uint32_t bc[2];
+  __shared__ int scan_scratch[kTokWaves + 1];
+  const int unit = blockIdx.x, b = unit / c.Hkv, g = unit - b * c.Hkv;
+  const int n = seq_len(c, b);
+  const int kk = min(k, n);
+  int32_t *out = sel_idx + (size_t)unit * cap;
+  const int tid = threadIdx.x;
+  if (tid == 0) sel_count[unit] = kk;
+  if (kk <= 0) return;
+  if (kk >= n) {
+    for (int i = tid; i < n; i += kTokThreads) out[i] = i;
+    return;
+  }
+  const int nb = (n + kCandSegTokens - 1) / kCandSegTokens;
+  const int32_t *cnt = reinterpret_cast<const int32_t *>(cand + lay.count) + (size_t)unit * lay.nb;
+  const float2 *seg = reinterpret_cast<const float2 *>(cand + lay.seg) + (size_t)unit * lay.nb * kCandSegTokens;
+  int base = 0;
+  for (int s0 = 0; s0 < nb; s0 += kTokThreads) {
+    const int s = s0 + tid;
+    const int v = s < nb ? cnt[s] : 0;
+    int tot;
+    const int ex = block_excl_scan<kTokThreads>(v, scan_scratch, &tot);
+    if (s < nb) soff[s] = base + ex;
+    base += tot;
+  }
+  if (tid == 0) soff[nb] = base;
+  __syncthreads();
+  const int total = base;
+  uint32_t T, need;
+  if (total >= kk && total <= kTokCand) {
+    for (int f = tid; f < total; f += kTokThreads) {
+      int lo = 0, hi = nb - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (soff[mid] <= f) lo = mid; else hi = mid - 1;
+      }
+      const float2 e = seg[(size_t)lo * kCandSegTokens + (f - soff[lo])];
+      ckey[f] = f32_order_key(e.x);
+      cidx[f] = __float_as_int(e.y);
+    }
+    __syncthreads();
+    auto lget = [&](int i) { return ckey[i]; };
+    auto lidx = [&](int i) { return cidx[i]; };
+    radix_kth<kTokThreads>(lget, total, (uint32_t)kk, hist, bc, T, need);
+    ordered_take<kTokThreads>(lget, lidx, total, T, need, out, scan_scratch);
+    return;
+  }
+  // exact fallback: recompute every key of the unit
+  const uint16_t *kproj = *reinterpret_cast<const uint16_t *const *>(cand + lay.hdr);
+  const int R = *reinterpret_cast<const int32_t *>(cand + lay.hdr + 8);
+  const double *qq = reinterpret_cast<const double *>(cand + lay.qt) + (size_t)(b * c.Hq + g * G) * R;
+  auto gget = [&](int t) -> uint32_t {
+    const int phys = c.bt[(size_t)b * c.maxP + t / c.S];
+    const uint4 *row = reinterpret_cast<const uint4 *>(kproj + (((size_t)phys * c.Hkv + g) * c.S + t % c.S) * R);
+    double acc[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) acc[h] = 0.0;
+    for (int i0 = 0; i0 < R / 8; ++i0) {
+      const uint4 w = row[i0];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) {
+        const double dx = (ii & 1) ? bf16_hi(ww[ii / 2]) : bf16_lo(ww[ii / 2]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h] = fma(qq[h * R + i0 * 8 + ii], dx, acc[h]);
+      }
+    }
+    double best = acc[0];
+#pragma unroll
+    for (int h = 1; h < G; ++h) best = fmax(best, acc[h]);
+    return f32_order_key((float)best);
+  };
+  auto gidx = [](int i) { return i; };
+  radix_kth<kTokThreads>(gget, n, (uint32_t)kk, hist, bc, T, need);
+  ordered_take<kTokThreads>(gget, gidx, n, T, need, out, scan_scratch);
+}
+
 // Every page (or token) of the sequence.
 __global__ void select_all_kernel(CacheView c, int tokens, int32_t *__restrict__ sel_idx,
                                   int32_t *__restrict__ sel_count, int cap) {
@@ -424,6 +592,53 @@ hipError_t launch_select_topk(const CacheView &c, const float *key, int key_stri
   else
     select_topk_kernel<<<c.B * c.Hkv, kSelThreads, 0, st>>>(c, key, key_stride, policy, k, pct, sel_idx, sel_count,
                                                             cap);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int R>
+static hipError_t token_bound_r(const CacheView &c, const void *q, int k, const float *proj, const uint16_t *kproj,
+                                char *cand, const CandLayout &lay, hipStream_t st) {
+  switch (c.G) {
+    case 1: token_bound_kernel<T, D, R, 1><<<c.B * c.Hkv, 256, 0, st>>>(c, static_cast<const T *>(q), k, proj, kproj, cand, lay); break;
+    case 2: token_bound_kernel<T, D, R, 2><<<c.B * c.Hkv, 256, 0, st>>>(c, static_cast<const T *>(q), k, proj, kproj, cand, lay); break;
+    case 4: token_bound_kernel<T, D, R, 4><<<c.B * c.Hkv, 256, 0, st>>>(c, static_cast<const T *>(q), k, proj, kproj, cand, lay); break;
+    case 8: token_bound_kernel<T, D, R, 8><<<c.B * c.Hkv, 256, 0, st>>>(c, static_cast<const T *>(q), k, proj, kproj, cand, lay); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t token_bound_d(const CacheView &c, const void *q, int k, int r, const float *proj,
+                                const uint16_t *kproj, char *cand, const CandLayout &lay, hipStream_t st) {
+  switch (r) {
+    case 16: return token_bound_r<T, D, 16>(c, q, k, proj, kproj, cand, lay, st);
+    case 32: return token_bound_r<T, D, 32>(c, q, k, proj, kproj, cand, lay, st);
+    case 64: return token_bound_r<T, D, 64>(c, q, k, proj, kproj, cand, lay, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_token_bound(const CacheView &c, int dtype, const void *q, int k, int r, const float *proj,
+                              const uint16_t *kproj, char *cand, hipStream_t st) {
+  const CandLayout lay(c.B, c.Hq, c.Hkv, c.maxP * c.S, 64);   // layout independent of the rank
+  if (dtype == 0)
+    return c.D == 64 ? token_bound_d<float, 64>(c, q, k, r, proj, kproj, cand, lay, st)
+                     : token_bound_d<float, 128>(c, q, k, r, proj, kproj, cand, lay, st);
+  return c.D == 64 ? token_bound_d<uint16_t, 64>(c, q, k, r, proj, kproj, cand, lay, st)
+                   : token_bound_d<uint16_t, 128>(c, q, k, r, proj, kproj, cand, lay, st);
+}
+
+hipError_t launch_select_token_cand(const CacheView &c, int k, int r, const char *cand, int32_t *sel_idx,
+                                    int32_t *sel_count, int cap, hipStream_t st) {
+  const CandLayout lay(c.B, c.Hq, c.Hkv, c.maxP * c.S, 64);   // layout independent of the rank
+  switch (c.G) {
+    case 1: select_token_cand_kernel<1><<<c.B * c.Hkv, kTokThreads, 0, st>>>(c, k, cand, lay, sel_idx, sel_count, cap); break;
+    case 2: select_token_cand_kernel<2><<<c.B * c.Hkv, kTokThreads, 0, st>>>(c, k, cand, lay, sel_idx, sel_count, cap); break;
+    case 4: select_token_cand_kernel<4><<<c.B * c.Hkv, kTokThreads, 0, st>>>(c, k, cand, lay, sel_idx, sel_count, cap); break;
+    case 8: select_token_cand_kernel<8><<<c.B * c.Hkv, kTokThreads, 0, st>>>(c, k, cand, lay, sel_idx, sel_count, cap); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -43,13 +43,15 @@ class GpuStep:
     outs: dict = field(default_factory=dict)
 
 
-def gpu_step(w: W.Workload, alphas=None, split=0, policy=None, cap=None) -> GpuStep:
+def gpu_step(w: W.Workload, alphas=None, split=0, policy=None, cap=None, fused=False) -> GpuStep:
+    """fused: projected token scores kept only as the candidate set of the top-k (no dense keys)."""
     cfg = w.cfg
     cache = skv.PagedCache(w.k, w.v, w.block_table, w.seq_lens, w.Hq)
     kind = cfg["score"]
     meta = skv.build_page_meta(cache, (kind,), proj=w.proj)
-    scores = skv.score_pages(cache, meta, w.q, kind)
     pol = policy or cfg["policy"]
+    token_k = cfg.get("k", 0) if (fused and kind == "proj" and pol == "token_topk") else 0
+    scores = skv.score_pages(cache, meta, w.q, kind, token_k=token_k)
     sel = skv.select_pages(cache, scores, pol, k=cfg.get("k", 0), budget_pct=cfg.get("pct", 0),
                            alpha=cfg.get("sel_alpha", 1.5), delta=cfg.get("delta", 0.0),
                            tokens=1 if kind == "proj" else 0, cap=cap)

@@ -69,6 +69,33 @@ def test_full_cache_comparator(dev, name, alpha):
     H.compare(w, st, alphas=(alpha,), check_meta=False)
 
 
+@pytest.mark.parametrize("over", [dict(B=2, L=20000, k=512), dict(B=2, L=5000, k=512),
+                                  dict(B=3, lens=[0, 9000, 40000], k=2048), dict(B=2, lens=[1500, 30000], k=1000)])
+def test_fused_token_topk_matches_oracle(dev, over):
+    """Projected scoring kept as the candidate set of the top-k (no dense keys) selects the same tokens."""
+    H.log(f"[parity fused token top-k] {over}")
+    w = W.make("token128k", device=dev, **over)
+    st = H.gpu_step(w, fused=True)
+    assert st.scores.key is None
+    H.compare(w, st)
+
+
+def test_fused_token_topk_falls_back_when_the_sample_misleads(dev):
+    """Keys of every sampled position are zeroed, so the sampled bound admits about half of all
+    tokens (more than the candidate buffer holds): the selection must re-score every token and still
+    match the oracle."""
+    H.log("[parity fused token top-k fallback]")
+    L = 20000
+    w = W.make("token128k", device=dev, B=2, L=L, k=512)
+    run, stride = 2048 // 64, L // 64
+    pos = [(s // run) * stride + s % run for s in range(2048)]
+    for b in range(w.B):
+        for t in pos:
+            w.k[int(w.block_table[b, t // w.S]), :, t % w.S, :] = 0
+    st = H.gpu_step(w, fused=True)
+    H.compare(w, st)
+
+
 def test_k_at_least_pages_and_tokens_selects_all(dev):
     H.log("[edge] k >= P_b, k >= L_b")
     w = W.make("gqa32k", device=dev, B=2, lens=[700, 33], k=400)
@@ -111,7 +138,7 @@ def test_determinism(dev):
 def test_full_size_sampled(dev, name):
     H.log(f"[parity full size] {name}")
     w = W.make(name, device=dev)
-    st = H.gpu_step(w)
+    st = H.gpu_step(w, fused=True)   # the benchmark's configuration (fused for token top-k)
     seqs = FULL_SAMPLE[name]
     if seqs == "ends":
         order = np.argsort(w.lens)
