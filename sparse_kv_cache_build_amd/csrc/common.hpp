@@ -148,6 +148,57 @@ __device__ __forceinline__ float proj_row_key(const uint4 (&w)[R / 8], QP qq) {
   return (float)best;
 }
 
+// Approximate projected key for the token candidate filter. With qb the bf16 rounding of q~ and
+// k the bf16 row, a_h = sum_j qb_hj k_j is evaluated by v_dot2_f32_bf16 (bf16 products are exact
+// in float32, the sums are float32) and n1 = sum_j |k_j| the same way. The exact key of every
+// head then satisfies |key_h - a_h| <= rel * n1 + abs with the coefficients of filter_coef:
+//  - rounding q~ to bf16 moves each product by at most 2^-9 |q~_j k_j|;
+//  - a dot2 step rounds at most twice, so the float32 sums are off by at most (R + 2) 2^-24
+//    sum_j |q~_j k_j|; the float64 sum of the exact key and its rounding to float add less
+//    than 2^-23 of it; for R <= 64 all of this stays below 2^-8.9 sum_j |q~_j k_j|;
+//  - sum_j |q~_j k_j| <= max|q~| n1, with n1 low by at most a factor 1 - 2^-18;
+//  so rel = 2^-8 max|q~| covers the relative part with a factor of two to spare. The absolute
+//  terms cover subnormal inputs, products or sums flushed to zero (below R 2^-126 (max|q~| + 1)).
+// max|q~| >= 2^127 could round a bf16 q~ to infinity: rel is then infinite and every token passes.
+struct FilterCoef {
+  float rel, abs;
+};
+__device__ __forceinline__ FilterCoef filter_coef(float qmax) {
+  FilterCoef f;
+  f.rel = qmax < 0x1p127f ? qmax * 0x1p-8f + 0x1p-125f : INFINITY;
+  f.abs = qmax * 0x1p-119f + 0x1p-100f;
+  return f;
+}
+
+// Upper estimate of the projected key of one row (max over the G heads): a + rel * n1 + abs, or
+// +infinity when that bound is not finite and below 2^118 (no float32 overflow is then possible in
+// a) or the estimate is NaN. qp holds the unit's G * R/2 bf16 pairs of q~.
+template <int R, int G>
+__device__ __forceinline__ float proj_row_upper(const uint4 (&w)[R / 8], const uint32_t *qp, FilterCoef fc) {
+  float acc[G], n1 = 0.0f;
+#pragma unroll
+  for (int h = 0; h < G; ++h) acc[h] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < R / 8; ++i) {
+    const uint32_t ww[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        acc[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qp[h * (R / 2) + i * 4 + p]),
+                                                 __builtin_bit_cast(bf16x2_t, ww[p]), acc[h], false);
+      n1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ww[p] & 0x7fff7fffu),
+                                           __builtin_bit_cast(bf16x2_t, 0x3f803f80u), n1, false);
+    }
+  }
+  float a = acc[0];
+#pragma unroll
+  for (int h = 1; h < G; ++h) a = fmaxf(a, acc[h]);
+  const float e = fmaf(fc.rel, n1, fc.abs);
+  const float hi = a + e;
+  return (e < 0x1p118f && hi == hi) ? hi : INFINITY;
+}
+
 // Projected-key row of token t of unit (b, g) (t < L): R/8 16-byte loads through the block table.
 template <int R>
 __device__ __forceinline__ void proj_row_load(const CacheView &c, const uint16_t *kproj, int b, int g, int t,
@@ -162,12 +213,14 @@ __device__ __forceinline__ void proj_row_load(const CacheView &c, const uint16_t
 // selection reads (one buffer, regions 256-byte aligned):
 //   hdr   kproj pointer (8 bytes) and the rank R (4 bytes), for the exact fallback of the selection
 //   bound [U] uint32     order key T_lo of each unit (candidates are the tokens with key >= T_lo)
-//   qt    [B*Hq*R] f64   projected queries q~
-//   count [U][NB] int32  candidates of each segment (NB = segments of kCandSegTokens tokens)
+//   qt    [B*Hq*R] f64   projected queries q~ (float values)
+//   qb    [B*Hq*R] bf16  q~ rounded to bf16, for the approximate filter of the scorer
+//   qc    [U][2] float   the filter's error-bound coefficients of each unit
+//   count [U][NB] int32  candidates of each group (NB = groups of kCandSegTokens tokens)
 //   seg   [U][NB][kCandSegTokens] float2 (key, token index bits), in token order
-constexpr int kCandSegTokens = 128;
+constexpr int kCandSegTokens = 1024;
 struct CandLayout {
-  size_t hdr, bound, qt, count, seg, total;
+  size_t hdr, bound, qt, qb, qc, count, seg, total;
   int nb;
   __host__ __device__ static size_t align(size_t x) { return (x + 255) / 256 * 256; }
   __host__ __device__ CandLayout(int B, int Hq, int Hkv, int Lmax, int R) {
@@ -176,7 +229,9 @@ struct CandLayout {
     hdr = 0;
     bound = align(hdr + 16);
     qt = align(bound + sizeof(uint32_t) * U);
-    count = align(qt + sizeof(double) * (size_t)B * Hq * R);
+    qb = align(qt + sizeof(double) * (size_t)B * Hq * R);
+    qc = align(qb + sizeof(uint16_t) * (size_t)B * Hq * R);
+    count = align(qc + sizeof(float) * 2 * U);
     seg = align(count + sizeof(int32_t) * U * nb);
     total = align(seg + sizeof(float2) * U * nb * kCandSegTokens);
   }
@@ -209,16 +264,19 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: row_shr 1, 2, 4, 8 scan each
+// row of 16 lanes (lanes without a source add 0), row_bcast:15 adds the last lane of rows 0 and 2
+// into rows 1 and 3, row_bcast:31 adds lane 31 into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);
   return v;
 }
+__device__ __forceinline__ int wave_incl_scan(int v) { return (int)wave_incl_scan((uint32_t)v); }
 
 // Block-wide exclusive prefix sum for blocks of NT threads (NT a multiple of 64, <= 1024).
 // `scratch` holds NT/64 + 1 ints of shared memory. Returns the exclusive prefix; *total gets the
@@ -227,23 +285,19 @@ template <int NT>
 __device__ __forceinline__ int block_excl_scan(int v, int *scratch, int *total) {
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  int incl = wave_incl_scan(v);
+  const int incl = wave_incl_scan(v);
   if (lane == kWave - 1) scratch[w] = incl;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < NW; ++i) {
-      int t = scratch[i];
-      scratch[i] = run;
-      run += t;
-    }
-    scratch[NW] = run;
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {   // independent broadcast reads of the wave totals
+    const int t = scratch[i];
+    before += i < w ? t : 0;
+    tot += t;
   }
-  __syncthreads();
-  int res = scratch[w] + incl - v;
-  *total = scratch[NW];
-  __syncthreads();
-  return res;
+  *total = tot;
+  __syncthreads();   // scratch is reused by the next call
+  return before + incl - v;
 }
 
 template <int NT>

@@ -162,43 +162,102 @@ __global__ __launch_bounds__(256) void score_proj_kernel(CacheView c, const uint
   }
 }
 
-// Fused PROJ scoring for a token top-k: the same keys, but only tokens whose order key is >= the
-// unit's bound T_lo are written, as (key, token) pairs in token order into a candidate segment,
-// with the segment's count. Each wave owns one segment of kCandSegTokens consecutive tokens
-// (lane and lane + 64), compacts with ballots and needs no barrier.
+// Fused PROJ scoring for a token top-k. Only tokens whose exact key has order key >= the unit's
+// bound T_lo are written, as (key, token) pairs in token order into the candidate segment of
+// their group, with the group's count. One wave per group of kCandSegTokens consecutive tokens,
+// in steps of 128 (two rows per lane; the next step's rows are loaded while the current step is
+// filtered):
+//  1. filter: each token's upper estimate of its key (proj_row_upper, bf16 dot2 with an error
+//     bound) against T_lo; tokens that pass go, in token order, into the wave's LDS list;
+//  2. exact: the listed tokens, 64 at a time, get the exact key (rows read again, mostly from L2)
+//     and the ones with order key >= T_lo are compacted into the segment with ballots.
+// The estimate never falls below the exact key, so the filter loses no token of the exact set;
+// it only spares the float64 arithmetic for the tokens that cannot reach T_lo.
 template <int R, int G>
 __global__ __launch_bounds__(256) void score_proj_cand_kernel(CacheView c, const uint16_t *__restrict__ kproj,
                                                               const double *__restrict__ qt,
+                                                              const uint32_t *__restrict__ qb,
+                                                              const float2 *__restrict__ qc,
                                                               const uint32_t *__restrict__ bound,
                                                               int32_t *__restrict__ count, float2 *__restrict__ segs,
                                                               int nb) {
-  static_assert(2 * kWave == kCandSegTokens, "a wave covers one candidate segment");
+  constexpr int GT = kCandSegTokens, STEP = 2 * kWave, NST = GT / STEP;
+  __shared__ int cl[256 / kWave][GT];
   const int unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
   const int L = seq_len(c, b);
-  const int lane = threadIdx.x & (kWave - 1);
-  const int sid = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;   // segment of this wave
-  const int ts = sid * kCandSegTokens;
-  if (ts >= L || sid >= nb) return;
-  const double *qq = qt + (size_t)(b * c.Hq + g * G) * R;
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  const int gid = blockIdx.x * (256 / kWave) + wv;   // group of this wave
+  const int tg = gid * GT;
+  if (tg >= L || gid >= nb) return;
+  const uint32_t *qp = qb + (size_t)(b * c.Hq + g * G) * (R / 2);
   const uint32_t Tlo = bound[unit];
-  uint4 w[2][R / 8];
+  const float2 cf = qc[unit];
+  const FilterCoef fc{cf.x, cf.y};
+  const bool pow2 = (c.S & (c.S - 1)) == 0;   // uniform: shifts instead of divisions
+  const int sh = 31 - __clz(c.S);
+  auto rowp = [&](int t) -> const uint4 * {
+    int pg, in;
+    if (pow2) {
+      pg = t >> sh;
+      in = t & (c.S - 1);
+    } else {
+      pg = t / c.S;
+      in = t - pg * c.S;
+    }
+    const int phys = c.bt[(size_t)b * c.maxP + pg];
+    return reinterpret_cast<const uint4 *>(kproj + (((size_t)phys * c.Hkv + g) * c.S + in) * R);
+  };
+  auto load = [&](int s, uint4 (&x)[2][R / 8]) {
+    const int ts = tg + s * STEP;
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-    if (ts + u * kWave + lane < L) proj_row_load<R>(c, kproj, b, g, ts + u * kWave + lane, w[u]);
-  float2 *seg = segs + ((size_t)unit * nb + sid) * kCandSegTokens;
+    for (int u = 0; u < 2; ++u) {
+      const uint4 *row = rowp(min(ts + u * kWave + lane, L - 1));
+#pragma unroll
+      for (int i = 0; i < R / 8; ++i) x[u][i] = row[i];
+    }
+  };
+  int nc = 0;
+  auto filter = [&](int s, const uint4 (&x)[2][R / 8]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = tg + s * STEP + u * kWave + lane;
+      const bool keep = t < L && f32_order_key(proj_row_upper<R, G>(x[u], qp, fc)) >= Tlo;
+      const uint64_t bal = __ballot(keep);
+      if (keep)
+        cl[wv][nc + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] = t;
+      nc += __popcll(bal);
+    }
+  };
+  const int nst = min(NST, (L - tg + STEP - 1) / STEP);
+  uint4 w0[2][R / 8], w1[2][R / 8];
+  load(0, w0);
+  for (int s = 0; s < nst; s += 2) {   // ping-pong buffers: no dynamic register indexing
+    if (s + 1 < nst) load(s + 1, w1);
+    filter(s, w0);
+    if (s + 1 >= nst) break;
+    if (s + 2 < nst) load(s + 2, w0);
+    filter(s + 1, w1);
+  }
+  __builtin_amdgcn_wave_barrier();
+  const double *qq = qt + (size_t)(b * c.Hq + g * G) * R;
+  float2 *seg = segs + ((size_t)unit * nb + gid) * GT;
   int base = 0;
+  for (int i0 = 0; i0 < nc; i0 += kWave) {
+    const int i = i0 + lane;
+    const int t = i < nc ? cl[wv][i] : tg;
+    uint4 x[R / 8];
+    const uint4 *row = rowp(t);
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int t = ts + u * kWave + lane;
-    const float kv = t < L ? proj_row_key<R, G>(w[u], qq) : 0.0f;
-    const bool keep = t < L && f32_order_key(kv) >= Tlo;
+    for (int j = 0; j < R / 8; ++j) x[j] = row[j];
+    const float kv = proj_row_key<R, G>(x, qq);
+    const bool keep = i < nc && f32_order_key(kv) >= Tlo;
     const uint64_t bal = __ballot(keep);
     if (keep)
       seg[base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] =
           make_float2(kv, __int_as_float(t));
     base += __popcll(bal);
   }
-  if (lane == 0) count[(size_t)unit * nb + sid] = base;
+  if (lane == 0) count[(size_t)unit * nb + gid] = base;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -263,6 +322,8 @@ static hipError_t proj_cand_r(const CacheView &c, const uint16_t *kproj, char *c
   const dim3 grid((lay.nb + 3) / 4, c.B * c.Hkv);
   SKV_DISPATCH_G(c.G, score_proj_cand_kernel<R, GG><<<grid, 256, 0, st>>>(
                           c, kproj, reinterpret_cast<const double *>(cand + lay.qt),
+                          reinterpret_cast<const uint32_t *>(cand + lay.qb),
+                          reinterpret_cast<const float2 *>(cand + lay.qc),
                           reinterpret_cast<const uint32_t *>(cand + lay.bound),
                           reinterpret_cast<int32_t *>(cand + lay.count), reinterpret_cast<float2 *>(cand + lay.seg),
                           lay.nb))

@@ -43,15 +43,24 @@ __device__ __forceinline__ SelSize sel_size(const CacheView &c, int b, int polic
 // `hist` holds NT/64 * 256 words, `bc` 2 words of shared memory. Every thread must call it.
 // With digits < 4 only the leading digits are resolved: T then has its low bits cleared, which
 // makes it a lower bound of the r-th largest key with at least r keys >= T.
+// When every key lies in [lo, hi], the leading digits that lo and hi share are common to all keys
+// and need no pass: a candidate set drawn from above a bound has one or two in front.
 template <int NT, typename Get>
 __device__ void radix_kth(Get get, int n, uint32_t r, uint32_t *hist, uint32_t *bc, uint32_t &T, uint32_t &need,
-                          int digits = 4) {
+                          int digits = 4, uint32_t lo = 0u, uint32_t hi = 0xffffffffu) {
   constexpr int NW = NT / kWave;
   const int tid = threadIdx.x;
   uint32_t *mine = hist + (tid / kWave) * 256;
-  uint32_t prefix = 0, mask = 0;
+  const int last = 32 - 8 * digits;
+  int first = 24;
+  uint32_t mask = 0;
+  while (first >= last && ((lo ^ hi) >> first) == 0) {
+    mask |= 0xffu << first;
+    first -= 8;
+  }
+  uint32_t prefix = lo & mask;
   need = r;
-  for (int shift = 24; shift >= 32 - 8 * digits; shift -= 8) {
+  for (int shift = first; shift >= last; shift -= 8) {
     for (int i = tid; i < NW * 256; i += NT) hist[i] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += NT) {
@@ -61,22 +70,87 @@ __device__ void radix_kth(Get get, int n, uint32_t r, uint32_t *hist, uint32_t *
     __syncthreads();
     // the wanted digit v has count(> v) < need <= count(>= v); lane l owns digits 4l .. 4l+3
     if (tid < kWave) {
-      uint32_t c4[4], local = 0;
+      uint32_t c4[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t cnt = 0;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) cnt += hist[w * 256 + 4 * tid + i];
-        c4[i] = cnt;
-        local += cnt;
+      for (int w = 0; w < NW; ++w) {   // one 16-byte read per wave histogram (no bank conflicts)
+        const uint4 h4 = reinterpret_cast<const uint4 *>(hist + w * 256)[tid];
+        c4[0] += h4.x;
+        c4[1] += h4.y;
+        c4[2] += h4.z;
+        c4[3] += h4.w;
       }
-      uint32_t incl = local;  // inclusive suffix sum over lanes (higher lanes: larger digits)
+      const uint32_t local = c4[0] + c4[1] + c4[2] + c4[3];
+      // keys in the digits of higher lanes: the wave total minus the inclusive prefix
+      const uint32_t pre = wave_incl_scan(local);
+      uint32_t above = __builtin_amdgcn_readlane(pre, kWave - 1) - pre;
 #pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t t = __shfl_down(incl, o, kWave);
-        if (tid + o < kWave) incl += t;
+      for (int i = 3; i >= 0; --i) {
+        if (above < need && above + c4[i] >= need) {
+          bc[0] = prefix | ((uint32_t)(4 * tid + i) << shift);
+          bc[1] = need - above;
+        }
+        above += c4[i];
       }
-      uint32_t above = incl - local;
+    }
+    __syncthreads();
+    prefix = bc[0];
+    need = bc[1];
+    mask |= 0xffu << shift;
+    __syncthreads();
+  }
+  T = prefix;
+}
+
+// radix_kth over keys a thread holds in registers: slot j of thread t is key i = t + j * NT (valid
+// when i < n). The keys are read once, not per pass, and within a wave the lanes whose digit
+// equals the first active lane's are counted with one atomic (the leading digits of a candidate
+// set fall into few bins, where per-lane atomics on one address serialize).
+template <int NT, int KPT>
+__device__ void radix_kth_regs(const uint32_t (&u)[KPT], int n, uint32_t r, uint32_t *hist, uint32_t *bc,
+                               uint32_t &T, uint32_t &need, int digits, uint32_t lo, uint32_t hi) {
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  uint32_t *mine = hist + (tid / kWave) * 256;
+  const int last = 32 - 8 * digits;
+  int first = 24;
+  uint32_t mask = 0;
+  while (first >= last && ((lo ^ hi) >> first) == 0) {
+    mask |= 0xffu << first;
+    first -= 8;
+  }
+  uint32_t prefix = lo & mask;
+  need = r;
+  for (int shift = first; shift >= last; shift -= 8) {
+    for (int i = tid; i < NW * 256; i += NT) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const bool in = tid + j * NT < n && (u[j] & mask) == prefix;
+      const uint32_t d = (u[j] >> shift) & 0xffu;
+      const uint64_t act = __ballot(in);
+      if (act != 0) {
+        const int leader = __ffsll((unsigned long long)act) - 1;
+        const uint32_t ld = __builtin_amdgcn_readlane(d, leader);
+        const uint64_t same = __ballot(in && d == ld);
+        if (lane == leader) atomicAdd(&mine[ld], (uint32_t)__popcll(same));
+        if (in && d != ld) atomicAdd(&mine[d], 1u);
+      }
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      uint32_t c4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {   // one 16-byte read per wave histogram (no bank conflicts)
+        const uint4 h4 = reinterpret_cast<const uint4 *>(hist + w * 256)[tid];
+        c4[0] += h4.x;
+        c4[1] += h4.y;
+        c4[2] += h4.z;
+        c4[3] += h4.w;
+      }
+      const uint32_t local = c4[0] + c4[1] + c4[2] + c4[3];
+      // keys in the digits of higher lanes: the wave total minus the inclusive prefix
+      const uint32_t pre = wave_incl_scan(local);
+      uint32_t above = __builtin_amdgcn_readlane(pre, kWave - 1) - pre;
 #pragma unroll
       for (int i = 3; i >= 0; --i) {
         if (above < need && above + c4[i] >= need) {
@@ -125,7 +199,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(CacheView c, c
                                                                   int32_t *__restrict__ sel_idx,
                                                                   int32_t *__restrict__ sel_count, int cap) {
   __shared__ uint32_t skeys[kSelLds];
-  __shared__ uint32_t hist[kSelThreads / kWave * 256];
+  __shared__ __align__(16) uint32_t hist[kSelThreads / kWave * 256];
   __shared__ uint32_t bc[2];
   __shared__ int scan_scratch[kSelThreads / kWave + 1];
   const int unit = blockIdx.x, b = unit / c.Hkv;
@@ -173,7 +247,7 @@ __global__ __launch_bounds__(kTokThreads) void select_topk_large_kernel(CacheVie
                                                                         int32_t *__restrict__ sel_count, int cap) {
   __shared__ uint32_t ckey[kTokCand];
   __shared__ int32_t cidx[kTokCand];
-  __shared__ uint32_t hist[kTokWaves * 256];
+  __shared__ __align__(16) uint32_t hist[kTokWaves * 256];
   __shared__ uint32_t bc[2];
   __shared__ int scan_scratch[kTokWaves + 1];
   __shared__ int seg_cnt[kTokWaves];
@@ -315,21 +389,31 @@ constexpr int kMaxCandBlocks = 8192; // candidate segments per unit the selectio
 
 // Step 1 of the fused token top-k, one block per unit:
 //  - q~ of the unit's G heads (the same float64 sums as the projected-query prep), into the
-//    candidate set and LDS;
-//  - keys of 2048 sampled tokens (64 evenly spaced runs of 32), with the scorer's exact arithmetic;
-//  - T_lo = the r-th largest sampled key with its low 16 bits cleared (a lower bound),
-//    r = k * 2048 / L plus a 4-sigma margin. Short sequences (L <= 8192) or k >= L keep every token.
+//    candidate set;
+//  - q~ rounded to bf16 and the error-bound coefficients of the approximate key (filter_coef),
+//    for the scorer's filter;
+//  - 2048 sampled tokens (64 evenly spaced runs of 32) get a lower estimate of their key: the
+//    approximate key minus its error bound;
+//  - T_lo = the r-th largest estimate with its low 16 bits cleared, r = k * 2048 / L plus a
+//    4-sigma margin. Short sequences (L <= 8192) or k >= L keep every token.
+// T_lo only steers how many candidates the scorer keeps: the selection certifies it by counting
+// (at least k exact keys >= T_lo) and otherwise recomputes the unit exactly.
+constexpr int kBoundThreads = 1024;
 template <typename T, int D, int R, int G>
-__global__ __launch_bounds__(256) void token_bound_kernel(CacheView c, const T *__restrict__ q, int k,
-                                                          const float *__restrict__ proj,
-                                                          const uint16_t *__restrict__ kproj, char *__restrict__ cand,
-                                                          CandLayout lay) {
-  constexpr int PER = kBoundSample / 256;   // sampled tokens per thread
+__global__ __launch_bounds__(kBoundThreads) void token_bound_kernel(CacheView c, const T *__restrict__ q, int k,
+                                                                   const float *__restrict__ proj,
+                                                                   const uint16_t *__restrict__ kproj,
+                                                                   char *__restrict__ cand, CandLayout lay) {
+  constexpr int NT = kBoundThreads;
+  constexpr int PER = kBoundSample / NT;    // sampled tokens per thread
+  constexpr int PPT = R * D / NT;           // elements of P per thread (R * D is a multiple of NT)
+  static_assert(PPT >= 1 && PPT * NT == R * D, "P tile");
+  static_assert(G * R <= NT, "one thread per projected query element");
   __shared__ float ps[R][D + 1];            // P, padded rows
   __shared__ float qf[G][D];
-  __shared__ double qs[G * R];
-  __shared__ uint32_t sk[kBoundSample];
-  __shared__ uint32_t hist[256 / kWave * 256];
+  __shared__ uint16_t qh[G * R];            // bf16 q~
+  __shared__ uint32_t qmax_bits;
+  __shared__ __align__(16) uint32_t hist[NT / kWave * 256];
   __shared__ uint32_t bc[2];
   const int unit = blockIdx.x, b = unit / c.Hkv, g = unit - b * c.Hkv;
   const int tid = threadIdx.x;
@@ -337,52 +421,106 @@ __global__ __launch_bounds__(256) void token_bound_kernel(CacheView c, const T *
     *reinterpret_cast<const uint16_t **>(cand + lay.hdr) = kproj;
     *reinterpret_cast<int32_t *>(cand + lay.hdr + 8) = R;
   }
+  if (tid == 0) qmax_bits = 0u;
+  // loads in the order they are needed: P and q, the block-table entries of the sampled tokens,
+  // then the sampled rows, which stay in flight while q~ is formed
+  float pv[PPT];
+#pragma unroll
+  for (int u = 0; u < PPT; ++u) pv[u] = proj[u * NT + tid];
+  const T *qb = q + ((size_t)b * c.Hq + g * G) * D;
+  const float qv = tid < G * D ? Elem<T>::get(qb, tid) : 0.0f;
   const int L = seq_len(c, b);
   const int kk = min(k, L);
   const bool sample = !(kk >= L || L <= kTokCand);
-  // issue the sampled rows' loads first; they are used after q~ is ready
   const int run = kBoundSample / 64, stride = L / 64;
+  int tok[PER], phys[PER];
   uint4 w[PER][R / 8];
-  if (sample)
+  if (sample) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int s = u * 256 + tid;
-      proj_row_load<R>(c, kproj, b, g, (s / run) * stride + s % run, w[u]);
+      const int s = u * NT + tid;
+      tok[u] = (s / run) * stride + s % run;
+      phys[u] = c.bt[(size_t)b * c.maxP + tok[u] / c.S];
     }
-  for (int i = tid; i < R * D; i += 256) ps[i / D][i % D] = proj[i];
-  for (int i = tid; i < G * D; i += 256) qf[i / D][i % D] = Elem<T>::get(q + ((size_t)b * c.Hq + g * G) * D, i);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const uint4 *row = reinterpret_cast<const uint4 *>(
+          kproj + (((size_t)phys[u] * c.Hkv + g) * c.S + tok[u] % c.S) * R);
+#pragma unroll
+      for (int i = 0; i < R / 8; ++i) w[u][i] = row[i];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < PPT; ++u) ps[(u * NT + tid) / D][(u * NT + tid) % D] = pv[u];
+  if (tid < G * D) qf[tid / D][tid % D] = qv;
   __syncthreads();
-  // q~ of the unit's G heads: the float64 sum over j ascending of P[i][j] q[j]
+  // q~ of the unit's G heads: the float64 sum over j ascending of P[i][j] q[j], rounded to float
   double *qt = reinterpret_cast<double *>(cand + lay.qt) + (size_t)(b * c.Hq + g * G) * R;
-  for (int i = tid; i < G * R; i += 256) {
-    const int h = i / R, ii = i - h * R;
+  if (tid < G * R) {
+    const int h = tid / R, ii = tid - h * R;
     double acc = 0.0;
 #pragma unroll 8
     for (int j = 0; j < D; ++j) acc = fma((double)ps[ii][j], (double)qf[h][j], acc);
-    const double qd = (double)(float)acc;
-    qs[i] = qd;
-    qt[i] = qd;
+    const float qf32 = (float)acc;
+    qt[tid] = (double)qf32;
+    const uint32_t bits = __float_as_uint(qf32);
+    const uint16_t hb = (uint16_t)((bits + 0x7fffu + ((bits >> 16) & 1u)) >> 16);   // nearest even
+    qh[tid] = hb;
+    reinterpret_cast<uint16_t *>(cand + lay.qb)[(size_t)(b * c.Hq + g * G) * R + tid] = hb;
+    const float am = wave_max(fabsf(qf32));
+    if ((tid & (kWave - 1)) == 0) atomicMax(&qmax_bits, __float_as_uint(am));
   }
   __syncthreads();
+  const FilterCoef fc = filter_coef(__uint_as_float(qmax_bits));
   uint32_t *bound = reinterpret_cast<uint32_t *>(cand + lay.bound);
+  if (tid == 0) reinterpret_cast<float2 *>(cand + lay.qc)[unit] = make_float2(fc.rel, fc.abs);
   if (!sample) {
     if (tid == 0) bound[unit] = 0u;
     return;
   }
+  const uint32_t *qp = reinterpret_cast<const uint32_t *>(qh);
+  float acc[PER][G], n1[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    int zero = 0;
-    asm volatile("" : "+s"(zero));   // keeps the q~ reads from LDS per token (no hoisting)
-    sk[u * 256 + tid] = f32_order_key(proj_row_key<R, G>(w[u], qs + zero));
+    n1[u] = 0.0f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) acc[u][h] = 0.0f;
   }
-  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < R / 8; ++i) {
+    int zero = 0;
+    asm volatile("" : "+s"(zero));   // keeps each chunk's q~ reads from LDS within the chunk
+    const uint32_t *qpi = qp + zero;
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {
+      uint32_t kw[PER];
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        kw[u] = pr == 0 ? w[u][i].x : pr == 1 ? w[u][i].y : pr == 2 ? w[u][i].z : w[u][i].w;
+        n1[u] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kw[u] & 0x7fff7fffu),
+                                                __builtin_bit_cast(bf16x2_t, 0x3f803f80u), n1[u], false);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const bf16x2_t qq = __builtin_bit_cast(bf16x2_t, qpi[h * (R / 2) + i * 4 + pr]);
+#pragma unroll
+        for (int u = 0; u < PER; ++u)
+          acc[u][h] = __builtin_amdgcn_fdot2_f32_bf16(qq, __builtin_bit_cast(bf16x2_t, kw[u]), acc[u][h], false);
+      }
+    }
+  }
+  uint32_t sk[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    float a = acc[u][0];
+#pragma unroll
+    for (int h = 1; h < G; ++h) a = fmaxf(a, acc[u][h]);
+    sk[u] = f32_order_key(a - fmaf(fc.rel, n1[u], fc.abs));
+  }
   const double expect = (double)kk * kBoundSample / L;
   const double rs = ceil(expect + 4.0 * sqrt(expect) + 16.0);
   uint32_t Tlo = 0, need;
-  if (rs < kBoundSample) {
-    auto get = [&](int i) { return sk[i]; };
-    radix_kth<256>(get, kBoundSample, (uint32_t)rs, hist, bc, Tlo, need, 2);
-  }
+  if (rs < kBoundSample) radix_kth_regs<NT, PER>(sk, kBoundSample, (uint32_t)rs, hist, bc, Tlo, need, 2, 0u, 0xffffffffu);
   if (tid == 0) bound[unit] = Tlo;
 }
 
@@ -398,9 +536,10 @@ __global__ __launch_bounds__(kTokThreads) void select_token_cand_kernel(CacheVie
   __shared__ uint32_t ckey[kTokCand];
   __shared__ int32_t cidx[kTokCand];
   __shared__ int soff[kMaxCandBlocks + 1];
-  __shared__ uint32_t hist[kTokWaves * 256];
+  __shared__ __align__(16) uint32_t hist[kTokWaves * 256];
   __shared__ uint32_t bc[2];
   __shared__ int scan_scratch[kTokWaves + 1];
+  __shared__ uint32_t range[2 * kTokWaves];
   const int unit = blockIdx.x, b = unit / c.Hkv, g = unit - b * c.Hkv;
   const int n = seq_len(c, b);
   const int kk = min(k, n);
@@ -429,20 +568,60 @@ __global__ __launch_bounds__(kTokThreads) void select_token_cand_kernel(CacheVie
   const int total = base;
   uint32_t T, need;
   if (total >= kk && total <= kTokCand) {
-    for (int f = tid; f < total; f += kTokThreads) {
-      int lo = 0, hi = nb - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (soff[mid] <= f) lo = mid; else hi = mid - 1;
+    // candidate f sits in the segment s with soff[s] <= f < soff[s + 1]: eight independent
+    // fixed-depth binary searches per thread, then all eight loads in flight at once
+    constexpr int GPT = kTokCand / kTokThreads;
+    int sg[GPT];
+#pragma unroll
+    for (int j = 0; j < GPT; ++j) sg[j] = 0;
+    // slots past the end load the last candidate (total >= kk >= 1) and are dropped.
+    // soff[nb] = total exceeds every f searched, so m >= nb needs no test of its own: the eight
+    // LDS reads of a step are unconditional and overlap
+    int fs[GPT];
+#pragma unroll
+    for (int j = 0; j < GPT; ++j) fs[j] = min(tid + j * kTokThreads, total - 1);
+    for (int step = 1 << (31 - __clz(nb)); step > 0; step >>= 1) {
+      int v[GPT];
+#pragma unroll
+      for (int j = 0; j < GPT; ++j) v[j] = soff[min(sg[j] + step, nb)];
+#pragma unroll
+      for (int j = 0; j < GPT; ++j) sg[j] = v[j] <= fs[j] ? sg[j] + step : sg[j];
+    }
+    float2 e[GPT];
+#pragma unroll
+    for (int j = 0; j < GPT; ++j) e[j] = seg[(size_t)sg[j] * kCandSegTokens + (fs[j] - soff[sg[j]])];
+    uint32_t u[GPT], kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+    for (int j = 0; j < GPT; ++j) {
+      const int f = tid + j * kTokThreads;
+      u[j] = f32_order_key(e[j].x);
+      if (f < total) {
+        ckey[f] = u[j];
+        cidx[f] = __float_as_int(e[j].y);
+        kmin = min(kmin, u[j]);
+        kmax = max(kmax, u[j]);
       }
-      const float2 e = seg[(size_t)lo * kCandSegTokens + (f - soff[lo])];
-      ckey[f] = f32_order_key(e.x);
-      cidx[f] = __float_as_int(e.y);
+    }
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, kWave));
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, kWave));
+    }
+    if ((tid & (kWave - 1)) == 0) {
+      range[tid / kWave] = kmin;
+      range[kTokWaves + tid / kWave] = kmax;
     }
     __syncthreads();
+    kmin = 0xffffffffu;
+    kmax = 0u;
+#pragma unroll
+    for (int w = 0; w < kTokWaves; ++w) {
+      kmin = min(kmin, range[w]);
+      kmax = max(kmax, range[kTokWaves + w]);
+    }
     auto lget = [&](int i) { return ckey[i]; };
     auto lidx = [&](int i) { return cidx[i]; };
-    radix_kth<kTokThreads>(lget, total, (uint32_t)kk, hist, bc, T, need);
+    radix_kth_regs<kTokThreads, GPT>(u, total, (uint32_t)kk, hist, bc, T, need, 4, kmin, kmax);
     ordered_take<kTokThreads>(lget, lidx, total, T, need, out, scan_scratch);
     return;
   }
@@ -599,10 +778,10 @@ template <typename T, int D, int R>
 static hipError_t token_bound_r(const CacheView &c, const void *q, int k, const float *proj, const uint16_t *kproj,
                                 char *cand, const CandLayout &lay, hipStream_t st) {
   switch (c.G) {
-    case 1: token_bound_kernel<T, D, R, 1><<<c.B * c.Hkv, 256, 0, st>>>(c, static_cast<const T *>(q), k, proj, kproj, cand, lay); break;
-    case 2: token_bound_kernel<T, D, R, 2><<<c.B * c.Hkv, 256, 0, st>>>(c, static_cast<const T *>(q), k, proj, kproj, cand, lay); break;
-    case 4: token_bound_kernel<T, D, R, 4><<<c.B * c.Hkv, 256, 0, st>>>(c, static_cast<const T *>(q), k, proj, kproj, cand, lay); break;
-    case 8: token_bound_kernel<T, D, R, 8><<<c.B * c.Hkv, 256, 0, st>>>(c, static_cast<const T *>(q), k, proj, kproj, cand, lay); break;
+    case 1: token_bound_kernel<T, D, R, 1><<<c.B * c.Hkv, kBoundThreads, 0, st>>>(c, static_cast<const T *>(q), k, proj, kproj, cand, lay); break;
+    case 2: token_bound_kernel<T, D, R, 2><<<c.B * c.Hkv, kBoundThreads, 0, st>>>(c, static_cast<const T *>(q), k, proj, kproj, cand, lay); break;
+    case 4: token_bound_kernel<T, D, R, 4><<<c.B * c.Hkv, kBoundThreads, 0, st>>>(c, static_cast<const T *>(q), k, proj, kproj, cand, lay); break;
+    case 8: token_bound_kernel<T, D, R, 8><<<c.B * c.Hkv, kBoundThreads, 0, st>>>(c, static_cast<const T *>(q), k, proj, kproj, cand, lay); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

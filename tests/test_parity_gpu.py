@@ -96,6 +96,42 @@ def test_fused_token_topk_falls_back_when_the_sample_misleads(dev):
     H.compare(w, st)
 
 
+def test_fused_token_topk_keeps_tokens_the_estimate_undercounts(dev):
+    """The scorer filters with a bf16 estimate of each key plus an error bound. Here the estimate of
+    'trap' rows is 0 while their exact key is X/32: P = diag(1 + 2^-10 on channels 0-15,
+    1 - 2^-10 on 16-31) and q = 1 on those channels give q~ entries that both round to bf16 1.0,
+    and a trap row k = (X x16, -X x16) cancels under the rounded q~ but not under q~ itself.
+    Trap keys 8 .. 16 straddle the top-512 threshold (about 11 for the N(0, 1) rows), so a filter
+    without its error bound would drop the selected traps."""
+    H.log("[parity fused token top-k, cancelling rows]")
+    L, R = 20000, 32
+    w = W.make("token128k", device=dev, B=2, L=L, k=512)
+    P = torch.zeros((R, w.d), dtype=torch.float32)
+    P[torch.arange(16), torch.arange(16)] = 1.0 + 2.0 ** -10
+    P[torch.arange(16, 32), torch.arange(16, 32)] = 1.0 - 2.0 ** -10
+    w.proj = P.to(dev)
+    w.q[:, :, :R] = 1.0
+    gen = torch.Generator().manual_seed(77)
+    xs = torch.tensor([256.0, 320.0, 384.0, 448.0, 512.0])
+    traps = {}
+    for b in range(w.B):
+        pos = torch.randperm(L, generator=gen)[:400]
+        xv = xs[torch.randint(0, len(xs), (400,), generator=gen)]
+        traps[b] = (pos.numpy(), xv.numpy())
+        for t, x in zip(pos.tolist(), xv.tolist()):
+            row = w.k[int(w.block_table[b, t // w.S]), :, t % w.S, :]
+            row[:, :16] = x
+            row[:, 16:R] = -x
+    st = H.gpu_step(w, fused=True)
+    H.compare(w, st)
+    idx, cnt = st.sel.idx.cpu().numpy(), st.sel.count.cpu().numpy()
+    for b in range(w.B):
+        pos, xv = traps[b]
+        for g in range(w.Hkv):
+            chosen = np.isin(pos, idx[b, g, :cnt[b, g]])
+            assert chosen.any() and not chosen.all(), (b, g, int(chosen.sum()))
+
+
 def test_k_at_least_pages_and_tokens_selects_all(dev):
     H.log("[edge] k >= P_b, k >= L_b")
     w = W.make("gqa32k", device=dev, B=2, lens=[700, 33], k=400)
