@@ -119,7 +119,14 @@ typedef struct skv_scores {
                       SKV_OP_CANDIDATES, &token_k, 0) bytes, 256-byte aligned. The selection that
                       consumes it also reads the projected keys (meta->kproj), which must still hold
                       the same values */
+  int32_t token_phase; /* PROJ with token_k > 0: which part of the candidate scoring a call runs.
+                          SKV_TOKEN_PHASE_ALL (0) both; SKV_TOKEN_PHASE_BOUND (1) only the sampled
+                          bound (projected queries and T_lo into cand); SKV_TOKEN_PHASE_FILTER (2)
+                          only the filtered scoring of every token, which needs a BOUND call with
+                          the same q and cand before it on the same stream. Ignored otherwise */
 } skv_scores;
+
+enum { SKV_TOKEN_PHASE_ALL = 0, SKV_TOKEN_PHASE_BOUND = 1, SKV_TOKEN_PHASE_FILTER = 2 };
 
 /* Query-aware scores ("EntmaxKV" s2.A; "Joint Subspace Sparse Attention" abstract).
  *   BOX:   key[b][g][p] = RN_f32(max over the G query heads h of g of

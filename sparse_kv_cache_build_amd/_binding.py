@@ -48,7 +48,7 @@ class Meta(C.Structure):
 
 class Scores(C.Structure):
     _fields_ = [("key", C.c_void_p), ("m", C.c_void_p), ("s", C.c_void_p), ("shat", C.c_void_p),
-                ("token_k", C.c_int32), ("cand", C.c_void_p)]
+                ("token_k", C.c_int32), ("cand", C.c_void_p), ("token_phase", C.c_int32)]
 
 
 class SelectParams(C.Structure):
@@ -200,7 +200,7 @@ class ScoreBuffers:
         else:
             raise ValueError(kind)
         ptrs = [t.data_ptr() if t is not None else None for t in (self.key, self.m, self.s, self.shat)]
-        self.sc = Scores(*ptrs, self.token_k, self.cand.data_ptr() if self.cand is not None else None)
+        self.sc = Scores(*ptrs, self.token_k, self.cand.data_ptr() if self.cand is not None else None, 0)
         kind_i = C.c_int32(_KIND[kind])
         self.ws = _workspace(cache, workspace_bytes(cache, OP_SCORE, kind_i))
 
@@ -209,11 +209,17 @@ class ScoreBuffers:
         return C.byref(self.sc)
 
 
+TOKEN_PHASE_ALL, TOKEN_PHASE_BOUND, TOKEN_PHASE_FILTER = 0, 1, 2
+
+
 def score_pages(cache: PagedCache, meta: PageMeta, q, kind: str, sm_scale=None, out: ScoreBuffers | None = None,
-                token_k: int = 0, stream=None) -> ScoreBuffers:
+                token_k: int = 0, stream=None, phase: int = TOKEN_PHASE_ALL) -> ScoreBuffers:
+    """phase (candidate scoring only): TOKEN_PHASE_BOUND / TOKEN_PHASE_FILTER run its two parts
+    as separate calls, the bound first."""
     assert q.dtype == cache.dtype and q.is_contiguous() and tuple(q.shape) == (cache.B, cache.Hq, cache.d)
     out = out or ScoreBuffers(cache, kind, token_k)
     scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(cache.d)
+    out.sc.token_phase = int(phase)
     _check(lib().skv_score_pages(cache.ref, meta.ref, _ptr(q), _KIND[kind], scale, out.ref, _ptr(out.ws),
                                  out.ws.numel(), _stream(stream)), "skv_score_pages")
     return out

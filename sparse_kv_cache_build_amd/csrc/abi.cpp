@@ -208,10 +208,16 @@ skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q,
       if (!out->cand || !aligned(out->cand, 256)) return SKV_ERR_INVALID_ARG;
       const skv::CandLayout lay(c->batch, c->num_q_heads, c->num_kv_heads, c->max_pages * c->page_size, 64);
       if (lay.nb > 8192) return SKV_ERR_UNSUPPORTED;
+      const int32_t ph = out->token_phase;
+      if (ph != SKV_TOKEN_PHASE_ALL && ph != SKV_TOKEN_PHASE_BOUND && ph != SKV_TOKEN_PHASE_FILTER)
+        return SKV_ERR_INVALID_ARG;
       (void)hipGetLastError();
-      hipError_t e = skv::launch_token_bound(v, c->dtype, q, out->token_k, m->proj_rank, m->proj, m->kproj,
-                                             static_cast<char *>(out->cand), s);
-      if (e == hipSuccess) e = skv::launch_score_proj_cand(v, m->proj_rank, m->kproj, static_cast<char *>(out->cand), s);
+      hipError_t e = hipSuccess;
+      if (ph != SKV_TOKEN_PHASE_FILTER)
+        e = skv::launch_token_bound(v, c->dtype, q, out->token_k, m->proj_rank, m->proj, m->kproj,
+                                    static_cast<char *>(out->cand), s);
+      if (e == hipSuccess && ph != SKV_TOKEN_PHASE_BOUND)
+        e = skv::launch_score_proj_cand(v, m->proj_rank, m->kproj, static_cast<char *>(out->cand), s);
       return hip_status(e);
     }
     if (!out->key) return SKV_ERR_INVALID_ARG;

@@ -169,8 +169,9 @@ __global__ __launch_bounds__(256) void score_proj_kernel(CacheView c, const uint
 // filtered):
 //  1. filter: each token's upper estimate of its key (proj_row_upper, bf16 dot2 with an error
 //     bound) against T_lo; tokens that pass go, in token order, into the wave's LDS list;
-//  2. exact: the listed tokens, 64 at a time, get the exact key (rows read again, mostly from L2)
-//     and the ones with order key >= T_lo are compacted into the segment with ballots.
+//  2. exact: the listed tokens, 64 at a time, get the exact key and the ones with order key >= T_lo
+//     are compacted into the segment with ballots. The filter keeps the rows of the first 64
+//     listed tokens in LDS (by then they have left L2); later rounds read their rows again.
 // The estimate never falls below the exact key, so the filter loses no token of the exact set;
 // it only spares the float64 arithmetic for the tokens that cannot reach T_lo.
 template <int R, int G>
@@ -183,6 +184,7 @@ __global__ __launch_bounds__(256) void score_proj_cand_kernel(CacheView c, const
                                                               int nb) {
   constexpr int GT = kCandSegTokens, STEP = 2 * kWave, NST = GT / STEP;
   __shared__ int cl[256 / kWave][GT];
+  __shared__ uint4 rc[256 / kWave][kWave][R / 8];   // rows of the first 64 listed tokens
   const int unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
   const int L = seq_len(c, b);
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
@@ -223,8 +225,14 @@ __global__ __launch_bounds__(256) void score_proj_cand_kernel(CacheView c, const
       const int t = tg + s * STEP + u * kWave + lane;
       const bool keep = t < L && f32_order_key(proj_row_upper<R, G>(x[u], qp, fc)) >= Tlo;
       const uint64_t bal = __ballot(keep);
-      if (keep)
-        cl[wv][nc + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] = t;
+      if (keep) {
+        const int slot = nc + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        cl[wv][slot] = t;
+        if (slot < kWave) {
+#pragma unroll
+          for (int i = 0; i < R / 8; ++i) rc[wv][slot][i] = x[u][i];
+        }
+      }
       nc += __popcll(bal);
     }
   };
@@ -246,9 +254,14 @@ __global__ __launch_bounds__(256) void score_proj_cand_kernel(CacheView c, const
     const int i = i0 + lane;
     const int t = i < nc ? cl[wv][i] : tg;
     uint4 x[R / 8];
-    const uint4 *row = rowp(t);
+    if (i0 == 0) {   // the first 64 rows were kept in LDS by the filter (long evicted from L2)
 #pragma unroll
-    for (int j = 0; j < R / 8; ++j) x[j] = row[j];
+      for (int j = 0; j < R / 8; ++j) x[j] = rc[wv][lane][j];
+    } else {
+      const uint4 *row = rowp(t);
+#pragma unroll
+      for (int j = 0; j < R / 8; ++j) x[j] = row[j];
+    }
     const float kv = proj_row_key<R, G>(x, qq);
     const bool keep = i < nc && f32_order_key(kv) >= Tlo;
     const uint64_t bal = __ballot(keep);

@@ -137,6 +137,11 @@ def test_score_and_meta_validation(L):
     st = L.skv_score_pages(C.byref(c), C.byref(m), C.c_void_p(FAKE), B.SCORE_GAUSS, 0.1, C.byref(out),
                            C.c_void_p(FAKE), 1 << 20, None)
     assert st == B.SKV_ERR_INVALID_ARG                              # gauss metadata not present
+    mp = B.Meta(B.META_PROJ, None, None, 32, FAKE, FAKE)
+    for phase in (-1, 3):   # the candidate scoring has two parts: 0 both, 1 bound, 2 filter
+        outp = B.Scores(None, None, None, None, 64, FAKE, phase)
+        assert L.skv_score_pages(C.byref(c), C.byref(mp), C.c_void_p(FAKE), B.SCORE_PROJ, 0.1, C.byref(outp),
+                                 None, 0, None) == B.SKV_ERR_INVALID_ARG
     mp = B.Meta(B.META_PROJ, None, None, 24, FAKE, FAKE)
     assert L.skv_build_page_meta(C.byref(c), C.byref(mp), None) == B.SKV_ERR_UNSUPPORTED   # rank 24
     assert L.skv_build_page_meta(C.byref(c), C.byref(B.Meta(0, None, None, 0, None, None)), None) == \
