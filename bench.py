@@ -38,9 +38,9 @@ def log(*a):
 class Step:
     """Preallocated buffers of one decode step on one buffer set."""
 
-    def __init__(self, w: W.Workload, alpha: float, split: int = 0):
+    def __init__(self, w: W.Workload, alpha: float, split: int = 0, full: bool = False):
         cfg = w.cfg
-        self.w, self.alpha = w, alpha
+        self.w, self.alpha, self.full = w, alpha, full
         self.kind = cfg["score"]
         self.cache = skv.PagedCache(w.k, w.v, w.block_table, w.seq_lens, w.Hq)
         t0 = time.time()
@@ -48,28 +48,39 @@ class Step:
         torch.cuda.synchronize()
         self.meta_s = time.time() - t0
         # token top-k: keep only the candidate set of the selection (fused scoring, no dense keys)
-        self.fused = cfg["policy"] == "token_topk"
+        self.fused = cfg["policy"] == "token_topk" and not full
         self.scores = skv.ScoreBuffers(self.cache, self.kind, cfg.get("k", 0) if self.fused else 0)
-        p = skv.select_params(cfg["policy"], k=cfg.get("k", 0), budget_pct=cfg.get("pct", 0),
-                              alpha=cfg.get("sel_alpha", 1.5), delta=cfg.get("delta", 0.0),
-                              tokens=1 if self.kind == "proj" else 0)
+        if full:   # full-cache comparator: every page, the same attention kernels
+            p = skv.select_params("all", tokens=0)
+        else:
+            p = skv.select_params(cfg["policy"], k=cfg.get("k", 0), budget_pct=cfg.get("pct", 0),
+                                  alpha=cfg.get("sel_alpha", 1.5), delta=cfg.get("delta", 0.0),
+                                  tokens=1 if self.kind == "proj" else 0)
         self.sel = skv.Selection(self.cache, p)
         self.attn = skv.AttnBuffers(self.cache, skv.attn_params(self.cache, alpha, None, self.sel.granularity, split),
                                     self.sel.cap)
 
     def pre(self):
-        """Work before the dominant kernel: the sampled bound of the fused token scoring."""
-        if self.fused:
+        """Work before the dominant kernel: the sampled bound of the fused token scoring, or the
+        selection of every page for the full-cache comparator."""
+        if self.full:
+            skv.select_pages(self.cache, self.scores, None, out=self.sel)
+        elif self.fused:
             skv.score_pages(self.cache, self.meta, self.w.q, self.kind, out=self.scores, phase=skv.TOKEN_PHASE_BOUND)
 
     def score(self):
-        """The dominant kernel: the filtered token scoring, or the page scorer."""
-        skv.score_pages(self.cache, self.meta, self.w.q, self.kind, out=self.scores,
-                        phase=skv.TOKEN_PHASE_FILTER if self.fused else skv.TOKEN_PHASE_ALL)
+        """The dominant kernel: the filtered token scoring, the page scorer, or (full-cache
+        comparator) the attention over every page."""
+        if self.full:
+            skv.sparse_decode_attn(self.cache, self.w.q, self.sel, out=self.attn)
+        else:
+            skv.score_pages(self.cache, self.meta, self.w.q, self.kind, out=self.scores,
+                            phase=skv.TOKEN_PHASE_FILTER if self.fused else skv.TOKEN_PHASE_ALL)
 
     def rest(self):
-        skv.select_pages(self.cache, self.scores, None, out=self.sel)
-        skv.sparse_decode_attn(self.cache, self.w.q, self.sel, out=self.attn)
+        if not self.full:
+            skv.select_pages(self.cache, self.scores, None, out=self.sel)
+            skv.sparse_decode_attn(self.cache, self.w.q, self.sel, out=self.attn)
 
     def run(self):
         self.pre()
@@ -99,7 +110,9 @@ def step_bytes(st: Step):
     P = (lens + S - 1) // S
     cnt = st.sel.count.cpu().numpy().astype(np.int64)
     bt = int(P.sum()) * w.Hkv * 4        # block-table entries, read once per unit
-    if st.kind == "box":
+    if st.full:
+        meta, keys_out = 0, 0
+    elif st.kind == "box":
         meta = int(P.sum()) * w.Hkv * 2 * d * e
         keys_out = w.B * w.Hkv * w.maxP * 4
     elif st.kind == "gauss":
@@ -125,13 +138,15 @@ def step_bytes(st: Step):
     v_rows = k_rows if st.alpha == 1.0 else 0
     q_out = w.B * w.Hq * d * (e + 4)
     total = meta + bt + k_rows * kv_row + v_rows * kv_row + q_out
-    return total, meta + keys_out + bt, dict(meta=meta, k_rows=k_rows, v_rows=v_rows, q_out=q_out,
-                                             keys_out=keys_out, block_table=bt)
+    dom = (k_rows + v_rows) * kv_row + q_out if st.full else meta + keys_out + bt
+    return total, dom, dict(meta=meta, k_rows=k_rows, v_rows=v_rows, q_out=q_out, keys_out=keys_out, block_table=bt)
 
 
 def dominant_kernel(st: Step) -> str:
     """The kernel the roofline record covers (the timed score call launches exactly it, except the
     page scorers, which first run a small query-prep kernel)."""
+    if st.full:
+        return "attn_softmax_kernel" if st.alpha == 1.0 else "attn_entmax_logits_kernel"
     if st.fused:
         return "score_proj_cand_kernel"
     return {"box": "score_box_kernel", "gauss": "score_gauss_kernel", "proj": "score_proj_kernel"}[st.kind]
@@ -212,6 +227,8 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="buffer sets rotated per step (0: enough to exceed 2x MALL)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--graph", action="store_true", help="replay the stages as HIP graphs instead of launching them")
+    ap.add_argument("--full", action="store_true",
+                    help="full-cache comparator: attention over every page with the same kernels, no scoring")
     ap.add_argument("--calibrate", action="store_true",
                     help="after timing, copy a 1 GiB buffer 3 times (reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -226,14 +243,14 @@ def main():
     alpha = args.alpha if args.alpha is not None else cfg["alphas"][0]
 
     log(f"[bench] drawing {name} on {dev}")
-    sets = [Step(W.make(name, device=dev), alpha, args.split)]
+    sets = [Step(W.make(name, device=dev), alpha, args.split, args.full)]
     sets[0].run()
     torch.cuda.synchronize()
     total, score_bytes, det = step_bytes(sets[0])
     n_sets = args.sets or max(1, math.ceil(2 * MALL_BYTES / max(total, 1)))
     for i in range(1, n_sets):
         log(f"[bench] buffer set {i + 1}/{n_sets}")
-        sets.append(Step(W.make(name, device=dev, seed=cfg["seed"] + 100 * i), alpha, args.split))
+        sets.append(Step(W.make(name, device=dev, seed=cfg["seed"] + 100 * i), alpha, args.split, args.full))
     meta_s = sets[0].meta_s
     graphs = args.graph
     if graphs:
@@ -274,6 +291,19 @@ def main():
     score_gbps = score_bytes / (score_ms * 1e-3) / 1e9
     log(f"[bench] {ms * 1e3:.1f} us/step, score stage {score_ms * 1e3:.1f} us")
 
+    # metadata upkeep per decode step, outside the step: one new token per sequence (its page's box or
+    # moments recomputed, or its projected key written)
+    st0 = sets[0]
+    for _ in range(3):
+        skv.append_page_meta(st0.cache, st0.meta, 1)
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for _ in range(20):
+        skv.append_page_meta(st0.cache, st0.meta, 1)
+    a1.record(stream)
+    torch.cuda.synchronize()
+    append_us = a0.elapsed_time(a1) / 20 * 1e3
+
     if args.calibrate:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -283,7 +313,7 @@ def main():
         del src, dst
 
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and not args.full:   # the comparator is context: no oracle baseline
         log("[bench] CPU oracle baseline")
         cpu = cpu_baseline(name, {}, alpha)
 
@@ -306,10 +336,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "batch": w0.B, "ctx": int(max(w0.lens)), "mean_ctx": float(np.mean(w0.lens)),
                    "q_heads": w0.Hq, "kv_heads": w0.Hkv, "head_dim": w0.d, "page": w0.S, "kv_dtype": "bf16"
-                   if w0.dtype == torch.bfloat16 else "f32", "select": sel_desc[cfg["policy"]],
+                   if w0.dtype == torch.bfloat16 else "f32",
+                   "select": "every page (full-cache comparator)" if args.full else sel_desc[cfg["policy"]],
                    "attn": "softmax" if alpha == 1.0 else f"{alpha}-entmax", "bytes_per_step": int(total),
                    "achieved_GBps": round(gbps, 1), "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
                    "buffer_sets": n_sets, "hip_graphs": graphs, "meta_build_s": round(meta_s, 4),
+                   "meta_append_us": round(append_us, 2),
                    "bytes_detail": det},
         "roofline": {"bound": "hbm", "kernel": dominant_kernel(sets[0]), "achieved": round(score_gbps, 1),
                      "peak": PEAK_GBPS, "unit": "GB/s", "frac": round(score_gbps / PEAK_GBPS, 4),

@@ -3,7 +3,8 @@
  * grouped-query (GQA) KV cache, for AMD Instinct MI355X (gfx950).
  *
  * The calls follow the pipeline the pages describe for one decode step:
- *   skv_build_page_meta    per-page metadata, once per page at prefill/append time
+ *   skv_build_page_meta    per-page metadata, once per page at prefill time
+ *   skv_append_page_meta   the same metadata kept current for the pages that new tokens reach
  *                          ("EntmaxKV" summary, s2.A: box bounds k_min/k_max and Gaussian
  *                          moments stored per page; "Joint Subspace Sparse Attention" abstract:
  *                          keys cached in a shared low-dimensional subspace)
@@ -102,6 +103,17 @@ typedef struct skv_meta {
  * written. Errors: SKV_ERR_INVALID_ARG for null or inconsistent arguments or a missing output
  * of a requested kind; SKV_ERR_UNSUPPORTED outside the supported set. */
 skv_status skv_build_page_meta(const skv_cache *c, const skv_meta *m, void *stream);
+
+/* Keeps the metadata current while decoding. The metadata is stored per page and maintained as
+ * the cache grows ("EntmaxKV" s2.A). The caller has written the last n_new tokens of every
+ * sequence into k (seq_lens already counts them; a sequence shorter than n_new counts all its
+ * tokens as new). For every page holding one of those tokens, BOX and GAUSS are recomputed over
+ * all valid tokens of the page, and PROJ rows are written for the new tokens only. Afterwards the
+ * metadata of those pages equals what skv_build_page_meta writes for them (bit for bit, same
+ * arithmetic); every other page and row is left untouched. A page holds at most S tokens, so
+ * the work per sequence and KV head is O(S d), whatever the context length.
+ * Errors: as skv_build_page_meta, and SKV_ERR_INVALID_ARG for n_new < 1. */
+skv_status skv_append_page_meta(const skv_cache *c, const skv_meta *m, int32_t n_new, void *stream);
 
 /* ------------------------------------------------------------------ scores */
 

@@ -24,8 +24,8 @@ SCORE_BOX, SCORE_GAUSS, SCORE_PROJ = 0, 1, 2
 SEL_TOPK, SEL_BUDGET, SEL_THRESH_GAUSS, SEL_TOKEN_TOPK, SEL_ALL = range(5)
 OP_SCORE, OP_SELECT, OP_ATTN, OP_CANDIDATES = 0, 1, 2, 3
 
-EXPORTS = ("skv_build_page_meta", "skv_score_pages", "skv_select_pages", "skv_sparse_decode_attn",
-           "skv_workspace_bytes", "skv_status_str")
+EXPORTS = ("skv_build_page_meta", "skv_append_page_meta", "skv_score_pages", "skv_select_pages",
+           "skv_sparse_decode_attn", "skv_workspace_bytes", "skv_status_str")
 
 
 class SkvError(RuntimeError):
@@ -72,6 +72,7 @@ def lib():
         L = C.CDLL(LIB_PATH)
         P, I, F, S = C.c_void_p, C.c_int32, C.c_float, C.c_size_t
         L.skv_build_page_meta.argtypes = [P, P, P]
+        L.skv_append_page_meta.argtypes = [P, P, I, P]
         L.skv_score_pages.argtypes = [P, P, P, I, F, P, P, S, P]
         L.skv_select_pages.argtypes = [P, P, P, P, P, I, P, P, S, P]
         L.skv_sparse_decode_attn.argtypes = [P, P, P, P, I, P, P, P, S, P]
@@ -163,6 +164,13 @@ class PageMeta:
 def build_page_meta(cache: PagedCache, kinds=("box",), proj=None, stream=None) -> PageMeta:
     meta = PageMeta(cache, kinds, proj)
     _check(lib().skv_build_page_meta(cache.ref, meta.ref, _stream(stream)), "skv_build_page_meta")
+    return meta
+
+
+def append_page_meta(cache: PagedCache, meta: PageMeta, n_new: int = 1, stream=None) -> PageMeta:
+    """After the last n_new tokens of every sequence were written into the cache (seq_lens counting
+    them): bring the metadata of the pages holding them up to date."""
+    _check(lib().skv_append_page_meta(cache.ref, meta.ref, int(n_new), _stream(stream)), "skv_append_page_meta")
     return meta
 
 

@@ -163,7 +163,8 @@ skv_status skv_workspace_bytes(const skv_cache *c, int32_t op, const void *param
   return SKV_ERR_INVALID_ARG;
 }
 
-skv_status skv_build_page_meta(const skv_cache *c, const skv_meta *m, void *stream) {
+// Shared by the build and the append: metadata kinds, outputs and the projection's LDS fit.
+static skv_status meta_args(const skv_cache *c, const skv_meta *m) {
   skv_status st = check_cache(c);
   if (st != SKV_OK) return st;
   if (!m || m->kinds == 0 || (m->kinds & ~(uint32_t)(SKV_META_BOX | SKV_META_GAUSS | SKV_META_PROJ)))
@@ -178,11 +179,28 @@ skv_status skv_build_page_meta(const skv_cache *c, const skv_meta *m, void *stre
     const size_t lds = sizeof(float) * ((size_t)m->proj_rank * (c->head_dim + 1) + (size_t)c->page_size * c->head_dim);
     if (lds > 65536) return SKV_ERR_UNSUPPORTED;
   }
+  return SKV_OK;
+}
+
+static skv_status meta_launch(const skv_cache *c, const skv_meta *m, int tail, void *stream) {
+  const bool box = m->kinds & SKV_META_BOX, gauss = m->kinds & SKV_META_GAUSS, proj = m->kinds & SKV_META_PROJ;
   (void)hipGetLastError();
-  const hipError_t e = skv::launch_build_meta(view(c), c->dtype, box ? m->box : nullptr, gauss ? m->gauss : nullptr,
-                                              m->proj_rank, proj ? m->proj : nullptr, proj ? m->kproj : nullptr,
-                                              static_cast<hipStream_t>(stream));
+  const hipError_t e = skv::launch_build_meta(view(c), c->dtype, tail, box ? m->box : nullptr,
+                                              gauss ? m->gauss : nullptr, m->proj_rank, proj ? m->proj : nullptr,
+                                              proj ? m->kproj : nullptr, static_cast<hipStream_t>(stream));
   return hip_status(e);
+}
+
+skv_status skv_build_page_meta(const skv_cache *c, const skv_meta *m, void *stream) {
+  const skv_status st = meta_args(c, m);
+  return st != SKV_OK ? st : meta_launch(c, m, 0, stream);
+}
+
+skv_status skv_append_page_meta(const skv_cache *c, const skv_meta *m, int32_t n_new, void *stream) {
+  const skv_status st = meta_args(c, m);
+  if (st != SKV_OK) return st;
+  if (n_new < 1) return SKV_ERR_INVALID_ARG;
+  return meta_launch(c, m, n_new, stream);
 }
 
 skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q, int32_t kind, float sm_scale,

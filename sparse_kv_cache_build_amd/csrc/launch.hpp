@@ -23,8 +23,8 @@ struct AttnArgs {
   float *cand_max;   // [U, G, nsplit]
 };
 
-hipError_t launch_build_meta(const CacheView &c, int dtype, void *box, float *gauss, int r, const float *proj,
-                             uint16_t *kproj, hipStream_t st);
+hipError_t launch_build_meta(const CacheView &c, int dtype, int tail, void *box, float *gauss, int r,
+                             const float *proj, uint16_t *kproj, hipStream_t st);
 hipError_t launch_score_box(const CacheView &c, int dtype, const void *q, const void *box, float *key, double *ws,
                             hipStream_t st);
 hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, const float *gauss, double scale, float *m,

@@ -1,6 +1,8 @@
 // Page metadata builder ("EntmaxKV" summary s2.A: per-page box bounds and Gaussian moments;
 // "Joint Subspace Sparse Attention" abstract: keys cached in a shared low-dimensional subspace).
-// Runs once per page at prefill / append time, off the per-step path.
+// Runs once per page at prefill time, and after an append for the pages holding the new tokens
+// (tail > 0: only pages holding one of the last `tail` tokens of a sequence, recomputed over all
+// their valid tokens, so the result equals a full build of those pages). Off the per-step path.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -11,11 +13,17 @@ namespace skv {
 //   box:   exact min / max over the valid tokens, stored as the original element bits.
 //   gauss: float64 mean (sum over t ascending, divided by n), then float64 mean squared
 //          deviation, each rounded once to float32.
+// First logical page a build (tail == 0) or an append of `tail` tokens covers.
+__device__ __forceinline__ int first_page(const CacheView &c, int L, int tail) {
+  return tail > 0 ? max(0, L - tail) / c.S : 0;
+}
+
 template <typename T>
-__global__ __launch_bounds__(256) void meta_box_gauss_kernel(CacheView c, T *__restrict__ box,
+__global__ __launch_bounds__(256) void meta_box_gauss_kernel(CacheView c, int tail, T *__restrict__ box,
                                                              float *__restrict__ gauss) {
-  const int p = blockIdx.x, b = blockIdx.y;
+  const int b = blockIdx.y;
   const int L = seq_len(c, b);
+  const int p = first_page(c, L, tail) + blockIdx.x;
   if (p >= num_pages(c, L)) return;
   const int n = min(c.S, L - p * c.S);
   const int phys = c.bt[(size_t)b * c.maxP + p];
@@ -55,23 +63,25 @@ __global__ __launch_bounds__(256) void meta_box_gauss_kernel(CacheView c, T *__r
 // per (logical page, KV head): the page's keys and P are staged in LDS as float (exact), then
 // each thread owns (token, i) pairs.
 template <typename T>
-__global__ __launch_bounds__(256) void meta_proj_kernel(CacheView c, int r, const float *__restrict__ proj,
+__global__ __launch_bounds__(256) void meta_proj_kernel(CacheView c, int tail, int r, const float *__restrict__ proj,
                                                         uint16_t *__restrict__ kproj) {
   extern __shared__ float smem[];
-  const int p = blockIdx.x, b = blockIdx.y / c.Hkv, g = blockIdx.y % c.Hkv;
+  const int b = blockIdx.y / c.Hkv, g = blockIdx.y % c.Hkv;
   const int L = seq_len(c, b);
+  const int p = first_page(c, L, tail) + blockIdx.x;
   if (p >= num_pages(c, L)) return;
   const int n = min(c.S, L - p * c.S);
+  const int t0 = tail > 0 ? max(0, L - tail - p * c.S) : 0;   // first row of the page to write
   const int phys = c.bt[(size_t)b * c.maxP + p];
   const int ldp = c.D + 1;  // padded row stride of P (bank spread across i)
   float *Ps = smem;                     // [r][D+1]
   float *Ks = smem + (size_t)r * ldp;   // [n][D]
   const T *K = static_cast<const T *>(c.k) + ((size_t)phys * c.Hkv + g) * c.S * c.D;
   for (int i = threadIdx.x; i < r * c.D; i += blockDim.x) Ps[(i / c.D) * ldp + i % c.D] = proj[i];
-  for (int i = threadIdx.x; i < n * c.D; i += blockDim.x) Ks[i] = Elem<T>::get(K, i);
+  for (int i = t0 * c.D + threadIdx.x; i < n * c.D; i += blockDim.x) Ks[i] = Elem<T>::get(K, i);
   __syncthreads();
   uint16_t *out = kproj + ((size_t)phys * c.Hkv + g) * c.S * r;
-  for (int pair = threadIdx.x; pair < n * r; pair += blockDim.x) {
+  for (int pair = t0 * r + threadIdx.x; pair < n * r; pair += blockDim.x) {
     const int t = pair / r, i = pair - t * r;
     const float *pr = Ps + i * ldp, *kr = Ks + t * c.D;
     double acc = 0.0;
@@ -80,22 +90,24 @@ __global__ __launch_bounds__(256) void meta_proj_kernel(CacheView c, int r, cons
   }
 }
 
-hipError_t launch_build_meta(const CacheView &c, int dtype, void *box, float *gauss, int r, const float *proj,
-                             uint16_t *kproj, hipStream_t st) {
-  const dim3 grid(c.maxP, c.B);
+hipError_t launch_build_meta(const CacheView &c, int dtype, int tail, void *box, float *gauss, int r,
+                             const float *proj, uint16_t *kproj, hipStream_t st) {
+  // pages per sequence: all of them, or those the last `tail` tokens can touch
+  const int np = tail > 0 ? min(c.maxP, (tail + c.S - 1) / c.S + 1) : c.maxP;
+  const dim3 grid(np, c.B);
   if (box || gauss) {
     if (dtype == 0)
-      meta_box_gauss_kernel<float><<<grid, 256, 0, st>>>(c, static_cast<float *>(box), gauss);
+      meta_box_gauss_kernel<float><<<grid, 256, 0, st>>>(c, tail, static_cast<float *>(box), gauss);
     else
-      meta_box_gauss_kernel<uint16_t><<<grid, 256, 0, st>>>(c, static_cast<uint16_t *>(box), gauss);
+      meta_box_gauss_kernel<uint16_t><<<grid, 256, 0, st>>>(c, tail, static_cast<uint16_t *>(box), gauss);
   }
   if (kproj) {
     const size_t lds = sizeof(float) * ((size_t)r * (c.D + 1) + (size_t)c.S * c.D);
-    const dim3 g2(c.maxP, c.B * c.Hkv);
+    const dim3 g2(np, c.B * c.Hkv);
     if (dtype == 0)
-      meta_proj_kernel<float><<<g2, 256, lds, st>>>(c, r, proj, kproj);
+      meta_proj_kernel<float><<<g2, 256, lds, st>>>(c, tail, r, proj, kproj);
     else
-      meta_proj_kernel<uint16_t><<<g2, 256, lds, st>>>(c, r, proj, kproj);
+      meta_proj_kernel<uint16_t><<<g2, 256, lds, st>>>(c, tail, r, proj, kproj);
   }
   return hipGetLastError();
 }

@@ -148,6 +148,11 @@ def test_score_and_meta_validation(L):
         B.SKV_ERR_INVALID_ARG
     assert L.skv_build_page_meta(C.byref(c), C.byref(B.Meta(B.META_GAUSS, None, None, 0, None, None)), None) == \
         B.SKV_ERR_INVALID_ARG
+    mb = B.Meta(B.META_BOX, FAKE, None, 0, None, None)
+    assert L.skv_append_page_meta(C.byref(c), C.byref(mb), 0, None) == B.SKV_ERR_INVALID_ARG   # n_new < 1
+    assert L.skv_append_page_meta(C.byref(c), C.byref(mp), 1, None) == B.SKV_ERR_UNSUPPORTED   # rank 24
+    assert L.skv_append_page_meta(C.byref(c), C.byref(B.Meta(B.META_GAUSS, None, None, 0, None, None)), 1,
+                                  None) == B.SKV_ERR_INVALID_ARG
 
 
 def test_binding_raises_without_library(monkeypatch, tmp_path):

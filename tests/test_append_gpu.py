@@ -1,0 +1,105 @@
+"""GPU parity of skv_append_page_meta: after new tokens, the metadata of the pages holding them must
+equal a full build at the new lengths (GPU and oracle), and every other page and row must be left
+as it was."""
+from types import SimpleNamespace
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as H
+import sparse_kv_cache_build_amd as skv
+import workloads as W
+from oracle import pipeline
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (workload, overrides, n_new): one token inside a page, one token opening a page, several tokens
+    # across page boundaries, a sequence shorter than n_new, an empty sequence, page size 64
+    ("gqa32k", dict(B=3, lens=[3000, 3009, 4096]), 1),
+    ("gqa32k", dict(B=3, lens=[3001, 16, 1]), 1),
+    ("long_gauss", dict(B=3, lens=[6000, 6033, 5]), 37),
+    ("token128k", dict(B=3, lens=[5000, 4097, 0], k=512), 3),
+    ("token128k", dict(B=2, lens=[5000, 20], k=512), 40),
+    ("ragged", dict(B=3, lens=[4500, 129, 64]), 2),
+]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def _used_pages(w, lens):
+    bt = w.block_table.cpu().numpy()
+    return {int(bt[b, p]): (b, p) for b in range(w.B) for p in range((lens[b] + w.S - 1) // w.S)}
+
+
+def _snapshot(meta):
+    return {k: getattr(meta, k).clone() for k in ("box", "gauss", "kproj") if getattr(meta, k) is not None}
+
+
+@pytest.mark.parametrize("name,over,n_new", CASES)
+def test_append_equals_rebuild(dev, name, over, n_new):
+    H.log(f"[append] {name} {over} n_new={n_new}")
+    w = W.make(name, device=dev, **over)
+    kind = w.cfg["score"]
+    new = [int(x) for x in w.lens]
+    old = [max(0, L - n_new) for L in new]
+    cache = skv.PagedCache(w.k, w.v, w.block_table, w.seq_lens, w.Hq)
+    w.seq_lens.copy_(torch.tensor(old, dtype=torch.int32))
+    meta = skv.build_page_meta(cache, (kind,), proj=w.proj)
+    torch.cuda.synchronize()
+    before = _snapshot(meta)
+    w.seq_lens.copy_(torch.tensor(new, dtype=torch.int32))
+    skv.append_page_meta(cache, meta, n_new)
+    ref = skv.build_page_meta(cache, (kind,), proj=w.proj)
+    torch.cuda.synchronize()
+
+    # 1. equal to a fresh build of every page in use, bit for bit
+    for phys, (b, p) in _used_pages(w, new).items():
+        if kind == "proj":
+            n = min(w.S, new[b] - p * w.S)
+            assert torch.equal(meta.kproj[phys, :, :n], ref.kproj[phys, :, :n]), (b, p)
+        else:
+            t = meta.box if kind == "box" else meta.gauss
+            r = ref.box if kind == "box" else ref.gauss
+            assert torch.equal(t[phys], r[phys]), (b, p)
+
+    # 2. untouched: pages and kproj rows that hold no new token
+    for phys, (b, p) in _used_pages(w, old).items():
+        first_new = old[b]                     # tokens >= old[b] are new
+        if kind == "proj":
+            n_old = min(w.S, old[b] - p * w.S)
+            assert torch.equal(meta.kproj[phys, :, :n_old], before["kproj"][phys, :, :n_old]), (b, p)
+        elif (p + 1) * w.S <= first_new:       # the page ended before the new tokens
+            key = "box" if kind == "box" else "gauss"
+            assert torch.equal(getattr(meta, key)[phys], before[key][phys]), (b, p)
+
+    # 3. equal to the oracle's build at the new lengths
+    h = W.host_arrays(w)
+    c = H.oracle_cache(h)
+    spec = H.spec_of(w)
+    md = pipeline.build_metadata(c, spec)
+    H._compare_meta(w, SimpleNamespace(meta=meta), c, md, h["phys_map"], spec)
+
+
+def test_append_sequence_of_single_tokens_matches_one_build(dev):
+    """Twenty decode steps of one token each, from lengths that cross page boundaries."""
+    H.log("[append] 20 single-token steps")
+    w = W.make("gqa32k", device=dev, B=2, lens=[1000, 45])
+    final = [int(x) for x in w.lens]
+    cache = skv.PagedCache(w.k, w.v, w.block_table, w.seq_lens, w.Hq)
+    lens = [L - 20 for L in final]
+    w.seq_lens.copy_(torch.tensor(lens, dtype=torch.int32))
+    meta = skv.build_page_meta(cache, ("box", "gauss"))
+    for _ in range(20):
+        lens = [L + 1 for L in lens]
+        w.seq_lens.copy_(torch.tensor(lens, dtype=torch.int32))
+        skv.append_page_meta(cache, meta, 1)
+    ref = skv.build_page_meta(cache, ("box", "gauss"))
+    torch.cuda.synchronize()
+    for phys in _used_pages(w, final):
+        assert torch.equal(meta.box[phys], ref.box[phys]) and torch.equal(meta.gauss[phys], ref.gauss[phys]), phys
