@@ -18,6 +18,8 @@
 //          query head) keeps the pairs with z' > max_all - 1, bisects tau, refines it with the
 //          closed form on the support (alpha = 2, 1.5), and accumulates p v reading V rows with
 //          p > 0 only.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -232,6 +234,38 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(CacheView c, const int3
 
 // ---------------------------------------------------------------- entmax pass 1
 
+// Per-head maximum and ordered compaction of z' > max - 1 for pass 1 (logits of the partition
+// in LDS: zs[h * rps + r]; rows past NR are not read). Every thread of the block must call it.
+template <int G>
+__device__ __forceinline__ void entmax_compact(const float *zs, int rps, int NR, int unit, int split, int nsplit,
+                                               int row0, float2 *__restrict__ cand, int32_t *__restrict__ cand_cnt,
+                                               float *__restrict__ cand_max, int *scan_scratch, float *redf) {
+  const int tid = threadIdx.x;
+  for (int h = 0; h < G; ++h) {
+    float mx = -INFINITY;
+    for (int r = tid; r < NR; r += kAttnThreads) mx = fmaxf(mx, zs[h * rps + r]);
+    mx = block_max<kAttnThreads>(mx, redf);
+    const size_t lid = ((size_t)unit * G + h) * nsplit + split;
+    float2 *cl = cand + lid * rps;
+    // ordered compaction of z' > mx - 1 (contiguous chunk of rows per thread)
+    const int per = (NR + kAttnThreads - 1) / kAttnThreads;
+    const int r0 = min(NR, tid * per), r1 = min(NR, r0 + per);
+    int nk = 0;
+    for (int r = r0; r < r1; ++r) nk += zs[h * rps + r] > mx - 1.0f;
+    int tot;
+    int pos = block_excl_scan<kAttnThreads>(nk, scan_scratch, &tot);
+    for (int r = r0; r < r1; ++r) {
+      const float z = zs[h * rps + r];
+      if (z > mx - 1.0f) cl[pos++] = make_float2(z, __int_as_float(row0 + r));
+    }
+    if (tid == 0) {
+      cand_cnt[lid] = tot;
+      cand_max[lid] = mx;
+    }
+  }
+}
+
+
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
     CacheView c, const T *__restrict__ q, const int32_t *__restrict__ sel_idx, const int32_t *__restrict__ sel_count,
@@ -287,28 +321,86 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
       if (r + u * RL::RGB < NR) logits(r + u * RL::RGB, o[u], kx[u]);
   }
   __syncthreads();
-  for (int h = 0; h < G; ++h) {
-    float mx = -INFINITY;
-    for (int r = tid; r < NR; r += kAttnThreads) mx = fmaxf(mx, zs[h * rps + r]);
-    mx = block_max<kAttnThreads>(mx, redf);
-    const size_t lid = ((size_t)unit * G + h) * nsplit + split;
-    float2 *cl = cand + lid * rps;
-    // ordered compaction of z' > mx - 1 (contiguous chunk of rows per thread)
-    const int per = (NR + kAttnThreads - 1) / kAttnThreads;
-    const int r0 = min(NR, tid * per), r1 = min(NR, r0 + per);
-    int nk = 0;
-    for (int r = r0; r < r1; ++r) nk += zs[h * rps + r] > mx - 1.0f;
-    int tot;
-    int pos = block_excl_scan<kAttnThreads>(nk, scan_scratch, &tot);
-    for (int r = r0; r < r1; ++r) {
-      const float z = zs[h * rps + r];
-      if (z > mx - 1.0f) cl[pos++] = make_float2(z, __int_as_float(it0 * rows_per_item + r));
+  entmax_compact<G>(zs, rps, NR, unit, split, nsplit, it0 * rows_per_item, cand, cand_cnt, cand_max, scan_scratch,
+                    redf);
+}
+
+// Entmax pass 1 for bf16 caches on the matrix cores: the logits of a 16-row tile for all G heads
+// are one 16 x 16 product of the tile's K rows (A, 16 x d) with q^T of the group (B, d x 16, heads
+// past G zero), d/32 v_mfma_f32_16x16x32_bf16 per tile. Lane l supplies A[l % 16][8 (l / 16) ..]
+// and B[8 (l / 16) ..][l % 16] of each 32-wide slice of d and receives the logits of rows
+// 4 (l / 16) .. + 3 for head l % 16. Each wave takes every fourth tile, with the K loads of UNR
+// tiles in flight before their products. bf16 products are exact and the sums are float32, as
+// on the VALU path.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D, int G>
+__global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_mfma_kernel(
+    CacheView c, const uint16_t *__restrict__ q, const int32_t *__restrict__ sel_idx,
+    const int32_t *__restrict__ sel_count, int cap, int gran, int spi, int nsplit, float zscale,
+    float2 *__restrict__ cand, int32_t *__restrict__ cand_cnt, float *__restrict__ cand_max) {
+  constexpr int KB = D / 32, UNR = 4, NWV = kAttnThreads / kWave;
+  extern __shared__ float zs[];  // [G][rps] logits, then [rps] row offsets (8-byte aligned)
+  __shared__ int scan_scratch[kAttnThreads / kWave + 1];
+  __shared__ float redf[kAttnThreads / kWave];
+  const int split = blockIdx.x, unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
+  const int count = min(max(sel_count[unit], 0), cap);
+  const int rows_per_item = gran ? 1 : c.S;
+  const int rps = spi * rows_per_item;
+  const int it0 = split * spi, it1 = min(count, it0 + spi);
+  const int NR = max(0, it1 - it0) * rows_per_item;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int L = seq_len(c, b);
+  RowMap rm{sel_idx + (size_t)unit * cap, c.bt + (size_t)b * c.maxP, gran, c.S, c.Hkv, g, D, L, num_pages(c, L)};
+  const int n = lane & 15, kq = 8 * (lane >> 4);
+  bf16x8_t qb[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (n < G) w = *reinterpret_cast<const uint4 *>(q + ((size_t)b * c.Hq + g * G + n) * D + 32 * kb + kq);
+    qb[kb] = __builtin_bit_cast(bf16x8_t, w);
+  }
+  long long *roff = reinterpret_cast<long long *>(zs + ((G * rps + 1) & ~1));
+  for (int r = tid; r < NR; r += kAttnThreads) {
+    const int it = r / rows_per_item;
+    roff[r] = rm.row_offset(it0 + it, r - it * rows_per_item);
+  }
+  __syncthreads();
+  const uint16_t *K = static_cast<const uint16_t *>(c.k);
+  const int ntile = (NR + 15) / 16;
+  for (int t0 = wave; t0 < ntile; t0 += NWV * UNR) {
+    bf16x8_t a[UNR][KB];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int row = (t0 + u * NWV) * 16 + (lane & 15);
+      const long long o = row < NR ? roff[row] : -1;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        uint4 w = make_uint4(0u, 0u, 0u, 0u);
+        if (o >= 0) w = *reinterpret_cast<const uint4 *>(K + o + 32 * kb + kq);
+        a[u][kb] = __builtin_bit_cast(bf16x8_t, w);
+      }
     }
-    if (tid == 0) {
-      cand_cnt[lid] = tot;
-      cand_max[lid] = mx;
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int tb = (t0 + u * NWV) * 16;
+      if (tb >= NR) break;
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][kb], qb[kb], acc, 0, 0, 0);
+      if (n < G) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = tb + 4 * (lane >> 4) + i;
+          if (r < NR) zs[n * rps + r] = roff[r] >= 0 ? acc[i] * zscale : -INFINITY;
+        }
+      }
     }
   }
+  __syncthreads();
+  entmax_compact<G>(zs, rps, NR, unit, split, nsplit, it0 * rows_per_item, cand, cand_cnt, cand_max, scan_scratch,
+                    redf);
 }
 
 // ---------------------------------------------------------------- entmax threshold and p V
@@ -533,9 +625,15 @@ static hipError_t attn_typed(const AttnArgs &a, hipStream_t st) {
   const int rps = a.spi * (a.gran ? 1 : c.S);
   const size_t lds = sizeof(float) * (size_t)((c.G * rps + 1) & ~1) + sizeof(long long) * (size_t)rps;
   const float zscale = a.sm_scale * (a.alpha - 1.0f);
-  SKV_ATTN_DISPATCH_G(c.G, attn_entmax_logits_kernel<T, D, GG><<<grid, kAttnThreads, lds, st>>>(
-                               c, q, a.sel_idx, a.sel_count, a.cap, a.gran, a.spi, a.nsplit, zscale, a.cand,
-                               a.cand_cnt, a.cand_max))
+  if constexpr (std::is_same<T, uint16_t>::value) {   // bf16: logits on the matrix cores
+    SKV_ATTN_DISPATCH_G(c.G, attn_entmax_logits_mfma_kernel<D, GG><<<grid, kAttnThreads, lds, st>>>(
+                                 c, q, a.sel_idx, a.sel_count, a.cap, a.gran, a.spi, a.nsplit, zscale, a.cand,
+                                 a.cand_cnt, a.cand_max))
+  } else {
+    SKV_ATTN_DISPATCH_G(c.G, attn_entmax_logits_kernel<T, D, GG><<<grid, kAttnThreads, lds, st>>>(
+                                 c, q, a.sel_idx, a.sel_count, a.cap, a.gran, a.spi, a.nsplit, zscale, a.cand,
+                                 a.cand_cnt, a.cand_max))
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int kind = a.alpha == 1.5f ? 1 : (a.alpha == 2.0f ? 2 : 3);

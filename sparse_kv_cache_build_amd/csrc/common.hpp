@@ -72,6 +72,12 @@ template <>
 struct Packed8<uint16_t> {
   uint4 w;
   __device__ __forceinline__ void load(const uint16_t *p) { w = *reinterpret_cast<const uint4 *>(p); }
+  __device__ __forceinline__ void zero() { w = make_uint4(0u, 0u, 0u, 0u); }
+  // element j (0..7) as float; j is a compile-time constant after unrolling
+  __device__ __forceinline__ float at(int j) const {
+    const uint32_t x = j < 2 ? w.x : j < 4 ? w.y : j < 6 ? w.z : w.w;
+    return (j & 1) ? bf16_hi(x) : bf16_lo(x);
+  }
   __device__ __forceinline__ float dot(const Packed8 &k) const {
     float acc = 0.0f;
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, k.w.x), acc, false);
@@ -86,6 +92,11 @@ template <>
 struct Packed8<float> {
   float x[8];
   __device__ __forceinline__ void load(const float *p) { Elem<float>::load8(p, x); }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = 0.0f;
+  }
+  __device__ __forceinline__ float at(int j) const { return x[j]; }
   __device__ __forceinline__ float dot(const Packed8 &k) const {
     float acc = 0.0f;
 #pragma unroll
