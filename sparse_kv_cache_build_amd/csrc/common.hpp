@@ -337,6 +337,25 @@ __device__ __forceinline__ double block_sum(double v, double *scratch) {
   return r;
 }
 
+// Block sums of two doubles in one reduction round (scratch: NT/64 double2).
+template <int NT>
+__device__ __forceinline__ void block_sum2(double &a, double &b, double2 *scratch) {
+  constexpr int NW = NT / kWave;
+  a = wave_sum(a);
+  b = wave_sum(b);
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[threadIdx.x / kWave] = make_double2(a, b);
+  __syncthreads();
+  a = 0.0;
+  b = 0.0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const double2 t = scratch[i];
+    a += t.x;
+    b += t.y;
+  }
+  __syncthreads();
+}
+
 template <int NT>
 __device__ __forceinline__ double block_max(double v, double *scratch) {
   constexpr int NW = NT / kWave;

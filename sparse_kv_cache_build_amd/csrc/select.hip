@@ -693,14 +693,25 @@ __device__ __forceinline__ void gauss_moment(float mu, float sd, bool sparsemax,
 }
 
 // tau_hat per (sequence, query head): root of F(tau) = sum_p n_p E_p(tau) - 1, which is convex
-// and non-increasing. Newton's method started at tau0 = (alpha-1) max_p m_p - 1, where F >= 0,
-// moves right monotonically without passing the root. Per-page terms in float32, sums in
-// float64. Stops when the step falls below 2^-22 max(1, |tau|) or after 64 steps.
-__global__ __launch_bounds__(256) void tau_hat_kernel(CacheView c, const float *__restrict__ m,
-                                                      const float *__restrict__ s, float alpha,
-                                                      float *__restrict__ tau_out) {
-  __shared__ double red[256 / kWave];
-  __shared__ float redf[256 / kWave];
+// and non-increasing. Start at tau0 = (alpha-1) max_p m_p - 1, where F >= 0. Far from the root F
+// falls off like a Gaussian tail, where plain Newton steps are short; each step is instead
+// Newton's on log S, S = F + 1 (-log(S) S / F'), which tends to the plain step as S -> 1 and comes
+// back from the right after a pass; while log S > 2 the step is halved (there the full step passes
+// the root by about half). A bracket [lo, hi] (F(lo) >= 0 > F(hi)) safeguards it: a
+// proposal outside falls back to the plain Newton step from the left (at or left of the root, F
+// being convex), else to bisection. Per-page terms in float32, sums in float64, one block
+// reduction per step. Stops when the bracket is below 2^-20 max(1, |tau|), when the plain step
+// -F/F' from either side is that small (then taken: F is at its float noise level), when tau (a
+// float) no longer moves, or after 64 steps. The
+// scaled page terms stay in LDS across the steps (pages beyond kTauLds are read each step).
+constexpr int kTauThreads = 1024;
+constexpr int kTauLds = 4096;
+__global__ __launch_bounds__(kTauThreads) void tau_hat_kernel(CacheView c, const float *__restrict__ m,
+                                                              const float *__restrict__ s, float alpha,
+                                                              float *__restrict__ tau_out) {
+  __shared__ float t_mu[kTauLds], t_sd[kTauLds], t_n[kTauLds];
+  __shared__ double2 red2[kTauThreads / kWave];
+  __shared__ float redf[kTauThreads / kWave];
   const int bh = blockIdx.x, b = bh / c.Hq;
   const int L = seq_len(c, b);
   const int P = num_pages(c, L);
@@ -712,41 +723,74 @@ __global__ __launch_bounds__(256) void tau_hat_kernel(CacheView c, const float *
   const float am1 = alpha - 1.0f;
   const bool sparsemax = alpha == 2.0f;
   float mx = -INFINITY;
-  for (int p = threadIdx.x; p < P; p += 256) mx = fmaxf(mx, mr[p]);
-  mx = block_max<256>(mx, redf);
-  float tau = am1 * mx - 1.0f;
+  for (int p = threadIdx.x; p < P; p += kTauThreads) {
+    const float mv = mr[p];
+    mx = fmaxf(mx, mv);
+    if (p < kTauLds) {
+      t_mu[p] = am1 * mv;
+      t_sd[p] = am1 * sr[p];
+      t_n[p] = (float)min(c.S, L - p * c.S);
+    }
+  }
+  mx = block_max<kTauThreads>(mx, redf);   // its barrier also publishes the LDS terms
+  float tau = am1 * mx - 1.0f, lo = tau, hi = INFINITY;
   for (int it = 0; it < 64; ++it) {
     double F = 0.0, dF = 0.0;
-    for (int p = threadIdx.x; p < P; p += 256) {
-      const float n = (float)min(c.S, L - p * c.S);
+    for (int p = threadIdx.x; p < P; p += kTauThreads) {
+      float mu, sd, n;
+      if (p < kTauLds) {
+        mu = t_mu[p];
+        sd = t_sd[p];
+        n = t_n[p];
+      } else {
+        mu = am1 * mr[p];
+        sd = am1 * sr[p];
+        n = (float)min(c.S, L - p * c.S);
+      }
       float E, dE;
-      gauss_moment(am1 * mr[p] - tau, am1 * sr[p], sparsemax, E, dE);
+      gauss_moment(mu - tau, sd, sparsemax, E, dE);
       F += (double)(n * E);
       dF += (double)(n * dE);
     }
-    F = block_sum<256>(F, red) - 1.0;
-    dF = block_sum<256>(dF, red);
-    if (!(F > 0.0) || !(dF < 0.0)) break;
-    const double step = -F / dF;
-    tau = (float)((double)tau + step);
-    if (step <= 0x1p-22 * fmax(1.0, fabs((double)tau))) break;
+    block_sum2<kTauThreads>(F, dF, red2);
+    F -= 1.0;
+    if (!(F != 0.0)) break;   // on the root, or not a number
+    if (F > 0.0) lo = tau; else hi = tau;
+    const double tol = 0x1p-20 * fmax(1.0, fabs((double)tau));
+    if ((double)hi - (double)lo <= tol) break;
+    const double S = F + 1.0;
+    const bool left_ok = F > 0.0 && dF < 0.0;
+    if (dF < 0.0 && fabs(F / dF) <= tol) {   // within the float noise of F: one plain step
+      tau = (float)((double)tau - F / dF);
+      break;
+    }
+    float next = NAN;
+    if (dF < 0.0 && S > 0.0) {
+      const double ls = log(S);
+      next = (float)((double)tau - (ls > 2.0 ? 0.5 : 1.0) * ls * S / dF);   // halved far out, where it overshoots
+    }
+    if (!(next > lo && next < hi) && left_ok) next = (float)((double)tau - F / dF);
+    if (!(next > lo && next < hi)) next = hi < INFINITY ? 0.5f * (lo + hi) : lo + 2.0f * (tau - lo + 1.0f);
+    if (next == tau) break;
+    tau = next;
   }
   if (threadIdx.x == 0) tau_out[bh] = tau;
 }
 
 // Keep page p of unit (b, g) iff some head h of g has (alpha-1) shat_h(p) > tau_h - delta;
 // ordered compaction.
-__global__ __launch_bounds__(256) void select_thresh_kernel(CacheView c, const float *__restrict__ shat,
-                                                            const float *__restrict__ tau, float alpha, float delta,
-                                                            int32_t *__restrict__ sel_idx,
-                                                            int32_t *__restrict__ sel_count, int cap) {
-  __shared__ int scan_scratch[256 / kWave + 1];
+constexpr int kThreshThreads = 1024;
+__global__ __launch_bounds__(kThreshThreads) void select_thresh_kernel(CacheView c, const float *__restrict__ shat,
+                                                                       const float *__restrict__ tau, float alpha,
+                                                                       float delta, int32_t *__restrict__ sel_idx,
+                                                                       int32_t *__restrict__ sel_count, int cap) {
+  __shared__ int scan_scratch[kThreshThreads / kWave + 1];
   const int unit = blockIdx.x, b = unit / c.Hkv, g = unit - b * c.Hkv;
   const int P = num_pages(c, seq_len(c, b));
   const float am1 = alpha - 1.0f;
   int32_t *out = sel_idx + (size_t)unit * cap;
   int base = 0;
-  for (int p0 = 0; p0 < P; p0 += 256) {
+  for (int p0 = 0; p0 < P; p0 += kThreshThreads) {
     const int p = p0 + threadIdx.x;
     int keep = 0;
     if (p < P)
@@ -755,7 +799,7 @@ __global__ __launch_bounds__(256) void select_thresh_kernel(CacheView c, const f
         if (am1 * shat[(size_t)bh * c.maxP + p] > tau[bh] - delta) keep = 1;
       }
     int tot;
-    const int pos = block_excl_scan<256>(keep, scan_scratch, &tot);
+    const int pos = block_excl_scan<kThreshThreads>(keep, scan_scratch, &tot);
     if (keep) out[base + pos] = p;
     base += tot;
   }
@@ -830,10 +874,10 @@ hipError_t launch_select_all(const CacheView &c, int tokens, int32_t *sel_idx, i
 
 hipError_t launch_select_thresh(const CacheView &c, const float *m, const float *s, const float *shat, float alpha,
                                 float delta, float *tau, int32_t *sel_idx, int32_t *sel_count, int cap, hipStream_t st) {
-  tau_hat_kernel<<<c.B * c.Hq, 256, 0, st>>>(c, m, s, alpha, tau);
+  tau_hat_kernel<<<c.B * c.Hq, kTauThreads, 0, st>>>(c, m, s, alpha, tau);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  select_thresh_kernel<<<c.B * c.Hkv, 256, 0, st>>>(c, shat, tau, alpha, delta, sel_idx, sel_count, cap);
+  select_thresh_kernel<<<c.B * c.Hkv, kThreshThreads, 0, st>>>(c, shat, tau, alpha, delta, sel_idx, sel_count, cap);
   return hipGetLastError();
 }
 
