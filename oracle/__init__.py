@@ -69,13 +69,18 @@ def _declare(L):
         "orc_meta_gauss": (None, [_P, _P, _P]),
         "orc_meta_proj": (None, [_P, _I, _P, _P]),
         "orc_score_box": (None, [_P, _P, _P, _P]),
-        "orc_score_gauss": (None, [_P, _P, _P, _D, _P, _P, _P]),
+        "orc_score_gauss": (None, [_P, _P, _P, _D, _I, _P, _P, _P]),
+        "orc_Phi_inv": (_D, [_D]),
+        "orc_Phi_inv_upper": (_D, [_D]),
         "orc_score_proj": (None, [_P, _I, _P, _P, _P]),
         "orc_select_topk": (_I, [_P, _I, _I, _P]),
         "orc_budget_k": (_I, [_I, _I]),
         "orc_gauss_partial_moment": (_D, [_D, _D, _D, _D]),
+        "orc_gauss_partial_moment_quad": (_D, [_D, _D, _D, _D]),
+        "orc_trunc_power_moment": (_D, [_D, _D]),
         "orc_tau_hat": (_D, [_P, _P, _P, _I, _D]),
         "orc_select_thresh": (_I, [_P, _P, _I, _I, _D, _D, _P]),
+        "orc_select_thresh_box": (_I, [_P, _P, _I, _I, _D, _D, _D, _P]),
         "orc_softmax": (None, [_P, _I, _P]),
         "orc_sparsemax": (_D, [_P, _I, _P]),
         "orc_entmax15": (_D, [_P, _I, _P]),
@@ -168,11 +173,22 @@ def score_box(c: Cache, kmin, kmax):
     return key
 
 
-def score_gauss(c: Cache, mean, var, scale: float):
+def score_gauss(c: Cache, mean, var, scale: float, quantile: bool = False):
+    """quantile: estimated maximum m + s Phi^-1(1 - 1/n) instead of m + s sqrt(2 ln n)."""
     shape = (c.B, c.Hq, c.maxP)
     m, s, shat = np.empty(shape), np.empty(shape), np.empty(shape)
-    lib().orc_score_gauss(c.ref, _ptr(mean), _ptr(var), float(scale), _ptr(m), _ptr(s), _ptr(shat))
+    lib().orc_score_gauss(c.ref, _ptr(mean), _ptr(var), float(scale), int(bool(quantile)), _ptr(m), _ptr(s),
+                          _ptr(shat))
     return m, s, shat
+
+
+def Phi_inv(p: float) -> float:
+    return float(lib().orc_Phi_inv(float(p)))
+
+
+def Phi_inv_upper(q: float) -> float:
+    """Phi^-1(1 - q)."""
+    return float(lib().orc_Phi_inv_upper(float(q)))
 
 
 def score_proj(c: Cache, P: np.ndarray, kproj: np.ndarray):
@@ -197,11 +213,31 @@ def gauss_partial_moment(mu: float, sd: float, tau: float, alpha: float) -> floa
     return float(lib().orc_gauss_partial_moment(mu, sd, tau, alpha))
 
 
+def gauss_partial_moment_quad(mu: float, sd: float, tau: float, alpha: float) -> float:
+    """The same expectation by quadrature for every alpha (the closed forms bypassed)."""
+    return float(lib().orc_gauss_partial_moment_quad(mu, sd, tau, alpha))
+
+
+def trunc_power_moment(a: float, k: float) -> float:
+    """E[(Z + a)_+^k], Z ~ N(0, 1)."""
+    return float(lib().orc_trunc_power_moment(float(a), float(k)))
+
+
 def tau_hat(m: np.ndarray, s: np.ndarray, n: np.ndarray, alpha: float) -> float:
     m = np.ascontiguousarray(m, dtype=np.float64)
     s = np.ascontiguousarray(s, dtype=np.float64)
     n = np.ascontiguousarray(n, dtype=np.int32)
     return float(lib().orc_tau_hat(_ptr(m), _ptr(s), _ptr(n), m.size, float(alpha)))
+
+
+def select_thresh_box(key: np.ndarray, tau: np.ndarray, scale: float, alpha: float, delta: float) -> np.ndarray:
+    key = np.ascontiguousarray(key, dtype=np.float64)
+    tau = np.ascontiguousarray(tau, dtype=np.float64)
+    P = key.size
+    out = np.empty(max(P, 1), dtype=np.int32)
+    n = lib().orc_select_thresh_box(_ptr(key), _ptr(tau), tau.size, P, float(scale), float(alpha), float(delta),
+                                    _ptr(out))
+    return out[:n].copy()
 
 
 def select_thresh(shat: np.ndarray, tau: np.ndarray, alpha: float, delta: float) -> np.ndarray:

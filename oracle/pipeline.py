@@ -6,7 +6,7 @@ selection -> attention over the selected KV only; [JSSA] abstract for the token-
 
   metadata  box (kmin, kmax) | gauss (mean, var) | proj (k~ = RN_bf16(P k))
   scores    box key per (b, g, page) | gauss (m, s, shat) per (b, h, page) | proj key per (b, g, token)
-  select    topk(k) | budget(pct) | thresh(alpha, delta) | token_topk(k) | all
+  select    topk(k) | budget(pct) | thresh(alpha, delta) | thresh_box(alpha, delta) | token_topk(k) | all
   attend    alpha = 1 (softmax) or alpha in (1, 2] (entmax) per query head over the selection
 """
 from __future__ import annotations
@@ -17,13 +17,13 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from . import (Cache, attend_full_head, attend_head, budget_k, meta_box, meta_gauss, meta_proj,
-               score_box, score_gauss, score_proj, select_thresh, select_topk, tau_hat)
+               score_box, score_gauss, score_proj, select_thresh, select_thresh_box, select_topk, tau_hat)
 
 
 @dataclass
 class Spec:
     score: str                 # 'box' | 'gauss' | 'proj'
-    policy: str                # 'topk' | 'budget' | 'thresh' | 'token_topk' | 'all'
+    policy: str                # 'topk' | 'budget' | 'thresh' | 'thresh_box' | 'token_topk' | 'all'
     k: int = 0
     pct: int = 0
     sel_alpha: float = 1.5     # alpha of the Gaussian threshold
@@ -31,6 +31,7 @@ class Spec:
     alphas: tuple = (1.0,)     # attention alphas to evaluate
     scale: float = 0.0         # logit scale; 0 means 1/sqrt(d)
     proj: np.ndarray | None = None
+    gauss_max: str = "sqrt2log"  # estimated page maximum: m + s sqrt(2 ln n) | 'quantile': m + s Phi^-1(1 - 1/n)
 
 
 @dataclass
@@ -61,24 +62,31 @@ def scale_of(spec: Spec, d: int) -> float:
     return spec.scale if spec.scale else 1.0 / math.sqrt(d)
 
 
+def _needs(spec: Spec):
+    """Score kinds a step needs: the threshold with the box key uses both box and Gaussian."""
+    return {spec.score} | ({"box", "gauss"} if spec.policy == "thresh_box" else set())
+
+
 def build_metadata(c: Cache, spec: Spec) -> Metadata:
     md = Metadata()
-    if spec.score == "box":
+    kinds = _needs(spec)
+    if "box" in kinds:
         md.kmin, md.kmax = meta_box(c)
-    elif spec.score == "gauss":
+    if "gauss" in kinds:
         md.mean, md.var = meta_gauss(c)
-    elif spec.score == "proj":
+    if "proj" in kinds:
         md.kproj = meta_proj(c, spec.proj)
     return md
 
 
 def compute_scores(c: Cache, spec: Spec, md: Metadata) -> Scores:
     sc = Scores()
-    if spec.score == "box":
+    kinds = _needs(spec)
+    if "box" in kinds:
         sc.key = score_box(c, md.kmin, md.kmax)
-    elif spec.score == "gauss":
-        sc.m, sc.s, sc.shat = score_gauss(c, md.mean, md.var, scale_of(spec, c.d))
-    elif spec.score == "proj":
+    if "gauss" in kinds:
+        sc.m, sc.s, sc.shat = score_gauss(c, md.mean, md.var, scale_of(spec, c.d), spec.gauss_max == "quantile")
+    if "proj" in kinds:
         sc.key = score_proj(c, spec.proj, md.kproj)
     return sc
 
@@ -98,13 +106,16 @@ def select_unit(c: Cache, spec: Spec, sc: Scores, b: int, g: int) -> UnitResult:
         return UnitResult(sel=select_topk(sc.key[b, g, :P_b], budget_k(P_b, spec.pct)))
     if spec.policy == "token_topk":
         return UnitResult(sel=select_topk(sc.key[b, g, :L_b], spec.k))
-    if spec.policy == "thresh":
+    if spec.policy in ("thresh", "thresh_box"):
         heads = range(g * c.G, g * c.G + c.G)
         if P_b == 0:
             return UnitResult(sel=np.zeros(0, np.int32), tau_hat=np.full(c.G, np.nan))
         n = page_counts(c, b)
         taus = np.array([tau_hat(sc.m[b, h, :P_b], sc.s[b, h, :P_b], n, spec.sel_alpha) for h in heads])
-        sel = select_thresh(sc.shat[b, g * c.G:(g + 1) * c.G, :P_b], taus, spec.sel_alpha, spec.delta)
+        if spec.policy == "thresh":
+            sel = select_thresh(sc.shat[b, g * c.G:(g + 1) * c.G, :P_b], taus, spec.sel_alpha, spec.delta)
+        else:
+            sel = select_thresh_box(sc.key[b, g, :P_b], taus, scale_of(spec, c.d), spec.sel_alpha, spec.delta)
         return UnitResult(sel=sel, tau_hat=taus)
     raise ValueError(spec.policy)
 

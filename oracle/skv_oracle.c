@@ -212,9 +212,38 @@ void orc_score_box(const orc_cache *c, const double *kmin, const double *kmax, f
  * s = scale * sqrt(sum_j q_j^2 var_j). The "estimated maximum score" of s2.B is read as
  * shat = m + s * sqrt(2 ln n_p), the standard bound on the expected maximum of n_p Gaussians
  * (shat = m when n_p = 1). Outputs [B, Hq, maxP]; invalid pages get NaN. */
-void orc_score_gauss(const orc_cache *c, const double *mean, const double *var, double scale,
+static double orc_Phi(double a);
+
+/* Phi^-1(p) for 0 < p < 1: bisection on Phi over [-40, 40] down to adjacent doubles. */
+double orc_Phi_inv(double p) {
+  double lo = -40.0, hi = 40.0;
+  for (int it = 0; it < 200 && hi - lo > 0.0; ++it) {
+    double mid = 0.5 * (lo + hi);
+    if (mid <= lo || mid >= hi) break;
+    if (orc_Phi(mid) < p) lo = mid; else hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+/* Phi^-1(1 - q) for 0 < q < 1, accurate in the upper tail: bisection on the upper tail
+ * Q(x) = erfc(x / sqrt 2) / 2 = q (1 - q itself would lose the digits of a small q). */
+double orc_Phi_inv_upper(double q) {
+  double lo = -40.0, hi = 40.0;
+  for (int it = 0; it < 200 && hi - lo > 0.0; ++it) {
+    double mid = 0.5 * (lo + hi);
+    if (mid <= lo || mid >= hi) break;
+    if (0.5 * erfc(mid / sqrt(2.0)) > q) lo = mid; else hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+void orc_score_gauss(const orc_cache *c, const double *mean, const double *var, double scale, int32_t quantile,
                      double *m, double *s, double *shat) {
   int32_t G = c->Hq / c->Hkv;
+  /* the estimated-maximum factor per page size n: sqrt(2 ln n), or Phi^-1(1 - 1/n) (quantile) */
+  double *fac = (double *)malloc(sizeof(double) * (size_t)(c->S + 1));
+  for (int32_t n = 1; n <= c->S; ++n)
+    fac[n] = n == 1 ? 0.0 : (quantile ? orc_Phi_inv_upper(1.0 / n) : sqrt(2.0 * log((double)n)));
   for (int32_t b = 0; b < c->B; ++b)
     for (int32_t h = 0; h < c->Hq; ++h)
       for (int32_t p = 0; p < c->maxP; ++p) {
@@ -233,8 +262,9 @@ void orc_score_gauss(const orc_cache *c, const double *mean, const double *var, 
         int32_t n = orc_page_tokens(c, b, p);
         m[o] = scale * sm;
         s[o] = scale * sqrt(sv);
-        shat[o] = m[o] + s[o] * sqrt(2.0 * log((double)n));
+        shat[o] = m[o] + s[o] * fac[n];
       }
+  free(fac);
 }
 
 /* [JSSA] abstract, token-level scoring in the shared subspace: q~_h = RN_f32(P q_h) (float64
@@ -324,12 +354,52 @@ int32_t orc_budget_k(int32_t P_b, int32_t pct) {
 static double orc_Phi(double a) { return 0.5 * erfc(-a / sqrt(2.0)); }
 static double orc_phi(double a) { return exp(-0.5 * a * a) / sqrt(2.0 * acos(-1.0)); }
 
-/* E[(X - tau)_+^(1/(alpha-1))] for X ~ N(mu_x, sd_x^2), in closed form for alpha = 2
- * (first partial moment) and alpha = 1.5 (second partial moment). With mu = mu_x - tau and
- * a = mu / sd: alpha = 2 gives mu Phi(a) + sd phi(a); alpha = 1.5 gives
- * (mu^2 + sd^2) Phi(a) + mu sd phi(a). A zero sd gives the point-mass value. */
+/* I_k(a) = integral over u >= 0 of u^k phi(u - a) du, the k-th truncated power moment of a unit
+ * Gaussian shifted by a: E[(Z + a)_+^k] for Z ~ N(0, 1). The integrand is smooth on (0, inf) and
+ * below 1e-300 beyond u = max(a, 0) + 40. Adaptive Simpson (Lyness' error estimate, tolerance
+ * halved at each split), run separately on panels of width at most 1/2 so that no peak falls
+ * between the sample points of a coarse first estimate. */
+static double orc_ik_f(double u, double a, double k) { return pow(u, k) * exp(-0.5 * (u - a) * (u - a)); }
+
+static double orc_simpson(double a, double k, double l, double r, double fl, double fm, double fr, double whole,
+                          double tol, int depth) {
+  double m = 0.5 * (l + r), lm = 0.5 * (l + m), rm = 0.5 * (m + r);
+  double flm = orc_ik_f(lm, a, k), frm = orc_ik_f(rm, a, k);
+  double left = (m - l) / 6.0 * (fl + 4.0 * flm + fm), right = (r - m) / 6.0 * (fm + 4.0 * frm + fr);
+  double diff = left + right - whole;
+  if (depth <= 0 || fabs(diff) <= 15.0 * tol) return left + right + diff / 15.0;
+  return orc_simpson(a, k, l, m, fl, flm, fm, left, 0.5 * tol, depth - 1) +
+         orc_simpson(a, k, m, r, fm, frm, fr, right, 0.5 * tol, depth - 1);
+}
+
+double orc_trunc_power_moment(double a, double k) {
+  if (a < -40.0) return 0.0;
+  double U = (a > 0.0 ? a : 0.0) + 40.0;
+  int panels = (int)ceil(U / 0.5);
+  double h = U / panels, sum = 0.0;
+  for (int i = 0; i < panels; ++i) {
+    double l = i * h, r = l + h, m = 0.5 * (l + r);
+    double fl = orc_ik_f(l, a, k), fm = orc_ik_f(m, a, k), fr = orc_ik_f(r, a, k);
+    double whole = h / 6.0 * (fl + 4.0 * fm + fr);
+    sum += orc_simpson(a, k, l, r, fl, fm, fr, whole, 1e-14 * fabs(whole) + 1e-300, 30);
+  }
+  return sum / sqrt(2.0 * acos(-1.0));
+}
+
+/* E[(X - tau)_+^(1/(alpha-1))] for X ~ N(mu_x, sd_x^2). With mu = mu_x - tau and a = mu / sd:
+ * alpha = 2 (first partial moment) gives mu Phi(a) + sd phi(a); alpha = 1.5 (second) gives
+ * (mu^2 + sd^2) Phi(a) + mu sd phi(a); any other alpha in (1, 2) gives sd^k I_k(a) with
+ * k = 1/(alpha-1) by quadrature (orc_trunc_power_moment). A zero sd gives the point-mass value
+ * mu_+^k. orc_gauss_partial_moment_quad always takes the quadrature (used to pin it). */
+double orc_gauss_partial_moment_quad(double mu_x, double sd_x, double tau, double alpha) {
+  double mu = mu_x - tau, k = 1.0 / (alpha - 1.0);
+  if (sd_x == 0.0) return mu > 0 ? pow(mu, k) : 0.0;
+  return pow(sd_x, k) * orc_trunc_power_moment(mu / sd_x, k);
+}
+
 double orc_gauss_partial_moment(double mu_x, double sd_x, double tau, double alpha) {
   double mu = mu_x - tau;
+  if (alpha != 2.0 && alpha != 1.5) return orc_gauss_partial_moment_quad(mu_x, sd_x, tau, alpha);
   if (sd_x == 0.0) {
     double pos = mu > 0 ? mu : 0.0;
     return alpha == 2.0 ? pos : pos * pos;
@@ -346,7 +416,7 @@ double orc_gauss_partial_moment(double mu_x, double sd_x, double tau, double alp
  * (alpha-1) max_p m_p - 1 gives F(lo) >= 0 (Jensen: E[f(X)] >= f(E X) for the convex
  * f(x) = (x - tau)_+^(1/(alpha-1)), and the top page alone contributes >= 1); hi is pushed
  * right by doubling until F(hi) < 0; then bisection until hi - lo <= 2^-40 max(1, |lo|).
- * Only pages with n_p > 0 enter. alpha must be 1.5 or 2. Returns tau_hat (NaN if P = 0). */
+ * Only pages with n_p > 0 enter; alpha in (1, 2]. Returns tau_hat (NaN if P = 0). */
 static double orc_F(const double *m, const double *s, const int32_t *n, int32_t P, double alpha, double tau) {
   double f = -1.0;
   for (int32_t p = 0; p < P; ++p)
@@ -384,6 +454,22 @@ int32_t orc_select_thresh(const double *shat, const double *tau_hat, int32_t G, 
       if ((alpha - 1.0) * shat[(size_t)hh * P + p] > tau_hat[hh] - delta) keep = 1;
     if (keep) out[cnt++] = p;
   }
+  return cnt;
+}
+
+/* The threshold policy with the box bound as the page's estimated maximum (reading: the box
+ * key of a KV head is max over its G query heads of the unscaled bound U_h(p), so the test
+ * compares it with the lowest threshold of the group): keep page p iff
+ * (alpha-1) scale key[p] > min_h tau_hat_h - delta. Any page the per-head test
+ * (alpha-1) scale U_h(p) > tau_hat_h - delta keeps is kept. Emits ascending indices. */
+int32_t orc_select_thresh_box(const double *key, const double *tau_hat, int32_t G, int32_t P, double scale,
+                              double alpha, double delta, int32_t *out) {
+  double tmin = INFINITY;
+  for (int32_t hh = 0; hh < G; ++hh)
+    if (tau_hat[hh] < tmin) tmin = tau_hat[hh];
+  int32_t cnt = 0;
+  for (int32_t p = 0; p < P; ++p)
+    if ((alpha - 1.0) * scale * key[p] > tmin - delta) out[cnt++] = p;
   return cnt;
 }
 

@@ -302,6 +302,124 @@ def test_tau_hat_brackets_root_of_monotone_equation(orc):
         assert tau >= 0.5 * m.max() - 1
 
 
+def _phi(a):
+    return math.exp(-0.5 * a * a) / math.sqrt(2 * math.pi)
+
+
+def _Phi(a):
+    return 0.5 * scipy.special.erfc(-a / math.sqrt(2))
+
+
+@pytest.mark.parametrize("a", [-6.0, -3.5, -0.7, 0.0, 0.4, 2.0, 9.0, 35.0])
+def test_truncated_power_moment_matches_closed_forms_at_integer_powers(orc, a):
+    # E[(Z + a)_+^k] for integer k: k = 1, 2, 3 reduce to Phi and phi (scipy's erfc here); below
+    # a = -6 the closed forms cancel catastrophically, and the quadrature is pinned by scipy instead
+    closed = {1: a * _Phi(a) + _phi(a),
+              2: (a * a + 1) * _Phi(a) + a * _phi(a),
+              3: (a ** 3 + 3 * a) * _Phi(a) + (a * a + 2) * _phi(a)}
+    for k, want in closed.items():
+        assert orc.trunc_power_moment(a, k) == pytest.approx(want, rel=1e-10, abs=1e-300)
+
+
+@pytest.mark.parametrize("k", [1.25, 1.6, 2.5, 4.0, 10.0])
+def test_truncated_power_moment_matches_scipy_quad(orc, k):
+    for a in (-12.0, -6.0, -1.3, 0.0, 0.8, 3.0, 12.0):
+        f = lambda u: u ** k * _phi(u - a)
+        ref, _ = scipy.integrate.quad(f, 0.0, max(a, 0.0) + 40.0, epsabs=1e-300, epsrel=1e-12, limit=400,
+                                      points=[max(a, 0.0)])
+        assert orc.trunc_power_moment(a, k) == pytest.approx(ref, rel=1e-9, abs=1e-300)
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0])
+def test_general_alpha_moment_reproduces_closed_forms(orc, alpha):
+    rng = _rng(31)
+    for _ in range(30):
+        mu, sd, tau = rng.normal(0, 2), rng.uniform(0.05, 3), rng.normal(0, 2)
+        assert orc.gauss_partial_moment_quad(mu, sd, tau, alpha) == pytest.approx(
+            orc.gauss_partial_moment(mu, sd, tau, alpha), rel=1e-10, abs=1e-14)
+    assert orc.gauss_partial_moment_quad(2.0, 0.0, 0.5, 1.25) == pytest.approx(1.5 ** 4, rel=1e-15)   # point mass
+    assert orc.gauss_partial_moment_quad(0.2, 0.0, 0.5, 1.25) == 0.0
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.75])
+def test_tau_hat_general_alpha_degenerate_pages_equal_exact_entmax_threshold(orc, alpha):
+    # s = 0 turns the normalization equation into the exact entmax normalization over n_p copies
+    # of m_p; the oracle's entmax for these alpha is its own bisection on the logits
+    rng = _rng(32)
+    for _ in range(6):
+        P = int(rng.integers(1, 30))
+        m = rng.normal(0, 2, P)
+        n = rng.integers(1, 17, P).astype(np.int32)
+        tau = orc.tau_hat(m, np.zeros(P), n, alpha)
+        _, tau_exact = orc.entmax(np.repeat(m, n), alpha)
+        assert tau == pytest.approx(tau_exact, abs=1e-9)
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.8])
+def test_tau_hat_general_alpha_is_root_of_equation_by_scipy(orc, alpha):
+    rng = _rng(33)
+    P = 12
+    m, s = rng.normal(0, 1, P), rng.uniform(0.1, 1.5, P)
+    n = np.full(P, 16, np.int32)
+    tau = orc.tau_hat(m, s, n, alpha)
+    k = 1.0 / (alpha - 1.0)
+
+    def F(t):
+        tot = -1.0
+        for mm, ss, nn in zip(m, s, n):
+            mu, sd = (alpha - 1) * mm, (alpha - 1) * ss
+            f = lambda x: (x - t) ** k * _phi((x - mu) / sd) / sd
+            v, _ = scipy.integrate.quad(f, t, max(t, mu) + 40 * sd, epsabs=1e-300, epsrel=1e-11, limit=200)
+            tot += nn * v
+        return tot
+    assert abs(F(tau)) < 1e-7
+    assert F(tau - 1e-3) > 0 > F(tau + 1e-3)
+
+
+def test_phi_inverse_matches_scipy_ppf_and_isf(orc):
+    import scipy.stats
+    for p in (1e-12, 0.01, 0.25, 0.5, 0.75, 15 / 16, 31 / 32, 63 / 64):
+        assert orc.Phi_inv(p) == pytest.approx(scipy.stats.norm.ppf(p), rel=1e-12, abs=1e-12)
+    for n in (2, 3, 16, 64, 1024, 10 ** 9):
+        assert orc.Phi_inv_upper(1 / n) == pytest.approx(scipy.stats.norm.isf(1 / n), rel=1e-12, abs=1e-12)
+
+
+def test_score_gauss_quantile_max_uses_phi_inverse(orc):
+    c = _f32_cache(_rng(34), B=1, Hq=2, Hkv=1, d=16, S=8, lens=(29,))
+    mean, var = orc.meta_gauss(c)
+    m, s, shat = orc.score_gauss(c, mean, var, 0.25)
+    mq, sq, shatq = orc.score_gauss(c, mean, var, 0.25, quantile=True)
+    assert np.array_equal(m, mq) and np.array_equal(s, sq)
+    import scipy.stats
+    for p in range(c.pages(0)):
+        n = c.page_tokens(0, p)
+        fac = scipy.stats.norm.isf(1 / n) if n > 1 else 0.0
+        assert shatq[0, :, p] == pytest.approx(m[0, :, p] + s[0, :, p] * fac, rel=1e-12, abs=1e-12)
+        assert shat[0, :, p] == pytest.approx(m[0, :, p] + s[0, :, p] * math.sqrt(2 * math.log(n)), rel=1e-12,
+                                              abs=1e-12)
+
+
+def test_select_thresh_box_is_the_box_test_and_covers_the_per_head_test(orc):
+    # brute force: keep iff (alpha-1) scale key > min tau - delta, key = max over the group's heads of
+    # the unscaled box bound; every page that some head's own bound would keep is kept
+    c = _f32_cache(_rng(35), B=1, Hq=4, Hkv=1, d=16, S=8, lens=(200,))
+    kmin, kmax = orc.meta_box(c)
+    key = orc.score_box(c, kmin, kmax)[0, 0, :c.pages(0)].astype(np.float64)
+    q = _dec(c.q)[0]
+    U = np.zeros((4, c.pages(0)))
+    for p in range(c.pages(0)):
+        lo, hi = kmin[c.block_table[0, p], 0].astype(np.float64), kmax[c.block_table[0, p], 0].astype(np.float64)
+        U[:, p] = np.maximum(q * lo, q * hi).sum(1)
+    taus = np.array([0.4, 0.9, 0.7, 1.3])
+    scale, alpha, delta = 0.25, 1.5, 0.1
+    got = orc.select_thresh_box(key, taus, scale, alpha, delta)
+    want = np.nonzero((alpha - 1) * scale * key > taus.min() - delta)[0]
+    assert np.array_equal(got, want)
+    per_head = np.nonzero(((alpha - 1) * scale * U > (taus - delta)[:, None]).any(0))[0]
+    assert set(per_head) <= set(got)
+    assert np.allclose(key, U.max(0), rtol=1e-6)
+
+
 def test_select_thresh_keeps_iff_some_head_clears_threshold(orc):
     shat = np.array([[0.0, 3.0, 1.0, 2.0], [2.5, 0.0, 0.0, 0.5]])
     tau = np.array([1.2, 1.0])
