@@ -117,11 +117,11 @@ skv_status skv_append_page_meta(const skv_cache *c, const skv_meta *m, int32_t n
 
 /* ------------------------------------------------------------------ scores */
 
-enum { SKV_SCORE_BOX = 0, SKV_SCORE_GAUSS = 1, SKV_SCORE_PROJ = 2 };
+enum { SKV_SCORE_BOX = 0, SKV_SCORE_GAUSS = 1, SKV_SCORE_PROJ = 2, SKV_SCORE_GAUSS_Q = 3 };
 
 typedef struct skv_scores {
   float *key;   /* BOX: [B, Hkv, max_pages]; PROJ: [B, Hkv, max_pages * S] */
-  float *m;     /* GAUSS: [B, Hq, max_pages] Gaussian mean of the scaled scores of the page */
+  float *m;     /* GAUSS, GAUSS_Q: [B, Hq, max_pages] Gaussian mean of the scaled scores of the page */
   float *s;     /* GAUSS: [B, Hq, max_pages] its standard deviation */
   float *shat;  /* GAUSS: [B, Hq, max_pages] estimated maximum m + s sqrt(2 ln n_p) */
   int32_t token_k; /* PROJ only. 0: write every key into `key`. k > 0: write only the token candidates
@@ -146,6 +146,9 @@ enum { SKV_TOKEN_PHASE_ALL = 0, SKV_TOKEN_PHASE_BOUND = 1, SKV_TOKEN_PHASE_FILTE
  *          page's box; float64 sum over j ascending (products are exact), unscaled.
  *   GAUSS: per query head, m = sm_scale sum_j q_j mean_j, s = sm_scale sqrt(sum_j q_j^2 var_j),
  *          shat = m + s sqrt(2 ln n_p) (n_p valid tokens of the page; shat = m for n_p = 1).
+ *   GAUSS_Q: the same m and s (GAUSS metadata, GAUSS outputs), with the estimated maximum
+ *          shat = m + s Phi^-1(1 - 1/n_p), the normal quantile exceeded by one of n_p draws on
+ *          average ("EntmaxKV" s2.B leaves the estimate open).
  *   PROJ:  q~_h = RN_f32(proj q_h) (float64 sum), u_h(t) = sum_i q~_h[i] k~_t[i] (float64 sum,
  *          i ascending), key[b][g][t] = RN_f32(max over the G heads of g of u_h(t)).
  * Entries past the sequence (p >= ceil(L_b / S), or t >= L_b) are -inf (BOX, PROJ) or NaN
@@ -163,16 +166,18 @@ enum {
   SKV_SEL_BUDGET = 1,       /* the ceil(budget_pct * P_b / 100) pages (at least 1) with the largest BOX key */
   SKV_SEL_THRESH_GAUSS = 2, /* Gaussian-aware entmax threshold (GAUSS scores) */
   SKV_SEL_TOKEN_TOPK = 3,   /* the k tokens with the largest PROJ key */
-  SKV_SEL_ALL = 4           /* every page (tokens == 0) or every token (tokens == 1): full cache */
+  SKV_SEL_ALL = 4,          /* every page (tokens == 0) or every token (tokens == 1): full cache */
+  SKV_SEL_THRESH_BOX = 5    /* the entmax threshold of THRESH_GAUSS tested against the BOX key */
 };
 
 typedef struct skv_select_params {
   int32_t policy;     /* SKV_SEL_* */
   int32_t k;          /* TOPK, TOKEN_TOPK: k >= 1 */
   int32_t budget_pct; /* BUDGET: 1..100 */
-  float alpha;        /* THRESH_GAUSS: 1.5 or 2 */
-  float delta;        /* THRESH_GAUSS: safety margin Delta >= 0, in units of tau */
+  float alpha;        /* THRESH_GAUSS, THRESH_BOX: 1 < alpha <= 2 */
+  float delta;        /* THRESH_GAUSS, THRESH_BOX: safety margin Delta >= 0, in units of tau */
   int32_t tokens;     /* ALL: 0 pages, 1 tokens */
+  float scale;        /* THRESH_BOX: the logit scale c (z = c q . k) the GAUSS scores were taken with */
 } skv_select_params;
 
 /* Candidate selection, one selection per (sequence, KV head) shared by its G query heads
@@ -182,10 +187,17 @@ typedef struct skv_select_params {
  *   THRESH_GAUSS ("EntmaxKV" s2.B policy 2): per query head, tau_hat solves
  *     sum_p n_p E[((alpha-1) Z_p - tau)_+^(1/(alpha-1))] = 1 with Z_p ~ N(m_p, s_p^2); a page is
  *     kept iff some head h of the group has (alpha-1) shat_h(p) > tau_hat_h - delta.
- *     tau_hat [B, Hq] float32 receives the thresholds (unused pointer otherwise).
+ *     tau_hat [B, Hq] float32 receives the thresholds (unused pointer otherwise). alpha = 1.5
+ *     and 2 use the closed forms of the expectation; any other alpha in (1, 2) evaluates it by
+ *     Gauss-Legendre quadrature (about 20x the work per page and step).
+ *   THRESH_BOX: tau_hat as THRESH_GAUSS (from the GAUSS m, s); the page's estimated maximum is
+ *     the deterministic box bound ("EntmaxKV" s2.A): keep iff (alpha-1) scale key[p] >
+ *     min_h tau_hat_h - delta, key = the BOX key (max over the group's heads of the unscaled
+ *     bound). No page the per-head box test would keep is dropped. Needs the BOX key and the
+ *     GAUSS m, s in the same skv_scores.
  * Output: sel_idx [B, Hkv, cap] int32 holds the kept logical page (or token) indices in
  * ascending order, sel_count [B, Hkv] int32 their number; entries past the count are not
- * written. cap must be >= k (TOPK, TOKEN_TOPK), >= max_pages (BUDGET, THRESH_GAUSS, ALL pages)
+ * written. cap must be >= k (TOPK, TOKEN_TOPK), >= max_pages (BUDGET, THRESH_*, ALL pages)
  * or >= max_pages * S (ALL tokens), else SKV_ERR_CAPACITY. workspace: skv_workspace_bytes(c,
  * SKV_OP_SELECT, p, cap). The scores are those written by skv_score_pages for the same cache. */
 skv_status skv_select_pages(const skv_cache *c, const skv_scores *sc, const skv_select_params *p,

@@ -355,33 +355,83 @@ static double orc_Phi(double a) { return 0.5 * erfc(-a / sqrt(2.0)); }
 static double orc_phi(double a) { return exp(-0.5 * a * a) / sqrt(2.0 * acos(-1.0)); }
 
 /* I_k(a) = integral over u >= 0 of u^k phi(u - a) du, the k-th truncated power moment of a unit
- * Gaussian shifted by a: E[(Z + a)_+^k] for Z ~ N(0, 1). The integrand is smooth on (0, inf) and
- * below 1e-300 beyond u = max(a, 0) + 40. Adaptive Simpson (Lyness' error estimate, tolerance
- * halved at each split), run separately on panels of width at most 1/2 so that no peak falls
- * between the sample points of a coarse first estimate. */
-static double orc_ik_f(double u, double a, double k) { return pow(u, k) * exp(-0.5 * (u - a) * (u - a)); }
+ * Gaussian shifted by a: E[(Z + a)_+^k] for Z ~ N(0, 1). The integrand is below 1e-40 of its peak
+ * outside [max(0, a - 14), max(a, 0) + 14] (u^k grows with u). Adaptive Gauss-Legendre on panels
+ * of width at most 1/2 over that range: a 20-point
+ * rule on an interval is accepted when it agrees with the rule on its two halves to 1e-14
+ * relative, else both halves are refined. The 20 nodes and weights are the roots of the Legendre
+ * polynomial P_20 (Newton from the Chebyshev-like guesses) and 2 / ((1 - x^2) P_20'(x)^2). On the
+ * panel that starts at 0 the variable is u = h v^2, so that the u^k endpoint becomes the smooth
+ * v^(2k+1). */
+#define ORC_GL_N 20
+static double orc_gl_x[ORC_GL_N], orc_gl_w[ORC_GL_N];
+static int orc_gl_ready = 0;
 
-static double orc_simpson(double a, double k, double l, double r, double fl, double fm, double fr, double whole,
-                          double tol, int depth) {
-  double m = 0.5 * (l + r), lm = 0.5 * (l + m), rm = 0.5 * (m + r);
-  double flm = orc_ik_f(lm, a, k), frm = orc_ik_f(rm, a, k);
-  double left = (m - l) / 6.0 * (fl + 4.0 * flm + fm), right = (r - m) / 6.0 * (fm + 4.0 * frm + fr);
-  double diff = left + right - whole;
-  if (depth <= 0 || fabs(diff) <= 15.0 * tol) return left + right + diff / 15.0;
-  return orc_simpson(a, k, l, m, fl, flm, fm, left, 0.5 * tol, depth - 1) +
-         orc_simpson(a, k, m, r, fm, frm, fr, right, 0.5 * tol, depth - 1);
+static void orc_gl_init(void) {
+  const int n = ORC_GL_N;
+  for (int i = 0; i < n; ++i) {
+    double x = cos(acos(-1.0) * (i + 0.75) / (n + 0.5)), dp = 1.0;
+    for (int it = 0; it < 100; ++it) {
+      double p0 = 1.0, p1 = x;   /* P_0, P_1; then the three-term recurrence up to P_n */
+      for (int m = 2; m <= n; ++m) {
+        double p2 = ((2.0 * m - 1.0) * x * p1 - (m - 1.0) * p0) / m;
+        p0 = p1;
+        p1 = p2;
+      }
+      dp = n * (x * p1 - p0) / (x * x - 1.0);
+      double dx = p1 / dp;
+      x -= dx;
+      if (fabs(dx) < 1e-16) break;
+    }
+    orc_gl_x[i] = x;
+    orc_gl_w[i] = 2.0 / ((1.0 - x * x) * dp * dp);
+  }
+  orc_gl_ready = 1;
+}
+
+/* the integrand on [l, r]; sq: the panel variable is v with u = sq * v^2 */
+static double orc_gl_rule(double a, double k, double l, double r, double sq) {
+  double c = 0.5 * (l + r), h = 0.5 * (r - l), sum = 0.0;
+  for (int i = 0; i < ORC_GL_N; ++i) {
+    double t = c + h * orc_gl_x[i], u = t, jac = 1.0;
+    if (sq > 0.0) {
+      u = sq * t * t;
+      jac = 2.0 * sq * t;
+    }
+    sum += orc_gl_w[i] * pow(u, k) * exp(-0.5 * (u - a) * (u - a)) * jac;
+  }
+  return h * sum;
+}
+
+static double orc_gl_adapt(double a, double k, double l, double r, double sq, double whole, double floor_abs,
+                           int depth) {
+  double m = 0.5 * (l + r);
+  double left = orc_gl_rule(a, k, l, m, sq), right = orc_gl_rule(a, k, m, r, sq);
+  double diff = fabs(left + right - whole);
+  if (depth <= 0 || diff <= 1e-14 * fabs(left + right) || diff <= floor_abs) return left + right;
+  return orc_gl_adapt(a, k, l, m, sq, left, floor_abs, depth - 1) +
+         orc_gl_adapt(a, k, m, r, sq, right, floor_abs, depth - 1);
 }
 
 double orc_trunc_power_moment(double a, double k) {
+  if (!orc_gl_ready) orc_gl_init();
   if (a < -40.0) return 0.0;
-  double U = (a > 0.0 ? a : 0.0) + 40.0;
-  int panels = (int)ceil(U / 0.5);
-  double h = U / panels, sum = 0.0;
+  /* u^k grows with u, so below u = a - 14 the integrand is also below 1e-40 of its peak */
+  double L0 = a > 14.0 ? a - 14.0 : 0.0, U = (a > 0.0 ? a : 0.0) + 14.0;
+  int panels = (int)ceil((U - L0) / 0.5);
+  double h = (U - L0) / panels, sum = 0.0, est[64], coarse = 0.0;
+  /* a coarse pass first: a panel whose refinement changes less than 1e-16 of the whole integral
+   * is accepted even where its own relative change stays larger (near underflow) */
   for (int i = 0; i < panels; ++i) {
-    double l = i * h, r = l + h, m = 0.5 * (l + r);
-    double fl = orc_ik_f(l, a, k), fm = orc_ik_f(m, a, k), fr = orc_ik_f(r, a, k);
-    double whole = h / 6.0 * (fl + 4.0 * fm + fr);
-    sum += orc_simpson(a, k, l, r, fl, fm, fr, whole, 1e-14 * fabs(whole) + 1e-300, 30);
+    int at0 = i == 0 && L0 == 0.0;   /* a first panel at 0 in v over [0, 1] with u = h v^2 */
+    double l = at0 ? 0.0 : L0 + i * h, r = at0 ? 1.0 : L0 + (i + 1) * h, sq = at0 ? h : 0.0;
+    est[i] = orc_gl_rule(a, k, l, r, sq);
+    coarse += fabs(est[i]);
+  }
+  for (int i = 0; i < panels; ++i) {
+    int at0 = i == 0 && L0 == 0.0;
+    double l = at0 ? 0.0 : L0 + i * h, r = at0 ? 1.0 : L0 + (i + 1) * h, sq = at0 ? h : 0.0;
+    sum += orc_gl_adapt(a, k, l, r, sq, est[i], 1e-16 * coarse, 25);
   }
   return sum / sqrt(2.0 * acos(-1.0));
 }

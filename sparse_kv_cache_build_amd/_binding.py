@@ -20,8 +20,8 @@ LIB_PATH = os.path.join(_PKG, "libskv.so")
 SKV_OK, SKV_ERR_INVALID_ARG, SKV_ERR_UNSUPPORTED, SKV_ERR_CAPACITY, SKV_ERR_WORKSPACE, SKV_ERR_HIP = range(6)
 DTYPE_F32, DTYPE_BF16 = 0, 1
 META_BOX, META_GAUSS, META_PROJ = 1, 2, 4
-SCORE_BOX, SCORE_GAUSS, SCORE_PROJ = 0, 1, 2
-SEL_TOPK, SEL_BUDGET, SEL_THRESH_GAUSS, SEL_TOKEN_TOPK, SEL_ALL = range(5)
+SCORE_BOX, SCORE_GAUSS, SCORE_PROJ, SCORE_GAUSS_Q = 0, 1, 2, 3
+SEL_TOPK, SEL_BUDGET, SEL_THRESH_GAUSS, SEL_TOKEN_TOPK, SEL_ALL, SEL_THRESH_BOX = range(6)
 OP_SCORE, OP_SELECT, OP_ATTN, OP_CANDIDATES = 0, 1, 2, 3
 
 EXPORTS = ("skv_build_page_meta", "skv_append_page_meta", "skv_score_pages", "skv_select_pages",
@@ -53,7 +53,7 @@ class Scores(C.Structure):
 
 class SelectParams(C.Structure):
     _fields_ = [("policy", C.c_int32), ("k", C.c_int32), ("budget_pct", C.c_int32), ("alpha", C.c_float),
-                ("delta", C.c_float), ("tokens", C.c_int32)]
+                ("delta", C.c_float), ("tokens", C.c_int32), ("scale", C.c_float)]
 
 
 class AttnParams(C.Structure):
@@ -184,7 +184,7 @@ def _workspace(cache, nbytes: int):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=cache.device)
 
 
-_KIND = {"box": SCORE_BOX, "gauss": SCORE_GAUSS, "proj": SCORE_PROJ}
+_KIND = {"box": SCORE_BOX, "gauss": SCORE_GAUSS, "proj": SCORE_PROJ, "gauss_q": SCORE_GAUSS_Q}
 
 
 class ScoreBuffers:
@@ -203,7 +203,7 @@ class ScoreBuffers:
             self.cand = torch.empty(n, dtype=torch.uint8, device=dev)
         elif kind == "proj":
             self.key = torch.empty((B, Hkv, maxP * S), dtype=torch.float32, device=dev)
-        elif kind == "gauss":
+        elif kind in ("gauss", "gauss_q"):
             self.m, self.s, self.shat = (torch.empty((B, Hq, maxP), dtype=torch.float32, device=dev) for _ in range(3))
         else:
             raise ValueError(kind)
@@ -234,11 +234,28 @@ def score_pages(cache: PagedCache, meta: PageMeta, q, kind: str, sm_scale=None, 
 
 
 _POLICY = {"topk": SEL_TOPK, "budget": SEL_BUDGET, "thresh": SEL_THRESH_GAUSS, "token_topk": SEL_TOKEN_TOPK,
-           "all": SEL_ALL}
+           "all": SEL_ALL, "thresh_box": SEL_THRESH_BOX}
 
 
-def select_params(policy: str, k=0, budget_pct=0, alpha=1.5, delta=0.0, tokens=0) -> SelectParams:
-    return SelectParams(_POLICY[policy], int(k), int(budget_pct), float(alpha), float(delta), int(tokens))
+def select_params(policy: str, k=0, budget_pct=0, alpha=1.5, delta=0.0, tokens=0, scale=0.0) -> SelectParams:
+    """scale: the logit scale of the Gaussian scores (thresh_box only)."""
+    return SelectParams(_POLICY[policy], int(k), int(budget_pct), float(alpha), float(delta), int(tokens),
+                        float(scale))
+
+
+class CombinedScores:
+    """One skv_scores holding the BOX key of `box` and the Gaussian m, s, shat of `gauss` (the
+    threshold policy with the box key reads both)."""
+
+    def __init__(self, box: "ScoreBuffers", gauss: "ScoreBuffers"):
+        self.parts = (box, gauss)
+        self.key, self.m, self.s, self.shat = box.key, gauss.m, gauss.s, gauss.shat
+        self.sc = Scores(box.key.data_ptr(), gauss.m.data_ptr(), gauss.s.data_ptr(), gauss.shat.data_ptr(), 0,
+                         None, 0)
+
+    @property
+    def ref(self):
+        return C.byref(self.sc)
 
 
 def select_cap(cache: PagedCache, p: SelectParams) -> int:
@@ -263,9 +280,12 @@ class Selection:
         self.granularity = 1 if (p.policy == SEL_TOKEN_TOPK or (p.policy == SEL_ALL and p.tokens)) else 0
 
 
-def select_pages(cache: PagedCache, scores: ScoreBuffers, policy: str, k=0, budget_pct=0, alpha=1.5, delta=0.0,
-                 tokens=0, cap=None, out: Selection | None = None, stream=None) -> Selection:
-    p = out.p if out is not None else select_params(policy, k, budget_pct, alpha, delta, tokens)
+def select_pages(cache: PagedCache, scores, policy: str, k=0, budget_pct=0, alpha=1.5, delta=0.0,
+                 tokens=0, cap=None, out: Selection | None = None, stream=None, scale=None) -> Selection:
+    """scores: ScoreBuffers, or CombinedScores for the threshold with the box key. scale: the logit
+    scale of the Gaussian scores (default 1/sqrt(d))."""
+    sc = float(scale) if scale is not None else 1.0 / math.sqrt(cache.d)
+    p = out.p if out is not None else select_params(policy, k, budget_pct, alpha, delta, tokens, sc)
     out = out or Selection(cache, p, cap)
     _check(lib().skv_select_pages(cache.ref, scores.ref, C.byref(p), _ptr(out.idx), _ptr(out.count), out.cap,
                                   _ptr(out.tau_hat), _ptr(out.ws), out.ws.numel(), _stream(stream)),

@@ -136,7 +136,7 @@ skv_status skv_workspace_bytes(const skv_cache *c, int32_t op, const void *param
   if (st != SKV_OK) return st;
   if (op == SKV_OP_SCORE) {
     const int kind = *static_cast<const int32_t *>(params);
-    if (kind < SKV_SCORE_BOX || kind > SKV_SCORE_PROJ) return SKV_ERR_INVALID_ARG;
+    if (kind < SKV_SCORE_BOX || kind > SKV_SCORE_GAUSS_Q) return SKV_ERR_INVALID_ARG;
     *bytes = score_ws(c, kind, 64);
     return SKV_OK;
   }
@@ -213,7 +213,7 @@ skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q,
   const CacheView v = view(c);
   if (kind == SKV_SCORE_BOX) {
     if (!(m->kinds & SKV_META_BOX) || !m->box || !out->key || !aligned(m->box, 16)) return SKV_ERR_INVALID_ARG;
-  } else if (kind == SKV_SCORE_GAUSS) {
+  } else if (kind == SKV_SCORE_GAUSS || kind == SKV_SCORE_GAUSS_Q) {
     if (!(m->kinds & SKV_META_GAUSS) || !m->gauss || !out->m || !out->s || !out->shat || !aligned(m->gauss, 16))
       return SKV_ERR_INVALID_ARG;
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SKV_ERR_INVALID_ARG;
@@ -249,8 +249,9 @@ skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q,
   hipError_t e;
   if (kind == SKV_SCORE_BOX)
     e = skv::launch_score_box(v, c->dtype, q, m->box, out->key, ws, s);
-  else if (kind == SKV_SCORE_GAUSS)
-    e = skv::launch_score_gauss(v, c->dtype, q, m->gauss, (double)sm_scale, out->m, out->s, out->shat, ws, s);
+  else if (kind == SKV_SCORE_GAUSS || kind == SKV_SCORE_GAUSS_Q)
+    e = skv::launch_score_gauss(v, c->dtype, q, m->gauss, (double)sm_scale, kind == SKV_SCORE_GAUSS_Q, out->m,
+                                out->s, out->shat, ws, s);
   else
     e = skv::launch_score_proj(v, c->dtype, q, m->proj_rank, m->proj, m->kproj, out->key, ws, s);
   return hip_status(e);
@@ -290,12 +291,17 @@ skv_status skv_select_pages(const skv_cache *c, const skv_scores *sc, const skv_
       return hip_status(
           skv::launch_select_topk(v, sc->key, maxP, p->policy, 0, p->budget_pct, sel_idx, sel_count, cap, s));
     }
-    case SKV_SEL_THRESH_GAUSS: {
-      if (!sc->m || !sc->s || !sc->shat || !tau_hat) return SKV_ERR_INVALID_ARG;
+    case SKV_SEL_THRESH_GAUSS:
+    case SKV_SEL_THRESH_BOX: {
+      const bool box = p->policy == SKV_SEL_THRESH_BOX;
+      if (!sc->m || !sc->s || !tau_hat || (box ? !sc->key : !sc->shat)) return SKV_ERR_INVALID_ARG;
       if (!std::isfinite(p->delta) || p->delta < 0.0f) return SKV_ERR_INVALID_ARG;
       if (!std::isfinite(p->alpha) || !(p->alpha > 1.0f && p->alpha <= 2.0f)) return SKV_ERR_INVALID_ARG;
-      if (p->alpha != 1.5f && p->alpha != 2.0f) return SKV_ERR_UNSUPPORTED;
+      if (box && (!std::isfinite(p->scale) || !(p->scale > 0.0f))) return SKV_ERR_INVALID_ARG;
       if (cap < maxP) return SKV_ERR_CAPACITY;
+      if (box)
+        return hip_status(skv::launch_select_thresh_box(v, sc->m, sc->s, sc->key, p->alpha, p->scale, p->delta, tau_hat,
+                                                        sel_idx, sel_count, cap, s));
       return hip_status(skv::launch_select_thresh(v, sc->m, sc->s, sc->shat, p->alpha, p->delta, tau_hat, sel_idx,
                                                   sel_count, cap, s));
     }

@@ -27,8 +27,8 @@ hipError_t launch_build_meta(const CacheView &c, int dtype, int tail, void *box,
                              const float *proj, uint16_t *kproj, hipStream_t st);
 hipError_t launch_score_box(const CacheView &c, int dtype, const void *q, const void *box, float *key, double *ws,
                             hipStream_t st);
-hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, const float *gauss, double scale, float *m,
-                              float *s, float *shat, double *ws, hipStream_t st);
+hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, const float *gauss, double scale,
+                              int quantile, float *m, float *s, float *shat, double *ws, hipStream_t st);
 hipError_t launch_score_proj(const CacheView &c, int dtype, const void *q, int r, const float *proj,
                              const uint16_t *kproj, float *key, double *ws, hipStream_t st);
 hipError_t launch_score_proj_cand(const CacheView &c, int r, const uint16_t *kproj, char *cand, hipStream_t st);
@@ -40,6 +40,11 @@ hipError_t launch_select_topk(const CacheView &c, const float *key, int key_stri
                               int32_t *sel_idx, int32_t *sel_count, int cap, hipStream_t st);
 hipError_t launch_select_all(const CacheView &c, int tokens, int32_t *sel_idx, int32_t *sel_count, int cap,
                              hipStream_t st);
+hipError_t launch_tau_hat(const CacheView &c, const float *m, const float *s, float alpha, float *tau,
+                          hipStream_t st);
+hipError_t launch_select_thresh_box(const CacheView &c, const float *m, const float *s, const float *key, float alpha,
+                                    float scale, float delta, float *tau, int32_t *sel_idx, int32_t *sel_count,
+                                    int cap, hipStream_t st);
 hipError_t launch_select_thresh(const CacheView &c, const float *m, const float *s, const float *shat, float alpha,
                                 float delta, float *tau, int32_t *sel_idx, int32_t *sel_count, int cap, hipStream_t st);
 hipError_t launch_attn(const AttnArgs &a, hipStream_t st);

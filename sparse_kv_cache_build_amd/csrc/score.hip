@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void score_box_kernel(CacheView c, const T *__
 // q_j^2 var_j) (float64), shat = m + s sqrt(2 ln n_p). Outputs [B, Hq, maxP].
 template <int D, int G>
 __global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const float *__restrict__ gauss,
-                                                          const double *__restrict__ qpm, double scale,
+                                                          const double *__restrict__ qpm, double scale, int quantile,
                                                           float *__restrict__ m_out, float *__restrict__ s_out,
                                                           float *__restrict__ shat_out) {
   const int unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
@@ -129,7 +129,9 @@ __global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const flo
       }
     }
   }
-  const double lg = sqrt(2.0 * log((double)n));
+  // estimated maximum of the page's n scores: m + s sqrt(2 ln n), or (quantile) m + s Phi^-1(1 - 1/n)
+  // = m + s sqrt(2) erfcinv(2 / n)
+  const double lg = n <= 1 ? 0.0 : (quantile ? 1.4142135623730951 * erfcinv(2.0 / n) : sqrt(2.0 * log((double)n)));
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const double m = scale * sm[h], s = scale * sqrt(sv[h]);
@@ -307,19 +309,21 @@ hipError_t launch_score_box(const CacheView &c, int dtype, const void *q, const 
 }
 
 template <int D>
-static hipError_t gauss_d(const CacheView &c, const float *gauss, const double *qpm, double scale, float *m, float *s,
+static hipError_t gauss_d(const CacheView &c, const float *gauss, const double *qpm, double scale, int quantile, float *m, float *s,
                           float *shat, hipStream_t st) {
   const dim3 grid((c.maxP + 255) / 256, c.B * c.Hkv);
-  SKV_DISPATCH_G(c.G, score_gauss_kernel<D, GG><<<grid, 256, 0, st>>>(c, gauss, qpm, scale, m, s, shat))
+  SKV_DISPATCH_G(c.G, score_gauss_kernel<D, GG><<<grid, 256, 0, st>>>(c, gauss, qpm, scale, quantile, m, s, shat))
   return hipGetLastError();
 }
 
-hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, const float *gauss, double scale, float *m,
+hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, const float *gauss, double scale,
+                              int quantile, float *m,
                               float *s, float *shat, double *ws, hipStream_t st) {
   const int n = c.B * c.Hq * c.D;
   hipError_t e = dtype == 0 ? qprep_pair<float>(q, n, 1, ws, st) : qprep_pair<uint16_t>(q, n, 1, ws, st);
   if (e != hipSuccess) return e;
-  return c.D == 64 ? gauss_d<64>(c, gauss, ws, scale, m, s, shat, st) : gauss_d<128>(c, gauss, ws, scale, m, s, shat, st);
+  return c.D == 64 ? gauss_d<64>(c, gauss, ws, scale, quantile, m, s, shat, st)
+                    : gauss_d<128>(c, gauss, ws, scale, quantile, m, s, shat, st);
 }
 
 template <int R>

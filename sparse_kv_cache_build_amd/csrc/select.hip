@@ -692,6 +692,60 @@ __device__ __forceinline__ void gauss_moment(float mu, float sd, bool sparsemax,
   }
 }
 
+// E[(X - tau)_+^k] for any power k = 1/(alpha-1) >= 1 and its tau-derivative -k E[(X - tau)_+^(k-1)],
+// X ~ N(mu + tau, sd^2) (mu = mean - tau): sd^k I_k(a) and -k sd^(k-1) I_(k-1)(a) with a = mu / sd and
+// I_j(a) = integral over u >= 0 of u^j phi(u - a) du. Gauss-Legendre, 8 nodes per panel of width at
+// most 2 over [max(0, a - 9), max(0, a) + 9] (phi is below 3e-18 of its peak outside); the panel
+// that starts at 0 is integrated in v with u = h v^2, which smooths the u^k endpoint. a < -9:
+// both are below float resolution and taken as 0.
+__device__ __forceinline__ void gauss_moment_general(float mu, float sd, float k, float &E, float &dE) {
+  if (sd <= 0.0f) {
+    const float pos = fmaxf(mu, 0.0f);
+    E = pos > 0.0f ? powf(pos, k) : 0.0f;
+    dE = pos > 0.0f ? -k * powf(pos, k - 1.0f) : 0.0f;
+    return;
+  }
+  const float a = mu / sd;
+  if (a < -9.0f) {
+    E = 0.0f;
+    dE = 0.0f;
+    return;
+  }
+  // Gauss-Legendre abscissae and weights of order 8 on [-1, 1] (positive half)
+  const float gx[4] = {0.18343464249564980f, 0.52553240991632899f, 0.79666647741362674f, 0.96028985649753623f};
+  const float gw[4] = {0.36268378337836198f, 0.31370664587788729f, 0.22238103445337447f, 0.10122853629037626f};
+  const float lo = fmaxf(a - 9.0f, 0.0f), hi = fmaxf(a, 0.0f) + 9.0f;
+  const int np = (int)ceilf(0.5f * (hi - lo));
+  const float h = (hi - lo) / np;
+  float ik = 0.0f, ik1 = 0.0f;
+  for (int pn = 0; pn < np; ++pn) {
+    const float l = lo + pn * h;
+    const bool at0 = l == 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x = i < 4 ? -gx[3 - i] : gx[i - 4];
+      const float w = i < 4 ? gw[3 - i] : gw[i - 4];
+      const float t = 0.5f * (1.0f + x);
+      float u, wt;
+      if (at0) {   // u = h t^2, du = 2 h t dt
+        u = h * t * t;
+        wt = w * 0.5f * 2.0f * h * t;
+      } else {
+        u = l + h * t;
+        wt = w * 0.5f * h;
+      }
+      const float d = u - a;
+      const float e = expf(-0.5f * d * d) * wt;
+      const float p1 = powf(u, k - 1.0f);
+      ik1 += p1 * e;
+      ik += p1 * u * e;
+    }
+  }
+  const float c = 0.39894228040143268f;   // 1 / sqrt(2 pi)
+  E = powf(sd, k) * ik * c;
+  dE = -k * powf(sd, k - 1.0f) * ik1 * c;
+}
+
 // tau_hat per (sequence, query head): root of F(tau) = sum_p n_p E_p(tau) - 1, which is convex
 // and non-increasing. Start at tau0 = (alpha-1) max_p m_p - 1, where F >= 0. Far from the root F
 // falls off like a Gaussian tail, where plain Newton steps are short; each step is instead
@@ -706,6 +760,8 @@ __device__ __forceinline__ void gauss_moment(float mu, float sd, bool sparsemax,
 // scaled page terms stay in LDS across the steps (pages beyond kTauLds are read each step).
 constexpr int kTauThreads = 1024;
 constexpr int kTauLds = 4096;
+// KIND: 0 alpha = 1.5, 1 alpha = 2 (closed forms), 2 any other alpha in (1, 2) (quadrature)
+template <int KIND>
 __global__ __launch_bounds__(kTauThreads) void tau_hat_kernel(CacheView c, const float *__restrict__ m,
                                                               const float *__restrict__ s, float alpha,
                                                               float *__restrict__ tau_out) {
@@ -721,7 +777,7 @@ __global__ __launch_bounds__(kTauThreads) void tau_hat_kernel(CacheView c, const
     return;
   }
   const float am1 = alpha - 1.0f;
-  const bool sparsemax = alpha == 2.0f;
+  const float kpow = 1.0f / am1;
   float mx = -INFINITY;
   for (int p = threadIdx.x; p < P; p += kTauThreads) {
     const float mv = mr[p];
@@ -748,7 +804,10 @@ __global__ __launch_bounds__(kTauThreads) void tau_hat_kernel(CacheView c, const
         n = (float)min(c.S, L - p * c.S);
       }
       float E, dE;
-      gauss_moment(mu - tau, sd, sparsemax, E, dE);
+      if (KIND == 2)
+        gauss_moment_general(mu - tau, sd, kpow, E, dE);
+      else
+        gauss_moment(mu - tau, sd, KIND == 1, E, dE);
       F += (double)(n * E);
       dF += (double)(n * dE);
     }
@@ -798,6 +857,35 @@ __global__ __launch_bounds__(kThreshThreads) void select_thresh_kernel(CacheView
         const int bh = b * c.Hq + g * c.G + h;
         if (am1 * shat[(size_t)bh * c.maxP + p] > tau[bh] - delta) keep = 1;
       }
+    int tot;
+    const int pos = block_excl_scan<kThreshThreads>(keep, scan_scratch, &tot);
+    if (keep) out[base + pos] = p;
+    base += tot;
+  }
+  if (threadIdx.x == 0) sel_count[unit] = base;
+}
+
+// The threshold policy with the box bound as the page's estimated maximum ("EntmaxKV" summary
+// s2.A's deterministic bound in s2.B's threshold test): keep page p of unit (b, g) iff
+// (alpha-1) scale key[p] > min_h tau_h - delta over the G heads of g, key = the unit's box key
+// (max over its heads of the unscaled bound). Every page the per-head box test would keep is kept.
+__global__ __launch_bounds__(kThreshThreads) void select_thresh_box_kernel(CacheView c, const float *__restrict__ key,
+                                                                           const float *__restrict__ tau, float alpha,
+                                                                           float scale, float delta,
+                                                                           int32_t *__restrict__ sel_idx,
+                                                                           int32_t *__restrict__ sel_count, int cap) {
+  __shared__ int scan_scratch[kThreshThreads / kWave + 1];
+  const int unit = blockIdx.x, b = unit / c.Hkv, g = unit - b * c.Hkv;
+  const int P = num_pages(c, seq_len(c, b));
+  float tmin = INFINITY;
+  for (int h = 0; h < c.G; ++h) tmin = fminf(tmin, tau[b * c.Hq + g * c.G + h]);
+  const float bar = tmin - delta, f = (alpha - 1.0f) * scale;
+  const float *kr = key + (size_t)unit * c.maxP;
+  int32_t *out = sel_idx + (size_t)unit * cap;
+  int base = 0;
+  for (int p0 = 0; p0 < P; p0 += kThreshThreads) {
+    const int p = p0 + threadIdx.x;
+    const int keep = p < P && f * kr[p] > bar;
     int tot;
     const int pos = block_excl_scan<kThreshThreads>(keep, scan_scratch, &tot);
     if (keep) out[base + pos] = p;
@@ -872,10 +960,31 @@ hipError_t launch_select_all(const CacheView &c, int tokens, int32_t *sel_idx, i
   return hipGetLastError();
 }
 
+hipError_t launch_tau_hat(const CacheView &c, const float *m, const float *s, float alpha, float *tau,
+                          hipStream_t st) {
+  const dim3 grid(c.B * c.Hq);
+  if (alpha == 1.5f)
+    tau_hat_kernel<0><<<grid, kTauThreads, 0, st>>>(c, m, s, alpha, tau);
+  else if (alpha == 2.0f)
+    tau_hat_kernel<1><<<grid, kTauThreads, 0, st>>>(c, m, s, alpha, tau);
+  else
+    tau_hat_kernel<2><<<grid, kTauThreads, 0, st>>>(c, m, s, alpha, tau);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_thresh_box(const CacheView &c, const float *m, const float *s, const float *key, float alpha,
+                                    float scale, float delta, float *tau, int32_t *sel_idx, int32_t *sel_count,
+                                    int cap, hipStream_t st) {
+  hipError_t e = launch_tau_hat(c, m, s, alpha, tau, st);
+  if (e != hipSuccess) return e;
+  select_thresh_box_kernel<<<c.B * c.Hkv, kThreshThreads, 0, st>>>(c, key, tau, alpha, scale, delta, sel_idx,
+                                                                   sel_count, cap);
+  return hipGetLastError();
+}
+
 hipError_t launch_select_thresh(const CacheView &c, const float *m, const float *s, const float *shat, float alpha,
                                 float delta, float *tau, int32_t *sel_idx, int32_t *sel_count, int cap, hipStream_t st) {
-  tau_hat_kernel<<<c.B * c.Hq, kTauThreads, 0, st>>>(c, m, s, alpha, tau);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_tau_hat(c, m, s, alpha, tau, st);
   if (e != hipSuccess) return e;
   select_thresh_kernel<<<c.B * c.Hkv, kThreshThreads, 0, st>>>(c, shat, tau, alpha, delta, sel_idx, sel_count, cap);
   return hipGetLastError();

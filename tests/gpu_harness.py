@@ -28,10 +28,12 @@ def log(*a):
 
 def spec_of(w: W.Workload, alphas=None) -> pipeline.Spec:
     cfg = w.cfg
-    return pipeline.Spec(score=cfg["score"], policy=cfg["policy"], k=cfg.get("k", 0), pct=cfg.get("pct", 0),
+    score = "gauss" if cfg["score"] == "gauss_q" else cfg["score"]
+    return pipeline.Spec(score=score, policy=cfg["policy"], k=cfg.get("k", 0), pct=cfg.get("pct", 0),
                          sel_alpha=cfg.get("sel_alpha", 1.5), delta=cfg.get("delta", 0.0),
                          alphas=tuple(alphas or cfg["alphas"]),
-                         proj=w.proj.cpu().numpy() if w.proj is not None else None)
+                         proj=w.proj.cpu().numpy() if w.proj is not None else None,
+                         gauss_max="quantile" if cfg["score"] == "gauss_q" else "sqrt2log")
 
 
 @dataclass
@@ -48,10 +50,13 @@ def gpu_step(w: W.Workload, alphas=None, split=0, policy=None, cap=None, fused=F
     cfg = w.cfg
     cache = skv.PagedCache(w.k, w.v, w.block_table, w.seq_lens, w.Hq)
     kind = cfg["score"]
-    meta = skv.build_page_meta(cache, (kind,), proj=w.proj)
     pol = policy or cfg["policy"]
+    meta_kinds = ("gauss" if kind == "gauss_q" else kind,) + (("box",) if pol == "thresh_box" else ())
+    meta = skv.build_page_meta(cache, meta_kinds, proj=w.proj)
     token_k = cfg.get("k", 0) if (fused and kind == "proj" and pol == "token_topk") else 0
     scores = skv.score_pages(cache, meta, w.q, kind, token_k=token_k)
+    if pol == "thresh_box":   # the box key beside the Gaussian m, s in one skv_scores
+        scores = skv.CombinedScores(skv.score_pages(cache, meta, w.q, "box"), scores)
     sel = skv.select_pages(cache, scores, pol, k=cfg.get("k", 0), budget_pct=cfg.get("pct", 0),
                            alpha=cfg.get("sel_alpha", 1.5), delta=cfg.get("delta", 0.0),
                            tokens=1 if kind == "proj" else 0, cap=cap)
@@ -91,12 +96,16 @@ def compare(w: W.Workload, st: GpuStep, seqs=None, alphas=None, check_meta=True)
     rep = Report()
     pm = h["phys_map"]
     G = w.G
-    if check_meta:
+    if check_meta and spec.policy != "thresh_box":
         _compare_meta(w, st, c, md, pm, spec)
     idx = st.sel.idx.cpu().numpy()
     cnt = st.sel.count.cpu().numpy()
     outs = {a: o.cpu().numpy() for a, o in st.outs.items()}
-    gkey = st.scores.key.cpu().numpy() if st.scores.key is not None else None
+    gkey = st.scores.key.cpu().numpy() if (st.scores.key is not None and spec.policy != "thresh_box") else None
+    if spec.policy == "thresh_box":   # the box key of the combined scores: bit-exact as well
+        bk = st.scores.key.cpu().numpy()
+        for i, b in enumerate(seqs):
+            assert np.array_equal(bk[b, :, :c.maxP], sc.key[i, :, :c.maxP]), f"box key mismatch in sequence {b}"
     for i, b in enumerate(seqs):
         for g in range(w.Hkv):
             rep.units += 1
@@ -110,7 +119,7 @@ def compare(w: W.Workload, st: GpuStep, seqs=None, alphas=None, check_meta=True)
             r = pipeline.select_unit(c, spec, sc, i, g)
             got = idx[b, g, :cnt[b, g]]
             same = len(got) == len(r.sel) and np.array_equal(got, r.sel)
-            if spec.policy == "thresh":
+            if spec.policy in ("thresh", "thresh_box"):
                 tau_g = st.sel.tau_hat[b, g * G:(g + 1) * G].cpu().numpy().astype(np.float64)
                 if np.all(np.isnan(r.tau_hat)):          # empty sequence: no threshold
                     assert np.all(np.isnan(tau_g)) and len(got) == 0, (b, g, tau_g, got)
@@ -119,8 +128,13 @@ def compare(w: W.Workload, st: GpuStep, seqs=None, alphas=None, check_meta=True)
                     (b, g, tau_g, r.tau_hat)
                 if not same:
                     diff = np.setxor1d(got, r.sel)
-                    shat = sc.shat[i, g * G:(g + 1) * G, :]
-                    margin = np.max((spec.sel_alpha - 1.0) * shat[:, diff] - (r.tau_hat[:, None] - spec.delta), axis=0)
+                    if spec.policy == "thresh":
+                        shat = sc.shat[i, g * G:(g + 1) * G, :]
+                        margin = np.max((spec.sel_alpha - 1.0) * shat[:, diff] - (r.tau_hat[:, None] - spec.delta),
+                                        axis=0)
+                    else:
+                        margin = ((spec.sel_alpha - 1.0) * pipeline.scale_of(spec, c.d) * sc.key[i, g, diff]
+                                  - (r.tau_hat.min() - spec.delta))
                     assert np.all(np.abs(margin) <= TAU_TOL * max(1.0, np.abs(r.tau_hat).max())), (b, g, diff, margin)
                     rep.near_ties += len(diff)
             else:

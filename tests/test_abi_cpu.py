@@ -111,7 +111,7 @@ def test_select_capacity_and_policy_checks(L):
 
     def sel(policy, cap, **kw):
         p = B.SelectParams(policy, kw.get("k", 0), kw.get("pct", 0), kw.get("alpha", 1.5), kw.get("delta", 0.5),
-                           kw.get("tokens", 0))
+                           kw.get("tokens", 0), kw.get("scale", 0.1))
         return L.skv_select_pages(C.byref(c), C.byref(sc), C.byref(p), C.c_void_p(FAKE), C.c_void_p(FAKE), cap,
                                   C.c_void_p(FAKE), None, 0, None)
 
@@ -121,7 +121,10 @@ def test_select_capacity_and_policy_checks(L):
     assert sel(B.SEL_BUDGET, 3, pct=5) == B.SKV_ERR_CAPACITY        # ceil(5% of 64) = 4
     assert sel(B.SEL_BUDGET, 4, pct=0) == B.SKV_ERR_INVALID_ARG
     assert sel(B.SEL_THRESH_GAUSS, 63, alpha=1.5) == B.SKV_ERR_CAPACITY
-    assert sel(B.SEL_THRESH_GAUSS, 64, alpha=1.25) == B.SKV_ERR_UNSUPPORTED
+    assert sel(B.SEL_THRESH_GAUSS, 64, alpha=1.0) == B.SKV_ERR_INVALID_ARG   # any alpha in (1, 2]
+    assert sel(B.SEL_THRESH_BOX, 63, alpha=1.25) == B.SKV_ERR_CAPACITY
+    assert sel(B.SEL_THRESH_BOX, 64, alpha=1.25, scale=0.0) == B.SKV_ERR_INVALID_ARG
+    assert sel(B.SEL_THRESH_BOX, 64, alpha=2.5) == B.SKV_ERR_INVALID_ARG
     assert sel(B.SEL_THRESH_GAUSS, 64, alpha=3.0) == B.SKV_ERR_INVALID_ARG
     assert sel(B.SEL_THRESH_GAUSS, 64, alpha=1.5, delta=-1.0) == B.SKV_ERR_INVALID_ARG
     assert sel(B.SEL_ALL, 64 * 16 - 1, tokens=1) == B.SKV_ERR_CAPACITY

@@ -132,6 +132,32 @@ def test_fused_token_topk_keeps_tokens_the_estimate_undercounts(dev):
             assert chosen.any() and not chosen.all(), (b, g, int(chosen.sum()))
 
 
+@pytest.mark.parametrize("over,shrink", [
+    (dict(sel_alpha=1.25, delta=0.0, drift_sd=2.0), False),        # tau_hat by quadrature
+    (dict(sel_alpha=1.75), False),
+    (dict(policy="thresh_box", delta=0.0), True),                  # box bound as the page maximum
+    (dict(policy="thresh_box", sel_alpha=1.25, delta=0.0, drift_sd=2.0), True),
+    (dict(score="gauss_q", delta=1.5), False),                     # estimated maximum m + s Phi^-1(1 - 1/n)
+])
+def test_threshold_variants_match_oracle(dev, over, shrink):
+    """Variants of the Gaussian-aware threshold: any alpha in (1, 2], the box key in the test,
+    the quantile estimate of the page maximum. tau_hat within 1e-4 relative; decisions that close
+    to the threshold are certified near-ties; everything else bit-exact. With `shrink` the keys of
+    every third page are scaled by 0.05 (bf16), so that the loose box bound still drops pages."""
+    H.log(f"[parity threshold variant] {over} shrink={shrink}")
+    w = W.make("long_gauss", device=dev, **dict(B=2, L=2500, Hq=8, Hkv=2, **over))
+    if shrink:
+        for b in range(w.B):
+            for p in range(0, w.pages(b), 3):
+                ph = int(w.block_table[b, p])
+                w.k[ph] = (w.k[ph].float() * 0.05).to(w.k.dtype)
+    st = H.gpu_step(w)
+    rep = H.compare(w, st)
+    cnt = st.sel.count.cpu().numpy()
+    assert cnt.min() > 0 and cnt.max() < w.pages(0), cnt   # the case selects a proper subset
+    H.log(f"  units={rep.units} near_ties={rep.near_ties} max_err/tol={rep.max_err:.3f} counts={cnt.ravel()}")
+
+
 def test_k_at_least_pages_and_tokens_selects_all(dev):
     H.log("[edge] k >= P_b, k >= L_b")
     w = W.make("gqa32k", device=dev, B=2, lens=[700, 33], k=400)
