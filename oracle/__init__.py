@@ -68,6 +68,8 @@ def _declare(L):
         "orc_meta_box": (None, [_P, _P, _P]),
         "orc_meta_gauss": (None, [_P, _P, _P]),
         "orc_meta_proj": (None, [_P, _I, _P, _P]),
+        "orc_meta_pool": (None, [_P, _I, _P]),
+        "orc_score_pool": (None, [_P, _I, _P, _P]),
         "orc_score_box": (None, [_P, _P, _P, _P]),
         "orc_score_gauss": (None, [_P, _P, _P, _D, _I, _P, _P, _P]),
         "orc_Phi_inv": (_D, [_D]),
@@ -165,6 +167,19 @@ def meta_proj(c: Cache, P: np.ndarray):
     kproj = np.zeros((c.Nphys, c.Hkv, c.S, r), dtype=np.uint16)
     lib().orc_meta_proj(c.ref, r, _ptr(P), _ptr(kproj))
     return kproj
+
+
+def meta_pool(c: Cache, pb: int):
+    """Sub-block mean keys [Nphys, Hkv, S / pb, d] float32 (NaN where not written)."""
+    pool = np.full((c.Nphys, c.Hkv, c.S // pb, c.d), np.nan, dtype=np.float32)
+    lib().orc_meta_pool(c.ref, int(pb), _ptr(pool))
+    return pool
+
+
+def score_pool(c: Cache, pb: int, pool: np.ndarray):
+    key = np.empty((c.B, c.Hkv, c.maxP), dtype=np.float32)
+    lib().orc_score_pool(c.ref, int(pb), _ptr(pool), _ptr(key))
+    return key
 
 
 def score_box(c: Cache, kmin, kmax):

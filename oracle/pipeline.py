@@ -4,8 +4,8 @@ TEST INFRASTRUCTURE (see ``oracle/__init__.py``). The step is the pages' pipelin
 ([EKV] "EntmaxKV" summary s2: page metadata -> query-aware page scores -> candidate
 selection -> attention over the selected KV only; [JSSA] abstract for the token-level variant):
 
-  metadata  box (kmin, kmax) | gauss (mean, var) | proj (k~ = RN_bf16(P k))
-  scores    box key per (b, g, page) | gauss (m, s, shat) per (b, h, page) | proj key per (b, g, token)
+  metadata  box (kmin, kmax) | gauss (mean, var) | proj (k~ = RN_bf16(P k)) | pool (sub-block mean keys)
+  scores    box / pool key per (b, g, page) | gauss (m, s, shat) per (b, h, page) | proj key per (b, g, token)
   select    topk(k) | budget(pct) | thresh(alpha, delta) | thresh_box(alpha, delta) | token_topk(k) | all
   attend    alpha = 1 (softmax) or alpha in (1, 2] (entmax) per query head over the selection
 """
@@ -16,13 +16,13 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from . import (Cache, attend_full_head, attend_head, budget_k, meta_box, meta_gauss, meta_proj,
-               score_box, score_gauss, score_proj, select_thresh, select_thresh_box, select_topk, tau_hat)
+from . import (Cache, attend_full_head, attend_head, budget_k, meta_box, meta_gauss, meta_pool, meta_proj,
+               score_box, score_gauss, score_pool, score_proj, select_thresh, select_thresh_box, select_topk, tau_hat)
 
 
 @dataclass
 class Spec:
-    score: str                 # 'box' | 'gauss' | 'proj'
+    score: str                 # 'box' | 'gauss' | 'proj' | 'pool'
     policy: str                # 'topk' | 'budget' | 'thresh' | 'thresh_box' | 'token_topk' | 'all'
     k: int = 0
     pct: int = 0
@@ -32,6 +32,7 @@ class Spec:
     scale: float = 0.0         # logit scale; 0 means 1/sqrt(d)
     proj: np.ndarray | None = None
     gauss_max: str = "sqrt2log"  # estimated page maximum: m + s sqrt(2 ln n) | 'quantile': m + s Phi^-1(1 - 1/n)
+    pool_block: int = 4          # tokens per sub-block of the pooled page key
 
 
 @dataclass
@@ -41,6 +42,7 @@ class Metadata:
     mean: np.ndarray | None = None
     var: np.ndarray | None = None
     kproj: np.ndarray | None = None
+    pool: np.ndarray | None = None
 
 
 @dataclass
@@ -76,6 +78,8 @@ def build_metadata(c: Cache, spec: Spec) -> Metadata:
         md.mean, md.var = meta_gauss(c)
     if "proj" in kinds:
         md.kproj = meta_proj(c, spec.proj)
+    if "pool" in kinds:
+        md.pool = meta_pool(c, spec.pool_block)
     return md
 
 
@@ -88,6 +92,8 @@ def compute_scores(c: Cache, spec: Spec, md: Metadata) -> Scores:
         sc.m, sc.s, sc.shat = score_gauss(c, md.mean, md.var, scale_of(spec, c.d), spec.gauss_max == "quantile")
     if "proj" in kinds:
         sc.key = score_proj(c, spec.proj, md.kproj)
+    if "pool" in kinds:
+        sc.key = score_pool(c, spec.pool_block, md.pool)
     return sc
 
 

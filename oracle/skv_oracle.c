@@ -154,6 +154,31 @@ void orc_meta_gauss(const orc_cache *c, double *mean, double *var) {
     }
 }
 
+/* [NOSA] section 1, block-level selection scores: mean pooling within sub-blocks, then max
+ * pooling over the block. Reading: a page is the block; its sub-blocks are the runs of
+ * pb consecutive token slots [j pb, j pb + pb) (pb divides S); the metadata of sub-block j is
+ * RN_f32 of the float64 mean (sum over its valid tokens t ascending, then divided by their number)
+ * of the keys, stored [Nphys, Hkv, S / pb, d]; sub-blocks without a valid token are not written.
+ * The mean of the scores q . k_t over a sub-block equals q . (its mean key), so pooling scores and
+ * pooling keys agree. */
+void orc_meta_pool(const orc_cache *c, int32_t pb, float *pool) {
+  int32_t nsb = c->S / pb;
+  for (int32_t b = 0; b < c->B; ++b)
+    for (int32_t p = 0; p < orc_pages(c, b); ++p) {
+      int32_t phys = orc_phys(c, b, p), n = orc_page_tokens(c, b, p);
+      for (int32_t g = 0; g < c->Hkv; ++g)
+        for (int32_t sb = 0; sb < nsb; ++sb) {
+          int32_t t0 = sb * pb, t1 = t0 + pb < n ? t0 + pb : n;
+          if (t0 >= t1) continue;
+          for (int32_t j = 0; j < c->d; ++j) {
+            double sum = 0.0;
+            for (int32_t t = t0; t < t1; ++t) sum += orc_decode(c->k, orc_kv_at(c, phys, g, t, j), c->dtype);
+            pool[(((size_t)phys * c->Hkv + g) * nsb + sb) * c->d + j] = (float)(sum / (t1 - t0));
+          }
+        }
+    }
+}
+
 /* [JSSA] abstract: keys are scored in a shared low-dimensional subspace. Reading: one
  * projection P [r, d] (float32) shared by queries and keys of every head; the projected key
  * k~_t[i] = RN_bf16(sum_j P[i][j] k_t[j]), summed in float64 over j ascending, is cached per
@@ -265,6 +290,33 @@ void orc_score_gauss(const orc_cache *c, const double *mean, const double *var, 
         shat[o] = m[o] + s[o] * fac[n];
       }
   free(fac);
+}
+
+/* [NOSA] section 1, pooled page key: key[b][g][p] = RN_f32(max over the G query heads h of g and
+ * over the sub-blocks j holding a valid token of sum_i q_hi pool_j[i]), the sum in float64 over i
+ * ascending (products of the bf16 or float32 query with float32 means are exact in float64);
+ * -inf past the sequence. */
+void orc_score_pool(const orc_cache *c, int32_t pb, const float *pool, float *key) {
+  int32_t G = c->Hq / c->Hkv, nsb = c->S / pb;
+  for (int32_t b = 0; b < c->B; ++b)
+    for (int32_t g = 0; g < c->Hkv; ++g)
+      for (int32_t p = 0; p < c->maxP; ++p) {
+        size_t o = ((size_t)b * c->Hkv + g) * c->maxP + p;
+        if (p >= orc_pages(c, b)) {
+          key[o] = -INFINITY;
+          continue;
+        }
+        int32_t phys = orc_phys(c, b, p), n = orc_page_tokens(c, b, p);
+        double best = -INFINITY;
+        for (int32_t sb = 0; sb < nsb && sb * pb < n; ++sb)
+          for (int32_t hh = 0; hh < G; ++hh) {
+            const float *mv = pool + (((size_t)phys * c->Hkv + g) * nsb + sb) * c->d;
+            double u = 0.0;
+            for (int32_t i = 0; i < c->d; ++i) u += orc_q(c, b, g * G + hh, i) * (double)mv[i];
+            if (u > best) best = u;
+          }
+        key[o] = (float)best;
+      }
 }
 
 /* [JSSA] abstract, token-level scoring in the shared subspace: q~_h = RN_f32(P q_h) (float64

@@ -213,6 +213,59 @@ def test_gauss_max_estimate_bounds_expected_page_max(orc):
         assert draws <= math.sqrt(2 * math.log(n))
 
 
+def _seq_dot(a, b):
+    """float64 dot product summed in index order (the oracle's order)."""
+    return np.cumsum(a * b, axis=-1)[..., -1]
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_pool_single_token_blocks_give_exact_page_max(orc, bf16):
+    # sub-blocks of one token: the pooled key is the exact maximum score of the page's tokens
+    c = _f32_cache(_rng(41), B=2, Hq=4, Hkv=2, d=16, S=8, lens=(37, 21), bf16=bf16)
+    pool = orc.meta_pool(c, 1)
+    key = orc.score_pool(c, 1, pool)
+    q = _dec(c.q)
+    for b, L in enumerate((37, 21)):
+        for g in range(2):
+            rows = _rows(c, b, g, c.k)                       # [L, d] in token order
+            for p in range(c.pages(b)):
+                t = np.arange(p * c.S, min(L, (p + 1) * c.S))
+                u = _seq_dot(rows[t][:, None, :], q[b, 2 * g:2 * g + 2][None, :, :])
+                assert key[b, g, p] == np.float32(u.max()), (b, g, p)
+            assert np.all(key[b, g, c.pages(b):] == -np.inf)
+
+
+def test_pool_means_are_float32_of_float64_means_and_partial_blocks_count_valid_tokens(orc):
+    c = _f32_cache(_rng(42), B=1, Hq=2, Hkv=1, d=16, S=8, lens=(29,), bf16=True)
+    pb = 4
+    pool = orc.meta_pool(c, pb)
+    rows = _rows(c, 0, 0, c.k)
+    for p in range(c.pages(0)):
+        ph = c.block_table[0, p]
+        for sb in range(c.S // pb):
+            t = np.arange(p * c.S + sb * pb, min(29, p * c.S + sb * pb + pb))
+            if len(t) == 0:
+                assert np.all(np.isnan(pool[ph, 0, sb])), (p, sb)   # no valid token: not written
+                continue
+            want = (np.cumsum(rows[t], axis=0)[-1] / len(t)).astype(np.float32)
+            assert np.array_equal(pool[ph, 0, sb], want), (p, sb)
+
+
+def test_pool_key_is_max_over_blocks_of_mean_scores(orc):
+    # pooling keys = pooling scores (linearity), up to the float32 rounding of the means
+    c = _f32_cache(_rng(43), B=1, Hq=4, Hkv=1, d=16, S=8, lens=(40,), bf16=True)
+    pb = 2
+    key = orc.score_pool(c, pb, orc.meta_pool(c, pb))
+    q, rows = _dec(c.q)[0], _rows(c, 0, 0, c.k)
+    z = rows @ q.T                                           # [40, 4] exact scores
+    for p in range(c.pages(0)):
+        blocks = z[p * 8:(p + 1) * 8].reshape(4, 2, 4).mean(axis=1)
+        assert key[0, 0, p] == pytest.approx(blocks.max(), rel=1e-6, abs=1e-6)
+    whole = orc.score_pool(c, 8, orc.meta_pool(c, 8))       # one block per page: q . mean key
+    for p in range(c.pages(0)):
+        assert whole[0, 0, p] == pytest.approx(z[p * 8:(p + 1) * 8].mean(axis=0).max(), rel=1e-6, abs=1e-6)
+
+
 def test_score_proj_identity_projection_ranks_exact_scores(orc):
     c = _f32_cache(_rng(11), B=1, Hq=4, Hkv=1, d=16, S=8, lens=(61,), bf16=True)
     P = np.eye(c.d, dtype=np.float32)
