@@ -44,7 +44,8 @@ class Step:
         self.kind = cfg["score"]
         self.cache = skv.PagedCache(w.k, w.v, w.block_table, w.seq_lens, w.Hq)
         t0 = time.time()
-        self.meta = skv.build_page_meta(self.cache, (self.kind,), proj=w.proj)
+        self.meta = skv.build_page_meta(self.cache, ("gauss" if self.kind == "gauss_q" else self.kind,), proj=w.proj,
+                                        pool_block=cfg.get("pool_block", 0))
         torch.cuda.synchronize()
         self.meta_s = time.time() - t0
         # token top-k: keep only the candidate set of the selection (fused scoring, no dense keys)
@@ -115,9 +116,14 @@ def step_bytes(st: Step):
     elif st.kind == "box":
         meta = int(P.sum()) * w.Hkv * 2 * d * e
         keys_out = w.B * w.Hkv * w.maxP * 4
-    elif st.kind == "gauss":
+    elif st.kind in ("gauss", "gauss_q"):
         meta = int(P.sum()) * w.Hkv * 2 * d * 4
         keys_out = 3 * w.B * w.Hq * w.maxP * 4
+    elif st.kind == "pool":              # float32 means of the sub-blocks holding a token
+        pb = w.cfg["pool_block"]
+        n_sb = int(sum(-(-min(S, int(L) - p * S) // pb) for L in lens for p in range(-(-int(L) // S))))
+        meta = n_sb * w.Hkv * d * 4
+        keys_out = w.B * w.Hkv * w.maxP * 4
     else:
         r = w.proj.shape[0]
         meta = int(lens.sum()) * w.Hkv * r * 2
@@ -149,7 +155,8 @@ def dominant_kernel(st: Step) -> str:
         return "attn_softmax_kernel" if st.alpha == 1.0 else "attn_entmax_logits_kernel"
     if st.fused:
         return "score_proj_cand_kernel"
-    return {"box": "score_box_kernel", "gauss": "score_gauss_kernel", "proj": "score_proj_kernel"}[st.kind]
+    return {"box": "score_box_kernel", "gauss": "score_gauss_kernel", "gauss_q": "score_gauss_kernel",
+            "proj": "score_proj_kernel", "pool": "score_pool_kernel"}[st.kind]
 
 
 def recorded_traffic(workload: str, kernel: str):
@@ -179,9 +186,12 @@ def cpu_baseline(name: str, over: dict, alpha: float, budget_s: float = 20.0):
     cores = len(os.sched_getaffinity(0))
     threads = max(1, min(cores, 16))
     w = W.make(name, device="cpu", **dict(over, B=1))
-    spec = pipeline.Spec(score=w.cfg["score"], policy=w.cfg["policy"], k=w.cfg.get("k", 0), pct=w.cfg.get("pct", 0),
+    spec = pipeline.Spec(score="gauss" if w.cfg["score"] == "gauss_q" else w.cfg["score"], policy=w.cfg["policy"],
+                         k=w.cfg.get("k", 0), pct=w.cfg.get("pct", 0),
                          sel_alpha=w.cfg.get("sel_alpha", 1.5), delta=w.cfg.get("delta", 0.0), alphas=(alpha,),
-                         proj=w.proj.numpy() if w.proj is not None else None)
+                         proj=w.proj.numpy() if w.proj is not None else None,
+                         gauss_max="quantile" if w.cfg["score"] == "gauss_q" else "sqrt2log",
+                         pool_block=w.cfg.get("pool_block", 4))
     h = W.host_arrays(w)
     n_units = min(w.Hkv, threads)
     caches = []
@@ -317,7 +327,9 @@ def main():
         log("[bench] CPU oracle baseline")
         cpu = cpu_baseline(name, {}, alpha)
 
-    sel_desc = {"topk": f"top-{cfg.get('k')} pages by box bound", "budget": f"{cfg.get('pct')}% page budget by box bound",
+    key_desc = {"box": "box bound", "pool": f"pooled key (sub-blocks of {cfg.get('pool_block')})",
+                "gauss": "Gaussian estimated maximum", "gauss_q": "Gaussian quantile maximum"}.get(cfg["score"], cfg["score"])
+    sel_desc = {"topk": f"top-{cfg.get('k')} pages by {key_desc}", "budget": f"{cfg.get('pct')}% page budget by {key_desc}",
                 "thresh": f"Gaussian entmax threshold (alpha {cfg.get('sel_alpha')}, Delta {cfg.get('delta')})",
                 "token_topk": f"top-{cfg.get('k')} tokens per KV head, rank-{cfg.get('proj_rank')} projection"}
     w0 = sets[0].w

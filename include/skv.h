@@ -82,7 +82,7 @@ typedef struct skv_cache {
 
 /* ------------------------------------------------------------------ page metadata */
 
-enum { SKV_META_BOX = 1, SKV_META_GAUSS = 2, SKV_META_PROJ = 4 };
+enum { SKV_META_BOX = 1, SKV_META_GAUSS = 2, SKV_META_PROJ = 4, SKV_META_POOL = 8 };
 
 typedef struct skv_meta {
   uint32_t kinds;     /* OR of SKV_META_* to build (build_page_meta) / available (score) */
@@ -91,6 +91,8 @@ typedef struct skv_meta {
   int32_t proj_rank;  /* PROJ:  r, 1..64 */
   const float *proj;  /* PROJ:  [r, d] float32 projection shared by queries and keys */
   uint16_t *kproj;    /* PROJ:  [Nphys, Hkv, S, r] bf16 bit patterns */
+  int32_t pool_block; /* POOL:  tokens per sub-block, dividing S */
+  float *pool;        /* POOL:  [Nphys, Hkv, S / pool_block, d] float32 sub-block mean keys */
 } skv_meta;
 
 /* Builds the requested metadata of every page in use (p < ceil(L_b / S)) from the valid tokens
@@ -99,8 +101,11 @@ typedef struct skv_meta {
  *   GAUSS: per-coordinate mean and population variance, computed in float64 (mean first, then
  *          mean squared deviation) and rounded once to float32.
  *   PROJ:  k~_t[i] = RN_bf16(sum_j proj[i][j] k_t[j]), the sum in float64 over j ascending.
- * Rows of metadata of unused physical pages, and kproj rows of tokens past L_b, are not
- * written. Errors: SKV_ERR_INVALID_ARG for null or inconsistent arguments or a missing output
+ *   POOL:  per sub-block of pool_block token slots, RN_f32 of the float64 mean of its valid keys
+ *          (sum over t ascending, divided by their number) ("NOSA" summary s1: mean pooling
+ *          within sub-blocks).
+ * Rows of metadata of unused physical pages, kproj rows of tokens past L_b and pool rows of
+ * sub-blocks without a valid token are not written. Errors: SKV_ERR_INVALID_ARG for null or inconsistent arguments or a missing output
  * of a requested kind; SKV_ERR_UNSUPPORTED outside the supported set. */
 skv_status skv_build_page_meta(const skv_cache *c, const skv_meta *m, void *stream);
 
@@ -117,10 +122,10 @@ skv_status skv_append_page_meta(const skv_cache *c, const skv_meta *m, int32_t n
 
 /* ------------------------------------------------------------------ scores */
 
-enum { SKV_SCORE_BOX = 0, SKV_SCORE_GAUSS = 1, SKV_SCORE_PROJ = 2, SKV_SCORE_GAUSS_Q = 3 };
+enum { SKV_SCORE_BOX = 0, SKV_SCORE_GAUSS = 1, SKV_SCORE_PROJ = 2, SKV_SCORE_GAUSS_Q = 3, SKV_SCORE_POOL = 4 };
 
 typedef struct skv_scores {
-  float *key;   /* BOX: [B, Hkv, max_pages]; PROJ: [B, Hkv, max_pages * S] */
+  float *key;   /* BOX, POOL: [B, Hkv, max_pages]; PROJ: [B, Hkv, max_pages * S] */
   float *m;     /* GAUSS, GAUSS_Q: [B, Hq, max_pages] Gaussian mean of the scaled scores of the page */
   float *s;     /* GAUSS: [B, Hq, max_pages] its standard deviation */
   float *shat;  /* GAUSS: [B, Hq, max_pages] estimated maximum m + s sqrt(2 ln n_p) */
@@ -151,6 +156,10 @@ enum { SKV_TOKEN_PHASE_ALL = 0, SKV_TOKEN_PHASE_BOUND = 1, SKV_TOKEN_PHASE_FILTE
  *          average ("EntmaxKV" s2.B leaves the estimate open).
  *   PROJ:  q~_h = RN_f32(proj q_h) (float64 sum), u_h(t) = sum_i q~_h[i] k~_t[i] (float64 sum,
  *          i ascending), key[b][g][t] = RN_f32(max over the G heads of g of u_h(t)).
+ *   POOL:  key[b][g][p] = RN_f32(max over the G heads h of g and the sub-blocks j of the page
+ *          holding a valid token of sum_i q_hi pool_j[i]) (float64 sum, i ascending; products
+ *          exact), unscaled: mean pooling of the scores within sub-blocks, then max pooling over
+ *          the page ("NOSA" summary s1). TOPK and BUDGET select on it like on the BOX key.
  * Entries past the sequence (p >= ceil(L_b / S), or t >= L_b) are -inf (BOX, PROJ) or NaN
  * (GAUSS). `q` is [B, Hq, d] in the cache dtype. `workspace` must hold
  * skv_workspace_bytes(c, SKV_OP_SCORE, &kind, 0) bytes (256-byte aligned).

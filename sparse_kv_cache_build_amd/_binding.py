@@ -19,8 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libskv.so")
 # status codes
 SKV_OK, SKV_ERR_INVALID_ARG, SKV_ERR_UNSUPPORTED, SKV_ERR_CAPACITY, SKV_ERR_WORKSPACE, SKV_ERR_HIP = range(6)
 DTYPE_F32, DTYPE_BF16 = 0, 1
-META_BOX, META_GAUSS, META_PROJ = 1, 2, 4
-SCORE_BOX, SCORE_GAUSS, SCORE_PROJ, SCORE_GAUSS_Q = 0, 1, 2, 3
+META_BOX, META_GAUSS, META_PROJ, META_POOL = 1, 2, 4, 8
+SCORE_BOX, SCORE_GAUSS, SCORE_PROJ, SCORE_GAUSS_Q, SCORE_POOL = 0, 1, 2, 3, 4
 SEL_TOPK, SEL_BUDGET, SEL_THRESH_GAUSS, SEL_TOKEN_TOPK, SEL_ALL, SEL_THRESH_BOX = range(6)
 OP_SCORE, OP_SELECT, OP_ATTN, OP_CANDIDATES = 0, 1, 2, 3
 
@@ -43,7 +43,7 @@ class Cache(C.Structure):
 
 class Meta(C.Structure):
     _fields_ = [("kinds", C.c_uint32), ("box", C.c_void_p), ("gauss", C.c_void_p), ("proj_rank", C.c_int32),
-                ("proj", C.c_void_p), ("kproj", C.c_void_p)]
+                ("proj", C.c_void_p), ("kproj", C.c_void_p), ("pool_block", C.c_int32), ("pool", C.c_void_p)]
 
 
 class Scores(C.Structure):
@@ -135,11 +135,12 @@ class PagedCache:
 class PageMeta:
     """Per-page metadata tensors (see skv_meta in include/skv.h)."""
 
-    def __init__(self, cache: PagedCache, kinds=("box",), proj=None):
+    def __init__(self, cache: PagedCache, kinds=("box",), proj=None, pool_block: int = 0):
         dev, Np, Hkv, d = cache.device, cache.Nphys, cache.Hkv, cache.d
         self.kinds = 0
-        self.box = self.gauss = self.kproj = None
+        self.box = self.gauss = self.kproj = self.pool = None
         self.proj = proj
+        self.pool_block = int(pool_block)
         if "box" in kinds:
             self.kinds |= META_BOX
             self.box = torch.empty((Np, Hkv, 2, d), dtype=cache.dtype, device=dev)
@@ -150,19 +151,24 @@ class PageMeta:
             assert proj is not None and proj.dtype == torch.float32 and proj.is_contiguous()
             self.kinds |= META_PROJ
             self.kproj = torch.zeros((Np, Hkv, cache.S, proj.shape[0]), dtype=torch.int16, device=dev)
+        if "pool" in kinds:
+            assert self.pool_block > 0 and cache.S % self.pool_block == 0, "pool_block must divide the page size"
+            self.kinds |= META_POOL
+            self.pool = torch.empty((Np, Hkv, cache.S // self.pool_block, d), dtype=torch.float32, device=dev)
         r = proj.shape[0] if proj is not None else 0
         self.m = Meta(self.kinds, self.box.data_ptr() if self.box is not None else None,
                       self.gauss.data_ptr() if self.gauss is not None else None, r,
                       proj.data_ptr() if proj is not None else None,
-                      self.kproj.data_ptr() if self.kproj is not None else None)
+                      self.kproj.data_ptr() if self.kproj is not None else None,
+                      self.pool_block, self.pool.data_ptr() if self.pool is not None else None)
 
     @property
     def ref(self):
         return C.byref(self.m)
 
 
-def build_page_meta(cache: PagedCache, kinds=("box",), proj=None, stream=None) -> PageMeta:
-    meta = PageMeta(cache, kinds, proj)
+def build_page_meta(cache: PagedCache, kinds=("box",), proj=None, stream=None, pool_block: int = 0) -> PageMeta:
+    meta = PageMeta(cache, kinds, proj, pool_block)
     _check(lib().skv_build_page_meta(cache.ref, meta.ref, _stream(stream)), "skv_build_page_meta")
     return meta
 
@@ -184,7 +190,7 @@ def _workspace(cache, nbytes: int):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=cache.device)
 
 
-_KIND = {"box": SCORE_BOX, "gauss": SCORE_GAUSS, "proj": SCORE_PROJ, "gauss_q": SCORE_GAUSS_Q}
+_KIND = {"box": SCORE_BOX, "gauss": SCORE_GAUSS, "proj": SCORE_PROJ, "gauss_q": SCORE_GAUSS_Q, "pool": SCORE_POOL}
 
 
 class ScoreBuffers:
@@ -196,7 +202,7 @@ class ScoreBuffers:
         self.kind = kind
         self.token_k = int(token_k) if kind == "proj" else 0
         self.key = self.m = self.s = self.shat = self.cand = None
-        if kind == "box":
+        if kind in ("box", "pool"):
             self.key = torch.empty((B, Hkv, maxP), dtype=torch.float32, device=dev)
         elif kind == "proj" and self.token_k > 0:
             n = workspace_bytes(cache, OP_CANDIDATES, C.c_int32(self.token_k))

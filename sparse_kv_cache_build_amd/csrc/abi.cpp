@@ -136,7 +136,7 @@ skv_status skv_workspace_bytes(const skv_cache *c, int32_t op, const void *param
   if (st != SKV_OK) return st;
   if (op == SKV_OP_SCORE) {
     const int kind = *static_cast<const int32_t *>(params);
-    if (kind < SKV_SCORE_BOX || kind > SKV_SCORE_GAUSS_Q) return SKV_ERR_INVALID_ARG;
+    if (kind < SKV_SCORE_BOX || kind > SKV_SCORE_POOL) return SKV_ERR_INVALID_ARG;
     *bytes = score_ws(c, kind, 64);
     return SKV_OK;
   }
@@ -167,10 +167,15 @@ skv_status skv_workspace_bytes(const skv_cache *c, int32_t op, const void *param
 static skv_status meta_args(const skv_cache *c, const skv_meta *m) {
   skv_status st = check_cache(c);
   if (st != SKV_OK) return st;
-  if (!m || m->kinds == 0 || (m->kinds & ~(uint32_t)(SKV_META_BOX | SKV_META_GAUSS | SKV_META_PROJ)))
+  if (!m || m->kinds == 0 ||
+      (m->kinds & ~(uint32_t)(SKV_META_BOX | SKV_META_GAUSS | SKV_META_PROJ | SKV_META_POOL)))
     return SKV_ERR_INVALID_ARG;
   const bool box = m->kinds & SKV_META_BOX, gauss = m->kinds & SKV_META_GAUSS, proj = m->kinds & SKV_META_PROJ;
   if ((box && !m->box) || (gauss && !m->gauss)) return SKV_ERR_INVALID_ARG;
+  if (m->kinds & SKV_META_POOL) {
+    if (!m->pool || !aligned(m->pool, 16) || m->pool_block < 1 || c->page_size % m->pool_block != 0)
+      return SKV_ERR_INVALID_ARG;
+  }
   if (box && !aligned(m->box, 16)) return SKV_ERR_INVALID_ARG;
   if (gauss && !aligned(m->gauss, 16)) return SKV_ERR_INVALID_ARG;
   if (proj) {
@@ -184,10 +189,12 @@ static skv_status meta_args(const skv_cache *c, const skv_meta *m) {
 
 static skv_status meta_launch(const skv_cache *c, const skv_meta *m, int tail, void *stream) {
   const bool box = m->kinds & SKV_META_BOX, gauss = m->kinds & SKV_META_GAUSS, proj = m->kinds & SKV_META_PROJ;
+  const bool pool = m->kinds & SKV_META_POOL;
   (void)hipGetLastError();
   const hipError_t e = skv::launch_build_meta(view(c), c->dtype, tail, box ? m->box : nullptr,
                                               gauss ? m->gauss : nullptr, m->proj_rank, proj ? m->proj : nullptr,
-                                              proj ? m->kproj : nullptr, static_cast<hipStream_t>(stream));
+                                              proj ? m->kproj : nullptr, m->pool_block, pool ? m->pool : nullptr,
+                                              static_cast<hipStream_t>(stream));
   return hip_status(e);
 }
 
@@ -213,6 +220,10 @@ skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q,
   const CacheView v = view(c);
   if (kind == SKV_SCORE_BOX) {
     if (!(m->kinds & SKV_META_BOX) || !m->box || !out->key || !aligned(m->box, 16)) return SKV_ERR_INVALID_ARG;
+  } else if (kind == SKV_SCORE_POOL) {
+    if (!(m->kinds & SKV_META_POOL) || !m->pool || !out->key || !aligned(m->pool, 16) || m->pool_block < 1 ||
+        c->page_size % m->pool_block != 0)
+      return SKV_ERR_INVALID_ARG;
   } else if (kind == SKV_SCORE_GAUSS || kind == SKV_SCORE_GAUSS_Q) {
     if (!(m->kinds & SKV_META_GAUSS) || !m->gauss || !out->m || !out->s || !out->shat || !aligned(m->gauss, 16))
       return SKV_ERR_INVALID_ARG;
@@ -249,6 +260,8 @@ skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q,
   hipError_t e;
   if (kind == SKV_SCORE_BOX)
     e = skv::launch_score_box(v, c->dtype, q, m->box, out->key, ws, s);
+  else if (kind == SKV_SCORE_POOL)
+    e = skv::launch_score_pool(v, c->dtype, q, m->pool_block, m->pool, out->key, ws, s);
   else if (kind == SKV_SCORE_GAUSS || kind == SKV_SCORE_GAUSS_Q)
     e = skv::launch_score_gauss(v, c->dtype, q, m->gauss, (double)sm_scale, kind == SKV_SCORE_GAUSS_Q, out->m,
                                 out->s, out->shat, ws, s);

@@ -24,11 +24,13 @@ struct AttnArgs {
 };
 
 hipError_t launch_build_meta(const CacheView &c, int dtype, int tail, void *box, float *gauss, int r,
-                             const float *proj, uint16_t *kproj, hipStream_t st);
+                             const float *proj, uint16_t *kproj, int pb, float *pool, hipStream_t st);
 hipError_t launch_score_box(const CacheView &c, int dtype, const void *q, const void *box, float *key, double *ws,
                             hipStream_t st);
 hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, const float *gauss, double scale,
                               int quantile, float *m, float *s, float *shat, double *ws, hipStream_t st);
+hipError_t launch_score_pool(const CacheView &c, int dtype, const void *q, int pb, const float *pool, float *key,
+                             double *ws, hipStream_t st);
 hipError_t launch_score_proj(const CacheView &c, int dtype, const void *q, int r, const float *proj,
                              const uint16_t *kproj, float *key, double *ws, hipStream_t st);
 hipError_t launch_score_proj_cand(const CacheView &c, int r, const uint16_t *kproj, char *cand, hipStream_t st);

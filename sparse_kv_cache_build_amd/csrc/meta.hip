@@ -59,6 +59,31 @@ __global__ __launch_bounds__(256) void meta_box_gauss_kernel(CacheView c, int ta
   }
 }
 
+// Pooled keys: per sub-block of pb token slots of the page, RN_f32 of the float64 mean of its
+// valid keys (t ascending). One workgroup per logical page (p, b); threads sweep (KV head,
+// coordinate) pairs like the box / moment kernel.
+template <typename T>
+__global__ __launch_bounds__(256) void meta_pool_kernel(CacheView c, int tail, int pb, float *__restrict__ pool) {
+  const int b = blockIdx.y;
+  const int L = seq_len(c, b);
+  const int p = first_page(c, L, tail) + blockIdx.x;
+  if (p >= num_pages(c, L)) return;
+  const int n = min(c.S, L - p * c.S);
+  const int nsb = c.S / pb;
+  const int phys = c.bt[(size_t)b * c.maxP + p];
+  const T *K = static_cast<const T *>(c.k);
+  for (int idx = threadIdx.x; idx < c.Hkv * c.D; idx += blockDim.x) {
+    const int g = idx / c.D, j = idx - g * c.D;
+    const size_t base = ((size_t)phys * c.Hkv + g) * c.S * c.D + j;
+    for (int sb = 0; sb < nsb && sb * pb < n; ++sb) {
+      const int t1 = min(n, sb * pb + pb);
+      double sum = 0.0;
+      for (int t = sb * pb; t < t1; ++t) sum += (double)Elem<T>::get(K, base + (size_t)t * c.D);
+      pool[(((size_t)phys * c.Hkv + g) * nsb + sb) * c.D + j] = (float)(sum / (t1 - sb * pb));
+    }
+  }
+}
+
 // Projected keys k~_t[i] = RN_bf16(sum_j P[i][j] k_t[j]) (float64, j ascending). One workgroup
 // per (logical page, KV head): the page's keys and P are staged in LDS as float (exact), then
 // each thread owns (token, i) pairs.
@@ -91,7 +116,7 @@ __global__ __launch_bounds__(256) void meta_proj_kernel(CacheView c, int tail, i
 }
 
 hipError_t launch_build_meta(const CacheView &c, int dtype, int tail, void *box, float *gauss, int r,
-                             const float *proj, uint16_t *kproj, hipStream_t st) {
+                             const float *proj, uint16_t *kproj, int pb, float *pool, hipStream_t st) {
   // pages per sequence: all of them, or those the last `tail` tokens can touch
   const int np = tail > 0 ? min(c.maxP, (tail + c.S - 1) / c.S + 1) : c.maxP;
   const dim3 grid(np, c.B);
@@ -100,6 +125,12 @@ hipError_t launch_build_meta(const CacheView &c, int dtype, int tail, void *box,
       meta_box_gauss_kernel<float><<<grid, 256, 0, st>>>(c, tail, static_cast<float *>(box), gauss);
     else
       meta_box_gauss_kernel<uint16_t><<<grid, 256, 0, st>>>(c, tail, static_cast<uint16_t *>(box), gauss);
+  }
+  if (pool) {
+    if (dtype == 0)
+      meta_pool_kernel<float><<<grid, 256, 0, st>>>(c, tail, pb, pool);
+    else
+      meta_pool_kernel<uint16_t><<<grid, 256, 0, st>>>(c, tail, pb, pool);
   }
   if (kproj) {
     const size_t lds = sizeof(float) * ((size_t)r * (c.D + 1) + (size_t)c.S * c.D);

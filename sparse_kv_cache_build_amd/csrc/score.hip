@@ -88,6 +88,96 @@ __global__ __launch_bounds__(256) void score_box_kernel(CacheView c, const T *__
   *out = (float)best;
 }
 
+// POOL key. A row is one (page, sub-block) pair; a wave takes tiles of 64 rows: 64 >> lw pages with
+// 2^lw rows each (a power of two covering the page's S/pb sub-blocks, at most 64; more sub-blocks
+// than that take several tiles). Each tile is read in chunks of 32 coordinates: every lane loads
+// 16 bytes of eight rows, so one load instruction covers eight whole 128-byte lines, and the chunk
+// goes through LDS to the lane that owns the row. That lane sums q_hi pool_j[i] in float64 with i
+// ascending (the query terms come from the (q, q^2) staging), takes the largest over the heads and
+// its valid sub-blocks (those holding a token), the page's lanes combine, and key[b][g][p] is the
+// float32 rounding of the result; -inf past the sequence. The next chunk is loaded while the current
+// one is summed.
+template <int D, int G>
+__global__ __launch_bounds__(256) void score_pool_kernel(CacheView c, int pb, int lw, const float *__restrict__ pool,
+                                                         const double *__restrict__ qpm, float *__restrict__ key) {
+  constexpr int CW = 32, NC = D / CW, LDR = CW + 4;   // chunk width, chunks per row, padded LDS row
+  __shared__ double qs[G * D];
+  __shared__ float xs[4][64 * LDR];
+  const int unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int W = 1 << lw, PT = 64 >> lw;
+  const int p0 = (blockIdx.x * 4 + wave) * PT;
+  const int L = seq_len(c, b), np = num_pages(c, L), nsb = c.S / pb;
+  if ((int)blockIdx.x * 4 * PT >= np) {   // every page of the block lies past the sequence
+    for (int i = threadIdx.x; i < 4 * PT; i += blockDim.x)
+      if (blockIdx.x * 4 * PT + i < c.maxP) key[(size_t)unit * c.maxP + blockIdx.x * 4 * PT + i] = -INFINITY;
+    return;
+  }
+  const int T = (nsb + W - 1) >> lw;
+  const double *qq = qpm + (size_t)(b * c.Hq + g * G) * D * 2;
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) qs[i] = qq[(size_t)i * 2];
+  const int *bt = c.bt + (size_t)b * c.maxP;
+  // element offset of a tile row in the pool array, -1 for rows without a valid token
+  auto row_off = [&](int row, int t) -> long long {
+    const int p = p0 + (row >> lw), sb = t * W + (row & (W - 1));
+    if (p >= np || sb >= nsb || sb * pb >= min(c.S, L - p * c.S)) return -1;
+    return (((long long)bt[p] * c.Hkv + g) * nsb + sb) * D;
+  };
+  const int lrow = lane >> 3, lcol = (lane & 7) * 4;   // load side: rows lrow + 8k, 4 columns
+  const int my_p = p0 + (lane >> lw), my_j = lane & (W - 1);
+  const int my_n = my_p < np ? min(c.S, L - my_p * c.S) : 0;
+  float *xw = xs[wave];
+  long long off[8];
+  float4 r[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    off[k] = row_off(lrow + 8 * k, 0);
+    r[k] = off[k] >= 0 ? *reinterpret_cast<const float4 *>(pool + off[k] + lcol) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  double best = -INFINITY, acc[G];
+  const int total = T * NC;
+  for (int s = 0; s < total; ++s) {
+    const int t = s / NC, ch = s - t * NC;
+    __syncthreads();   // the previous chunk has been read (and qs is staged)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) *reinterpret_cast<float4 *>(xw + (lrow + 8 * k) * LDR + lcol) = r[k];
+    if (s + 1 < total) {
+      const int t1 = (s + 1) / NC, c1 = s + 1 - t1 * NC;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (c1 == 0) off[k] = row_off(lrow + 8 * k, t1);
+        r[k] = off[k] >= 0 ? *reinterpret_cast<const float4 *>(pool + off[k] + c1 * CW + lcol)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    __syncthreads();
+    if (ch == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc[h] = 0.0;
+    }
+    const float *xr = xw + lane * LDR;
+    const double *qc = qs + ch * CW;
+#pragma unroll
+    for (int i = 0; i < CW; i += 4) {
+      const float4 x = *reinterpret_cast<const float4 *>(xr + i);
+      const float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h] = fma(qc[h * D + i + e], (double)xv[e], acc[h]);
+    }
+    if (ch == NC - 1) {
+      const int sb = t * W + my_j;
+      if (my_p < np && sb < nsb && sb * pb < my_n) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) best = fmax(best, acc[h]);
+      }
+    }
+  }
+  for (int o = W >> 1; o > 0; o >>= 1) best = fmax(best, __shfl_xor(best, o));
+  if (my_j == 0 && my_p < c.maxP) key[(size_t)unit * c.maxP + my_p] = my_p < np ? (float)best : -INFINITY;
+}
+
 // GAUSS scores: one lane per page, G heads. m = scale sum_j q_j mean_j, s = scale sqrt(sum_j
 // q_j^2 var_j) (float64), shat = m + s sqrt(2 ln n_p). Outputs [B, Hq, maxP].
 template <int D, int G>
@@ -324,6 +414,24 @@ hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, cons
   if (e != hipSuccess) return e;
   return c.D == 64 ? gauss_d<64>(c, gauss, ws, scale, quantile, m, s, shat, st)
                     : gauss_d<128>(c, gauss, ws, scale, quantile, m, s, shat, st);
+}
+
+template <int D>
+static hipError_t pool_d(const CacheView &c, int pb, const float *pool, const double *qpm, float *key, hipStream_t st) {
+  int lw = 0;
+  while ((1 << lw) < c.S / pb && lw < 6) ++lw;
+  const int pages_per_block = 4 * (64 >> lw);
+  const dim3 grid((c.maxP + pages_per_block - 1) / pages_per_block, c.B * c.Hkv);
+  SKV_DISPATCH_G(c.G, score_pool_kernel<D, GG><<<grid, 256, 0, st>>>(c, pb, lw, pool, qpm, key))
+  return hipGetLastError();
+}
+
+hipError_t launch_score_pool(const CacheView &c, int dtype, const void *q, int pb, const float *pool, float *key,
+                             double *ws, hipStream_t st) {
+  const int n = c.B * c.Hq * c.D;
+  hipError_t e = dtype == 0 ? qprep_pair<float>(q, n, 1, ws, st) : qprep_pair<uint16_t>(q, n, 1, ws, st);
+  if (e != hipSuccess) return e;
+  return c.D == 64 ? pool_d<64>(c, pb, pool, ws, key, st) : pool_d<128>(c, pb, pool, ws, key, st);
 }
 
 template <int R>

@@ -33,7 +33,8 @@ def spec_of(w: W.Workload, alphas=None) -> pipeline.Spec:
                          sel_alpha=cfg.get("sel_alpha", 1.5), delta=cfg.get("delta", 0.0),
                          alphas=tuple(alphas or cfg["alphas"]),
                          proj=w.proj.cpu().numpy() if w.proj is not None else None,
-                         gauss_max="quantile" if cfg["score"] == "gauss_q" else "sqrt2log")
+                         gauss_max="quantile" if cfg["score"] == "gauss_q" else "sqrt2log",
+                         pool_block=cfg.get("pool_block", 4))
 
 
 @dataclass
@@ -52,7 +53,7 @@ def gpu_step(w: W.Workload, alphas=None, split=0, policy=None, cap=None, fused=F
     kind = cfg["score"]
     pol = policy or cfg["policy"]
     meta_kinds = ("gauss" if kind == "gauss_q" else kind,) + (("box",) if pol == "thresh_box" else ())
-    meta = skv.build_page_meta(cache, meta_kinds, proj=w.proj)
+    meta = skv.build_page_meta(cache, meta_kinds, proj=w.proj, pool_block=cfg.get("pool_block", 0))
     token_k = cfg.get("k", 0) if (fused and kind == "proj" and pol == "token_topk") else 0
     scores = skv.score_pages(cache, meta, w.q, kind, token_k=token_k)
     if pol == "thresh_box":   # the box key beside the Gaussian m, s in one skv_scores
@@ -110,7 +111,7 @@ def compare(w: W.Workload, st: GpuStep, seqs=None, alphas=None, check_meta=True)
         for g in range(w.Hkv):
             rep.units += 1
             if gkey is not None:
-                n = c.maxP if spec.score == "box" else c.maxP * c.S
+                n = c.maxP if spec.score in ("box", "pool") else c.maxP * c.S
                 ok = np.array_equal(gkey[b, g, :n], sc.key[i, g, :n])
                 if not ok:
                     bad = np.nonzero(gkey[b, g, :n] != sc.key[i, g, :n])[0]
@@ -170,6 +171,15 @@ def _compare_meta(w, st, c, md, pm, spec):
         ga = st.meta.gauss[gp].cpu().numpy()
         assert np.array_equal(ga[:, :, 0], md.mean[used].astype(np.float32)), "mean mismatch"
         assert np.array_equal(ga[:, :, 1], md.var[used].astype(np.float32)), "var mismatch"
+    elif spec.score == "pool":
+        po = st.meta.pool[gp].cpu().numpy()            # [n, Hkv, S/pb, d]; sub-blocks with a token only
+        owner = {}
+        for i in range(c.B):
+            for p in range(c.pages(i)):
+                owner[int(c.block_table[i, p])] = c.page_tokens(i, p)
+        for n, pg in enumerate(used):
+            nsb = -(-owner[int(pg)] // spec.pool_block)
+            assert np.array_equal(po[n, :, :nsb], md.pool[pg, :, :nsb]), f"pool mismatch page {pg}"
     elif spec.score == "proj":
         kp = st.meta.kproj[gp].cpu().numpy().view(np.uint16)
         owner = {}

@@ -156,6 +156,15 @@ def test_score_and_meta_validation(L):
     assert L.skv_append_page_meta(C.byref(c), C.byref(mp), 1, None) == B.SKV_ERR_UNSUPPORTED   # rank 24
     assert L.skv_append_page_meta(C.byref(c), C.byref(B.Meta(B.META_GAUSS, None, None, 0, None, None)), 1,
                                   None) == B.SKV_ERR_INVALID_ARG
+    # pooled keys: the sub-block size must divide the page size (16 here) and the array must be given
+    for pb, ptr in ((3, FAKE), (0, FAKE), (32, FAKE), (4, None), (4, FAKE + 4)):
+        mq = B.Meta(B.META_POOL, None, None, 0, None, None, pb, ptr)
+        assert L.skv_build_page_meta(C.byref(c), C.byref(mq), None) == B.SKV_ERR_INVALID_ARG, (pb, ptr)
+        assert L.skv_score_pages(C.byref(c), C.byref(mq), C.c_void_p(FAKE), B.SCORE_POOL, 0.1, C.byref(out),
+                                 C.c_void_p(FAKE), 1 << 20, None) == B.SKV_ERR_INVALID_ARG, (pb, ptr)
+    mq = B.Meta(B.META_BOX, FAKE, None, 0, None, None, 4, FAKE)    # pool array given, kind not set
+    assert L.skv_score_pages(C.byref(c), C.byref(mq), C.c_void_p(FAKE), B.SCORE_POOL, 0.1, C.byref(out),
+                             C.c_void_p(FAKE), 1 << 20, None) == B.SKV_ERR_INVALID_ARG
 
 
 def test_binding_raises_without_library(monkeypatch, tmp_path):

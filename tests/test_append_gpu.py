@@ -23,6 +23,7 @@ CASES = [
     ("token128k", dict(B=3, lens=[5000, 4097, 0], k=512), 3),
     ("token128k", dict(B=2, lens=[5000, 20], k=512), 40),
     ("ragged", dict(B=3, lens=[4500, 129, 64]), 2),
+    ("pool32k", dict(B=3, lens=[3000, 3003, 5]), 3),   # pooled key: sub-blocks of 4 in pages of 16
 ]
 
 
@@ -38,7 +39,12 @@ def _used_pages(w, lens):
 
 
 def _snapshot(meta):
-    return {k: getattr(meta, k).clone() for k in ("box", "gauss", "kproj") if getattr(meta, k) is not None}
+    return {k: getattr(meta, k).clone() for k in ("box", "gauss", "kproj", "pool") if getattr(meta, k) is not None}
+
+
+def _page_meta(meta, kind, phys):
+    """The page's metadata for kinds defined on the whole page (box, gauss) or on its sub-blocks."""
+    return getattr(meta, "gauss" if kind == "gauss_q" else kind)[phys]
 
 
 @pytest.mark.parametrize("name,over,n_new", CASES)
@@ -50,23 +56,25 @@ def test_append_equals_rebuild(dev, name, over, n_new):
     old = [max(0, L - n_new) for L in new]
     cache = skv.PagedCache(w.k, w.v, w.block_table, w.seq_lens, w.Hq)
     w.seq_lens.copy_(torch.tensor(old, dtype=torch.int32))
-    meta = skv.build_page_meta(cache, (kind,), proj=w.proj)
+    pb = w.cfg.get("pool_block", 0)
+    meta = skv.build_page_meta(cache, (kind,), proj=w.proj, pool_block=pb)
     torch.cuda.synchronize()
     before = _snapshot(meta)
     w.seq_lens.copy_(torch.tensor(new, dtype=torch.int32))
     skv.append_page_meta(cache, meta, n_new)
-    ref = skv.build_page_meta(cache, (kind,), proj=w.proj)
+    ref = skv.build_page_meta(cache, (kind,), proj=w.proj, pool_block=pb)
     torch.cuda.synchronize()
 
     # 1. equal to a fresh build of every page in use, bit for bit
     for phys, (b, p) in _used_pages(w, new).items():
+        n = min(w.S, new[b] - p * w.S)
         if kind == "proj":
-            n = min(w.S, new[b] - p * w.S)
             assert torch.equal(meta.kproj[phys, :, :n], ref.kproj[phys, :, :n]), (b, p)
+        elif kind == "pool":                    # sub-blocks holding a token
+            nsb = -(-n // pb)
+            assert torch.equal(meta.pool[phys, :, :nsb], ref.pool[phys, :, :nsb]), (b, p)
         else:
-            t = meta.box if kind == "box" else meta.gauss
-            r = ref.box if kind == "box" else ref.gauss
-            assert torch.equal(t[phys], r[phys]), (b, p)
+            assert torch.equal(_page_meta(meta, kind, phys), _page_meta(ref, kind, phys)), (b, p)
 
     # 2. untouched: pages and kproj rows that hold no new token
     for phys, (b, p) in _used_pages(w, old).items():
@@ -75,7 +83,7 @@ def test_append_equals_rebuild(dev, name, over, n_new):
             n_old = min(w.S, old[b] - p * w.S)
             assert torch.equal(meta.kproj[phys, :, :n_old], before["kproj"][phys, :, :n_old]), (b, p)
         elif (p + 1) * w.S <= first_new:       # the page ended before the new tokens
-            key = "box" if kind == "box" else "gauss"
+            key = "gauss" if kind == "gauss_q" else kind
             assert torch.equal(getattr(meta, key)[phys], before[key][phys]), (b, p)
 
     # 3. equal to the oracle's build at the new lengths

@@ -20,9 +20,11 @@ SMALL = {
     "long_gauss": dict(B=2, L=6000),
     "token128k": dict(B=2, L=5000, k=512),
     "ragged": dict(B=5, lens=[0, 100, 4500, 20000, 12345]),
+    "pool32k": dict(B=2, lens=[3003, 2998]),
 }
 
-FULL_SAMPLE = {"tiny": None, "gqa32k": [0, 5], "long_gauss": [1], "token128k": [3], "ragged": "ends"}
+FULL_SAMPLE = {"tiny": None, "gqa32k": [0, 5], "long_gauss": [1], "token128k": [3], "ragged": "ends",
+               "pool32k": [6]}
 
 
 @pytest.fixture(scope="module")
@@ -38,6 +40,17 @@ def test_small_parity(dev, name):
     st = H.gpu_step(w)
     rep = H.compare(w, st)
     H.log(f"  units={rep.units} near_ties={rep.near_ties} max_err/tol={rep.max_err:.3f}")
+
+
+@pytest.mark.parametrize("over", [dict(pool_block=1), dict(pool_block=16), dict(pool_block=2, S=64, k=20),
+                                  dict(pool_block=8, dtype="f32", Hq=8, Hkv=2, d=64, k=30)])
+def test_pooled_key_block_sizes(dev, over):
+    """Sub-blocks of one token (the largest q.k on the page), of the whole page, and in pages of 64
+    and a float32 cache with d=64."""
+    H.log(f"[parity pool] {over}")
+    w = W.make("pool32k", device=dev, **{**SMALL["pool32k"], **over})
+    st = H.gpu_step(w)
+    H.compare(w, st)
 
 
 @pytest.mark.parametrize("name,split", [("gqa32k", 1), ("gqa32k", 3), ("token128k", 7), ("ragged", 1),

@@ -4,7 +4,7 @@ This module only draws inputs. It holds none of the method's arithmetic (no meta
 selection or attention) and imports neither the GPU binding nor the oracle. Both sides receive
 the same bytes: GPU tests use the tensors directly, the oracle gets host copies (``host_cache``).
 
-Five workloads, shaped like the pages' long-context decode settings (GQA 32/8 x 128 as in
+Six workloads, shaped like the pages' long-context decode settings (GQA 32/8 x 128 as in
 Llama-3.1-8B, 32K to 256K contexts, bf16):
 
   tiny        B=1, 1/1 heads, d=64, L=4096, page 16, float32 N(0,1); top-32 pages by box bound;
@@ -19,6 +19,9 @@ Llama-3.1-8B, 32K to 256K contexts, bf16):
               orthonormal rows (QR of a seeded Gaussian); top-2048 tokens per KV head; softmax
   ragged      64 sequences, L ~ U{8192..262144}, 64/8 heads, d=128, page 64, bf16 N(0,1);
               5% page budget by box bound; sparsemax (alpha=2)
+  pool32k     the gqa32k draw (seed 1006) with the pooled page key instead of the box bound: means
+              of 4-token sub-blocks, the page key the largest q.mean over sub-blocks and query
+              heads; top-64 pages; softmax and alpha=1.5
 
 Physical pages are a seeded permutation (block_table), so every kernel goes through the
 indirection. Any field can be overridden (smaller B or L for parity cases, ragged tails).
@@ -43,6 +46,8 @@ CONFIGS = {
                       proj_rank=32, score="proj", policy="token_topk", k=2048, alphas=(1.0,)),
     "ragged": dict(B=64, Hq=64, Hkv=8, d=128, Lmin=8192, Lmax=262144, S=64, dtype="bf16", seed=1005,
                    score="box", policy="budget", pct=5, alphas=(2.0,)),
+    "pool32k": dict(B=8, Hq=32, Hkv=8, d=128, L=32768, S=16, dtype="bf16", seed=1006,
+                    planted=4, zstar=16.0, score="pool", pool_block=4, policy="topk", k=64, alphas=(1.0, 1.5)),
 }
 
 
