@@ -70,6 +70,9 @@ def _declare(L):
         "orc_meta_proj": (None, [_P, _I, _P, _P]),
         "orc_meta_pool": (None, [_P, _I, _P]),
         "orc_score_pool": (None, [_P, _I, _P, _P]),
+        "orc_meta_lsh": (None, [_P, _I, _I, _P, _P, _P]),
+        "orc_lsh_tables": (None, [_P, _I, _I, _P, _D, _P]),
+        "orc_score_lsh": (None, [_P, _I, _I, _P, _P, _P, _P]),
         "orc_score_box": (None, [_P, _P, _P, _P]),
         "orc_score_gauss": (None, [_P, _P, _P, _D, _I, _P, _P, _P]),
         "orc_Phi_inv": (_D, [_D]),
@@ -179,6 +182,36 @@ def meta_pool(c: Cache, pb: int):
 def score_pool(c: Cache, pb: int, pool: np.ndarray):
     key = np.empty((c.B, c.Hkv, c.maxP), dtype=np.float32)
     lib().orc_score_pool(c.ref, int(pb), _ptr(pool), _ptr(key))
+    return key
+
+
+def meta_lsh(c: Cache, planes: np.ndarray):
+    """Soft-LSH metadata for hyperplanes planes [L, P, d]: bucket ids [Nphys, Hkv, S, L] uint8 and
+    value norms [Nphys, Hkv, S] float32 (NaN / 255 where not written)."""
+    planes = np.ascontiguousarray(planes, dtype=np.float32)
+    L, P, _ = planes.shape
+    bucket = np.full((c.Nphys, c.Hkv, c.S, L), 255, dtype=np.uint8)
+    vnorm = np.full((c.Nphys, c.Hkv, c.S), np.nan, dtype=np.float32)
+    lib().orc_meta_lsh(c.ref, int(L), int(P), _ptr(planes), _ptr(bucket), _ptr(vnorm))
+    return bucket, vnorm
+
+
+def lsh_tables(c: Cache, planes: np.ndarray, tau: float):
+    """Fixed-point bucket masses [B, Hq, L, 2^P] uint32 (2^24 = probability 1). tau is rounded to
+    float32 first, the precision in which the C ABI takes it."""
+    planes = np.ascontiguousarray(planes, dtype=np.float32)
+    L, P, _ = planes.shape
+    tab = np.empty((c.B, c.Hq, L, 1 << P), dtype=np.uint32)
+    lib().orc_lsh_tables(c.ref, int(L), int(P), _ptr(planes), float(np.float32(tau)), _ptr(tab))
+    return tab
+
+
+def score_lsh(c: Cache, bucket: np.ndarray, vnorm: np.ndarray, tab: np.ndarray):
+    """Soft-collision token keys [B, Hkv, maxP * S] float32."""
+    L, nb = tab.shape[2], tab.shape[3]
+    key = np.empty((c.B, c.Hkv, c.maxP * c.S), dtype=np.float32)
+    lib().orc_score_lsh(c.ref, int(L), int(nb).bit_length() - 1, _ptr(bucket), _ptr(vnorm),
+                        _ptr(np.ascontiguousarray(tab, dtype=np.uint32)), _ptr(key))
     return key
 
 

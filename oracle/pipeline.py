@@ -5,7 +5,9 @@ TEST INFRASTRUCTURE (see ``oracle/__init__.py``). The step is the pages' pipelin
 selection -> attention over the selected KV only; [JSSA] abstract for the token-level variant):
 
   metadata  box (kmin, kmax) | gauss (mean, var) | proj (k~ = RN_bf16(P k)) | pool (sub-block mean keys)
-  scores    box / pool key per (b, g, page) | gauss (m, s, shat) per (b, h, page) | proj key per (b, g, token)
+            | lsh (bucket ids per table, value norms)
+  scores    box / pool key per (b, g, page) | gauss (m, s, shat) per (b, h, page)
+            | proj / lsh key per (b, g, token)
   select    topk(k) | budget(pct) | thresh(alpha, delta) | thresh_box(alpha, delta) | token_topk(k) | all
   attend    alpha = 1 (softmax) or alpha in (1, 2] (entmax) per query head over the selection
 """
@@ -16,13 +18,14 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from . import (Cache, attend_full_head, attend_head, budget_k, meta_box, meta_gauss, meta_pool, meta_proj,
-               score_box, score_gauss, score_pool, score_proj, select_thresh, select_thresh_box, select_topk, tau_hat)
+from . import (Cache, attend_full_head, attend_head, budget_k, lsh_tables, meta_box, meta_gauss, meta_lsh, meta_pool,
+               meta_proj, score_box, score_gauss, score_lsh, score_pool, score_proj, select_thresh, select_thresh_box,
+               select_topk, tau_hat)
 
 
 @dataclass
 class Spec:
-    score: str                 # 'box' | 'gauss' | 'proj' | 'pool'
+    score: str                 # 'box' | 'gauss' | 'proj' | 'pool' | 'lsh'
     policy: str                # 'topk' | 'budget' | 'thresh' | 'thresh_box' | 'token_topk' | 'all'
     k: int = 0
     pct: int = 0
@@ -33,6 +36,8 @@ class Spec:
     proj: np.ndarray | None = None
     gauss_max: str = "sqrt2log"  # estimated page maximum: m + s sqrt(2 ln n) | 'quantile': m + s Phi^-1(1 - 1/n)
     pool_block: int = 4          # tokens per sub-block of the pooled page key
+    lsh_planes: np.ndarray | None = None   # soft-LSH hyperplanes [L, P, d] float32
+    lsh_tau: float = 1.0                   # soft-LSH temperature
 
 
 @dataclass
@@ -43,6 +48,8 @@ class Metadata:
     var: np.ndarray | None = None
     kproj: np.ndarray | None = None
     pool: np.ndarray | None = None
+    lsh_bucket: np.ndarray | None = None
+    vnorm: np.ndarray | None = None
 
 
 @dataclass
@@ -51,6 +58,7 @@ class Scores:
     m: np.ndarray | None = None        # gauss [B,Hq,maxP]
     s: np.ndarray | None = None
     shat: np.ndarray | None = None
+    lsh_tab: np.ndarray | None = None  # lsh [B,Hq,L,2^P] uint32 fixed-point bucket masses
 
 
 @dataclass
@@ -80,6 +88,8 @@ def build_metadata(c: Cache, spec: Spec) -> Metadata:
         md.kproj = meta_proj(c, spec.proj)
     if "pool" in kinds:
         md.pool = meta_pool(c, spec.pool_block)
+    if "lsh" in kinds:
+        md.lsh_bucket, md.vnorm = meta_lsh(c, spec.lsh_planes)
     return md
 
 
@@ -94,6 +104,9 @@ def compute_scores(c: Cache, spec: Spec, md: Metadata) -> Scores:
         sc.key = score_proj(c, spec.proj, md.kproj)
     if "pool" in kinds:
         sc.key = score_pool(c, spec.pool_block, md.pool)
+    if "lsh" in kinds:
+        sc.lsh_tab = lsh_tables(c, spec.lsh_planes, spec.lsh_tau)
+        sc.key = score_lsh(c, md.lsh_bucket, md.vnorm, sc.lsh_tab)
     return sc
 
 
@@ -104,7 +117,7 @@ def page_counts(c: Cache, b: int) -> np.ndarray:
 def select_unit(c: Cache, spec: Spec, sc: Scores, b: int, g: int) -> UnitResult:
     P_b, L_b = c.pages(b), c.length(b)
     if spec.policy == "all":
-        n = L_b if spec.score == "proj" else P_b
+        n = L_b if spec.score in ("proj", "lsh") else P_b
         return UnitResult(sel=np.arange(n, dtype=np.int32))
     if spec.policy == "topk":
         return UnitResult(sel=select_topk(sc.key[b, g, :P_b], spec.k))
@@ -127,7 +140,7 @@ def select_unit(c: Cache, spec: Spec, sc: Scores, b: int, g: int) -> UnitResult:
 
 
 def attend_unit(c: Cache, spec: Spec, b: int, g: int, sel: np.ndarray, alpha: float) -> np.ndarray:
-    gran = 1 if spec.score == "proj" else 0
+    gran = 1 if spec.score in ("proj", "lsh") else 0
     sc = scale_of(spec, c.d)
     return np.stack([attend_head(c, b, h, sel, gran, alpha, sc)[0] for h in range(g * c.G, (g + 1) * c.G)])
 

@@ -15,8 +15,11 @@
  *            lunghi" (ai.info, 2610.19026), authors' abstract: token-level scoring in a shared
  *            low-dimensional q/k subspace, distinct selection per KV head, GQA paged layout.
  *   [SOCKET] "SOCKET - Estimador de Kernel de Colisao Suave para Atencao Esparsa"
- *            (gist.science/pt/paper/2602.06283), Methodology step 4: deterministic top-k of
- *            per-key scores, then exact attention over the kept keys.
+ *            (gist.science/pt/paper/2602.06283), Methodology, soft LSH steps 1-4: hashing of
+ *            keys into L tables with cached value norms, soft bucket assignment of the query,
+ *            per-key soft-collision scores, deterministic top-k and exact attention.
+ *   [NOSA]   "NOSA: Atencao Esparsa Nativa e Descarregavel" (gist.science/pt/paper/2510.13602),
+ *            Algorithm: mean pooling over sub-blocks, then max pooling, as a block score.
  *   alpha-entmax itself is not printed on the pages; it is taken from its published
  *   definition (Peters, Niculae & Martins, 2019): p = [(alpha-1) z - tau]_+^(1/(alpha-1)),
  *   sum p = 1; alpha -> 1 is softmax, alpha = 2 is sparsemax (Martins & Astudillo, 2016).
@@ -198,6 +201,41 @@ void orc_meta_proj(const orc_cache *c, int32_t r, const float *P, uint16_t *kpro
     }
 }
 
+/* [SOCKET] Methodology, soft LSH step 1 (prefill): each key is hashed into L tables by random
+ * projections, one bucket id per table, and the norm of its value vector is kept. Reading (the
+ * page names neither the hash family nor the table width): table l has P hyperplanes
+ * w_{l,0..P-1} (float32 rows of planes [L, P, d], given); bit i of the key's bucket id is set iff
+ * w_{l,i}.k > 0, the dot a float64 sum over j ascending (f32 x bf16 and f32 x f32 products are
+ * exact in float64), so ids lie in [0, 2^P). The value norm is RN_f32(sqrt(sum_j v_j^2)), the sum
+ * in float64. Outputs bucket [Nphys, Hkv, S, L] uint8 and vnorm [Nphys, Hkv, S] float32; rows of
+ * invalid tokens are left untouched. */
+void orc_meta_lsh(const orc_cache *c, int32_t L, int32_t P, const float *planes, uint8_t *bucket, float *vnorm) {
+  for (int32_t b = 0; b < c->B; ++b)
+    for (int32_t p = 0; p < orc_pages(c, b); ++p) {
+      int32_t phys = orc_phys(c, b, p), n = orc_page_tokens(c, b, p);
+      for (int32_t g = 0; g < c->Hkv; ++g)
+        for (int32_t t = 0; t < n; ++t) {
+          size_t row = ((size_t)phys * c->Hkv + g) * c->S + t;
+          for (int32_t l = 0; l < L; ++l) {
+            uint32_t id = 0;
+            for (int32_t i = 0; i < P; ++i) {
+              const float *w = planes + ((size_t)l * P + i) * c->d;
+              double dot = 0.0;
+              for (int32_t j = 0; j < c->d; ++j) dot += (double)w[j] * orc_decode(c->k, orc_kv_at(c, phys, g, t, j), c->dtype);
+              if (dot > 0.0) id |= 1u << i;
+            }
+            bucket[row * L + l] = (uint8_t)id;
+          }
+          double ss = 0.0;
+          for (int32_t j = 0; j < c->d; ++j) {
+            double x = orc_decode(c->v, orc_kv_at(c, phys, g, t, j), c->dtype);
+            ss += x * x;
+          }
+          vnorm[row] = (float)sqrt(ss);
+        }
+    }
+}
+
 /* ------------------------------------------------------------------ page / token scores */
 
 /* [EKV] s2.A, bounding box: the largest q.k over all keys in the box [kmin, kmax] is
@@ -354,6 +392,79 @@ void orc_score_proj(const orc_cache *c, int32_t r, const float *P, const uint16_
       }
     }
   free(qt);
+}
+
+/* [SOCKET] Methodology, soft LSH step 2 (decode): the query does not take one bucket per table but
+ * a probability distribution over all of them, a softmax with temperature tau of a soft hash
+ * score built from its projections on the table's hyperplanes. Reading: z_i = w_{l,i}.q / ||q||
+ * (float64 sums over j ascending; z = 0 when q = 0), and bucket beta, with sign vector s
+ * (s_i = +1 where bit i of beta is set, else -1), gets
+ *   p_l(beta) = exp(<s, z>/tau) / sum over the 2^P sign vectors s' of exp(<s', z>/tau).
+ * The normaliser factorises over the bits, so p_l(beta) = prod_i sigma(2 s_i z_i / tau) with
+ * sigma(x) = 1 / (1 + exp(-x)); that product form is what is computed (bits ascending, the
+ * argument formed as (+-2 z_i) / tau). The mass is kept in fixed point, T = p * 2^24 rounded to
+ * the nearest integer (ties to even), so that the sums of step 3 are exact. tau is used as given.
+ * Output tab [B, Hq, L, 2^P] uint32. */
+void orc_lsh_tables(const orc_cache *c, int32_t L, int32_t P, const float *planes, double tau, uint32_t *tab) {
+  int32_t nb = 1 << P;
+  double *sp = (double *)malloc(sizeof(double) * (size_t)P), *sn = (double *)malloc(sizeof(double) * (size_t)P);
+  for (int32_t b = 0; b < c->B; ++b)
+    for (int32_t h = 0; h < c->Hq; ++h) {
+      double ss = 0.0;
+      for (int32_t j = 0; j < c->d; ++j) ss += orc_q(c, b, h, j) * orc_q(c, b, h, j);
+      double nq = sqrt(ss);
+      for (int32_t l = 0; l < L; ++l) {
+        for (int32_t i = 0; i < P; ++i) {
+          const float *w = planes + ((size_t)l * P + i) * c->d;
+          double dot = 0.0;
+          for (int32_t j = 0; j < c->d; ++j) dot += (double)w[j] * orc_q(c, b, h, j);
+          double z = nq > 0.0 ? dot / nq : 0.0;
+          sp[i] = 1.0 / (1.0 + exp(-((2.0 * z) / tau)));
+          sn[i] = 1.0 / (1.0 + exp(-((-2.0 * z) / tau)));
+        }
+        uint32_t *out = tab + (((size_t)b * c->Hq + h) * L + l) * nb;
+        for (int32_t beta = 0; beta < nb; ++beta) {
+          double pr = 1.0;
+          for (int32_t i = 0; i < P; ++i) pr *= (beta >> i) & 1 ? sp[i] : sn[i];
+          out[beta] = (uint32_t)rint(ldexp(pr, 24));
+        }
+      }
+    }
+  free(sp);
+  free(sn);
+}
+
+/* [SOCKET] Methodology, soft LSH step 3: a key's score gathers the probability mass the query puts
+ * on the key's own bucket over all L tables, weighted by the norm of the key's value vector.
+ * Reading for GQA (one selection per KV head): the largest of the G query heads' sums.
+ *   key(t) = RN_f32(||v_t|| * (max_h sum_l T_{h,l}[bucket_l(t)]) * 2^-24),
+ * the integer sums exact, the product one float64 multiplication. Output key [B, Hkv, maxP*S];
+ * tokens at or beyond L_b get -inf. */
+void orc_score_lsh(const orc_cache *c, int32_t L, int32_t P, const uint8_t *bucket, const float *vnorm,
+                   const uint32_t *tab, float *key) {
+  int32_t G = c->Hq / c->Hkv, nb = 1 << P;
+  size_t Lmax = (size_t)c->maxP * c->S;
+  for (int32_t b = 0; b < c->B; ++b)
+    for (int32_t g = 0; g < c->Hkv; ++g) {
+      int64_t len = orc_len(c, b);
+      for (size_t t = 0; t < Lmax; ++t) {
+        float *out = &key[((size_t)b * c->Hkv + g) * Lmax + t];
+        if ((int64_t)t >= len) {
+          *out = -INFINITY;
+          continue;
+        }
+        int32_t phys = orc_phys(c, b, (int32_t)(t / c->S));
+        size_t row = ((size_t)phys * c->Hkv + g) * c->S + t % c->S;
+        uint64_t best = 0;
+        for (int32_t hh = 0; hh < G; ++hh) {
+          const uint32_t *th = tab + ((size_t)b * c->Hq + g * G + hh) * L * nb;
+          uint64_t sum = 0;
+          for (int32_t l = 0; l < L; ++l) sum += th[(size_t)l * nb + bucket[row * L + l]];
+          if (sum > best) best = sum;
+        }
+        *out = (float)((double)vnorm[row] * ldexp((double)best, -24));
+      }
+    }
 }
 
 /* ------------------------------------------------------------------ selection */

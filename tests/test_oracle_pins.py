@@ -654,3 +654,140 @@ def test_tiny_step_support_recovery_and_bound(orc):
         delta = p[0].reshape(-1, c.S)[~kept].sum()
         Bn = np.linalg.norm(_rows(c, 0, 0, c.v), axis=1).max()
         assert np.linalg.norm(r.out[a][0] - full[0]) <= 2 * Bn * delta + 1e-12
+
+
+# ---------------------------------------------------------------- soft-LSH token scores (SOCKET)
+
+def _planes(rng, L, P, d):
+    return rng.standard_normal((L, P, d)).astype(np.float32)
+
+
+def _sign_matrix(P):
+    """[2^P, P]: row beta holds +1 where bit i of beta is set, else -1."""
+    beta = np.arange(1 << P)[:, None]
+    return np.where((beta >> np.arange(P)[None, :]) & 1, 1.0, -1.0)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_lsh_buckets_are_sign_patterns_of_numpy_projections(orc, bf16):
+    rng = _rng(301)
+    c = _f32_cache(rng, bf16=bf16)
+    W_ = _planes(rng, 5, 6, c.d)
+    bucket, vnorm = orc.meta_lsh(c, W_)
+    for b in range(c.B):
+        for g in range(c.Hkv):
+            K = _rows(c, b, g, c.k)                                   # [L, d]
+            dots = np.einsum("lpd,td->tlp", W_.astype(np.float64), K)  # [L_b, tables, bits]
+            assert np.abs(dots).min() > 1e-9                           # no sign is decided by rounding
+            ids = ((dots > 0) << np.arange(6)[None, None, :]).sum(-1)
+            t = np.arange(c.length(b))
+            got = bucket[c.block_table[b, t // c.S], g, t % c.S]
+            assert np.array_equal(got, ids)
+            vn = np.sqrt(np.sum(_rows(c, b, g, c.v) ** 2, axis=1)).astype(np.float32)
+            gv = vnorm[c.block_table[b, t // c.S], g, t % c.S]
+            assert np.all(np.abs(gv.view(np.int32) - vn.view(np.int32)) <= 1)   # rounding order only
+
+
+@pytest.mark.parametrize("tau", [0.3, 1.0, 4.0])
+def test_lsh_tables_equal_softmax_over_all_buckets(orc, tau):
+    """The soft assignment, by its definition: a softmax over all 2^P sign vectors of <s, z>/tau."""
+    rng = _rng(302)
+    c = _f32_cache(rng, bf16=True)
+    P = 5
+    W_ = _planes(rng, 4, P, c.d)
+    tab = orc.lsh_tables(c, W_, tau)
+    S_ = _sign_matrix(P)
+    t32 = float(np.float32(tau))
+    for b in range(c.B):
+        for h in range(c.Hq):
+            q = _dec(c.q[b, h])
+            z = W_.astype(np.float64) @ q / np.linalg.norm(q)          # [L, P]
+            p = scipy.special.softmax(z @ S_.T / t32, axis=1)          # [L, 2^P]
+            x = p * 2.0 ** 24
+            ref = np.rint(x)
+            diff = tab[b, h].astype(np.int64) - ref.astype(np.int64)
+            near = np.abs(x - np.floor(x) - 0.5) < 1e-6
+            assert np.all(np.abs(diff) <= 1) and np.all((diff == 0) | near), (b, h)
+
+
+def test_lsh_tables_limits_and_zero_query(orc):
+    rng = _rng(303)
+    c = _f32_cache(rng)
+    P = 4
+    W_ = _planes(rng, 3, P, c.d)
+    # probabilities sum to one (up to the rounding of each of the 2^P masses)
+    tab = orc.lsh_tables(c, W_, 1.0).astype(np.int64)
+    assert np.all(np.abs(tab.sum(-1) - 2 ** 24) <= 2 ** P // 2)
+    # tau -> 0: all mass on the query's own (hard) bucket: plain sign-random-projection hashing
+    hard = orc.lsh_tables(c, W_, 1e-6)
+    for b in range(c.B):
+        for h in range(c.Hq):
+            z = W_.astype(np.float64) @ c.q[b, h].astype(np.float64)
+            ids = ((z > 0) << np.arange(P)[None, :]).sum(-1)
+            for l in range(3):
+                expect = np.zeros(1 << P, np.uint32)
+                expect[ids[l]] = 2 ** 24
+                assert np.array_equal(hard[b, h, l], expect)
+    # tau -> infinity: uniform
+    flat = orc.lsh_tables(c, W_, 1e12)
+    assert np.all(flat == 2 ** (24 - P))
+    # a zero query puts equal mass on every bucket
+    c.q[0, 1] = 0
+    c2 = oracle.Cache(q=c.q, k=c.k, v=c.v, block_table=c.block_table, seq_lens=c.seq_lens)
+    assert np.all(orc.lsh_tables(c2, W_, 1.0)[0, 1] == 2 ** (24 - P))
+
+
+def test_lsh_token_scores_match_brute_force_soft_collision(orc):
+    """End to end against the definition evaluated with numpy and scipy (no fixed point): the key
+    of token t is ||v_t|| times the largest over the group's heads of sum_l p_l(bucket_l(t))."""
+    rng = _rng(304)
+    c = _f32_cache(rng, bf16=True, lens=(45, 80))
+    P, L, tau = 6, 8, 0.7
+    W_ = _planes(rng, L, P, c.d)
+    spec = pipeline.Spec(score="lsh", policy="token_topk", k=10, lsh_planes=W_, lsh_tau=tau)
+    md = pipeline.build_metadata(c, spec)
+    sc = pipeline.compute_scores(c, spec, md)
+    S_ = _sign_matrix(P)
+    for b in range(c.B):
+        Lb = c.length(b)
+        for g in range(c.Hkv):
+            K, V = _rows(c, b, g, c.k), _rows(c, b, g, c.v)
+            ids = (((np.einsum("lpd,td->tlp", W_.astype(np.float64), K) > 0) << np.arange(P)).sum(-1))  # [Lb, L]
+            best = np.zeros(Lb)
+            for h in range(g * c.G, (g + 1) * c.G):
+                q = _dec(c.q[b, h])
+                p = scipy.special.softmax((W_.astype(np.float64) @ q / np.linalg.norm(q)) @ S_.T
+                                          / float(np.float32(tau)), axis=1)
+                best = np.maximum(best, p[np.arange(L)[None, :], ids].sum(1))
+            ref = np.linalg.norm(V, axis=1) * best
+            got = sc.key[b, g, :Lb].astype(np.float64)
+            # fixed point (2^-24 per table) and two float32 roundings
+            assert np.all(np.abs(got - ref) <= np.linalg.norm(V, axis=1) * L * 2.0 ** -24 + 2e-7 * ref)
+            assert np.all(np.isneginf(sc.key[b, g, Lb:]))
+            r = pipeline.select_unit(c, spec, sc, b, g)
+            order = np.lexsort((np.arange(Lb), -ref))[:spec.k]
+            gap = np.sort(ref)[::-1]
+            if gap[spec.k - 1] - gap[spec.k] > 1e-5 * gap[0]:                  # no near-tie at the cut
+                assert np.array_equal(r.sel, np.sort(order))
+
+
+def test_lsh_single_table_at_zero_temperature_is_hard_collision_times_value_norm(orc):
+    """One table and tau -> 0: the score is ||v|| where the key's bucket equals the query's own
+    bucket for some head of the group, and 0 elsewhere (plain LSH collision)."""
+    rng = _rng(305)
+    c = _f32_cache(rng, lens=(64, 30))
+    P = 2
+    W_ = _planes(rng, 1, P, c.d)
+    spec = pipeline.Spec(score="lsh", policy="token_topk", k=5, lsh_planes=W_, lsh_tau=1e-6)
+    md = pipeline.build_metadata(c, spec)
+    sc = pipeline.compute_scores(c, spec, md)
+    for b in range(c.B):
+        Lb = c.length(b)
+        for g in range(c.Hkv):
+            K, V = _rows(c, b, g, c.k), _rows(c, b, g, c.v)
+            kid = ((K @ W_[0].T.astype(np.float64) > 0) << np.arange(P)).sum(-1)
+            qid = [int(((W_[0].astype(np.float64) @ c.q[b, h].astype(np.float64) > 0) << np.arange(P)).sum())
+                   for h in range(g * c.G, (g + 1) * c.G)]
+            hit = np.isin(kid, qid)
+            ref = np.where(hit, np.linalg.norm(V, axis=1), 0.0).astype(np.float32)
+            assert np.array_equal(sc.key[b, g, :Lb], ref)
