@@ -45,18 +45,18 @@ class Step:
         self.cache = skv.PagedCache(w.k, w.v, w.block_table, w.seq_lens, w.Hq)
         t0 = time.time()
         self.meta = skv.build_page_meta(self.cache, ("gauss" if self.kind == "gauss_q" else self.kind,), proj=w.proj,
-                                        pool_block=cfg.get("pool_block", 0))
+                                        pool_block=cfg.get("pool_block", 0), lsh_planes=w.lsh_planes)
         torch.cuda.synchronize()
         self.meta_s = time.time() - t0
         # token top-k: keep only the candidate set of the selection (fused scoring, no dense keys)
-        self.fused = cfg["policy"] == "token_topk" and not full
+        self.fused = cfg["policy"] == "token_topk" and cfg["score"] == "proj" and not full
         self.scores = skv.ScoreBuffers(self.cache, self.kind, cfg.get("k", 0) if self.fused else 0)
         if full:   # full-cache comparator: every page, the same attention kernels
             p = skv.select_params("all", tokens=0)
         else:
             p = skv.select_params(cfg["policy"], k=cfg.get("k", 0), budget_pct=cfg.get("pct", 0),
                                   alpha=cfg.get("sel_alpha", 1.5), delta=cfg.get("delta", 0.0),
-                                  tokens=1 if self.kind == "proj" else 0)
+                                  tokens=1 if self.kind in ("proj", "lsh") else 0)
         self.sel = skv.Selection(self.cache, p)
         self.attn = skv.AttnBuffers(self.cache, skv.attn_params(self.cache, alpha, None, self.sel.granularity, split),
                                     self.sel.cap)
@@ -76,7 +76,8 @@ class Step:
             skv.sparse_decode_attn(self.cache, self.w.q, self.sel, out=self.attn)
         else:
             skv.score_pages(self.cache, self.meta, self.w.q, self.kind, out=self.scores,
-                            phase=skv.TOKEN_PHASE_FILTER if self.fused else skv.TOKEN_PHASE_ALL)
+                            phase=skv.TOKEN_PHASE_FILTER if self.fused else skv.TOKEN_PHASE_ALL,
+                            temperature=self.w.cfg.get("lsh_tau"))
 
     def rest(self):
         if not self.full:
@@ -124,6 +125,9 @@ def step_bytes(st: Step):
         n_sb = int(sum(-(-min(S, int(L) - p * S) // pb) for L in lens for p in range(-(-int(L) // S))))
         meta = n_sb * w.Hkv * d * 4
         keys_out = w.B * w.Hkv * w.maxP * 4
+    elif st.kind == "lsh":               # bucket ids (one byte per table) and the value norm of every token
+        meta = int(lens.sum()) * w.Hkv * (w.cfg["lsh_tables"] + 4)
+        keys_out = w.B * w.Hkv * w.maxP * S * 4
     else:
         r = w.proj.shape[0]
         meta = int(lens.sum()) * w.Hkv * r * 2
@@ -156,7 +160,7 @@ def dominant_kernel(st: Step) -> str:
     if st.fused:
         return "score_proj_cand_kernel"
     return {"box": "score_box_kernel", "gauss": "score_gauss_kernel", "gauss_q": "score_gauss_kernel",
-            "proj": "score_proj_kernel", "pool": "score_pool_kernel"}[st.kind]
+            "proj": "score_proj_kernel", "pool": "score_pool_kernel", "lsh": "score_lsh_kernel"}[st.kind]
 
 
 def recorded_traffic(workload: str, kernel: str):
@@ -191,7 +195,9 @@ def cpu_baseline(name: str, over: dict, alpha: float, budget_s: float = 20.0):
                          sel_alpha=w.cfg.get("sel_alpha", 1.5), delta=w.cfg.get("delta", 0.0), alphas=(alpha,),
                          proj=w.proj.numpy() if w.proj is not None else None,
                          gauss_max="quantile" if w.cfg["score"] == "gauss_q" else "sqrt2log",
-                         pool_block=w.cfg.get("pool_block", 4))
+                         pool_block=w.cfg.get("pool_block", 4),
+                         lsh_planes=w.lsh_planes.numpy() if w.lsh_planes is not None else None,
+                         lsh_tau=w.cfg.get("lsh_tau", 1.0))
     h = W.host_arrays(w)
     n_units = min(w.Hkv, threads)
     caches = []
@@ -331,7 +337,10 @@ def main():
                 "gauss": "Gaussian estimated maximum", "gauss_q": "Gaussian quantile maximum"}.get(cfg["score"], cfg["score"])
     sel_desc = {"topk": f"top-{cfg.get('k')} pages by {key_desc}", "budget": f"{cfg.get('pct')}% page budget by {key_desc}",
                 "thresh": f"Gaussian entmax threshold (alpha {cfg.get('sel_alpha')}, Delta {cfg.get('delta')})",
-                "token_topk": f"top-{cfg.get('k')} tokens per KV head, rank-{cfg.get('proj_rank')} projection"}
+                "token_topk": (f"top-{cfg.get('k')} tokens per KV head, " + (
+                    f"soft-LSH scores ({cfg.get('lsh_tables')} tables x {cfg.get('lsh_bits')} bits, "
+                    f"temperature {cfg.get('lsh_tau')})" if cfg["score"] == "lsh"
+                    else f"rank-{cfg.get('proj_rank')} projection"))}
     w0 = sets[0].w
     line = {
         "metric": METRIC,

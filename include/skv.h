@@ -82,7 +82,7 @@ typedef struct skv_cache {
 
 /* ------------------------------------------------------------------ page metadata */
 
-enum { SKV_META_BOX = 1, SKV_META_GAUSS = 2, SKV_META_PROJ = 4, SKV_META_POOL = 8 };
+enum { SKV_META_BOX = 1, SKV_META_GAUSS = 2, SKV_META_PROJ = 4, SKV_META_POOL = 8, SKV_META_LSH = 16 };
 
 typedef struct skv_meta {
   uint32_t kinds;     /* OR of SKV_META_* to build (build_page_meta) / available (score) */
@@ -93,6 +93,11 @@ typedef struct skv_meta {
   uint16_t *kproj;    /* PROJ:  [Nphys, Hkv, S, r] bf16 bit patterns */
   int32_t pool_block; /* POOL:  tokens per sub-block, dividing S */
   float *pool;        /* POOL:  [Nphys, Hkv, S / pool_block, d] float32 sub-block mean keys */
+  int32_t lsh_tables; /* LSH:   number of hash tables L: 16, 32, 48 or 64 */
+  int32_t lsh_bits;   /* LSH:   hyperplanes per table P, 1..8 (2^P buckets) */
+  const float *lsh_planes; /* LSH: [L, P, d] float32 hyperplanes (read only) */
+  uint8_t *lsh_bucket; /* LSH:  [Nphys, Hkv, S, L] bucket id of every token in every table */
+  float *vnorm;       /* LSH:   [Nphys, Hkv, S] float32 norm of every token's value vector */
 } skv_meta;
 
 /* Builds the requested metadata of every page in use (p < ceil(L_b / S)) from the valid tokens
@@ -104,28 +109,40 @@ typedef struct skv_meta {
  *   POOL:  per sub-block of pool_block token slots, RN_f32 of the float64 mean of its valid keys
  *          (sum over t ascending, divided by their number) ("NOSA" summary s1: mean pooling
  *          within sub-blocks).
- * Rows of metadata of unused physical pages, kproj rows of tokens past L_b and pool rows of
- * sub-blocks without a valid token are not written. Errors: SKV_ERR_INVALID_ARG for null or inconsistent arguments or a missing output
- * of a requested kind; SKV_ERR_UNSUPPORTED outside the supported set. */
+ *   LSH:   per token and table l, the bucket id whose bit i is set iff lsh_planes[l][i] . k_t > 0
+ *          (float64 sum over j ascending, exact products), and vnorm = RN_f32(sqrt(sum_j v_j^2))
+ *          (float64 sum) ("SOCKET" summary, Methodology, soft LSH step 1: keys hashed into L
+ *          tables by random projections at prefill, value norms cached).
+ * Not written: metadata of unused physical pages, kproj and LSH rows of tokens past L_b, and pool
+ * rows of sub-blocks without a valid token.
+ * Errors: SKV_ERR_INVALID_ARG for null or inconsistent arguments or a missing output of a
+ * requested kind; SKV_ERR_UNSUPPORTED outside the supported set. */
 skv_status skv_build_page_meta(const skv_cache *c, const skv_meta *m, void *stream);
 
 /* Keeps the metadata current while decoding. The metadata is stored per page and maintained as
  * the cache grows ("EntmaxKV" s2.A). The caller has written the last n_new tokens of every
  * sequence into k (seq_lens already counts them; a sequence shorter than n_new counts all its
- * tokens as new). For every page holding one of those tokens, BOX and GAUSS are recomputed over
- * all valid tokens of the page, and PROJ rows are written for the new tokens only. Afterwards the
- * metadata of those pages equals what skv_build_page_meta writes for them (bit for bit, same
- * arithmetic); every other page and row is left untouched. A page holds at most S tokens, so
+ * tokens as new). For every page holding one of those tokens, BOX, GAUSS and POOL are
+ * recomputed over all valid tokens of the page, and PROJ and LSH rows are written for the new
+ * tokens only. Afterwards the metadata of those pages equals what skv_build_page_meta writes for
+ * them (bit for bit, same arithmetic); every other page and row is left untouched. A page holds at most S tokens, so
  * the work per sequence and KV head is O(S d), whatever the context length.
  * Errors: as skv_build_page_meta, and SKV_ERR_INVALID_ARG for n_new < 1. */
 skv_status skv_append_page_meta(const skv_cache *c, const skv_meta *m, int32_t n_new, void *stream);
 
 /* ------------------------------------------------------------------ scores */
 
-enum { SKV_SCORE_BOX = 0, SKV_SCORE_GAUSS = 1, SKV_SCORE_PROJ = 2, SKV_SCORE_GAUSS_Q = 3, SKV_SCORE_POOL = 4 };
+enum {
+  SKV_SCORE_BOX = 0,
+  SKV_SCORE_GAUSS = 1,
+  SKV_SCORE_PROJ = 2,
+  SKV_SCORE_GAUSS_Q = 3,
+  SKV_SCORE_POOL = 4,
+  SKV_SCORE_LSH = 5
+};
 
 typedef struct skv_scores {
-  float *key;   /* BOX, POOL: [B, Hkv, max_pages]; PROJ: [B, Hkv, max_pages * S] */
+  float *key;   /* BOX, POOL: [B, Hkv, max_pages]; PROJ, LSH: [B, Hkv, max_pages * S] */
   float *m;     /* GAUSS, GAUSS_Q: [B, Hq, max_pages] Gaussian mean of the scaled scores of the page */
   float *s;     /* GAUSS: [B, Hq, max_pages] its standard deviation */
   float *shat;  /* GAUSS: [B, Hq, max_pages] estimated maximum m + s sqrt(2 ln n_p) */
@@ -160,10 +177,19 @@ enum { SKV_TOKEN_PHASE_ALL = 0, SKV_TOKEN_PHASE_BOUND = 1, SKV_TOKEN_PHASE_FILTE
  *          holding a valid token of sum_i q_hi pool_j[i]) (float64 sum, i ascending; products
  *          exact), unscaled: mean pooling of the scores within sub-blocks, then max pooling over
  *          the page ("NOSA" summary s1). TOPK and BUDGET select on it like on the BOX key.
+ *   LSH:   soft-collision token scores ("SOCKET" summary, Methodology, soft LSH steps 2-3). Per
+ *          query head and table l, z_i = lsh_planes[l][i] . q / ||q|| (float64; 0 for q = 0) and
+ *          bucket beta gets the softmax mass p_l(beta) = prod_i sigma(2 s_i z_i / tau), s_i = +1
+ *          where bit i of beta is set and -1 elsewhere, sigma(x) = 1 / (1 + exp(-x)) (the exact
+ *          factorisation of a softmax over all 2^P sign vectors of <s, z> / tau), held as the
+ *          integer T = p * 2^24 rounded to nearest even. key[b][g][t] = RN_f32(vnorm_t *
+ *          (max over the G heads of sum_l T_l[bucket_l(t)]) * 2^-24), one float64 product. The
+ *          temperature tau > 0 is passed in `sm_scale`. Needs G * L * 2^P <= 16384. Select with
+ *          SKV_SEL_TOKEN_TOPK (tokens = 1).
  * Entries past the sequence (p >= ceil(L_b / S), or t >= L_b) are -inf (BOX, PROJ) or NaN
  * (GAUSS). `q` is [B, Hq, d] in the cache dtype. `workspace` must hold
  * skv_workspace_bytes(c, SKV_OP_SCORE, &kind, 0) bytes (256-byte aligned).
- * Errors: SKV_ERR_INVALID_ARG (null pointers, kind not in m->kinds, bad sm_scale),
+ * Errors: SKV_ERR_INVALID_ARG (null pointers, kind not in m->kinds, bad sm_scale or temperature),
  * SKV_ERR_WORKSPACE, SKV_ERR_UNSUPPORTED, SKV_ERR_HIP. */
 skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q, int32_t kind, float sm_scale,
                            const skv_scores *out, void *workspace, size_t workspace_bytes, void *stream);
@@ -174,7 +200,7 @@ enum {
   SKV_SEL_TOPK = 0,         /* the k pages with the largest BOX key */
   SKV_SEL_BUDGET = 1,       /* the ceil(budget_pct * P_b / 100) pages (at least 1) with the largest BOX key */
   SKV_SEL_THRESH_GAUSS = 2, /* Gaussian-aware entmax threshold (GAUSS scores) */
-  SKV_SEL_TOKEN_TOPK = 3,   /* the k tokens with the largest PROJ key */
+  SKV_SEL_TOKEN_TOPK = 3,   /* the k tokens with the largest PROJ or LSH key */
   SKV_SEL_ALL = 4,          /* every page (tokens == 0) or every token (tokens == 1): full cache */
   SKV_SEL_THRESH_BOX = 5    /* the entmax threshold of THRESH_GAUSS tested against the BOX key */
 };

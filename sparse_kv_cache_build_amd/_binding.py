@@ -19,8 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libskv.so")
 # status codes
 SKV_OK, SKV_ERR_INVALID_ARG, SKV_ERR_UNSUPPORTED, SKV_ERR_CAPACITY, SKV_ERR_WORKSPACE, SKV_ERR_HIP = range(6)
 DTYPE_F32, DTYPE_BF16 = 0, 1
-META_BOX, META_GAUSS, META_PROJ, META_POOL = 1, 2, 4, 8
-SCORE_BOX, SCORE_GAUSS, SCORE_PROJ, SCORE_GAUSS_Q, SCORE_POOL = 0, 1, 2, 3, 4
+META_BOX, META_GAUSS, META_PROJ, META_POOL, META_LSH = 1, 2, 4, 8, 16
+SCORE_BOX, SCORE_GAUSS, SCORE_PROJ, SCORE_GAUSS_Q, SCORE_POOL, SCORE_LSH = 0, 1, 2, 3, 4, 5
 SEL_TOPK, SEL_BUDGET, SEL_THRESH_GAUSS, SEL_TOKEN_TOPK, SEL_ALL, SEL_THRESH_BOX = range(6)
 OP_SCORE, OP_SELECT, OP_ATTN, OP_CANDIDATES = 0, 1, 2, 3
 
@@ -43,7 +43,9 @@ class Cache(C.Structure):
 
 class Meta(C.Structure):
     _fields_ = [("kinds", C.c_uint32), ("box", C.c_void_p), ("gauss", C.c_void_p), ("proj_rank", C.c_int32),
-                ("proj", C.c_void_p), ("kproj", C.c_void_p), ("pool_block", C.c_int32), ("pool", C.c_void_p)]
+                ("proj", C.c_void_p), ("kproj", C.c_void_p), ("pool_block", C.c_int32), ("pool", C.c_void_p),
+                ("lsh_tables", C.c_int32), ("lsh_bits", C.c_int32), ("lsh_planes", C.c_void_p),
+                ("lsh_bucket", C.c_void_p), ("vnorm", C.c_void_p)]
 
 
 class Scores(C.Structure):
@@ -135,12 +137,14 @@ class PagedCache:
 class PageMeta:
     """Per-page metadata tensors (see skv_meta in include/skv.h)."""
 
-    def __init__(self, cache: PagedCache, kinds=("box",), proj=None, pool_block: int = 0):
+    def __init__(self, cache: PagedCache, kinds=("box",), proj=None, pool_block: int = 0, lsh_planes=None):
+        """lsh_planes: [tables, bits, d] float32 hyperplanes of the soft-LSH kind."""
         dev, Np, Hkv, d = cache.device, cache.Nphys, cache.Hkv, cache.d
         self.kinds = 0
-        self.box = self.gauss = self.kproj = self.pool = None
+        self.box = self.gauss = self.kproj = self.pool = self.lsh_bucket = self.vnorm = None
         self.proj = proj
         self.pool_block = int(pool_block)
+        self.lsh_planes = lsh_planes
         if "box" in kinds:
             self.kinds |= META_BOX
             self.box = torch.empty((Np, Hkv, 2, d), dtype=cache.dtype, device=dev)
@@ -155,20 +159,31 @@ class PageMeta:
             assert self.pool_block > 0 and cache.S % self.pool_block == 0, "pool_block must divide the page size"
             self.kinds |= META_POOL
             self.pool = torch.empty((Np, Hkv, cache.S // self.pool_block, d), dtype=torch.float32, device=dev)
+        tables = bits = 0
+        if "lsh" in kinds:
+            assert lsh_planes is not None and lsh_planes.dtype == torch.float32 and lsh_planes.is_contiguous()
+            tables, bits = int(lsh_planes.shape[0]), int(lsh_planes.shape[1])
+            self.kinds |= META_LSH
+            self.lsh_bucket = torch.zeros((Np, Hkv, cache.S, tables), dtype=torch.uint8, device=dev)
+            self.vnorm = torch.zeros((Np, Hkv, cache.S), dtype=torch.float32, device=dev)
         r = proj.shape[0] if proj is not None else 0
         self.m = Meta(self.kinds, self.box.data_ptr() if self.box is not None else None,
                       self.gauss.data_ptr() if self.gauss is not None else None, r,
                       proj.data_ptr() if proj is not None else None,
                       self.kproj.data_ptr() if self.kproj is not None else None,
-                      self.pool_block, self.pool.data_ptr() if self.pool is not None else None)
+                      self.pool_block, self.pool.data_ptr() if self.pool is not None else None,
+                      tables, bits, lsh_planes.data_ptr() if self.lsh_bucket is not None else None,
+                      self.lsh_bucket.data_ptr() if self.lsh_bucket is not None else None,
+                      self.vnorm.data_ptr() if self.vnorm is not None else None)
 
     @property
     def ref(self):
         return C.byref(self.m)
 
 
-def build_page_meta(cache: PagedCache, kinds=("box",), proj=None, stream=None, pool_block: int = 0) -> PageMeta:
-    meta = PageMeta(cache, kinds, proj, pool_block)
+def build_page_meta(cache: PagedCache, kinds=("box",), proj=None, stream=None, pool_block: int = 0,
+                    lsh_planes=None) -> PageMeta:
+    meta = PageMeta(cache, kinds, proj, pool_block, lsh_planes)
     _check(lib().skv_build_page_meta(cache.ref, meta.ref, _stream(stream)), "skv_build_page_meta")
     return meta
 
@@ -190,7 +205,8 @@ def _workspace(cache, nbytes: int):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=cache.device)
 
 
-_KIND = {"box": SCORE_BOX, "gauss": SCORE_GAUSS, "proj": SCORE_PROJ, "gauss_q": SCORE_GAUSS_Q, "pool": SCORE_POOL}
+_KIND = {"box": SCORE_BOX, "gauss": SCORE_GAUSS, "proj": SCORE_PROJ, "gauss_q": SCORE_GAUSS_Q, "pool": SCORE_POOL,
+         "lsh": SCORE_LSH}
 
 
 class ScoreBuffers:
@@ -207,7 +223,7 @@ class ScoreBuffers:
         elif kind == "proj" and self.token_k > 0:
             n = workspace_bytes(cache, OP_CANDIDATES, C.c_int32(self.token_k))
             self.cand = torch.empty(n, dtype=torch.uint8, device=dev)
-        elif kind == "proj":
+        elif kind in ("proj", "lsh"):
             self.key = torch.empty((B, Hkv, maxP * S), dtype=torch.float32, device=dev)
         elif kind in ("gauss", "gauss_q"):
             self.m, self.s, self.shat = (torch.empty((B, Hq, maxP), dtype=torch.float32, device=dev) for _ in range(3))
@@ -227,12 +243,17 @@ TOKEN_PHASE_ALL, TOKEN_PHASE_BOUND, TOKEN_PHASE_FILTER = 0, 1, 2
 
 
 def score_pages(cache: PagedCache, meta: PageMeta, q, kind: str, sm_scale=None, out: ScoreBuffers | None = None,
-                token_k: int = 0, stream=None, phase: int = TOKEN_PHASE_ALL) -> ScoreBuffers:
+                token_k: int = 0, stream=None, phase: int = TOKEN_PHASE_ALL, temperature=None) -> ScoreBuffers:
     """phase (candidate scoring only): TOKEN_PHASE_BOUND / TOKEN_PHASE_FILTER run its two parts
-    as separate calls, the bound first."""
+    as separate calls, the bound first. temperature: the soft-LSH temperature ("lsh" only; it
+    travels in the scale argument of the C call)."""
     assert q.dtype == cache.dtype and q.is_contiguous() and tuple(q.shape) == (cache.B, cache.Hq, cache.d)
     out = out or ScoreBuffers(cache, kind, token_k)
-    scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(cache.d)
+    if kind == "lsh":
+        assert temperature is not None, "the soft-LSH scores need a temperature"
+        scale = float(temperature)
+    else:
+        scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(cache.d)
     out.sc.token_phase = int(phase)
     _check(lib().skv_score_pages(cache.ref, meta.ref, _ptr(q), _KIND[kind], scale, out.ref, _ptr(out.ws),
                                  out.ws.numel(), _stream(stream)), "skv_score_pages")

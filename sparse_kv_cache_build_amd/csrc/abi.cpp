@@ -56,8 +56,13 @@ skv_status hip_status(hipError_t e) { return e == hipSuccess ? SKV_OK : SKV_ERR_
 
 bool rank_ok(int r) { return r == 16 || r == 32 || r == 64; }
 
-size_t score_ws(const skv_cache *c, int kind, int r) {
+bool lsh_ok(int L, int P) { return (L == 16 || L == 32 || L == 48 || L == 64) && P >= 1 && P <= 8; }
+
+// Workspace of a scoring call. LSH: the bucket masses of every unit, G * L * 2^P uint32 each
+// (`lsh_entries` per unit; the size query, which does not see L and P, assumes the maximum).
+size_t score_ws(const skv_cache *c, int kind, int r, size_t lsh_entries = skv::kLshMaxEntries) {
   if (kind == SKV_SCORE_PROJ) return round_up(sizeof(double) * (size_t)c->batch * c->num_q_heads * r);
+  if (kind == SKV_SCORE_LSH) return round_up(sizeof(uint32_t) * (size_t)c->batch * c->num_kv_heads * lsh_entries);
   return round_up(sizeof(double) * 2 * (size_t)c->batch * c->num_q_heads * c->head_dim);
 }
 
@@ -136,7 +141,7 @@ skv_status skv_workspace_bytes(const skv_cache *c, int32_t op, const void *param
   if (st != SKV_OK) return st;
   if (op == SKV_OP_SCORE) {
     const int kind = *static_cast<const int32_t *>(params);
-    if (kind < SKV_SCORE_BOX || kind > SKV_SCORE_POOL) return SKV_ERR_INVALID_ARG;
+    if (kind < SKV_SCORE_BOX || kind > SKV_SCORE_LSH) return SKV_ERR_INVALID_ARG;
     *bytes = score_ws(c, kind, 64);
     return SKV_OK;
   }
@@ -168,13 +173,19 @@ static skv_status meta_args(const skv_cache *c, const skv_meta *m) {
   skv_status st = check_cache(c);
   if (st != SKV_OK) return st;
   if (!m || m->kinds == 0 ||
-      (m->kinds & ~(uint32_t)(SKV_META_BOX | SKV_META_GAUSS | SKV_META_PROJ | SKV_META_POOL)))
+      (m->kinds & ~(uint32_t)(SKV_META_BOX | SKV_META_GAUSS | SKV_META_PROJ | SKV_META_POOL | SKV_META_LSH)))
     return SKV_ERR_INVALID_ARG;
   const bool box = m->kinds & SKV_META_BOX, gauss = m->kinds & SKV_META_GAUSS, proj = m->kinds & SKV_META_PROJ;
   if ((box && !m->box) || (gauss && !m->gauss)) return SKV_ERR_INVALID_ARG;
   if (m->kinds & SKV_META_POOL) {
     if (!m->pool || !aligned(m->pool, 16) || m->pool_block < 1 || c->page_size % m->pool_block != 0)
       return SKV_ERR_INVALID_ARG;
+  }
+  if (m->kinds & SKV_META_LSH) {
+    if (!m->lsh_planes || !m->lsh_bucket || !m->vnorm || !aligned(m->lsh_bucket, 16) || !aligned(m->lsh_planes, 4) ||
+        !aligned(m->vnorm, 4))
+      return SKV_ERR_INVALID_ARG;
+    if (!lsh_ok(m->lsh_tables, m->lsh_bits)) return SKV_ERR_UNSUPPORTED;
   }
   if (box && !aligned(m->box, 16)) return SKV_ERR_INVALID_ARG;
   if (gauss && !aligned(m->gauss, 16)) return SKV_ERR_INVALID_ARG;
@@ -191,10 +202,12 @@ static skv_status meta_launch(const skv_cache *c, const skv_meta *m, int tail, v
   const bool box = m->kinds & SKV_META_BOX, gauss = m->kinds & SKV_META_GAUSS, proj = m->kinds & SKV_META_PROJ;
   const bool pool = m->kinds & SKV_META_POOL;
   (void)hipGetLastError();
-  const hipError_t e = skv::launch_build_meta(view(c), c->dtype, tail, box ? m->box : nullptr,
-                                              gauss ? m->gauss : nullptr, m->proj_rank, proj ? m->proj : nullptr,
-                                              proj ? m->kproj : nullptr, m->pool_block, pool ? m->pool : nullptr,
-                                              static_cast<hipStream_t>(stream));
+  hipError_t e = skv::launch_build_meta(view(c), c->dtype, tail, box ? m->box : nullptr, gauss ? m->gauss : nullptr,
+                                        m->proj_rank, proj ? m->proj : nullptr, proj ? m->kproj : nullptr,
+                                        m->pool_block, pool ? m->pool : nullptr, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && (m->kinds & SKV_META_LSH))
+    e = skv::launch_build_lsh(view(c), c->dtype, tail, m->lsh_tables, m->lsh_bits, m->lsh_planes, m->lsh_bucket,
+                              m->vnorm, static_cast<hipStream_t>(stream));
   return hip_status(e);
 }
 
@@ -224,6 +237,14 @@ skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q,
     if (!(m->kinds & SKV_META_POOL) || !m->pool || !out->key || !aligned(m->pool, 16) || m->pool_block < 1 ||
         c->page_size % m->pool_block != 0)
       return SKV_ERR_INVALID_ARG;
+  } else if (kind == SKV_SCORE_LSH) {
+    if (!(m->kinds & SKV_META_LSH) || !m->lsh_planes || !m->lsh_bucket || !m->vnorm || !out->key ||
+        !aligned(m->lsh_bucket, 16) || !aligned(m->lsh_planes, 4) || !aligned(m->vnorm, 4))
+      return SKV_ERR_INVALID_ARG;
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SKV_ERR_INVALID_ARG;   // the temperature
+    if (!lsh_ok(m->lsh_tables, m->lsh_bits) ||
+        ((size_t)c->num_q_heads / c->num_kv_heads) * ((size_t)m->lsh_tables << m->lsh_bits) > skv::kLshMaxEntries)
+      return SKV_ERR_UNSUPPORTED;
   } else if (kind == SKV_SCORE_GAUSS || kind == SKV_SCORE_GAUSS_Q) {
     if (!(m->kinds & SKV_META_GAUSS) || !m->gauss || !out->m || !out->s || !out->shat || !aligned(m->gauss, 16))
       return SKV_ERR_INVALID_ARG;
@@ -253,7 +274,10 @@ skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q,
   } else {
     return SKV_ERR_INVALID_ARG;
   }
-  const size_t need = score_ws(c, kind, m->proj_rank);
+  const size_t need =
+      score_ws(c, kind, m->proj_rank,
+               kind == SKV_SCORE_LSH ? ((size_t)c->num_q_heads / c->num_kv_heads) * ((size_t)m->lsh_tables << m->lsh_bits)
+                                     : 0);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 8)) return SKV_ERR_WORKSPACE;
   double *ws = static_cast<double *>(workspace);
   (void)hipGetLastError();
@@ -262,6 +286,9 @@ skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q,
     e = skv::launch_score_box(v, c->dtype, q, m->box, out->key, ws, s);
   else if (kind == SKV_SCORE_POOL)
     e = skv::launch_score_pool(v, c->dtype, q, m->pool_block, m->pool, out->key, ws, s);
+  else if (kind == SKV_SCORE_LSH)
+    e = skv::launch_score_lsh(v, c->dtype, q, m->lsh_tables, m->lsh_bits, m->lsh_planes, sm_scale, m->lsh_bucket,
+                              m->vnorm, out->key, workspace, s);
   else if (kind == SKV_SCORE_GAUSS || kind == SKV_SCORE_GAUSS_Q)
     e = skv::launch_score_gauss(v, c->dtype, q, m->gauss, (double)sm_scale, kind == SKV_SCORE_GAUSS_Q, out->m,
                                 out->s, out->shat, ws, s);

@@ -8,6 +8,9 @@
 namespace skv {
 
 constexpr int kWave = 64;
+constexpr int kLshTok = 4096;       // tokens per workgroup of the soft-LSH scorer
+constexpr int kLshMaxProj = 512;    // tables x hyperplanes per table (64 x 8)
+constexpr int kLshMaxEntries = 16384;   // G x tables x 2^P bucket masses of one unit (64 KiB of LDS)
 
 // Plain view of the paged cache passed by value to kernels.
 struct CacheView {

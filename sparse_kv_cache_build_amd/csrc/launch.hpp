@@ -25,7 +25,12 @@ struct AttnArgs {
 
 hipError_t launch_build_meta(const CacheView &c, int dtype, int tail, void *box, float *gauss, int r,
                              const float *proj, uint16_t *kproj, int pb, float *pool, hipStream_t st);
+hipError_t launch_build_lsh(const CacheView &c, int dtype, int tail, int L, int P, const float *planes,
+                            uint8_t *bucket, float *vnorm, hipStream_t st);
 hipError_t launch_score_box(const CacheView &c, int dtype, const void *q, const void *box, float *key, double *ws,
+                            hipStream_t st);
+hipError_t launch_score_lsh(const CacheView &c, int dtype, const void *q, int L, int P, const float *planes,
+                            float tau, const uint8_t *bucket, const float *vnorm, float *key, void *ws,
                             hipStream_t st);
 hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, const float *gauss, double scale,
                               int quantile, float *m, float *s, float *shat, double *ws, hipStream_t st);

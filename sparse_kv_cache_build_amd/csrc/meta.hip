@@ -115,6 +115,94 @@ __global__ __launch_bounds__(256) void meta_proj_kernel(CacheView c, int tail, i
   }
 }
 
+// Soft-LSH metadata. One workgroup per logical page (p, b) covers the page's rows (KV head g,
+// token t), in chunks of 64 rows staged in LDS as float (exact). Work items are (table l, row)
+// pairs, with l constant over a wave in full chunks so that the hyperplanes of table l are
+// wave-uniform (scalar loads); each item takes the P float64 dot products of its row in
+// coordinate order, bit i of the bucket id being (dot_i > 0). Rows [t0, n) of the page are
+// written: all of them for a build, the new tokens for an append. The value norm of each row is
+// RN_f32(sqrt) of its float64 sum of squares.
+template <typename T, int D, int P>
+__global__ __launch_bounds__(256) void meta_lsh_kernel(CacheView c, int tail, int L, const float *__restrict__ planes,
+                                                       uint8_t *__restrict__ bucket, float *__restrict__ vnorm) {
+  constexpr int RC = 64, LDR = D + 1;
+  __shared__ float Ks[RC * LDR];
+  const int b = blockIdx.y;
+  const int len = seq_len(c, b);
+  const int p = first_page(c, len, tail) + blockIdx.x;
+  if (p >= num_pages(c, len)) return;
+  const int n = min(c.S, len - p * c.S);
+  const int t0 = tail > 0 ? max(0, len - tail - p * c.S) : 0;
+  const int cnt = n - t0, rows = c.Hkv * cnt;   // row r: KV head r / cnt, token t0 + r % cnt
+  const int phys = c.bt[(size_t)b * c.maxP + p];
+  const T *K = static_cast<const T *>(c.k);
+  const T *V = static_cast<const T *>(c.v);
+  for (int r0 = 0; r0 < rows; r0 += RC) {
+    const int nr = min(RC, rows - r0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < nr * D; i += blockDim.x) {
+      const int r = r0 + i / D, j = i % D, g = r / cnt, t = t0 + r % cnt;
+      Ks[(i / D) * LDR + j] = Elem<T>::get(K, (((size_t)phys * c.Hkv + g) * c.S + t) * D + j);
+    }
+    __syncthreads();
+    for (int item = threadIdx.x; item < L * nr; item += blockDim.x) {
+      // full chunks: table l is constant over each wave (scalar loads of its hyperplanes); a
+      // partial chunk (an append touches a few rows) packs its (table, row) items densely
+      const int l = nr == RC ? __builtin_amdgcn_readfirstlane(item / RC) : item / nr;
+      const int rr = item - l * nr;
+      const float *w = planes + (size_t)l * P * D;
+      const float *kr = Ks + rr * LDR;
+      double acc[P];
+#pragma unroll
+      for (int i = 0; i < P; ++i) acc[i] = 0.0;
+      for (int j = 0; j < D; ++j) {
+        const double kv = kr[j];
+#pragma unroll
+        for (int i = 0; i < P; ++i) acc[i] = fma((double)w[i * D + j], kv, acc[i]);
+      }
+      uint32_t id = 0;
+#pragma unroll
+      for (int i = 0; i < P; ++i) id |= (acc[i] > 0.0 ? 1u : 0u) << i;
+      const int r = r0 + rr, g = r / cnt, t = t0 + r % cnt;
+      bucket[(((size_t)phys * c.Hkv + g) * c.S + t) * L + l] = (uint8_t)id;
+    }
+    for (int rr = threadIdx.x; rr < nr; rr += blockDim.x) {
+      const int r = r0 + rr, g = r / cnt, t = t0 + r % cnt;
+      const size_t row = ((size_t)phys * c.Hkv + g) * c.S + t;
+      double ss = 0.0;
+      for (int j = 0; j < D; ++j) {
+        const double x = Elem<T>::get(V, row * D + j);
+        ss = fma(x, x, ss);
+      }
+      vnorm[row] = (float)sqrt(ss);
+    }
+  }
+}
+
+template <typename T, int D>
+static hipError_t lsh_meta_d(const CacheView &c, int tail, int L, int P, const float *planes, uint8_t *bucket,
+                             float *vnorm, const dim3 &grid, hipStream_t st) {
+  switch (P) {
+#define SKV_LSH_P(PP) \
+  case PP: meta_lsh_kernel<T, D, PP><<<grid, 256, 0, st>>>(c, tail, L, planes, bucket, vnorm); break;
+    SKV_LSH_P(1) SKV_LSH_P(2) SKV_LSH_P(3) SKV_LSH_P(4) SKV_LSH_P(5) SKV_LSH_P(6) SKV_LSH_P(7) SKV_LSH_P(8)
+#undef SKV_LSH_P
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_build_lsh(const CacheView &c, int dtype, int tail, int L, int P, const float *planes,
+                            uint8_t *bucket, float *vnorm, hipStream_t st) {
+  const int np = tail > 0 ? min(c.maxP, (tail + c.S - 1) / c.S + 1) : c.maxP;
+  const dim3 grid(np, c.B);
+  if (c.D == 64)
+    return dtype == 0 ? lsh_meta_d<float, 64>(c, tail, L, P, planes, bucket, vnorm, grid, st)
+                      : lsh_meta_d<uint16_t, 64>(c, tail, L, P, planes, bucket, vnorm, grid, st);
+  return dtype == 0 ? lsh_meta_d<float, 128>(c, tail, L, P, planes, bucket, vnorm, grid, st)
+                    : lsh_meta_d<uint16_t, 128>(c, tail, L, P, planes, bucket, vnorm, grid, st);
+}
+
 hipError_t launch_build_meta(const CacheView &c, int dtype, int tail, void *box, float *gauss, int r,
                              const float *proj, uint16_t *kproj, int pb, float *pool, hipStream_t st) {
   // pages per sequence: all of them, or those the last `tail` tokens can touch

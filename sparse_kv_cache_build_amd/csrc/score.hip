@@ -178,6 +178,112 @@ __global__ __launch_bounds__(256) void score_pool_kernel(CacheView c, int pb, in
   if (my_j == 0 && my_p < c.maxP) key[(size_t)unit * c.maxP + my_p] = my_p < np ? (float)best : -INFINITY;
 }
 
+// Soft-LSH bucket masses of one query head, one workgroup per (b, h): z_i = w_{l,i} . q / ||q||
+// (float64 sums in coordinate order; 0 for q = 0), the two sigmoids sigma(+-2 z_i / tau) of every
+// hyperplane, then for each table l and bucket beta the product over the bits (ascending) of the
+// sigmoid the bit's sign picks, stored as the integer p * 2^24 rounded to nearest even. Layout
+// [B, Hkv, L, 2^P, G]: the G heads of one bucket are adjacent for the scorer.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void lsh_prep_kernel(CacheView c, const T *__restrict__ q, int L, int P,
+                                                       const float *__restrict__ planes, double tau,
+                                                       uint32_t *__restrict__ tab) {
+  __shared__ double qs[D];
+  __shared__ double sg[2 * kLshMaxProj];   // [l * P + i][+, -]
+  __shared__ double nq;
+  const int bh = blockIdx.x, b = bh / c.Hq, h = bh - b * c.Hq, g = h / c.G, hh = h - g * c.G;
+  for (int j = threadIdx.x; j < D; j += blockDim.x) qs[j] = (double)Elem<T>::get(q, (size_t)bh * D + j);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double ss = 0.0;
+    for (int j = 0; j < D; ++j) ss = fma(qs[j], qs[j], ss);
+    nq = sqrt(ss);
+  }
+  __syncthreads();
+  for (int m = threadIdx.x; m < L * P; m += blockDim.x) {
+    const float *w = planes + (size_t)m * D;
+    double dot = 0.0;
+    for (int j = 0; j < D; ++j) dot = fma((double)w[j], qs[j], dot);
+    const double z = nq > 0.0 ? dot / nq : 0.0;
+    sg[2 * m] = 1.0 / (1.0 + exp(-((2.0 * z) / tau)));
+    sg[2 * m + 1] = 1.0 / (1.0 + exp(-((-2.0 * z) / tau)));
+  }
+  __syncthreads();
+  const int nb = 1 << P;
+  uint32_t *out = tab + (size_t)(b * c.Hkv + g) * L * nb * c.G;
+  for (int e = threadIdx.x; e < L * nb; e += blockDim.x) {
+    const int l = e >> P, beta = e & (nb - 1);
+    double pr = 1.0;
+    for (int i = 0; i < P; ++i) pr *= sg[2 * (l * P + i) + (((beta >> i) & 1) ? 0 : 1)];
+    out[(size_t)e * c.G + hh] = (uint32_t)rint(ldexp(pr, 24));
+  }
+}
+
+// Soft-collision token keys: one workgroup per (kLshTok tokens, unit). The unit's bucket masses
+// [L, 2^P, G] are copied into LDS; a lane per token reads its L bucket ids (16-byte loads; the
+// tokens of a page are adjacent rows), adds up the G heads' masses of its bucket over the tables
+// (uint32, exact), and key = RN_f32(vnorm * (largest sum) * 2^-24), one float64 product. Tokens
+// past the sequence get -inf.
+template <int G>
+__global__ __launch_bounds__(256) void score_lsh_kernel(CacheView c, int L, int P, const uint8_t *__restrict__ bucket,
+                                                        const float *__restrict__ vnorm,
+                                                        const uint32_t *__restrict__ tab, float *__restrict__ key) {
+  extern __shared__ uint4 ts4[];
+  const uint32_t *ts = reinterpret_cast<const uint32_t *>(ts4);
+  const int unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
+  const int len = seq_len(c, b);
+  const int ntok = c.maxP * c.S;
+  const int t0 = blockIdx.x * kLshTok, t1 = min(ntok, t0 + kLshTok);
+  float *out = key + (size_t)unit * ntok;
+  if (t0 >= len) {
+    for (int t = t0 + threadIdx.x; t < t1; t += blockDim.x) out[t] = -INFINITY;
+    return;
+  }
+  const int ne = (L << P) * G;   // a multiple of 16 (L is)
+  const uint4 *src = reinterpret_cast<const uint4 *>(tab + (size_t)unit * ne);
+  for (int i = threadIdx.x; i < ne / 4; i += blockDim.x) ts4[i] = src[i];
+  __syncthreads();
+  const int *bt = c.bt + (size_t)b * c.maxP;
+  const uint32_t nbm = (1u << P) - 1;
+  for (int t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
+    if (t >= len) {
+      out[t] = -INFINITY;
+      continue;
+    }
+    const int p = t / c.S;
+    const size_t row = ((size_t)bt[p] * c.Hkv + g) * c.S + (t - p * c.S);
+    const uint4 *bq = reinterpret_cast<const uint4 *>(bucket + row * L);
+    uint32_t sum[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) sum[hh] = 0;
+    for (int lq = 0; lq < L / 16; ++lq) {
+      const uint4 wv = bq[lq];
+      const uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t bb = (w4[k >> 2] >> (8 * (k & 3))) & nbm;   // ids are < 2^P; the mask keeps LDS in range
+        const uint32_t *e = ts + (((size_t)(lq * 16 + k) << P) + bb) * G;
+        if constexpr (G >= 4) {
+#pragma unroll
+          for (int h4 = 0; h4 < G; h4 += 4) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(e + h4);
+            sum[h4] += v.x;
+            sum[h4 + 1] += v.y;
+            sum[h4 + 2] += v.z;
+            sum[h4 + 3] += v.w;
+          }
+        } else {
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) sum[hh] += e[hh];
+        }
+      }
+    }
+    uint32_t best = sum[0];
+#pragma unroll
+    for (int hh = 1; hh < G; ++hh) best = max(best, sum[hh]);
+    out[t] = (float)((double)vnorm[row] * ldexp((double)best, -24));
+  }
+}
+
 // GAUSS scores: one lane per page, G heads. m = scale sum_j q_j mean_j, s = scale sqrt(sum_j
 // q_j^2 var_j) (float64), shat = m + s sqrt(2 ln n_p). Outputs [B, Hq, maxP].
 template <int D, int G>
@@ -487,6 +593,30 @@ hipError_t launch_score_proj(const CacheView &c, int dtype, const void *q, int r
     case 64: return proj_r<64>(c, kproj, ws, key, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int D>
+static hipError_t lsh_d(const CacheView &c, int dtype, const void *q, int L, int P, const float *planes, double tau,
+                        const uint8_t *bucket, const float *vnorm, float *key, uint32_t *tab, hipStream_t st) {
+  if (dtype == 0)
+    lsh_prep_kernel<float, D><<<c.B * c.Hq, 256, 0, st>>>(c, static_cast<const float *>(q), L, P, planes, tau, tab);
+  else
+    lsh_prep_kernel<uint16_t, D><<<c.B * c.Hq, 256, 0, st>>>(c, static_cast<const uint16_t *>(q), L, P, planes, tau,
+                                                             tab);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((c.maxP * c.S + kLshTok - 1) / kLshTok, c.B * c.Hkv);
+  const size_t lds = sizeof(uint32_t) * ((size_t)L << P) * c.G;
+  SKV_DISPATCH_G(c.G, score_lsh_kernel<GG><<<grid, 256, lds, st>>>(c, L, P, bucket, vnorm, tab, key))
+  return hipGetLastError();
+}
+
+hipError_t launch_score_lsh(const CacheView &c, int dtype, const void *q, int L, int P, const float *planes,
+                            float tau, const uint8_t *bucket, const float *vnorm, float *key, void *ws,
+                            hipStream_t st) {
+  uint32_t *tab = static_cast<uint32_t *>(ws);
+  return c.D == 64 ? lsh_d<64>(c, dtype, q, L, P, planes, (double)tau, bucket, vnorm, key, tab, st)
+                   : lsh_d<128>(c, dtype, q, L, P, planes, (double)tau, bucket, vnorm, key, tab, st);
 }
 
 }  // namespace skv

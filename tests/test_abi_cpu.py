@@ -162,6 +162,26 @@ def test_score_and_meta_validation(L):
         assert L.skv_build_page_meta(C.byref(c), C.byref(mq), None) == B.SKV_ERR_INVALID_ARG, (pb, ptr)
         assert L.skv_score_pages(C.byref(c), C.byref(mq), C.c_void_p(FAKE), B.SCORE_POOL, 0.1, C.byref(out),
                                  C.c_void_p(FAKE), 1 << 20, None) == B.SKV_ERR_INVALID_ARG, (pb, ptr)
+    # soft-LSH: 16..64 tables in steps of 16, 1..8 bits, G * tables * 2^bits <= 16384, temperature > 0
+    def lsh(tables, bits, bucket=FAKE, vnorm=FAKE, planes=FAKE):
+        return B.Meta(B.META_LSH, None, None, 0, None, None, 0, None, tables, bits, planes, bucket, vnorm)
+
+    for tables, bits, st in ((20, 4, B.SKV_ERR_UNSUPPORTED), (32, 9, B.SKV_ERR_UNSUPPORTED),
+                             (32, 0, B.SKV_ERR_UNSUPPORTED), (80, 4, B.SKV_ERR_UNSUPPORTED)):
+        assert L.skv_build_page_meta(C.byref(c), C.byref(lsh(tables, bits)), None) == st, (tables, bits)
+    for kw in (dict(bucket=None), dict(vnorm=None), dict(planes=None), dict(bucket=FAKE + 8)):
+        assert L.skv_build_page_meta(C.byref(c), C.byref(lsh(32, 6, **kw)), None) == B.SKV_ERR_INVALID_ARG, kw
+    big = 1 << 24
+    assert L.skv_score_pages(C.byref(c), C.byref(lsh(64, 7)), C.c_void_p(FAKE), B.SCORE_LSH, 1.0, C.byref(out),
+                             C.c_void_p(FAKE), big, None) == B.SKV_ERR_UNSUPPORTED      # G=4: 4 * 64 * 128 > 16384
+    assert L.skv_score_pages(C.byref(c), C.byref(lsh(64, 8)), C.c_void_p(FAKE), B.SCORE_LSH, 1.0, C.byref(out),
+                             C.c_void_p(FAKE), big, None) == B.SKV_ERR_UNSUPPORTED
+    for tau in (0.0, -1.0, float("nan"), float("inf")):
+        assert L.skv_score_pages(C.byref(c), C.byref(lsh(32, 6)), C.c_void_p(FAKE), B.SCORE_LSH, tau, C.byref(out),
+                                 C.c_void_p(FAKE), big, None) == B.SKV_ERR_INVALID_ARG, tau
+    small = 2 * 8 * 4 * 32 * 64 * 4 - 256                                            # B Hkv G L 2^P uint32, short
+    assert L.skv_score_pages(C.byref(c), C.byref(lsh(32, 6)), C.c_void_p(FAKE), B.SCORE_LSH, 1.0, C.byref(out),
+                             C.c_void_p(FAKE), small, None) == B.SKV_ERR_WORKSPACE
     mq = B.Meta(B.META_BOX, FAKE, None, 0, None, None, 4, FAKE)    # pool array given, kind not set
     assert L.skv_score_pages(C.byref(c), C.byref(mq), C.c_void_p(FAKE), B.SCORE_POOL, 0.1, C.byref(out),
                              C.c_void_p(FAKE), 1 << 20, None) == B.SKV_ERR_INVALID_ARG

@@ -24,6 +24,7 @@ CASES = [
     ("token128k", dict(B=2, lens=[5000, 20], k=512), 40),
     ("ragged", dict(B=3, lens=[4500, 129, 64]), 2),
     ("pool32k", dict(B=3, lens=[3000, 3003, 5]), 3),   # pooled key: sub-blocks of 4 in pages of 16
+    ("socket128k", dict(B=3, lens=[5000, 4113, 2], k=256), 19),   # soft-LSH buckets and value norms
 ]
 
 
@@ -39,7 +40,8 @@ def _used_pages(w, lens):
 
 
 def _snapshot(meta):
-    return {k: getattr(meta, k).clone() for k in ("box", "gauss", "kproj", "pool") if getattr(meta, k) is not None}
+    keys = ("box", "gauss", "kproj", "pool", "lsh_bucket", "vnorm")
+    return {k: getattr(meta, k).clone() for k in keys if getattr(meta, k) is not None}
 
 
 def _page_meta(meta, kind, phys):
@@ -57,12 +59,12 @@ def test_append_equals_rebuild(dev, name, over, n_new):
     cache = skv.PagedCache(w.k, w.v, w.block_table, w.seq_lens, w.Hq)
     w.seq_lens.copy_(torch.tensor(old, dtype=torch.int32))
     pb = w.cfg.get("pool_block", 0)
-    meta = skv.build_page_meta(cache, (kind,), proj=w.proj, pool_block=pb)
+    meta = skv.build_page_meta(cache, (kind,), proj=w.proj, pool_block=pb, lsh_planes=w.lsh_planes)
     torch.cuda.synchronize()
     before = _snapshot(meta)
     w.seq_lens.copy_(torch.tensor(new, dtype=torch.int32))
     skv.append_page_meta(cache, meta, n_new)
-    ref = skv.build_page_meta(cache, (kind,), proj=w.proj, pool_block=pb)
+    ref = skv.build_page_meta(cache, (kind,), proj=w.proj, pool_block=pb, lsh_planes=w.lsh_planes)
     torch.cuda.synchronize()
 
     # 1. equal to a fresh build of every page in use, bit for bit
@@ -70,6 +72,9 @@ def test_append_equals_rebuild(dev, name, over, n_new):
         n = min(w.S, new[b] - p * w.S)
         if kind == "proj":
             assert torch.equal(meta.kproj[phys, :, :n], ref.kproj[phys, :, :n]), (b, p)
+        elif kind == "lsh":
+            assert torch.equal(meta.lsh_bucket[phys, :, :n], ref.lsh_bucket[phys, :, :n]), (b, p)
+            assert torch.equal(meta.vnorm[phys, :, :n], ref.vnorm[phys, :, :n]), (b, p)
         elif kind == "pool":                    # sub-blocks holding a token
             nsb = -(-n // pb)
             assert torch.equal(meta.pool[phys, :, :nsb], ref.pool[phys, :, :nsb]), (b, p)
@@ -79,9 +84,10 @@ def test_append_equals_rebuild(dev, name, over, n_new):
     # 2. untouched: pages and kproj rows that hold no new token
     for phys, (b, p) in _used_pages(w, old).items():
         first_new = old[b]                     # tokens >= old[b] are new
-        if kind == "proj":
+        if kind in ("proj", "lsh"):                 # per-token rows: the old ones stay as they were
             n_old = min(w.S, old[b] - p * w.S)
-            assert torch.equal(meta.kproj[phys, :, :n_old], before["kproj"][phys, :, :n_old]), (b, p)
+            for key in (("kproj",) if kind == "proj" else ("lsh_bucket", "vnorm")):
+                assert torch.equal(getattr(meta, key)[phys, :, :n_old], before[key][phys, :, :n_old]), (b, p)
         elif (p + 1) * w.S <= first_new:       # the page ended before the new tokens
             key = "gauss" if kind == "gauss_q" else kind
             assert torch.equal(getattr(meta, key)[phys], before[key][phys]), (b, p)

@@ -21,10 +21,11 @@ SMALL = {
     "token128k": dict(B=2, L=5000, k=512),
     "ragged": dict(B=5, lens=[0, 100, 4500, 20000, 12345]),
     "pool32k": dict(B=2, lens=[3003, 2998]),
+    "socket128k": dict(B=2, lens=[5000, 3001], k=512),
 }
 
 FULL_SAMPLE = {"tiny": None, "gqa32k": [0, 5], "long_gauss": [1], "token128k": [3], "ragged": "ends",
-               "pool32k": [6]}
+               "pool32k": [6], "socket128k": [2]}
 
 
 @pytest.fixture(scope="module")
@@ -49,6 +50,24 @@ def test_pooled_key_block_sizes(dev, over):
     and a float32 cache with d=64."""
     H.log(f"[parity pool] {over}")
     w = W.make("pool32k", device=dev, **{**SMALL["pool32k"], **over})
+    st = H.gpu_step(w)
+    H.compare(w, st)
+
+
+@pytest.mark.parametrize("over", [
+    dict(lsh_tables=16, lsh_bits=1, lsh_tau=0.2),
+    dict(lsh_tables=48, lsh_bits=4, lsh_tau=3.0),
+    dict(lsh_tables=32, lsh_bits=8, Hq=8, Hkv=4, lsh_tau=1.0),                # G = 2, 256 buckets
+    dict(lsh_tables=64, lsh_bits=6, lsh_tau=0.5),                             # G = 4, 64 tables
+    dict(lsh_tables=16, lsh_bits=7, Hq=64, Hkv=8, lsh_tau=0.5),               # G = 8, 16384 masses
+    dict(lsh_tables=32, lsh_bits=5, dtype="f32", d=64, Hq=4, Hkv=4, S=64),    # G = 1, float32, page 64
+    dict(B=4, lens=[0, 1, 17, 4097], k=100),                                  # empty, single-token, k >= L_b
+])
+def test_soft_lsh_variants(dev, over):
+    """Soft-LSH token scores with 16 to 64 tables of 1 to 8 bits, every group size, a float32 cache,
+    page size 64 and ragged / empty sequences: buckets, norms and keys bit-exact, selections exact."""
+    H.log(f"[parity lsh] {over}")
+    w = W.make("socket128k", device=dev, **{**SMALL["socket128k"], **over})
     st = H.gpu_step(w)
     H.compare(w, st)
 

@@ -4,7 +4,7 @@ This module only draws inputs. It holds none of the method's arithmetic (no meta
 selection or attention) and imports neither the GPU binding nor the oracle. Both sides receive
 the same bytes: GPU tests use the tensors directly, the oracle gets host copies (``host_cache``).
 
-Six workloads, shaped like the pages' long-context decode settings (GQA 32/8 x 128 as in
+Seven workloads, shaped like the pages' long-context decode settings (GQA 32/8 x 128 as in
 Llama-3.1-8B, 32K to 256K contexts, bf16):
 
   tiny        B=1, 1/1 heads, d=64, L=4096, page 16, float32 N(0,1); top-32 pages by box bound;
@@ -22,6 +22,9 @@ Llama-3.1-8B, 32K to 256K contexts, bf16):
   pool32k     the gqa32k draw (seed 1006) with the pooled page key instead of the box bound: means
               of 4-token sub-blocks, the page key the largest q.mean over sub-blocks and query
               heads; top-64 pages; softmax and alpha=1.5
+  socket128k  B=4, 32/8, d=128, L=131072, page 16, bf16 N(0,1); 32 soft-LSH tables of 6 random
+              N(0,1) hyperplanes each (float32), temperature 0.5; top-4096 tokens per KV head
+              (32x sparsity); softmax
 
 Physical pages are a seeded permutation (block_table), so every kernel goes through the
 indirection. Any field can be overridden (smaller B or L for parity cases, ragged tails).
@@ -48,6 +51,8 @@ CONFIGS = {
                    score="box", policy="budget", pct=5, alphas=(2.0,)),
     "pool32k": dict(B=8, Hq=32, Hkv=8, d=128, L=32768, S=16, dtype="bf16", seed=1006,
                     planted=4, zstar=16.0, score="pool", pool_block=4, policy="topk", k=64, alphas=(1.0, 1.5)),
+    "socket128k": dict(B=4, Hq=32, Hkv=8, d=128, L=131072, S=16, dtype="bf16", seed=1007, score="lsh",
+                       lsh_tables=32, lsh_bits=6, lsh_tau=0.5, policy="token_topk", k=4096, alphas=(1.0,)),
 }
 
 
@@ -70,6 +75,7 @@ class Workload:
     seq_lens: torch.Tensor     # [B] int32
     lens: list                 # host copy of seq_lens
     proj: torch.Tensor | None = None     # [r, d] float32 (token128k)
+    lsh_planes: torch.Tensor | None = None   # [tables, bits, d] float32 (socket128k)
     planted: np.ndarray | None = None    # [B, Hkv, n] token positions (gqa32k)
     extra: dict = field(default_factory=dict)
 
@@ -146,6 +152,9 @@ def make(name: str, device="cpu", **over) -> Workload:
         a = torch.randn((d, r), generator=gen, device=dev, dtype=torch.float32).double().cpu()
         qm, _ = torch.linalg.qr(a)           # [d, r], orthonormal columns
         w.proj = qm.t().contiguous().float().to(dev)   # [r, d], orthonormal rows
+    if cfg.get("lsh_tables"):
+        w.lsh_planes = torch.randn((int(cfg["lsh_tables"]), int(cfg["lsh_bits"]), d), generator=gen, device=dev,
+                                   dtype=torch.float32)
     return w
 
 
