@@ -746,6 +746,53 @@ __device__ __forceinline__ void gauss_moment_general(float mu, float sd, float k
   dE = -k * powf(sd, k - 1.0f) * ik1 * c;
 }
 
+// The same moments from a table: log I_k and log I_(k-1) at a = -9 + i / 32, i = 0 .. 800
+// (a in [-9, 16]), filled once per workgroup by the quadrature above (at sd = 1), then evaluated by
+// Catmull-Rom cubics in a. I_k is an infinitely smooth function of a (a convolution with phi) and
+// its logarithm is nearly quadratic, so the cubic's error is far below float resolution of F's
+// terms. The two end cells, a >= 16 and non-finite table values use the quadrature directly.
+constexpr int kItabN = 801;
+constexpr float kItabLo = -9.0f, kItabStep = 32.0f;   // grid origin and points per unit of a
+
+__device__ void itab_fill(float k, float *__restrict__ lk, float *__restrict__ lk1) {
+  for (int i = threadIdx.x; i < kItabN; i += blockDim.x) {
+    float E, dE;
+    gauss_moment_general(kItabLo + (float)i / kItabStep, 1.0f, k, E, dE);
+    lk[i] = logf(E);
+    lk1[i] = logf(-dE / k);
+  }
+}
+
+__device__ __forceinline__ float catmull_rom(const float *t, int i, float u) {
+  const float p0 = t[i - 1], p1 = t[i], p2 = t[i + 1], p3 = t[i + 2];
+  return p1 + 0.5f * u * (p2 - p0 + u * (2.0f * p0 - 5.0f * p1 + 4.0f * p2 - p3 + u * (3.0f * (p1 - p2) + p3 - p0)));
+}
+
+__device__ __forceinline__ void gauss_moment_tab(float mu, float sd, float k, const float *lk, const float *lk1,
+                                                 float &E, float &dE) {
+  if (sd > 0.0f) {
+    const float a = mu / sd;
+    if (a < -9.0f) {
+      E = 0.0f;
+      dE = 0.0f;
+      return;
+    }
+    const float x = (a - kItabLo) * kItabStep;
+    const int i = (int)x;
+    if (i >= 1 && i <= kItabN - 3) {
+      const float u = x - (float)i;
+      const float vk = catmull_rom(lk, i, u), vk1 = catmull_rom(lk1, i, u);
+      if (isfinite(vk) && isfinite(vk1)) {   // sd^k I_k and k sd^(k-1) I_(k-1), in the log domain
+        const float ls = logf(sd);
+        E = expf(fmaf(k, ls, vk));
+        dE = -k * expf(fmaf(k - 1.0f, ls, vk1));
+        return;
+      }
+    }
+  }
+  gauss_moment_general(mu, sd, k, E, dE);
+}
+
 // tau_hat per (sequence, query head): root of F(tau) = sum_p n_p E_p(tau) - 1, which is convex
 // and non-increasing. Start at tau0 = (alpha-1) max_p m_p - 1, where F >= 0. Far from the root F
 // falls off like a Gaussian tail, where plain Newton steps are short; each step is instead
@@ -760,7 +807,7 @@ __device__ __forceinline__ void gauss_moment_general(float mu, float sd, float k
 // scaled page terms stay in LDS across the steps (pages beyond kTauLds are read each step).
 constexpr int kTauThreads = 1024;
 constexpr int kTauLds = 4096;
-// KIND: 0 alpha = 1.5, 1 alpha = 2 (closed forms), 2 any other alpha in (1, 2) (quadrature)
+// KIND: 0 alpha = 1.5, 1 alpha = 2 (closed forms), 2 any other alpha in (1, 2) (tabulated quadrature)
 template <int KIND>
 __global__ __launch_bounds__(kTauThreads) void tau_hat_kernel(CacheView c, const float *__restrict__ m,
                                                               const float *__restrict__ s, float alpha,
@@ -768,6 +815,7 @@ __global__ __launch_bounds__(kTauThreads) void tau_hat_kernel(CacheView c, const
   __shared__ float t_mu[kTauLds], t_sd[kTauLds], t_n[kTauLds];
   __shared__ double2 red2[kTauThreads / kWave];
   __shared__ float redf[kTauThreads / kWave];
+  __shared__ float t_lk[KIND == 2 ? kItabN : 1], t_lk1[KIND == 2 ? kItabN : 1];
   const int bh = blockIdx.x, b = bh / c.Hq;
   const int L = seq_len(c, b);
   const int P = num_pages(c, L);
@@ -778,6 +826,7 @@ __global__ __launch_bounds__(kTauThreads) void tau_hat_kernel(CacheView c, const
   }
   const float am1 = alpha - 1.0f;
   const float kpow = 1.0f / am1;
+  if (KIND == 2) itab_fill(kpow, t_lk, t_lk1);   // published by the barrier of block_max below
   float mx = -INFINITY;
   for (int p = threadIdx.x; p < P; p += kTauThreads) {
     const float mv = mr[p];
@@ -805,7 +854,7 @@ __global__ __launch_bounds__(kTauThreads) void tau_hat_kernel(CacheView c, const
       }
       float E, dE;
       if (KIND == 2)
-        gauss_moment_general(mu - tau, sd, kpow, E, dE);
+        gauss_moment_tab(mu - tau, sd, kpow, t_lk, t_lk1, E, dE);
       else
         gauss_moment(mu - tau, sd, KIND == 1, E, dE);
       F += (double)(n * E);
