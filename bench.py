@@ -163,18 +163,27 @@ def dominant_kernel(st: Step) -> str:
             "proj": "score_proj_kernel", "pool": "score_pool_kernel", "lsh": "score_lsh_kernel"}[st.kind]
 
 
+def kernel_sources_sha256(sources) -> str:
+    """One hash over the listed source files (repository-relative paths), in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in sources:
+        h.update(open(os.path.join(ROOT, rel), "rb").read())
+    return h.hexdigest()
+
+
 def recorded_traffic(workload: str, kernel: str):
     """HBM bytes per launch of the dominant kernel from the committed PMC record (profiles/), or None
-    when there is no record or the kernel source changed since the counters were taken."""
-    import hashlib
+    when there is no record or a source the kernel is built from changed since the counters were
+    taken (the record lists the files and their joint hash)."""
     path = os.path.join(ROOT, "profiles", f"{workload}_score_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, rec["source"])
-    if rec.get("kernel") != kernel or not os.path.exists(src):
+    srcs = rec.get("sources")
+    if rec.get("kernel") != kernel or not srcs or not all(os.path.exists(os.path.join(ROOT, f)) for f in srcs):
         return None
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+    if kernel_sources_sha256(srcs) != rec.get("sources_sha256"):
         return None
     return int(rec["traffic_bytes"])
 
