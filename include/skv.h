@@ -95,7 +95,7 @@ typedef struct skv_meta {
   float *pool;        /* POOL:  [Nphys, Hkv, S / pool_block, d] float32 sub-block mean keys */
   int32_t lsh_tables; /* LSH:   number of hash tables L: 16, 32, 48 or 64 */
   int32_t lsh_bits;   /* LSH:   hyperplanes per table P, 1..8 (2^P buckets) */
-  const float *lsh_planes; /* LSH: [L, P, d] float32 hyperplanes (read only) */
+  const float *lsh_planes; /* LSH: [L, P, d] float32 hyperplanes (read only, 16-byte aligned) */
   uint8_t *lsh_bucket; /* LSH:  [Nphys, Hkv, S, L] bucket id of every token in every table */
   float *vnorm;       /* LSH:   [Nphys, Hkv, S] float32 norm of every token's value vector */
 } skv_meta;
@@ -223,8 +223,8 @@ typedef struct skv_select_params {
  *     sum_p n_p E[((alpha-1) Z_p - tau)_+^(1/(alpha-1))] = 1 with Z_p ~ N(m_p, s_p^2); a page is
  *     kept iff some head h of the group has (alpha-1) shat_h(p) > tau_hat_h - delta.
  *     tau_hat [B, Hq] float32 receives the thresholds (unused pointer otherwise). alpha = 1.5
- *     and 2 use the closed forms of the expectation; any other alpha in (1, 2) evaluates it by
- *     Gauss-Legendre quadrature (about 20x the work per page and step).
+ *     and 2 use the closed forms of the expectation; any other alpha in (1, 2) evaluates it from a
+ *     table of the needed Gaussian integrals, filled once per solve by Gauss-Legendre quadrature.
  *   THRESH_BOX: tau_hat as THRESH_GAUSS (from the GAUSS m, s); the page's estimated maximum is
  *     the deterministic box bound ("EntmaxKV" s2.A): keep iff (alpha-1) scale key[p] >
  *     min_h tau_hat_h - delta, key = the BOX key (max over the group's heads of the unscaled
@@ -233,8 +233,13 @@ typedef struct skv_select_params {
  * Output: sel_idx [B, Hkv, cap] int32 holds the kept logical page (or token) indices in
  * ascending order, sel_count [B, Hkv] int32 their number; entries past the count are not
  * written. cap must be >= k (TOPK, TOKEN_TOPK), >= max_pages (BUDGET, THRESH_*, ALL pages)
- * or >= max_pages * S (ALL tokens), else SKV_ERR_CAPACITY. workspace: skv_workspace_bytes(c,
- * SKV_OP_SELECT, p, cap). The scores are those written by skv_score_pages for the same cache. */
+ * or >= max_pages * S (ALL tokens), else SKV_ERR_CAPACITY. The scores are those written by
+ * skv_score_pages for the same cache.
+ * workspace: optional. skv_workspace_bytes(c, SKV_OP_SELECT, p, cap) is non-zero only for
+ * TOKEN_TOPK over dense keys (token_k = 0): given at least that many bytes, 256-byte aligned, the
+ * selection runs on many workgroups per (sequence, KV head) (a sampled bound, a filtered pass and
+ * an exact selection among the candidates); with less it runs on one workgroup per (sequence, KV
+ * head). Both give the same indices. */
 skv_status skv_select_pages(const skv_cache *c, const skv_scores *sc, const skv_select_params *p,
                             int32_t *sel_idx, int32_t *sel_count, int32_t cap, float *tau_hat, void *workspace,
                             size_t workspace_bytes, void *stream);

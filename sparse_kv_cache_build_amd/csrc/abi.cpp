@@ -145,8 +145,13 @@ skv_status skv_workspace_bytes(const skv_cache *c, int32_t op, const void *param
     *bytes = score_ws(c, kind, 64);
     return SKV_OK;
   }
-  if (op == SKV_OP_SELECT) {
+  if (op == SKV_OP_SELECT) {   // token top-k over dense keys: the candidate segments of the many-block path
+    const skv_select_params *p = static_cast<const skv_select_params *>(params);
     *bytes = 0;
+    if (p->policy == SKV_SEL_TOKEN_TOPK) {
+      const skv::CandLayout lay(c->batch, c->num_q_heads, c->num_kv_heads, c->max_pages * c->page_size, 64);
+      if (lay.nb <= 8192) *bytes = lay.total;
+    }
     return SKV_OK;
   }
   if (op == SKV_OP_CANDIDATES) {
@@ -182,7 +187,7 @@ static skv_status meta_args(const skv_cache *c, const skv_meta *m) {
       return SKV_ERR_INVALID_ARG;
   }
   if (m->kinds & SKV_META_LSH) {
-    if (!m->lsh_planes || !m->lsh_bucket || !m->vnorm || !aligned(m->lsh_bucket, 16) || !aligned(m->lsh_planes, 4) ||
+    if (!m->lsh_planes || !m->lsh_bucket || !m->vnorm || !aligned(m->lsh_bucket, 16) || !aligned(m->lsh_planes, 16) ||
         !aligned(m->vnorm, 4))
       return SKV_ERR_INVALID_ARG;
     if (!lsh_ok(m->lsh_tables, m->lsh_bits)) return SKV_ERR_UNSUPPORTED;
@@ -239,7 +244,7 @@ skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q,
       return SKV_ERR_INVALID_ARG;
   } else if (kind == SKV_SCORE_LSH) {
     if (!(m->kinds & SKV_META_LSH) || !m->lsh_planes || !m->lsh_bucket || !m->vnorm || !out->key ||
-        !aligned(m->lsh_bucket, 16) || !aligned(m->lsh_planes, 4) || !aligned(m->vnorm, 4))
+        !aligned(m->lsh_bucket, 16) || !aligned(m->lsh_planes, 16) || !aligned(m->vnorm, 4))
       return SKV_ERR_INVALID_ARG;
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SKV_ERR_INVALID_ARG;   // the temperature
     if (!lsh_ok(m->lsh_tables, m->lsh_bits) ||
@@ -300,8 +305,6 @@ skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q,
 skv_status skv_select_pages(const skv_cache *c, const skv_scores *sc, const skv_select_params *p, int32_t *sel_idx,
                             int32_t *sel_count, int32_t cap, float *tau_hat, void *workspace, size_t workspace_bytes,
                             void *stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   skv_status st = check_cache(c);
   if (st != SKV_OK) return st;
   if (!sc || !p || !sel_idx || !sel_count || cap < 1) return SKV_ERR_INVALID_ARG;
@@ -322,6 +325,12 @@ skv_status skv_select_pages(const skv_cache *c, const skv_scores *sc, const skv_
       }
       if (p->k < 1 || !sc->key) return SKV_ERR_INVALID_ARG;
       if (cap < p->k) return SKV_ERR_CAPACITY;
+      if (p->policy == SKV_SEL_TOKEN_TOPK && workspace && aligned(workspace, 256)) {
+        const skv::CandLayout lay(c->batch, c->num_q_heads, c->num_kv_heads, Lmax, 64);
+        if (lay.nb <= 8192 && workspace_bytes >= lay.total)
+          return hip_status(skv::launch_select_token_dense(v, sc->key, Lmax, p->k, static_cast<char *>(workspace),
+                                                           sel_idx, sel_count, cap, s));
+      }
       const int stride = p->policy == SKV_SEL_TOPK ? maxP : Lmax;
       return hip_status(skv::launch_select_topk(v, sc->key, stride, p->policy, p->k, 0, sel_idx, sel_count, cap, s));
     }

@@ -43,6 +43,8 @@ hipError_t launch_token_bound(const CacheView &c, int dtype, const void *q, int 
                               const uint16_t *kproj, char *cand, hipStream_t st);
 hipError_t launch_select_token_cand(const CacheView &c, int k, int r, const char *cand, int32_t *sel_idx,
                                     int32_t *sel_count, int cap, hipStream_t st);
+hipError_t launch_select_token_dense(const CacheView &c, const float *key, int key_stride, int k, char *ws,
+                                     int32_t *sel_idx, int32_t *sel_count, int cap, hipStream_t st);
 hipError_t launch_select_topk(const CacheView &c, const float *key, int key_stride, int policy, int k, int pct,
                               int32_t *sel_idx, int32_t *sel_count, int cap, hipStream_t st);
 hipError_t launch_select_all(const CacheView &c, int tokens, int32_t *sel_idx, int32_t *sel_count, int cap,

@@ -200,9 +200,18 @@ __global__ __launch_bounds__(256) void lsh_prep_kernel(CacheView c, const T *__r
   }
   __syncthreads();
   for (int m = threadIdx.x; m < L * P; m += blockDim.x) {
-    const float *w = planes + (size_t)m * D;
+    const float4 *w4 = reinterpret_cast<const float4 *>(planes + (size_t)m * D);
+    float4 wr[D / 4];   // the whole hyperplane in flight before the (sequential) sum
+#pragma unroll
+    for (int j = 0; j < D / 4; ++j) wr[j] = w4[j];
     double dot = 0.0;
-    for (int j = 0; j < D; ++j) dot = fma((double)w[j], qs[j], dot);
+#pragma unroll
+    for (int j = 0; j < D / 4; ++j) {
+      dot = fma((double)wr[j].x, qs[4 * j], dot);
+      dot = fma((double)wr[j].y, qs[4 * j + 1], dot);
+      dot = fma((double)wr[j].z, qs[4 * j + 2], dot);
+      dot = fma((double)wr[j].w, qs[4 * j + 3], dot);
+    }
     const double z = nq > 0.0 ? dot / nq : 0.0;
     sg[2 * m] = 1.0 / (1.0 + exp(-((2.0 * z) / tau)));
     sg[2 * m + 1] = 1.0 / (1.0 + exp(-((-2.0 * z) / tau)));

@@ -524,13 +524,101 @@ __global__ __launch_bounds__(kBoundThreads) void token_bound_kernel(CacheView c,
   if (tid == 0) bound[unit] = Tlo;
 }
 
+// Token top-k over dense keys on many workgroups (the caller gave the selection a workspace laid
+// out like the fused candidate set): the bound of step 1 of select_topk_large_kernel, one block
+// per unit; then one wave per group of kCandSegTokens keys writes the keys >= T_lo as (key, token)
+// into its segment, in token order, with the count; then select_token_cand_kernel selects exactly.
+__global__ __launch_bounds__(kTokThreads) void dense_bound_kernel(CacheView c, const float *__restrict__ key,
+                                                                  int key_stride, int k, uint32_t *__restrict__ bound) {
+  __shared__ uint32_t ckey[kTokSample];
+  __shared__ __align__(16) uint32_t hist[kTokWaves * 256];
+  __shared__ uint32_t bc[2];
+  const int unit = blockIdx.x, b = unit / c.Hkv;
+  const int n = seq_len(c, b);
+  const int kk = min(k, n);
+  uint32_t Tlo = 0;   // short sequences: every key is a candidate
+  if (kk >= 1 && kk < n && n > kTokCand) {
+    const float *kr = key + (size_t)unit * key_stride;
+    const int run = kTokSample / 64, stride = n / 64;
+    for (int s = threadIdx.x; s < kTokSample; s += kTokThreads)
+      ckey[s] = f32_order_key(kr[(s / run) * stride + s % run]);
+    __syncthreads();
+    const double expect = (double)kk * kTokSample / n;
+    const double rs = ceil(expect + 4.0 * sqrt(expect) + 16.0);
+    if (rs < kTokSample) {
+      uint32_t T, need;
+      auto lget = [&](int i) { return ckey[i]; };
+      radix_kth<kTokThreads>(lget, kTokSample, (uint32_t)rs, hist, bc, T, need, 2);   // a lower bound suffices
+      Tlo = T;
+    }
+  }
+  if (threadIdx.x == 0) bound[unit] = Tlo;
+}
+
+__global__ __launch_bounds__(256) void dense_filter_kernel(CacheView c, const float *__restrict__ key, int key_stride,
+                                                           int vec, const uint32_t *__restrict__ bound,
+                                                           int32_t *__restrict__ count, float2 *__restrict__ segs,
+                                                           int nb) {
+  constexpr int GT = kCandSegTokens, NT = GT / (4 * kWave);   // tiles of 4 keys per lane
+  const int unit = blockIdx.y, b = unit / c.Hkv;
+  const int n = seq_len(c, b);
+  const int lane = threadIdx.x & (kWave - 1), gid = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int tg = gid * GT;
+  if (tg >= n || gid >= nb) return;
+  const uint32_t Tlo = bound[unit];
+  const float *kr = key + (size_t)unit * key_stride;
+  float2 *seg = segs + ((size_t)unit * nb + gid) * GT;
+  float x[NT][4];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {   // every load in flight before any compaction
+    const int i = tg + j * 4 * kWave + 4 * lane;
+    if (vec && i + 3 < n) {
+      const float4 f = *reinterpret_cast<const float4 *>(kr + i);
+      x[j][0] = f.x;
+      x[j][1] = f.y;
+      x[j][2] = f.z;
+      x[j][3] = f.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[j][e] = i + e < n ? kr[i + e] : 0.0f;
+    }
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int i = tg + j * 4 * kWave + 4 * lane;
+    bool f[4];
+    uint64_t bal[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[e] = i + e < n && f32_order_key(x[j][e]) >= Tlo;
+      bal[e] = __ballot(f[e]);
+    }
+    // token order is lane-major within a tile: rank = keys of lower lanes + lower e in this lane
+    int pos = cnt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      pos += __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal[e], 0u));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (f[e]) seg[pos] = make_float2(x[j][e], __int_as_float(i + e));
+      pos += f[e] ? 1 : 0;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cnt += __popcll(bal[e]);
+  }
+  if (lane == 0) count[(size_t)unit * nb + gid] = cnt;
+}
+
 // Step 3 of the fused token top-k, one block per unit: gather the unit's candidate segments in
 // segment order (so in token order) into LDS and select exactly there.
 // When fewer than k candidates arrived, or more than LDS holds, every key of the unit is
-// recomputed from the projected keys (same arithmetic) and selected by radix over global memory.
-template <int G>
+// recomputed from the projected keys (same arithmetic), or read from the dense keys (DENSE), and
+// selected by radix over global memory.
+template <int G, bool DENSE>
 __global__ __launch_bounds__(kTokThreads) void select_token_cand_kernel(CacheView c, int k,
                                                                         const char *__restrict__ cand, CandLayout lay,
+                                                                        const float *__restrict__ dkey, int dstride,
                                                                         int32_t *__restrict__ sel_idx,
                                                                         int32_t *__restrict__ sel_count, int cap) {
   __shared__ uint32_t ckey[kTokCand];
@@ -623,6 +711,14 @@ __global__ __launch_bounds__(kTokThreads) void select_token_cand_kernel(CacheVie
     auto lidx = [&](int i) { return cidx[i]; };
     radix_kth_regs<kTokThreads, GPT>(u, total, (uint32_t)kk, hist, bc, T, need, 4, kmin, kmax);
     ordered_take<kTokThreads>(lget, lidx, total, T, need, out, scan_scratch);
+    return;
+  }
+  if constexpr (DENSE) {   // exact fallback over the dense keys
+    const float *kr = dkey + (size_t)unit * dstride;
+    auto dget = [&](int t) -> uint32_t { return f32_order_key(kr[t]); };
+    auto didx = [](int i) { return i; };
+    radix_kth<kTokThreads>(dget, n, (uint32_t)kk, hist, bc, T, need);
+    ordered_take<kTokThreads>(dget, didx, n, T, need, out, scan_scratch);
     return;
   }
   // exact fallback: recompute every key of the unit
@@ -992,13 +1088,32 @@ hipError_t launch_token_bound(const CacheView &c, int dtype, const void *q, int 
 hipError_t launch_select_token_cand(const CacheView &c, int k, int r, const char *cand, int32_t *sel_idx,
                                     int32_t *sel_count, int cap, hipStream_t st) {
   const CandLayout lay(c.B, c.Hq, c.Hkv, c.maxP * c.S, 64);   // layout independent of the rank
+  const dim3 grid(c.B * c.Hkv);
   switch (c.G) {
-    case 1: select_token_cand_kernel<1><<<c.B * c.Hkv, kTokThreads, 0, st>>>(c, k, cand, lay, sel_idx, sel_count, cap); break;
-    case 2: select_token_cand_kernel<2><<<c.B * c.Hkv, kTokThreads, 0, st>>>(c, k, cand, lay, sel_idx, sel_count, cap); break;
-    case 4: select_token_cand_kernel<4><<<c.B * c.Hkv, kTokThreads, 0, st>>>(c, k, cand, lay, sel_idx, sel_count, cap); break;
-    case 8: select_token_cand_kernel<8><<<c.B * c.Hkv, kTokThreads, 0, st>>>(c, k, cand, lay, sel_idx, sel_count, cap); break;
+#define SKV_TOKCAND(GG)                                                                                         \
+  case GG:                                                                                                      \
+    select_token_cand_kernel<GG, false><<<grid, kTokThreads, 0, st>>>(c, k, cand, lay, nullptr, 0, sel_idx, \
+                                                                      sel_count, cap);                      \
+    break;
+    SKV_TOKCAND(1) SKV_TOKCAND(2) SKV_TOKCAND(4) SKV_TOKCAND(8)
+#undef SKV_TOKCAND
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_select_token_dense(const CacheView &c, const float *key, int key_stride, int k, char *ws,
+                                     int32_t *sel_idx, int32_t *sel_count, int cap, hipStream_t st) {
+  const CandLayout lay(c.B, c.Hq, c.Hkv, c.maxP * c.S, 64);
+  uint32_t *bound = reinterpret_cast<uint32_t *>(ws + lay.bound);
+  int32_t *count = reinterpret_cast<int32_t *>(ws + lay.count);
+  float2 *segs = reinterpret_cast<float2 *>(ws + lay.seg);
+  const int U = c.B * c.Hkv;
+  dense_bound_kernel<<<U, kTokThreads, 0, st>>>(c, key, key_stride, k, bound);
+  const int vec = (key_stride % 4 == 0) && (reinterpret_cast<uintptr_t>(key) % 16 == 0);
+  dense_filter_kernel<<<dim3((lay.nb + 3) / 4, U), 256, 0, st>>>(c, key, key_stride, vec, bound, count, segs, lay.nb);
+  select_token_cand_kernel<1, true><<<U, kTokThreads, 0, st>>>(c, k, ws, lay, key, key_stride, sel_idx, sel_count,
+                                                                cap);
   return hipGetLastError();
 }
 

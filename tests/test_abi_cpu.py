@@ -105,6 +105,20 @@ def test_workspace_sizes_follow_plan(L):
     assert st == 0 and n_ent >= cand
 
 
+def test_select_workspace_only_for_dense_token_topk(L):
+    """The selection needs no workspace, except the optional candidate segments of the token top-k
+    over dense keys: 8 bytes per token position plus per-unit counts and bounds."""
+    c = cache()
+    n = C.c_size_t(0)
+    for pol in (B.SEL_TOPK, B.SEL_BUDGET, B.SEL_THRESH_GAUSS, B.SEL_ALL, B.SEL_THRESH_BOX):
+        p = B.SelectParams(pol, 4, 5, 1.5, 0.5, 0, 0.1)
+        assert L.skv_workspace_bytes(C.byref(c), B.OP_SELECT, C.byref(p), 64, C.byref(n)) == 0 and n.value == 0
+    p = B.SelectParams(B.SEL_TOKEN_TOPK, 64, 0, 1.5, 0.5, 1, 0.1)
+    assert L.skv_workspace_bytes(C.byref(c), B.OP_SELECT, C.byref(p), 64, C.byref(n)) == 0
+    U, tokens = 2 * 8, 64 * 16
+    assert n.value >= U * tokens * 8 and n.value % 256 == 0
+
+
 def test_select_capacity_and_policy_checks(L):
     c = cache()
     sc = B.Scores(FAKE, FAKE, FAKE, FAKE)
@@ -169,7 +183,7 @@ def test_score_and_meta_validation(L):
     for tables, bits, st in ((20, 4, B.SKV_ERR_UNSUPPORTED), (32, 9, B.SKV_ERR_UNSUPPORTED),
                              (32, 0, B.SKV_ERR_UNSUPPORTED), (80, 4, B.SKV_ERR_UNSUPPORTED)):
         assert L.skv_build_page_meta(C.byref(c), C.byref(lsh(tables, bits)), None) == st, (tables, bits)
-    for kw in (dict(bucket=None), dict(vnorm=None), dict(planes=None), dict(bucket=FAKE + 8)):
+    for kw in (dict(bucket=None), dict(vnorm=None), dict(planes=None), dict(bucket=FAKE + 8), dict(planes=FAKE + 4)):
         assert L.skv_build_page_meta(C.byref(c), C.byref(lsh(32, 6, **kw)), None) == B.SKV_ERR_INVALID_ARG, kw
     big = 1 << 24
     assert L.skv_score_pages(C.byref(c), C.byref(lsh(64, 7)), C.c_void_p(FAKE), B.SCORE_LSH, 1.0, C.byref(out),

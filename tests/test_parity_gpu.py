@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import gpu_harness as H
+import sparse_kv_cache_build_amd as skv
 import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -241,3 +242,30 @@ def test_full_size_sampled(dev, name):
     H.log(f"  sampled seqs={seqs} units={rep.units} near_ties={rep.near_ties} max_err/tol={rep.max_err:.3f}")
     del st, w
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,over,k", [
+    ("socket128k", dict(B=2, lens=[40000, 9000]), 700),
+    ("socket128k", dict(B=3, lens=[40000, 100, 0]), 10000),       # more than LDS holds: the exact fallback
+    ("token128k", dict(B=2, lens=[30000, 20001]), 512),
+])
+def test_dense_token_topk_many_workgroups_equals_one(dev, name, over, k):
+    """The token top-k over dense keys with a selection workspace (bound, filtered pass on many
+    workgroups, selection among candidates) against the one-workgroup path without it."""
+    H.log(f"[dense token top-k] {name} {over} k={k}")
+    w = W.make(name, device=dev, **over)
+    st = H.gpu_step(w)
+    p = skv.select_params("token_topk", k=k, tokens=1)
+    many = skv.Selection(st.cache, p)
+    assert many.ws.numel() >= skv.workspace_bytes(st.cache, skv._binding.OP_SELECT, p, many.cap) > 256
+    one = skv.Selection(st.cache, p)
+    one.ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    skv.select_pages(st.cache, st.scores, None, out=many)
+    skv.select_pages(st.cache, st.scores, None, out=one)
+    torch.cuda.synchronize()
+    cm, co = many.count.cpu().numpy(), one.count.cpu().numpy()
+    assert np.array_equal(cm, co)
+    im, io = many.idx.cpu().numpy(), one.idx.cpu().numpy()
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            assert np.array_equal(im[b, g, :cm[b, g]], io[b, g, :co[b, g]]), (b, g)
