@@ -235,32 +235,69 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(CacheView c, const int3
 // ---------------------------------------------------------------- entmax pass 1
 
 // Per-head maximum and ordered compaction of z' > max - 1 for pass 1 (logits of the partition
-// in LDS: zs[h * rps + r]; rows past NR are not read). Every thread of the block must call it.
+// in LDS: zs[h * rps + r]; rows past NR are not read). All G heads at once: every thread takes a
+// contiguous chunk of rows, so the thread order is the row order; the maxima and the survivor
+// counts of the G heads are combined over the block with one barrier each. Every thread of the
+// block must call it.
 template <int G>
 __device__ __forceinline__ void entmax_compact(const float *zs, int rps, int NR, int unit, int split, int nsplit,
                                                int row0, float2 *__restrict__ cand, int32_t *__restrict__ cand_cnt,
-                                               float *__restrict__ cand_max, int *scan_scratch, float *redf) {
-  const int tid = threadIdx.x;
+                                               float *__restrict__ cand_max) {
+  constexpr int NW = kAttnThreads / kWave;
+  __shared__ float wmax[NW][G];
+  __shared__ int wcnt[NW][G];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int per = (NR + kAttnThreads - 1) / kAttnThreads;
+  const int r0 = min(NR, tid * per), r1 = min(NR, r0 + per);
+  float mx[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) mx[h] = -INFINITY;
+  for (int r = r0; r < r1; ++r)
+#pragma unroll
+    for (int h = 0; h < G; ++h) mx[h] = fmaxf(mx[h], zs[h * rps + r]);
+#pragma unroll
   for (int h = 0; h < G; ++h) {
-    float mx = -INFINITY;
-    for (int r = tid; r < NR; r += kAttnThreads) mx = fmaxf(mx, zs[h * rps + r]);
-    mx = block_max<kAttnThreads>(mx, redf);
+    const float m = wave_max_dpp(mx[h]);
+    if (lane == 0) wmax[w][h] = m;
+  }
+  __syncthreads();
+  int nk[G], incl[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float m = wmax[0][h];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) m = fmaxf(m, wmax[i][h]);
+    mx[h] = m;
+    nk[h] = 0;
+  }
+  for (int r = r0; r < r1; ++r)
+#pragma unroll
+    for (int h = 0; h < G; ++h) nk[h] += zs[h * rps + r] > mx[h] - 1.0f ? 1 : 0;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    incl[h] = wave_incl_scan(nk[h]);
+    if (lane == kWave - 1) wcnt[w][h] = incl[h];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const int t = wcnt[i][h];
+      before += i < w ? t : 0;
+      tot += t;
+    }
     const size_t lid = ((size_t)unit * G + h) * nsplit + split;
     float2 *cl = cand + lid * rps;
-    // ordered compaction of z' > mx - 1 (contiguous chunk of rows per thread)
-    const int per = (NR + kAttnThreads - 1) / kAttnThreads;
-    const int r0 = min(NR, tid * per), r1 = min(NR, r0 + per);
-    int nk = 0;
-    for (int r = r0; r < r1; ++r) nk += zs[h * rps + r] > mx - 1.0f;
-    int tot;
-    int pos = block_excl_scan<kAttnThreads>(nk, scan_scratch, &tot);
+    int pos = before + incl[h] - nk[h];
     for (int r = r0; r < r1; ++r) {
       const float z = zs[h * rps + r];
-      if (z > mx - 1.0f) cl[pos++] = make_float2(z, __int_as_float(row0 + r));
+      if (z > mx[h] - 1.0f) cl[pos++] = make_float2(z, __int_as_float(row0 + r));
     }
     if (tid == 0) {
       cand_cnt[lid] = tot;
-      cand_max[lid] = mx;
+      cand_max[lid] = mx[h];
     }
   }
 }
@@ -273,8 +310,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
     float *__restrict__ cand_max) {
   using RL = RowLayout<D>;
   extern __shared__ float zs[];  // [G][rps] logits, then [rps] row offsets (8-byte aligned)
-  __shared__ int scan_scratch[kAttnThreads / kWave + 1];
-  __shared__ float redf[kAttnThreads / kWave];
   const int split = blockIdx.x, unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
   const int count = min(max(sel_count[unit], 0), cap);
   const int rows_per_item = gran ? 1 : c.S;
@@ -321,8 +356,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
       if (r + u * RL::RGB < NR) logits(r + u * RL::RGB, o[u], kx[u]);
   }
   __syncthreads();
-  entmax_compact<G>(zs, rps, NR, unit, split, nsplit, it0 * rows_per_item, cand, cand_cnt, cand_max, scan_scratch,
-                    redf);
+  entmax_compact<G>(zs, rps, NR, unit, split, nsplit, it0 * rows_per_item, cand, cand_cnt, cand_max);
 }
 
 // Entmax pass 1 for bf16 caches on the matrix cores: the logits of a 16-row tile for all G heads
@@ -342,8 +376,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_mfma_kernel(
     float2 *__restrict__ cand, int32_t *__restrict__ cand_cnt, float *__restrict__ cand_max) {
   constexpr int KB = D / 32, UNR = 4, NWV = kAttnThreads / kWave;
   extern __shared__ float zs[];  // [G][rps] logits, then [rps] row offsets (8-byte aligned)
-  __shared__ int scan_scratch[kAttnThreads / kWave + 1];
-  __shared__ float redf[kAttnThreads / kWave];
   const int split = blockIdx.x, unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
   const int count = min(max(sel_count[unit], 0), cap);
   const int rows_per_item = gran ? 1 : c.S;
@@ -399,8 +431,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_mfma_kernel(
     }
   }
   __syncthreads();
-  entmax_compact<G>(zs, rps, NR, unit, split, nsplit, it0 * rows_per_item, cand, cand_cnt, cand_max, scan_scratch,
-                    redf);
+  entmax_compact<G>(zs, rps, NR, unit, split, nsplit, it0 * rows_per_item, cand, cand_cnt, cand_max);
 }
 
 // ---------------------------------------------------------------- entmax threshold and p V

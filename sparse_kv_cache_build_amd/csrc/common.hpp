@@ -292,6 +292,19 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
 }
 __device__ __forceinline__ int wave_incl_scan(int v) { return (int)wave_incl_scan((uint32_t)v); }
 
+// Wave maximum with DPP moves (row_shr 1, 2, 4, 8, then row_bcast 15 and 31 as in the scan above):
+// lane 63 ends with the maximum of all 64 lanes, read back as a wave-uniform value.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  const int ninf = __float_as_int(-INFINITY);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x111, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x112, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x114, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x118, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x142, 0xa, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), 0x143, 0xc, 0xf, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+
 // Block-wide exclusive prefix sum for blocks of NT threads (NT a multiple of 64, <= 1024).
 // `scratch` holds NT/64 + 1 ints of shared memory. Returns the exclusive prefix; *total gets the
 // block sum. Contains __syncthreads: every thread of the block must call it.
