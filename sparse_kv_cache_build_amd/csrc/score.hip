@@ -293,47 +293,84 @@ __global__ __launch_bounds__(256) void score_lsh_kernel(CacheView c, int L, int 
   }
 }
 
-// GAUSS scores: one lane per page, G heads. m = scale sum_j q_j mean_j, s = scale sqrt(sum_j
-// q_j^2 var_j) (float64), shat = m + s sqrt(2 ln n_p). Outputs [B, Hq, maxP].
+// GAUSS scores. m = scale sum_j q_j mean_j, s = scale sqrt(sum_j q_j^2 var_j) (float64, j
+// ascending), shat = m + s sqrt(2 ln n_p) (or the quantile maximum). Outputs [B, Hq, maxP]; NaN past
+// the sequence. A wave owns 64 pages (a lane each, G heads); their rows are read in chunks of 16
+// coordinates (64 bytes of the mean row and 64 of the variance row: 8 lanes per page, eight pages per
+// load instruction) into LDS, where each lane sums its page; the (q, q^2) pairs come from LDS as
+// broadcast reads. The next chunk is loaded while the current one is summed.
 template <int D, int G>
 __global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const float *__restrict__ gauss,
                                                           const double *__restrict__ qpm, double scale, int quantile,
                                                           float *__restrict__ m_out, float *__restrict__ s_out,
                                                           float *__restrict__ shat_out) {
+  constexpr int CW = 16, NC = D / CW, LDR = 2 * CW + 4, NK = 8;   // 64 rows, 8 per load instruction
+  __shared__ double2 qs[G * D];
+  __shared__ float xs[4][64 * LDR];
   const int unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
-  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int pblk = blockIdx.x * 256, p0 = pblk + wave * 64;
+  const int L = seq_len(c, b), np = num_pages(c, L);
+  const size_t ob = (size_t)(b * c.Hq + g * G) * c.maxP;
+  if (pblk >= np) {   // every page of the block lies past the sequence
+    for (int i = threadIdx.x; i < 256 * G; i += blockDim.x) {
+      const int p = pblk + i % 256, h = i / 256;
+      if (p < c.maxP) m_out[ob + (size_t)h * c.maxP + p] = s_out[ob + (size_t)h * c.maxP + p] =
+          shat_out[ob + (size_t)h * c.maxP + p] = NAN;
+    }
+    return;
+  }
+  const double2 *qq = reinterpret_cast<const double2 *>(qpm + (size_t)(b * c.Hq + g * G) * D * 2);
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) qs[i] = qq[i];
+  const int *bt = c.bt + (size_t)b * c.maxP;
+  // load side: lane -> page lrow + 8k, half (mean or variance row) and 4 of the 16 columns
+  const int lrow = lane >> 3, half = (lane >> 2) & 1, lcol = (lane & 3) * 4;
+  long long off[NK];
+  float4 r[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const int p = p0 + lrow + 8 * k;
+    off[k] = p < np ? (((long long)bt[p] * c.Hkv + g) * 2 + half) * D + lcol : -1;
+    r[k] = off[k] >= 0 ? *reinterpret_cast<const float4 *>(gauss + off[k]) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float *xw = xs[wave];
+  double sm[G], sv[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) sm[h] = sv[h] = 0.0;
+  for (int ch = 0; ch < NC; ++ch) {
+    __syncthreads();   // the previous chunk has been read (and qs is staged)
+#pragma unroll
+    for (int k = 0; k < NK; ++k) *reinterpret_cast<float4 *>(xw + (lrow + 8 * k) * LDR + half * CW + lcol) = r[k];
+    if (ch + 1 < NC) {
+#pragma unroll
+      for (int k = 0; k < NK; ++k)
+        r[k] = off[k] >= 0 ? *reinterpret_cast<const float4 *>(gauss + off[k] + (ch + 1) * CW)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+    const float *xm = xw + lane * LDR, *xv = xm + CW;
+    const double2 *qc = qs + ch * CW;
+#pragma unroll 2   // bounded unrolling: the q pairs of a coordinate live only while it is summed
+    for (int j = 0; j < CW; ++j) {
+      const double dm = xm[j], dv = xv[j];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const double2 qp = qc[h * D + j];
+        sm[h] = fma(qp.x, dm, sm[h]);
+        sv[h] = fma(qp.y, dv, sv[h]);
+      }
+    }
+  }
+  const int p = p0 + lane;
   if (p >= c.maxP) return;
-  const int L = seq_len(c, b);
-  const size_t o0 = (size_t)(b * c.Hq + g * G) * c.maxP + p;
-  if (p >= num_pages(c, L)) {
+  const size_t o0 = ob + p;
+  if (p >= np) {
 #pragma unroll
     for (int h = 0; h < G; ++h) m_out[o0 + (size_t)h * c.maxP] = s_out[o0 + (size_t)h * c.maxP] =
         shat_out[o0 + (size_t)h * c.maxP] = NAN;
     return;
   }
   const int n = min(c.S, L - p * c.S);
-  const int phys = c.bt[(size_t)b * c.maxP + p];
-  const float *mu = gauss + ((size_t)phys * c.Hkv + g) * 2 * D;
-  const float *var = mu + D;
-  const double *qq = qpm + (size_t)(b * c.Hq + g * G) * D * 2;
-  double sm[G], sv[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) sm[h] = sv[h] = 0.0;
-#pragma unroll
-  for (int j0 = 0; j0 < D; j0 += 8) {
-    float xm[8], xv[8];
-    Elem<float>::load8(mu + j0, xm);
-    Elem<float>::load8(var + j0, xv);
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const double dm = xm[jj], dv = xv[jj];
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        sm[h] = fma(qq[((size_t)h * D + j0 + jj) * 2], dm, sm[h]);
-        sv[h] = fma(qq[((size_t)h * D + j0 + jj) * 2 + 1], dv, sv[h]);
-      }
-    }
-  }
   // estimated maximum of the page's n scores: m + s sqrt(2 ln n), or (quantile) m + s Phi^-1(1 - 1/n)
   // = m + s sqrt(2) erfcinv(2 / n)
   const double lg = n <= 1 ? 0.0 : (quantile ? 1.4142135623730951 * erfcinv(2.0 / n) : sqrt(2.0 * log((double)n)));
