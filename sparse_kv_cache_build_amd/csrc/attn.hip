@@ -458,7 +458,7 @@ __global__ __launch_bounds__(kWave) void attn_entmax_solve_kernel(
   constexpr int RG = kWave / RL::LPR;  // row groups in the wave
   __shared__ float cz[kSolveCap];
   __shared__ int cslot[kSolveCap];
-  __shared__ int soff[kSolveSplits + 1];
+  __shared__ __align__(8) int soff[kSolveSplits + 1];   // later reused as the support's row offsets
   const int bh = blockIdx.x, b = bh / c.Hq, h = bh - b * c.Hq, g = h / c.G, hh = h - g * c.G;
   const int unit = b * c.Hkv + g;
   const int lane = threadIdx.x;
@@ -584,7 +584,7 @@ __global__ __launch_bounds__(kWave) void attn_entmax_solve_kernel(
     psum = wave_sum(psum);
     norm = psum > 0.0 ? (float)(1.0 / psum) : 1.0f;
   }
-  // p V over rows with p > 0; row groups take entries round-robin
+  // p V over rows with p > 0
   const int lr = lane % RL::LPR, rg = lane / RL::LPR;
   const int L = seq_len(c, b);
   RowMap rm{sel_idx + (size_t)unit * cap, c.bt + (size_t)b * c.maxP, gran, c.S, c.Hkv, g, D, L, num_pages(c, L)};
@@ -592,27 +592,65 @@ __global__ __launch_bounds__(kWave) void attn_entmax_solve_kernel(
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-  for (int i = rg; i < nn; i += RG) {
-    float z;
-    int slot;
-    if (in_lds) {
-      z = cz[i];
-      slot = cslot[i];
-    } else {
-      const float2 e = entry(i);
-      z = e.x;
-      slot = __float_as_int(e.y);
+  if (in_lds) {
+    // 1. every lane at once: p and the row offset of each survivor, the support compacted in order
+    //    (p over cz, offsets over the split offsets, which are no longer needed); entries are read
+    //    before any write of the round, and a write position never passes the entries read so far
+    long long *voff = reinterpret_cast<long long *>(soff);
+    int m = 0;
+    for (int i0 = 0; i0 < n; i0 += kWave) {
+      const int i = i0 + lane;
+      float pv = 0.0f;
+      long long off = -1;
+      if (i < n) {
+        const float x = cz[i] - tau;
+        if (x > 0.0f) {
+          const int slot = cslot[i], item = slot / rows_per_item;
+          off = rm.row_offset(item, slot - item * rows_per_item);
+          pv = pw(x) * norm;
+        }
+      }
+      const bool keep = off >= 0;
+      const uint64_t bal = __ballot(keep);
+      if (keep) {
+        const int pos = m + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        cz[pos] = pv;
+        voff[pos] = off;
+      }
+      m += __popcll(bal);
     }
-    const float x = z - tau;
-    if (!(x > 0.0f)) continue;
-    const float p = pw(x) * norm;
-    const int item = slot / rows_per_item;
-    const long long off = rm.row_offset(item, slot - item * rows_per_item);
-    if (off < 0) continue;
-    float vx[8];
-    Elem<T>::load8(V + off + lr * 8, vx);
+    __syncthreads();
+    // 2. row groups take the support round-robin, eight rows' V loads in flight per group
+    constexpr int UV = 8;
+    for (int j0 = rg; j0 < m; j0 += UV * RG) {
+      float vx[UV][8];
+      float pj[UV];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = fmaf(p, vx[j], acc[j]);
+      for (int u = 0; u < UV; ++u) {
+        const int j = j0 + u * RG;
+        pj[u] = j < m ? cz[j] : 0.0f;
+        if (j < m) Elem<T>::load8(V + voff[j] + lr * 8, vx[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < UV; ++u)
+        if (j0 + u * RG < m)
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) acc[jj] = fmaf(pj[u], vx[u][jj], acc[jj]);
+    }
+  } else {
+    for (int i = rg; i < nn; i += RG) {   // survivors beyond LDS: walk the flat list
+      const float2 e = entry(i);
+      const float x = e.x - tau;
+      if (!(x > 0.0f)) continue;
+      const float p = pw(x) * norm;
+      const int slot = __float_as_int(e.y), item = slot / rows_per_item;
+      const long long off = rm.row_offset(item, slot - item * rows_per_item);
+      if (off < 0) continue;
+      float vx[8];
+      Elem<T>::load8(V + off + lr * 8, vx);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(p, vx[j], acc[j]);
+    }
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
