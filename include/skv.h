@@ -281,6 +281,24 @@ enum { SKV_OP_SCORE = 0, SKV_OP_SELECT = 1, SKV_OP_ATTN = 2, SKV_OP_CANDIDATES =
  * Host-only; enqueues nothing. Writes *bytes; SKV_ERR_INVALID_ARG on bad arguments. */
 skv_status skv_workspace_bytes(const skv_cache *c, int32_t op, const void *params, int32_t cap, size_t *bytes);
 
+/* Kernel timer, a measurement aid. Between skv_kernel_timer_start and skv_kernel_timer_stop the
+ * library records a pair of HIP events on the caller's stream immediately before and after each
+ * launch of one class of kernel, so that the pair times that kernel alone:
+ *   SKV_TIMER_SCORE: the scoring kernel of skv_score_pages (box, Gaussian, pooled, projected or
+ *     soft-LSH scorer, or the candidate filter of the fused token top-k), after its query
+ *     preparation kernel;
+ *   SKV_TIMER_ATTN: the first kernel of skv_sparse_decode_attn (the softmax split kernel, or the
+ *     entmax logits kernel), before its combine or solve kernel.
+ * Only calls on the device current at skv_kernel_timer_start are timed, at most `capacity` of them
+ * (1 .. 65536); launches on a stream under graph capture are not timed. The library creates the
+ * events at start (2 * capacity hipEventCreate calls) and destroys them at stop.
+ * skv_kernel_timer_stop waits for the recorded events and writes the number of timed launches and
+ * their summed duration in milliseconds. Errors: SKV_ERR_INVALID_ARG for a bad class or capacity,
+ * a start while the timer runs, a stop while it does not, or null outputs; SKV_ERR_HIP. */
+enum { SKV_TIMER_SCORE = 1, SKV_TIMER_ATTN = 2 };
+skv_status skv_kernel_timer_start(int32_t which, int32_t capacity);
+skv_status skv_kernel_timer_stop(int32_t *count, double *total_ms);
+
 /* Static, human-readable name of a status code. Never NULL. */
 const char *skv_status_str(skv_status s);
 

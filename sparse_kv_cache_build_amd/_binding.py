@@ -23,9 +23,11 @@ META_BOX, META_GAUSS, META_PROJ, META_POOL, META_LSH = 1, 2, 4, 8, 16
 SCORE_BOX, SCORE_GAUSS, SCORE_PROJ, SCORE_GAUSS_Q, SCORE_POOL, SCORE_LSH = 0, 1, 2, 3, 4, 5
 SEL_TOPK, SEL_BUDGET, SEL_THRESH_GAUSS, SEL_TOKEN_TOPK, SEL_ALL, SEL_THRESH_BOX = range(6)
 OP_SCORE, OP_SELECT, OP_ATTN, OP_CANDIDATES = 0, 1, 2, 3
+TIMER_SCORE, TIMER_ATTN = 1, 2
 
 EXPORTS = ("skv_build_page_meta", "skv_append_page_meta", "skv_score_pages", "skv_select_pages",
-           "skv_sparse_decode_attn", "skv_workspace_bytes", "skv_status_str")
+           "skv_sparse_decode_attn", "skv_workspace_bytes", "skv_kernel_timer_start", "skv_kernel_timer_stop",
+           "skv_status_str")
 
 
 class SkvError(RuntimeError):
@@ -79,12 +81,40 @@ def lib():
         L.skv_select_pages.argtypes = [P, P, P, P, P, I, P, P, S, P]
         L.skv_sparse_decode_attn.argtypes = [P, P, P, P, I, P, P, P, S, P]
         L.skv_workspace_bytes.argtypes = [P, I, P, I, C.POINTER(C.c_size_t)]
+        L.skv_kernel_timer_start.argtypes = [I, I]
+        L.skv_kernel_timer_stop.argtypes = [C.POINTER(C.c_int32), C.POINTER(C.c_double)]
         L.skv_status_str.argtypes = [I]
         L.skv_status_str.restype = C.c_char_p
         for n in EXPORTS[:-1]:
             getattr(L, n).restype = C.c_int
         _lib = L
     return _lib
+
+
+class KernelTimer:
+    """Times one class of kernel alone with HIP events the library records around each launch
+    (skv_kernel_timer_start/stop): "score" for the scoring kernel of score_pages after its query
+    preparation, "attn" for the first kernel of sparse_decode_attn. Use as a context manager;
+    `count` and `total_ms` are set on exit, after the recorded events have completed."""
+
+    def __init__(self, which: str = "score", capacity: int = 4096):
+        self.which = {"score": TIMER_SCORE, "attn": TIMER_ATTN}[which]
+        self.capacity = capacity
+        self.count, self.total_ms = 0, 0.0
+
+    def __enter__(self):
+        _check(lib().skv_kernel_timer_start(self.which, self.capacity), "skv_kernel_timer_start")
+        return self
+
+    def __exit__(self, *exc):
+        n, ms = C.c_int32(0), C.c_double(0.0)
+        _check(lib().skv_kernel_timer_stop(C.byref(n), C.byref(ms)), "skv_kernel_timer_stop")
+        self.count, self.total_ms = int(n.value), float(ms.value)
+        return False
+
+    @property
+    def avg_ms(self) -> float:
+        return self.total_ms / self.count if self.count else float("nan")
 
 
 def status_str(code: int) -> str:

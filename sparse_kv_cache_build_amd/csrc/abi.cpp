@@ -2,8 +2,11 @@
 // Nothing is enqueued unless every argument checks out. See include/skv.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
+#include <vector>
 
 #include "launch.hpp"
 #include "skv.h"
@@ -11,6 +14,28 @@
 namespace {
 
 using skv::CacheView;
+
+// The kernel timer's state: event pairs created at start, filled in launch order.
+struct KernelTimer {
+  std::mutex mu;
+  std::atomic<int> which{0};   // 0: not running
+  int device = -1;
+  int capacity = 0;
+  int used = 0;                // closed pairs
+  bool open = false;           // a start event recorded for the pair `used`
+  std::vector<hipEvent_t> ev;  // 2 * capacity: (before, after) per launch
+};
+KernelTimer g_timer;
+
+void timer_release() {
+  for (hipEvent_t e : g_timer.ev)
+    if (e) (void)hipEventDestroy(e);
+  g_timer.ev.clear();
+  g_timer.capacity = g_timer.used = 0;
+  g_timer.open = false;
+  g_timer.device = -1;
+  g_timer.which.store(0);
+}
 
 constexpr size_t kAlign = 256;
 
@@ -122,6 +147,47 @@ int budget_cap(int maxP, int pct) {
 }  // namespace
 
 extern "C" {
+
+skv_status skv_kernel_timer_start(int32_t which, int32_t capacity) {
+  if ((which != SKV_TIMER_SCORE && which != SKV_TIMER_ATTN) || capacity < 1 || capacity > 65536)
+    return SKV_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  if (g_timer.which.load() != 0) return SKV_ERR_INVALID_ARG;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SKV_ERR_HIP;
+  g_timer.ev.assign(2 * (size_t)capacity, nullptr);
+  for (hipEvent_t &e : g_timer.ev)
+    if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+      timer_release();
+      return SKV_ERR_HIP;
+    }
+  g_timer.device = dev;
+  g_timer.capacity = capacity;
+  g_timer.used = 0;
+  g_timer.open = false;
+  g_timer.which.store(which);
+  return SKV_OK;
+}
+
+skv_status skv_kernel_timer_stop(int32_t *count, double *total_ms) {
+  if (!count || !total_ms) return SKV_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  if (g_timer.which.load() == 0) return SKV_ERR_INVALID_ARG;
+  double sum = 0.0;
+  skv_status st = SKV_OK;
+  for (int i = 0; i < g_timer.used && st == SKV_OK; ++i) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(g_timer.ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_timer.ev[2 * i], g_timer.ev[2 * i + 1]) != hipSuccess)
+      st = SKV_ERR_HIP;
+    sum += ms;
+  }
+  *count = g_timer.used;
+  *total_ms = sum;
+  timer_release();
+  return st;
+}
 
 const char *skv_status_str(skv_status s) {
   switch (s) {
@@ -398,3 +464,32 @@ skv_status skv_sparse_decode_attn(const skv_cache *c, const void *q, const int32
 }
 
 }  // extern "C"
+
+namespace skv {
+
+void timer_mark(int which, int edge, hipStream_t st) {
+  if (g_timer.which.load(std::memory_order_relaxed) != which) return;
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  if (g_timer.which.load() != which) return;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != g_timer.device) {
+    (void)hipGetLastError();
+    return;
+  }
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+    (void)hipGetLastError();
+    return;
+  }
+  if (edge == 0) {
+    if (g_timer.used >= g_timer.capacity) return;
+    g_timer.open = hipEventRecord(g_timer.ev[2 * g_timer.used], st) == hipSuccess;
+  } else {
+    if (!g_timer.open) return;
+    if (hipEventRecord(g_timer.ev[2 * g_timer.used + 1], st) == hipSuccess) ++g_timer.used;
+    g_timer.open = false;
+  }
+  (void)hipGetLastError();
+}
+
+}  // namespace skv

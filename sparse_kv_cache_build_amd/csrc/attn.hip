@@ -684,9 +684,10 @@ static hipError_t attn_typed(const AttnArgs &a, hipStream_t st) {
     const float scale_log2 = a.sm_scale * 1.4426950408889634f;
     const int rps_s = a.spi * (a.gran ? 1 : c.S);
     const size_t lds_s = sizeof(long long) * (size_t)rps_s;
+    timer_mark(kTimerAttn, 0, st);
     SKV_ATTN_DISPATCH_G(c.G, attn_softmax_kernel<T, D, GG><<<grid, kAttnThreads, lds_s, st>>>(
                                  c, q, a.sel_idx, a.sel_count, a.cap, a.gran, a.spi, a.nsplit, scale_log2, a.part, a.out))
-    hipError_t e = hipGetLastError();
+    hipError_t e = timed_launch_status(kTimerAttn, st);
     if (e != hipSuccess || a.nsplit == 1) return e;
     attn_combine_kernel<D><<<c.B * c.Hq, D, 0, st>>>(c, a.sel_count, a.cap, a.spi, a.nsplit, a.part, a.out);
     return hipGetLastError();
@@ -694,6 +695,7 @@ static hipError_t attn_typed(const AttnArgs &a, hipStream_t st) {
   const int rps = a.spi * (a.gran ? 1 : c.S);
   const size_t lds = sizeof(float) * (size_t)((c.G * rps + 1) & ~1) + sizeof(long long) * (size_t)rps;
   const float zscale = a.sm_scale * (a.alpha - 1.0f);
+  timer_mark(kTimerAttn, 0, st);
   if constexpr (std::is_same<T, uint16_t>::value) {   // bf16: logits on the matrix cores
     SKV_ATTN_DISPATCH_G(c.G, attn_entmax_logits_mfma_kernel<D, GG><<<grid, kAttnThreads, lds, st>>>(
                                  c, q, a.sel_idx, a.sel_count, a.cap, a.gran, a.spi, a.nsplit, zscale, a.cand,
@@ -703,7 +705,7 @@ static hipError_t attn_typed(const AttnArgs &a, hipStream_t st) {
                                  c, q, a.sel_idx, a.sel_count, a.cap, a.gran, a.spi, a.nsplit, zscale, a.cand,
                                  a.cand_cnt, a.cand_max))
   }
-  hipError_t e = hipGetLastError();
+  hipError_t e = timed_launch_status(kTimerAttn, st);
   if (e != hipSuccess) return e;
   const int kind = a.alpha == 1.5f ? 1 : (a.alpha == 2.0f ? 2 : 3);
   const dim3 g2(c.B * c.Hq);

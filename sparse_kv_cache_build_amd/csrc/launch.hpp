@@ -23,6 +23,19 @@ struct AttnArgs {
   float *cand_max;   // [U, G, nsplit]
 };
 
+// Kernel timer (a measurement aid, run by skv_kernel_timer_start/stop): records a HIP event on `st`
+// before (edge 0) or after (edge 1) a launch of kernel class `which` while the timer runs for that
+// class; otherwise returns at once. A failed record is cleared so the launch's own status stands.
+enum { kTimerScore = 1, kTimerAttn = 2 };
+void timer_mark(int which, int edge, hipStream_t st);
+
+// The launch status of the kernel just launched, with the timer's closing mark after it.
+inline hipError_t timed_launch_status(int which, hipStream_t st) {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) timer_mark(which, 1, st);
+  return e;
+}
+
 hipError_t launch_build_meta(const CacheView &c, int dtype, int tail, void *box, float *gauss, int r,
                              const float *proj, uint16_t *kproj, int pb, float *pool, hipStream_t st);
 hipError_t launch_build_lsh(const CacheView &c, int dtype, int tail, int L, int P, const float *planes,

@@ -537,8 +537,9 @@ static hipError_t qprep_pair(const void *q, int n, int gauss, double *ws, hipStr
 template <typename T, int D>
 static hipError_t box_d(const CacheView &c, const void *box, const double *qpm, float *key, hipStream_t st) {
   const dim3 grid((c.maxP + 255) / 256, c.B * c.Hkv);
+  timer_mark(kTimerScore, 0, st);
   SKV_DISPATCH_G(c.G, score_box_kernel<T, D, GG><<<grid, 256, 0, st>>>(c, static_cast<const T *>(box), qpm, key))
-  return hipGetLastError();
+  return timed_launch_status(kTimerScore, st);
 }
 
 hipError_t launch_score_box(const CacheView &c, int dtype, const void *q, const void *box, float *key, double *ws,
@@ -554,8 +555,9 @@ template <int D>
 static hipError_t gauss_d(const CacheView &c, const float *gauss, const double *qpm, double scale, int quantile, float *m, float *s,
                           float *shat, hipStream_t st) {
   const dim3 grid((c.maxP + 255) / 256, c.B * c.Hkv);
+  timer_mark(kTimerScore, 0, st);
   SKV_DISPATCH_G(c.G, score_gauss_kernel<D, GG><<<grid, 256, 0, st>>>(c, gauss, qpm, scale, quantile, m, s, shat))
-  return hipGetLastError();
+  return timed_launch_status(kTimerScore, st);
 }
 
 hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, const float *gauss, double scale,
@@ -574,8 +576,9 @@ static hipError_t pool_d(const CacheView &c, int pb, const float *pool, const do
   while ((1 << lw) < c.S / pb && lw < 6) ++lw;
   const int pages_per_block = 4 * (64 >> lw);
   const dim3 grid((c.maxP + pages_per_block - 1) / pages_per_block, c.B * c.Hkv);
+  timer_mark(kTimerScore, 0, st);
   SKV_DISPATCH_G(c.G, score_pool_kernel<D, GG><<<grid, 256, 0, st>>>(c, pb, lw, pool, qpm, key))
-  return hipGetLastError();
+  return timed_launch_status(kTimerScore, st);
 }
 
 hipError_t launch_score_pool(const CacheView &c, int dtype, const void *q, int pb, const float *pool, float *key,
@@ -589,14 +592,16 @@ hipError_t launch_score_pool(const CacheView &c, int dtype, const void *q, int p
 template <int R>
 static hipError_t proj_r(const CacheView &c, const uint16_t *kproj, const double *qt, float *key, hipStream_t st) {
   const dim3 grid((c.maxP * c.S + 256 * kProjTPT - 1) / (256 * kProjTPT), c.B * c.Hkv);
+  timer_mark(kTimerScore, 0, st);
   SKV_DISPATCH_G(c.G, score_proj_kernel<R, GG><<<grid, 256, 0, st>>>(c, kproj, qt, key))
-  return hipGetLastError();
+  return timed_launch_status(kTimerScore, st);
 }
 
 template <int R>
 static hipError_t proj_cand_r(const CacheView &c, const uint16_t *kproj, char *cand, const CandLayout &lay,
                               hipStream_t st) {
   const dim3 grid((lay.nb + 3) / 4, c.B * c.Hkv);
+  timer_mark(kTimerScore, 0, st);
   SKV_DISPATCH_G(c.G, score_proj_cand_kernel<R, GG><<<grid, 256, 0, st>>>(
                           c, kproj, reinterpret_cast<const double *>(cand + lay.qt),
                           reinterpret_cast<const uint32_t *>(cand + lay.qb),
@@ -604,7 +609,7 @@ static hipError_t proj_cand_r(const CacheView &c, const uint16_t *kproj, char *c
                           reinterpret_cast<const uint32_t *>(cand + lay.bound),
                           reinterpret_cast<int32_t *>(cand + lay.count), reinterpret_cast<float2 *>(cand + lay.seg),
                           lay.nb))
-  return hipGetLastError();
+  return timed_launch_status(kTimerScore, st);
 }
 
 hipError_t launch_score_proj_cand(const CacheView &c, int r, const uint16_t *kproj, char *cand, hipStream_t st) {
@@ -653,8 +658,9 @@ static hipError_t lsh_d(const CacheView &c, int dtype, const void *q, int L, int
   if (e != hipSuccess) return e;
   const dim3 grid((c.maxP * c.S + kLshTok - 1) / kLshTok, c.B * c.Hkv);
   const size_t lds = sizeof(uint32_t) * ((size_t)L << P) * c.G;
+  timer_mark(kTimerScore, 0, st);
   SKV_DISPATCH_G(c.G, score_lsh_kernel<GG><<<grid, 256, lds, st>>>(c, L, P, bucket, vnorm, tab, key))
-  return hipGetLastError();
+  return timed_launch_status(kTimerScore, st);
 }
 
 hipError_t launch_score_lsh(const CacheView &c, int dtype, const void *q, int L, int P, const float *planes,

@@ -206,3 +206,14 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         B.lib()
+
+
+def test_kernel_timer_argument_checks(L):
+    """Refusals that need no device: bad class or capacity, a stop while the timer is not running,
+    null outputs."""
+    n, ms = C.c_int32(-1), C.c_double(-1.0)
+    for which, cap in [(0, 16), (3, 16), (B.TIMER_SCORE, 0), (B.TIMER_ATTN, -1), (B.TIMER_SCORE, 65537)]:
+        assert L.skv_kernel_timer_start(which, cap) == B.SKV_ERR_INVALID_ARG, (which, cap)
+    assert L.skv_kernel_timer_stop(C.byref(n), C.byref(ms)) == B.SKV_ERR_INVALID_ARG
+    assert L.skv_kernel_timer_stop(None, None) == B.SKV_ERR_INVALID_ARG
+    assert n.value == -1 and ms.value == -1.0
