@@ -103,9 +103,12 @@ def test_full_cache_comparator(dev, name, alpha):
 
 
 @pytest.mark.parametrize("over", [dict(B=2, L=20000, k=512), dict(B=2, L=5000, k=512),
-                                  dict(B=3, lens=[0, 9000, 40000], k=2048), dict(B=2, lens=[1500, 30000], k=1000)])
+                                  dict(B=3, lens=[0, 9000, 40000], k=2048), dict(B=2, lens=[1500, 30000], k=1000),
+                                  dict(B=2, lens=[3000, 7001], k=300, S=8), dict(B=2, lens=[2500, 6000], k=400, S=48),
+                                  dict(B=2, lens=[5000, 2100], k=256, S=64)])
 def test_fused_token_topk_matches_oracle(dev, over):
-    """Projected scoring kept as the candidate set of the top-k (no dense keys) selects the same tokens."""
+    """Projected scoring kept as the candidate set of the top-k (no dense keys) selects the same tokens,
+    also for pages of 8 and 48 tokens (block-table entries loaded per row) and 64 (one per lane)."""
     H.log(f"[parity fused token top-k] {over}")
     w = W.make("token128k", device=dev, **over)
     st = H.gpu_step(w, fused=True)
