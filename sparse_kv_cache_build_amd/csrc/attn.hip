@@ -41,14 +41,17 @@ struct RowMap {
   const int32_t *bt;   // block table row of the sequence
   int gran, S, Hkv, g, D, L, P;
   __device__ __forceinline__ long long row_offset(int item, int t_in_page) const {
+    return offset_of(sel[item], t_in_page);
+  }
+  // the same from the selection entry e (a token, or a page) already read
+  __device__ __forceinline__ long long offset_of(int e, int t_in_page) const {
     int page, t;
     if (gran) {
-      const int tok = sel[item];
-      if (tok < 0 || tok >= L) return -1;
-      page = tok / S;
-      t = tok - page * S;
+      if (e < 0 || e >= L) return -1;
+      page = e / S;
+      t = e - page * S;
     } else {
-      page = sel[item];
+      page = e;
       if (page < 0 || page >= P) return -1;
       t = t_in_page;
       if (t >= min(S, L - page * S)) return -1;
@@ -439,15 +442,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_mfma_kernel(
 // One wave per query head. ALPHA_KIND: 1 -> alpha = 1.5, 2 -> alpha = 2, 3 -> any alpha in (1, 2).
 //  1. max_all = max of the split maxima; only z' > max_all - 1 can carry weight.
 //  2. The per-split pair lists are read as one flat list (split-major, row order) through prefix
-//     offsets in LDS, and the survivors are compacted into LDS in that order (ballots).
+//     offsets in LDS, and the survivors are compacted into LDS in that order (ballots). Splits
+//     whose maximum is at most max_all - 1 are skipped.
 //  3. Bisection on tau over [max_all - 1, max_all - n^(1-alpha)], then the closed form on the
 //     support {z' > tau}, iterated until the support size repeats (alpha = 2: tau = (sum z' - 1) / k;
 //     alpha = 1.5: tau = mean - sqrt((1 - k var) / k), the smaller root of sum (z' - tau)^2 = 1).
+//     For alpha = 1.5 and 2 the bisection stops once no survivor lies in (lo, hi]: the support is
+//     then settled. Up to 256 survivors are held in registers; sums over lanes use DPP.
 //  4. p = (z' - tau)_+^(1/(alpha-1)) (renormalized for other alpha), out = sum p v over rows with
 //     p > 0, read in place through the selection and block table.
 // When the survivors do not fit in LDS, steps 3-4 read the flat list from global memory instead.
 constexpr int kSolveCap = 1024;     // survivors staged in LDS
 constexpr int kSolveSplits = 2048;  // split offsets staged in LDS (the planner keeps nsplit below)
+constexpr int kStageU = 8;          // pair-list entries per lane and staging round
 
 template <typename T, int D, int ALPHA_KIND>
 __global__ __launch_bounds__(kWave) void attn_entmax_solve_kernel(
@@ -469,19 +476,31 @@ __global__ __launch_bounds__(kWave) void attn_entmax_solve_kernel(
   const size_t lid0 = ((size_t)unit * c.G + hh) * nsplit;
   float *o = out + (size_t)bh * D;
 
-  float mx = -INFINITY;
-  for (int s = lane; s < ns; s += kWave) mx = fmaxf(mx, cand_max[lid0 + s]);
-  mx = wave_max(mx);
+  // the maxima and counts of the first 64 splits are read together (most units have no more)
+  float mx = -INFINITY, mx0 = -INFINITY;
+  int cnt0 = 0;
+  if (lane < ns) {
+    mx0 = cand_max[lid0 + lane];
+    cnt0 = cand_cnt[lid0 + lane];
+  }
+  mx = mx0;
+  for (int s = lane + kWave; s < ns; s += kWave) mx = fmaxf(mx, cand_max[lid0 + s]);
+  mx = wave_max_dpp(mx);
   if (mx == -INFINITY) {  // nothing selected
     for (int j = lane; j < D; j += kWave) o[j] = 0.0f;
     return;
   }
   const float lo_bound = mx - 1.0f;
-  // prefix offsets of the split lists (exclusive), 64 splits per step
+  // prefix offsets of the split lists (exclusive), 64 splits per step; a split whose maximum is
+  // at most max_all - 1 holds no survivor and is left out
   int run = 0;
   for (int s0 = 0; s0 < ns; s0 += kWave) {
     const int s = s0 + lane;
-    const int cnt = s < ns ? cand_cnt[lid0 + s] : 0;
+    int cnt = 0;
+    if (s0 == 0)
+      cnt = mx0 > lo_bound ? cnt0 : 0;
+    else if (s < ns && cand_max[lid0 + s] > lo_bound)
+      cnt = cand_cnt[lid0 + s];
     const int incl = wave_incl_scan(cnt);
     if (s < ns) soff[s] = run + incl - cnt;
     run += __shfl(incl, kWave - 1, kWave);
@@ -498,27 +517,48 @@ __global__ __launch_bounds__(kWave) void attn_entmax_solve_kernel(
     }
     return cand[(lid0 + lo) * rps + (f - soff[lo])];
   };
-  // survivors into LDS, in flat order; four loads in flight per lane
+  // survivors into LDS, in flat order; U entries per lane and round (1 when the list fits one
+  // round, else kStageU), their splits found by binary searches run side by side (a fixed number
+  // of halving steps), then all their loads in flight
+  int top = 1;
+  while (top < ns) top <<= 1;
   int n = 0;
-  for (int f0 = 0; f0 < nraw; f0 += 4 * kWave) {
-    float2 e[4];
+  auto stage = [&](auto uu) {
+    constexpr int U = decltype(uu)::value;
+    for (int f0 = 0; f0 < nraw; f0 += U * kWave) {
+      int sp[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int f = f0 + u * kWave + lane;
-      e[u] = f < nraw ? entry(f) : make_float2(-INFINITY, 0.0f);
-    }
+      for (int u = 0; u < U; ++u) sp[u] = 0;
+      for (int step = top >> 1; step > 0; step >>= 1) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bool keep = e[u].x > lo_bound;
-      const uint64_t bal = __ballot(keep);
-      const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-      if (keep && pos < kSolveCap) {
-        cz[pos] = e[u].x;
-        cslot[pos] = __float_as_int(e[u].y);
+        for (int u = 0; u < U; ++u) {   // soff[ns] = nraw exceeds every entry index read below
+          const int f = f0 + u * kWave + lane, m = sp[u] + step;
+          sp[u] = soff[min(m, ns)] <= f ? m : sp[u];
+        }
       }
-      n += __popcll(bal);
+      float2 e[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int f = f0 + u * kWave + lane;
+        e[u] = f < nraw ? cand[(lid0 + sp[u]) * rps + (f - soff[sp[u]])] : make_float2(-INFINITY, 0.0f);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool keep = e[u].x > lo_bound;
+        const uint64_t bal = __ballot(keep);
+        const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        if (keep && pos < kSolveCap) {
+          cz[pos] = e[u].x;
+          cslot[pos] = __float_as_int(e[u].y);
+        }
+        n += __popcll(bal);
+      }
     }
-  }
+  };
+  if (nraw <= kWave)
+    stage(std::integral_constant<int, 1>{});
+  else
+    stage(std::integral_constant<int, kStageU>{});
   __syncthreads();
   const bool in_lds = n <= kSolveCap;
   const int nn = in_lds ? n : nraw;   // in global mode the unfiltered list is walked (z' <= max - 1 weighs 0)
@@ -530,37 +570,124 @@ __global__ __launch_bounds__(kWave) void attn_entmax_solve_kernel(
     if (ALPHA_KIND == 2) return x;
     return powf(x, inv);
   };
+  // up to ZR * 64 survivors (the usual case) are also held in registers, lane-strided like cz;
+  // empty slots hold -inf and add nothing
+  constexpr int ZR = 4;
+  const bool in_regs = n <= ZR * kWave;
+  float zr[ZR];
+#pragma unroll
+  for (int j = 0; j < ZR; ++j) {
+    const int i = lane + j * kWave;
+    zr[j] = (in_regs && i < n) ? cz[i] : -INFINITY;
+  }
+  const int L = seq_len(c, b);
+  RowMap rm{sel_idx + (size_t)unit * cap, c.bt + (size_t)b * c.maxP, gran, c.S, c.Hkv, g, D, L, num_pages(c, L)};
+  // the selection entries of the register-held survivors are read now, their block-table entries
+  // after the bisection, so that both loads wait behind the threshold arithmetic, not after it
+  int selv[ZR], tin[ZR];
+#pragma unroll
+  for (int j = 0; j < ZR; ++j) {
+    const int i = lane + j * kWave;
+    selv[j] = -1;
+    tin[j] = 0;
+    if (in_regs && i < n) {
+      const int slot = cslot[i], item = slot / rows_per_item;
+      tin[j] = slot - item * rows_per_item;
+      selv[j] = rm.sel[item];
+    }
+  }
+  // 3. bisection; for alpha = 1.5 and 2 it stops as soon as no survivor lies in (lo, hi]: the
+  //    support {z' > tau} is then settled and the closed form below gives tau from it
   float lo = lo_bound, hi = mx - powf((float)n, -am1);
+  int klo = n, khi = -1;   // survivors above lo and above hi (-1: not counted)
+  if (ALPHA_KIND != 3 && in_regs) {   // every survivor above hi: the support is all of them
+    int c0 = 0;
+#pragma unroll
+    for (int j = 0; j < ZR; ++j) c0 += zr[j] > hi ? 1 : 0;
+    khi = wave_sum_dpp(c0);
+  }
   for (int it = 0; it < 40; ++it) {
+    if (ALPHA_KIND != 3 && klo == khi) break;
+    if (ALPHA_KIND != 3 && in_regs && khi >= 0 && klo - khi == 1) {
+      // one survivor z_j left in (lo, hi]: F at z_j says which side of it tau lies on, and the
+      // interval then holds no survivor inside: lo = z_j (tau >= z_j) or hi = z_j (tau < z_j)
+      float zj = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < ZR; ++j) zj = (zr[j] > lo && zr[j] <= hi) ? fmaxf(zj, zr[j]) : zj;
+      zj = wave_max_dpp(zj);
+      double sj = 0.0;
+#pragma unroll
+      for (int j = 0; j < ZR; ++j) {
+        const float x = zr[j] - zj;
+        if (x > 0.0f) sj += (double)pw(x);
+      }
+      if (wave_sum_dpp(sj) >= 1.0) {
+        lo = zj;
+        klo = khi;
+      } else {
+        hi = zj;
+      }
+      break;
+    }
     const float mid = 0.5f * (lo + hi);
     if (mid <= lo || mid >= hi) break;
     double sum = 0.0;
-    for (int i = lane; i < nn; i += kWave) {
-      const float x = z_at(i) - mid;
-      if (x > 0.0f) sum += (double)pw(x);
+    int cnt = 0;
+    if (in_regs) {
+#pragma unroll
+      for (int j = 0; j < ZR; ++j) {
+        const float x = zr[j] - mid;
+        if (x > 0.0f) {
+          sum += (double)pw(x);
+          ++cnt;
+        }
+      }
+    } else {
+      for (int i = lane; i < nn; i += kWave) {
+        const float x = z_at(i) - mid;
+        if (x > 0.0f) {
+          sum += (double)pw(x);
+          ++cnt;
+        }
+      }
     }
-    if (wave_sum(sum) >= 1.0)
+    sum = wave_sum_dpp(sum);
+    cnt = wave_sum_dpp(cnt);
+    if (sum >= 1.0) {
       lo = mid;
-    else
+      klo = cnt;
+    } else {
       hi = mid;
+      khi = cnt;
+    }
   }
+  long long offr[ZR];
+#pragma unroll
+  for (int j = 0; j < ZR; ++j) offr[j] = (in_regs && lane + j * kWave < n) ? rm.offset_of(selv[j], tin[j]) : -1;
   float tau = lo;
   if (ALPHA_KIND != 3) {
     int prev = -1;
     for (int it = 0; it < 16; ++it) {
       double k = 0.0, s1 = 0.0, s2 = 0.0;
-      for (int i = lane; i < nn; i += kWave) {
-        const float z = z_at(i);
-        if (z > tau) {
-          const double y = (double)z - (double)mx;
-          k += 1.0;
-          s1 += y;
-          s2 += y * y;
+      auto add = [&](float z) {
+        const double y = (double)z - (double)mx;
+        k += 1.0;
+        s1 += y;
+        s2 += y * y;
+      };
+      if (in_regs) {
+#pragma unroll
+        for (int j = 0; j < ZR; ++j)
+          if (zr[j] > tau) add(zr[j]);
+      } else {
+        for (int i = lane; i < nn; i += kWave) {
+          const float z = z_at(i);
+          if (z > tau) add(z);
         }
       }
-      k = wave_sum(k);
-      s1 = wave_sum(s1);
-      s2 = wave_sum(s2);
+      k = wave_sum_dpp(k);
+      s1 = wave_sum_dpp(s1);
+      s2 = wave_sum_dpp(s2);
       if (k <= 0.0 || (int)k == prev) break;
       prev = (int)k;
       double ty;
@@ -577,17 +704,23 @@ __global__ __launch_bounds__(kWave) void attn_entmax_solve_kernel(
   float norm = 1.0f;
   if (ALPHA_KIND == 3) {
     double psum = 0.0;
-    for (int i = lane; i < nn; i += kWave) {
-      const float x = z_at(i) - tau;
-      if (x > 0.0f) psum += pw(x);
+    if (in_regs) {
+#pragma unroll
+      for (int j = 0; j < ZR; ++j) {
+        const float x = zr[j] - tau;
+        if (x > 0.0f) psum += pw(x);
+      }
+    } else {
+      for (int i = lane; i < nn; i += kWave) {
+        const float x = z_at(i) - tau;
+        if (x > 0.0f) psum += pw(x);
+      }
     }
-    psum = wave_sum(psum);
+    psum = wave_sum_dpp(psum);
     norm = psum > 0.0 ? (float)(1.0 / psum) : 1.0f;
   }
   // p V over rows with p > 0
   const int lr = lane % RL::LPR, rg = lane / RL::LPR;
-  const int L = seq_len(c, b);
-  RowMap rm{sel_idx + (size_t)unit * cap, c.bt + (size_t)b * c.maxP, gran, c.S, c.Hkv, g, D, L, num_pages(c, L)};
   const T *V = static_cast<const T *>(c.v);
   float acc[8];
 #pragma unroll
@@ -598,7 +731,21 @@ __global__ __launch_bounds__(kWave) void attn_entmax_solve_kernel(
     //    before any write of the round, and a write position never passes the entries read so far
     long long *voff = reinterpret_cast<long long *>(soff);
     int m = 0;
-    for (int i0 = 0; i0 < n; i0 += kWave) {
+    if (in_regs) {   // the same from the registers (offsets already resolved)
+#pragma unroll
+      for (int j = 0; j < ZR; ++j) {
+        const float x = zr[j] - tau;
+        const bool keep = x > 0.0f && offr[j] >= 0;
+        const uint64_t bal = __ballot(keep);
+        if (keep) {
+          const int pos = m + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+          cz[pos] = pw(x) * norm;
+          voff[pos] = offr[j];
+        }
+        m += __popcll(bal);
+      }
+    }
+    for (int i0 = 0; i0 < (in_regs ? 0 : n); i0 += kWave) {
       const int i = i0 + lane;
       float pv = 0.0f;
       long long off = -1;

@@ -305,6 +305,32 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
 }
 
+// Wave sums with DPP moves in the pattern of wave_incl_scan (lane 63 ends with the total, read
+// back as a wave-uniform value): a fixed order, so the result is reproducible, and no LDS round
+// trips. A double moves as its two 32-bit halves; lanes without a source add +0.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROWS, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROWS, 0xf, false);
+  return __longlong_as_double((long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+__device__ __forceinline__ double wave_sum_dpp(double v) {
+  v += dpp_f64<0x111, 0xf>(v);
+  v += dpp_f64<0x112, 0xf>(v);
+  v += dpp_f64<0x114, 0xf>(v);
+  v += dpp_f64<0x118, 0xf>(v);
+  v += dpp_f64<0x142, 0xa>(v);
+  v += dpp_f64<0x143, 0xc>(v);
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, kWave - 1);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), kWave - 1);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ __forceinline__ int wave_sum_dpp(int v) {
+  return __builtin_amdgcn_readlane((int)wave_incl_scan((uint32_t)v), kWave - 1);
+}
+
 // Block-wide exclusive prefix sum for blocks of NT threads (NT a multiple of 64, <= 1024).
 // `scratch` holds NT/64 + 1 ints of shared memory. Returns the exclusive prefix; *total gets the
 // block sum. Contains __syncthreads: every thread of the block must call it.
