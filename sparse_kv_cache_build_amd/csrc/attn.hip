@@ -2,8 +2,11 @@
 // its s1 and s3). Token-granular selections read rows in place through block_table, with no
 // gathered copy ("Joint Subspace Sparse Attention" abstract).
 //
-// Work decomposition (split-K over the selection): block (split, unit) takes `spi` consecutive
-// selected items (pages or tokens) of unit (b, g) and all G query heads of g. Inside a block a
+// Work decomposition (split-K over the selection): the unit's selected items (pages or tokens)
+// are spread evenly over its nsplit splits (ceil(count / nsplit) each, never more than the
+// planned `spi`, so that a selection shorter than the capacity still keeps every split busy);
+// block (split, unit) takes one such run of consecutive items of unit (b, g) and all G query
+// heads of g. Inside a block a
 // row (one token's d coordinates) is read by a group of D/8 lanes, 8 coordinates per lane
 // (16-byte loads for bf16), so a wave covers 4 (d = 128) or 8 (d = 64) rows per step and the
 // block's 4 waves 16 or 32 rows. q . k is a per-lane partial dot product summed over the lane
@@ -24,6 +27,11 @@
 #include "launch.hpp"
 
 namespace skv {
+
+// Items per split for a unit with `count` selected items (at most spi when count <= cap).
+__device__ __forceinline__ int items_per_split(int count, int nsplit) {
+  return max(1, (count + nsplit - 1) / nsplit);
+}
 
 constexpr int kAttnThreads = 256;
 
@@ -75,9 +83,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_softmax_kernel(
   extern __shared__ long long roff[];   // element offset of each row of the partition, -1 if none
   const int split = blockIdx.x, unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
   const int count = min(max(sel_count[unit], 0), cap);
-  const int it0 = split * spi;
+  const int ipb = items_per_split(count, nsplit);
+  const int it0 = split * ipb;
   if (it0 >= count && !(split == 0 && nsplit == 1)) return;  // empty split (count is known to the combine)
-  const int it1 = min(count, it0 + spi);
+  const int it1 = min(count, it0 + ipb);
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int lr = lane % RL::LPR, rg = wave * RL::RPW + lane / RL::LPR;
   const int L = seq_len(c, b);
@@ -203,7 +212,8 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(CacheView c, const int3
   const int bh = blockIdx.x, b = bh / c.Hq, h = bh - b * c.Hq, g = h / c.G, hh = h - g * c.G;
   const int unit = b * c.Hkv + g;
   const int count = min(max(sel_count[unit], 0), cap);
-  const int ns = min(nsplit, (count + spi - 1) / spi);
+  const int ipb = items_per_split(count, nsplit);
+  const int ns = min(nsplit, (count + ipb - 1) / ipb);
   const int j = threadIdx.x;
   const size_t stride = (size_t)c.G * (D + 2);
   const float *p0 = part + ((size_t)unit * nsplit * c.G + hh) * (D + 2);
@@ -317,7 +327,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
   const int count = min(max(sel_count[unit], 0), cap);
   const int rows_per_item = gran ? 1 : c.S;
   const int rps = spi * rows_per_item;
-  const int it0 = split * spi, it1 = min(count, it0 + spi);
+  const int ipb = items_per_split(count, nsplit);
+  const int it0 = split * ipb, it1 = min(count, it0 + ipb);
   const int NR = max(0, it1 - it0) * rows_per_item;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int lr = lane % RL::LPR, rg = wave * RL::RPW + lane / RL::LPR;
@@ -383,7 +394,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_mfma_kernel(
   const int count = min(max(sel_count[unit], 0), cap);
   const int rows_per_item = gran ? 1 : c.S;
   const int rps = spi * rows_per_item;
-  const int it0 = split * spi, it1 = min(count, it0 + spi);
+  const int ipb = items_per_split(count, nsplit);
+  const int it0 = split * ipb, it1 = min(count, it0 + ipb);
   const int NR = max(0, it1 - it0) * rows_per_item;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int L = seq_len(c, b);
@@ -472,7 +484,8 @@ __global__ __launch_bounds__(kWave) void attn_entmax_solve_kernel(
   const int count = min(max(sel_count[unit], 0), cap);
   const int rows_per_item = gran ? 1 : c.S;
   const int rps = spi * rows_per_item;
-  const int ns = min(nsplit, (count + spi - 1) / spi);
+  const int ipb = items_per_split(count, nsplit);
+  const int ns = min(nsplit, (count + ipb - 1) / ipb);
   const size_t lid0 = ((size_t)unit * c.G + hh) * nsplit;
   float *o = out + (size_t)bh * D;
 
