@@ -329,6 +329,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
   const int rps = spi * rows_per_item;
   const int ipb = items_per_split(count, nsplit);
   const int it0 = split * ipb, it1 = min(count, it0 + ipb);
+  if (it0 >= count) return;   // past the splits in use: the solve reads none of its lists
   const int NR = max(0, it1 - it0) * rows_per_item;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int lr = lane % RL::LPR, rg = wave * RL::RPW + lane / RL::LPR;
@@ -396,6 +397,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_mfma_kernel(
   const int rps = spi * rows_per_item;
   const int ipb = items_per_split(count, nsplit);
   const int it0 = split * ipb, it1 = min(count, it0 + ipb);
+  if (it0 >= count) return;   // past the splits in use: the solve reads none of its lists
   const int NR = max(0, it1 - it0) * rows_per_item;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int L = seq_len(c, b);
