@@ -383,8 +383,8 @@ __device__ __forceinline__ double block_sum(double v, double *scratch) {
 template <int NT>
 __device__ __forceinline__ void block_sum2(double &a, double &b, double2 *scratch) {
   constexpr int NW = NT / kWave;
-  a = wave_sum(a);
-  b = wave_sum(b);
+  a = wave_sum_dpp(a);
+  b = wave_sum_dpp(b);
   if ((threadIdx.x & (kWave - 1)) == 0) scratch[threadIdx.x / kWave] = make_double2(a, b);
   __syncthreads();
   a = 0.0;
