@@ -201,16 +201,31 @@ __global__ __launch_bounds__(256) void lsh_prep_kernel(CacheView c, const T *__r
   __syncthreads();
   for (int m = threadIdx.x; m < L * P; m += blockDim.x) {
     const float4 *w4 = reinterpret_cast<const float4 *>(planes + (size_t)m * D);
-    float4 wr[D / 4];   // the whole hyperplane in flight before the (sequential) sum
+    // the hyperplane streams in chunks of 32 coordinates, the next chunk loading while one is
+    // summed; each chunk's query terms are read from LDS into registers before its sum, so the
+    // sequential FMA chain never waits on LDS
+    constexpr int CH = 8, NCH = D / 4 / CH;
+    float4 wa[CH], wb[CH];
 #pragma unroll
-    for (int j = 0; j < D / 4; ++j) wr[j] = w4[j];
+    for (int j = 0; j < CH; ++j) wa[j] = w4[j];
     double dot = 0.0;
 #pragma unroll
-    for (int j = 0; j < D / 4; ++j) {
-      dot = fma((double)wr[j].x, qs[4 * j], dot);
-      dot = fma((double)wr[j].y, qs[4 * j + 1], dot);
-      dot = fma((double)wr[j].z, qs[4 * j + 2], dot);
-      dot = fma((double)wr[j].w, qs[4 * j + 3], dot);
+    for (int k = 0; k < NCH; ++k) {
+      if (k + 1 < NCH)
+#pragma unroll
+        for (int j = 0; j < CH; ++j) wb[j] = w4[(k + 1) * CH + j];
+      double qc[4 * CH];
+#pragma unroll
+      for (int j = 0; j < 4 * CH; ++j) qc[j] = qs[4 * CH * k + j];
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        dot = fma((double)wa[j].x, qc[4 * j], dot);
+        dot = fma((double)wa[j].y, qc[4 * j + 1], dot);
+        dot = fma((double)wa[j].z, qc[4 * j + 2], dot);
+        dot = fma((double)wa[j].w, qc[4 * j + 3], dot);
+      }
+#pragma unroll
+      for (int j = 0; j < CH; ++j) wa[j] = wb[j];
     }
     const double z = nq > 0.0 ? dot / nq : 0.0;
     sg[2 * m] = 1.0 / (1.0 + exp(-((2.0 * z) / tau)));
@@ -222,7 +237,12 @@ __global__ __launch_bounds__(256) void lsh_prep_kernel(CacheView c, const T *__r
   for (int e = threadIdx.x; e < L * nb; e += blockDim.x) {
     const int l = e >> P, beta = e & (nb - 1);
     double pr = 1.0;
-    for (int i = 0; i < P; ++i) pr *= sg[2 * (l * P + i) + (((beta >> i) & 1) ? 0 : 1)];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {   // P <= 8; the reads go out together (index clamped in range)
+      const int m = min(l * P + i, L * P - 1);
+      const double v = sg[2 * m + (((beta >> i) & 1) ? 0 : 1)];
+      pr = i < P ? pr * v : pr;
+    }
     out[(size_t)e * c.G + hh] = (uint32_t)rint(ldexp(pr, 24));
   }
 }
