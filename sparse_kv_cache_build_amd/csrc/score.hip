@@ -136,9 +136,10 @@ __global__ __launch_bounds__(256) void score_pool_kernel(CacheView c, int pb, in
   }
   double best = -INFINITY, acc[G];
   const int total = T * NC;
+  __syncthreads();   // qs is staged; from here on each wave uses only its own rows in LDS
   for (int s = 0; s < total; ++s) {
     const int t = s / NC, ch = s - t * NC;
-    __syncthreads();   // the previous chunk has been read (and qs is staged)
+    __builtin_amdgcn_wave_barrier();   // the wave has read the previous chunk
 #pragma unroll
     for (int k = 0; k < 8; ++k) *reinterpret_cast<float4 *>(xw + (lrow + 8 * k) * LDR + lcol) = r[k];
     if (s + 1 < total) {
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(256) void score_pool_kernel(CacheView c, int pb, in
                            : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();   // the chunk is in LDS for every lane of the wave
     if (ch == 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h) acc[h] = 0.0;
@@ -357,8 +358,9 @@ __global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const flo
   double sm[G], sv[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) sm[h] = sv[h] = 0.0;
+  __syncthreads();   // qs is staged; from here on each wave uses only its own rows in LDS
   for (int ch = 0; ch < NC; ++ch) {
-    __syncthreads();   // the previous chunk has been read (and qs is staged)
+    __builtin_amdgcn_wave_barrier();   // the wave has read the previous chunk
 #pragma unroll
     for (int k = 0; k < NK; ++k) *reinterpret_cast<float4 *>(xw + (lrow + 8 * k) * LDR + half * CW + lcol) = r[k];
     if (ch + 1 < NC) {
@@ -367,7 +369,7 @@ __global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const flo
         r[k] = off[k] >= 0 ? *reinterpret_cast<const float4 *>(gauss + off[k] + (ch + 1) * CW)
                            : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();   // the chunk is in LDS for every lane of the wave
     const float *xm = xw + lane * LDR, *xv = xm + CW;
     const double2 *qc = qs + ch * CW;
 #pragma unroll 2   // bounded unrolling: the q pairs of a coordinate live only while it is summed
