@@ -158,7 +158,7 @@ __global__ __launch_bounds__(256) void score_pool_kernel(CacheView c, int pb, in
     }
     const float *xr = xw + lane * LDR;
     const double *qc = qs + ch * CW;
-#pragma unroll
+#pragma unroll 1   // not unrolled: the query terms of 4 coordinates live at a time (4 waves per SIMD)
     for (int i = 0; i < CW; i += 4) {
       const float4 x = *reinterpret_cast<const float4 *>(xr + i);
       const float xv[4] = {x.x, x.y, x.z, x.w};
