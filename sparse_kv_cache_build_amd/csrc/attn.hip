@@ -111,7 +111,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_softmax_kernel(
     const int it = r / rows_per_item;
     return rm.row_offset(it0 + it, r - it * rows_per_item);
   };
-  auto accumulate = [&](const Packed8<T> &kx, const float (&vx)[8]) {
+  auto accumulate = [&](const Packed8<T> &kx, const Packed8<T> &vp) {
+    float vx[8];   // V stays packed until its row is used
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vx[j] = vp.at(j);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float z = group_sum<RL::LPR>(qv[h].dot(kx)) * scale_log2;
@@ -134,15 +137,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_softmax_kernel(
   __syncthreads();
   for (int r = rg; r < NR; r += UNR * RL::RGB) {
     long long o[UNR];
-    Packed8<T> kx[UNR];
-    float vx[UNR][8];
+    Packed8<T> kx[UNR], vx[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int ru = r + u * RL::RGB;
       o[u] = ru < NR ? roff[ru] : -1;
       if (o[u] >= 0) {
         kx[u].load(K + o[u] + lr * 8);
-        Elem<T>::load8(V + o[u] + lr * 8, vx[u]);
+        vx[u].load(V + o[u] + lr * 8);
       }
     }
 #pragma unroll
