@@ -19,7 +19,8 @@
  * Conventions shared by every call
  *   - Memory: every pointer in a struct or argument is a device pointer unless stated
  *     otherwise; the caller owns all memory, including workspaces (size them with
- *     skv_workspace_bytes). The library never allocates, frees or keeps caller memory.
+ *     skv_workspace_bytes). The library never allocates, frees or keeps caller memory (the
+ *     kernel timer below, a measurement aid, creates and destroys HIP events of its own).
  *   - Streams: `stream` is a hipStream_t (NULL = the null stream). Every call only enqueues
  *     work on it and returns; nothing is synchronised. Results are valid once the stream
  *     reaches the enqueued work.
