@@ -38,3 +38,28 @@ def test_graph_replays_match_eager(name, over):
         st.run()                      # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(st.attn.out, ref_out)
+
+
+def test_kernel_timer_skips_captured_launches():
+    """Launches recorded into a graph while the kernel timer runs are not timed (an event record
+    on a capturing stream would become part of the graph); eager launches around them are, and the
+    replays still match the eager result."""
+    print("[graph] kernel timer under capture", flush=True)
+    import sparse_kv_cache_build_amd as skv
+    w = W.make("gqa32k", device="cuda:0", B=2, L=3000)
+    st = bench.Step(w, 1.0)
+    st.run()
+    torch.cuda.synchronize()
+    ref = st.attn.out.clone()
+    with skv.KernelTimer("score", capacity=16) as kt:
+        st.score()                    # eager: timed
+        st.capture()                  # the capture records the scoring launch once: not timed
+        st.score()                    # eager: timed
+        torch.cuda.synchronize()
+    assert kt.count == 2, kt.count
+    for _ in range(2):
+        st.attn.out.zero_()
+        st.g_score.replay()
+        st.g_rest.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.attn.out, ref)
