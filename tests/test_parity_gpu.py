@@ -102,6 +102,20 @@ def test_full_cache_comparator(dev, name, alpha):
     H.compare(w, st, alphas=(alpha,), check_meta=False)
 
 
+@pytest.mark.parametrize("lens", [[600, 700], [2000, 3100]])
+@pytest.mark.parametrize("alpha", [1.5, 2.0, 1.25])
+def test_entmax_many_survivors(dev, lens, alpha):
+    """Keys scaled down so that every logit lies within 1 of the maximum (in z' units): the solve
+    keeps hundreds (LDS-staged) or thousands (the pair lists walked in global memory) of survivors,
+    beyond the ones held in registers."""
+    H.log(f"[parity entmax survivors] lens={lens} alpha={alpha}")
+    w = W.make("gqa32k", device=dev, B=2, lens=lens)
+    w.k.mul_(1e-3)
+    w.cfg = dict(w.cfg, policy="all")
+    st = H.gpu_step(w, alphas=(alpha,))
+    H.compare(w, st, alphas=(alpha,), check_meta=False)
+
+
 @pytest.mark.parametrize("over", [dict(B=2, L=20000, k=512), dict(B=2, L=5000, k=512),
                                   dict(B=3, lens=[0, 9000, 40000], k=2048), dict(B=2, lens=[1500, 30000], k=1000),
                                   dict(B=2, lens=[3000, 7001], k=300, S=8), dict(B=2, lens=[2500, 6000], k=400, S=48),
