@@ -102,6 +102,21 @@ def test_full_cache_comparator(dev, name, alpha):
     H.compare(w, st, alphas=(alpha,), check_meta=False)
 
 
+@pytest.mark.parametrize("over", [dict(proj_rank=16, Hq=8, Hkv=8), dict(proj_rank=64, Hq=16, Hkv=8),
+                                  dict(proj_rank=32, Hq=64, Hkv=8), dict(proj_rank=64, Hq=64, Hkv=8),
+                                  dict(proj_rank=16, Hq=8, Hkv=4, d=64)])
+@pytest.mark.parametrize("fused", [True, False])
+def test_projected_ranks_and_groups(dev, over, fused):
+    """Projected token keys at ranks 16, 32 and 64 and GQA groups of 1, 2 and 8 (d = 128 and 64),
+    kept as the fused candidate set or as dense keys."""
+    H.log(f"[parity projected] {over} fused={fused}")
+    w = W.make("token128k", device=dev, B=2, lens=[9000, 4100], k=512, **over)
+    st = H.gpu_step(w, fused=fused)
+    if fused:
+        assert st.scores.key is None
+    H.compare(w, st)
+
+
 @pytest.mark.parametrize("lens", [[600, 700], [2000, 3100]])
 @pytest.mark.parametrize("alpha", [1.5, 2.0, 1.25])
 def test_entmax_many_survivors(dev, lens, alpha):
