@@ -102,6 +102,20 @@ def test_full_cache_comparator(dev, name, alpha):
     H.compare(w, st, alphas=(alpha,), check_meta=False)
 
 
+@pytest.mark.parametrize("name,over", [("gqa32k", dict(Hq=16, Hkv=8)), ("gqa32k", dict(Hq=64, Hkv=8, d=64)),
+                                       ("gqa32k", dict(Hq=8, Hkv=8, d=64, dtype="f32")),
+                                       ("long_gauss", dict(Hq=16, Hkv=8)), ("long_gauss", dict(Hq=64, Hkv=8)),
+                                       ("long_gauss", dict(Hq=8, Hkv=4, d=64, dtype="f32")),
+                                       ("ragged", dict(Hq=16, Hkv=8, alphas=(1.0, 1.5)))])
+def test_page_keys_over_groups(dev, name, over):
+    """Box and Gaussian page keys, their selections and attention at GQA groups of 1, 2, 4 and 8,
+    d = 64 and 128, bf16 and float32 caches."""
+    H.log(f"[parity groups] {name} {over}")
+    w = W.make(name, device=dev, **{**SMALL[name], **over})
+    st = H.gpu_step(w)
+    H.compare(w, st)
+
+
 @pytest.mark.parametrize("over", [dict(proj_rank=16, Hq=8, Hkv=8), dict(proj_rank=64, Hq=16, Hkv=8),
                                   dict(proj_rank=32, Hq=64, Hkv=8), dict(proj_rank=64, Hq=64, Hkv=8),
                                   dict(proj_rank=16, Hq=8, Hkv=4, d=64)])
