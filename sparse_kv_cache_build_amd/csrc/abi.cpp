@@ -102,7 +102,7 @@ skv_status attn_plan(const skv_cache *c, const skv_attn_params *p, int cap, Attn
   const int rows_per_item = p->granularity ? 1 : c->page_size;
   const bool entmax = p->alpha != 1.0f;
   const int64_t U = (int64_t)c->batch * c->num_kv_heads;
-  const int rmax = entmax ? 512 : 1024;   // rows per partition
+  const int rmax = 1024;   // rows per partition (entmax: at most 40 KiB of logits and offsets at G = 8)
   int64_t spi = p->split;
   if (spi <= 0) {
     spi = ((int64_t)cap * U + 1023) / 1024;   // about 1024 partitions in total
