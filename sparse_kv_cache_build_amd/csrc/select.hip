@@ -422,14 +422,19 @@ __global__ __launch_bounds__(kBoundThreads) void token_bound_kernel(CacheView c,
     *reinterpret_cast<int32_t *>(cand + lay.hdr + 8) = R;
   }
   if (tid == 0) qmax_bits = 0u;
-  // loads in the order they are needed: P and q, the block-table entries of the sampled tokens,
-  // then the sampled rows, which stay in flight while q~ is formed
+  // P and q are staged first, so that the barrier waits for them only; the block-table entries
+  // of the sampled tokens are then in flight while q~ is formed, and the sampled rows while the
+  // filter coefficients are settled
   float pv[PPT];
 #pragma unroll
   for (int u = 0; u < PPT; ++u) pv[u] = proj[u * NT + tid];
   const T *qb = q + ((size_t)b * c.Hq + g * G) * D;
   const float qv = tid < G * D ? Elem<T>::get(qb, tid) : 0.0f;
   const int L = seq_len(c, b);
+#pragma unroll
+  for (int u = 0; u < PPT; ++u) ps[(u * NT + tid) / D][(u * NT + tid) % D] = pv[u];
+  if (tid < G * D) qf[tid / D][tid % D] = qv;
+  __syncthreads();
   const int kk = min(k, L);
   const bool sample = !(kk >= L || L <= kTokCand);
   const int run = kBoundSample / 64, stride = L / 64;
@@ -442,18 +447,7 @@ __global__ __launch_bounds__(kBoundThreads) void token_bound_kernel(CacheView c,
       tok[u] = (s / run) * stride + s % run;
       phys[u] = c.bt[(size_t)b * c.maxP + tok[u] / c.S];
     }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const uint4 *row = reinterpret_cast<const uint4 *>(
-          kproj + (((size_t)phys[u] * c.Hkv + g) * c.S + tok[u] % c.S) * R);
-#pragma unroll
-      for (int i = 0; i < R / 8; ++i) w[u][i] = row[i];
-    }
   }
-#pragma unroll
-  for (int u = 0; u < PPT; ++u) ps[(u * NT + tid) / D][(u * NT + tid) % D] = pv[u];
-  if (tid < G * D) qf[tid / D][tid % D] = qv;
-  __syncthreads();
   // q~ of the unit's G heads: the float64 sum over j ascending of P[i][j] q[j], rounded to float
   double *qt = reinterpret_cast<double *>(cand + lay.qt) + (size_t)(b * c.Hq + g * G) * R;
   if (tid < G * R) {
@@ -469,6 +463,15 @@ __global__ __launch_bounds__(kBoundThreads) void token_bound_kernel(CacheView c,
     reinterpret_cast<uint16_t *>(cand + lay.qb)[(size_t)(b * c.Hq + g * G) * R + tid] = hb;
     const float am = wave_max(fabsf(qf32));
     if ((tid & (kWave - 1)) == 0) atomicMax(&qmax_bits, __float_as_uint(am));
+  }
+  if (sample) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const uint4 *row = reinterpret_cast<const uint4 *>(
+          kproj + (((size_t)phys[u] * c.Hkv + g) * c.S + tok[u] % c.S) * R);
+#pragma unroll
+      for (int i = 0; i < R / 8; ++i) w[u][i] = row[i];
+    }
   }
   __syncthreads();
   const FilterCoef fc = filter_coef(__uint_as_float(qmax_bits));
