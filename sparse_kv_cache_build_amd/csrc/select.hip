@@ -693,11 +693,8 @@ __global__ __launch_bounds__(kTokThreads) void select_token_cand_kernel(CacheVie
         kmax = max(kmax, u[j]);
       }
     }
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, kWave));
-      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, kWave));
-    }
+    kmin = wave_umin_dpp(kmin);
+    kmax = wave_umax_dpp(kmax);
     if ((tid & (kWave - 1)) == 0) {
       range[tid / kWave] = kmin;
       range[kTokWaves + tid / kWave] = kmax;
