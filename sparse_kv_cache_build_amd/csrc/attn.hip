@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_softmax_kernel(
     CacheView c, const T *__restrict__ q, const int32_t *__restrict__ sel_idx, const int32_t *__restrict__ sel_count,
     int cap, int gran, int spi, int nsplit, float scale_log2, float *__restrict__ part, float *__restrict__ out) {
   using RL = RowLayout<D>;
-  constexpr int UNR = 2;   // rows per lane group in flight (more was measured slower: 4 -> +2.6 us at token128k)
+  constexpr int UNR = 2;   // rows per lane group in flight (three or four measured slower)
   __shared__ float s_m[G][RL::RGB];
   __shared__ float s_l[G][RL::RGB];
   __shared__ float s_acc[kAttnThreads / kWave][G][D];
