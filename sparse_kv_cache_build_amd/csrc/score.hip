@@ -316,19 +316,16 @@ __global__ __launch_bounds__(256) void score_lsh_kernel(CacheView c, int L, int 
 
 // GAUSS scores. m = scale sum_j q_j mean_j, s = scale sqrt(sum_j q_j^2 var_j) (float64, j
 // ascending), shat = m + s sqrt(2 ln n_p) (or the quantile maximum). Outputs [B, Hq, maxP]; NaN past
-// the sequence. A wave owns 64 pages (a lane each, G heads); their rows are read in chunks of 32
-// coordinates (128 bytes of the mean row and 128 of the variance row: 16 lanes per page, four pages
-// per load instruction; 16 coordinates at G = 8, where two blocks per CU would not fit in LDS) into
-// LDS, where each lane sums its page; the (q, q^2) pairs come from LDS as broadcast reads. The next
-// chunk is loaded while the current one is summed.
+// the sequence. A wave owns 64 pages (a lane each, G heads); their rows are read in chunks of 16
+// coordinates (64 bytes of the mean row and 64 of the variance row: 8 lanes per page, eight pages per
+// load instruction) into LDS, where each lane sums its page; the (q, q^2) pairs come from LDS as
+// broadcast reads. The next chunk is loaded while the current one is summed.
 template <int D, int G>
 __global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const float *__restrict__ gauss,
                                                           const double *__restrict__ qpm, double scale, int quantile,
                                                           float *__restrict__ m_out, float *__restrict__ s_out,
                                                           float *__restrict__ shat_out) {
-  // CW coordinates per chunk: a page's chunk is CW / 2 lanes wide (mean and variance halves of
-  // CW / 4 lanes each), PPI pages per load instruction, NK load instructions for the wave's 64 pages
-  constexpr int CW = G <= 4 ? 32 : 16, NC = D / CW, LDR = 2 * CW + 4, LPP = CW / 2, PPI = 64 / LPP, NK = 64 / PPI;
+  constexpr int CW = 16, NC = D / CW, LDR = 2 * CW + 4, NK = 8;   // 64 rows, 8 per load instruction
   __shared__ double2 qs[G * D];
   __shared__ float xs[4][64 * LDR];
   const int unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
@@ -348,12 +345,12 @@ __global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const flo
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) qs[i] = qq[i];
   const int *bt = c.bt + (size_t)b * c.maxP;
   // load side: lane -> page lrow + 8k, half (mean or variance row) and 4 of the 16 columns
-  const int lrow = lane / LPP, half = (lane / (LPP / 2)) & 1, lcol = (lane % (LPP / 2)) * 4;
+  const int lrow = lane >> 3, half = (lane >> 2) & 1, lcol = (lane & 3) * 4;
   long long off[NK];
   float4 r[NK];
 #pragma unroll
   for (int k = 0; k < NK; ++k) {
-    const int p = p0 + lrow + PPI * k;
+    const int p = p0 + lrow + 8 * k;
     off[k] = p < np ? (((long long)bt[p] * c.Hkv + g) * 2 + half) * D + lcol : -1;
     r[k] = off[k] >= 0 ? *reinterpret_cast<const float4 *>(gauss + off[k]) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
@@ -365,7 +362,7 @@ __global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const flo
   for (int ch = 0; ch < NC; ++ch) {
     __builtin_amdgcn_wave_barrier();   // the wave has read the previous chunk
 #pragma unroll
-    for (int k = 0; k < NK; ++k) *reinterpret_cast<float4 *>(xw + (lrow + PPI * k) * LDR + half * CW + lcol) = r[k];
+    for (int k = 0; k < NK; ++k) *reinterpret_cast<float4 *>(xw + (lrow + 8 * k) * LDR + half * CW + lcol) = r[k];
     if (ch + 1 < NC) {
 #pragma unroll
       for (int k = 0; k < NK; ++k)
