@@ -45,6 +45,16 @@ __global__ __launch_bounds__(64) void qprep_proj_kernel(const T *__restrict__ q,
   out[(size_t)bh * r + i] = (double)(float)acc;
 }
 
+// element jj of a row slice held as 16-byte words (jj a compile-time constant after unrolling)
+template <typename T, int N>
+__device__ __forceinline__ float box_elem(const uint4 (&r)[N], int jj) {
+  const int w = sizeof(T) == 4 ? jj : jj >> 1;
+  const uint4 v = r[w >> 2];
+  const uint32_t x = (w & 3) == 0 ? v.x : (w & 3) == 1 ? v.y : (w & 3) == 2 ? v.z : v.w;
+  if constexpr (sizeof(T) == 4) return __uint_as_float(x);
+  else return (jj & 1) ? bf16_hi(x) : bf16_lo(x);
+}
+
 // BOX key: one lane per page. key[b][g][p] = RN_f32(max_h sum_j (q+_hj kmax_j + q-_hj kmin_j)).
 // For each coordinate exactly one of the two products is nonzero (or both are zero), so the
 // float64 running sum equals sum_j max(q_hj kmin_j, q_hj kmax_j) accumulated in order.
@@ -64,17 +74,28 @@ __global__ __launch_bounds__(256) void score_box_kernel(CacheView c, const T *__
   const T *lo = box + ((size_t)phys * c.Hkv + g) * 2 * D;
   const T *hi = lo + D;
   const double *qq = qpm + (size_t)(b * c.Hq + g * G) * D * 2;
+  // The row is read in groups of NV 16-byte loads issued together (a whole 128-byte line, or half
+  // of one at G = 8, where the registers of a whole line cost more occupancy than they save), so
+  // that each line is fetched about once. Left to the scheduler, the loads of a line were spread
+  // over the arithmetic, and the line was often evicted in between: about twice the bytes fetched.
+  constexpr int NV = (G >= 8 ? 64 : 128) / 16, EPV = 16 / (int)sizeof(T), GC = NV * EPV;
+  static_assert(D % GC == 0, "a group of coordinates must divide the row");
+  const uint4 *lo4 = reinterpret_cast<const uint4 *>(lo), *hi4 = reinterpret_cast<const uint4 *>(hi);
   double acc[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) acc[h] = 0.0;
 #pragma unroll
-  for (int j0 = 0; j0 < D; j0 += 8) {
-    float xl[8], xh[8];
-    Elem<T>::load8(lo + j0, xl);
-    Elem<T>::load8(hi + j0, xh);
+  for (int j0 = 0; j0 < D; j0 += GC) {
+    uint4 rl[NV], rh[NV];
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const double dl = xl[jj], dh = xh[jj];
+    for (int i = 0; i < NV; ++i) {
+      rl[i] = lo4[j0 / EPV + i];
+      rh[i] = hi4[j0 / EPV + i];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep the group's loads together (no wait is implied)
+#pragma unroll
+    for (int jj = 0; jj < GC; ++jj) {
+      const double dl = box_elem<T>(rl, jj), dh = box_elem<T>(rh, jj);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         acc[h] = fma(qq[((size_t)h * D + j0 + jj) * 2], dh, acc[h]);
