@@ -104,6 +104,8 @@ def test_full_cache_comparator(dev, name, alpha):
 
 @pytest.mark.parametrize("name,over", [("gqa32k", dict(Hq=16, Hkv=8)), ("gqa32k", dict(Hq=64, Hkv=8, d=64)),
                                        ("gqa32k", dict(Hq=8, Hkv=8, d=64, dtype="f32")),
+                                       ("gqa32k", dict(Hq=16, Hkv=4, dtype="f32")),
+                                       ("gqa32k", dict(Hq=32, Hkv=4, dtype="f32")),
                                        ("long_gauss", dict(Hq=16, Hkv=8)), ("long_gauss", dict(Hq=64, Hkv=8)),
                                        ("long_gauss", dict(Hq=8, Hkv=4, d=64, dtype="f32")),
                                        ("ragged", dict(Hq=16, Hkv=8, alphas=(1.0, 1.5)))])
