@@ -87,7 +87,8 @@ enum { SKV_META_BOX = 1, SKV_META_GAUSS = 2, SKV_META_PROJ = 4, SKV_META_POOL = 
 
 typedef struct skv_meta {
   uint32_t kinds;     /* OR of SKV_META_* to build (build_page_meta) / available (score) */
-  void *box;          /* BOX:   [Nphys, Hkv, 2, d] cache dtype: row 0 k_min, row 1 k_max */
+  void *box;          /* BOX:   [Nphys, Hkv, d/C, 2, C] cache dtype, C = 64 bytes of elements
+                         (32 bf16, 16 float32): 64-byte blocks of k_min and of k_max alternate */
   float *gauss;       /* GAUSS: [Nphys, Hkv, 2, d] float32: row 0 mean, row 1 variance */
   int32_t proj_rank;  /* PROJ:  r, 1..64 */
   const float *proj;  /* PROJ:  [r, d] float32 projection shared by queries and keys */

@@ -177,7 +177,8 @@ class PageMeta:
         self.lsh_planes = lsh_planes
         if "box" in kinds:
             self.kinds |= META_BOX
-            self.box = torch.empty((Np, Hkv, 2, d), dtype=cache.dtype, device=dev)
+            cb = 64 // (2 if cache.dtype == torch.bfloat16 else 4)   # coordinates per 64-byte block
+            self.box = torch.empty((Np, Hkv, d // cb, 2, cb), dtype=cache.dtype, device=dev)
         if "gauss" in kinds:
             self.kinds |= META_GAUSS
             self.gauss = torch.empty((Np, Hkv, 2, d), dtype=torch.float32, device=dev)

@@ -10,7 +10,8 @@ namespace skv {
 
 // One workgroup per logical page (p, b); threads sweep (KV head, coordinate) pairs so that each
 // token row is read with consecutive coordinates across consecutive threads.
-//   box:   exact min / max over the valid tokens, stored as the original element bits.
+//   box:   exact min / max over the valid tokens, stored as the original element bits, the
+//          64-byte blocks of the min row and of the max row alternating ([d / C][2][C], C = 64 bytes).
 //   gauss: float64 mean (sum over t ascending, divided by n), then float64 mean squared
 //          deviation, each rounded once to float32.
 // First logical page a build (tail == 0) or an append of `tail` tokens covers.
@@ -41,8 +42,11 @@ __global__ __launch_bounds__(256) void meta_box_gauss_kernel(CacheView c, int ta
         if (fx < flo) { flo = fx; lo = x; }
         if (fx > fhi) { fhi = fx; hi = x; }
       }
-      box[mo] = lo;
-      box[mo + c.D] = hi;
+      // 64-byte blocks of the min and max rows alternate, so one 128-byte line holds both
+      constexpr int C = 64 / (int)sizeof(T);
+      const size_t bo = ((size_t)phys * c.Hkv + g) * 2 * c.D + (size_t)(j / C) * 2 * C + (j % C);
+      box[bo] = lo;
+      box[bo + C] = hi;
     }
     if (gauss) {
       double sum = 0.0;

@@ -71,26 +71,30 @@ __global__ __launch_bounds__(256) void score_box_kernel(CacheView c, const T *__
     return;
   }
   const int phys = c.bt[(size_t)b * c.maxP + p];
-  const T *lo = box + ((size_t)phys * c.Hkv + g) * 2 * D;
-  const T *hi = lo + D;
+  // the page's box: 128-byte lines, each the min row's and the max row's values of the same C
+  // coordinates (64 bytes each)
+  const uint4 *row = reinterpret_cast<const uint4 *>(box + ((size_t)phys * c.Hkv + g) * 2 * D);
   const double *qq = qpm + (size_t)(b * c.Hq + g * G) * D * 2;
-  // The row is read in groups of NV 16-byte loads issued together (a whole 128-byte line, or half
-  // of one at G = 8, where the registers of a whole line cost more occupancy than they save), so
-  // that each line is fetched about once. Left to the scheduler, the loads of a line were spread
-  // over the arithmetic, and the line was often evicted in between: about twice the bytes fetched.
-  constexpr int NV = (G >= 8 ? 64 : 128) / 16, EPV = 16 / (int)sizeof(T), GC = NV * EPV;
+  // The lines are read in groups of NL whole lines, their 16-byte loads issued together, so that
+  // each line is fetched once. Left to the scheduler, the loads of a line were spread over the
+  // arithmetic, and the line was often evicted in between. One line per group at G = 8, where the
+  // registers of two would cost more occupancy than they save.
+  constexpr int NL = G >= 8 ? 1 : 2, NV = 4 * NL, EPV = 16 / (int)sizeof(T), GC = NV * EPV;
   static_assert(D % GC == 0, "a group of coordinates must divide the row");
-  const uint4 *lo4 = reinterpret_cast<const uint4 *>(lo), *hi4 = reinterpret_cast<const uint4 *>(hi);
   double acc[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) acc[h] = 0.0;
 #pragma unroll
   for (int j0 = 0; j0 < D; j0 += GC) {
-    uint4 rl[NV], rh[NV];
+    uint4 rl[NV], rh[NV];   // the group's min values, then its max values, coordinates in order
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      rl[i] = lo4[j0 / EPV + i];
-      rh[i] = hi4[j0 / EPV + i];
+    for (int l = 0; l < NL; ++l) {
+      const uint4 *ln = row + (size_t)(j0 / GC * NL + l) * 8;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        rl[4 * l + i] = ln[i];
+        rh[4 * l + i] = ln[4 + i];
+      }
     }
     __builtin_amdgcn_sched_barrier(0);   // keep the group's loads together (no wait is implied)
 #pragma unroll

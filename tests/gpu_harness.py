@@ -224,9 +224,10 @@ def _compare_meta(w, st, c, md, pm, spec):
         return
     gp = torch.from_numpy(pm[used]).to(w.k.device)
     if spec.score == "box":
-        box = bf16_to_f64(st.meta.box[gp])          # [n, Hkv, 2, d]
-        assert np.array_equal(box[:, :, 0], md.kmin[used]), "kmin mismatch"
-        assert np.array_equal(box[:, :, 1], md.kmax[used]), "kmax mismatch"
+        box = bf16_to_f64(st.meta.box[gp])          # [n, Hkv, d / C, 2, C]: min and max blocks alternate
+        n_, h_ = box.shape[:2]
+        assert np.array_equal(box[:, :, :, 0].reshape(n_, h_, -1), md.kmin[used]), "kmin mismatch"
+        assert np.array_equal(box[:, :, :, 1].reshape(n_, h_, -1), md.kmax[used]), "kmax mismatch"
     elif spec.score == "gauss":
         ga = st.meta.gauss[gp].cpu().numpy()
         assert np.array_equal(ga[:, :, 0], md.mean[used].astype(np.float32)), "mean mismatch"
