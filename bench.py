@@ -43,11 +43,18 @@ class Step:
         self.w, self.alpha, self.full = w, alpha, full
         self.kind = cfg["score"]
         self.cache = skv.PagedCache(w.k, w.v, w.block_table, w.seq_lens, w.Hq)
-        t0 = time.time()
-        self.meta = skv.build_page_meta(self.cache, ("gauss" if self.kind == "gauss_q" else self.kind,), proj=w.proj,
-                                        pool_block=cfg.get("pool_block", 0), lsh_planes=w.lsh_planes)
+        self.events = None   # timing events for the dominant kernel (skv.event_pair())
+        meta_kinds = ("gauss" if self.kind == "gauss_q" else self.kind,)
+        self.meta = skv.build_page_meta(self.cache, meta_kinds, proj=w.proj, pool_block=cfg.get("pool_block", 0),
+                                        lsh_planes=w.lsh_planes)
+        # the build timed on its second run (the first also loads the kernels' code)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        skv._binding._check(skv.lib().skv_build_page_meta(self.cache.ref, self.meta.ref, skv._binding._stream(None)),
+                            "skv_build_page_meta")
+        e1.record()
         torch.cuda.synchronize()
-        self.meta_s = time.time() - t0
+        self.meta_s = e0.elapsed_time(e1) * 1e-3
         # token top-k: keep only the candidate set of the selection (fused scoring, no dense keys)
         self.fused = cfg["policy"] == "token_topk" and cfg["score"] == "proj" and not full
         self.scores = skv.ScoreBuffers(self.cache, self.kind, cfg.get("k", 0) if self.fused else 0)
@@ -73,11 +80,11 @@ class Step:
         """The dominant kernel: the filtered token scoring, the page scorer, or (full-cache
         comparator) the attention over every page."""
         if self.full:
-            skv.sparse_decode_attn(self.cache, self.w.q, self.sel, out=self.attn)
+            skv.sparse_decode_attn(self.cache, self.w.q, self.sel, out=self.attn, events=self.events)
         else:
             skv.score_pages(self.cache, self.meta, self.w.q, self.kind, out=self.scores,
                             phase=skv.TOKEN_PHASE_FILTER if self.fused else skv.TOKEN_PHASE_ALL,
-                            temperature=self.w.cfg.get("lsh_tau"))
+                            temperature=self.w.cfg.get("lsh_tau"), events=self.events)
 
     def rest(self):
         if not self.full:
@@ -149,7 +156,17 @@ def step_bytes(st: Step):
     q_out = w.B * w.Hq * d * (e + 4)
     total = meta + bt + k_rows * kv_row + v_rows * kv_row + q_out
     dom = (k_rows + v_rows) * kv_row + q_out if st.full else meta + keys_out + bt
-    return total, dom, dict(meta=meta, k_rows=k_rows, v_rows=v_rows, q_out=q_out, keys_out=keys_out, block_table=bt)
+    det = dict(meta=meta, block_table=bt, k=k_rows * kv_row, v=v_rows * kv_row, q_out=q_out)
+    assert sum(det.values()) == total
+    return total, dom, det, dict(selected_rows=k_rows, weighted_rows=v_rows, keys_written_bytes=keys_out)
+
+
+def meta_read_bytes(w: W.Workload) -> int:
+    """Bytes of the cache the metadata build reads: K of every valid token (and V for the soft-LSH
+    value norms)."""
+    e = 2 if w.dtype == torch.bfloat16 else 4
+    n = int(np.array(w.lens).sum()) * w.Hkv * w.d * e
+    return 2 * n if w.cfg["score"] == "lsh" else n
 
 
 def dominant_kernel(st: Step) -> str:
@@ -190,17 +207,21 @@ def recorded_traffic(workload: str, kernel: str):
     return int(rec["traffic_bytes"])
 
 
-def cpu_baseline(name: str, over: dict, alpha: float, budget_s: float = 20.0):
-    """The float64 oracle (unchanged) on a bounded sample: units (sequence, KV head) drawn on the
-    CPU with the workload's shapes, run in parallel threads, one unit per task. Metadata is built
-    first (prefill work, not timed); score + select + attention of the sampled units is timed and
-    scaled to whole steps."""
+def cpu_baseline(name: str, alpha: float, max_threads: int = 16):
+    """The float64 oracle (unchanged) on a bounded sample of the workload: units (sequence, KV head)
+    of sequences drawn on the CPU with the workload's shapes at full context. Metadata is built
+    first (prefill work, not timed). Timed: score + select + attention of each sampled unit, one
+    unit per task on a pool of threads (the oracle releases the GIL), then scaled to whole steps;
+    and one unit alone on one thread. The pool uses every core the process may run on, up to
+    max_threads (the CPU share of one GPU's host)."""
     import oracle
     from oracle import pipeline
 
-    cores = len(os.sched_getaffinity(0))
-    threads = max(1, min(cores, 16))
-    w = W.make(name, device="cpu", **dict(over, B=1))
+    host_cores = len(os.sched_getaffinity(0))
+    threads = max(1, min(host_cores, max_threads))
+    cfg = W.CONFIGS[name]
+    n_seq = max(1, -(-threads // cfg["Hkv"]))          # enough sequences for one unit per thread
+    w = W.make(name, device="cpu", B=n_seq)
     spec = pipeline.Spec(score="gauss" if w.cfg["score"] == "gauss_q" else w.cfg["score"], policy=w.cfg["policy"],
                          k=w.cfg.get("k", 0), pct=w.cfg.get("pct", 0),
                          sel_alpha=w.cfg.get("sel_alpha", 1.5), delta=w.cfg.get("delta", 0.0), alphas=(alpha,),
@@ -209,15 +230,16 @@ def cpu_baseline(name: str, over: dict, alpha: float, budget_s: float = 20.0):
                          pool_block=w.cfg.get("pool_block", 4),
                          lsh_planes=w.lsh_planes.numpy() if w.lsh_planes is not None else None,
                          lsh_tau=w.cfg.get("lsh_tau", 1.0))
-    h = W.host_arrays(w)
-    n_units = min(w.Hkv, threads)
     caches = []
-    for g in range(n_units):   # one KV head per sub-cache (exact bytes of that head)
-        G = w.G
-        caches.append(oracle.Cache(q=np.ascontiguousarray(h["q"][:, g * G:(g + 1) * G]),
-                                   k=np.ascontiguousarray(h["k"][:, g:g + 1]),
-                                   v=np.ascontiguousarray(h["v"][:, g:g + 1]),
-                                   block_table=h["block_table"], seq_lens=h["seq_lens"]))
+    G = w.G
+    for b in range(n_seq):     # one unit per sub-cache (exact bytes of that sequence and KV head)
+        h = W.host_arrays(w, [b])
+        for g in range(w.Hkv):
+            caches.append(oracle.Cache(q=np.ascontiguousarray(h["q"][:, g * G:(g + 1) * G]),
+                                       k=np.ascontiguousarray(h["k"][:, g:g + 1]),
+                                       v=np.ascontiguousarray(h["v"][:, g:g + 1]),
+                                       block_table=h["block_table"], seq_lens=h["seq_lens"]))
+    n_units = len(caches)
     with cf.ThreadPoolExecutor(threads) as ex:
         mds = list(ex.map(lambda c: pipeline.build_metadata(c, spec), caches))
 
@@ -227,20 +249,70 @@ def cpu_baseline(name: str, over: dict, alpha: float, budget_s: float = 20.0):
         r = pipeline.run_unit(c, spec, sc, 0, 0)
         return len(r.sel)
 
+    t0 = time.perf_counter()
+    one(0)
+    single = time.perf_counter() - t0
     reps, t = 0, 0.0
     with cf.ThreadPoolExecutor(threads) as ex:
-        while t < 2.0 and reps < 50:
+        while t < 5.0 and reps < 50:
             t0 = time.perf_counter()
             list(ex.map(one, range(n_units)))
             t += time.perf_counter() - t0
             reps += 1
     per_round = t / reps
-    units_total = W.CONFIGS[name]["B"] * W.CONFIGS[name]["Hkv"] if "B" not in over else over["B"] * w.Hkv
+    units_total = sum(1 for _ in range(cfg["B"])) * cfg["Hkv"]
     steps_per_s = (n_units / units_total) / per_round
-    return dict(value=steps_per_s, unit="steps/s", cores=threads, kind="oracle",
-                sample=f"{n_units} units (1 sequence x {n_units} KV heads, {w.G} query heads each) of {name} at full "
-                       f"context ({w.lens[0]} tokens), metadata prebuilt; score+select+attention timed over {reps} "
-                       f"round(s), {per_round:.3f} s per round, scaled by {units_total} units per step")
+    return dict(value=steps_per_s, unit="steps/s", cores=threads, host_cores=host_cores, kind="oracle",
+                single_thread_unit_s=round(single, 4),
+                single_thread_steps_per_s=1.0 / (single * units_total),
+                sample=f"{n_units} units ({n_seq} sequence(s) x {w.Hkv} KV heads, {G} query heads each) of {name} at "
+                       f"full context ({w.lens[0]} tokens), metadata prebuilt; score+select+attention on {threads} "
+                       f"threads over {reps} round(s), {per_round:.3f} s per round, scaled by {units_total} units "
+                       f"per step; one unit alone on one thread took {single:.3f} s")
+
+
+def w0_row_bytes(w: W.Workload) -> int:
+    return w.d * (2 if w.dtype == torch.bfloat16 else 4)
+
+
+def reference_ceilings(dev, n_rows: int, row_bytes: int, reps: int = 5):
+    """Reference rates on this GPU (torch's own kernels, context for the roofline fractions):
+    a 1 GiB copy (read + write), a read-only reduction over 1 GiB, and a gather of n_rows random
+    rows of row_bytes from a 4 GiB table into a contiguous buffer (read + write of the rows)."""
+    def timed(fn):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3
+
+    out = {}
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t = timed(lambda: dst.copy_(src))
+    out["copy_1GiB_GBps"] = round(2 * (1 << 30) / t / 1e9, 1)
+    del dst
+    x = src.view(torch.int32)
+    x.fill_(1)
+    t = timed(lambda: torch.sum(x, dtype=torch.int64))
+    out["read_1GiB_GBps"] = round((1 << 30) / t / 1e9, 1)
+    del src, x
+    n_rows = max(1, int(n_rows))
+    table = torch.empty(((4 << 30) // row_bytes, row_bytes // 2), dtype=torch.bfloat16, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    idx = torch.randint(0, table.shape[0], (n_rows,), generator=g, device=dev)
+    t = timed(lambda: torch.index_select(table, 0, idx))
+    out["gather_rows"] = n_rows
+    out["gather_row_bytes"] = row_bytes
+    out["gather_GBps"] = round(n_rows * row_bytes / t / 1e9, 1)
+    del table, idx
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -258,6 +330,9 @@ def main():
                     help="full-cache comparator: attention over every page with the same kernels, no scoring")
     ap.add_argument("--calibrate", action="store_true",
                     help="after timing, copy a 1 GiB buffer 3 times (reference kernel for HBM byte counters)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="also time reference kernels: a 1 GiB copy, a 1 GiB read-only reduction and a gather of "
+                         "the step's number of random 256-byte rows")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the decode path has no multi-GPU mode "
@@ -273,7 +348,7 @@ def main():
     sets = [Step(W.make(name, device=dev), alpha, args.split, args.full)]
     sets[0].run()
     torch.cuda.synchronize()
-    total, score_bytes, det = step_bytes(sets[0])
+    total, score_bytes, det, rows = step_bytes(sets[0])
     n_sets = args.sets or max(1, math.ceil(2 * MALL_BYTES / max(total, 1)))
     for i in range(1, n_sets):
         log(f"[bench] buffer set {i + 1}/{n_sets}")
@@ -318,18 +393,22 @@ def main():
         score_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
         timed_by = "HIP events around the scoring graph's replay"
     else:
-        # the library records HIP events on the launch stream right around the dominant kernel
-        with skv.KernelTimer("attn" if args.full else "score", capacity=args.steps) as kt:
-            start.record(stream)
-            for i in range(args.steps):
-                pre_fn[i % n_sets]()
-                score_fn[i % n_sets]()
-                rest_fn[i % n_sets]()
-            end.record(stream)
-            torch.cuda.synchronize()
-        assert kt.count == args.steps, (kt.count, args.steps)
-        score_ms = kt.avg_ms
-        timed_by = "HIP events recorded by the library around each launch of the kernel"
+        # caller-owned event pairs, one per step, that the library records on the launch stream right
+        # around the dominant kernel
+        pairs = [skv.event_pair() for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(args.steps):
+            sets[i % n_sets].events = pairs[i]
+            pre_fn[i % n_sets]()
+            score_fn[i % n_sets]()
+            rest_fn[i % n_sets]()
+        end.record(stream)
+        torch.cuda.synchronize()
+        for st in sets:
+            st.events = None
+        score_ms = sum(a.elapsed_time(b) for a, b in pairs) / args.steps
+        timed_by = "HIP events the library records around each launch of the kernel"
     ms = start.elapsed_time(end) / args.steps
     sps = 1000.0 / ms
     gbps = total / (ms * 1e-3) / 1e9
@@ -356,11 +435,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    ceil = reference_ceilings(dev, rows["selected_rows"], w0_row_bytes(sets[0].w)) if args.ceilings else None
 
     cpu = None
     if not args.no_cpu and not args.full:   # the comparator is context: no oracle baseline
         log("[bench] CPU oracle baseline")
-        cpu = cpu_baseline(name, {}, alpha)
+        cpu = cpu_baseline(name, alpha)
 
     key_desc = {"box": "box bound", "pool": f"pooled key (sub-blocks of {cfg.get('pool_block')})",
                 "gauss": "Gaussian estimated maximum", "gauss_q": "Gaussian quantile maximum"}.get(cfg["score"], cfg["score"])
@@ -382,7 +462,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if w0.dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
         "config": {"workload": name, "batch": w0.B, "ctx": int(max(w0.lens)), "mean_ctx": float(np.mean(w0.lens)),
                    "q_heads": w0.Hq, "kv_heads": w0.Hkv, "head_dim": w0.d, "page": w0.S, "kv_dtype": "bf16"
@@ -390,9 +470,11 @@ def main():
                    "select": "every page (full-cache comparator)" if args.full else sel_desc[cfg["policy"]],
                    "attn": "softmax" if alpha == 1.0 else f"{alpha}-entmax", "bytes_per_step": int(total),
                    "achieved_GBps": round(gbps, 1), "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
-                   "buffer_sets": n_sets, "hip_graphs": graphs, "meta_build_s": round(meta_s, 4),
+                   "accumulation": "fp32 (attention), fp64 (ranking keys)",
+                   "buffer_sets": n_sets, "hip_graphs": graphs, "meta_build_s": round(meta_s, 6),
+                   "meta_build_GBps": round(meta_read_bytes(w0) / meta_s / 1e9, 1),
                    "meta_append_us": round(append_us, 2),
-                   "bytes_detail": det},
+                   "bytes_detail": det, **rows},
         "roofline": {"bound": "hbm", "kernel": dominant_kernel(sets[0]), "achieved": round(score_gbps, 1),
                      "peak": PEAK_GBPS, "unit": "GB/s", "frac": round(score_gbps / PEAK_GBPS, 4),
                      "traffic": recorded_traffic(name, dominant_kernel(sets[0])),
@@ -400,6 +482,8 @@ def main():
                      "timed_by": timed_by},
         "cpu_baseline": cpu,
     }
+    if ceil is not None:
+        line["ceilings"] = ceil
     print(json.dumps(line), flush=True)
 
 

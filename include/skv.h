@@ -19,8 +19,8 @@
  * Conventions shared by every call
  *   - Memory: every pointer in a struct or argument is a device pointer unless stated
  *     otherwise; the caller owns all memory, including workspaces (size them with
- *     skv_workspace_bytes). The library never allocates, frees or keeps caller memory (the
- *     kernel timer below, a measurement aid, creates and destroys HIP events of its own).
+ *     skv_workspace_bytes). The library never allocates or frees memory, creates no HIP objects
+ *     and keeps no mutable state between calls.
  *   - Streams: `stream` is a hipStream_t (NULL = the null stream). Every call only enqueues
  *     work on it and returns; nothing is synchronised. Results are valid once the stream
  *     reaches the enqueued work.
@@ -160,6 +160,12 @@ typedef struct skv_scores {
                           bound (projected queries and T_lo into cand); SKV_TOKEN_PHASE_FILTER (2)
                           only the filtered scoring of every token, which needs a BOUND call with
                           the same q and cand before it on the same stream. Ignored otherwise */
+  void *ev_begin;  /* optional hipEvent_t pair owned by the caller (a measurement aid): when both are */
+  void *ev_end;    /* non-null, skv_score_pages records ev_begin on the stream right before the scoring
+                      kernel proper (after any query-preparation kernel; for the candidate scoring of a
+                      token top-k, the filtered pass) and ev_end right after it, so that their elapsed
+                      time is that kernel alone. Not recorded while the stream is being captured into a
+                      graph. A failed record returns SKV_ERR_HIP. Ignored by skv_select_pages */
 } skv_scores;
 
 enum { SKV_TOKEN_PHASE_ALL = 0, SKV_TOKEN_PHASE_BOUND = 1, SKV_TOKEN_PHASE_FILTER = 2 };
@@ -253,6 +259,9 @@ typedef struct skv_attn_params {
   float sm_scale;      /* logit scale c: z_t = c q_h . k_t (c > 0, finite) */
   int32_t granularity; /* 0: sel_idx holds logical pages; 1: sel_idx holds token positions */
   int32_t split;       /* selected items (pages or tokens) per split-K partition; 0 = automatic */
+  void *ev_begin;      /* optional caller-owned hipEvent_t pair, recorded right before and right after */
+  void *ev_end;        /* the first attention kernel (the softmax split kernel or the entmax logits
+                          kernel); as in skv_scores. NULL: not recorded */
 } skv_attn_params;
 
 /* Attention of every query head over the KV rows its KV head selected ("EntmaxKV" s2.C; the
@@ -282,24 +291,6 @@ enum { SKV_OP_SCORE = 0, SKV_OP_SELECT = 1, SKV_OP_ATTN = 2, SKV_OP_CANDIDATES =
  * candidate set (CANDIDATES: the size of skv_scores.cand); cap as passed to that call.
  * Host-only; enqueues nothing. Writes *bytes; SKV_ERR_INVALID_ARG on bad arguments. */
 skv_status skv_workspace_bytes(const skv_cache *c, int32_t op, const void *params, int32_t cap, size_t *bytes);
-
-/* Kernel timer, a measurement aid. Between skv_kernel_timer_start and skv_kernel_timer_stop the
- * library records a pair of HIP events on the caller's stream immediately before and after each
- * launch of one class of kernel, so that the pair times that kernel alone:
- *   SKV_TIMER_SCORE: the scoring kernel of skv_score_pages (box, Gaussian, pooled, projected or
- *     soft-LSH scorer, or the candidate filter of the fused token top-k), after its query
- *     preparation kernel;
- *   SKV_TIMER_ATTN: the first kernel of skv_sparse_decode_attn (the softmax split kernel, or the
- *     entmax logits kernel), before its combine or solve kernel.
- * Only calls on the device current at skv_kernel_timer_start are timed, at most `capacity` of them
- * (1 .. 65536); launches on a stream under graph capture are not timed. The library creates the
- * events at start (2 * capacity hipEventCreate calls) and destroys them at stop.
- * skv_kernel_timer_stop waits for the recorded events and writes the number of timed launches and
- * their summed duration in milliseconds. Errors: SKV_ERR_INVALID_ARG for a bad class or capacity,
- * a start while the timer runs, a stop while it does not, or null outputs; SKV_ERR_HIP. */
-enum { SKV_TIMER_SCORE = 1, SKV_TIMER_ATTN = 2 };
-skv_status skv_kernel_timer_start(int32_t which, int32_t capacity);
-skv_status skv_kernel_timer_stop(int32_t *count, double *total_ms);
 
 /* Static, human-readable name of a status code. Never NULL. */
 const char *skv_status_str(skv_status s);

@@ -21,19 +21,28 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "skv_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# SKV_ORACLE_LIB names another build of the same source (the mutation test points it at copies of
+# the oracle with planted mistakes)
+_LIB = os.environ.get("SKV_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 F32, BF16 = 0, 1
 
 
+GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+
+def compile_source(src: str, out: str, extra=()) -> str:
+    """Compile an oracle source file into a shared library (no fast-math, no FMA contraction)."""
+    tmp = out + ".tmp"
+    subprocess.check_call(["gcc", *GCC_FLAGS, *extra, "-o", tmp, src, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
 def build(force: bool = True) -> str:
-    """Compile ``skv_oracle.c`` into ``liboracle.so`` with gcc (no fast-math, no FMA contraction)."""
+    """Compile ``skv_oracle.c`` into ``liboracle.so`` with gcc."""
     if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(
-            ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
-             "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
+        compile_source(_SRC, _LIB)
     return _LIB
 
 

@@ -23,11 +23,9 @@ META_BOX, META_GAUSS, META_PROJ, META_POOL, META_LSH = 1, 2, 4, 8, 16
 SCORE_BOX, SCORE_GAUSS, SCORE_PROJ, SCORE_GAUSS_Q, SCORE_POOL, SCORE_LSH = 0, 1, 2, 3, 4, 5
 SEL_TOPK, SEL_BUDGET, SEL_THRESH_GAUSS, SEL_TOKEN_TOPK, SEL_ALL, SEL_THRESH_BOX = range(6)
 OP_SCORE, OP_SELECT, OP_ATTN, OP_CANDIDATES = 0, 1, 2, 3
-TIMER_SCORE, TIMER_ATTN = 1, 2
 
 EXPORTS = ("skv_build_page_meta", "skv_append_page_meta", "skv_score_pages", "skv_select_pages",
-           "skv_sparse_decode_attn", "skv_workspace_bytes", "skv_kernel_timer_start", "skv_kernel_timer_stop",
-           "skv_status_str")
+           "skv_sparse_decode_attn", "skv_workspace_bytes", "skv_status_str")
 
 
 class SkvError(RuntimeError):
@@ -52,7 +50,8 @@ class Meta(C.Structure):
 
 class Scores(C.Structure):
     _fields_ = [("key", C.c_void_p), ("m", C.c_void_p), ("s", C.c_void_p), ("shat", C.c_void_p),
-                ("token_k", C.c_int32), ("cand", C.c_void_p), ("token_phase", C.c_int32)]
+                ("token_k", C.c_int32), ("cand", C.c_void_p), ("token_phase", C.c_int32),
+                ("ev_begin", C.c_void_p), ("ev_end", C.c_void_p)]
 
 
 class SelectParams(C.Structure):
@@ -61,7 +60,8 @@ class SelectParams(C.Structure):
 
 
 class AttnParams(C.Structure):
-    _fields_ = [("alpha", C.c_float), ("sm_scale", C.c_float), ("granularity", C.c_int32), ("split", C.c_int32)]
+    _fields_ = [("alpha", C.c_float), ("sm_scale", C.c_float), ("granularity", C.c_int32), ("split", C.c_int32),
+                ("ev_begin", C.c_void_p), ("ev_end", C.c_void_p)]
 
 
 _lib = None
@@ -81,8 +81,6 @@ def lib():
         L.skv_select_pages.argtypes = [P, P, P, P, P, I, P, P, S, P]
         L.skv_sparse_decode_attn.argtypes = [P, P, P, P, I, P, P, P, S, P]
         L.skv_workspace_bytes.argtypes = [P, I, P, I, C.POINTER(C.c_size_t)]
-        L.skv_kernel_timer_start.argtypes = [I, I]
-        L.skv_kernel_timer_stop.argtypes = [C.POINTER(C.c_int32), C.POINTER(C.c_double)]
         L.skv_status_str.argtypes = [I]
         L.skv_status_str.restype = C.c_char_p
         for n in EXPORTS[:-1]:
@@ -91,30 +89,21 @@ def lib():
     return _lib
 
 
-class KernelTimer:
-    """Times one class of kernel alone with HIP events the library records around each launch
-    (skv_kernel_timer_start/stop): "score" for the scoring kernel of score_pages after its query
-    preparation, "attn" for the first kernel of sparse_decode_attn. Use as a context manager;
-    `count` and `total_ms` are set on exit, after the recorded events have completed."""
+def event_pair():
+    """Two timing events (torch.cuda.Event) that exist on the device, for the `events` argument of
+    score_pages and sparse_decode_attn: the library records them right around one kernel launch,
+    and start.elapsed_time(end) is then that kernel alone. The caller owns them."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()   # torch creates an event on its first record
+    b.record()
+    return a, b
 
-    def __init__(self, which: str = "score", capacity: int = 4096):
-        self.which = {"score": TIMER_SCORE, "attn": TIMER_ATTN}[which]
-        self.capacity = capacity
-        self.count, self.total_ms = 0, 0.0
 
-    def __enter__(self):
-        _check(lib().skv_kernel_timer_start(self.which, self.capacity), "skv_kernel_timer_start")
-        return self
-
-    def __exit__(self, *exc):
-        n, ms = C.c_int32(0), C.c_double(0.0)
-        _check(lib().skv_kernel_timer_stop(C.byref(n), C.byref(ms)), "skv_kernel_timer_stop")
-        self.count, self.total_ms = int(n.value), float(ms.value)
-        return False
-
-    @property
-    def avg_ms(self) -> float:
-        return self.total_ms / self.count if self.count else float("nan")
+def _events(events):
+    if events is None:
+        return None, None
+    a, b = events
+    return C.c_void_p(a.cuda_event), C.c_void_p(b.cuda_event)
 
 
 def status_str(code: int) -> str:
@@ -261,7 +250,7 @@ class ScoreBuffers:
         else:
             raise ValueError(kind)
         ptrs = [t.data_ptr() if t is not None else None for t in (self.key, self.m, self.s, self.shat)]
-        self.sc = Scores(*ptrs, self.token_k, self.cand.data_ptr() if self.cand is not None else None, 0)
+        self.sc = Scores(*ptrs, self.token_k, self.cand.data_ptr() if self.cand is not None else None, 0, None, None)
         kind_i = C.c_int32(_KIND[kind])
         self.ws = _workspace(cache, workspace_bytes(cache, OP_SCORE, kind_i))
 
@@ -274,10 +263,12 @@ TOKEN_PHASE_ALL, TOKEN_PHASE_BOUND, TOKEN_PHASE_FILTER = 0, 1, 2
 
 
 def score_pages(cache: PagedCache, meta: PageMeta, q, kind: str, sm_scale=None, out: ScoreBuffers | None = None,
-                token_k: int = 0, stream=None, phase: int = TOKEN_PHASE_ALL, temperature=None) -> ScoreBuffers:
+                token_k: int = 0, stream=None, phase: int = TOKEN_PHASE_ALL, temperature=None,
+                events=None) -> ScoreBuffers:
     """phase (candidate scoring only): TOKEN_PHASE_BOUND / TOKEN_PHASE_FILTER run its two parts
     as separate calls, the bound first. temperature: the soft-LSH temperature ("lsh" only; it
-    travels in the scale argument of the C call)."""
+    travels in the scale argument of the C call). events: a pair from event_pair(), recorded right
+    around the scoring kernel proper."""
     assert q.dtype == cache.dtype and q.is_contiguous() and tuple(q.shape) == (cache.B, cache.Hq, cache.d)
     out = out or ScoreBuffers(cache, kind, token_k)
     if kind == "lsh":
@@ -286,6 +277,7 @@ def score_pages(cache: PagedCache, meta: PageMeta, q, kind: str, sm_scale=None, 
     else:
         scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(cache.d)
     out.sc.token_phase = int(phase)
+    out.sc.ev_begin, out.sc.ev_end = _events(events)
     _check(lib().skv_score_pages(cache.ref, meta.ref, _ptr(q), _KIND[kind], scale, out.ref, _ptr(out.ws),
                                  out.ws.numel(), _stream(stream)), "skv_score_pages")
     return out
@@ -309,7 +301,7 @@ class CombinedScores:
         self.parts = (box, gauss)
         self.key, self.m, self.s, self.shat = box.key, gauss.m, gauss.s, gauss.shat
         self.sc = Scores(box.key.data_ptr(), gauss.m.data_ptr(), gauss.s.data_ptr(), gauss.shat.data_ptr(), 0,
-                         None, 0)
+                         None, 0, None, None)
 
     @property
     def ref(self):
@@ -361,13 +353,15 @@ class AttnBuffers:
 
 def attn_params(cache: PagedCache, alpha=1.0, sm_scale=None, granularity=0, split=0) -> AttnParams:
     scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(cache.d)
-    return AttnParams(float(alpha), scale, int(granularity), int(split))
+    return AttnParams(float(alpha), scale, int(granularity), int(split), None, None)
 
 
 def sparse_decode_attn(cache: PagedCache, q, sel: Selection, alpha=1.0, sm_scale=None, split=0,
-                       out: AttnBuffers | None = None, stream=None):
+                       out: AttnBuffers | None = None, stream=None, events=None):
+    """events: a pair from event_pair(), recorded right around the first attention kernel."""
     assert q.dtype == cache.dtype and q.is_contiguous() and tuple(q.shape) == (cache.B, cache.Hq, cache.d)
     out = out or AttnBuffers(cache, attn_params(cache, alpha, sm_scale, sel.granularity, split), sel.cap)
+    out.p.ev_begin, out.p.ev_end = _events(events)
     _check(lib().skv_sparse_decode_attn(cache.ref, _ptr(q), _ptr(sel.idx), _ptr(sel.count), sel.cap,
                                         C.byref(out.p), _ptr(out.out), _ptr(out.ws), out.ws.numel(),
                                         _stream(stream)), "skv_sparse_decode_attn")

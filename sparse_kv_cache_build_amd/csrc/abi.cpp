@@ -2,10 +2,8 @@
 // Nothing is enqueued unless every argument checks out. See include/skv.h for the contract.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstdint>
-#include <mutex>
 #include <vector>
 
 #include "launch.hpp"
@@ -14,28 +12,6 @@
 namespace {
 
 using skv::CacheView;
-
-// The kernel timer's state: event pairs created at start, filled in launch order.
-struct KernelTimer {
-  std::mutex mu;
-  std::atomic<int> which{0};   // 0: not running
-  int device = -1;
-  int capacity = 0;
-  int used = 0;                // closed pairs
-  bool open = false;           // a start event recorded for the pair `used`
-  std::vector<hipEvent_t> ev;  // 2 * capacity: (before, after) per launch
-};
-KernelTimer g_timer;
-
-void timer_release() {
-  for (hipEvent_t e : g_timer.ev)
-    if (e) (void)hipEventDestroy(e);
-  g_timer.ev.clear();
-  g_timer.capacity = g_timer.used = 0;
-  g_timer.open = false;
-  g_timer.device = -1;
-  g_timer.which.store(0);
-}
 
 constexpr size_t kAlign = 256;
 
@@ -78,6 +54,13 @@ CacheView view(const skv_cache *c) {
 }
 
 skv_status hip_status(hipError_t e) { return e == hipSuccess ? SKV_OK : SKV_ERR_HIP; }
+
+skv::KernelEvents events(void *begin, void *end) {
+  skv::KernelEvents e;
+  e.begin = static_cast<hipEvent_t>(begin);
+  e.end = static_cast<hipEvent_t>(end);
+  return e;
+}
 
 bool rank_ok(int r) { return r == 16 || r == 32 || r == 64; }
 
@@ -147,47 +130,6 @@ int budget_cap(int maxP, int pct) {
 }  // namespace
 
 extern "C" {
-
-skv_status skv_kernel_timer_start(int32_t which, int32_t capacity) {
-  if ((which != SKV_TIMER_SCORE && which != SKV_TIMER_ATTN) || capacity < 1 || capacity > 65536)
-    return SKV_ERR_INVALID_ARG;
-  std::lock_guard<std::mutex> lk(g_timer.mu);
-  if (g_timer.which.load() != 0) return SKV_ERR_INVALID_ARG;
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess) return SKV_ERR_HIP;
-  g_timer.ev.assign(2 * (size_t)capacity, nullptr);
-  for (hipEvent_t &e : g_timer.ev)
-    if (hipEventCreate(&e) != hipSuccess) {
-      e = nullptr;
-      timer_release();
-      return SKV_ERR_HIP;
-    }
-  g_timer.device = dev;
-  g_timer.capacity = capacity;
-  g_timer.used = 0;
-  g_timer.open = false;
-  g_timer.which.store(which);
-  return SKV_OK;
-}
-
-skv_status skv_kernel_timer_stop(int32_t *count, double *total_ms) {
-  if (!count || !total_ms) return SKV_ERR_INVALID_ARG;
-  std::lock_guard<std::mutex> lk(g_timer.mu);
-  if (g_timer.which.load() == 0) return SKV_ERR_INVALID_ARG;
-  double sum = 0.0;
-  skv_status st = SKV_OK;
-  for (int i = 0; i < g_timer.used && st == SKV_OK; ++i) {
-    float ms = 0.0f;
-    if (hipEventSynchronize(g_timer.ev[2 * i + 1]) != hipSuccess ||
-        hipEventElapsedTime(&ms, g_timer.ev[2 * i], g_timer.ev[2 * i + 1]) != hipSuccess)
-      st = SKV_ERR_HIP;
-    sum += ms;
-  }
-  *count = g_timer.used;
-  *total_ms = sum;
-  timer_release();
-  return st;
-}
 
 const char *skv_status_str(skv_status s) {
   switch (s) {
@@ -302,6 +244,7 @@ skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q,
   if (!aligned(q, 16)) return SKV_ERR_INVALID_ARG;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const CacheView v = view(c);
+  const skv::KernelEvents ev = events(out->ev_begin, out->ev_end);
   if (kind == SKV_SCORE_BOX) {
     if (!(m->kinds & SKV_META_BOX) || !m->box || !out->key || !aligned(m->box, 16)) return SKV_ERR_INVALID_ARG;
   } else if (kind == SKV_SCORE_POOL) {
@@ -338,7 +281,7 @@ skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q,
         e = skv::launch_token_bound(v, c->dtype, q, out->token_k, m->proj_rank, m->proj, m->kproj,
                                     static_cast<char *>(out->cand), s);
       if (e == hipSuccess && ph != SKV_TOKEN_PHASE_BOUND)
-        e = skv::launch_score_proj_cand(v, m->proj_rank, m->kproj, static_cast<char *>(out->cand), s);
+        e = skv::launch_score_proj_cand(v, m->proj_rank, m->kproj, static_cast<char *>(out->cand), s, ev);
       return hip_status(e);
     }
     if (!out->key) return SKV_ERR_INVALID_ARG;
@@ -354,17 +297,17 @@ skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q,
   (void)hipGetLastError();
   hipError_t e;
   if (kind == SKV_SCORE_BOX)
-    e = skv::launch_score_box(v, c->dtype, q, m->box, out->key, ws, s);
+    e = skv::launch_score_box(v, c->dtype, q, m->box, out->key, ws, s, ev);
   else if (kind == SKV_SCORE_POOL)
-    e = skv::launch_score_pool(v, c->dtype, q, m->pool_block, m->pool, out->key, ws, s);
+    e = skv::launch_score_pool(v, c->dtype, q, m->pool_block, m->pool, out->key, ws, s, ev);
   else if (kind == SKV_SCORE_LSH)
     e = skv::launch_score_lsh(v, c->dtype, q, m->lsh_tables, m->lsh_bits, m->lsh_planes, sm_scale, m->lsh_bucket,
-                              m->vnorm, out->key, workspace, s);
+                              m->vnorm, out->key, workspace, s, ev);
   else if (kind == SKV_SCORE_GAUSS || kind == SKV_SCORE_GAUSS_Q)
     e = skv::launch_score_gauss(v, c->dtype, q, m->gauss, (double)sm_scale, kind == SKV_SCORE_GAUSS_Q, out->m,
-                                out->s, out->shat, ws, s);
+                                out->s, out->shat, ws, s, ev);
   else
-    e = skv::launch_score_proj(v, c->dtype, q, m->proj_rank, m->proj, m->kproj, out->key, ws, s);
+    e = skv::launch_score_proj(v, c->dtype, q, m->proj_rank, m->proj, m->kproj, out->key, ws, s, ev);
   return hip_status(e);
 }
 
@@ -430,18 +373,20 @@ skv_status skv_select_pages(const skv_cache *c, const skv_scores *sc, const skv_
   }
 }
 
-skv_status skv_sparse_decode_attn(const skv_cache *c, const void *q, const int32_t *sel_idx, const int32_t *sel_count,
-                                  int32_t cap, const skv_attn_params *p, float *out, void *workspace,
-                                  size_t workspace_bytes, void *stream) {
+// Validation and split-K plan shared by both attention entry points.
+static skv_status attn_check(const skv_cache *c, const void *q, const int32_t *sel_idx, const int32_t *sel_count,
+                             int32_t cap, const skv_attn_params *p, float *out, AttnPlan *plan) {
   skv_status st = check_cache(c);
   if (st != SKV_OK) return st;
   if (!q || !sel_idx || !sel_count || !out || cap < 1) return SKV_ERR_INVALID_ARG;
   if (!aligned(q, 16)) return SKV_ERR_INVALID_ARG;
   if ((st = check_attn_params(p)) != SKV_OK) return st;
-  AttnPlan plan;
-  if ((st = attn_plan(c, p, cap, &plan)) != SKV_OK) return st;
-  if (plan.total && (!workspace || workspace_bytes < plan.total || !aligned(workspace, 16))) return SKV_ERR_WORKSPACE;
-  char *ws = static_cast<char *>(workspace);
+  return attn_plan(c, p, cap, plan);
+}
+
+static skv_status attn_launch(const skv_cache *c, const void *q, const int32_t *sel_idx, const int32_t *sel_count,
+                              int32_t cap, const skv_attn_params *p, float *out, char *ws, const AttnPlan &plan,
+                              void *stream) {
   skv::AttnArgs a;
   a.c = view(c);
   a.dtype = c->dtype;
@@ -459,37 +404,19 @@ skv_status skv_sparse_decode_attn(const skv_cache *c, const void *q, const int32
   a.cand = plan.cand ? reinterpret_cast<float2 *>(ws) : nullptr;
   a.cand_cnt = plan.cnt ? reinterpret_cast<int32_t *>(ws + plan.cand) : nullptr;
   a.cand_max = plan.mx ? reinterpret_cast<float *>(ws + plan.cand + plan.cnt) : nullptr;
+  a.ev = events(p->ev_begin, p->ev_end);
   (void)hipGetLastError();
   return hip_status(skv::launch_attn(a, static_cast<hipStream_t>(stream)));
 }
 
-}  // extern "C"
-
-namespace skv {
-
-void timer_mark(int which, int edge, hipStream_t st) {
-  if (g_timer.which.load(std::memory_order_relaxed) != which) return;
-  std::lock_guard<std::mutex> lk(g_timer.mu);
-  if (g_timer.which.load() != which) return;
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev != g_timer.device) {
-    (void)hipGetLastError();
-    return;
-  }
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
-    (void)hipGetLastError();
-    return;
-  }
-  if (edge == 0) {
-    if (g_timer.used >= g_timer.capacity) return;
-    g_timer.open = hipEventRecord(g_timer.ev[2 * g_timer.used], st) == hipSuccess;
-  } else {
-    if (!g_timer.open) return;
-    if (hipEventRecord(g_timer.ev[2 * g_timer.used + 1], st) == hipSuccess) ++g_timer.used;
-    g_timer.open = false;
-  }
-  (void)hipGetLastError();
+skv_status skv_sparse_decode_attn(const skv_cache *c, const void *q, const int32_t *sel_idx, const int32_t *sel_count,
+                                  int32_t cap, const skv_attn_params *p, float *out, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+  AttnPlan plan;
+  skv_status st = attn_check(c, q, sel_idx, sel_count, cap, p, out, &plan);
+  if (st != SKV_OK) return st;
+  if (plan.total && (!workspace || workspace_bytes < plan.total || !aligned(workspace, 16))) return SKV_ERR_WORKSPACE;
+  return attn_launch(c, q, sel_idx, sel_count, cap, p, out, static_cast<char *>(workspace), plan, stream);
 }
 
-}  // namespace skv
+}  // extern "C"

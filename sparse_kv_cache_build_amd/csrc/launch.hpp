@@ -8,6 +8,30 @@
 
 namespace skv {
 
+// Optional caller-owned HIP events, recorded on the launch stream right before and right after one
+// kernel launch, so that their elapsed time is that kernel alone (a measurement aid). Nothing is
+// recorded when either event is null or the stream is being captured into a graph. The library keeps
+// no state of its own for them.
+struct KernelEvents {
+  hipEvent_t begin = nullptr, end = nullptr;
+  bool active(hipStream_t st) const {
+    if (!begin || !end) return false;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+    return cs == hipStreamCaptureStatusNone;
+  }
+  hipError_t before(hipStream_t st) const { return active(st) ? hipEventRecord(begin, st) : hipSuccess; }
+  // the launch status of the kernel just launched, then the closing record
+  hipError_t after(hipStream_t st) const {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return active(st) ? hipEventRecord(end, st) : hipSuccess;
+  }
+};
+
 struct AttnArgs {
   CacheView c;
   int dtype;
@@ -21,37 +45,28 @@ struct AttnArgs {
   float2 *cand;      // entmax (z', slot) pairs [U, G, nsplit, rps]
   int32_t *cand_cnt; // [U, G, nsplit]
   float *cand_max;   // [U, G, nsplit]
+  KernelEvents ev;   // around the first attention kernel
 };
-
-// Kernel timer (a measurement aid, run by skv_kernel_timer_start/stop): records a HIP event on `st`
-// before (edge 0) or after (edge 1) a launch of kernel class `which` while the timer runs for that
-// class; otherwise returns at once. A failed record is cleared so the launch's own status stands.
-enum { kTimerScore = 1, kTimerAttn = 2 };
-void timer_mark(int which, int edge, hipStream_t st);
-
-// The launch status of the kernel just launched, with the timer's closing mark after it.
-inline hipError_t timed_launch_status(int which, hipStream_t st) {
-  const hipError_t e = hipGetLastError();
-  if (e == hipSuccess) timer_mark(which, 1, st);
-  return e;
-}
 
 hipError_t launch_build_meta(const CacheView &c, int dtype, int tail, void *box, float *gauss, int r,
                              const float *proj, uint16_t *kproj, int pb, float *pool, hipStream_t st);
 hipError_t launch_build_lsh(const CacheView &c, int dtype, int tail, int L, int P, const float *planes,
                             uint8_t *bucket, float *vnorm, hipStream_t st);
 hipError_t launch_score_box(const CacheView &c, int dtype, const void *q, const void *box, float *key, double *ws,
-                            hipStream_t st);
+                            hipStream_t st, const KernelEvents &ev);
 hipError_t launch_score_lsh(const CacheView &c, int dtype, const void *q, int L, int P, const float *planes,
                             float tau, const uint8_t *bucket, const float *vnorm, float *key, void *ws,
-                            hipStream_t st);
+                            hipStream_t st, const KernelEvents &ev);
 hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, const float *gauss, double scale,
-                              int quantile, float *m, float *s, float *shat, double *ws, hipStream_t st);
+                              int quantile, float *m, float *s, float *shat, double *ws, hipStream_t st,
+                              const KernelEvents &ev);
 hipError_t launch_score_pool(const CacheView &c, int dtype, const void *q, int pb, const float *pool, float *key,
-                             double *ws, hipStream_t st);
+                             double *ws, hipStream_t st, const KernelEvents &ev);
 hipError_t launch_score_proj(const CacheView &c, int dtype, const void *q, int r, const float *proj,
-                             const uint16_t *kproj, float *key, double *ws, hipStream_t st);
-hipError_t launch_score_proj_cand(const CacheView &c, int r, const uint16_t *kproj, char *cand, hipStream_t st);
+                             const uint16_t *kproj, float *key, double *ws, hipStream_t st,
+                             const KernelEvents &ev);
+hipError_t launch_score_proj_cand(const CacheView &c, int r, const uint16_t *kproj, char *cand, hipStream_t st,
+                                  const KernelEvents &ev);
 hipError_t launch_token_bound(const CacheView &c, int dtype, const void *q, int k, int r, const float *proj,
                               const uint16_t *kproj, char *cand, hipStream_t st);
 hipError_t launch_select_token_cand(const CacheView &c, int k, int r, const char *cand, int32_t *sel_idx,

@@ -582,73 +582,81 @@ static hipError_t qprep_pair(const void *q, int n, int gauss, double *ws, hipStr
   }
 
 template <typename T, int D>
-static hipError_t box_d(const CacheView &c, const void *box, const double *qpm, float *key, hipStream_t st) {
+static hipError_t box_d(const CacheView &c, const void *box, const double *qpm, float *key, hipStream_t st,
+                        const KernelEvents &ev) {
   const dim3 grid((c.maxP + 255) / 256, c.B * c.Hkv);
-  timer_mark(kTimerScore, 0, st);
+  hipError_t e0 = ev.before(st);
+  if (e0 != hipSuccess) return e0;
   SKV_DISPATCH_G(c.G, score_box_kernel<T, D, GG><<<grid, 256, 0, st>>>(c, static_cast<const T *>(box), qpm, key))
-  return timed_launch_status(kTimerScore, st);
+  return ev.after(st);
 }
 
 hipError_t launch_score_box(const CacheView &c, int dtype, const void *q, const void *box, float *key, double *ws,
-                            hipStream_t st) {
+                            hipStream_t st, const KernelEvents &ev) {
   const int n = c.B * c.Hq * c.D;
   hipError_t e = dtype == 0 ? qprep_pair<float>(q, n, 0, ws, st) : qprep_pair<uint16_t>(q, n, 0, ws, st);
   if (e != hipSuccess) return e;
-  if (c.D == 64) return dtype == 0 ? box_d<float, 64>(c, box, ws, key, st) : box_d<uint16_t, 64>(c, box, ws, key, st);
-  return dtype == 0 ? box_d<float, 128>(c, box, ws, key, st) : box_d<uint16_t, 128>(c, box, ws, key, st);
+  if (c.D == 64) return dtype == 0 ? box_d<float, 64>(c, box, ws, key, st, ev) : box_d<uint16_t, 64>(c, box, ws, key, st, ev);
+  return dtype == 0 ? box_d<float, 128>(c, box, ws, key, st, ev) : box_d<uint16_t, 128>(c, box, ws, key, st, ev);
 }
 
 template <int D>
 static hipError_t gauss_d(const CacheView &c, const float *gauss, const double *qpm, double scale, int quantile, float *m, float *s,
-                          float *shat, hipStream_t st) {
+                          float *shat, hipStream_t st, const KernelEvents &ev) {
   const dim3 grid((c.maxP + 255) / 256, c.B * c.Hkv);
-  timer_mark(kTimerScore, 0, st);
+  hipError_t e0 = ev.before(st);
+  if (e0 != hipSuccess) return e0;
   SKV_DISPATCH_G(c.G, score_gauss_kernel<D, GG><<<grid, 256, 0, st>>>(c, gauss, qpm, scale, quantile, m, s, shat))
-  return timed_launch_status(kTimerScore, st);
+  return ev.after(st);
 }
 
 hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, const float *gauss, double scale,
                               int quantile, float *m,
-                              float *s, float *shat, double *ws, hipStream_t st) {
+                              float *s, float *shat, double *ws, hipStream_t st, const KernelEvents &ev) {
   const int n = c.B * c.Hq * c.D;
   hipError_t e = dtype == 0 ? qprep_pair<float>(q, n, 1, ws, st) : qprep_pair<uint16_t>(q, n, 1, ws, st);
   if (e != hipSuccess) return e;
-  return c.D == 64 ? gauss_d<64>(c, gauss, ws, scale, quantile, m, s, shat, st)
-                    : gauss_d<128>(c, gauss, ws, scale, quantile, m, s, shat, st);
+  return c.D == 64 ? gauss_d<64>(c, gauss, ws, scale, quantile, m, s, shat, st, ev)
+                    : gauss_d<128>(c, gauss, ws, scale, quantile, m, s, shat, st, ev);
 }
 
 template <int D>
-static hipError_t pool_d(const CacheView &c, int pb, const float *pool, const double *qpm, float *key, hipStream_t st) {
+static hipError_t pool_d(const CacheView &c, int pb, const float *pool, const double *qpm, float *key, hipStream_t st,
+                         const KernelEvents &ev) {
   int lw = 0;
   while ((1 << lw) < c.S / pb && lw < 6) ++lw;
   const int pages_per_block = 4 * (64 >> lw);
   const dim3 grid((c.maxP + pages_per_block - 1) / pages_per_block, c.B * c.Hkv);
-  timer_mark(kTimerScore, 0, st);
+  hipError_t e0 = ev.before(st);
+  if (e0 != hipSuccess) return e0;
   SKV_DISPATCH_G(c.G, score_pool_kernel<D, GG><<<grid, 256, 0, st>>>(c, pb, lw, pool, qpm, key))
-  return timed_launch_status(kTimerScore, st);
+  return ev.after(st);
 }
 
 hipError_t launch_score_pool(const CacheView &c, int dtype, const void *q, int pb, const float *pool, float *key,
-                             double *ws, hipStream_t st) {
+                             double *ws, hipStream_t st, const KernelEvents &ev) {
   const int n = c.B * c.Hq * c.D;
   hipError_t e = dtype == 0 ? qprep_pair<float>(q, n, 1, ws, st) : qprep_pair<uint16_t>(q, n, 1, ws, st);
   if (e != hipSuccess) return e;
-  return c.D == 64 ? pool_d<64>(c, pb, pool, ws, key, st) : pool_d<128>(c, pb, pool, ws, key, st);
+  return c.D == 64 ? pool_d<64>(c, pb, pool, ws, key, st, ev) : pool_d<128>(c, pb, pool, ws, key, st, ev);
 }
 
 template <int R>
-static hipError_t proj_r(const CacheView &c, const uint16_t *kproj, const double *qt, float *key, hipStream_t st) {
+static hipError_t proj_r(const CacheView &c, const uint16_t *kproj, const double *qt, float *key, hipStream_t st,
+                         const KernelEvents &ev) {
   const dim3 grid((c.maxP * c.S + 256 * kProjTPT - 1) / (256 * kProjTPT), c.B * c.Hkv);
-  timer_mark(kTimerScore, 0, st);
+  hipError_t e0 = ev.before(st);
+  if (e0 != hipSuccess) return e0;
   SKV_DISPATCH_G(c.G, score_proj_kernel<R, GG><<<grid, 256, 0, st>>>(c, kproj, qt, key))
-  return timed_launch_status(kTimerScore, st);
+  return ev.after(st);
 }
 
 template <int R>
 static hipError_t proj_cand_r(const CacheView &c, const uint16_t *kproj, char *cand, const CandLayout &lay,
-                              hipStream_t st) {
+                              hipStream_t st, const KernelEvents &ev) {
   const dim3 grid((lay.nb + 3) / 4, c.B * c.Hkv);
-  timer_mark(kTimerScore, 0, st);
+  hipError_t e0 = ev.before(st);
+  if (e0 != hipSuccess) return e0;
   SKV_DISPATCH_G(c.G, score_proj_cand_kernel<R, GG><<<grid, 256, 0, st>>>(
                           c, kproj, reinterpret_cast<const double *>(cand + lay.qt),
                           reinterpret_cast<const uint32_t *>(cand + lay.qb),
@@ -656,21 +664,23 @@ static hipError_t proj_cand_r(const CacheView &c, const uint16_t *kproj, char *c
                           reinterpret_cast<const uint32_t *>(cand + lay.bound),
                           reinterpret_cast<int32_t *>(cand + lay.count), reinterpret_cast<float2 *>(cand + lay.seg),
                           lay.nb))
-  return timed_launch_status(kTimerScore, st);
+  return ev.after(st);
 }
 
-hipError_t launch_score_proj_cand(const CacheView &c, int r, const uint16_t *kproj, char *cand, hipStream_t st) {
+hipError_t launch_score_proj_cand(const CacheView &c, int r, const uint16_t *kproj, char *cand, hipStream_t st,
+                                  const KernelEvents &ev) {
   const CandLayout lay(c.B, c.Hq, c.Hkv, c.maxP * c.S, 64);   // layout independent of the rank
   switch (r) {
-    case 16: return proj_cand_r<16>(c, kproj, cand, lay, st);
-    case 32: return proj_cand_r<32>(c, kproj, cand, lay, st);
-    case 64: return proj_cand_r<64>(c, kproj, cand, lay, st);
+    case 16: return proj_cand_r<16>(c, kproj, cand, lay, st, ev);
+    case 32: return proj_cand_r<32>(c, kproj, cand, lay, st, ev);
+    case 64: return proj_cand_r<64>(c, kproj, cand, lay, st, ev);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_score_proj(const CacheView &c, int dtype, const void *q, int r, const float *proj,
-                             const uint16_t *kproj, float *key, double *ws, hipStream_t st) {
+                             const uint16_t *kproj, float *key, double *ws, hipStream_t st,
+                             const KernelEvents &ev) {
   const int BH = c.B * c.Hq;
   if (dtype == 0) {
     if (c.D == 64)
@@ -686,16 +696,17 @@ hipError_t launch_score_proj(const CacheView &c, int dtype, const void *q, int r
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (r) {
-    case 16: return proj_r<16>(c, kproj, ws, key, st);
-    case 32: return proj_r<32>(c, kproj, ws, key, st);
-    case 64: return proj_r<64>(c, kproj, ws, key, st);
+    case 16: return proj_r<16>(c, kproj, ws, key, st, ev);
+    case 32: return proj_r<32>(c, kproj, ws, key, st, ev);
+    case 64: return proj_r<64>(c, kproj, ws, key, st, ev);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int D>
 static hipError_t lsh_d(const CacheView &c, int dtype, const void *q, int L, int P, const float *planes, double tau,
-                        const uint8_t *bucket, const float *vnorm, float *key, uint32_t *tab, hipStream_t st) {
+                        const uint8_t *bucket, const float *vnorm, float *key, uint32_t *tab, hipStream_t st,
+                        const KernelEvents &ev) {
   if (dtype == 0)
     lsh_prep_kernel<float, D><<<c.B * c.Hq, 256, 0, st>>>(c, static_cast<const float *>(q), L, P, planes, tau, tab);
   else
@@ -705,17 +716,18 @@ static hipError_t lsh_d(const CacheView &c, int dtype, const void *q, int L, int
   if (e != hipSuccess) return e;
   const dim3 grid((c.maxP * c.S + kLshTok - 1) / kLshTok, c.B * c.Hkv);
   const size_t lds = sizeof(uint32_t) * ((size_t)L << P) * c.G;
-  timer_mark(kTimerScore, 0, st);
+  hipError_t e0 = ev.before(st);
+  if (e0 != hipSuccess) return e0;
   SKV_DISPATCH_G(c.G, score_lsh_kernel<GG><<<grid, 256, lds, st>>>(c, L, P, bucket, vnorm, tab, key))
-  return timed_launch_status(kTimerScore, st);
+  return ev.after(st);
 }
 
 hipError_t launch_score_lsh(const CacheView &c, int dtype, const void *q, int L, int P, const float *planes,
                             float tau, const uint8_t *bucket, const float *vnorm, float *key, void *ws,
-                            hipStream_t st) {
+                            hipStream_t st, const KernelEvents &ev) {
   uint32_t *tab = static_cast<uint32_t *>(ws);
-  return c.D == 64 ? lsh_d<64>(c, dtype, q, L, P, planes, (double)tau, bucket, vnorm, key, tab, st)
-                   : lsh_d<128>(c, dtype, q, L, P, planes, (double)tau, bucket, vnorm, key, tab, st);
+  return c.D == 64 ? lsh_d<64>(c, dtype, q, L, P, planes, (double)tau, bucket, vnorm, key, tab, st, ev)
+                   : lsh_d<128>(c, dtype, q, L, P, planes, (double)tau, bucket, vnorm, key, tab, st, ev);
 }
 
 }  // namespace skv

@@ -2,7 +2,10 @@
 oracle (CPU, raw inputs only) and compares them. Used by the GPU parity tests."""
 from __future__ import annotations
 
+import concurrent.futures as cf
+import json
 import math
+import os
 import sys
 from dataclasses import dataclass, field
 
@@ -24,6 +27,18 @@ TAU_TOL = 1e-4
 def log(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+def record(entry: dict):
+    """Appends one JSON line to the file named by the environment variable SKV_PARITY_RECORD, if
+    set: the per-test parity summary (units compared, certified near-ties with their margins,
+    largest error as a fraction of the tolerance)."""
+    path = os.environ.get("SKV_PARITY_RECORD")
+    if not path:
+        return
+    entry = dict(entry, test=os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0])
+    with open(path, "a") as f:
+        f.write(json.dumps(entry) + "\n")
 
 
 def spec_of(w: W.Workload, alphas=None) -> pipeline.Spec:
@@ -87,6 +102,22 @@ class Report:
     near_ties: int = 0
     max_err: float = 0.0
     notes: list = field(default_factory=list)
+    ties: list = field(default_factory=list)        # certified near-ties: (seq, kv head, indices, margins)
+    tie_units_checked: int = 0                      # near-tie units whose outputs were checked on the GPU's set
+
+    def merge(self, o: "Report"):
+        self.units += o.units
+        self.near_ties += o.near_ties
+        self.max_err = max(self.max_err, o.max_err)
+        self.notes += o.notes
+        self.ties += o.ties
+        self.tie_units_checked += o.tie_units_checked
+
+    def entry(self, w: W.Workload, seqs, **extra) -> dict:
+        return dict(workload=w.name, B=w.B, Hq=w.Hq, Hkv=w.Hkv, d=w.d, S=w.S, max_len=w.max_len,
+                    seqs=None if seqs is None else [int(x) for x in seqs], units=self.units,
+                    near_ties=self.near_ties, tie_units_checked=self.tie_units_checked,
+                    max_err_over_tol=round(self.max_err, 4), ties=self.ties[:50], **extra)
 
 
 def compare(w: W.Workload, st: GpuStep, seqs=None, alphas=None, check_meta=True) -> Report:
@@ -102,6 +133,8 @@ def compare(w: W.Workload, st: GpuStep, seqs=None, alphas=None, check_meta=True)
     G = w.G
     if check_meta and spec.policy != "thresh_box":
         _compare_meta(w, st, c, md, pm, spec)
+    if spec.score == "gauss" or spec.policy == "thresh_box":
+        _compare_gauss_scores(w, st, c, pm, spec, seqs)
     idx = st.sel.idx.cpu().numpy()
     cnt = st.sel.count.cpu().numpy()
     outs = {a: o.cpu().numpy() for a, o in st.outs.items()}
@@ -151,27 +184,177 @@ def compare(w: W.Workload, st: GpuStep, seqs=None, alphas=None, check_meta=True)
                                   - (r.tau_hat.min() - spec.delta))
                     assert np.all(np.abs(margin) <= TAU_TOL * max(1.0, np.abs(r.tau_hat).max())), (b, g, diff, margin)
                     rep.near_ties += len(diff)
+                    rep.ties.append(dict(seq=int(b), kv_head=int(g), indices=[int(x) for x in diff],
+                                         margins=[float(x) for x in np.atleast_1d(margin)]))
             elif not same and slack > 0.0:   # differences only among keys within the slack of the cut
                 kk = np.sort(sc.key[i, g, :c.length(b)].astype(np.float64))[::-1]
                 cut = kk[min(spec.k, len(kk)) - 1]
                 diff = np.setxor1d(got, r.sel)
                 vn = pipeline_vnorm(c, md, i, g)
-                assert np.all(np.abs(sc.key[i, g, diff] - cut) <= 2 * vn[diff] * slack * 2.0 ** -24 + 1e-6 * abs(cut)), \
-                    (b, g, diff)
+                gaps = np.abs(sc.key[i, g, diff] - cut)
+                assert np.all(gaps <= 2 * vn[diff] * slack * 2.0 ** -24 + 1e-6 * abs(cut)), (b, g, diff)
                 rep.near_ties += len(diff)
+                rep.ties.append(dict(seq=int(b), kv_head=int(g), indices=[int(x) for x in diff],
+                                     margins=[float(x) for x in gaps]))
             else:
                 assert same, f"selection mismatch unit ({b},{g}): gpu {got[:10]}.. ({len(got)}) oracle " \
                              f"{r.sel[:10]}.. ({len(r.sel)})"
+            # values: against the oracle's attention over the GPU's own selection (the same set where
+            # the selections agree; where certified near-ties changed it, the GPU's set)
             if not same:
-                continue
+                rep.tie_units_checked += 1
             for a in spec.alphas:
-                ref = pipeline.attend_unit(c, spec, i, g, r.sel, a)
+                ref = pipeline.attend_unit(c, spec, i, g, r.sel if same else got, a)
                 gpu = outs[a][b, g * G:(g + 1) * G]
                 err = np.abs(gpu - ref)
                 rep.max_err = max(rep.max_err, float((err / (ATOL + RTOL * np.abs(ref))).max()))
                 assert np.all(err <= ATOL + RTOL * np.abs(ref)), \
                     f"output mismatch unit ({b},{g}) alpha {a}: max abs err {err.max():.3g}"
     return rep
+
+
+def check(w: W.Workload, st: GpuStep, seqs=None, alphas=None, check_meta=True, **extra) -> Report:
+    """compare() (one sequence per thread when several are given), then the parity record of the
+    test (record())."""
+    if seqs is not None and len(seqs) > 1:
+        rep = compare_seqs(w, st, seqs, alphas=alphas, check_meta=check_meta)
+    else:
+        rep = compare(w, st, seqs=seqs, alphas=alphas, check_meta=check_meta)
+    record(rep.entry(w, seqs, **extra))
+    return rep
+
+
+def compare_seqs(w: W.Workload, st: GpuStep, seqs, alphas=None, check_meta=True, threads=16) -> Report:
+    """compare() of each sequence in `seqs` on its own, in parallel threads (the oracle releases
+    the GIL), merged into one report."""
+    rep = Report()
+    with cf.ThreadPoolExecutor(min(threads, max(1, len(seqs)))) as ex:
+        for r in ex.map(lambda b: compare(w, st, seqs=[b], alphas=alphas, check_meta=check_meta), list(seqs)):
+            rep.merge(r)
+    return rep
+
+
+def _compare_gauss_scores(w, st, c, pm, spec, seqs):
+    """Stage parity of the Gaussian scores: the oracle's m, s and estimated maximum computed from
+    the GPU's own float32 moments of the same pages, element by element. The tolerance is what a
+    float32 accumulation of the d terms could add (d 2^-24 of the sum of absolute terms, with a
+    margin), plus the final rounding to float32."""
+    ga = st.meta.gauss[torch.from_numpy(pm).to(w.k.device)].cpu().numpy().astype(np.float64)
+    mean, var = np.ascontiguousarray(ga[:, :, 0]), np.ascontiguousarray(ga[:, :, 1])
+    scale = pipeline.scale_of(spec, c.d)
+    m, s, shat = oracle.score_gauss(c, mean, var, scale, spec.gauss_max == "quantile")
+    sc = st.scores
+    gm, gs, gh = (t[list(seqs)].cpu().numpy().astype(np.float64) for t in (sc.m, sc.s, sc.shat))
+    q = bf16_to_f64(w.q[list(seqs)])
+    eps = 2.0 * c.d * 2.0 ** -24
+    for i in range(c.B):
+        P = c.pages(i)
+        if P == 0:
+            continue
+        phys = c.block_table[i, :P]
+        n = np.array([c.page_tokens(i, p) for p in range(P)])
+        fac = np.where(n > 1, (shat[i, :, :P] - m[i, :, :P]) / np.where(s[i, :, :P] > 0, s[i, :, :P], 1.0), 0.0)
+        for h in range(c.Hq):
+            g = h // c.G
+            am = scale * (np.abs(mean[phys, g]) @ np.abs(q[i, h]))
+            tol_m = eps * am + 2.0 ** -23 * np.abs(m[i, h, :P]) + 1e-30
+            tol_s = eps * s[i, h, :P] + 1e-30
+            tol_h = tol_m + tol_s * np.abs(fac[h]) + 2.0 ** -23 * np.abs(shat[i, h, :P])
+            for name, got, ref, tol in (("m", gm, m, tol_m), ("s", gs, s, tol_s), ("shat", gh, shat, tol_h)):
+                err = np.abs(got[i, h, :P] - ref[i, h, :P])
+                assert np.all(err <= tol), \
+                    f"gaussian {name} mismatch seq {seqs[i]} head {h}: max err {err.max():.3g} at page {err.argmax()}"
+            assert np.all(np.isnan(gm[i, h, P:c.maxP])), f"gaussian m past the sequence must be NaN ({seqs[i]}, {h})"
+
+
+def stage_parity_box_budget(w: W.Workload, st: GpuStep, seqs, pct: int, threads=16) -> int:
+    """Stage parity of the page scoring and selection on every sequence in `seqs`: the oracle's box
+    keys computed from the GPU's own box metadata (bit-identical bytes) must equal the GPU's keys
+    bit for bit, and the oracle's budget selection over those keys must equal the GPU's selection.
+    Needs no K or V on the host. Returns the number of units compared."""
+    bt = w.block_table.cpu().numpy()
+    key = st.scores.key.cpu().numpy()
+    idx, cnt = st.sel.idx.cpu().numpy(), st.sel.count.cpu().numpy()
+    qb = W.host_arrays_q(w)
+
+    def one(b):
+        P = w.pages(b)
+        if P == 0:
+            assert np.all(cnt[b] == 0), b
+            return w.Hkv
+        box = bf16_to_f64(st.meta.box[torch.from_numpy(bt[b, :P].astype(np.int64)).to(w.k.device)])
+        n_, h_ = box.shape[:2]
+        kmin = np.ascontiguousarray(box[:, :, :, 0].reshape(n_, h_, -1))
+        kmax = np.ascontiguousarray(box[:, :, :, 1].reshape(n_, h_, -1))
+        kdt = np.uint16 if w.dtype == torch.bfloat16 else np.float32
+        dummy = np.zeros((P, w.Hkv, w.S, w.d), dtype=kdt)    # never read by the scoring (zero pages, untouched)
+        c = oracle.Cache(q=qb[b:b + 1], k=dummy, v=dummy, block_table=np.arange(P, dtype=np.int32)[None, :],
+                         seq_lens=np.array([w.lens[b]], dtype=np.int32))
+        ok = oracle.score_box(c, kmin, kmax)
+        for g in range(w.Hkv):
+            assert np.array_equal(ok[0, g, :P], key[b, g, :P]), f"box key mismatch ({b},{g})"
+            ref = oracle.select_topk(ok[0, g, :P], oracle.budget_k(P, pct))
+            got = idx[b, g, :cnt[b, g]]
+            assert len(got) == len(ref) and np.array_equal(got, ref), f"selection mismatch ({b},{g})"
+        return w.Hkv
+
+    with cf.ThreadPoolExecutor(threads) as ex:
+        return sum(ex.map(one, list(seqs)))
+
+
+def full_cache_invariants(w: W.Workload, st: GpuStep, seqs, threads=16) -> dict:
+    """The error bound of the sparse output against the full-cache output ("EntmaxKV" s3): with
+    delta the full-cache weight of the tokens left out of the selection and B the largest value
+    norm of the sequence, |o_full - o_sparse|_2 <= 2 B delta. Checked on the GPU's outputs, with the
+    output tolerance added for the GPU's own rounding; also reports the recall of the full-cache
+    support (tokens with weight > 0) by the selection."""
+    spec = spec_of(w)
+    idx, cnt = st.sel.idx.cpu().numpy(), st.sel.count.cpu().numpy()
+    outs = {a: o.cpu().numpy() for a, o in st.outs.items()}
+    gran = 1 if spec.score in ("proj", "lsh") else 0
+    stats = dict(units=0, max_delta=0.0, min_recall=1.0, max_ratio=0.0)
+
+    def one(b):
+        h = W.host_arrays(w, [b])
+        c = oracle_cache(h)
+        res = []
+        L = c.length(0)
+        t = np.arange(L)
+        for g in range(w.Hkv):
+            sel = idx[b, g, :cnt[b, g]]
+            keep = np.zeros(max(L, c.pages(0) * c.S), dtype=bool)
+            if gran:
+                keep[sel] = True
+            else:
+                for p in sel:
+                    keep[p * c.S:(p + 1) * c.S] = True
+            keep = keep[:L]
+            vb = h["v"][c.block_table[0, t // c.S], g, t % c.S]     # [L, d] raw bytes of the valid rows
+            rows = ((vb.astype(np.uint32) << 16).view(np.float32) if vb.dtype == np.uint16 else vb).astype(np.float64)
+            Bv = float(np.sqrt((rows * rows).sum(1)).max()) if L else 0.0
+            for a in spec.alphas:
+                full, ps = pipeline.full_reference(c, spec, 0, g, a)
+                sparse = pipeline.attend_unit(c, spec, 0, g, sel, a)
+                for hh in range(w.G):
+                    p = ps[hh]
+                    delta = float(p[~keep].sum())
+                    supp = p > 0
+                    recall = float(keep[supp].mean()) if supp.any() else 1.0
+                    tol = np.linalg.norm(ATOL + RTOL * np.abs(sparse[hh]))
+                    gap = float(np.linalg.norm(full[hh] - outs[a][b, g * w.G + hh]))
+                    bound = 2.0 * Bv * delta + tol
+                    assert gap <= bound, (b, g, hh, a, gap, 2.0 * Bv * delta, tol)
+                    res.append((delta, recall, gap / bound if bound > 0 else 0.0))
+        return res
+
+    with cf.ThreadPoolExecutor(min(threads, max(1, len(seqs)))) as ex:
+        for res in ex.map(one, list(seqs)):
+            for delta, recall, ratio in res:
+                stats["units"] += 1
+                stats["max_delta"] = max(stats["max_delta"], delta)
+                stats["min_recall"] = min(stats["min_recall"], recall)
+                stats["max_ratio"] = max(stats["max_ratio"], ratio)
+    return stats
 
 
 def pipeline_vnorm(c, md, i, g):

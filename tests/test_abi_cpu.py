@@ -208,12 +208,40 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
         B.lib()
 
 
-def test_kernel_timer_argument_checks(L):
-    """Refusals that need no device: bad class or capacity, a stop while the timer is not running,
-    null outputs."""
-    n, ms = C.c_int32(-1), C.c_double(-1.0)
-    for which, cap in [(0, 16), (3, 16), (B.TIMER_SCORE, 0), (B.TIMER_ATTN, -1), (B.TIMER_SCORE, 65537)]:
-        assert L.skv_kernel_timer_start(which, cap) == B.SKV_ERR_INVALID_ARG, (which, cap)
-    assert L.skv_kernel_timer_stop(C.byref(n), C.byref(ms)) == B.SKV_ERR_INVALID_ARG
-    assert L.skv_kernel_timer_stop(None, None) == B.SKV_ERR_INVALID_ARG
-    assert n.value == -1 and ms.value == -1.0
+def test_struct_layouts_match_the_header():
+    """The binding's structures carry the fields of the header's, in order (the optional timing
+    events at the end of skv_scores and skv_attn_params)."""
+    text = open(HEADER).read()
+
+    def fields(struct):
+        body = text[text.index("typedef struct " + struct):]
+        body = body[body.index("{") + 1:body.index("} " + struct)]
+        body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+        return [m.group(1) for m in re.finditer(r"(\w+)\s*;", body)]
+
+    for struct, py in [("skv_cache", B.Cache), ("skv_meta", B.Meta), ("skv_scores", B.Scores),
+                       ("skv_select_params", B.SelectParams), ("skv_attn_params", B.AttnParams)]:
+        assert fields(struct) == [f[0] for f in py._fields_], struct
+
+
+def test_library_keeps_no_host_state(L):
+    """The boundary keeps no mutable global state on the host: the shared object defines no
+    writable data symbols of its own. Excluded: the loader's and HIP's registration records, the
+    host handles of the kernels (one object per __global__ function, filled in when the code
+    object is registered and only read afterwards)."""
+    import subprocess
+    out = subprocess.run(["nm", "--defined-only", "-C", B.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    own = []
+    for line in out.splitlines():
+        parts = line.split(maxsplit=2)
+        if len(parts) < 3 or parts[1] not in "BbDd":
+            continue
+        name = parts[2]
+        if name.startswith(("__hip", "_GLOBAL", "_DYNAMIC", "DW.ref.", "__dso", "__TMC", "completed", "_edata",
+                            "__bss", "_end", "__data", "__init_array", "__fini_array", "__do_global", "__frame")):
+            continue
+        if name.startswith("skv::") and name.endswith(")"):   # a kernel's host handle
+            continue
+        own.append(name)
+    assert own == [], own

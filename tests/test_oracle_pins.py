@@ -130,6 +130,19 @@ def test_meta_proj_rounds_float64_sum_to_nearest_bf16(orc):
     assert got[0] == 0x3f80 and got[1] == 0x3f81
 
 
+def test_meta_proj_rounds_once_not_through_float32(orc):
+    # P row [1, 2^-8] on k = (1, 1 + 2^-22): the float64 sum 1 + 2^-8 + 2^-30 lies just above the
+    # midpoint between bf16 1.0 and 1 + 2^-7, so one rounding gives 1 + 2^-7 (0x3f81); through
+    # float32 first it would become the tie 1 + 2^-8 and then 1.0 (0x3f80)
+    q = np.zeros((1, 1, 2), np.float32)
+    k = np.array([1.0, 1.0 + 2 ** -22], np.float32).reshape(1, 1, 1, 2)
+    c = oracle.Cache(q=q, k=k, v=k.copy(), block_table=np.zeros((1, 1), np.int32),
+                     seq_lens=np.array([1], np.int32))
+    P = np.array([[1.0, 2.0 ** -8], [-1.0, -(2.0 ** -8)]], np.float32)
+    got = orc.meta_proj(c, P)[0, 0, 0]
+    assert got[0] == 0x3f81 and got[1] == 0xbf81
+
+
 # ---------------------------------------------------------------- scores
 
 def test_score_box_is_upper_bound_of_true_max_and_tight_for_single_tokens(orc):
@@ -211,6 +224,44 @@ def test_gauss_max_estimate_bounds_expected_page_max(orc):
     for n in (2, 16, 32, 64):
         draws = rng.standard_normal((20000, n)).max(1).mean()
         assert draws <= math.sqrt(2 * math.log(n))
+
+
+def test_gauss_max_factor_of_the_oracle_is_the_chernoff_bound_on_the_expected_maximum(orc):
+    """The oracle's estimated page maximum, read back as the factor f = (shat - m) / s of pages
+    holding n = 1 .. 64 valid tokens, against what fixes it without its formula:
+      - the moment-generating-function bound on the expected maximum of n standard normals,
+        E[max] <= min over lam > 0 of (ln n) / lam + lam / 2, minimised numerically by scipy;
+      - Monte Carlo: f lies above the mean maximum of n draws (it bounds it) and by less than
+        0.65 (the bound's slack for n <= 64; sqrt(ln n) falls below the mean, sqrt(2 log2 n)
+        and 2 ln n above the slack);
+      - n = 1: shat = m.
+    A page's valid-token count, not the page size, is n (partial last pages)."""
+    import scipy.optimize
+    rng = _rng(31)
+    S, d = 64, 16
+    lens = (64 * 3 + 1, 64 * 2 + 2, 64 + 3, 5, 16, 33, 64 + 17)
+    c = _f32_cache(rng, B=len(lens), Hq=2, Hkv=1, d=d, S=S, lens=lens)
+    mean, var = orc.meta_gauss(c)
+    m, s, shat = orc.score_gauss(c, mean, var, 0.3)
+    seen = {}
+    for b in range(c.B):
+        for p in range(c.pages(b)):
+            n = c.page_tokens(b, p)
+            for h in range(c.Hq):
+                if n == 1:
+                    assert shat[b, h, p] == m[b, h, p]
+                else:
+                    assert s[b, h, p] > 0
+                    seen.setdefault(n, []).append((shat[b, h, p] - m[b, h, p]) / s[b, h, p])
+    assert {2, 3, 5, 16, 17, 33, 64} <= set(seen)
+    for n, fs in seen.items():
+        f = fs[0]
+        assert np.allclose(fs, f, rtol=1e-12, atol=0)
+        res = scipy.optimize.minimize_scalar(lambda lam: math.log(n) / lam + lam / 2, bounds=(1e-3, 50.0),
+                                             method="bounded", options=dict(xatol=1e-12))
+        assert f == pytest.approx(res.fun, rel=1e-6), (n, f, res.fun)
+        mc = rng.standard_normal((200000, n)).max(1).mean()
+        assert mc - 0.01 <= f <= mc + 0.65, (n, f, mc)
 
 
 def _seq_dot(a, b):
@@ -463,11 +514,15 @@ def test_select_thresh_box_is_the_box_test_and_covers_the_per_head_test(orc):
     for p in range(c.pages(0)):
         lo, hi = kmin[c.block_table[0, p], 0].astype(np.float64), kmax[c.block_table[0, p], 0].astype(np.float64)
         U[:, p] = np.maximum(q * lo, q * hi).sum(1)
-    taus = np.array([0.4, 0.9, 0.7, 1.3])
     scale, alpha, delta = 0.25, 1.5, 0.1
+    v = (alpha - 1) * scale * key
+    lo_v, hi_v = np.quantile(v, [0.2, 0.8])
+    taus = np.array([lo_v, hi_v, 0.5 * (lo_v + hi_v), hi_v + 0.1]) + delta   # cuts inside the keys' spread
     got = orc.select_thresh_box(key, taus, scale, alpha, delta)
-    want = np.nonzero((alpha - 1) * scale * key > taus.min() - delta)[0]
+    want = np.nonzero(v > taus.min() - delta)[0]
     assert np.array_equal(got, want)
+    assert 0 < len(got) < c.pages(0)
+    assert len(got) > len(np.nonzero(v > taus.max() - delta)[0])   # the lowest threshold decides
     per_head = np.nonzero(((alpha - 1) * scale * U > (taus - delta)[:, None]).any(0))[0]
     assert set(per_head) <= set(got)
     assert np.allclose(key, U.max(0), rtol=1e-6)

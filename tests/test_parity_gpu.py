@@ -25,8 +25,18 @@ SMALL = {
     "socket128k": dict(B=2, lens=[5000, 3001], k=512),
 }
 
-FULL_SAMPLE = {"tiny": None, "gqa32k": [0, 5], "long_gauss": [1], "token128k": [3], "ragged": "ends",
-               "pool32k": [6], "socket128k": [2]}
+# Sequences the oracle checks end to end at full size (None: every sequence). ragged: eight seeded
+# sequences, the shortest and the longest among them; its selection is checked on all 64 by stage
+# parity (test_ragged_full_stage_parity_all_sequences).
+FULL_SAMPLE = {"tiny": None, "gqa32k": None, "long_gauss": None, "token128k": [0, 5, 10, 15], "ragged": "seeded8",
+               "pool32k": None, "socket128k": [2]}
+
+
+def ragged_sample(w) -> list:
+    order = np.argsort(w.lens)
+    rest = [int(x) for x in order[1:-1]]
+    pick = np.random.default_rng(1005).choice(len(rest), 6, replace=False)
+    return sorted([int(order[0]), int(order[-1])] + [rest[i] for i in pick])
 
 
 @pytest.fixture(scope="module")
@@ -40,7 +50,7 @@ def test_small_parity(dev, name):
     H.log(f"[parity small] {name} {SMALL[name]}")
     w = W.make(name, device=dev, **SMALL[name])
     st = H.gpu_step(w)
-    rep = H.compare(w, st)
+    rep = H.check(w, st)
     H.log(f"  units={rep.units} near_ties={rep.near_ties} max_err/tol={rep.max_err:.3f}")
 
 
@@ -52,7 +62,7 @@ def test_pooled_key_block_sizes(dev, over):
     H.log(f"[parity pool] {over}")
     w = W.make("pool32k", device=dev, **{**SMALL["pool32k"], **over})
     st = H.gpu_step(w)
-    H.compare(w, st)
+    H.check(w, st)
 
 
 @pytest.mark.parametrize("over", [
@@ -70,7 +80,7 @@ def test_soft_lsh_variants(dev, over):
     H.log(f"[parity lsh] {over}")
     w = W.make("socket128k", device=dev, **{**SMALL["socket128k"], **over})
     st = H.gpu_step(w)
-    H.compare(w, st)
+    H.check(w, st)
 
 
 @pytest.mark.parametrize("name,split", [("gqa32k", 1), ("gqa32k", 3), ("token128k", 7), ("ragged", 1),
@@ -79,7 +89,7 @@ def test_explicit_splits_match_oracle(dev, name, split):
     H.log(f"[parity split] {name} split={split}")
     w = W.make(name, device=dev, **SMALL[name])
     st = H.gpu_step(w, split=split)
-    H.compare(w, st, check_meta=False)
+    H.check(w, st, check_meta=False)
 
 
 @pytest.mark.parametrize("name,alphas", [("gqa32k", (1.0, 1.5, 2.0, 1.25)), ("tiny", (1.0, 1.5, 2.0)),
@@ -88,7 +98,7 @@ def test_alphas_over_selection(dev, name, alphas):
     H.log(f"[parity alphas] {name} {alphas}")
     w = W.make(name, device=dev, **SMALL[name])
     st = H.gpu_step(w, alphas=alphas)
-    H.compare(w, st, alphas=alphas, check_meta=False)
+    H.check(w, st, alphas=alphas, check_meta=False)
 
 
 @pytest.mark.parametrize("name", ["gqa32k", "ragged", "token128k"])
@@ -99,7 +109,7 @@ def test_full_cache_comparator(dev, name, alpha):
     w = W.make(name, device=dev, **SMALL[name])
     w.cfg = dict(w.cfg, policy="all")
     st = H.gpu_step(w, alphas=(alpha,))
-    H.compare(w, st, alphas=(alpha,), check_meta=False)
+    H.check(w, st, alphas=(alpha,), check_meta=False)
 
 
 @pytest.mark.parametrize("name,over", [("gqa32k", dict(Hq=16, Hkv=8)), ("gqa32k", dict(Hq=64, Hkv=8, d=64)),
@@ -115,7 +125,7 @@ def test_page_keys_over_groups(dev, name, over):
     H.log(f"[parity groups] {name} {over}")
     w = W.make(name, device=dev, **{**SMALL[name], **over})
     st = H.gpu_step(w)
-    H.compare(w, st)
+    H.check(w, st)
 
 
 @pytest.mark.parametrize("over", [dict(proj_rank=16, Hq=8, Hkv=8), dict(proj_rank=64, Hq=16, Hkv=8),
@@ -130,7 +140,7 @@ def test_projected_ranks_and_groups(dev, over, fused):
     st = H.gpu_step(w, fused=fused)
     if fused:
         assert st.scores.key is None
-    H.compare(w, st)
+    H.check(w, st)
 
 
 @pytest.mark.parametrize("lens", [[600, 700], [2000, 3100]])
@@ -144,7 +154,7 @@ def test_entmax_many_survivors(dev, lens, alpha):
     w.k.mul_(1e-3)
     w.cfg = dict(w.cfg, policy="all")
     st = H.gpu_step(w, alphas=(alpha,))
-    H.compare(w, st, alphas=(alpha,), check_meta=False)
+    H.check(w, st, alphas=(alpha,), check_meta=False)
 
 
 @pytest.mark.parametrize("over", [dict(B=2, L=20000, k=512), dict(B=2, L=5000, k=512),
@@ -158,7 +168,7 @@ def test_fused_token_topk_matches_oracle(dev, over):
     w = W.make("token128k", device=dev, **over)
     st = H.gpu_step(w, fused=True)
     assert st.scores.key is None
-    H.compare(w, st)
+    H.check(w, st)
 
 
 def test_fused_token_topk_falls_back_when_the_sample_misleads(dev):
@@ -174,7 +184,7 @@ def test_fused_token_topk_falls_back_when_the_sample_misleads(dev):
         for t in pos:
             w.k[int(w.block_table[b, t // w.S]), :, t % w.S, :] = 0
     st = H.gpu_step(w, fused=True)
-    H.compare(w, st)
+    H.check(w, st)
 
 
 def test_fused_token_topk_keeps_tokens_the_estimate_undercounts(dev):
@@ -204,7 +214,7 @@ def test_fused_token_topk_keeps_tokens_the_estimate_undercounts(dev):
             row[:, :16] = x
             row[:, 16:R] = -x
     st = H.gpu_step(w, fused=True)
-    H.compare(w, st)
+    H.check(w, st)
     idx, cnt = st.sel.idx.cpu().numpy(), st.sel.count.cpu().numpy()
     for b in range(w.B):
         pos, xv = traps[b]
@@ -233,7 +243,7 @@ def test_threshold_variants_match_oracle(dev, over, shrink):
                 ph = int(w.block_table[b, p])
                 w.k[ph] = (w.k[ph].float() * 0.05).to(w.k.dtype)
     st = H.gpu_step(w)
-    rep = H.compare(w, st)
+    rep = H.check(w, st)
     cnt = st.sel.count.cpu().numpy()
     assert cnt.min() > 0 and cnt.max() < w.pages(0), cnt   # the case selects a proper subset
     H.log(f"  units={rep.units} near_ties={rep.near_ties} max_err/tol={rep.max_err:.3f} counts={cnt.ravel()}")
@@ -245,11 +255,11 @@ def test_k_at_least_pages_and_tokens_selects_all(dev):
     st = H.gpu_step(w)
     cnt = st.sel.count.cpu().numpy()
     assert np.array_equal(cnt, np.array([[44] * 8, [3] * 8]))
-    H.compare(w, st)
+    H.check(w, st)
     w2 = W.make("token128k", device=dev, B=2, lens=[600, 1500], k=1000)
     st2 = H.gpu_step(w2)
     assert np.array_equal(st2.sel.count.cpu().numpy(), np.array([[600] * 8, [1000] * 8]))
-    H.compare(w2, st2)
+    H.check(w2, st2)
 
 
 def test_empty_sequence_gives_zero_output_and_no_selection(dev):
@@ -260,7 +270,7 @@ def test_empty_sequence_gives_zero_output_and_no_selection(dev):
         assert np.all(st.sel.count.cpu().numpy()[0] == 0), name
         for o in st.outs.values():
             assert torch.all(o[0] == 0).item(), name
-        H.compare(w, st)
+        H.check(w, st)
 
 
 def test_determinism(dev):
@@ -283,11 +293,41 @@ def test_full_size_sampled(dev, name):
     w = W.make(name, device=dev)
     st = H.gpu_step(w, fused=True)   # the benchmark's configuration (fused for token top-k)
     seqs = FULL_SAMPLE[name]
-    if seqs == "ends":
-        order = np.argsort(w.lens)
-        seqs = [int(order[0]), int(order[-1])]
-    rep = H.compare(w, st, seqs=seqs)
+    if seqs == "seeded8":
+        seqs = ragged_sample(w)
+    rep = H.check(w, st, seqs=seqs)
     H.log(f"  sampled seqs={seqs} units={rep.units} near_ties={rep.near_ties} max_err/tol={rep.max_err:.3f}")
+    del st, w
+    torch.cuda.empty_cache()
+
+
+def test_ragged_full_stage_parity_all_sequences(dev):
+    """All 64 sequences of the ragged workload at full size: the oracle's box keys from the GPU's own
+    box metadata equal the GPU keys bit for bit, and the oracle's 5 % budget selection over them
+    equals the GPU's selection (the end-to-end check from raw inputs covers eight sequences)."""
+    H.log("[stage parity] ragged, all 64 sequences")
+    w = W.make("ragged", device=dev)
+    st = H.gpu_step(w)
+    n = H.stage_parity_box_budget(w, st, range(w.B), w.cfg["pct"])
+    assert n == w.B * w.Hkv
+    H.record(dict(workload="ragged", kind="stage parity: box keys and budget selection", seqs=w.B, units=n))
+    H.log(f"  units={n}")
+    del st, w
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,seqs", [("ragged", "seeded8"), ("long_gauss", None), ("gqa32k", None)])
+def test_full_size_error_bound(dev, name, seqs):
+    """At full size, the GPU's sparse outputs against the oracle's full-cache outputs: within 2 B delta
+    ("EntmaxKV" s3), delta the full-cache weight of the tokens the selection leaves out, B the largest
+    value norm, plus the output tolerance. Reports the support recall and the largest delta."""
+    H.log(f"[error bound full size] {name}")
+    w = W.make(name, device=dev)
+    st = H.gpu_step(w)
+    seqs = ragged_sample(w) if seqs == "seeded8" else list(range(w.B))
+    stats = H.full_cache_invariants(w, st, seqs)
+    H.record(dict(workload=name, kind="full-cache error bound", seqs=seqs, **stats))
+    H.log(f"  {stats}")
     del st, w
     torch.cuda.empty_cache()
 

@@ -1,7 +1,8 @@
-"""The kernel timer of the C ABI (skv_kernel_timer_start/stop), a measurement aid: HIP events the
-library records on the launch stream right around each launch of the scoring kernel or the first
-attention kernel. It must time every call up to its capacity, stay within the time of the whole
-calls, and leave results bit-identical."""
+"""Timing events of the C ABI, a measurement aid: a caller-owned HIP event pair given to
+skv_score_pages (skv_scores.ev_begin / ev_end) or skv_sparse_decode_attn (skv_attn_params) is
+recorded on the launch stream right around the scoring kernel proper or the first attention
+kernel. The pair must time that one launch, stay within the time of the whole call, and leave the
+results bit-identical; calls without events record nothing."""
 import numpy as np
 import pytest
 import torch
@@ -26,43 +27,43 @@ def _outputs(sc: skv.ScoreBuffers):
 
 
 @pytest.mark.parametrize("name", list(CASES))
-def test_kernel_timer_times_each_scorer_launch(name):
-    H.log(f"[kernel timer score] {name} {CASES[name]}")
+def test_events_time_each_scorer_launch(name):
+    H.log(f"[kernel events score] {name} {CASES[name]}")
     w = W.make(name, device=torch.device("cuda:0"), **CASES[name])
     st = H.gpu_step(w)
     kind, tau = w.cfg["score"], w.cfg.get("lsh_tau")
     before = _outputs(st.scores)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n = 5
-    with skv.KernelTimer("score", capacity=16) as kt:
-        a.record()
-        for _ in range(n):
-            skv.score_pages(st.cache, st.meta, w.q, kind, out=st.scores, temperature=tau)
-        b.record()
-        torch.cuda.synchronize()
-    assert kt.count == n
-    assert 0.0 < kt.total_ms <= a.elapsed_time(b)
+    pairs = [skv.event_pair() for _ in range(5)]
+    torch.cuda.synchronize()
+    a.record()
+    for ev in pairs:
+        skv.score_pages(st.cache, st.meta, w.q, kind, out=st.scores, temperature=tau, events=ev)
+    b.record()
+    torch.cuda.synchronize()
+    times = [x.elapsed_time(y) for x, y in pairs]
+    assert all(t > 0.0 for t in times), times
+    assert sum(times) <= a.elapsed_time(b)
     for x, y in zip(before, _outputs(st.scores)):
         assert np.array_equal(x, y, equal_nan=True)
 
 
-def test_kernel_timer_capacity_and_classes():
-    """Launches past the capacity are not timed; the attention class ignores scoring calls and
-    times the attention kernel; a second start while running is refused."""
-    H.log("[kernel timer attn] token128k")
+def test_events_of_attention_and_calls_without_events():
+    """The attention pair times the first attention kernel; a later call without events leaves a
+    pair as it was; results are unchanged."""
+    H.log("[kernel events attn] token128k")
     w = W.make("token128k", device=torch.device("cuda:0"), **CASES["token128k"])
     st = H.gpu_step(w)
-    with skv.KernelTimer("score", capacity=2) as kt:
-        for _ in range(4):
-            skv.score_pages(st.cache, st.meta, w.q, "proj", out=st.scores)
-        with pytest.raises(skv.SkvError):
-            skv.KernelTimer("attn").__enter__()
-    assert kt.count == 2 and kt.total_ms > 0.0
     ref = st.outs[1.0].clone()
-    with skv.KernelTimer("attn", capacity=8) as kt:
+    ev = skv.event_pair()
+    torch.cuda.synchronize()
+    out = skv.sparse_decode_attn(st.cache, w.q, st.sel, alpha=1.0, events=ev)
+    torch.cuda.synchronize()
+    t0 = ev[0].elapsed_time(ev[1])
+    assert t0 > 0.0 and torch.equal(out, ref)
+    for _ in range(3):
+        out = skv.sparse_decode_attn(st.cache, w.q, st.sel, alpha=1.0)
         skv.score_pages(st.cache, st.meta, w.q, "proj", out=st.scores)
-        for _ in range(3):
-            out = skv.sparse_decode_attn(st.cache, w.q, st.sel, alpha=1.0)
-        torch.cuda.synchronize()
-    assert kt.count == 3 and kt.total_ms > 0.0
+    torch.cuda.synchronize()
+    assert ev[0].elapsed_time(ev[1]) == t0
     assert torch.equal(out, ref)

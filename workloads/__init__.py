@@ -165,20 +165,26 @@ def _outliers_and_drift(w: Workload, cfg, gen, dev, owner, pages):
     B, Hkv, d = w.B, w.Hkv, w.d
     rho, sd = float(cfg["drift_rho"]), float(cfg["drift_sd"])
     maxP = w.maxP
-    mu = torch.empty((B, Hkv, maxP, d), dtype=torch.float32, device=dev)
-    cur = sd * torch.randn((B, Hkv, d), generator=gen, device=dev)
+    cur = (sd * torch.randn((B, Hkv, d), generator=gen, device=dev)).cpu().numpy()
     innov = sd * math.sqrt(1.0 - rho * rho)
-    eps = torch.randn((maxP, B, Hkv, d), generator=gen, device=dev)
+    eps = torch.randn((maxP, B, Hkv, d), generator=gen, device=dev).cpu().numpy()
+    # The recursion runs on the host in float32 with the same operations as elementwise device
+    # arithmetic would (rho * cur and innov * eps rounded to float32, then their float32 sum),
+    # and the whole drift goes to the device in one copy: a per-page loop of device operations
+    # would issue several thousand tiny dispatches.
+    rho32, innov32 = np.float32(rho), np.float32(innov)
+    mu_h = np.empty((B, Hkv, maxP, d), dtype=np.float32)
     for p in range(maxP):
         if p:
-            cur = rho * cur + innov * eps[p]
-        mu[:, :, p] = cur
-    scale = torch.ones((B, Hkv, d), dtype=torch.float32, device=dev)
+            cur = rho32 * cur + innov32 * eps[p]
+        mu_h[:, :, p] = cur
+    mu = torch.from_numpy(mu_h).to(dev)
     nch = int(cfg["outlier_channels"])
-    for b in range(B):
-        for g in range(Hkv):
-            ch = torch.randperm(d, generator=gen, device=dev)[:nch]
-            scale[b, g, ch] = float(cfg["outlier_scale"])
+    # one permutation of the channels per (b, KV head), drawn in order, applied in one scatter
+    chans = torch.stack([torch.randperm(d, generator=gen, device=dev)[:nch] for _ in range(B * Hkv)])
+    scale = torch.ones((B * Hkv, d), dtype=torch.float32, device=dev)
+    scale.scatter_(1, chans, float(cfg["outlier_scale"]))
+    scale = scale.view(B, Hkv, d)
     # physical page -> its (b, p): add the drift and scale, chunk by chunk
     chunk = max(1, (1 << 24) // (Hkv * w.S * d))
     for i in range(0, w.Nphys, chunk):
@@ -215,6 +221,11 @@ def _bits(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
     return t.cpu().numpy().astype(np.float32, copy=False)
+
+
+def host_arrays_q(w: Workload) -> np.ndarray:
+    """Exact host bytes of the queries alone, [B, Hq, d]."""
+    return _bits(w.q)
 
 
 def host_arrays(w: Workload, seqs=None):
