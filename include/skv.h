@@ -282,6 +282,22 @@ skv_status skv_sparse_decode_attn(const skv_cache *c, const void *q, const int32
                                   const int32_t *sel_count, int32_t cap, const skv_attn_params *p, float *out,
                                   void *workspace, size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): skv_sparse_decode_attn without a workspace argument. Its
+ * workspace is a fixed device array inside the library, SKV_NOALLOC_SCRATCH_BYTES (64 MiB) on every
+ * GPU the library runs on, held until the process ends; the first call on a device looks up that
+ * device's copy. The call allocates nothing; the caller still passes every input and the output.
+ * Results equal skv_sparse_decode_attn's bit for bit (same kernels, same plan).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (concurrent streams
+ * or threads) race and must not be issued. Nothing needs clearing between calls.
+ * Errors: as skv_sparse_decode_attn, and SKV_ERR_WORKSPACE when the call needs more workspace than
+ * SKV_NOALLOC_SCRATCH_BYTES (skv_workspace_bytes(c, SKV_OP_ATTN, p, cap) says how much: large
+ * entmax selections, whose candidate lists are sized for every selected row, can exceed it). */
+#define SKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+skv_status skv_sparse_decode_attn_noalloc(const skv_cache *c, const void *q, const int32_t *sel_idx,
+                                          const int32_t *sel_count, int32_t cap, const skv_attn_params *p,
+                                          float *out, void *stream);
+
 /* ------------------------------------------------------------------ utilities */
 
 enum { SKV_OP_SCORE = 0, SKV_OP_SELECT = 1, SKV_OP_ATTN = 2, SKV_OP_CANDIDATES = 3 };

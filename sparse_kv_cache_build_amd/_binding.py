@@ -25,7 +25,8 @@ SEL_TOPK, SEL_BUDGET, SEL_THRESH_GAUSS, SEL_TOKEN_TOPK, SEL_ALL, SEL_THRESH_BOX 
 OP_SCORE, OP_SELECT, OP_ATTN, OP_CANDIDATES = 0, 1, 2, 3
 
 EXPORTS = ("skv_build_page_meta", "skv_append_page_meta", "skv_score_pages", "skv_select_pages",
-           "skv_sparse_decode_attn", "skv_workspace_bytes", "skv_status_str")
+           "skv_sparse_decode_attn", "skv_sparse_decode_attn_noalloc", "skv_workspace_bytes", "skv_status_str")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class SkvError(RuntimeError):
@@ -80,6 +81,7 @@ def lib():
         L.skv_score_pages.argtypes = [P, P, P, I, F, P, P, S, P]
         L.skv_select_pages.argtypes = [P, P, P, P, P, I, P, P, S, P]
         L.skv_sparse_decode_attn.argtypes = [P, P, P, P, I, P, P, P, S, P]
+        L.skv_sparse_decode_attn_noalloc.argtypes = [P, P, P, P, I, P, P, P]
         L.skv_workspace_bytes.argtypes = [P, I, P, I, C.POINTER(C.c_size_t)]
         L.skv_status_str.argtypes = [I]
         L.skv_status_str.restype = C.c_char_p
@@ -366,3 +368,18 @@ def sparse_decode_attn(cache: PagedCache, q, sel: Selection, alpha=1.0, sm_scale
                                         C.byref(out.p), _ptr(out.out), _ptr(out.ws), out.ws.numel(),
                                         _stream(stream)), "skv_sparse_decode_attn")
     return out.out
+
+
+def sparse_decode_attn_noalloc(cache: PagedCache, q, sel: Selection, out, alpha=1.0, sm_scale=None, split=0,
+                               stream=None):
+    """skv_sparse_decode_attn_noalloc: the same attention with the library's fixed device scratch as
+    its workspace (nothing allocated). `out` is a caller-owned float32 [B, Hq, d] tensor. Calls that
+    overlap on one GPU race."""
+    assert q.dtype == cache.dtype and q.is_contiguous() and tuple(q.shape) == (cache.B, cache.Hq, cache.d)
+    assert out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (cache.B, cache.Hq, cache.d)
+    p = attn_params(cache, alpha, sm_scale, sel.granularity, split)
+    _check(lib().skv_sparse_decode_attn_noalloc(cache.ref, _ptr(q), _ptr(sel.idx), _ptr(sel.count), sel.cap,
+                                                C.byref(p), _ptr(out), _stream(stream)),
+           "skv_sparse_decode_attn_noalloc")
+    return out
+

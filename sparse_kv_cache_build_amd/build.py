@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libskv.so")
-SOURCES = ["meta.hip", "score.hip", "select.hip", "attn.hip", "abi.cpp"]
+SOURCES = ["meta.hip", "score.hip", "select.hip", "attn.hip", "noalloc.hip", "abi.cpp"]
 ARCH = os.environ.get("SKV_OFFLOAD_ARCH", "gfx950")
 
 

@@ -419,4 +419,19 @@ skv_status skv_sparse_decode_attn(const skv_cache *c, const void *q, const int32
   return attn_launch(c, q, sel_idx, sel_count, cap, p, out, static_cast<char *>(workspace), plan, stream);
 }
 
+skv_status skv_sparse_decode_attn_noalloc(const skv_cache *c, const void *q, const int32_t *sel_idx,
+                                          const int32_t *sel_count, int32_t cap, const skv_attn_params *p,
+                                          float *out, void *stream) {
+  AttnPlan plan;
+  skv_status st = attn_check(c, q, sel_idx, sel_count, cap, p, out, &plan);
+  if (st != SKV_OK) return st;
+  if (plan.total > skv::kScratchBytes) return SKV_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if (plan.total && skv::scratch_address(&ws) != hipSuccess) {
+    (void)hipGetLastError();
+    return SKV_ERR_HIP;
+  }
+  return attn_launch(c, q, sel_idx, sel_count, cap, p, out, static_cast<char *>(ws), plan, stream);
+}
+
 }  // extern "C"

@@ -86,4 +86,9 @@ hipError_t launch_select_thresh(const CacheView &c, const float *m, const float 
                                 float delta, float *tau, int32_t *sel_idx, int32_t *sel_count, int cap, hipStream_t st);
 hipError_t launch_attn(const AttnArgs &a, hipStream_t st);
 
+// The fixed device scratch of skv_sparse_decode_attn_noalloc (noalloc.hip): kScratchBytes on each
+// device; scratch_address gives its device address on the current device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+hipError_t scratch_address(void **ptr);
+
 }  // namespace skv

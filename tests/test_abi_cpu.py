@@ -228,7 +228,9 @@ def test_library_keeps_no_host_state(L):
     """The boundary keeps no mutable global state on the host: the shared object defines no
     writable data symbols of its own. Excluded: the loader's and HIP's registration records, the
     host handles of the kernels (one object per __global__ function, filled in when the code
-    object is registered and only read afterwards)."""
+    object is registered and only read afterwards), and the one documented exception, the
+    fixed device scratch of skv_sparse_decode_attn_noalloc: its host-side stand-in and the table of
+    its device addresses (written once per device on the first call there)."""
     import subprocess
     out = subprocess.run(["nm", "--defined-only", "-C", B.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
@@ -243,5 +245,27 @@ def test_library_keeps_no_host_state(L):
             continue
         if name.startswith("skv::") and name.endswith(")"):   # a kernel's host handle
             continue
+        if name in ("skv::(anonymous namespace)::scratch", "skv::(anonymous namespace)::g_scratch_addr"):
+            continue
         own.append(name)
     assert own == [], own
+
+
+def test_noalloc_attention_rejects_before_touching_the_device(L):
+    """skv_sparse_decode_attn_noalloc validates like skv_sparse_decode_attn and refuses a call whose
+    workspace would exceed its fixed scratch (SKV_ERR_WORKSPACE), all before any device access."""
+    c = cache()
+    p = B.AttnParams(1.0, 0.088, 0, 0)
+    f = C.c_void_p(FAKE)
+    assert L.skv_sparse_decode_attn_noalloc(C.byref(c), None, f, f, 64, C.byref(p), f, None) == B.SKV_ERR_INVALID_ARG
+    assert L.skv_sparse_decode_attn_noalloc(C.byref(c), f, f, f, 0, C.byref(p), f, None) == B.SKV_ERR_INVALID_ARG
+    bad = B.AttnParams(0.5, 0.088, 0, 0)
+    assert L.skv_sparse_decode_attn_noalloc(C.byref(c), f, f, f, 64, C.byref(bad), f, None) == B.SKV_ERR_INVALID_ARG
+    # entmax over 4096 pages of 32 tokens for 32 units: candidate lists of about 134 MB
+    big = cache(batch=4, page_size=32, max_pages=4096, num_phys_pages=16384)
+    pe = B.AttnParams(1.5, 0.088, 0, 0)
+    n = C.c_size_t(0)
+    assert L.skv_workspace_bytes(C.byref(big), B.OP_ATTN, C.byref(pe), 4096, C.byref(n)) == B.SKV_OK
+    assert n.value > B.NOALLOC_SCRATCH_BYTES
+    assert L.skv_sparse_decode_attn_noalloc(C.byref(big), f, f, f, 4096, C.byref(pe), f, None) == B.SKV_ERR_WORKSPACE
+
