@@ -175,7 +175,9 @@ enum { SKV_TOKEN_PHASE_ALL = 0, SKV_TOKEN_PHASE_BOUND = 1, SKV_TOKEN_PHASE_FILTE
  *          U_h(p) = sum_j max(q_hj k_min_j, q_hj k_max_j)), the upper bound of q_h . k over the
  *          page's box; float64 sum over j ascending (products are exact), unscaled.
  *   GAUSS: per query head, m = sm_scale sum_j q_j mean_j, s = sm_scale sqrt(sum_j q_j^2 var_j),
- *          shat = m + s sqrt(2 ln n_p) (n_p valid tokens of the page; shat = m for n_p = 1).
+ *          shat = m + s sqrt(2 ln n_p) (n_p valid tokens of the page; shat = m for n_p = 1). The
+ *          sums run in float32 (the scores only feed the threshold estimate): each is within
+ *          about 2 d 2^-24 of the sum of the absolute terms of the float64 value.
  *   GAUSS_Q: the same m and s (GAUSS metadata, GAUSS outputs), with the estimated maximum
  *          shat = m + s Phi^-1(1 - 1/n_p), the normal quantile exceeded by one of n_p draws on
  *          average ("EntmaxKV" s2.B leaves the estimate open).
@@ -196,7 +198,8 @@ enum { SKV_TOKEN_PHASE_ALL = 0, SKV_TOKEN_PHASE_BOUND = 1, SKV_TOKEN_PHASE_FILTE
  *          SKV_SEL_TOKEN_TOPK (tokens = 1).
  * Entries past the sequence (p >= ceil(L_b / S), or t >= L_b) are -inf (BOX, PROJ) or NaN
  * (GAUSS). `q` is [B, Hq, d] in the cache dtype. `workspace` must hold
- * skv_workspace_bytes(c, SKV_OP_SCORE, &kind, 0) bytes (256-byte aligned).
+ * skv_workspace_bytes(c, SKV_OP_SCORE, &kind, 0) bytes (256-byte aligned; GAUSS and GAUSS_Q need
+ * none and may pass NULL).
  * Errors: SKV_ERR_INVALID_ARG (null pointers, kind not in m->kinds, bad sm_scale or temperature),
  * SKV_ERR_WORKSPACE, SKV_ERR_UNSUPPORTED, SKV_ERR_HIP. */
 skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q, int32_t kind, float sm_scale,

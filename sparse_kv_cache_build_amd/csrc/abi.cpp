@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 #include <vector>
 
 #include "launch.hpp"
@@ -69,6 +70,7 @@ bool lsh_ok(int L, int P) { return (L == 16 || L == 32 || L == 48 || L == 64) &&
 // Workspace of a scoring call. LSH: the bucket masses of every unit, G * L * 2^P uint32 each
 // (`lsh_entries` per unit; the size query, which does not see L and P, assumes the maximum).
 size_t score_ws(const skv_cache *c, int kind, int r, size_t lsh_entries = skv::kLshMaxEntries) {
+  if (kind == SKV_SCORE_GAUSS || kind == SKV_SCORE_GAUSS_Q) return 0;   // the scorer stages q itself
   if (kind == SKV_SCORE_PROJ) return round_up(sizeof(double) * (size_t)c->batch * c->num_q_heads * r);
   if (kind == SKV_SCORE_LSH) return round_up(sizeof(uint32_t) * (size_t)c->batch * c->num_kv_heads * lsh_entries);
   return round_up(sizeof(double) * 2 * (size_t)c->batch * c->num_q_heads * c->head_dim);
@@ -132,7 +134,12 @@ int budget_cap(int maxP, int pct) {
 extern "C" {
 
 const char *skv_status_str(skv_status s) {
-  switch (s) {
+  // A C caller may pass any int; in C++ loading it as the enum type would be undefined, so the
+  // argument's representation is read as an integer.
+  int v;
+  static_assert(sizeof v == sizeof s, "skv_status is int-sized");
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case SKV_OK: return "SKV_OK";
     case SKV_ERR_INVALID_ARG: return "SKV_ERR_INVALID_ARG";
     case SKV_ERR_UNSUPPORTED: return "SKV_ERR_UNSUPPORTED";
@@ -292,7 +299,7 @@ skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q,
       score_ws(c, kind, m->proj_rank,
                kind == SKV_SCORE_LSH ? ((size_t)c->num_q_heads / c->num_kv_heads) * ((size_t)m->lsh_tables << m->lsh_bits)
                                      : 0);
-  if (!workspace || workspace_bytes < need || !aligned(workspace, 8)) return SKV_ERR_WORKSPACE;
+  if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 8))) return SKV_ERR_WORKSPACE;
   double *ws = static_cast<double *>(workspace);
   (void)hipGetLastError();
   hipError_t e;
@@ -304,8 +311,8 @@ skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q,
     e = skv::launch_score_lsh(v, c->dtype, q, m->lsh_tables, m->lsh_bits, m->lsh_planes, sm_scale, m->lsh_bucket,
                               m->vnorm, out->key, workspace, s, ev);
   else if (kind == SKV_SCORE_GAUSS || kind == SKV_SCORE_GAUSS_Q)
-    e = skv::launch_score_gauss(v, c->dtype, q, m->gauss, (double)sm_scale, kind == SKV_SCORE_GAUSS_Q, out->m,
-                                out->s, out->shat, ws, s, ev);
+    e = skv::launch_score_gauss(v, c->dtype, q, m->gauss, sm_scale, kind == SKV_SCORE_GAUSS_Q, out->m, out->s,
+                                out->shat, s, ev);
   else
     e = skv::launch_score_proj(v, c->dtype, q, m->proj_rank, m->proj, m->kproj, out->key, ws, s, ev);
   return hip_status(e);

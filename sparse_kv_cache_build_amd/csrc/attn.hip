@@ -383,8 +383,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
 // 4 (l / 16) .. + 3 for head l % 16. Each wave takes every fourth tile, with the K loads of UNR
 // tiles in flight before their products. bf16 products are exact and the sums are float32, as
 // on the VALU path.
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <int D, int G>
 __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_mfma_kernel(

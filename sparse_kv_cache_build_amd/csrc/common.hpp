@@ -13,6 +13,10 @@ constexpr int kLshMaxProj = 512;    // tables x hyperplanes per table (64 x 8)
 constexpr int kLshMaxEntries = 16384;   // G x tables x 2^P bucket masses of one unit (64 KiB of LDS)
 
 // Plain view of the paged cache passed by value to kernels.
+// Operand and result vectors of the 16x16x32 bf16 matrix-core instruction.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 struct CacheView {
   int32_t B, Hq, Hkv, D, S, maxP, Nphys, G;
   const void *k;
@@ -444,6 +448,72 @@ __device__ __forceinline__ float group_sum(float v) {
   v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
   if (WIDTH == 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
   return v;
+}
+
+// Radix selection over order keys get(i), i < n: finds the r-th largest key T (1 <= r <= n) and
+// need = r - #(keys > T), i.e. how many keys equal to T belong to the top r. Four 8-bit digits,
+// most significant first. Each wave counts into its own 256-bin LDS histogram (the leading digits
+// of float keys fall into few bins, so one shared histogram would serialize the atomics); the
+// wave histograms are then summed. Integer atomics only, so the result is deterministic.
+// `hist` holds NT/64 * 256 words, `bc` 2 words of shared memory. Every thread must call it.
+// With digits < 4 only the leading digits are resolved: T then has its low bits cleared, which
+// makes it a lower bound of the r-th largest key with at least r keys >= T.
+// When every key lies in [lo, hi], the leading digits that lo and hi share are common to all keys
+// and need no pass: a candidate set drawn from above a bound has one or two in front.
+template <int NT, typename Get>
+__device__ void radix_kth(Get get, int n, uint32_t r, uint32_t *hist, uint32_t *bc, uint32_t &T, uint32_t &need,
+                          int digits = 4, uint32_t lo = 0u, uint32_t hi = 0xffffffffu) {
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x;
+  uint32_t *mine = hist + (tid / kWave) * 256;
+  const int last = 32 - 8 * digits;
+  int first = 24;
+  uint32_t mask = 0;
+  while (first >= last && ((lo ^ hi) >> first) == 0) {
+    mask |= 0xffu << first;
+    first -= 8;
+  }
+  uint32_t prefix = lo & mask;
+  need = r;
+  for (int shift = first; shift >= last; shift -= 8) {
+    for (int i = tid; i < NW * 256; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+      const uint32_t u = get(i);
+      if ((u & mask) == prefix) atomicAdd(&mine[(u >> shift) & 0xffu], 1u);
+    }
+    __syncthreads();
+    // the wanted digit v has count(> v) < need <= count(>= v); lane l owns digits 4l .. 4l+3
+    if (tid < kWave) {
+      uint32_t c4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {   // one 16-byte read per wave histogram (no bank conflicts)
+        const uint4 h4 = reinterpret_cast<const uint4 *>(hist + w * 256)[tid];
+        c4[0] += h4.x;
+        c4[1] += h4.y;
+        c4[2] += h4.z;
+        c4[3] += h4.w;
+      }
+      const uint32_t local = c4[0] + c4[1] + c4[2] + c4[3];
+      // keys in the digits of higher lanes: the wave total minus the inclusive prefix
+      const uint32_t pre = wave_incl_scan(local);
+      uint32_t above = __builtin_amdgcn_readlane(pre, kWave - 1) - pre;
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if (above < need && above + c4[i] >= need) {
+          bc[0] = prefix | ((uint32_t)(4 * tid + i) << shift);
+          bc[1] = need - above;
+        }
+        above += c4[i];
+      }
+    }
+    __syncthreads();
+    prefix = bc[0];
+    need = bc[1];
+    mask |= 0xffu << shift;
+    __syncthreads();
+  }
+  T = prefix;
 }
 
 }  // namespace skv

@@ -57,9 +57,8 @@ hipError_t launch_score_box(const CacheView &c, int dtype, const void *q, const 
 hipError_t launch_score_lsh(const CacheView &c, int dtype, const void *q, int L, int P, const float *planes,
                             float tau, const uint8_t *bucket, const float *vnorm, float *key, void *ws,
                             hipStream_t st, const KernelEvents &ev);
-hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, const float *gauss, double scale,
-                              int quantile, float *m, float *s, float *shat, double *ws, hipStream_t st,
-                              const KernelEvents &ev);
+hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, const float *gauss, float scale,
+                              int quantile, float *m, float *s, float *shat, hipStream_t st, const KernelEvents &ev);
 hipError_t launch_score_pool(const CacheView &c, int dtype, const void *q, int pb, const float *pool, float *key,
                              double *ws, hipStream_t st, const KernelEvents &ev);
 hipError_t launch_score_proj(const CacheView &c, int dtype, const void *q, int r, const float *proj,

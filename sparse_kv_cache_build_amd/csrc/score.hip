@@ -61,8 +61,8 @@ __device__ __forceinline__ float box_elem(const uint4 (&r)[N], int jj) {
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void score_box_kernel(CacheView c, const T *__restrict__ box,
                                                         const double *__restrict__ qpm, float *__restrict__ key) {
-  const int unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
-  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  const int g = blockIdx.x % c.Hkv, b = blockIdx.y, unit = b * c.Hkv + g;
+  const int p = (blockIdx.x / c.Hkv) * blockDim.x + threadIdx.x;
   if (p >= c.maxP) return;
   float *out = key + (size_t)unit * c.maxP + p;
   const int P = num_pages(c, seq_len(c, b));
@@ -129,13 +129,14 @@ __global__ __launch_bounds__(256) void score_pool_kernel(CacheView c, int pb, in
   __shared__ double qs[G * D];
   __shared__ float xs[4][64 * LDR];
   const int unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
+  const int bx = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int W = 1 << lw, PT = 64 >> lw;
-  const int p0 = (blockIdx.x * 4 + wave) * PT;
+  const int p0 = (bx * 4 + wave) * PT;
   const int L = seq_len(c, b), np = num_pages(c, L), nsb = c.S / pb;
-  if ((int)blockIdx.x * 4 * PT >= np) {   // every page of the block lies past the sequence
+  if (bx * 4 * PT >= np) {   // every page of the block lies past the sequence
     for (int i = threadIdx.x; i < 4 * PT; i += blockDim.x)
-      if (blockIdx.x * 4 * PT + i < c.maxP) key[(size_t)unit * c.maxP + blockIdx.x * 4 * PT + i] = -INFINITY;
+      if (bx * 4 * PT + i < c.maxP) key[(size_t)unit * c.maxP + bx * 4 * PT + i] = -INFINITY;
     return;
   }
   const int T = (nsb + W - 1) >> lw;
@@ -339,19 +340,22 @@ __global__ __launch_bounds__(256) void score_lsh_kernel(CacheView c, int L, int 
   }
 }
 
-// GAUSS scores. m = scale sum_j q_j mean_j, s = scale sqrt(sum_j q_j^2 var_j) (float64, j
-// ascending), shat = m + s sqrt(2 ln n_p) (or the quantile maximum). Outputs [B, Hq, maxP]; NaN past
-// the sequence. A wave owns 64 pages (a lane each, G heads); their rows are read in chunks of 16
-// coordinates (64 bytes of the mean row and 64 of the variance row: 8 lanes per page, eight pages per
-// load instruction) into LDS, where each lane sums its page; the (q, q^2) pairs come from LDS as
-// broadcast reads. The next chunk is loaded while the current one is summed.
-template <int D, int G>
-__global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const float *__restrict__ gauss,
-                                                          const double *__restrict__ qpm, double scale, int quantile,
+// GAUSS scores. m = scale sum_j q_j mean_j, s = scale sqrt(sum_j q_j^2 var_j), shat = m + s sqrt(2 ln
+// n_p) (or the quantile maximum); outputs [B, Hq, maxP], NaN past the sequence. The sums run in
+// float32, j ascending: the scores feed only the threshold estimate, whose decisions are compared
+// with a tolerance (a float32 sum of d terms is within about d 2^-24 of the sum of the absolute
+// terms). A block first stages the (q, q^2) pairs of its G query heads in LDS from q itself. A wave
+// owns 64 pages (a lane each, G heads); their rows are read in chunks of 16 coordinates (64 bytes of
+// the mean row and 64 of the variance row: 8 lanes per page, eight pages per load instruction) into
+// LDS, where each lane sums its page with the (q, q^2) pairs read as broadcasts (8 bytes per head
+// and coordinate). The next chunk is loaded while the current one is summed.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const T *__restrict__ q,
+                                                          const float *__restrict__ gauss, float scale, int quantile,
                                                           float *__restrict__ m_out, float *__restrict__ s_out,
                                                           float *__restrict__ shat_out) {
   constexpr int CW = 16, NC = D / CW, LDR = 2 * CW + 4, NK = 8;   // 64 rows, 8 per load instruction
-  __shared__ double2 qs[G * D];
+  __shared__ float2 qs[G * D];
   __shared__ float xs[4][64 * LDR];
   const int unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -366,8 +370,11 @@ __global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const flo
     }
     return;
   }
-  const double2 *qq = reinterpret_cast<const double2 *>(qpm + (size_t)(b * c.Hq + g * G) * D * 2);
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) qs[i] = qq[i];
+  const T *qg = q + (size_t)(b * c.Hq + g * G) * D;   // the G heads of the group are adjacent
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+    const float x = Elem<T>::get(qg, i);
+    qs[i] = make_float2(x, x * x);
+  }
   const int *bt = c.bt + (size_t)b * c.maxP;
   // load side: lane -> page lrow + 8k, half (mean or variance row) and 4 of the 16 columns
   const int lrow = lane >> 3, half = (lane >> 2) & 1, lcol = (lane & 3) * 4;
@@ -380,9 +387,9 @@ __global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const flo
     r[k] = off[k] >= 0 ? *reinterpret_cast<const float4 *>(gauss + off[k]) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   float *xw = xs[wave];
-  double sm[G], sv[G];
+  float sm[G], sv[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) sm[h] = sv[h] = 0.0;
+  for (int h = 0; h < G; ++h) sm[h] = sv[h] = 0.0f;
   __syncthreads();   // qs is staged; from here on each wave uses only its own rows in LDS
   for (int ch = 0; ch < NC; ++ch) {
     __builtin_amdgcn_wave_barrier();   // the wave has read the previous chunk
@@ -396,15 +403,15 @@ __global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const flo
     }
     __builtin_amdgcn_wave_barrier();   // the chunk is in LDS for every lane of the wave
     const float *xm = xw + lane * LDR, *xv = xm + CW;
-    const double2 *qc = qs + ch * CW;
-#pragma unroll 2   // bounded unrolling: the q pairs of a coordinate live only while it is summed
+    const float2 *qc = qs + ch * CW;
+#pragma unroll 4
     for (int j = 0; j < CW; ++j) {
-      const double dm = xm[j], dv = xv[j];
+      const float dm = xm[j], dv = xv[j];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const double2 qp = qc[h * D + j];
-        sm[h] = fma(qp.x, dm, sm[h]);
-        sv[h] = fma(qp.y, dv, sv[h]);
+        const float2 qp = qc[h * D + j];
+        sm[h] = fmaf(qp.x, dm, sm[h]);
+        sv[h] = fmaf(qp.y, dv, sv[h]);
       }
     }
   }
@@ -420,13 +427,14 @@ __global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const flo
   const int n = min(c.S, L - p * c.S);
   // estimated maximum of the page's n scores: m + s sqrt(2 ln n), or (quantile) m + s Phi^-1(1 - 1/n)
   // = m + s sqrt(2) erfcinv(2 / n)
-  const double lg = n <= 1 ? 0.0 : (quantile ? 1.4142135623730951 * erfcinv(2.0 / n) : sqrt(2.0 * log((double)n)));
+  const float lg =
+      n <= 1 ? 0.0f : (float)(quantile ? 1.4142135623730951 * erfcinv(2.0 / n) : sqrt(2.0 * log((double)n)));
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const double m = scale * sm[h], s = scale * sqrt(sv[h]);
-    m_out[o0 + (size_t)h * c.maxP] = (float)m;
-    s_out[o0 + (size_t)h * c.maxP] = (float)s;
-    shat_out[o0 + (size_t)h * c.maxP] = (float)(m + s * lg);
+    const float m = scale * sm[h], s = scale * sqrtf(sv[h]);
+    m_out[o0 + (size_t)h * c.maxP] = m;
+    s_out[o0 + (size_t)h * c.maxP] = s;
+    shat_out[o0 + (size_t)h * c.maxP] = fmaf(s, lg, m);
   }
 }
 
@@ -584,7 +592,9 @@ static hipError_t qprep_pair(const void *q, int n, int gauss, double *ws, hipStr
 template <typename T, int D>
 static hipError_t box_d(const CacheView &c, const void *box, const double *qpm, float *key, hipStream_t st,
                         const KernelEvents &ev) {
-  const dim3 grid((c.maxP + 255) / 256, c.B * c.Hkv);
+  // the Hkv blocks of one page range are adjacent in launch order (page block = x / Hkv), so the
+  // KV heads' boxes of a physical page (adjacent in memory) are read at about the same time
+  const dim3 grid(((c.maxP + 255) / 256) * c.Hkv, c.B);
   hipError_t e0 = ev.before(st);
   if (e0 != hipSuccess) return e0;
   SKV_DISPATCH_G(c.G, score_box_kernel<T, D, GG><<<grid, 256, 0, st>>>(c, static_cast<const T *>(box), qpm, key))
@@ -600,24 +610,24 @@ hipError_t launch_score_box(const CacheView &c, int dtype, const void *q, const 
   return dtype == 0 ? box_d<float, 128>(c, box, ws, key, st, ev) : box_d<uint16_t, 128>(c, box, ws, key, st, ev);
 }
 
-template <int D>
-static hipError_t gauss_d(const CacheView &c, const float *gauss, const double *qpm, double scale, int quantile, float *m, float *s,
-                          float *shat, hipStream_t st, const KernelEvents &ev) {
+template <typename T, int D>
+static hipError_t gauss_d(const CacheView &c, const void *q, const float *gauss, float scale, int quantile, float *m,
+                          float *s, float *shat, hipStream_t st, const KernelEvents &ev) {
   const dim3 grid((c.maxP + 255) / 256, c.B * c.Hkv);
+  const T *qt = static_cast<const T *>(q);
   hipError_t e0 = ev.before(st);
   if (e0 != hipSuccess) return e0;
-  SKV_DISPATCH_G(c.G, score_gauss_kernel<D, GG><<<grid, 256, 0, st>>>(c, gauss, qpm, scale, quantile, m, s, shat))
+  SKV_DISPATCH_G(c.G, score_gauss_kernel<T, D, GG><<<grid, 256, 0, st>>>(c, qt, gauss, scale, quantile, m, s, shat))
   return ev.after(st);
 }
 
-hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, const float *gauss, double scale,
-                              int quantile, float *m,
-                              float *s, float *shat, double *ws, hipStream_t st, const KernelEvents &ev) {
-  const int n = c.B * c.Hq * c.D;
-  hipError_t e = dtype == 0 ? qprep_pair<float>(q, n, 1, ws, st) : qprep_pair<uint16_t>(q, n, 1, ws, st);
-  if (e != hipSuccess) return e;
-  return c.D == 64 ? gauss_d<64>(c, gauss, ws, scale, quantile, m, s, shat, st, ev)
-                    : gauss_d<128>(c, gauss, ws, scale, quantile, m, s, shat, st, ev);
+hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, const float *gauss, float scale,
+                              int quantile, float *m, float *s, float *shat, hipStream_t st, const KernelEvents &ev) {
+  if (dtype == 0)
+    return c.D == 64 ? gauss_d<float, 64>(c, q, gauss, scale, quantile, m, s, shat, st, ev)
+                     : gauss_d<float, 128>(c, q, gauss, scale, quantile, m, s, shat, st, ev);
+  return c.D == 64 ? gauss_d<uint16_t, 64>(c, q, gauss, scale, quantile, m, s, shat, st, ev)
+                   : gauss_d<uint16_t, 128>(c, q, gauss, scale, quantile, m, s, shat, st, ev);
 }
 
 template <int D>
