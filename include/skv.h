@@ -29,7 +29,11 @@
  *     the HIP runtime returns SKV_ERR_HIP. Device-side data (seq_lens, block_table, counts)
  *     cannot be validated on the host: seq_lens are clamped to [0, max_pages * page_size],
  *     block_table entries of pages below the clamped length must lie in [0, num_phys_pages),
- *     sel_count entries are clamped to [0, cap].
+ *     sel_count entries are clamped to [0, cap]. With the environment variable SKV_DEBUG set
+ *     (to anything but "0"), every call first synchronises its stream and checks these on the
+ *     host: block_table entries of the pages in use in [0, num_phys_pages), and for the
+ *     attention also sel_count in [0, cap] and selections strictly ascending inside the
+ *     sequence; a violation returns SKV_ERR_INVALID_ARG and nothing is launched.
  *   - Threading: calls are reentrant; concurrent calls must not share output or workspace
  *     buffers.
  *   - Determinism: for a fixed input, launch configuration and device, outputs are bitwise

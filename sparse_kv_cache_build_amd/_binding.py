@@ -14,7 +14,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libskv.so")
+# SKV_LIB names another build of the same library (the sanitizer test loads one built with
+# host-side AddressSanitizer and UndefinedBehaviorSanitizer)
+LIB_PATH = os.environ.get("SKV_LIB") or os.path.join(_PKG, "libskv.so")
 
 # status codes
 SKV_OK, SKV_ERR_INVALID_ARG, SKV_ERR_UNSUPPORTED, SKV_ERR_CAPACITY, SKV_ERR_WORKSPACE, SKV_ERR_HIP = range(6)

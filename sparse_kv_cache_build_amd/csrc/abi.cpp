@@ -2,7 +2,9 @@
 // Nothing is enqueued unless every argument checks out. See include/skv.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstdint>
 #include <cstring>
 #include <vector>
@@ -124,6 +126,75 @@ skv_status check_attn_params(const skv_attn_params *p) {
   return SKV_OK;
 }
 
+// ---------------------------------------------------------------- SKV_DEBUG checks
+// With SKV_DEBUG set (to anything but "0"), a call first synchronises its stream, copies the
+// device-side inputs it indexes with to the host and checks them; an out-of-range entry returns
+// SKV_ERR_INVALID_ARG before anything is launched. Off by default: it costs a synchronisation and
+// host copies per call.
+bool debug_on() {
+  const char *e = std::getenv("SKV_DEBUG");
+  return e && *e && std::strcmp(e, "0") != 0;
+}
+
+skv_status debug_fetch(const int32_t *src, size_t n, std::vector<int32_t> &dst, hipStream_t s) {
+  dst.resize(n);
+  if (n == 0) return SKV_OK;
+  if (hipStreamSynchronize(s) != hipSuccess ||
+      hipMemcpy(dst.data(), src, n * sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess) {
+    (void)hipGetLastError();
+    return SKV_ERR_HIP;
+  }
+  return SKV_OK;
+}
+
+// seq_lens clamped as the kernels clamp them; block_table entries of the pages in use within
+// [0, num_phys_pages). Writes the clamped lengths.
+skv_status debug_check_cache(const skv_cache *c, hipStream_t s, std::vector<int64_t> &lens) {
+  std::vector<int32_t> raw, bt;
+  skv_status st = debug_fetch(c->seq_lens, (size_t)c->batch, raw, s);
+  if (st == SKV_OK) st = debug_fetch(c->block_table, (size_t)c->batch * c->max_pages, bt, s);
+  if (st != SKV_OK) return st;
+  const int64_t cap = (int64_t)c->max_pages * c->page_size;
+  lens.resize(c->batch);
+  for (int b = 0; b < c->batch; ++b) {
+    lens[b] = std::min<int64_t>(std::max<int64_t>(raw[b], 0), cap);
+    const int64_t P = (lens[b] + c->page_size - 1) / c->page_size;
+    for (int64_t p = 0; p < P; ++p) {
+      const int32_t x = bt[(size_t)b * c->max_pages + p];
+      if (x < 0 || x >= c->num_phys_pages) return SKV_ERR_INVALID_ARG;
+    }
+  }
+  return SKV_OK;
+}
+
+skv_status debug_check_cache(const skv_cache *c, hipStream_t s) {
+  std::vector<int64_t> lens;
+  return debug_check_cache(c, s, lens);
+}
+
+// A selection as skv_select_pages writes it: counts within [0, cap], entries inside the sequence
+// (logical pages below P_b, or tokens below L_b) and strictly ascending.
+skv_status debug_check_selection(const skv_cache *c, const int32_t *sel_idx, const int32_t *sel_count, int cap,
+                                 int gran, hipStream_t s) {
+  std::vector<int64_t> lens;
+  skv_status st = debug_check_cache(c, s, lens);
+  if (st != SKV_OK) return st;
+  const size_t U = (size_t)c->batch * c->num_kv_heads;
+  std::vector<int32_t> cnt, idx;
+  if ((st = debug_fetch(sel_count, U, cnt, s)) != SKV_OK || (st = debug_fetch(sel_idx, U * cap, idx, s)) != SKV_OK)
+    return st;
+  for (size_t u = 0; u < U; ++u) {
+    const int64_t L = lens[u / c->num_kv_heads];
+    const int64_t limit = gran ? L : (L + c->page_size - 1) / c->page_size;
+    if (cnt[u] < 0 || cnt[u] > cap) return SKV_ERR_INVALID_ARG;
+    for (int i = 0; i < cnt[u]; ++i) {
+      const int32_t e = idx[u * cap + i];
+      if (e < 0 || e >= limit || (i > 0 && e <= idx[u * cap + i - 1])) return SKV_ERR_INVALID_ARG;
+    }
+  }
+  return SKV_OK;
+}
+
 int budget_cap(int maxP, int pct) {
   const int64_t k = ((int64_t)pct * maxP + 99) / 100;
   return (int)std::max<int64_t>(1, k);
@@ -219,6 +290,10 @@ static skv_status meta_args(const skv_cache *c, const skv_meta *m) {
 }
 
 static skv_status meta_launch(const skv_cache *c, const skv_meta *m, int tail, void *stream) {
+  if (debug_on()) {
+    const skv_status st = debug_check_cache(c, static_cast<hipStream_t>(stream));
+    if (st != SKV_OK) return st;
+  }
   const bool box = m->kinds & SKV_META_BOX, gauss = m->kinds & SKV_META_GAUSS, proj = m->kinds & SKV_META_PROJ;
   const bool pool = m->kinds & SKV_META_POOL;
   (void)hipGetLastError();
@@ -250,6 +325,7 @@ skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q,
   if (!m || !q || !out) return SKV_ERR_INVALID_ARG;
   if (!aligned(q, 16)) return SKV_ERR_INVALID_ARG;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_on() && (st = debug_check_cache(c, s)) != SKV_OK) return st;
   const CacheView v = view(c);
   const skv::KernelEvents ev = events(out->ev_begin, out->ev_end);
   if (kind == SKV_SCORE_BOX) {
@@ -325,6 +401,7 @@ skv_status skv_select_pages(const skv_cache *c, const skv_scores *sc, const skv_
   if (st != SKV_OK) return st;
   if (!sc || !p || !sel_idx || !sel_count || cap < 1) return SKV_ERR_INVALID_ARG;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_on() && (st = debug_check_cache(c, s)) != SKV_OK) return st;
   const CacheView v = view(c);
   const int maxP = c->max_pages, Lmax = c->max_pages * c->page_size;
   (void)hipGetLastError();
@@ -394,6 +471,11 @@ static skv_status attn_check(const skv_cache *c, const void *q, const int32_t *s
 static skv_status attn_launch(const skv_cache *c, const void *q, const int32_t *sel_idx, const int32_t *sel_count,
                               int32_t cap, const skv_attn_params *p, float *out, char *ws, const AttnPlan &plan,
                               void *stream) {
+  if (debug_on()) {
+    const skv_status st =
+        debug_check_selection(c, sel_idx, sel_count, cap, p->granularity, static_cast<hipStream_t>(stream));
+    if (st != SKV_OK) return st;
+  }
   skv::AttnArgs a;
   a.c = view(c);
   a.dtype = c->dtype;
