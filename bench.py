@@ -276,9 +276,18 @@ def w0_row_bytes(w: W.Workload) -> int:
 
 
 def reference_ceilings(dev, n_rows: int, row_bytes: int, reps: int = 5):
-    """Reference rates on this GPU (torch's own kernels, context for the roofline fractions):
-    a 1 GiB copy (read + write), a read-only reduction over 1 GiB, and a gather of n_rows random
-    rows of row_bytes from a 4 GiB table into a contiguous buffer (read + write of the rows)."""
+    """Bandwidth ceilings on this GPU from the reference kernels of libskv_ref.so (context for the
+    roofline fractions): a plain streaming read of 1 GiB; a gather of n_rows random rows of
+    row_bytes, twice (K and V rows, as the attention reads them), from a 4 GiB table, each row read
+    by a group of row_bytes / 16 lanes; and torch's 1 GiB copy (read + write)."""
+    import ctypes as C
+    ref = C.CDLL(os.path.join(ROOT, "sparse_kv_cache_build_amd", "libskv_ref.so"))
+    ref.skv_ref_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
+    ref.skv_ref_gather_rows.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_void_p]
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    blocks = 256 * 8
+    sink = torch.empty(blocks, dtype=torch.int32, device=dev)
+
     def timed(fn):
         fn()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -290,27 +299,30 @@ def reference_ceilings(dev, n_rows: int, row_bytes: int, reps: int = 5):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps * 1e-3
 
+    def ok(rc):
+        assert rc == 0, rc
+
     out = {}
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    t = timed(lambda: ok(ref.skv_ref_stream_read(src.data_ptr(), (1 << 30) // 16, sink.data_ptr(), blocks, stream)))
+    out["stream_read_1GiB_GBps"] = round((1 << 30) / t / 1e9, 1)
     dst = torch.empty_like(src)
     t = timed(lambda: dst.copy_(src))
     out["copy_1GiB_GBps"] = round(2 * (1 << 30) / t / 1e9, 1)
-    del dst
-    x = src.view(torch.int32)
-    x.fill_(1)
-    t = timed(lambda: torch.sum(x, dtype=torch.int64))
-    out["read_1GiB_GBps"] = round((1 << 30) / t / 1e9, 1)
-    del src, x
+    del src, dst
     n_rows = max(1, int(n_rows))
-    table = torch.empty(((4 << 30) // row_bytes, row_bytes // 2), dtype=torch.bfloat16, device=dev)
+    words = row_bytes // 16
+    table = torch.ones(4 << 30, dtype=torch.uint8, device=dev)
     g = torch.Generator(device=dev)
     g.manual_seed(7)
-    idx = torch.randint(0, table.shape[0], (n_rows,), generator=g, device=dev)
-    t = timed(lambda: torch.index_select(table, 0, idx))
-    out["gather_rows"] = n_rows
+    rows_in_table = (4 << 30) // row_bytes
+    off = (torch.randint(0, rows_in_table, (2 * n_rows,), generator=g, device=dev) * words).to(torch.int64)
+    t = timed(lambda: ok(ref.skv_ref_gather_rows(table.data_ptr(), off.data_ptr(), 2 * n_rows, words,
+                                                   sink.data_ptr(), blocks, stream)))
+    out["gather_rows"] = 2 * n_rows
     out["gather_row_bytes"] = row_bytes
-    out["gather_GBps"] = round(n_rows * row_bytes / t / 1e9, 1)
-    del table, idx
+    out["gather_GBps"] = round(2 * n_rows * row_bytes / t / 1e9, 1)
+    del table, off
     torch.cuda.empty_cache()
     return out
 
