@@ -143,8 +143,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_softmax_kernel(
       const int ru = r + u * RL::RGB;
       o[u] = ru < NR ? roff[ru] : -1;
       if (o[u] >= 0) {
-        kx[u].load(K + o[u] + lr * 8);
-        vx[u].load(V + o[u] + lr * 8);
+        kx[u].load_once(K + o[u] + lr * 8);
+        vx[u].load_once(V + o[u] + lr * 8);
       }
     }
 #pragma unroll
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
     for (int u = 0; u < UNR; ++u) {
       const int ru = r + u * RL::RGB;
       o[u] = ru < NR ? roff[ru] : -1;
-      if (o[u] >= 0) kx[u].load(K + o[u] + lr * 8);
+      if (o[u] >= 0) kx[u].load_once(K + o[u] + lr * 8);
     }
 #pragma unroll
     for (int u = 0; u < UNR; ++u)

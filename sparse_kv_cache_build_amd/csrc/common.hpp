@@ -16,6 +16,18 @@ constexpr int kLshMaxEntries = 16384;   // G x tables x 2^P bucket masses of one
 // Operand and result vectors of the 16x16x32 bf16 matrix-core instruction.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte loads marked non-temporal, for data a kernel reads once per call (cache metadata, the
+// rows of the selected tokens): the lines are not kept in the caches for reuse.
+__device__ __forceinline__ uint4 ld_once(const uint4 *p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 ld_once(const float4 *p) {
+  const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
 
 struct CacheView {
   int32_t B, Hq, Hkv, D, S, maxP, Nphys, G;
@@ -79,6 +91,7 @@ template <>
 struct Packed8<uint16_t> {
   uint4 w;
   __device__ __forceinline__ void load(const uint16_t *p) { w = *reinterpret_cast<const uint4 *>(p); }
+  __device__ __forceinline__ void load_once(const uint16_t *p) { w = ld_once(reinterpret_cast<const uint4 *>(p)); }
   __device__ __forceinline__ void zero() { w = make_uint4(0u, 0u, 0u, 0u); }
   // element j (0..7) as float; j is a compile-time constant after unrolling
   __device__ __forceinline__ float at(int j) const {
@@ -99,6 +112,11 @@ template <>
 struct Packed8<float> {
   float x[8];
   __device__ __forceinline__ void load(const float *p) { Elem<float>::load8(p, x); }
+  __device__ __forceinline__ void load_once(const float *p) {
+    const float4 a = ld_once(reinterpret_cast<const float4 *>(p)), b = ld_once(reinterpret_cast<const float4 *>(p + 4));
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int j = 0; j < 8; ++j) x[j] = 0.0f;
@@ -163,6 +181,31 @@ __device__ __forceinline__ float proj_row_key(const uint4 (&w)[R / 8], QP qq) {
   double best = acc[0];
 #pragma unroll
   for (int h = 1; h < G; ++h) best = fmax(best, acc[h]);
+  return (float)best;
+}
+
+// The same key as proj_row_key, bit for bit (each head's float64 sum in the same order, the same
+// max), with the heads taken one at a time: a quarter of the registers live, for kernels that
+// evaluate it rarely next to a register-hungry main loop.
+template <int R, int G>
+__device__ __forceinline__ float proj_row_key_lean(const uint4 (&w)[R / 8], const double *qq) {
+  double best = 0.0;
+#pragma unroll 1
+  for (int h = 0; h < G; ++h) {
+    double acc = 0.0;
+#pragma unroll
+    for (int i0 = 0; i0 < R / 8; ++i0) {
+      uint32_t ww[4] = {w[i0].x, w[i0].y, w[i0].z, w[i0].w};
+      // opaque per head, so that the widened row is formed again for each head rather than kept
+      asm volatile("" : "+v"(ww[0]), "+v"(ww[1]), "+v"(ww[2]), "+v"(ww[3]));
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) {
+        const double dx = (ii & 1) ? bf16_hi(ww[ii / 2]) : bf16_lo(ww[ii / 2]);
+        acc = fma(qq[h * R + i0 * 8 + ii], dx, acc);
+      }
+    }
+    best = h == 0 ? acc : fmax(best, acc);
+  }
   return (float)best;
 }
 
@@ -437,14 +480,17 @@ __device__ __forceinline__ double block_max(double v, double *scratch) {
   return r;
 }
 
-// Sum over the `width` consecutive lanes of an aligned lane group (width 8 or 16) with DPP moves:
-// quad_perm [1,0,3,2] and [2,3,0,1] sum a quad, row_half_mirror pairs the two quads of 8 lanes,
-// row_mirror the two halves of a 16-lane row. Every lane of the group gets the group sum.
+// Sum over the `width` consecutive lanes of an aligned lane group (width 2, 4, 8 or 16) with DPP
+// moves: quad_perm [1,0,3,2] sums a pair, [2,3,0,1] then a quad, row_half_mirror pairs the two
+// quads of 8 lanes, row_mirror the two halves of a 16-lane row. Every lane of the group gets the
+// group sum, with the same bits (each step adds the same two values in either order).
 template <int WIDTH>
 __device__ __forceinline__ float group_sum(float v) {
-  static_assert(WIDTH == 8 || WIDTH == 16, "lane group of 8 or 16");
+  static_assert(WIDTH == 2 || WIDTH == 4 || WIDTH == 8 || WIDTH == 16, "lane group of 2, 4, 8 or 16");
   v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  if (WIDTH == 2) return v;
   v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  if (WIDTH == 4) return v;
   v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
   if (WIDTH == 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
   return v;

@@ -464,16 +464,20 @@ __global__ __launch_bounds__(256) void score_proj_kernel(CacheView c, const uint
 // Fused PROJ scoring for a token top-k. Only tokens whose exact key has order key >= the unit's
 // bound T_lo are written, as (key, token) pairs in token order into the candidate segment of
 // their group, with the group's count. One wave per group of kCandSegTokens consecutive tokens,
-// in steps of 128 (two rows per lane; the next step's rows are loaded while the current step is
-// filtered):
-//  1. filter: each token's upper estimate of its key (proj_row_upper, bf16 dot2 with an error
-//     bound) against T_lo; tokens that pass go, in token order, into the wave's LDS list;
-//  2. exact: the listed tokens, 64 at a time, get the exact key and the ones with order key >= T_lo
-//     are compacted into the segment with ballots. The filter keeps the rows of the first 64
-//     listed tokens in LDS (by then they have left L2); later rounds read their rows again.
+// in chunks of 64 tokens; the next two chunks' rows are loaded while the current one is filtered:
+//  1. load: a row of R bf16 values is R/8 lanes of 16 bytes, so one load instruction reads 512/R
+//     consecutive rows, whole 128-byte lines (runs of S R 2 bytes inside a page). The loads are
+//     marked non-temporal, as every row is read once. When S is a power of two and a multiple of
+//     512/R, the rows of one load lie in one page, whose block-table entry is wave-uniform;
+//  2. the chunk goes through the wave's LDS staging area, from which every lane reads one row;
+//  3. filter: the row's upper estimate of its key (proj_row_upper, q~ as scalar operands)
+//     against T_lo; rows that pass join the wave's LDS list of pending candidates, with their rows;
+//  4. exact: when a chunk would overflow the 64-entry list, and after the last chunk, the pending
+//     candidates (one lane each) get the exact key, and the ones with order key >= T_lo are
+//     appended to the segment with ballots.
 // The estimate never falls below the exact key, so the filter loses no token of the exact set;
 // it only spares the float64 arithmetic for the tokens that cannot reach T_lo.
-template <int R, int G>
+template <int R, int G, bool UNI>
 __global__ __launch_bounds__(256) void score_proj_cand_kernel(CacheView c, const uint16_t *__restrict__ kproj,
                                                               const double *__restrict__ qt,
                                                               const uint32_t *__restrict__ qb,
@@ -481,94 +485,111 @@ __global__ __launch_bounds__(256) void score_proj_cand_kernel(CacheView c, const
                                                               const uint32_t *__restrict__ bound,
                                                               int32_t *__restrict__ count, float2 *__restrict__ segs,
                                                               int nb) {
-  constexpr int GT = kCandSegTokens, STEP = 2 * kWave, NST = GT / STEP;
-  __shared__ int cl[256 / kWave][GT];
-  __shared__ uint4 rc[256 / kWave][kWave][R / 8];   // rows of the first 64 listed tokens
-  const int unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
+  constexpr int GT = kCandSegTokens, CH = kWave;                   // tokens per group, per chunk
+  constexpr int LPR = R / 8, TPI = kWave / LPR, NI = CH / TPI;     // lanes per row, rows per load, loads per chunk
+  constexpr int SROW = LPR + 1;   // staged row stride in 16-byte words (the pad spreads a row read over the banks)
+  __shared__ uint4 stg[256 / kWave][CH * SROW];
+  __shared__ uint4 rc[256 / kWave][kWave][LPR];   // rows of the pending candidates
+  __shared__ int cl[256 / kWave][kWave];          // their tokens
+  const int g = blockIdx.x % c.Hkv, b = blockIdx.y, unit = b * c.Hkv + g;
   const int L = seq_len(c, b);
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  const int gid = blockIdx.x * (256 / kWave) + wv;   // group of this wave
+  const int gid = (blockIdx.x / c.Hkv) * (256 / kWave) + wv;   // group of this wave
   const int tg = gid * GT;
   if (tg >= L || gid >= nb) return;
   const uint32_t *qp = qb + (size_t)(b * c.Hq + g * G) * (R / 2);
   const uint32_t Tlo = bound[unit];
   const float2 cf = qc[unit];
   const FilterCoef fc{cf.x, cf.y};
-  const bool pow2 = (c.S & (c.S - 1)) == 0;   // uniform: shifts instead of divisions
-  const int sh = 31 - __clz(c.S);
-  auto rowp = [&](int t) -> const uint4 * {
-    int pg, in;
-    if (pow2) {
-      pg = t >> sh;
-      in = t & (c.S - 1);
-    } else {
-      pg = t / c.S;
-      in = t - pg * c.S;
-    }
-    const int phys = c.bt[(size_t)b * c.maxP + pg];
-    return reinterpret_cast<const uint4 *>(kproj + (((size_t)phys * c.Hkv + g) * c.S + in) * R);
-  };
-  auto load = [&](int s, uint4 (&x)[2][R / 8]) {
-    const int ts = tg + s * STEP;
+  const int *btb = c.bt + (size_t)b * c.maxP;
+  const int sh = 31 - __clz(c.S);                   // log2 S when S is a power of two
+  const int part = lane % LPR, lrow = lane / LPR;   // the lane's 16 bytes of row lrow of a load
+  // UNI: the block-table entries of the group's pages, one per lane (pages past the sequence: 0)
+  constexpr int NV = (GT / TPI + kWave - 1) / kWave;
+  int vbt[NV];
+  if (UNI) {
+    const int pg0 = tg >> sh, npg = num_pages(c, L);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint4 *row = rowp(min(ts + u * kWave + lane, L - 1));
-#pragma unroll
-      for (int i = 0; i < R / 8; ++i) x[u][i] = row[i];
-    }
-  };
-  int nc = 0;
-  auto filter = [&](int s, const uint4 (&x)[2][R / 8]) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int t = tg + s * STEP + u * kWave + lane;
-      const bool keep = t < L && f32_order_key(proj_row_upper<R, G>(x[u], qp, fc)) >= Tlo;
-      const uint64_t bal = __ballot(keep);
-      if (keep) {
-        const int slot = nc + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-        cl[wv][slot] = t;
-        if (slot < kWave) {
-#pragma unroll
-          for (int i = 0; i < R / 8; ++i) rc[wv][slot][i] = x[u][i];
-        }
-      }
-      nc += __popcll(bal);
-    }
-  };
-  const int nst = min(NST, (L - tg + STEP - 1) / STEP);
-  uint4 w0[2][R / 8], w1[2][R / 8];
-  load(0, w0);
-  for (int s = 0; s < nst; s += 2) {   // ping-pong buffers: no dynamic register indexing
-    if (s + 1 < nst) load(s + 1, w1);
-    filter(s, w0);
-    if (s + 1 >= nst) break;
-    if (s + 2 < nst) load(s + 2, w0);
-    filter(s + 1, w1);
+    for (int v = 0; v < NV; ++v) vbt[v] = pg0 + v * kWave + lane < npg ? btb[pg0 + v * kWave + lane] : 0;
   }
-  __builtin_amdgcn_wave_barrier();
+  auto load = [&](int ch, uint4 (&x)[NI]) {
+    const int ts = tg + ch * CH;
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int t = min(ts + k * TPI + lrow, L - 1);   // rows past the sequence repeat the last one
+      int pg, phys;
+      if (UNI) {   // S is a power of two and a multiple of TPI: the load's rows share one page
+        pg = __builtin_amdgcn_readfirstlane(min(ts + k * TPI, L - 1)) >> sh;
+        const int pl = pg - (tg >> sh);   // the page's index in the group, below GT / S
+        phys = NV == 1 || pl < kWave ? __builtin_amdgcn_readlane(vbt[0], pl & (kWave - 1))
+                                     : __builtin_amdgcn_readlane(vbt[NV - 1], pl & (kWave - 1));
+      } else {
+        pg = t / c.S;
+        phys = btb[pg];
+      }
+      const uint4 *row =
+          reinterpret_cast<const uint4 *>(kproj + (((size_t)phys * c.Hkv + g) * c.S + (t - pg * c.S)) * R);
+      x[k] = ld_once(row + part);
+    }
+  };
   const double *qq = qt + (size_t)(b * c.Hq + g * G) * R;
   float2 *seg = segs + ((size_t)unit * nb + gid) * GT;
-  int base = 0;
-  for (int i0 = 0; i0 < nc; i0 += kWave) {
-    const int i = i0 + lane;
-    const int t = i < nc ? cl[wv][i] : tg;
-    uint4 x[R / 8];
-    if (i0 == 0) {   // the first 64 rows were kept in LDS by the filter (long evicted from L2)
+  int pend = 0, base = 0;
+  auto flush = [&]() {
+    __builtin_amdgcn_wave_barrier();
+    uint4 x[LPR];
 #pragma unroll
-      for (int j = 0; j < R / 8; ++j) x[j] = rc[wv][lane][j];
-    } else {
-      const uint4 *row = rowp(t);
-#pragma unroll
-      for (int j = 0; j < R / 8; ++j) x[j] = row[j];
-    }
-    const float kv = proj_row_key<R, G>(x, qq);
-    const bool keep = i < nc && f32_order_key(kv) >= Tlo;
+    for (int j = 0; j < LPR; ++j) x[j] = rc[wv][lane][j];
+    const int t = lane < pend ? cl[wv][lane] : tg;
+    const float kv = proj_row_key_lean<R, G>(x, qq);
+    const bool keep = lane < pend && f32_order_key(kv) >= Tlo;
     const uint64_t bal = __ballot(keep);
     if (keep)
       seg[base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] =
           make_float2(kv, __int_as_float(t));
     base += __popcll(bal);
+    pend = 0;
+    __builtin_amdgcn_wave_barrier();   // the list is read before it is refilled
+  };
+  auto filter = [&](int ch, const uint4 (&x)[NI]) {
+    uint4 *sw = stg[wv];
+    __builtin_amdgcn_wave_barrier();   // the previous chunk's rows have been read
+#pragma unroll
+    for (int k = 0; k < NI; ++k) sw[(k * TPI + lrow) * SROW + part] = x[k];
+    __builtin_amdgcn_wave_barrier();
+    uint4 row[LPR];
+#pragma unroll
+    for (int j = 0; j < LPR; ++j) row[j] = sw[lane * SROW + j];
+    const int t = tg + ch * CH + lane;
+    int zero = 0;
+    asm volatile("" : "+s"(zero));   // q~ is read again per chunk (scalar loads), not held in registers
+    const bool keep = t < L && f32_order_key(proj_row_upper<R, G>(row, qp + zero, fc)) >= Tlo;
+    const uint64_t bal = __ballot(keep);
+    const int n = __popcll(bal);
+    if (pend + n > kWave) flush();
+    if (keep) {
+      const int slot = pend + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      cl[wv][slot] = t;
+#pragma unroll
+      for (int j = 0; j < LPR; ++j) rc[wv][slot][j] = row[j];
+    }
+    pend += n;
+  };
+  const int nch = min(GT / CH, (L - tg + CH - 1) / CH);
+  uint4 w0[NI], w1[NI], w2[NI];   // two chunks in flight while a third is filtered
+  load(0, w0);
+  if (1 < nch) load(1, w1);
+  for (int ch = 0; ch < nch; ch += 3) {   // three buffers in rotation: no dynamic register indexing
+    if (ch + 2 < nch) load(ch + 2, w2);
+    filter(ch, w0);
+    if (ch + 1 >= nch) break;
+    if (ch + 3 < nch) load(ch + 3, w0);
+    filter(ch + 1, w1);
+    if (ch + 2 >= nch) break;
+    if (ch + 4 < nch) load(ch + 4, w1);
+    filter(ch + 2, w2);
   }
+  if (pend > 0) flush();
   if (lane == 0) count[(size_t)unit * nb + gid] = base;
 }
 
@@ -661,13 +682,15 @@ static hipError_t proj_r(const CacheView &c, const uint16_t *kproj, const double
   return ev.after(st);
 }
 
-template <int R>
+template <int R, bool UNI>
 static hipError_t proj_cand_r(const CacheView &c, const uint16_t *kproj, char *cand, const CandLayout &lay,
                               hipStream_t st, const KernelEvents &ev) {
-  const dim3 grid((lay.nb + 3) / 4, c.B * c.Hkv);
+  // the Hkv blocks of one token range are adjacent in launch order: the KV heads' rows of a
+  // physical page (adjacent in memory) are read at about the same time
+  const dim3 grid(((lay.nb + 3) / 4) * c.Hkv, c.B);
   hipError_t e0 = ev.before(st);
   if (e0 != hipSuccess) return e0;
-  SKV_DISPATCH_G(c.G, score_proj_cand_kernel<R, GG><<<grid, 256, 0, st>>>(
+  SKV_DISPATCH_G(c.G, score_proj_cand_kernel<R, GG, UNI><<<grid, 256, 0, st>>>(
                           c, kproj, reinterpret_cast<const double *>(cand + lay.qt),
                           reinterpret_cast<const uint32_t *>(cand + lay.qb),
                           reinterpret_cast<const float2 *>(cand + lay.qc),
@@ -680,10 +703,12 @@ static hipError_t proj_cand_r(const CacheView &c, const uint16_t *kproj, char *c
 hipError_t launch_score_proj_cand(const CacheView &c, int r, const uint16_t *kproj, char *cand, hipStream_t st,
                                   const KernelEvents &ev) {
   const CandLayout lay(c.B, c.Hq, c.Hkv, c.maxP * c.S, 64);   // layout independent of the rank
+  // rows of one load instruction: 512 / r; they share a page when S is a power-of-two multiple
+  const bool uni = (c.S & (c.S - 1)) == 0 && c.S % (512 / r) == 0;
   switch (r) {
-    case 16: return proj_cand_r<16>(c, kproj, cand, lay, st, ev);
-    case 32: return proj_cand_r<32>(c, kproj, cand, lay, st, ev);
-    case 64: return proj_cand_r<64>(c, kproj, cand, lay, st, ev);
+    case 16: return uni ? proj_cand_r<16, true>(c, kproj, cand, lay, st, ev) : proj_cand_r<16, false>(c, kproj, cand, lay, st, ev);
+    case 32: return uni ? proj_cand_r<32, true>(c, kproj, cand, lay, st, ev) : proj_cand_r<32, false>(c, kproj, cand, lay, st, ev);
+    case 64: return uni ? proj_cand_r<64, true>(c, kproj, cand, lay, st, ev) : proj_cand_r<64, false>(c, kproj, cand, lay, st, ev);
     default: return hipErrorInvalidValue;
   }
 }
