@@ -93,7 +93,8 @@ typedef struct skv_meta {
   uint32_t kinds;     /* OR of SKV_META_* to build (build_page_meta) / available (score) */
   void *box;          /* BOX:   [Nphys, Hkv, d/C, 2, C] cache dtype, C = 64 bytes of elements
                          (32 bf16, 16 float32): 64-byte blocks of k_min and of k_max alternate */
-  float *gauss;       /* GAUSS: [Nphys, Hkv, 2, d] float32: row 0 mean, row 1 variance */
+  float *gauss;       /* GAUSS: [Nphys, Hkv, d/16, 2, 16] float32: 64-byte blocks of the mean and
+                         of the variance row alternate (16 coordinates each) */
   int32_t proj_rank;  /* PROJ:  r, 1..64 */
   const float *proj;  /* PROJ:  [r, d] float32 projection shared by queries and keys */
   uint16_t *kproj;    /* PROJ:  [Nphys, Hkv, S, r] bf16 bit patterns */

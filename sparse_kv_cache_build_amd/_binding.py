@@ -174,7 +174,8 @@ class PageMeta:
             self.box = torch.empty((Np, Hkv, d // cb, 2, cb), dtype=cache.dtype, device=dev)
         if "gauss" in kinds:
             self.kinds |= META_GAUSS
-            self.gauss = torch.empty((Np, Hkv, 2, d), dtype=torch.float32, device=dev)
+            # 64-byte blocks of the mean and variance rows alternate
+            self.gauss = torch.empty((Np, Hkv, d // 16, 2, 16), dtype=torch.float32, device=dev)
         if "proj" in kinds:
             assert proj is not None and proj.dtype == torch.float32 and proj.is_contiguous()
             self.kinds |= META_PROJ

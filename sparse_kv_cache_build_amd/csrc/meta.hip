@@ -32,7 +32,8 @@ __global__ __launch_bounds__(256) void meta_box_gauss_kernel(CacheView c, int ta
   for (int idx = threadIdx.x; idx < c.Hkv * c.D; idx += blockDim.x) {
     const int g = idx / c.D, j = idx - g * c.D;
     const size_t base = ((size_t)phys * c.Hkv + g) * c.S * c.D + j;
-    const size_t mo = ((size_t)phys * c.Hkv + g) * 2 * c.D + j;
+    // 64-byte blocks of the mean and variance rows alternate, so one 128-byte line holds both
+    const size_t mo = ((size_t)phys * c.Hkv + g) * 2 * c.D + (size_t)(j / 16) * 32 + (j % 16);
     if (box) {
       T lo = K[base], hi = K[base];
       float flo = Elem<T>::get(K, base), fhi = flo;
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(256) void meta_box_gauss_kernel(CacheView c, int ta
         ss += dv * dv;
       }
       gauss[mo] = (float)mu;
-      gauss[mo + c.D] = (float)(ss / n);
+      gauss[mo + 16] = (float)(ss / n);
     }
   }
 }

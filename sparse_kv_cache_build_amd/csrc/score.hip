@@ -345,10 +345,11 @@ __global__ __launch_bounds__(256) void score_lsh_kernel(CacheView c, int L, int 
 // float32, j ascending: the scores feed only the threshold estimate, whose decisions are compared
 // with a tolerance (a float32 sum of d terms is within about d 2^-24 of the sum of the absolute
 // terms). A block first stages the (q, q^2) pairs of its G query heads in LDS from q itself. A wave
-// owns 64 pages (a lane each, G heads); their rows are read in chunks of 16 coordinates (64 bytes of
-// the mean row and 64 of the variance row: 8 lanes per page, eight pages per load instruction) into
-// LDS, where each lane sums its page with the (q, q^2) pairs read as broadcasts (8 bytes per head
-// and coordinate). The next chunk is loaded while the current one is summed.
+// owns 64 pages (a lane each, G heads); their rows are read in chunks of 16 coordinates, one whole
+// 128-byte line of the metadata (64 bytes of means, then the 64 bytes of variances of the same
+// coordinates: 8 lanes per page, eight pages per load instruction) into LDS, where each lane sums
+// its page with the (q, q^2) pairs read as broadcasts (8 bytes per head and coordinate). The next
+// chunk is loaded while the current one is summed.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const T *__restrict__ q,
                                                           const float *__restrict__ gauss, float scale, int quantile,
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const T *
 #pragma unroll
   for (int k = 0; k < NK; ++k) {
     const int p = p0 + lrow + 8 * k;
-    off[k] = p < np ? (((long long)bt[p] * c.Hkv + g) * 2 + half) * D + lcol : -1;
+    off[k] = p < np ? ((long long)bt[p] * c.Hkv + g) * 2 * D + half * CW + lcol : -1;
     r[k] = off[k] >= 0 ? *reinterpret_cast<const float4 *>(gauss + off[k]) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   float *xw = xs[wave];
@@ -398,7 +399,7 @@ __global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const T *
     if (ch + 1 < NC) {
 #pragma unroll
       for (int k = 0; k < NK; ++k)
-        r[k] = off[k] >= 0 ? *reinterpret_cast<const float4 *>(gauss + off[k] + (ch + 1) * CW)
+        r[k] = off[k] >= 0 ? *reinterpret_cast<const float4 *>(gauss + off[k] + (ch + 1) * 2 * CW)
                            : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     __builtin_amdgcn_wave_barrier();   // the chunk is in LDS for every lane of the wave

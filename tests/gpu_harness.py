@@ -240,7 +240,9 @@ def _compare_gauss_scores(w, st, c, pm, spec, seqs):
     float32 accumulation of the d terms could add (d 2^-24 of the sum of absolute terms, with a
     margin), plus the final rounding to float32."""
     ga = st.meta.gauss[torch.from_numpy(pm).to(w.k.device)].cpu().numpy().astype(np.float64)
-    mean, var = np.ascontiguousarray(ga[:, :, 0]), np.ascontiguousarray(ga[:, :, 1])
+    n_, h_ = ga.shape[:2]   # [n, Hkv, d / 16, 2, 16]: mean and variance blocks alternate
+    mean = np.ascontiguousarray(ga[:, :, :, 0].reshape(n_, h_, -1))
+    var = np.ascontiguousarray(ga[:, :, :, 1].reshape(n_, h_, -1))
     scale = pipeline.scale_of(spec, c.d)
     m, s, shat = oracle.score_gauss(c, mean, var, scale, spec.gauss_max == "quantile")
     sc = st.scores
@@ -412,9 +414,10 @@ def _compare_meta(w, st, c, md, pm, spec):
         assert np.array_equal(box[:, :, :, 0].reshape(n_, h_, -1), md.kmin[used]), "kmin mismatch"
         assert np.array_equal(box[:, :, :, 1].reshape(n_, h_, -1), md.kmax[used]), "kmax mismatch"
     elif spec.score == "gauss":
-        ga = st.meta.gauss[gp].cpu().numpy()
-        assert np.array_equal(ga[:, :, 0], md.mean[used].astype(np.float32)), "mean mismatch"
-        assert np.array_equal(ga[:, :, 1], md.var[used].astype(np.float32)), "var mismatch"
+        ga = st.meta.gauss[gp].cpu().numpy()           # [n, Hkv, d / 16, 2, 16]: mean and variance blocks alternate
+        n_, h_ = ga.shape[:2]
+        assert np.array_equal(ga[:, :, :, 0].reshape(n_, h_, -1), md.mean[used].astype(np.float32)), "mean mismatch"
+        assert np.array_equal(ga[:, :, :, 1].reshape(n_, h_, -1), md.var[used].astype(np.float32)), "var mismatch"
     elif spec.score == "pool":
         po = st.meta.pool[gp].cpu().numpy()            # [n, Hkv, S/pb, d]; sub-blocks with a token only
         owner = {}
