@@ -279,14 +279,17 @@ def reference_ceilings(dev, n_rows: int, row_bytes: int, reps: int = 5):
     """Bandwidth ceilings on this GPU from the reference kernels of libskv_ref.so (context for the
     roofline fractions): a plain streaming read of 1 GiB; a gather of n_rows random rows of
     row_bytes, twice (K and V rows, as the attention reads them), from a 4 GiB table, each row read
-    by a group of row_bytes / 16 lanes; and torch's 1 GiB copy (read + write)."""
+    by a group of row_bytes / 16 lanes; and torch's 1 GiB copy (read + write). The reads are timed
+    at several grid sizes, with plain and with non-temporal loads; the best of each is reported,
+    with every configuration's figure."""
     import ctypes as C
     ref = C.CDLL(os.path.join(ROOT, "sparse_kv_cache_build_amd", "libskv_ref.so"))
-    ref.skv_ref_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
-    ref.skv_ref_gather_rows.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_void_p]
+    ref.skv_ref_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_int, C.c_void_p]
+    ref.skv_ref_gather_rows.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_int,
+                                        C.c_void_p]
     stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
-    blocks = 256 * 8
-    sink = torch.empty(blocks, dtype=torch.int32, device=dev)
+    grids = (512, 1024, 2048, 4096, 8192)
+    sink = torch.empty(max(grids), dtype=torch.int32, device=dev)
 
     def timed(fn):
         fn()
@@ -302,10 +305,19 @@ def reference_ceilings(dev, n_rows: int, row_bytes: int, reps: int = 5):
     def ok(rc):
         assert rc == 0, rc
 
+    def sweep(nbytes, launch):
+        res = {f"{'nt' if nt else 'plain'}_{bl}": round(nbytes / timed(lambda: ok(launch(bl, nt))) / 1e9, 1)
+               for nt in (0, 1) for bl in grids}
+        best = max(res, key=res.get)
+        return res[best], best, res
+
     out = {}
     src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
-    t = timed(lambda: ok(ref.skv_ref_stream_read(src.data_ptr(), (1 << 30) // 16, sink.data_ptr(), blocks, stream)))
-    out["stream_read_1GiB_GBps"] = round((1 << 30) / t / 1e9, 1)
+    best, how, res = sweep(1 << 30, lambda bl, nt: ref.skv_ref_stream_read(src.data_ptr(), (1 << 30) // 16,
+                                                                            sink.data_ptr(), bl, nt, stream))
+    out["stream_read_1GiB_GBps"] = best
+    out["stream_read_best"] = how
+    out["stream_read_sweep"] = res
     dst = torch.empty_like(src)
     t = timed(lambda: dst.copy_(src))
     out["copy_1GiB_GBps"] = round(2 * (1 << 30) / t / 1e9, 1)
@@ -317,11 +329,13 @@ def reference_ceilings(dev, n_rows: int, row_bytes: int, reps: int = 5):
     g.manual_seed(7)
     rows_in_table = (4 << 30) // row_bytes
     off = (torch.randint(0, rows_in_table, (2 * n_rows,), generator=g, device=dev) * words).to(torch.int64)
-    t = timed(lambda: ok(ref.skv_ref_gather_rows(table.data_ptr(), off.data_ptr(), 2 * n_rows, words,
-                                                   sink.data_ptr(), blocks, stream)))
+    best, how, res = sweep(2 * n_rows * row_bytes, lambda bl, nt: ref.skv_ref_gather_rows(
+        table.data_ptr(), off.data_ptr(), 2 * n_rows, words, sink.data_ptr(), bl, nt, stream))
     out["gather_rows"] = 2 * n_rows
     out["gather_row_bytes"] = row_bytes
-    out["gather_GBps"] = round(2 * n_rows * row_bytes / t / 1e9, 1)
+    out["gather_GBps"] = best
+    out["gather_best"] = how
+    out["gather_sweep"] = res
     del table, off
     torch.cuda.empty_cache()
     return out
@@ -482,7 +496,8 @@ def main():
                    "select": "every page (full-cache comparator)" if args.full else sel_desc[cfg["policy"]],
                    "attn": "softmax" if alpha == 1.0 else f"{alpha}-entmax", "bytes_per_step": int(total),
                    "achieved_GBps": round(gbps, 1), "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
-                   "accumulation": "fp32 (attention), fp64 (ranking keys)",
+                   "accumulation": ("fp32 (Gaussian page scores, attention)" if cfg["score"] in ("gauss", "gauss_q")
+                                    else "fp32 (attention), fp64 (ranking keys)"),
                    "buffer_sets": n_sets, "hip_graphs": graphs, "meta_build_s": round(meta_s, 6),
                    "meta_build_GBps": round(meta_read_bytes(w0) / meta_s / 1e9, 1),
                    "meta_append_us": round(append_us, 2),
