@@ -519,84 +519,43 @@ static double orc_phi(double a) { return exp(-0.5 * a * a) / sqrt(2.0 * acos(-1.
 
 /* I_k(a) = integral over u >= 0 of u^k phi(u - a) du, the k-th truncated power moment of a unit
  * Gaussian shifted by a: E[(Z + a)_+^k] for Z ~ N(0, 1). The integrand is below 1e-40 of its peak
- * outside [max(0, a - 14), max(a, 0) + 14] (u^k grows with u). Adaptive Gauss-Legendre on panels
- * of width at most 1/2 over that range: a 20-point
- * rule on an interval is accepted when it agrees with the rule on its two halves to 1e-14
- * relative, else both halves are refined. The 20 nodes and weights are the roots of the Legendre
- * polynomial P_20 (Newton from the Chebyshev-like guesses) and 2 / ((1 - x^2) P_20'(x)^2). On the
- * panel that starts at 0 the variable is u = h v^2, so that the u^k endpoint becomes the smooth
- * v^(2k+1). */
-#define ORC_GL_N 20
-static double orc_gl_x[ORC_GL_N], orc_gl_w[ORC_GL_N];
-static int orc_gl_ready = 0;
-
-static void orc_gl_init(void) {
-  const int n = ORC_GL_N;
-  for (int i = 0; i < n; ++i) {
-    double x = cos(acos(-1.0) * (i + 0.75) / (n + 0.5)), dp = 1.0;
-    for (int it = 0; it < 100; ++it) {
-      double p0 = 1.0, p1 = x;   /* P_0, P_1; then the three-term recurrence up to P_n */
-      for (int m = 2; m <= n; ++m) {
-        double p2 = ((2.0 * m - 1.0) * x * p1 - (m - 1.0) * p0) / m;
-        p0 = p1;
-        p1 = p2;
-      }
-      dp = n * (x * p1 - p0) / (x * x - 1.0);
-      double dx = p1 / dp;
-      x -= dx;
-      if (fabs(dx) < 1e-16) break;
-    }
-    orc_gl_x[i] = x;
-    orc_gl_w[i] = 2.0 / ((1.0 - x * x) * dp * dp);
-  }
-  orc_gl_ready = 1;
+ * outside [max(0, a - 14), max(a, 0) + 14] (u^k grows with u), and that interval is integrated by
+ * the tanh-sinh (double-exponential) rule of Takahasi and Mori (1974): u = c + w tanh(x) with
+ * x = (pi/2) sinh t, du = w (pi/2) cosh t / cosh^2 x dt, and the trapezoid rule in t over
+ * [-4, 4] (beyond, the weights are below 1e-60 of the interval), its step halved until two
+ * successive levels agree to 1e-15 relative (at least five levels). The change of variable
+ * clusters the nodes at both ends, which absorbs the u^k behaviour at u = 0 for fractional k.
+ * Points near an end are placed by their distance to it, 2 w / (1 + e^(2|x|)), which keeps them
+ * accurate where tanh(x) rounds to +-1. */
+static double orc_ts_term(double a, double k, double l, double r, double t) {
+  const double hw = 0.5 * (r - l), x = 0.5 * acos(-1.0) * sinh(t);
+  if (fabs(x) > 350.0) return 0.0;
+  const double d = 2.0 * hw / (1.0 + exp(2.0 * fabs(x)));   /* distance from the nearer end */
+  const double u = x > 0.0 ? r - d : l + d;
+  const double ch = cosh(x);
+  const double wt = hw * 0.5 * acos(-1.0) * cosh(t) / (ch * ch);
+  return wt * pow(u, k) * exp(-0.5 * (u - a) * (u - a));
 }
 
-/* the integrand on [l, r]; sq: the panel variable is v with u = sq * v^2 */
-static double orc_gl_rule(double a, double k, double l, double r, double sq) {
-  double c = 0.5 * (l + r), h = 0.5 * (r - l), sum = 0.0;
-  for (int i = 0; i < ORC_GL_N; ++i) {
-    double t = c + h * orc_gl_x[i], u = t, jac = 1.0;
-    if (sq > 0.0) {
-      u = sq * t * t;
-      jac = 2.0 * sq * t;
-    }
-    sum += orc_gl_w[i] * pow(u, k) * exp(-0.5 * (u - a) * (u - a)) * jac;
+static double orc_tanh_sinh(double a, double k, double l, double r) {
+  const double T = 4.0;
+  double h = 0.5, sum = orc_ts_term(a, k, l, r, 0.0);
+  for (double t = h; t <= T; t += h) sum += orc_ts_term(a, k, l, r, t) + orc_ts_term(a, k, l, r, -t);
+  double prev = h * sum;
+  for (int level = 1; level <= 14; ++level) {
+    h *= 0.5;   /* the new nodes are the odd multiples of the halved step */
+    for (double t = h; t <= T; t += 2.0 * h) sum += orc_ts_term(a, k, l, r, t) + orc_ts_term(a, k, l, r, -t);
+    const double cur = h * sum;
+    if (level >= 5 && fabs(cur - prev) <= 1e-15 * fabs(cur)) return cur;
+    prev = cur;
   }
-  return h * sum;
-}
-
-static double orc_gl_adapt(double a, double k, double l, double r, double sq, double whole, double floor_abs,
-                           int depth) {
-  double m = 0.5 * (l + r);
-  double left = orc_gl_rule(a, k, l, m, sq), right = orc_gl_rule(a, k, m, r, sq);
-  double diff = fabs(left + right - whole);
-  if (depth <= 0 || diff <= 1e-14 * fabs(left + right) || diff <= floor_abs) return left + right;
-  return orc_gl_adapt(a, k, l, m, sq, left, floor_abs, depth - 1) +
-         orc_gl_adapt(a, k, m, r, sq, right, floor_abs, depth - 1);
+  return prev;
 }
 
 double orc_trunc_power_moment(double a, double k) {
-  if (!orc_gl_ready) orc_gl_init();
   if (a < -40.0) return 0.0;
-  /* u^k grows with u, so below u = a - 14 the integrand is also below 1e-40 of its peak */
-  double L0 = a > 14.0 ? a - 14.0 : 0.0, U = (a > 0.0 ? a : 0.0) + 14.0;
-  int panels = (int)ceil((U - L0) / 0.5);
-  double h = (U - L0) / panels, sum = 0.0, est[64], coarse = 0.0;
-  /* a coarse pass first: a panel whose refinement changes less than 1e-16 of the whole integral
-   * is accepted even where its own relative change stays larger (near underflow) */
-  for (int i = 0; i < panels; ++i) {
-    int at0 = i == 0 && L0 == 0.0;   /* a first panel at 0 in v over [0, 1] with u = h v^2 */
-    double l = at0 ? 0.0 : L0 + i * h, r = at0 ? 1.0 : L0 + (i + 1) * h, sq = at0 ? h : 0.0;
-    est[i] = orc_gl_rule(a, k, l, r, sq);
-    coarse += fabs(est[i]);
-  }
-  for (int i = 0; i < panels; ++i) {
-    int at0 = i == 0 && L0 == 0.0;
-    double l = at0 ? 0.0 : L0 + i * h, r = at0 ? 1.0 : L0 + (i + 1) * h, sq = at0 ? h : 0.0;
-    sum += orc_gl_adapt(a, k, l, r, sq, est[i], 1e-16 * coarse, 25);
-  }
-  return sum / sqrt(2.0 * acos(-1.0));
+  const double L0 = a > 14.0 ? a - 14.0 : 0.0, U = (a > 0.0 ? a : 0.0) + 14.0;
+  return orc_tanh_sinh(a, k, L0, U) / sqrt(2.0 * acos(-1.0));
 }
 
 /* E[(X - tau)_+^(1/(alpha-1))] for X ~ N(mu_x, sd_x^2). With mu = mu_x - tau and a = mu / sd:

@@ -71,7 +71,11 @@ MUTANTS = {
     "normalisation equation without the token counts": [
         ("if (n[p] > 0) f += n[p] * orc_gauss_partial_moment(", "if (n[p] > 0) f += orc_gauss_partial_moment(")],
     "truncated power moment with the wrong normal constant": [
-        ("return sum / sqrt(2.0 * acos(-1.0));", "return sum / sqrt(acos(-1.0));")],
+        ("return orc_tanh_sinh(a, k, L0, U) / sqrt(2.0 * acos(-1.0));", "return orc_tanh_sinh(a, k, L0, U) / sqrt(acos(-1.0));")],
+    "tanh-sinh weight without the cosh t factor": [
+        ("const double wt = hw * 0.5 * acos(-1.0) * cosh(t) / (ch * ch);", "const double wt = hw * 0.5 * acos(-1.0) / (ch * ch);")],
+    "tanh-sinh node distance from its end halved": [
+        ("const double d = 2.0 * hw / (1.0 + exp(2.0 * fabs(x)));", "const double d = hw / (1.0 + exp(2.0 * fabs(x)));")],
     "threshold margin added instead of subtracted": [
         ("> tau_hat[hh] - delta) keep = 1;", "> tau_hat[hh] + delta) keep = 1;")],
     "box threshold against the largest head threshold": [
