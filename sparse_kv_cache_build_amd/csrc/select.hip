@@ -916,8 +916,11 @@ __global__ __launch_bounds__(kTauThreads) void tau_hat_kernel(CacheView c, const
 }
 
 // Keep page p of unit (b, g) iff some head h of g has (alpha-1) shat_h(p) > tau_h - delta;
-// ordered compaction.
+// ordered compaction. Each thread takes kThreshPPT consecutive pages of a tile, with the loads of
+// all of them (and of every head) issued before the tests, so a tile costs one round of loads and
+// one block scan.
 constexpr int kThreshThreads = 1024;
+constexpr int kThreshPPT = 4;
 __global__ __launch_bounds__(kThreshThreads) void select_thresh_kernel(CacheView c, const float *__restrict__ shat,
                                                                        const float *__restrict__ tau, float alpha,
                                                                        float delta, int32_t *__restrict__ sel_idx,
@@ -928,17 +931,29 @@ __global__ __launch_bounds__(kThreshThreads) void select_thresh_kernel(CacheView
   const float am1 = alpha - 1.0f;
   int32_t *out = sel_idx + (size_t)unit * cap;
   int base = 0;
-  for (int p0 = 0; p0 < P; p0 += kThreshThreads) {
-    const int p = p0 + threadIdx.x;
-    int keep = 0;
-    if (p < P)
-      for (int h = 0; h < c.G; ++h) {
-        const int bh = b * c.Hq + g * c.G + h;
-        if (am1 * shat[(size_t)bh * c.maxP + p] > tau[bh] - delta) keep = 1;
-      }
+  for (int t0 = 0; t0 < P; t0 += kThreshThreads * kThreshPPT) {
+    const int p0 = t0 + threadIdx.x * kThreshPPT;
+    bool keep[kThreshPPT];
+#pragma unroll
+    for (int u = 0; u < kThreshPPT; ++u) keep[u] = false;
+    for (int h = 0; h < c.G; ++h) {
+      const int bh = b * c.Hq + g * c.G + h;
+      const float bar = tau[bh] - delta;
+      const float *sr = shat + (size_t)bh * c.maxP;
+      float x[kThreshPPT];
+#pragma unroll
+      for (int u = 0; u < kThreshPPT; ++u) x[u] = p0 + u < P ? sr[p0 + u] : -INFINITY;
+#pragma unroll
+      for (int u = 0; u < kThreshPPT; ++u) keep[u] = keep[u] || am1 * x[u] > bar;
+    }
+    int n = 0;
+#pragma unroll
+    for (int u = 0; u < kThreshPPT; ++u) n += keep[u] ? 1 : 0;
     int tot;
-    const int pos = block_excl_scan<kThreshThreads>(keep, scan_scratch, &tot);
-    if (keep) out[base + pos] = p;
+    int pos = base + block_excl_scan<kThreshThreads>(n, scan_scratch, &tot);
+#pragma unroll
+    for (int u = 0; u < kThreshPPT; ++u)
+      if (keep[u]) out[pos++] = p0 + u;
     base += tot;
   }
   if (threadIdx.x == 0) sel_count[unit] = base;
@@ -962,18 +977,27 @@ __global__ __launch_bounds__(kThreshThreads) void select_thresh_box_kernel(Cache
   const float *kr = key + (size_t)unit * c.maxP;
   int32_t *out = sel_idx + (size_t)unit * cap;
   int base = 0;
-  for (int p0 = 0; p0 < P; p0 += kThreshThreads) {
-    const int p = p0 + threadIdx.x;
-    const int keep = p < P && f * kr[p] > bar;
+  for (int t0 = 0; t0 < P; t0 += kThreshThreads * kThreshPPT) {
+    const int p0 = t0 + threadIdx.x * kThreshPPT;
+    float x[kThreshPPT];
+#pragma unroll
+    for (int u = 0; u < kThreshPPT; ++u) x[u] = p0 + u < P ? kr[p0 + u] : -INFINITY;
+    bool keep[kThreshPPT];
+    int n = 0;
+#pragma unroll
+    for (int u = 0; u < kThreshPPT; ++u) {
+      keep[u] = p0 + u < P && f * x[u] > bar;
+      n += keep[u] ? 1 : 0;
+    }
     int tot;
-    const int pos = block_excl_scan<kThreshThreads>(keep, scan_scratch, &tot);
-    if (keep) out[base + pos] = p;
+    int pos = base + block_excl_scan<kThreshThreads>(n, scan_scratch, &tot);
+#pragma unroll
+    for (int u = 0; u < kThreshPPT; ++u)
+      if (keep[u]) out[pos++] = p0 + u;
     base += tot;
   }
   if (threadIdx.x == 0) sel_count[unit] = base;
 }
-
-// ---------------------------------------------------------------- launchers
 
 hipError_t launch_select_topk(const CacheView &c, const float *key, int key_stride, int policy, int k, int pct,
                               int32_t *sel_idx, int32_t *sel_count, int cap, hipStream_t st) {
