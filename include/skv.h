@@ -285,7 +285,9 @@ typedef struct skv_attn_params {
  * sel_idx / sel_count / cap are as written by skv_select_pages (indices ascending, within the
  * sequence; others are skipped). out [B, Hq, d] float32; an empty selection gives zeros.
  * workspace: skv_workspace_bytes(c, SKV_OP_ATTN, p, cap). Errors: SKV_ERR_INVALID_ARG,
- * SKV_ERR_UNSUPPORTED, SKV_ERR_WORKSPACE, SKV_ERR_HIP. */
+ * SKV_ERR_UNSUPPORTED (also: entmax over a bf16 cache of 2^32 - 1 or more KV rows,
+ * num_phys_pages * num_kv_heads * page_size, more than device memory holds), SKV_ERR_WORKSPACE,
+ * SKV_ERR_HIP. */
 skv_status skv_sparse_decode_attn(const skv_cache *c, const void *q, const int32_t *sel_idx,
                                   const int32_t *sel_count, int32_t cap, const skv_attn_params *p, float *out,
                                   void *workspace, size_t workspace_bytes, void *stream);

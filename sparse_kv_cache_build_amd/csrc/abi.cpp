@@ -100,7 +100,7 @@ skv_status attn_plan(const skv_cache *c, const skv_attn_params *p, int cap, Attn
   const int64_t nsplit = (cap + spi - 1) / spi;
   const int64_t rps = spi * rows_per_item;
   // LDS of a partition: logits (entmax) and row offsets
-  if (entmax && (int64_t)G * rps * 4 + rps * 8 + 8 > 65536) return SKV_ERR_UNSUPPORTED;
+  if (entmax && (int64_t)G * 4 * ((rps + 3) / 4) * 4 + rps * 8 + 8 > 65536) return SKV_ERR_UNSUPPORTED;
   if (!entmax && rps * 8 > 32768) return SKV_ERR_UNSUPPORTED;
   out->spi = (int)spi;
   out->nsplit = (int)nsplit;
@@ -465,6 +465,11 @@ static skv_status attn_check(const skv_cache *c, const void *q, const int32_t *s
   if (!q || !sel_idx || !sel_count || !out || cap < 1) return SKV_ERR_INVALID_ARG;
   if (!aligned(q, 16)) return SKV_ERR_INVALID_ARG;
   if ((st = check_attn_params(p)) != SKV_OK) return st;
+  // the entmax logits kernel of bf16 caches keeps 32-bit row indices (any cache that fits in
+  // device memory has fewer than 2^32 - 1 rows)
+  if (p->alpha != 1.0f && c->dtype == SKV_DTYPE_BF16 &&
+      (uint64_t)c->num_phys_pages * c->num_kv_heads * c->page_size >= 0xffffffffull)
+    return SKV_ERR_UNSUPPORTED;
   return attn_plan(c, p, cap, plan);
 }
 

@@ -51,6 +51,11 @@ struct RowMap {
   __device__ __forceinline__ long long row_offset(int item, int t_in_page) const {
     return offset_of(sel[item], t_in_page);
   }
+  // the row's index in K / V ([Nphys, Hkv, S] rows of D elements), or -1
+  __device__ __forceinline__ long long row_index(int item, int t_in_page) const {
+    const long long o = offset_of(sel[item], t_in_page);
+    return o < 0 ? -1 : o / D;
+  }
   // the same from the selection entry e (a token, or a page) already read
   __device__ __forceinline__ long long offset_of(int e, int t_in_page) const {
     int page, t;
@@ -249,33 +254,47 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(CacheView c, const int3
 
 // ---------------------------------------------------------------- entmax pass 1
 
+// Logits of an entmax partition in LDS: head h, row r at h * 4 q + (r mod 4) q + r / 4 with
+// q = ceil(rps / 4). A thread of the compaction below reads a run of consecutive rows; with this
+// layout the threads of a wave read consecutive words at every step, so the reads are free of
+// bank conflicts (row-major, a stride of four words, they conflicted four ways).
+struct ZLayout {
+  int q;
+  __device__ __forceinline__ explicit ZLayout(int rps) : q((rps + 3) >> 2) {}
+  __device__ __forceinline__ int at(int h, int r) const { return h * 4 * q + (r & 3) * q + (r >> 2); }
+  __device__ __forceinline__ int floats(int g) const { return g * 4 * q; }
+};
+
 // Per-head maximum and ordered compaction of z' > max - 1 for pass 1 (logits of the partition
-// in LDS: zs[h * rps + r]; rows past NR are not read). All G heads at once: every thread takes a
-// contiguous chunk of rows, so the thread order is the row order; the maxima and the survivor
-// counts of the G heads are combined over the block with one barrier each. Every thread of the
-// block must call it.
+// in LDS as ZLayout; rows past NR are not read). All G heads at once: every thread takes a
+// contiguous chunk of rows, so the thread order is the row order; the survivor counts of the G
+// heads are combined over the block with one barrier. The per-wave maxima of the heads are in
+// wmax: filled by the caller when have_max (then published by a barrier before the call), else
+// computed here from the LDS logits. Every thread of the block must call it.
 template <int G>
-__device__ __forceinline__ void entmax_compact(const float *zs, int rps, int NR, int unit, int split, int nsplit,
-                                               int row0, float2 *__restrict__ cand, int32_t *__restrict__ cand_cnt,
+__device__ __forceinline__ void entmax_compact(const float *zs, ZLayout zl, int rps, int NR, int unit, int split,
+                                               int nsplit, int row0, float (*wmax)[G], bool have_max,
+                                               float2 *__restrict__ cand, int32_t *__restrict__ cand_cnt,
                                                float *__restrict__ cand_max) {
   constexpr int NW = kAttnThreads / kWave;
-  __shared__ float wmax[NW][G];
   __shared__ int wcnt[NW][G];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const int per = (NR + kAttnThreads - 1) / kAttnThreads;
   const int r0 = min(NR, tid * per), r1 = min(NR, r0 + per);
   float mx[G];
+  if (!have_max) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) mx[h] = -INFINITY;
-  for (int r = r0; r < r1; ++r)
+    for (int h = 0; h < G; ++h) mx[h] = -INFINITY;
+    for (int r = r0; r < r1; ++r)
 #pragma unroll
-    for (int h = 0; h < G; ++h) mx[h] = fmaxf(mx[h], zs[h * rps + r]);
+      for (int h = 0; h < G; ++h) mx[h] = fmaxf(mx[h], zs[zl.at(h, r)]);
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float m = wave_max_dpp(mx[h]);
-    if (lane == 0) wmax[w][h] = m;
+    for (int h = 0; h < G; ++h) {
+      const float m = wave_max_dpp(mx[h]);
+      if (lane == 0) wmax[w][h] = m;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   int nk[G], incl[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -287,7 +306,7 @@ __device__ __forceinline__ void entmax_compact(const float *zs, int rps, int NR,
   }
   for (int r = r0; r < r1; ++r)
 #pragma unroll
-    for (int h = 0; h < G; ++h) nk[h] += zs[h * rps + r] > mx[h] - 1.0f ? 1 : 0;
+    for (int h = 0; h < G; ++h) nk[h] += zs[zl.at(h, r)] > mx[h] - 1.0f ? 1 : 0;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     incl[h] = wave_incl_scan(nk[h]);
@@ -307,7 +326,7 @@ __device__ __forceinline__ void entmax_compact(const float *zs, int rps, int NR,
     float2 *cl = cand + lid * rps;
     int pos = before + incl[h] - nk[h];
     for (int r = r0; r < r1; ++r) {
-      const float z = zs[h * rps + r];
+      const float z = zs[zl.at(h, r)];
       if (z > mx[h] - 1.0f) cl[pos++] = make_float2(z, __int_as_float(row0 + r));
     }
     if (tid == 0) {
@@ -324,11 +343,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
     int cap, int gran, int spi, int nsplit, float zscale, float2 *__restrict__ cand, int32_t *__restrict__ cand_cnt,
     float *__restrict__ cand_max) {
   using RL = RowLayout<D>;
-  extern __shared__ float zs[];  // [G][rps] logits, then [rps] row offsets (8-byte aligned)
+  extern __shared__ float zs[];  // logits (ZLayout), then [rps] row offsets (8-byte aligned)
+  __shared__ float wmax[kAttnThreads / kWave][G];
   const int split = blockIdx.x, unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
   const int count = min(max(sel_count[unit], 0), cap);
   const int rows_per_item = gran ? 1 : c.S;
   const int rps = spi * rows_per_item;
+  const ZLayout zl(rps);
   const int ipb = items_per_split(count, nsplit);
   const int it0 = split * ipb, it1 = min(count, it0 + ipb);
   if (it0 >= count) return;   // past the splits in use: the solve reads none of its lists
@@ -352,10 +373,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
     for (int h = 0; h < G; ++h) {
       float z = 0.0f;
       if (off >= 0) z = group_sum<RL::LPR>(qv[h].dot(kx)) * zscale;
-      if (lr == h % RL::LPR) zs[h * rps + r] = off >= 0 ? z : -INFINITY;
+      if (lr == h % RL::LPR) zs[zl.at(h, r)] = off >= 0 ? z : -INFINITY;
     }
   };
-  long long *roff = reinterpret_cast<long long *>(zs + ((G * rps + 1) & ~1));
+  long long *roff = reinterpret_cast<long long *>(zs + ((zl.floats(G) + 1) & ~1));
   for (int r = tid; r < NR; r += kAttnThreads) roff[r] = row_off(r);
   __syncthreads();
   constexpr int UNR = 4;
@@ -373,7 +394,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
       if (r + u * RL::RGB < NR) logits(r + u * RL::RGB, o[u], kx[u]);
   }
   __syncthreads();
-  entmax_compact<G>(zs, rps, NR, unit, split, nsplit, it0 * rows_per_item, cand, cand_cnt, cand_max);
+  entmax_compact<G>(zs, zl, rps, NR, unit, split, nsplit, it0 * rows_per_item, wmax, false, cand, cand_cnt, cand_max);
 }
 
 // Entmax pass 1 for bf16 caches on the matrix cores: the logits of a 16-row tile for all G heads
@@ -390,11 +411,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_mfma_kernel(
     const int32_t *__restrict__ sel_count, int cap, int gran, int spi, int nsplit, float zscale,
     float2 *__restrict__ cand, int32_t *__restrict__ cand_cnt, float *__restrict__ cand_max) {
   constexpr int KB = D / 32, UNR = 4, NWV = kAttnThreads / kWave;
-  extern __shared__ float zs[];  // [G][rps] logits, then [rps] row offsets (8-byte aligned)
+  extern __shared__ float zs[];  // logits (ZLayout), then [rps] row offsets (8-byte aligned)
+  __shared__ float wmax[kAttnThreads / kWave][G];
   const int split = blockIdx.x, unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
   const int count = min(max(sel_count[unit], 0), cap);
   const int rows_per_item = gran ? 1 : c.S;
   const int rps = spi * rows_per_item;
+  const ZLayout zl(rps);
   const int ipb = items_per_split(count, nsplit);
   const int it0 = split * ipb, it1 = min(count, it0 + ipb);
   if (it0 >= count) return;   // past the splits in use: the solve reads none of its lists
@@ -410,24 +433,29 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_mfma_kernel(
     if (n < G) w = *reinterpret_cast<const uint4 *>(q + ((size_t)b * c.Hq + g * G + n) * D + 32 * kb + kq);
     qb[kb] = __builtin_bit_cast(bf16x8_t, w);
   }
-  long long *roff = reinterpret_cast<long long *>(zs + ((G * rps + 1) & ~1));
+  // row indices (not element offsets: half the LDS, which keeps four workgroups per CU at G = 8);
+  // every row of a cache that fits in memory has an index below 2^32 - 1
+  uint32_t *ridx = reinterpret_cast<uint32_t *>(zs + zl.floats(G));
   for (int r = tid; r < NR; r += kAttnThreads) {
     const int it = r / rows_per_item;
-    roff[r] = rm.row_offset(it0 + it, r - it * rows_per_item);
+    const long long ri = rm.row_index(it0 + it, r - it * rows_per_item);
+    ridx[r] = ri < 0 ? 0xffffffffu : (uint32_t)ri;
   }
   __syncthreads();
   const uint16_t *K = static_cast<const uint16_t *>(c.k);
   const int ntile = (NR + 15) / 16;
+  float mxl = -INFINITY;   // the largest logit of head n among this lane's rows
   for (int t0 = wave; t0 < ntile; t0 += NWV * UNR) {
     bf16x8_t a[UNR][KB];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int row = (t0 + u * NWV) * 16 + (lane & 15);
-      const long long o = row < NR ? roff[row] : -1;
+      const uint32_t ri = row < NR ? ridx[row] : 0xffffffffu;
+      const uint16_t *kr = K + (size_t)ri * D;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         uint4 w = make_uint4(0u, 0u, 0u, 0u);
-        if (o >= 0) w = *reinterpret_cast<const uint4 *>(K + o + 32 * kb + kq);
+        if (ri != 0xffffffffu) w = *reinterpret_cast<const uint4 *>(kr + 32 * kb + kq);
         a[u][kb] = __builtin_bit_cast(bf16x8_t, w);
       }
     }
@@ -442,13 +470,21 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = tb + 4 * (lane >> 4) + i;
-          if (r < NR) zs[n * rps + r] = roff[r] >= 0 ? acc[i] * zscale : -INFINITY;
+          if (r < NR) {
+            const float v = ridx[r] != 0xffffffffu ? acc[i] * zscale : -INFINITY;
+            zs[zl.at(n, r)] = v;
+            mxl = fmaxf(mxl, v);
+          }
         }
       }
     }
   }
+  // the lanes of head n (n, n + 16, n + 32, n + 48) hold disjoint row sets
+  mxl = fmaxf(mxl, __shfl_xor(mxl, 16, kWave));
+  mxl = fmaxf(mxl, __shfl_xor(mxl, 32, kWave));
+  if (lane < G) wmax[wave][lane] = mxl;
   __syncthreads();
-  entmax_compact<G>(zs, rps, NR, unit, split, nsplit, it0 * rows_per_item, cand, cand_cnt, cand_max);
+  entmax_compact<G>(zs, zl, rps, NR, unit, split, nsplit, it0 * rows_per_item, wmax, true, cand, cand_cnt, cand_max);
 }
 
 // ---------------------------------------------------------------- entmax threshold and p V
@@ -856,12 +892,14 @@ static hipError_t attn_typed(const AttnArgs &a, hipStream_t st) {
     return hipGetLastError();
   }
   const int rps = a.spi * (a.gran ? 1 : c.S);
-  const size_t lds = sizeof(float) * (size_t)((c.G * rps + 1) & ~1) + sizeof(long long) * (size_t)rps;
+  const int zq = (rps + 3) / 4;   // ZLayout of the logits
+  const size_t lds = sizeof(float) * (size_t)((c.G * 4 * zq + 1) & ~1) + sizeof(long long) * (size_t)rps;
+  const size_t lds_mfma = sizeof(float) * (size_t)(c.G * 4 * zq) + sizeof(uint32_t) * (size_t)rps;   // 32-bit row indices
   const float zscale = a.sm_scale * (a.alpha - 1.0f);
   hipError_t e0 = a.ev.before(st);
   if (e0 != hipSuccess) return e0;
   if constexpr (std::is_same<T, uint16_t>::value) {   // bf16: logits on the matrix cores
-    SKV_ATTN_DISPATCH_G(c.G, attn_entmax_logits_mfma_kernel<D, GG><<<grid, kAttnThreads, lds, st>>>(
+    SKV_ATTN_DISPATCH_G(c.G, attn_entmax_logits_mfma_kernel<D, GG><<<grid, kAttnThreads, lds_mfma, st>>>(
                                  c, q, a.sel_idx, a.sel_count, a.cap, a.gran, a.spi, a.nsplit, zscale, a.cand,
                                  a.cand_cnt, a.cand_max))
   } else {
