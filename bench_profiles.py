@@ -54,10 +54,11 @@ PASSES = {
 }
 
 # the source files a scoring kernel's HBM traffic depends on: its own file, the shared device
-# helpers and launch declarations, the metadata layout it reads, the host planner, the workload draw
+# helpers and launch declarations, the metadata layout it reads (written by meta.hip, sized by the
+# binding), the host planner, the workload draw
 TRAFFIC_SOURCES = ["sparse_kv_cache_build_amd/csrc/common.hpp", "sparse_kv_cache_build_amd/csrc/launch.hpp",
                    "sparse_kv_cache_build_amd/csrc/meta.hip", "sparse_kv_cache_build_amd/csrc/abi.cpp",
-                   "workloads/__init__.py"]
+                   "sparse_kv_cache_build_amd/_binding.py", "workloads/__init__.py"]
 
 
 def short(name: str) -> str:
