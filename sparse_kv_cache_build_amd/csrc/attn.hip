@@ -32,6 +32,13 @@ namespace skv {
 __device__ __forceinline__ int items_per_split(int count, int nsplit) {
   return max(1, (count + nsplit - 1) / nsplit);
 }
+// The same for the entmax passes, with at least two pages per split (never more than the planned
+// spi, so a split stays within its LDS and list capacity): a short selection then runs as fewer,
+// fuller partitions, each with fewer lists for the solve to merge.
+__device__ __forceinline__ int entmax_items_per_split(int count, int nsplit, int spi, int rows_per_item) {
+  const int least = min(spi, rows_per_item > 1 ? 2 : 1);
+  return max(least, (count + nsplit - 1) / nsplit);
+}
 
 constexpr int kAttnThreads = 256;
 
@@ -350,7 +357,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
   const int rows_per_item = gran ? 1 : c.S;
   const int rps = spi * rows_per_item;
   const ZLayout zl(rps);
-  const int ipb = items_per_split(count, nsplit);
+  const int ipb = entmax_items_per_split(count, nsplit, spi, rows_per_item);
   const int it0 = split * ipb, it1 = min(count, it0 + ipb);
   if (it0 >= count) return;   // past the splits in use: the solve reads none of its lists
   const int NR = max(0, it1 - it0) * rows_per_item;
@@ -418,7 +425,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_mfma_kernel(
   const int rows_per_item = gran ? 1 : c.S;
   const int rps = spi * rows_per_item;
   const ZLayout zl(rps);
-  const int ipb = items_per_split(count, nsplit);
+  const int ipb = entmax_items_per_split(count, nsplit, spi, rows_per_item);
   const int it0 = split * ipb, it1 = min(count, it0 + ipb);
   if (it0 >= count) return;   // past the splits in use: the solve reads none of its lists
   const int NR = max(0, it1 - it0) * rows_per_item;
@@ -522,7 +529,7 @@ __global__ __launch_bounds__(kWave) void attn_entmax_solve_kernel(
   const int count = min(max(sel_count[unit], 0), cap);
   const int rows_per_item = gran ? 1 : c.S;
   const int rps = spi * rows_per_item;
-  const int ipb = items_per_split(count, nsplit);
+  const int ipb = entmax_items_per_split(count, nsplit, spi, rows_per_item);
   const int ns = min(nsplit, (count + ipb - 1) / ipb);
   const size_t lid0 = ((size_t)unit * c.G + hh) * nsplit;
   float *o = out + (size_t)bh * D;
