@@ -95,9 +95,9 @@ typedef struct skv_meta {
                          (32 bf16, 16 float32): 64-byte blocks of k_min and of k_max alternate */
   float *gauss;       /* GAUSS: [Nphys, Hkv, d/16, 2, 16] float32: 64-byte blocks of the mean and
                          of the variance row alternate (16 coordinates each) */
-  int32_t proj_rank;  /* PROJ:  r, 1..64 */
+  int32_t proj_rank;  /* PROJ:  r: 16, 32 or 64 */
   const float *proj;  /* PROJ:  [r, d] float32 projection shared by queries and keys */
-  uint16_t *kproj;    /* PROJ:  [Nphys, Hkv, S, r] bf16 bit patterns */
+  uint16_t *kproj;    /* PROJ:  [Nphys, Hkv, S, r] bf16 bit patterns (16-byte aligned) */
   int32_t pool_block; /* POOL:  tokens per sub-block, dividing S */
   float *pool;        /* POOL:  [Nphys, Hkv, S / pool_block, d] float32 sub-block mean keys */
   int32_t lsh_tables; /* LSH:   number of hash tables L: 16, 32, 48 or 64 */

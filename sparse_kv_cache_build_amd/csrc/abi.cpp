@@ -281,10 +281,10 @@ static skv_status meta_args(const skv_cache *c, const skv_meta *m) {
   if (box && !aligned(m->box, 16)) return SKV_ERR_INVALID_ARG;
   if (gauss && !aligned(m->gauss, 16)) return SKV_ERR_INVALID_ARG;
   if (proj) {
-    if (!m->proj || !m->kproj) return SKV_ERR_INVALID_ARG;
+    if (!m->proj || !m->kproj || !aligned(m->kproj, 16)) return SKV_ERR_INVALID_ARG;
     if (!rank_ok(m->proj_rank)) return SKV_ERR_UNSUPPORTED;
-    const size_t lds = sizeof(float) * ((size_t)m->proj_rank * (c->head_dim + 1) + (size_t)c->page_size * c->head_dim);
-    if (lds > 65536) return SKV_ERR_UNSUPPORTED;
+    // rows of kproj are indexed in 32 bits (more rows than that would not fit next to K anyway)
+    if ((uint64_t)c->num_phys_pages * c->num_kv_heads * c->page_size > 0xffffffffull) return SKV_ERR_UNSUPPORTED;
   }
   return SKV_OK;
 }

@@ -135,7 +135,7 @@ struct Packed8<float> {
 // a round-to-odd intermediate with at least two extra bits makes the second rounding equal
 // to a single one. Below 2^-126 bf16 is subnormal with quantum 2^-133: round |x| * 2^133 to an
 // integer directly (it is the fraction field, and 128 carries into the smallest normal).
-__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+__device__ __forceinline__ uint16_t f64_to_bf16_edge(double x) {
   if (x != x) return 0x7fc0;
   uint16_t sign = signbit(x) ? 0x8000 : 0;
   double ax = fabs(x);
@@ -150,6 +150,21 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
   if ((u & 0x7f800000u) == 0x7f800000u) return sign | 0x7f80;  // +inf
   u += 0x7fffu + ((u >> 16) & 1u);
   return sign | (uint16_t)(u >> 16);
+}
+
+// The same rounding. Results in bf16's normal range (2^-126 <= |x| < 2^128 before rounding) are
+// rounded on the bit pattern: add 2^44 - 1 plus the lowest kept bit (bit 45) to the 64-bit word,
+// which rounds to nearest-even at 8 significant bits (a carry out of the fraction raises the
+// exponent, up to infinity), and rebias the exponent from 11 to 8 bits. Other inputs take the
+// general routine above.
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t hi = (uint32_t)(u >> 32), lo = (uint32_t)u;
+  const uint32_t e = (hi >> 20) & 0x7ffu;
+  if (e - 897u > 1150u - 897u) return f64_to_bf16_edge(x);
+  const uint32_t lsb = (hi >> 13) & 1u;
+  const uint32_t h = hi + 0xfffu + ((lo | lsb) != 0u ? 1u : 0u);  // carry of lo + 2^32 - 1 + lsb
+  return (uint16_t)(((h >> 16) & 0x8000u) | (((h >> 13) & 0x3ffffu) - (896u << 7)));
 }
 
 // Order-preserving map float -> uint32 (larger float, larger key); -0 and +0 map alike.

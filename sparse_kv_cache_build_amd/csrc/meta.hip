@@ -89,34 +89,148 @@ __global__ __launch_bounds__(256) void meta_pool_kernel(CacheView c, int tail, i
   }
 }
 
-// Projected keys k~_t[i] = RN_bf16(sum_j P[i][j] k_t[j]) (float64, j ascending). One workgroup
-// per (logical page, KV head): the page's keys and P are staged in LDS as float (exact), then
-// each thread owns (token, i) pairs.
+// Projected keys ("Joint Subspace Sparse Attention": keys kept in the shared rank-r subspace),
+// kproj[row][i] = RN_bf16(sum_j P[i][j] * K[row][j]), the float64 sum taken over j = 0..d-1 in
+// that order from 0 (each product of a float and a cache element is exact in float64).
+// Register-blocked: a wave owns 8 outputs i and 512 tokens of one (sequence, KV head), token
+// u * 64 + lane in slot u of each lane, and keeps the 64 float64 accumulators in registers. Per
+// coordinate it reads its 8 P values as float64 broadcasts from LDS and converts each token's K
+// value once, so every conversion feeds 8 fma and every P read feeds 8 tokens. The workgroup's
+// waves share one tile of tokens (SUB tiles of 512 for r = 16, whose 16 outputs take two waves per
+// tile). K goes from global memory straight to LDS (global_load_lds, 16 bytes a lane, so that each
+// instruction's lanes fill consecutive LDS slots) in chunks of 32 bytes per row, double-buffered;
+// each lane picks the piece for its slot such that the two pieces of a row trade places in every
+// other group of four rows, which lets 8 consecutive rows read their pieces conflict-free. Tokens
+// covered: [0, L) for a build, the last `tail` of them for an append. The P slab in LDS holds up
+// to 32 outputs; r = 64 takes two slabs per tile.
+constexpr int kProjTok = 8, kProjOut = 8, kProjSlab = 32, kProjTilesPerWg = 4;
+
 template <typename T>
-__global__ __launch_bounds__(256) void meta_proj_kernel(CacheView c, int tail, int r, const float *__restrict__ proj,
-                                                        uint16_t *__restrict__ kproj) {
-  extern __shared__ float smem[];
+__device__ __forceinline__ float proj_elem(const uint4 &w, int e) {
+  const uint32_t x = e / 2 == 0 ? w.x : e / 2 == 1 ? w.y : e / 2 == 2 ? w.z : w.w;
+  return (e & 1) ? bf16_hi(x) : bf16_lo(x);
+}
+template <>
+__device__ __forceinline__ float proj_elem<float>(const uint4 &w, int e) {
+  return __uint_as_float(e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w);
+}
+
+// 16 bytes per lane from global memory into LDS: lane i of the wave writes lds_base + 16 i
+// (lds_base uniform over the wave). The operands go through void pointers: with typed pointers the
+// host pass of a kernel template drops the launch stub.
+__device__ __forceinline__ void skv_load_lds16(const void *src, void *lds_base) {
+  __builtin_amdgcn_global_load_lds(const_cast<void *>(src), lds_base, 16, 0, 0);
+}
+
+// piece (0 or 1) of tile row rho that sits in its LDS slot `bit` (and, the map being its own
+// inverse, the slot that piece `bit` of the row sits in)
+__device__ __forceinline__ int proj_piece(int rho, int bit) { return bit ^ ((rho >> 2) & 1); }
+
+// row index (into K and kproj, in rows of the cache) of token tau of sequence b, KV head g
+__device__ __forceinline__ uint32_t proj_row(const CacheView &c, int b, int g, int tau) {
+  const int p = tau / c.S, t = tau - p * c.S;
+  return ((uint32_t)c.bt[(size_t)b * c.maxP + p] * c.Hkv + g) * c.S + t;
+}
+
+template <typename T, int D, int SUB>
+__global__ __launch_bounds__(256, 2) void meta_proj_kernel(CacheView c, int tail, int r, const float *__restrict__ proj,
+                                                           uint16_t *__restrict__ kproj) {
+  constexpr int PPJ = 16 / sizeof(T);          // coordinates per 16-byte piece
+  constexpr int CC = 2 * PPJ;                  // coordinates per staged chunk (32 bytes per row)
+  constexpr int NCH = D / CC;                  // chunks per row
+  constexpr int TT = SUB * 64 * kProjTok;      // tokens per tile
+  constexpr int NL = TT * 2 / 256;             // staging loads per thread and chunk
+  constexpr int SLAB = SUB == 2 ? 16 : kProjSlab;
+  __shared__ uint4 ks[2][TT * 2];                      // [buffer][row * 2 + slot]
+  __shared__ double2 pslab[SLAB / kProjOut][D][kProjOut / 2];
   const int b = blockIdx.y / c.Hkv, g = blockIdx.y % c.Hkv;
   const int L = seq_len(c, b);
-  const int p = first_page(c, L, tail) + blockIdx.x;
-  if (p >= num_pages(c, L)) return;
-  const int n = min(c.S, L - p * c.S);
-  const int t0 = tail > 0 ? max(0, L - tail - p * c.S) : 0;   // first row of the page to write
-  const int phys = c.bt[(size_t)b * c.maxP + p];
-  const int ldp = c.D + 1;  // padded row stride of P (bank spread across i)
-  float *Ps = smem;                     // [r][D+1]
-  float *Ks = smem + (size_t)r * ldp;   // [n][D]
-  const T *K = static_cast<const T *>(c.k) + ((size_t)phys * c.Hkv + g) * c.S * c.D;
-  for (int i = threadIdx.x; i < r * c.D; i += blockDim.x) Ps[(i / c.D) * ldp + i % c.D] = proj[i];
-  for (int i = t0 * c.D + threadIdx.x; i < n * c.D; i += blockDim.x) Ks[i] = Elem<T>::get(K, i);
-  __syncthreads();
-  uint16_t *out = kproj + ((size_t)phys * c.Hkv + g) * c.S * r;
-  for (int pair = t0 * r + threadIdx.x; pair < n * r; pair += blockDim.x) {
-    const int t = pair / r, i = pair - t * r;
-    const float *pr = Ps + i * ldp, *kr = Ks + t * c.D;
-    double acc = 0.0;
-    for (int j = 0; j < c.D; ++j) acc = fma((double)pr[j], (double)kr[j], acc);
-    out[(size_t)t * r + i] = f64_to_bf16(acc);
+  const int lo = tail > 0 ? max(0, L - tail) : 0, ntok = L - lo;
+  const int nslab = r / SLAB, obs = SLAB / kProjOut;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
+  const int ob = wave % obs, sub = wave / obs;
+  const T *K = static_cast<const T *>(c.k);
+  for (int it = 0; it < kProjTilesPerWg; ++it) {
+    const int tile0 = (blockIdx.x * kProjTilesPerWg + it) * TT;
+    if (tile0 >= ntok) break;  // uniform over the workgroup
+    // staging load k of this thread fills slot threadIdx.x % 2 of tile row threadIdx.x / 2 + 128 k
+    // (LDS slots 64 (wave + 4 k) + lane); a missing token stages the tile's first row instead
+    const T *src[NL];
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int rho = (int)threadIdx.x / 2 + 128 * k, tok = tile0 + rho;
+      src[k] = K + (size_t)proj_row(c, b, g, lo + (tok < ntok ? tok : tile0)) * D + proj_piece(rho, threadIdx.x & 1) * PPJ;
+    }
+    const int tbase = tile0 + sub * 64 * kProjTok;
+    const bool live = tbase < ntok;
+    const int rbase = sub * 64 * kProjTok + lane;  // tile row of slot u: rbase + 64 u
+    for (int s = 0; s < nslab; ++s) {
+      __syncthreads();  // the previous tile's or slab's LDS contents are no longer read
+      if (nslab > 1 || it == 0) {
+        double *pd = &pslab[0][0][0].x;
+        for (int e = threadIdx.x; e < SLAB * D; e += blockDim.x) {
+          const int i = e / D, j = e - i * D;
+          pd[((i / kProjOut) * D + j) * kProjOut + i % kProjOut] = proj[(size_t)(s * SLAB + i) * D + j];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NL; ++k) skv_load_lds16(src[k], &ks[0][64 * (wave + 4 * k)]);
+      double acc[kProjTok][kProjOut];
+#pragma unroll
+      for (int u = 0; u < kProjTok; ++u)
+#pragma unroll
+        for (int i = 0; i < kProjOut; ++i) acc[u][i] = 0.0;
+#pragma unroll 1
+      for (int ch = 0; ch < NCH; ++ch) {
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of chunk ch are in LDS
+        __syncthreads();                // everyone's are, and chunk ch - 1 is no longer read
+        if (ch + 1 < NCH) {
+#pragma unroll
+          for (int k = 0; k < NL; ++k)
+            skv_load_lds16(src[k] + (ch + 1) * CC, &ks[(ch + 1) & 1][64 * (wave + 4 * k)]);
+        }
+        if (!live) continue;
+        const uint4 *kb = ks[ch & 1];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          uint4 raw[kProjTok];
+#pragma unroll
+          for (int u = 0; u < kProjTok; ++u) {
+            const int rho = rbase + 64 * u;
+            raw[u] = kb[rho * 2 + proj_piece(rho, q)];
+          }
+#pragma unroll
+          for (int e = 0; e < PPJ; ++e) {
+            const int j = ch * CC + q * PPJ + e;
+            double pv[kProjOut];
+#pragma unroll
+            for (int i = 0; i < kProjOut / 2; ++i) {
+              const double2 w = pslab[ob][j][i];
+              pv[2 * i] = w.x;
+              pv[2 * i + 1] = w.y;
+            }
+#pragma unroll
+            for (int u = 0; u < kProjTok; ++u) {
+              const double kv = (double)proj_elem<T>(raw[u], e);
+#pragma unroll
+              for (int i = 0; i < kProjOut; ++i) acc[u][i] = fma(pv[i], kv, acc[u][i]);
+            }
+          }
+        }
+      }
+      if (!live) continue;
+#pragma unroll
+      for (int u = 0; u < kProjTok; ++u) {
+        const int tok = tbase + u * 64 + lane;
+        if (tok >= ntok) continue;
+        uint32_t w[kProjOut / 2];
+#pragma unroll
+        for (int i = 0; i < kProjOut / 2; ++i)
+          w[i] = (uint32_t)f64_to_bf16(acc[u][2 * i]) | ((uint32_t)f64_to_bf16(acc[u][2 * i + 1]) << 16);
+        *reinterpret_cast<uint4 *>(kproj + (size_t)proj_row(c, b, g, lo + tok) * r + s * SLAB + ob * kProjOut) =
+            make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
   }
 }
 
@@ -226,12 +340,22 @@ hipError_t launch_build_meta(const CacheView &c, int dtype, int tail, void *box,
       meta_pool_kernel<uint16_t><<<grid, 256, 0, st>>>(c, tail, pb, pool);
   }
   if (kproj) {
-    const size_t lds = sizeof(float) * ((size_t)r * (c.D + 1) + (size_t)c.S * c.D);
-    const dim3 g2(np, c.B * c.Hkv);
-    if (dtype == 0)
-      meta_proj_kernel<float><<<g2, 256, lds, st>>>(c, tail, r, proj, kproj);
-    else
-      meta_proj_kernel<uint16_t><<<g2, 256, lds, st>>>(c, tail, r, proj, kproj);
+    const int slab = min(r, kProjSlab);
+    const int sub = 4 / (slab / kProjOut);  // 512-token tiles per workgroup tile: 2 for r = 16
+    const int tile_tok = sub * 64 * kProjTok;
+    const long maxtok = tail > 0 ? min((long)tail, (long)c.maxP * c.S) : (long)c.maxP * c.S;
+    const long tiles = (maxtok + tile_tok - 1) / tile_tok;
+    const dim3 g2((unsigned)((tiles + kProjTilesPerWg - 1) / kProjTilesPerWg), c.B * c.Hkv);
+#define SKV_PROJ(TT, DD, SS) meta_proj_kernel<TT, DD, SS><<<g2, 256, 0, st>>>(c, tail, r, proj, kproj)
+#define SKV_PROJ_D(TT, SS) \
+  if (c.D == 64) SKV_PROJ(TT, 64, SS); else SKV_PROJ(TT, 128, SS);
+    if (dtype == 0) {
+      if (sub == 2) { SKV_PROJ_D(float, 2) } else { SKV_PROJ_D(float, 1) }
+    } else {
+      if (sub == 2) { SKV_PROJ_D(uint16_t, 2) } else { SKV_PROJ_D(uint16_t, 1) }
+    }
+#undef SKV_PROJ_D
+#undef SKV_PROJ
   }
   return hipGetLastError();
 }
