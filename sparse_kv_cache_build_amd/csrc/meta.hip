@@ -8,83 +8,203 @@
 
 namespace skv {
 
-// One workgroup per logical page (p, b); threads sweep (KV head, coordinate) pairs so that each
-// token row is read with consecutive coordinates across consecutive threads.
-//   box:   exact min / max over the valid tokens, stored as the original element bits, the
-//          64-byte blocks of the min row and of the max row alternating ([d / C][2][C], C = 64 bytes).
+// Box, moment and pooled-key builders. Work items are (page, KV head g, 16-byte slice o of the
+// key row): V = 16 / sizeof(T) consecutive coordinates, so 64 consecutive items read whole rows
+// (256 bytes for d = 128 bf16) and a wave instruction covers several rows. A workgroup takes
+// `ppw` consecutive pages of one sequence; each item walks its page's valid tokens in ascending
+// order, RB rows in flight.
+//   box:   min / max over the valid tokens from +inf / -inf with strict comparisons, stored as
+//          the element bits, the 64-byte blocks of the min row and of the max row alternating
+//          ([d / C][2][C], C = 64 bytes).
 //   gauss: float64 mean (sum over t ascending, divided by n), then float64 mean squared
-//          deviation, each rounded once to float32.
+//          deviation (each square rounded, then added), each rounded once to float32; the 64-byte
+//          blocks of the mean row and of the variance row alternate ([d / 16][2][16]).
 // First logical page a build (tail == 0) or an append of `tail` tokens covers.
 __device__ __forceinline__ int first_page(const CacheView &c, int L, int tail) {
   return tail > 0 ? max(0, L - tail) / c.S : 0;
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void meta_box_gauss_kernel(CacheView c, int tail, T *__restrict__ box,
+struct Slice;
+template <>
+struct Slice<uint16_t> {
+  static constexpr int V = 8;
+  static __device__ __forceinline__ void unpack(const uint4 &w, float (&x)[8]) {
+    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+  }
+  // element bits of two values (exact: a bf16 widened to float keeps its bits in the top half)
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+  }
+  static __device__ __forceinline__ uint4 pack(const float (&x)[8]) {
+    return make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
+  }
+};
+template <>
+struct Slice<float> {
+  static constexpr int V = 4;
+  static __device__ __forceinline__ void unpack(const uint4 &w, float (&x)[4]) {
+    x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y); x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
+  }
+  static __device__ __forceinline__ uint4 pack(const float (&x)[4]) {
+    return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3]));
+  }
+};
+
+// ss + dv * dv with the square rounded before the addition (no fused multiply-add)
+__device__ __forceinline__ double add_square(double ss, double dv) {
+#pragma clang fp contract(off)
+  return ss + dv * dv;
+}
+
+// Item `it` of a workgroup that covers pages [p0, p0 + ppw): page p, KV head g, slice o; returns
+// false past the sequence's last page. Rows of the item start at `row` (in rows of the cache).
+struct MetaItem {
+  int p, g, o, n;
+  size_t row;
+};
+__device__ __forceinline__ bool meta_item(const CacheView &c, int b, int L, int p0, int it, int spr, MetaItem &m) {
+  const int per_page = c.Hkv * spr;
+  const int pp = it / per_page, rem = it - pp * per_page;
+  m.p = p0 + pp;
+  if (m.p >= num_pages(c, L)) return false;
+  m.g = rem / spr;
+  m.o = rem - m.g * spr;
+  m.n = min(c.S, L - m.p * c.S);
+  m.row = ((size_t)c.bt[(size_t)b * c.maxP + m.p] * c.Hkv + m.g) * c.S;
+  return true;
+}
+
+constexpr int kMetaRows = 8;  // rows in flight per item
+
+template <typename T, bool BOX, bool GAUSS>
+__global__ __launch_bounds__(256) void meta_box_gauss_kernel(CacheView c, int tail, int ppw, T *__restrict__ box,
                                                              float *__restrict__ gauss) {
+  constexpr int V = Slice<T>::V;
   const int b = blockIdx.y;
   const int L = seq_len(c, b);
-  const int p = first_page(c, L, tail) + blockIdx.x;
-  if (p >= num_pages(c, L)) return;
-  const int n = min(c.S, L - p * c.S);
-  const int phys = c.bt[(size_t)b * c.maxP + p];
+  const int p0 = first_page(c, L, tail) + blockIdx.x * ppw;
+  const int spr = c.D / V;  // slices per row
   const T *K = static_cast<const T *>(c.k);
-  for (int idx = threadIdx.x; idx < c.Hkv * c.D; idx += blockDim.x) {
-    const int g = idx / c.D, j = idx - g * c.D;
-    const size_t base = ((size_t)phys * c.Hkv + g) * c.S * c.D + j;
-    // 64-byte blocks of the mean and variance rows alternate, so one 128-byte line holds both
-    const size_t mo = ((size_t)phys * c.Hkv + g) * 2 * c.D + (size_t)(j / 16) * 32 + (j % 16);
-    if (box) {
-      T lo = K[base], hi = K[base];
-      float flo = Elem<T>::get(K, base), fhi = flo;
-      for (int t = 1; t < n; ++t) {
-        T x = K[base + (size_t)t * c.D];
-        float fx = Elem<T>::get(K, base + (size_t)t * c.D);
-        if (fx < flo) { flo = fx; lo = x; }
-        if (fx > fhi) { fhi = fx; hi = x; }
-      }
-      // 64-byte blocks of the min and max rows alternate, so one 128-byte line holds both
-      constexpr int C = 64 / (int)sizeof(T);
-      const size_t bo = ((size_t)phys * c.Hkv + g) * 2 * c.D + (size_t)(j / C) * 2 * C + (j % C);
-      box[bo] = lo;
-      box[bo + C] = hi;
+  for (int it = threadIdx.x; it < ppw * c.Hkv * spr; it += blockDim.x) {
+    MetaItem m;
+    if (!meta_item(c, b, L, p0, it, spr, m)) break;  // items are page-major: the rest are past too
+    const uint4 *src = reinterpret_cast<const uint4 *>(K + m.row * c.D) + m.o;
+    const int rs = c.D / V;  // row stride in slices
+    float lo[V], hi[V];
+    double sum[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      lo[v] = __builtin_inff();
+      hi[v] = -__builtin_inff();
+      sum[v] = 0.0;
     }
-    if (gauss) {
-      double sum = 0.0;
-      for (int t = 0; t < n; ++t) sum += (double)Elem<T>::get(K, base + (size_t)t * c.D);
-      const double mu = sum / n;
-      double ss = 0.0;
-      for (int t = 0; t < n; ++t) {
-        const double dv = (double)Elem<T>::get(K, base + (size_t)t * c.D) - mu;
-        ss += dv * dv;
+    for (int t0 = 0; t0 < m.n; t0 += kMetaRows) {
+      uint4 w[kMetaRows];
+#pragma unroll
+      for (int r = 0; r < kMetaRows; ++r)
+        if (t0 + r < m.n) w[r] = GAUSS ? src[(size_t)(t0 + r) * rs] : ld_once(src + (size_t)(t0 + r) * rs);
+#pragma unroll
+      for (int r = 0; r < kMetaRows; ++r) {
+        if (t0 + r >= m.n) break;
+        float x[V];
+        Slice<T>::unpack(w[r], x);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          if (BOX) {
+            if (x[v] < lo[v]) lo[v] = x[v];
+            if (x[v] > hi[v]) hi[v] = x[v];
+          }
+          if (GAUSS) sum[v] += (double)x[v];
+        }
       }
-      gauss[mo] = (float)mu;
-      gauss[mo + 16] = (float)(ss / n);
+    }
+    const int j0 = m.o * V;
+    const size_t ob = (m.row / c.S) * 2 * c.D;  // (phys * Hkv + g) * 2d
+    if (BOX) {
+      constexpr int C = 64 / (int)sizeof(T);
+      uint4 *dst = reinterpret_cast<uint4 *>(box + ob + (size_t)(j0 / C) * 2 * C + (j0 % C));
+      dst[0] = Slice<T>::pack(lo);
+      dst[C / V] = Slice<T>::pack(hi);
+    }
+    if (GAUSS) {
+      double mu[V], ss[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        mu[v] = sum[v] / m.n;
+        ss[v] = 0.0;
+      }
+      for (int t0 = 0; t0 < m.n; t0 += kMetaRows) {
+        uint4 w[kMetaRows];
+#pragma unroll
+        for (int r = 0; r < kMetaRows; ++r)
+          if (t0 + r < m.n) w[r] = src[(size_t)(t0 + r) * rs];
+#pragma unroll
+        for (int r = 0; r < kMetaRows; ++r) {
+          if (t0 + r >= m.n) break;
+          float x[V];
+          Slice<T>::unpack(w[r], x);
+#pragma unroll
+          for (int v = 0; v < V; ++v) ss[v] = add_square(ss[v], (double)x[v] - mu[v]);
+        }
+      }
+      float mf[V], vf[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        mf[v] = (float)mu[v];
+        vf[v] = (float)(ss[v] / m.n);
+      }
+      float *gm = gauss + ob + (size_t)(j0 / 16) * 32 + (j0 % 16);
+#pragma unroll
+      for (int v = 0; v < V; v += 4) {
+        *reinterpret_cast<float4 *>(gm + v) = make_float4(mf[v], mf[v + 1], mf[v + 2], mf[v + 3]);
+        *reinterpret_cast<float4 *>(gm + 16 + v) = make_float4(vf[v], vf[v + 1], vf[v + 2], vf[v + 3]);
+      }
     }
   }
 }
 
 // Pooled keys: per sub-block of pb token slots of the page, RN_f32 of the float64 mean of its
-// valid keys (t ascending). One workgroup per logical page (p, b); threads sweep (KV head,
-// coordinate) pairs like the box / moment kernel.
+// valid keys (t ascending). Items as for the box / moment builder.
 template <typename T>
-__global__ __launch_bounds__(256) void meta_pool_kernel(CacheView c, int tail, int pb, float *__restrict__ pool) {
+__global__ __launch_bounds__(256) void meta_pool_kernel(CacheView c, int tail, int ppw, int pb, float *__restrict__ pool) {
+  constexpr int V = Slice<T>::V;
   const int b = blockIdx.y;
   const int L = seq_len(c, b);
-  const int p = first_page(c, L, tail) + blockIdx.x;
-  if (p >= num_pages(c, L)) return;
-  const int n = min(c.S, L - p * c.S);
-  const int nsb = c.S / pb;
-  const int phys = c.bt[(size_t)b * c.maxP + p];
+  const int p0 = first_page(c, L, tail) + blockIdx.x * ppw;
+  const int spr = c.D / V, nsb = c.S / pb;
   const T *K = static_cast<const T *>(c.k);
-  for (int idx = threadIdx.x; idx < c.Hkv * c.D; idx += blockDim.x) {
-    const int g = idx / c.D, j = idx - g * c.D;
-    const size_t base = ((size_t)phys * c.Hkv + g) * c.S * c.D + j;
-    for (int sb = 0; sb < nsb && sb * pb < n; ++sb) {
-      const int t1 = min(n, sb * pb + pb);
-      double sum = 0.0;
-      for (int t = sb * pb; t < t1; ++t) sum += (double)Elem<T>::get(K, base + (size_t)t * c.D);
-      pool[(((size_t)phys * c.Hkv + g) * nsb + sb) * c.D + j] = (float)(sum / (t1 - sb * pb));
+  for (int it = threadIdx.x; it < ppw * c.Hkv * spr; it += blockDim.x) {
+    MetaItem m;
+    if (!meta_item(c, b, L, p0, it, spr, m)) break;
+    const uint4 *src = reinterpret_cast<const uint4 *>(K + m.row * c.D) + m.o;
+    const int j0 = m.o * V;
+    for (int sb = 0; sb < nsb && sb * pb < m.n; ++sb) {
+      const int t1 = min(m.n, sb * pb + pb);
+      double sum[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) sum[v] = 0.0;
+      for (int t0 = sb * pb; t0 < t1; t0 += kMetaRows) {
+        uint4 w[kMetaRows];
+#pragma unroll
+        for (int r = 0; r < kMetaRows; ++r)
+          if (t0 + r < t1) w[r] = ld_once(src + (size_t)(t0 + r) * spr);
+#pragma unroll
+        for (int r = 0; r < kMetaRows; ++r) {
+          if (t0 + r >= t1) break;
+          float x[V];
+          Slice<T>::unpack(w[r], x);
+#pragma unroll
+          for (int v = 0; v < V; ++v) sum[v] += (double)x[v];
+        }
+      }
+      float *dst = pool + ((m.row / c.S) * nsb + sb) * c.D + j0;
+      const double cnt = t1 - sb * pb;
+#pragma unroll
+      for (int v = 0; v < V; v += 4)
+        *reinterpret_cast<float4 *>(dst + v) = make_float4((float)(sum[v] / cnt), (float)(sum[v + 1] / cnt),
+                                                           (float)(sum[v + 2] / cnt), (float)(sum[v + 3] / cnt));
     }
   }
 }
@@ -326,18 +446,27 @@ hipError_t launch_build_meta(const CacheView &c, int dtype, int tail, void *box,
                              const float *proj, uint16_t *kproj, int pb, float *pool, hipStream_t st) {
   // pages per sequence: all of them, or those the last `tail` tokens can touch
   const int np = tail > 0 ? min(c.maxP, (tail + c.S - 1) / c.S + 1) : c.maxP;
-  const dim3 grid(np, c.B);
+  // box / moments / pooled keys: pages per workgroup so that its 256 threads have an item each
+  const int items = c.Hkv * c.D / (dtype == 0 ? Slice<float>::V : Slice<uint16_t>::V);
+  const int ppw = max(1, 256 / items);
+  const dim3 gridw((np + ppw - 1) / ppw, c.B);
+#define SKV_BG(TT, BX, GS) \
+  meta_box_gauss_kernel<TT, BX, GS><<<gridw, 256, 0, st>>>(c, tail, ppw, static_cast<TT *>(box), gauss)
   if (box || gauss) {
-    if (dtype == 0)
-      meta_box_gauss_kernel<float><<<grid, 256, 0, st>>>(c, tail, static_cast<float *>(box), gauss);
-    else
-      meta_box_gauss_kernel<uint16_t><<<grid, 256, 0, st>>>(c, tail, static_cast<uint16_t *>(box), gauss);
+    if (dtype == 0) {
+      if (box && gauss) SKV_BG(float, true, true); else if (box) SKV_BG(float, true, false); else SKV_BG(float, false, true);
+    } else {
+      if (box && gauss) SKV_BG(uint16_t, true, true);
+      else if (box) SKV_BG(uint16_t, true, false);
+      else SKV_BG(uint16_t, false, true);
+    }
   }
+#undef SKV_BG
   if (pool) {
     if (dtype == 0)
-      meta_pool_kernel<float><<<grid, 256, 0, st>>>(c, tail, pb, pool);
+      meta_pool_kernel<float><<<gridw, 256, 0, st>>>(c, tail, ppw, pb, pool);
     else
-      meta_pool_kernel<uint16_t><<<grid, 256, 0, st>>>(c, tail, pb, pool);
+      meta_pool_kernel<uint16_t><<<gridw, 256, 0, st>>>(c, tail, ppw, pb, pool);
   }
   if (kproj) {
     const int slab = min(r, kProjSlab);
