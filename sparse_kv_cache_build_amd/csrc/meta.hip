@@ -209,20 +209,26 @@ __global__ __launch_bounds__(256) void meta_pool_kernel(CacheView c, int tail, i
   }
 }
 
-// Projected keys ("Joint Subspace Sparse Attention": keys kept in the shared rank-r subspace),
-// kproj[row][i] = RN_bf16(sum_j P[i][j] * K[row][j]), the float64 sum taken over j = 0..d-1 in
-// that order from 0 (each product of a float and a cache element is exact in float64).
-// Register-blocked: a wave owns 8 outputs i and 512 tokens of one (sequence, KV head), token
-// u * 64 + lane in slot u of each lane, and keeps the 64 float64 accumulators in registers. Per
-// coordinate it reads its 8 P values as float64 broadcasts from LDS and converts each token's K
-// value once, so every conversion feeds 8 fma and every P read feeds 8 tokens. The workgroup's
-// waves share one tile of tokens (SUB tiles of 512 for r = 16, whose 16 outputs take two waves per
-// tile). K goes from global memory straight to LDS (global_load_lds, 16 bytes a lane, so that each
-// instruction's lanes fill consecutive LDS slots) in chunks of 32 bytes per row, double-buffered;
-// each lane picks the piece for its slot such that the two pieces of a row trade places in every
-// other group of four rows, which lets 8 consecutive rows read their pieces conflict-free. Tokens
-// covered: [0, L) for a build, the last `tail` of them for an append. The P slab in LDS holds up
-// to 32 outputs; r = 64 takes two slabs per tile.
+// Float64 row dots of the projected-key and soft-LSH builders: every valid token row k of a
+// (sequence, KV head) against the rows w_i of a float matrix, dot_i = sum_j w_i[j] * k[j] taken in
+// float64 over j = 0..d-1 in that order from 0 (each product of a float and a cache element is
+// exact in float64).
+//   projected keys ("Joint Subspace Sparse Attention": keys kept in the shared rank-r subspace):
+//     the r rows of P, kproj[row][i] = RN_bf16(dot_i).
+//   soft LSH ("SOCKET" Methodology, soft LSH step 1): table l takes rows 8 l .. 8 l + 7, its P
+//     hyperplanes then zero rows; bucket[row][l] has bit i set iff dot_i > 0.
+// Register-blocked: a wave owns an output block of 8 rows (NOUT of them computed: 8, or P rounded
+// up to even) and 512 tokens, token u * 64 + lane in slot u of each lane, and keeps the float64
+// accumulators in registers. Per coordinate it reads its matrix values as float64 broadcasts from
+// LDS and converts each token's K value once, so every conversion feeds NOUT fma and every matrix
+// read feeds 8 tokens. The workgroup's waves share one tile of tokens (SUB tiles of 512 for r =
+// 16, whose 16 outputs take two waves per tile). K goes from global memory straight to LDS
+// (global_load_lds, 16 bytes a lane, so that each instruction's lanes fill consecutive LDS slots)
+// in chunks of 32 bytes per row, double-buffered; each lane picks the piece for its slot such that
+// the two pieces of a row trade places in every other group of four rows, which lets 8
+// consecutive rows read their pieces conflict-free. Tokens covered: [0, L) for a build, the last
+// `tail` of them for an append. The matrix slab in LDS holds up to 32 rows (4 output blocks);
+// larger matrices take several slabs per tile.
 constexpr int kProjTok = 8, kProjOut = 8, kProjSlab = 32, kProjTilesPerWg = 4;
 
 template <typename T>
@@ -252,9 +258,16 @@ __device__ __forceinline__ uint32_t proj_row(const CacheView &c, int b, int g, i
   return ((uint32_t)c.bt[(size_t)b * c.maxP + p] * c.Hkv + g) * c.S + t;
 }
 
-template <typename T, int D, int SUB>
-__global__ __launch_bounds__(256, 2) void meta_proj_kernel(CacheView c, int tail, int r, const float *__restrict__ proj,
-                                                           uint16_t *__restrict__ kproj) {
+struct RowDotJob {
+  int nrows;            // matrix rows in output blocks of 8: r, or 8 L
+  const float *mat;     // P [r][d], or the hyperplanes [L][P][d]
+  int lsh_L, lsh_P;     // soft LSH only
+  uint16_t *kproj;      // projected keys: [rows of the cache][r]
+  uint8_t *bucket;      // soft LSH: [rows of the cache][L]
+};
+
+template <typename T, int D, int SUB, int NOUT, bool LSH>
+__global__ __launch_bounds__(256, 2) void meta_rowdot_kernel(CacheView c, int tail, RowDotJob job) {
   constexpr int PPJ = 16 / sizeof(T);          // coordinates per 16-byte piece
   constexpr int CC = 2 * PPJ;                  // coordinates per staged chunk (32 bytes per row)
   constexpr int NCH = D / CC;                  // chunks per row
@@ -266,7 +279,7 @@ __global__ __launch_bounds__(256, 2) void meta_proj_kernel(CacheView c, int tail
   const int b = blockIdx.y / c.Hkv, g = blockIdx.y % c.Hkv;
   const int L = seq_len(c, b);
   const int lo = tail > 0 ? max(0, L - tail) : 0, ntok = L - lo;
-  const int nslab = r / SLAB, obs = SLAB / kProjOut;
+  const int nslab = job.nrows / SLAB, obs = SLAB / kProjOut;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
   const int ob = wave % obs, sub = wave / obs;
   const T *K = static_cast<const T *>(c.k);
@@ -289,17 +302,22 @@ __global__ __launch_bounds__(256, 2) void meta_proj_kernel(CacheView c, int tail
       if (nslab > 1 || it == 0) {
         double *pd = &pslab[0][0][0].x;
         for (int e = threadIdx.x; e < SLAB * D; e += blockDim.x) {
-          const int i = e / D, j = e - i * D;
-          pd[((i / kProjOut) * D + j) * kProjOut + i % kProjOut] = proj[(size_t)(s * SLAB + i) * D + j];
+          const int i = e / D, j = e - i * D, row = s * SLAB + i;
+          float w;
+          if (LSH)
+            w = (row & 7) < job.lsh_P ? job.mat[((size_t)(row >> 3) * job.lsh_P + (row & 7)) * D + j] : 0.0f;
+          else
+            w = job.mat[(size_t)row * D + j];
+          pd[((i / kProjOut) * D + j) * kProjOut + i % kProjOut] = w;
         }
       }
 #pragma unroll
       for (int k = 0; k < NL; ++k) skv_load_lds16(src[k], &ks[0][64 * (wave + 4 * k)]);
-      double acc[kProjTok][kProjOut];
+      double acc[kProjTok][NOUT];
 #pragma unroll
       for (int u = 0; u < kProjTok; ++u)
 #pragma unroll
-        for (int i = 0; i < kProjOut; ++i) acc[u][i] = 0.0;
+        for (int i = 0; i < NOUT; ++i) acc[u][i] = 0.0;
 #pragma unroll 1
       for (int ch = 0; ch < NCH; ++ch) {
         __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of chunk ch are in LDS
@@ -322,9 +340,9 @@ __global__ __launch_bounds__(256, 2) void meta_proj_kernel(CacheView c, int tail
 #pragma unroll
           for (int e = 0; e < PPJ; ++e) {
             const int j = ch * CC + q * PPJ + e;
-            double pv[kProjOut];
+            double pv[NOUT];
 #pragma unroll
-            for (int i = 0; i < kProjOut / 2; ++i) {
+            for (int i = 0; i < NOUT / 2; ++i) {
               const double2 w = pslab[ob][j][i];
               pv[2 * i] = w.x;
               pv[2 * i + 1] = w.y;
@@ -333,7 +351,7 @@ __global__ __launch_bounds__(256, 2) void meta_proj_kernel(CacheView c, int tail
             for (int u = 0; u < kProjTok; ++u) {
               const double kv = (double)proj_elem<T>(raw[u], e);
 #pragma unroll
-              for (int i = 0; i < kProjOut; ++i) acc[u][i] = fma(pv[i], kv, acc[u][i]);
+              for (int i = 0; i < NOUT; ++i) acc[u][i] = fma(pv[i], kv, acc[u][i]);
             }
           }
         }
@@ -343,103 +361,82 @@ __global__ __launch_bounds__(256, 2) void meta_proj_kernel(CacheView c, int tail
       for (int u = 0; u < kProjTok; ++u) {
         const int tok = tbase + u * 64 + lane;
         if (tok >= ntok) continue;
-        uint32_t w[kProjOut / 2];
+        const size_t row = proj_row(c, b, g, lo + tok);
+        if (LSH) {
+          uint32_t id = 0;
 #pragma unroll
-        for (int i = 0; i < kProjOut / 2; ++i)
-          w[i] = (uint32_t)f64_to_bf16(acc[u][2 * i]) | ((uint32_t)f64_to_bf16(acc[u][2 * i + 1]) << 16);
-        *reinterpret_cast<uint4 *>(kproj + (size_t)proj_row(c, b, g, lo + tok) * r + s * SLAB + ob * kProjOut) =
-            make_uint4(w[0], w[1], w[2], w[3]);
+          for (int i = 0; i < NOUT; ++i) id |= (i < job.lsh_P && acc[u][i] > 0.0 ? 1u : 0u) << i;
+          job.bucket[row * job.lsh_L + s * obs + ob] = (uint8_t)id;
+        } else {
+          uint32_t w[NOUT / 2];
+#pragma unroll
+          for (int i = 0; i < NOUT / 2; ++i)
+            w[i] = (uint32_t)f64_to_bf16(acc[u][2 * i]) | ((uint32_t)f64_to_bf16(acc[u][2 * i + 1]) << 16);
+          *reinterpret_cast<uint4 *>(job.kproj + row * job.nrows + s * SLAB + ob * kProjOut) =
+              make_uint4(w[0], w[1], w[2], w[3]);
+        }
       }
     }
   }
 }
 
-// Soft-LSH metadata. One workgroup per logical page (p, b) covers the page's rows (KV head g,
-// token t), in chunks of 64 rows staged in LDS as float (exact). Work items are (table l, row)
-// pairs, with l constant over a wave in full chunks so that the hyperplanes of table l are
-// wave-uniform (scalar loads); each item takes the P float64 dot products of its row in
-// coordinate order, bit i of the bucket id being (dot_i > 0). Rows [t0, n) of the page are
-// written: all of them for a build, the new tokens for an append. The value norm of each row is
-// RN_f32(sqrt) of its float64 sum of squares.
-template <typename T, int D, int P>
-__global__ __launch_bounds__(256) void meta_lsh_kernel(CacheView c, int tail, int L, const float *__restrict__ planes,
-                                                       uint8_t *__restrict__ bucket, float *__restrict__ vnorm) {
-  constexpr int RC = 64, LDR = D + 1;
-  __shared__ float Ks[RC * LDR];
-  const int b = blockIdx.y;
-  const int len = seq_len(c, b);
-  const int p = first_page(c, len, tail) + blockIdx.x;
-  if (p >= num_pages(c, len)) return;
-  const int n = min(c.S, len - p * c.S);
-  const int t0 = tail > 0 ? max(0, len - tail - p * c.S) : 0;
-  const int cnt = n - t0, rows = c.Hkv * cnt;   // row r: KV head r / cnt, token t0 + r % cnt
-  const int phys = c.bt[(size_t)b * c.maxP + p];
-  const T *K = static_cast<const T *>(c.k);
-  const T *V = static_cast<const T *>(c.v);
-  for (int r0 = 0; r0 < rows; r0 += RC) {
-    const int nr = min(RC, rows - r0);
-    __syncthreads();
-    for (int i = threadIdx.x; i < nr * D; i += blockDim.x) {
-      const int r = r0 + i / D, j = i % D, g = r / cnt, t = t0 + r % cnt;
-      Ks[(i / D) * LDR + j] = Elem<T>::get(K, (((size_t)phys * c.Hkv + g) * c.S + t) * D + j);
-    }
-    __syncthreads();
-    for (int item = threadIdx.x; item < L * nr; item += blockDim.x) {
-      // full chunks: table l is constant over each wave (scalar loads of its hyperplanes); a
-      // partial chunk (an append touches a few rows) packs its (table, row) items densely
-      const int l = nr == RC ? __builtin_amdgcn_readfirstlane(item / RC) : item / nr;
-      const int rr = item - l * nr;
-      const float *w = planes + (size_t)l * P * D;
-      const float *kr = Ks + rr * LDR;
-      double acc[P];
+// Value norms for soft LSH: vnorm[row] = RN_f32(sqrt(sum_j v_j^2)), the float64 sum over j
+// ascending (the square of a cache element is exact in float64, so the fma rounds once as the
+// addition alone would). One thread per token row of a (sequence, KV head), 16-byte loads.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void meta_vnorm_kernel(CacheView c, int tail, float *__restrict__ vnorm) {
+  constexpr int V = Slice<T>::V;
+  const int b = blockIdx.y / c.Hkv, g = blockIdx.y % c.Hkv;
+  const int L = seq_len(c, b);
+  const int lo = tail > 0 ? max(0, L - tail) : 0, ntok = L - lo;
+  const int tok = blockIdx.x * blockDim.x + threadIdx.x;
+  if (tok >= ntok) return;
+  const size_t row = proj_row(c, b, g, lo + tok);
+  const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const T *>(c.v) + row * D);
+  uint4 w[D / V];
 #pragma unroll
-      for (int i = 0; i < P; ++i) acc[i] = 0.0;
-      for (int j = 0; j < D; ++j) {
-        const double kv = kr[j];
+  for (int q = 0; q < D / V; ++q) w[q] = src[q];
+  double ss = 0.0;
 #pragma unroll
-        for (int i = 0; i < P; ++i) acc[i] = fma((double)w[i * D + j], kv, acc[i]);
-      }
-      uint32_t id = 0;
+  for (int q = 0; q < D / V; ++q) {
+    float x[V];
+    Slice<T>::unpack(w[q], x);
 #pragma unroll
-      for (int i = 0; i < P; ++i) id |= (acc[i] > 0.0 ? 1u : 0u) << i;
-      const int r = r0 + rr, g = r / cnt, t = t0 + r % cnt;
-      bucket[(((size_t)phys * c.Hkv + g) * c.S + t) * L + l] = (uint8_t)id;
-    }
-    for (int rr = threadIdx.x; rr < nr; rr += blockDim.x) {
-      const int r = r0 + rr, g = r / cnt, t = t0 + r % cnt;
-      const size_t row = ((size_t)phys * c.Hkv + g) * c.S + t;
-      double ss = 0.0;
-      for (int j = 0; j < D; ++j) {
-        const double x = Elem<T>::get(V, row * D + j);
-        ss = fma(x, x, ss);
-      }
-      vnorm[row] = (float)sqrt(ss);
-    }
+    for (int v = 0; v < V; ++v) ss = fma((double)x[v], (double)x[v], ss);
   }
+  vnorm[row] = (float)sqrt(ss);
+}
+
+// Launch geometry of the row-dot kernel: 512-token tiles (two per workgroup tile for a 16-row
+// matrix), kProjTilesPerWg tiles per workgroup, one grid row per (sequence, KV head).
+static dim3 rowdot_grid(const CacheView &c, int tail, int sub) {
+  const int tile_tok = sub * 64 * kProjTok;
+  const long maxtok = tail > 0 ? min((long)tail, (long)c.maxP * c.S) : (long)c.maxP * c.S;
+  const long tiles = (maxtok + tile_tok - 1) / tile_tok;
+  return dim3((unsigned)((tiles + kProjTilesPerWg - 1) / kProjTilesPerWg), c.B * c.Hkv);
 }
 
 template <typename T, int D>
-static hipError_t lsh_meta_d(const CacheView &c, int tail, int L, int P, const float *planes, uint8_t *bucket,
-                             float *vnorm, const dim3 &grid, hipStream_t st) {
-  switch (P) {
-#define SKV_LSH_P(PP) \
-  case PP: meta_lsh_kernel<T, D, PP><<<grid, 256, 0, st>>>(c, tail, L, planes, bucket, vnorm); break;
-    SKV_LSH_P(1) SKV_LSH_P(2) SKV_LSH_P(3) SKV_LSH_P(4) SKV_LSH_P(5) SKV_LSH_P(6) SKV_LSH_P(7) SKV_LSH_P(8)
-#undef SKV_LSH_P
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+static void lsh_meta_d(const CacheView &c, int tail, const RowDotJob &job, float *vnorm, hipStream_t st) {
+  const dim3 g2 = rowdot_grid(c, tail, 1);
+  const int P = job.lsh_P;
+  if (P <= 2) meta_rowdot_kernel<T, D, 1, 2, true><<<g2, 256, 0, st>>>(c, tail, job);
+  else if (P <= 4) meta_rowdot_kernel<T, D, 1, 4, true><<<g2, 256, 0, st>>>(c, tail, job);
+  else if (P <= 6) meta_rowdot_kernel<T, D, 1, 6, true><<<g2, 256, 0, st>>>(c, tail, job);
+  else meta_rowdot_kernel<T, D, 1, 8, true><<<g2, 256, 0, st>>>(c, tail, job);
+  const long maxtok = tail > 0 ? min((long)tail, (long)c.maxP * c.S) : (long)c.maxP * c.S;
+  meta_vnorm_kernel<T, D><<<dim3((unsigned)((maxtok + 255) / 256), c.B * c.Hkv), 256, 0, st>>>(c, tail, vnorm);
 }
 
 hipError_t launch_build_lsh(const CacheView &c, int dtype, int tail, int L, int P, const float *planes,
                             uint8_t *bucket, float *vnorm, hipStream_t st) {
-  const int np = tail > 0 ? min(c.maxP, (tail + c.S - 1) / c.S + 1) : c.maxP;
-  const dim3 grid(np, c.B);
-  if (c.D == 64)
-    return dtype == 0 ? lsh_meta_d<float, 64>(c, tail, L, P, planes, bucket, vnorm, grid, st)
-                      : lsh_meta_d<uint16_t, 64>(c, tail, L, P, planes, bucket, vnorm, grid, st);
-  return dtype == 0 ? lsh_meta_d<float, 128>(c, tail, L, P, planes, bucket, vnorm, grid, st)
-                    : lsh_meta_d<uint16_t, 128>(c, tail, L, P, planes, bucket, vnorm, grid, st);
+  const RowDotJob job{8 * L, planes, L, P, nullptr, bucket};
+  if (c.D == 64) {
+    if (dtype == 0) lsh_meta_d<float, 64>(c, tail, job, vnorm, st); else lsh_meta_d<uint16_t, 64>(c, tail, job, vnorm, st);
+  } else {
+    if (dtype == 0) lsh_meta_d<float, 128>(c, tail, job, vnorm, st); else lsh_meta_d<uint16_t, 128>(c, tail, job, vnorm, st);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_build_meta(const CacheView &c, int dtype, int tail, void *box, float *gauss, int r,
@@ -469,13 +466,10 @@ hipError_t launch_build_meta(const CacheView &c, int dtype, int tail, void *box,
       meta_pool_kernel<uint16_t><<<gridw, 256, 0, st>>>(c, tail, ppw, pb, pool);
   }
   if (kproj) {
-    const int slab = min(r, kProjSlab);
-    const int sub = 4 / (slab / kProjOut);  // 512-token tiles per workgroup tile: 2 for r = 16
-    const int tile_tok = sub * 64 * kProjTok;
-    const long maxtok = tail > 0 ? min((long)tail, (long)c.maxP * c.S) : (long)c.maxP * c.S;
-    const long tiles = (maxtok + tile_tok - 1) / tile_tok;
-    const dim3 g2((unsigned)((tiles + kProjTilesPerWg - 1) / kProjTilesPerWg), c.B * c.Hkv);
-#define SKV_PROJ(TT, DD, SS) meta_proj_kernel<TT, DD, SS><<<g2, 256, 0, st>>>(c, tail, r, proj, kproj)
+    const int sub = r == 16 ? 2 : 1;  // 512-token tiles per workgroup tile
+    const dim3 g2 = rowdot_grid(c, tail, sub);
+    const RowDotJob job{r, proj, 0, 0, kproj, nullptr};
+#define SKV_PROJ(TT, DD, SS) meta_rowdot_kernel<TT, DD, SS, 8, false><<<g2, 256, 0, st>>>(c, tail, job)
 #define SKV_PROJ_D(TT, SS) \
   if (c.D == 64) SKV_PROJ(TT, 64, SS); else SKV_PROJ(TT, 128, SS);
     if (dtype == 0) {
