@@ -482,6 +482,32 @@ __device__ __forceinline__ void block_sum2(double &a, double &b, double2 *scratc
   __syncthreads();
 }
 
+// Three sums at once; scratch holds 3 * NT / kWave doubles.
+template <int NT>
+__device__ __forceinline__ void block_sum3(double &a, double &b, double &c, double *scratch) {
+  constexpr int NW = NT / kWave;
+  a = wave_sum_dpp(a);
+  b = wave_sum_dpp(b);
+  c = wave_sum_dpp(c);
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    const int w = threadIdx.x / kWave;
+    scratch[w] = a;
+    scratch[NW + w] = b;
+    scratch[2 * NW + w] = c;
+  }
+  __syncthreads();
+  a = 0.0;
+  b = 0.0;
+  c = 0.0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    a += scratch[i];
+    b += scratch[NW + i];
+    c += scratch[2 * NW + i];
+  }
+  __syncthreads();
+}
+
 template <int NT>
 __device__ __forceinline__ double block_max(double v, double *scratch) {
   constexpr int NW = NT / kWave;
