@@ -380,6 +380,43 @@ __global__ __launch_bounds__(256, 2) void meta_rowdot_kernel(CacheView c, int ta
   }
 }
 
+// The same row dots for few tokens (an append of up to kPairMaxTok tokens per sequence), where a
+// tile would compute 512 tokens for a handful: one thread per (token, output row) for projected
+// keys, per (token, table) for soft LSH (its P chains side by side), each chain the float64 sum
+// over j = 0..d-1 from 0 as above, so that the results equal the tile kernel's.
+constexpr int kPairMaxTok = 128;
+template <typename T, int D, int P>   // P hyperplanes per table (soft LSH), 0 for projected keys
+__global__ __launch_bounds__(256) void meta_rowdot_pairs_kernel(CacheView c, int tail, RowDotJob job) {
+  const int b = blockIdx.y / c.Hkv, g = blockIdx.y % c.Hkv;
+  const int L = seq_len(c, b);
+  const int lo = tail > 0 ? max(0, L - tail) : 0, ntok = L - lo;
+  const int outs = P ? job.lsh_L : job.nrows;  // outputs per token: tables, or rows of P
+  const int pair = blockIdx.x * blockDim.x + threadIdx.x;
+  if (pair >= ntok * outs) return;
+  const int tok = pair / outs, o = pair - tok * outs;
+  const size_t row = proj_row(c, b, g, lo + tok);
+  const T *k = static_cast<const T *>(c.k) + row * D;
+  constexpr int NA = P ? P : 1;
+  const float *w = job.mat + (size_t)o * NA * D;
+  double acc[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) acc[i] = 0.0;
+#pragma unroll 8
+  for (int j = 0; j < D; ++j) {
+    const double kv = (double)Elem<T>::get(k, j);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) acc[i] = fma((double)w[(size_t)i * D + j], kv, acc[i]);
+  }
+  if (P) {
+    uint32_t id = 0;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) id |= (acc[i] > 0.0 ? 1u : 0u) << i;
+    job.bucket[row * job.lsh_L + o] = (uint8_t)id;
+  } else {
+    job.kproj[row * job.nrows + o] = f64_to_bf16(acc[0]);
+  }
+}
+
 // Value norms for soft LSH: vnorm[row] = RN_f32(sqrt(sum_j v_j^2)), the float64 sum over j
 // ascending (the square of a cache element is exact in float64, so the fma rounds once as the
 // addition alone would). One thread per token row of a (sequence, KV head), 16-byte loads.
@@ -407,24 +444,51 @@ __global__ __launch_bounds__(256) void meta_vnorm_kernel(CacheView c, int tail, 
   vnorm[row] = (float)sqrt(ss);
 }
 
+// tokens per sequence a call covers at most
+static long rowdot_tokens(const CacheView &c, int tail) {
+  return tail > 0 ? min((long)tail, (long)c.maxP * c.S) : (long)c.maxP * c.S;
+}
+
 // Launch geometry of the row-dot kernel: 512-token tiles (two per workgroup tile for a 16-row
 // matrix), kProjTilesPerWg tiles per workgroup, one grid row per (sequence, KV head).
 static dim3 rowdot_grid(const CacheView &c, int tail, int sub) {
   const int tile_tok = sub * 64 * kProjTok;
-  const long maxtok = tail > 0 ? min((long)tail, (long)c.maxP * c.S) : (long)c.maxP * c.S;
+  const long maxtok = rowdot_tokens(c, tail);
   const long tiles = (maxtok + tile_tok - 1) / tile_tok;
   return dim3((unsigned)((tiles + kProjTilesPerWg - 1) / kProjTilesPerWg), c.B * c.Hkv);
+}
+
+template <typename T, int D, int P>
+static void rowdot_pairs(const CacheView &c, int tail, const RowDotJob &job, hipStream_t st) {
+  const long pairs = rowdot_tokens(c, tail) * (P ? job.lsh_L : job.nrows);
+  meta_rowdot_pairs_kernel<T, D, P><<<dim3((unsigned)((pairs + 255) / 256), c.B * c.Hkv), 256, 0, st>>>(c, tail, job);
+}
+
+template <typename T, int D>
+static void lsh_pairs(const CacheView &c, int tail, const RowDotJob &job, hipStream_t st) {
+  switch (job.lsh_P) {
+    case 1: rowdot_pairs<T, D, 1>(c, tail, job, st); break;
+    case 2: rowdot_pairs<T, D, 2>(c, tail, job, st); break;
+    case 3: rowdot_pairs<T, D, 3>(c, tail, job, st); break;
+    case 4: rowdot_pairs<T, D, 4>(c, tail, job, st); break;
+    case 5: rowdot_pairs<T, D, 5>(c, tail, job, st); break;
+    case 6: rowdot_pairs<T, D, 6>(c, tail, job, st); break;
+    case 7: rowdot_pairs<T, D, 7>(c, tail, job, st); break;
+    default: rowdot_pairs<T, D, 8>(c, tail, job, st); break;
+  }
 }
 
 template <typename T, int D>
 static void lsh_meta_d(const CacheView &c, int tail, const RowDotJob &job, float *vnorm, hipStream_t st) {
   const dim3 g2 = rowdot_grid(c, tail, 1);
   const int P = job.lsh_P;
-  if (P <= 2) meta_rowdot_kernel<T, D, 1, 2, true><<<g2, 256, 0, st>>>(c, tail, job);
+  if (rowdot_tokens(c, tail) <= kPairMaxTok)
+    lsh_pairs<T, D>(c, tail, job, st);
+  else if (P <= 2) meta_rowdot_kernel<T, D, 1, 2, true><<<g2, 256, 0, st>>>(c, tail, job);
   else if (P <= 4) meta_rowdot_kernel<T, D, 1, 4, true><<<g2, 256, 0, st>>>(c, tail, job);
   else if (P <= 6) meta_rowdot_kernel<T, D, 1, 6, true><<<g2, 256, 0, st>>>(c, tail, job);
   else meta_rowdot_kernel<T, D, 1, 8, true><<<g2, 256, 0, st>>>(c, tail, job);
-  const long maxtok = tail > 0 ? min((long)tail, (long)c.maxP * c.S) : (long)c.maxP * c.S;
+  const long maxtok = rowdot_tokens(c, tail);
   meta_vnorm_kernel<T, D><<<dim3((unsigned)((maxtok + 255) / 256), c.B * c.Hkv), 256, 0, st>>>(c, tail, vnorm);
 }
 
@@ -472,10 +536,13 @@ hipError_t launch_build_meta(const CacheView &c, int dtype, int tail, void *box,
 #define SKV_PROJ(TT, DD, SS) meta_rowdot_kernel<TT, DD, SS, 8, false><<<g2, 256, 0, st>>>(c, tail, job)
 #define SKV_PROJ_D(TT, SS) \
   if (c.D == 64) SKV_PROJ(TT, 64, SS); else SKV_PROJ(TT, 128, SS);
+    const bool pairs = rowdot_tokens(c, tail) <= kPairMaxTok;
     if (dtype == 0) {
-      if (sub == 2) { SKV_PROJ_D(float, 2) } else { SKV_PROJ_D(float, 1) }
+      if (pairs) { if (c.D == 64) rowdot_pairs<float, 64, 0>(c, tail, job, st); else rowdot_pairs<float, 128, 0>(c, tail, job, st); }
+      else if (sub == 2) { SKV_PROJ_D(float, 2) } else { SKV_PROJ_D(float, 1) }
     } else {
-      if (sub == 2) { SKV_PROJ_D(uint16_t, 2) } else { SKV_PROJ_D(uint16_t, 1) }
+      if (pairs) { if (c.D == 64) rowdot_pairs<uint16_t, 64, 0>(c, tail, job, st); else rowdot_pairs<uint16_t, 128, 0>(c, tail, job, st); }
+      else if (sub == 2) { SKV_PROJ_D(uint16_t, 2) } else { SKV_PROJ_D(uint16_t, 1) }
     }
 #undef SKV_PROJ_D
 #undef SKV_PROJ

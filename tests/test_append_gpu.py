@@ -25,6 +25,10 @@ CASES = [
     ("ragged", dict(B=3, lens=[4500, 129, 64]), 2),
     ("pool32k", dict(B=3, lens=[3000, 3003, 5]), 3),   # pooled key: sub-blocks of 4 in pages of 16
     ("socket128k", dict(B=3, lens=[5000, 4113, 2], k=256), 19),   # soft-LSH buckets and value norms
+    # more than 128 new tokens per sequence: the projected keys and soft-LSH buckets take the tiled
+    # row-dot kernel (fewer take one thread per token and output)
+    ("token128k", dict(B=2, lens=[5000, 900], k=512), 700),
+    ("socket128k", dict(B=2, lens=[5000, 300], k=256), 300),
 ]
 
 
