@@ -123,7 +123,9 @@ typedef struct skv_meta {
  * Not written: metadata of unused physical pages, kproj and LSH rows of tokens past L_b, and pool
  * rows of sub-blocks without a valid token.
  * Errors: SKV_ERR_INVALID_ARG for null or inconsistent arguments or a missing output of a
- * requested kind; SKV_ERR_UNSUPPORTED outside the supported set. */
+ * requested kind; SKV_ERR_UNSUPPORTED outside the supported set (also: PROJ or LSH over a cache
+ * of more than 2^32 - 1 KV rows, num_phys_pages * num_kv_heads * page_size, more than device
+ * memory holds). */
 skv_status skv_build_page_meta(const skv_cache *c, const skv_meta *m, void *stream);
 
 /* Keeps the metadata current while decoding. The metadata is stored per page and maintained as

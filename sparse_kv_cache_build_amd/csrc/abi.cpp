@@ -283,9 +283,12 @@ static skv_status meta_args(const skv_cache *c, const skv_meta *m) {
   if (proj) {
     if (!m->proj || !m->kproj || !aligned(m->kproj, 16)) return SKV_ERR_INVALID_ARG;
     if (!rank_ok(m->proj_rank)) return SKV_ERR_UNSUPPORTED;
-    // rows of kproj are indexed in 32 bits (more rows than that would not fit next to K anyway)
-    if ((uint64_t)c->num_phys_pages * c->num_kv_heads * c->page_size > 0xffffffffull) return SKV_ERR_UNSUPPORTED;
   }
+  // the row-dot kernels of the projected keys and soft-LSH buckets index token rows in 32 bits
+  // (more rows than that would not fit next to K anyway)
+  if ((proj || (m->kinds & SKV_META_LSH)) &&
+      (uint64_t)c->num_phys_pages * c->num_kv_heads * c->page_size > 0xffffffffull)
+    return SKV_ERR_UNSUPPORTED;
   return SKV_OK;
 }
 

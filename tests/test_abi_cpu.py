@@ -196,6 +196,13 @@ def test_score_and_meta_validation(L):
     small = 2 * 8 * 4 * 32 * 64 * 4 - 256                                            # B Hkv G L 2^P uint32, short
     assert L.skv_score_pages(C.byref(c), C.byref(lsh(32, 6)), C.c_void_p(FAKE), B.SCORE_LSH, 1.0, C.byref(out),
                              C.c_void_p(FAKE), small, None) == B.SKV_ERR_WORKSPACE
+    # the row-dot kernels index KV rows in 32 bits: a cache of 2^32 rows or more is refused for
+    # projected and soft-LSH metadata before anything is launched
+    huge = cache(num_phys_pages=1 << 25, page_size=16)                  # 2^25 * 8 * 16 = 2^32 rows
+    mp32 = B.Meta(B.META_PROJ, None, None, 32, FAKE, FAKE)
+    assert L.skv_build_page_meta(C.byref(huge), C.byref(mp32), None) == B.SKV_ERR_UNSUPPORTED
+    assert L.skv_build_page_meta(C.byref(huge), C.byref(lsh(32, 6)), None) == B.SKV_ERR_UNSUPPORTED
+    assert L.skv_append_page_meta(C.byref(huge), C.byref(lsh(32, 6)), 1, None) == B.SKV_ERR_UNSUPPORTED
     mq = B.Meta(B.META_BOX, FAKE, None, 0, None, None, 4, FAKE)    # pool array given, kind not set
     assert L.skv_score_pages(C.byref(c), C.byref(mq), C.c_void_p(FAKE), B.SCORE_POOL, 0.1, C.byref(out),
                              C.c_void_p(FAKE), 1 << 20, None) == B.SKV_ERR_INVALID_ARG
