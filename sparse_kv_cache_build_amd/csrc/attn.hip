@@ -123,28 +123,32 @@ __global__ __launch_bounds__(kAttnThreads) void attn_softmax_kernel(
     const int it = r / rows_per_item;
     return rm.row_offset(it0 + it, r - it * rows_per_item);
   };
-  auto accumulate = [&](const Packed8<T> &kx, const Packed8<T> &vp) {
+  // one row's update from its G logits (the group's summed dot products); the exponents are at
+  // most 32, and weights below 2^-126 of the reference (flushed to zero by v_exp_f32) add nothing
+  // visible next to the reference row's weight of at least 1
+  auto accumulate = [&](const float *zdot, const Packed8<T> &vp) {
     float vx[8];   // V stays packed until its row is used
 #pragma unroll
     for (int j = 0; j < 8; ++j) vx[j] = vp.at(j);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float z = group_sum<RL::LPR>(qv[h].dot(kx)) * scale_log2;
+      const float z = zdot[h] * scale_log2;
       if (z > mref[h] + 32.0f) {  // rescale the state to a new reference
-        const float corr = exp2f(mref[h] - z);
+        const float corr = __builtin_amdgcn_exp2f(mref[h] - z);
         l[h] *= corr;
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[h][j] *= corr;
         mref[h] = z;
       }
-      const float p = exp2f(z - mref[h]);
+      const float p = __builtin_amdgcn_exp2f(z - mref[h]);
       l[h] += p;
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(p, vx[j], acc[h][j]);
     }
   };
   // row offsets first (selection entry -> block table -> row), then UNR rows per lane group per
-  // step with all their loads in flight before any is used
+  // step with all their loads in flight before any is used; the UNR * G dot products are summed
+  // over the lane group together (one level for all of them, then the next)
   for (int r = tid; r < NR; r += kAttnThreads) roff[r] = row_off(r);
   __syncthreads();
   for (int r = rg; r < NR; r += UNR * RL::RGB) {
@@ -157,11 +161,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_softmax_kernel(
       if (o[u] >= 0) {
         kx[u].load_once(K + o[u] + lr * 8);
         vx[u].load_once(V + o[u] + lr * 8);
+      } else {
+        kx[u].zero();
       }
     }
+    float zd[UNR * G];
 #pragma unroll
     for (int u = 0; u < UNR; ++u)
-      if (o[u] >= 0) accumulate(kx[u], vx[u]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) zd[u * G + h] = qv[h].dot(kx[u]);
+    group_sum_n<RL::LPR>(zd);
+#pragma unroll
+    for (int u = 0; u < UNR; ++u)
+      if (o[u] >= 0) accumulate(zd + u * G, vx[u]);
   }
   // merge the lane groups: common reference per head, then sums
   if (lr == 0)

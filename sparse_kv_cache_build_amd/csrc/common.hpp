@@ -537,6 +537,25 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// group_sum of N independent values at once, one reduction level for all of them before the
+// next, so that the DPP reads of one value fill the wait states after another's addition.
+template <int CTL, int N>
+__device__ __forceinline__ void group_sum_level(float (&v)[N]) {
+  float t[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) t[i] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[i]), CTL, 0xF, 0xF, false));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += t[i];
+}
+template <int WIDTH, int N>
+__device__ __forceinline__ void group_sum_n(float (&v)[N]) {
+  static_assert(WIDTH == 8 || WIDTH == 16, "lane group of 8 or 16");
+  group_sum_level<0xB1>(v);   // the steps of group_sum
+  group_sum_level<0x4E>(v);
+  group_sum_level<0x141>(v);
+  if (WIDTH == 16) group_sum_level<0x140>(v);
+}
+
 // Radix selection over order keys get(i), i < n: finds the r-th largest key T (1 <= r <= n) and
 // need = r - #(keys > T), i.e. how many keys equal to T belong to the top r. Four 8-bit digits,
 // most significant first. Each wave counts into its own 256-bin LDS histogram (the leading digits
