@@ -12,7 +12,7 @@ namespace skv {
 // key row): V = 16 / sizeof(T) consecutive coordinates, so 64 consecutive items read whole rows
 // (256 bytes for d = 128 bf16) and a wave instruction covers several rows. A workgroup takes
 // `ppw` consecutive pages of one sequence; each item walks its page's valid tokens in ascending
-// order, RB rows in flight.
+// order, kMetaRows rows in flight.
 //   box:   min / max over the valid tokens from +inf / -inf with strict comparisons, stored as
 //          the element bits, the 64-byte blocks of the min row and of the max row alternating
 //          ([d / C][2][C], C = 64 bytes).
