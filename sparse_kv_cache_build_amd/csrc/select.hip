@@ -150,10 +150,29 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(CacheView c, c
   uint32_t T, need;
   auto ident = [](int i) { return i; };
   if (sz.n <= kSelLds) {
-    for (int i = tid; i < sz.n; i += kSelThreads) skeys[i] = f32_order_key(kr[i]);
+    // the keys' range comes with the load: radix passes over the leading digits that every key
+    // shares are skipped (page keys of a unit share their leading byte as a rule)
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+    for (int i = tid; i < sz.n; i += kSelThreads) {
+      const uint32_t u = f32_order_key(kr[i]);
+      skeys[i] = u;
+      kmin = min(kmin, u);
+      kmax = max(kmax, u);
+    }
+    kmin = wave_umin_dpp(kmin);
+    kmax = wave_umax_dpp(kmax);
+    if ((tid & (kWave - 1)) == 0) {
+      hist[tid / kWave] = kmin;   // hist is free until the radix passes clear it
+      hist[kSelThreads / kWave + tid / kWave] = kmax;
+    }
     __syncthreads();
+    for (int w = 0; w < kSelThreads / kWave; ++w) {
+      kmin = min(kmin, hist[w]);
+      kmax = max(kmax, hist[kSelThreads / kWave + w]);
+    }
+    __syncthreads();   // every thread has read the range before the first pass clears hist
     auto get = [&](int i) { return skeys[i]; };
-    radix_kth<kSelThreads>(get, sz.n, (uint32_t)sz.k, hist, bc, T, need);
+    radix_kth<kSelThreads>(get, sz.n, (uint32_t)sz.k, hist, bc, T, need, 4, kmin, kmax);
     ordered_take<kSelThreads>(get, ident, sz.n, T, need, out, scan_scratch);
   } else {
     auto get = [&](int i) { return f32_order_key(kr[i]); };
