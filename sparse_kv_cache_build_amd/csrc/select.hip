@@ -895,6 +895,7 @@ __global__ __launch_bounds__(kTauThreads) void tau_hat_kernel(CacheView c, const
                                                               float *__restrict__ tau_out) {
   __shared__ float t_mu[kTauLds], t_sd[kTauLds], t_isd[kTauLds];
   __shared__ double red3[3 * (kTauThreads / kWave)];
+  __shared__ int s_step[2];   // tau (bits) and whether the iteration is over, from wave 0
   __shared__ float redf[kTauThreads / kWave];
   __shared__ float t_lk[KIND == 2 ? kItabN : 1], t_lk1[KIND == 2 ? kItabN : 1];
   const int bh = blockIdx.x, b = bh / c.Hq;
@@ -944,32 +945,67 @@ __global__ __launch_bounds__(kTauThreads) void tau_hat_kernel(CacheView c, const
       dF += (double)(n * dE);
       if (KIND != 2) d2F += (double)(n * d2E);
     }
-    block_sum3<kTauThreads>(F, dF, d2F, red3);
-    F -= 1.0;
-    if (!(F != 0.0)) break;   // on the root, or not a number
-    if (F > 0.0) lo = tau; else hi = tau;
-    const double tol = 0x1p-20 * fmax(1.0, fabs((double)tau));
-    if ((double)hi - (double)lo <= tol) break;
-    const double S = F + 1.0;
-    const bool left_ok = F > 0.0 && dF < 0.0;
-    if (dF < 0.0 && fabs(F / dF) <= tol) {   // within the float noise of F: one plain step
-      tau = (float)((double)tau - F / dF);
-      break;
+    // the waves' sums go to wave 0, which alone takes the step (the sums in the same order as a
+    // block reduction) and hands tau, and whether the iteration is over, to the others in LDS
+    F = wave_sum_dpp(F);
+    dF = wave_sum_dpp(dF);
+    d2F = wave_sum_dpp(d2F);
+    constexpr int NW = kTauThreads / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+      const int w = threadIdx.x / kWave;
+      red3[w] = F;
+      red3[NW + w] = dF;
+      red3[2 * NW + w] = d2F;
     }
-    float next = NAN;
-    if (dF < 0.0 && S > 0.0) {
-      const double ls = log(S);
-      if (KIND != 2) {
-        const double g1 = dF / S, g2 = (d2F * S - dF * dF) / (S * S), den = 2.0 * g1 * g1 - ls * g2;
-        if (den > 0.0) next = (float)((double)tau - 2.0 * ls * g1 / den);
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+      F = 0.0;
+      dF = 0.0;
+      d2F = 0.0;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        F += red3[i];
+        dF += red3[NW + i];
+        d2F += red3[2 * NW + i];
+      }
+      bool done = false;
+      F -= 1.0;
+      if (!(F != 0.0)) {   // on the root, or not a number
+        done = true;
       } else {
-        next = (float)((double)tau - (ls > 2.0 ? 0.5 : 1.0) * ls * S / dF);   // halved far out, where it overshoots
+        if (F > 0.0) lo = tau; else hi = tau;
+        const double tol = 0x1p-20 * fmax(1.0, fabs((double)tau));
+        const double S = F + 1.0;
+        const bool left_ok = F > 0.0 && dF < 0.0;
+        if ((double)hi - (double)lo <= tol) {
+          done = true;
+        } else if (dF < 0.0 && fabs(F / dF) <= tol) {   // within the float noise of F: one plain step
+          tau = (float)((double)tau - F / dF);
+          done = true;
+        } else {
+          float next = NAN;
+          if (dF < 0.0 && S > 0.0) {
+            const double ls = log(S);
+            if (KIND != 2) {
+              const double g1 = dF / S, g2 = (d2F * S - dF * dF) / (S * S), den = 2.0 * g1 * g1 - ls * g2;
+              if (den > 0.0) next = (float)((double)tau - 2.0 * ls * g1 / den);
+            } else {
+              next = (float)((double)tau - (ls > 2.0 ? 0.5 : 1.0) * ls * S / dF);   // halved far out, where it overshoots
+            }
+          }
+          if (!(next > lo && next < hi) && left_ok) next = (float)((double)tau - F / dF);
+          if (!(next > lo && next < hi)) next = hi < INFINITY ? 0.5f * (lo + hi) : lo + 2.0f * (tau - lo + 1.0f);
+          if (next == tau) done = true; else tau = next;
+        }
+      }
+      if (threadIdx.x == 0) {
+        s_step[0] = __float_as_int(tau);
+        s_step[1] = done ? 1 : 0;
       }
     }
-    if (!(next > lo && next < hi) && left_ok) next = (float)((double)tau - F / dF);
-    if (!(next > lo && next < hi)) next = hi < INFINITY ? 0.5f * (lo + hi) : lo + 2.0f * (tau - lo + 1.0f);
-    if (next == tau) break;
-    tau = next;
+    __syncthreads();
+    tau = __int_as_float(s_step[0]);
+    if (s_step[1]) break;
   }
   if (threadIdx.x == 0) tau_out[bh] = tau;
 }
