@@ -416,20 +416,26 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
   entmax_compact<G>(zs, zl, rps, NR, unit, split, nsplit, it0 * rows_per_item, wmax, false, cand, cand_cnt, cand_max);
 }
 
-// Entmax pass 1 for bf16 caches on the matrix cores: the logits of a 16-row tile for all G heads
-// are one 16 x 16 product of the tile's K rows (A, 16 x d) with q^T of the group (B, d x 16, heads
-// past G zero), d/32 v_mfma_f32_16x16x32_bf16 per tile. Lane l supplies A[l % 16][8 (l / 16) ..]
-// and B[8 (l / 16) ..][l % 16] of each 32-wide slice of d and receives the logits of rows
-// 4 (l / 16) .. + 3 for head l % 16. Each wave takes every fourth tile, with the K loads of UNR
-// tiles in flight before their products. bf16 products are exact and the sums are float32, as
-// on the VALU path.
+// Entmax pass 1 for bf16 caches on the matrix cores, on tiles of 8 rows. A dot product may take
+// its coordinates in any order, so each v_mfma_f32_16x16x32_bf16 covers 64 coordinates of 8 rows:
+// A row m = 2 p + s holds coordinates 64 kb + 32 s + [0, 32) of tile row p, B column c = n + 8 s'
+// holds the same slice (s') of head n's q (heads past G zero), and C[2 p + s][n + 8 s'] is a
+// partial dot product. The logit of row p and head n is C[2p][n] + C[2p + 1][n + 8]: the two
+// halves sit in lanes c and c + 8 of the same row of 16 lanes and are added with one DPP move.
+// Lane l supplies A[l % 16][8 (l / 16) ..], so the 8 lanes of tile row p read 128 consecutive
+// bytes and one load instruction reads 8 whole rows of 128-byte lines (a 16-row tile would split
+// every line over two instructions), and since every line is then read whole by one instruction
+// the loads are marked non-temporal. d/64 products per tile. Each wave takes every fourth tile,
+// with the K loads of UNR tiles in flight before their products. bf16 products are exact and the
+// sums are float32, as on the VALU path.
 
 template <int D, int G>
 __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_mfma_kernel(
     CacheView c, const uint16_t *__restrict__ q, const int32_t *__restrict__ sel_idx,
     const int32_t *__restrict__ sel_count, int cap, int gran, int spi, int nsplit, float zscale,
     float2 *__restrict__ cand, int32_t *__restrict__ cand_cnt, float *__restrict__ cand_max) {
-  constexpr int KB = D / 32, UNR = 4, NWV = kAttnThreads / kWave;
+  static_assert(G <= 8, "the B columns hold 8 heads times two coordinate halves");
+  constexpr int KB = D / 64, UNR = 4, NWV = kAttnThreads / kWave;
   extern __shared__ float zs[];  // logits (ZLayout), then [rps] row offsets (8-byte aligned)
   __shared__ float wmax[kAttnThreads / kWave][G];
   const int split = blockIdx.x, unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
@@ -444,12 +450,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_mfma_kernel(
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int L = seq_len(c, b);
   RowMap rm{sel_idx + (size_t)unit * cap, c.bt + (size_t)b * c.maxP, gran, c.S, c.Hkv, g, D, L, num_pages(c, L)};
-  const int n = lane & 15, kq = 8 * (lane >> 4);
+  // this lane's column of B: head n, coordinate half hs; its A row: tile row pr, half hs too
+  // (m = lane % 16 = 2 pr + hs); its 8 coordinates of the 32 of a half start at kq
+  const int col = lane & 15, n = col & 7, hs = col >> 3, kq = 8 * (lane >> 4);
+  const int pr = col >> 1, ha = col & 1;
   bf16x8_t qb[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     uint4 w = make_uint4(0u, 0u, 0u, 0u);
-    if (n < G) w = *reinterpret_cast<const uint4 *>(q + ((size_t)b * c.Hq + g * G + n) * D + 32 * kb + kq);
+    if (n < G)
+      w = *reinterpret_cast<const uint4 *>(q + ((size_t)b * c.Hq + g * G + n) * D + 64 * kb + 32 * hs + kq);
     qb[kb] = __builtin_bit_cast(bf16x8_t, w);
   }
   // row indices (not element offsets: half the LDS, which keeps four workgroups per CU at G = 8);
@@ -462,35 +472,43 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_mfma_kernel(
   }
   __syncthreads();
   const uint16_t *K = static_cast<const uint16_t *>(c.k);
-  const int ntile = (NR + 15) / 16;
-  float mxl = -INFINITY;   // the largest logit of head n among this lane's rows
+  const int ntile = (NR + 7) / 8;
+  float mxl = -INFINITY;   // the largest logit of head n among this lane's rows (lanes col < G)
   for (int t0 = wave; t0 < ntile; t0 += NWV * UNR) {
     bf16x8_t a[UNR][KB];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int row = (t0 + u * NWV) * 16 + (lane & 15);
+      const int row = (t0 + u * NWV) * 8 + pr;
       const uint32_t ri = row < NR ? ridx[row] : 0xffffffffu;
-      const uint16_t *kr = K + (size_t)ri * D;
+      const uint16_t *kr = K + (size_t)ri * D + 32 * ha + kq;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         uint4 w = make_uint4(0u, 0u, 0u, 0u);
-        if (ri != 0xffffffffu) w = *reinterpret_cast<const uint4 *>(kr + 32 * kb + kq);
+        if (ri != 0xffffffffu) w = ld_once(reinterpret_cast<const uint4 *>(kr + 64 * kb));
         a[u][kb] = __builtin_bit_cast(bf16x8_t, w);
       }
     }
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int tb = (t0 + u * NWV) * 16;
+      const int tb = (t0 + u * NWV) * 8;
       if (tb >= NR) break;
       f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][kb], qb[kb], acc, 0, 0, 0);
-      if (n < G) {
+      // acc[i] = C[4 (lane / 16) + i][col]: tile row 2 (lane / 16) + i / 2, A half i % 2. The
+      // second half of head n's dot product is in lane col + 8 (row_ror:8 within the 16 lanes),
+      // taken by every lane so that each source lane is active
+      float z[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = tb + 4 * (lane >> 4) + i;
+      for (int i = 0; i < 2; ++i)
+        z[i] = acc[2 * i] +
+               __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc[2 * i + 1]), 0x128, 0xf, 0xf, false));
+      if (col < G) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = tb + 2 * (lane >> 4) + i;
           if (r < NR) {
-            const float v = ridx[r] != 0xffffffffu ? acc[i] * zscale : -INFINITY;
+            const float v = ridx[r] != 0xffffffffu ? z[i] * zscale : -INFINITY;
             zs[zl.at(n, r)] = v;
             mxl = fmaxf(mxl, v);
           }
