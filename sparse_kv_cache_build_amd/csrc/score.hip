@@ -121,7 +121,8 @@ __global__ __launch_bounds__(256) void score_box_kernel(CacheView c, const T *__
 // ascending (the query terms come from the (q, q^2) staging), takes the largest over the heads and
 // its valid sub-blocks (those holding a token), the page's lanes combine, and key[b][g][p] is the
 // float32 rounding of the result; -inf past the sequence. The next chunk is loaded while the current
-// one is summed.
+// one is summed. Every line is read once and whole by one instruction, so the loads are marked
+// non-temporal.
 template <int D, int G>
 __global__ __launch_bounds__(256) void score_pool_kernel(CacheView c, int pb, int lw, const float *__restrict__ pool,
                                                          const double *__restrict__ qpm, float *__restrict__ key) {
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(256) void score_pool_kernel(CacheView c, int pb, in
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     off[k] = row_off(lrow + 8 * k, 0);
-    r[k] = off[k] >= 0 ? *reinterpret_cast<const float4 *>(pool + off[k] + lcol) : make_float4(0.f, 0.f, 0.f, 0.f);
+    r[k] = off[k] >= 0 ? ld_once(reinterpret_cast<const float4 *>(pool + off[k] + lcol)) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   double best = -INFINITY, acc[G];
   const int total = T * NC;
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(256) void score_pool_kernel(CacheView c, int pb, in
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         if (c1 == 0) off[k] = row_off(lrow + 8 * k, t1);
-        r[k] = off[k] >= 0 ? *reinterpret_cast<const float4 *>(pool + off[k] + c1 * CW + lcol)
+        r[k] = off[k] >= 0 ? ld_once(reinterpret_cast<const float4 *>(pool + off[k] + c1 * CW + lcol))
                            : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
@@ -349,7 +350,8 @@ __global__ __launch_bounds__(256) void score_lsh_kernel(CacheView c, int L, int 
 // 128-byte line of the metadata (64 bytes of means, then the 64 bytes of variances of the same
 // coordinates: 8 lanes per page, eight pages per load instruction) into LDS, where each lane sums
 // its page with the (q, q^2) pairs read as broadcasts (8 bytes per head and coordinate). The next
-// chunk is loaded while the current one is summed.
+// chunk is loaded while the current one is summed; the loads are non-temporal, each line being read
+// once and whole by one instruction.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const T *__restrict__ q,
                                                           const float *__restrict__ gauss, float scale, int quantile,
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const T *
   for (int k = 0; k < NK; ++k) {
     const int p = p0 + lrow + 8 * k;
     off[k] = p < np ? ((long long)bt[p] * c.Hkv + g) * 2 * D + half * CW + lcol : -1;
-    r[k] = off[k] >= 0 ? *reinterpret_cast<const float4 *>(gauss + off[k]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    r[k] = off[k] >= 0 ? ld_once(reinterpret_cast<const float4 *>(gauss + off[k])) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   float *xw = xs[wave];
   float sm[G], sv[G];
@@ -399,7 +401,7 @@ __global__ __launch_bounds__(256) void score_gauss_kernel(CacheView c, const T *
     if (ch + 1 < NC) {
 #pragma unroll
       for (int k = 0; k < NK; ++k)
-        r[k] = off[k] >= 0 ? *reinterpret_cast<const float4 *>(gauss + off[k] + (ch + 1) * 2 * CW)
+        r[k] = off[k] >= 0 ? ld_once(reinterpret_cast<const float4 *>(gauss + off[k] + (ch + 1) * 2 * CW))
                            : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     __builtin_amdgcn_wave_barrier();   // the chunk is in LDS for every lane of the wave
