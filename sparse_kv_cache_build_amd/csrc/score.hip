@@ -276,68 +276,110 @@ __global__ __launch_bounds__(256) void lsh_prep_kernel(CacheView c, const T *__r
 }
 
 // Soft-collision token keys: one workgroup per (kLshTok tokens, unit). The unit's bucket masses
-// [L, 2^P, G] are copied into LDS; a lane per token reads its L bucket ids (16-byte loads; the
-// tokens of a page are adjacent rows), adds up the G heads' masses of its bucket over the tables
-// (uint32, exact), and key = RN_f32(vnorm * (largest sum) * 2^-24), one float64 product. Tokens
-// past the sequence get -inf.
+// [L, 2^P, G] and the block-table entries of the workgroup's pages are copied into LDS. A token's
+// L bucket ids (L bytes, the tokens of a page adjacent rows) are read by L/16 lanes (4 when L = 48,
+// the fourth idle), 16 tables each, so one load instruction reads 64/lpt consecutive tokens' ids:
+// whole 128-byte lines, read once (non-temporal). Each lane adds up the G heads' masses of its
+// tables' buckets (uint32, exact, so the order of the sums does not matter), the token's lanes
+// combine their sums with DPP moves, and key = RN_f32(vnorm * (largest sum) * 2^-24), one float64
+// product. A lane takes 4 tokens per step, and the next step's ids are loaded while the current
+// ones are summed. Tokens past the sequence get -inf.
+constexpr int kLshUnr = 4;   // tokens per lane and step
 template <int G>
 __global__ __launch_bounds__(256) void score_lsh_kernel(CacheView c, int L, int P, const uint8_t *__restrict__ bucket,
                                                         const float *__restrict__ vnorm,
                                                         const uint32_t *__restrict__ tab, float *__restrict__ key) {
-  extern __shared__ uint4 ts4[];
+  extern __shared__ uint4 ts4[];   // masses, then the block-table entries of the workgroup's pages
   const uint32_t *ts = reinterpret_cast<const uint32_t *>(ts4);
   const int unit = blockIdx.y, b = unit / c.Hkv, g = unit - b * c.Hkv;
   const int len = seq_len(c, b);
   const int ntok = c.maxP * c.S;
   const int t0 = blockIdx.x * kLshTok, t1 = min(ntok, t0 + kLshTok);
   float *out = key + (size_t)unit * ntok;
-  if (t0 >= len) {
-    for (int t = t0 + threadIdx.x; t < t1; t += blockDim.x) out[t] = -INFINITY;
-    return;
-  }
+  const int tend = min(t1, len);   // tokens [t0, tend) are scored, [tend, t1) get -inf
+  for (int t = max(t0, tend) + threadIdx.x; t < t1; t += blockDim.x) out[t] = -INFINITY;
+  if (t0 >= tend) return;
   const int ne = (L << P) * G;   // a multiple of 16 (L is)
   const uint4 *src = reinterpret_cast<const uint4 *>(tab + (size_t)unit * ne);
   for (int i = threadIdx.x; i < ne / 4; i += blockDim.x) ts4[i] = src[i];
+  int *sbt = reinterpret_cast<int *>(ts4 + ne / 4);
+  const int p0 = t0 / c.S, np = (tend - 1) / c.S - p0 + 1;
+  const int *bt = c.bt + (size_t)b * c.maxP + p0;
+  for (int i = threadIdx.x; i < np; i += blockDim.x) sbt[i] = bt[i];
   __syncthreads();
-  const int *bt = c.bt + (size_t)b * c.maxP;
+  const int lpt = L == 16 ? 1 : (L == 32 ? 2 : 4);   // lanes per token
+  const int tpw = kWave / lpt;                        // tokens per wave and load instruction
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int piece = lane & (lpt - 1);
+  const bool has = piece * 16 < L;
   const uint32_t nbm = (1u << P) - 1;
-  for (int t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
-    if (t >= len) {
-      out[t] = -INFINITY;
-      continue;
-    }
-    const int p = t / c.S;
-    const size_t row = ((size_t)bt[p] * c.Hkv + g) * c.S + (t - p * c.S);
-    const uint4 *bq = reinterpret_cast<const uint4 *>(bucket + row * L);
-    uint32_t sum[G];
+  const int per_step = (256 / kWave) * kLshUnr * tpw;   // tokens of the workgroup per step
+  const int nstep = (tend - t0 + per_step - 1) / per_step;
+  // token u of this lane in step s
+  auto tok = [&](int s, int u) { return t0 + s * per_step + (u * (256 / kWave) + wave) * tpw + lane / lpt; };
+  auto load = [&](int s, uint4 (&w)[kLshUnr], float (&vn)[kLshUnr]) {
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) sum[hh] = 0;
-    for (int lq = 0; lq < L / 16; ++lq) {
-      const uint4 wv = bq[lq];
-      const uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const uint32_t bb = (w4[k >> 2] >> (8 * (k & 3))) & nbm;   // ids are < 2^P; the mask keeps LDS in range
-        const uint32_t *e = ts + (((size_t)(lq * 16 + k) << P) + bb) * G;
-        if constexpr (G >= 4) {
-#pragma unroll
-          for (int h4 = 0; h4 < G; h4 += 4) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(e + h4);
-            sum[h4] += v.x;
-            sum[h4 + 1] += v.y;
-            sum[h4 + 2] += v.z;
-            sum[h4 + 3] += v.w;
-          }
-        } else {
-#pragma unroll
-          for (int hh = 0; hh < G; ++hh) sum[hh] += e[hh];
-        }
+    for (int u = 0; u < kLshUnr; ++u) {
+      const int t = tok(s, u);
+      w[u] = make_uint4(0u, 0u, 0u, 0u);
+      vn[u] = 0.0f;
+      if (t < tend) {
+        const int p = t / c.S;
+        const size_t row = ((size_t)sbt[p - p0] * c.Hkv + g) * c.S + (t - p * c.S);
+        if (has) w[u] = ld_once(reinterpret_cast<const uint4 *>(bucket + row * L) + piece);
+        if (piece == 0) vn[u] = vnorm[row];
       }
     }
-    uint32_t best = sum[0];
+  };
+  uint4 wc[kLshUnr], wn[kLshUnr];
+  float vc[kLshUnr], vnx[kLshUnr];
+  load(0, wc, vc);
+  for (int s = 0; s < nstep; ++s) {   // uniform over the workgroup: every lane takes part in the DPP sums
+    if (s + 1 < nstep) load(s + 1, wn, vnx);
 #pragma unroll
-    for (int hh = 1; hh < G; ++hh) best = max(best, sum[hh]);
-    out[t] = (float)((double)vnorm[row] * ldexp((double)best, -24));
+    for (int u = 0; u < kLshUnr; ++u) {
+      uint32_t sum[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) sum[hh] = 0;
+      if (has) {
+        const uint32_t w4[4] = {wc[u].x, wc[u].y, wc[u].z, wc[u].w};
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const uint32_t bb = (w4[k >> 2] >> (8 * (k & 3))) & nbm;   // ids are < 2^P; the mask keeps LDS in range
+          const uint32_t *e = ts + (((size_t)(piece * 16 + k) << P) + bb) * G;
+          if constexpr (G >= 4) {
+#pragma unroll
+            for (int h4 = 0; h4 < G; h4 += 4) {
+              const uint4 v = *reinterpret_cast<const uint4 *>(e + h4);
+              sum[h4] += v.x;
+              sum[h4 + 1] += v.y;
+              sum[h4 + 2] += v.z;
+              sum[h4 + 3] += v.w;
+            }
+          } else {
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) sum[hh] += e[hh];
+          }
+        }
+      }
+      // the token's lanes are adjacent: add their sums (quad_perm xor 1, then xor 2)
+      if (lpt >= 2)
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) sum[hh] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sum[hh], 0xb1, 0xf, 0xf, false);
+      if (lpt >= 4)
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) sum[hh] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sum[hh], 0x4e, 0xf, 0xf, false);
+      uint32_t best = sum[0];
+#pragma unroll
+      for (int hh = 1; hh < G; ++hh) best = max(best, sum[hh]);
+      const int t = tok(s, u);
+      if (piece == 0 && t < tend) out[t] = (float)((double)vc[u] * ldexp((double)best, -24));
+    }
+#pragma unroll
+    for (int u = 0; u < kLshUnr; ++u) {
+      wc[u] = wn[u];
+      vc[u] = vnx[u];
+    }
   }
 }
 
@@ -753,7 +795,8 @@ static hipError_t lsh_d(const CacheView &c, int dtype, const void *q, int L, int
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((c.maxP * c.S + kLshTok - 1) / kLshTok, c.B * c.Hkv);
-  const size_t lds = sizeof(uint32_t) * ((size_t)L << P) * c.G;
+  // masses, then the block-table entries of the pages of kLshTok tokens (at most kLshTok / S + 2)
+  const size_t lds = sizeof(uint32_t) * ((size_t)L << P) * c.G + sizeof(int) * (size_t)(kLshTok / c.S + 2);
   hipError_t e0 = ev.before(st);
   if (e0 != hipSuccess) return e0;
   SKV_DISPATCH_G(c.G, score_lsh_kernel<GG><<<grid, 256, lds, st>>>(c, L, P, bucket, vnorm, tab, key))
