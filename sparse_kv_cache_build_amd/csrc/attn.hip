@@ -16,7 +16,8 @@
 //          logit exceeds the running reference by 2^32 (in log2 units), then the groups are
 //          merged in the block and across splits by a fixed-order log-sum-exp combine.
 // entmax:  pass 1 writes, per (unit, head, split), the split's maximum of z' = (alpha-1) z and the
-//          (z', slot) pairs with z' > max - 1, in row order. Since the global threshold satisfies
+//          (z', row) pairs with z' > max - 1, in row order (row: the V row's index, so the solve
+//          reads V without going back through the selection and the block table). Since the global threshold satisfies
 //          tau >= max_all z' - 1, no other row can carry weight. The solve kernel (one block per
 //          query head) keeps the pairs with z' > max_all - 1, bisects tau, refines it with the
 //          closed form on the support (alpha = 2, 1.5), and accumulates p v reading V rows with
@@ -289,10 +290,11 @@ struct ZLayout {
 // contiguous chunk of rows, so the thread order is the row order; the survivor counts of the G
 // heads are combined over the block with one barrier. The per-wave maxima of the heads are in
 // wmax: filled by the caller when have_max (then published by a barrier before the call), else
-// computed here from the LDS logits. Every thread of the block must call it.
-template <int G>
+// computed here from the LDS logits. rowid(r) is the K/V row index of partition row r (rows with a
+// finite logit are valid ones). Every thread of the block must call it.
+template <int G, typename RowId>
 __device__ __forceinline__ void entmax_compact(const float *zs, ZLayout zl, int rps, int NR, int unit, int split,
-                                               int nsplit, int row0, float (*wmax)[G], bool have_max,
+                                               int nsplit, RowId rowid, float (*wmax)[G], bool have_max,
                                                float2 *__restrict__ cand, int32_t *__restrict__ cand_cnt,
                                                float *__restrict__ cand_max) {
   constexpr int NW = kAttnThreads / kWave;
@@ -346,7 +348,7 @@ __device__ __forceinline__ void entmax_compact(const float *zs, ZLayout zl, int 
     int pos = before + incl[h] - nk[h];
     for (int r = r0; r < r1; ++r) {
       const float z = zs[zl.at(h, r)];
-      if (z > mx[h] - 1.0f) cl[pos++] = make_float2(z, __int_as_float(row0 + r));
+      if (z > mx[h] - 1.0f) cl[pos++] = make_float2(z, __uint_as_float(rowid(r)));
     }
     if (tid == 0) {
       cand_cnt[lid] = tot;
@@ -413,7 +415,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_kernel(
       if (r + u * RL::RGB < NR) logits(r + u * RL::RGB, o[u], kx[u]);
   }
   __syncthreads();
-  entmax_compact<G>(zs, zl, rps, NR, unit, split, nsplit, it0 * rows_per_item, wmax, false, cand, cand_cnt, cand_max);
+  auto rowid = [&](int r) { return (uint32_t)(roff[r] / D); };
+  entmax_compact<G>(zs, zl, rps, NR, unit, split, nsplit, rowid, wmax, false, cand, cand_cnt, cand_max);
 }
 
 // Entmax pass 1 for bf16 caches on the matrix cores, on tiles of 8 rows. A dot product may take
@@ -521,7 +524,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_mfma_kernel(
   mxl = fmaxf(mxl, __shfl_xor(mxl, 32, kWave));
   if (lane < G) wmax[wave][lane] = mxl;
   __syncthreads();
-  entmax_compact<G>(zs, zl, rps, NR, unit, split, nsplit, it0 * rows_per_item, wmax, true, cand, cand_cnt, cand_max);
+  auto rowid = [&](int r) { return ridx[r]; };
+  entmax_compact<G>(zs, zl, rps, NR, unit, split, nsplit, rowid, wmax, true, cand, cand_cnt, cand_max);
 }
 
 // ---------------------------------------------------------------- entmax threshold and p V
@@ -537,7 +541,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_entmax_logits_mfma_kernel(
 //     For alpha = 1.5 and 2 the bisection stops once no survivor lies in (lo, hi]: the support is
 //     then settled. Up to 256 survivors are held in registers; sums over lanes use DPP.
 //  4. p = (z' - tau)_+^(1/(alpha-1)) (renormalized for other alpha), out = sum p v over rows with
-//     p > 0, read in place through the selection and block table.
+//     p > 0, read in place at the V rows pass 1 recorded with each pair.
 // When the survivors do not fit in LDS, steps 3-4 read the flat list from global memory instead.
 constexpr int kSolveCap = 1024;     // survivors staged in LDS
 constexpr int kSolveSplits = 2048;  // split offsets staged in LDS (the planner keeps nsplit below)
@@ -551,7 +555,7 @@ __global__ __launch_bounds__(kWave) void attn_entmax_solve_kernel(
   using RL = RowLayout<D>;
   constexpr int RG = kWave / RL::LPR;  // row groups in the wave
   __shared__ float cz[kSolveCap];
-  __shared__ int cslot[kSolveCap];
+  __shared__ uint32_t crow[kSolveCap];   // the survivors' V rows
   __shared__ __align__(8) int soff[kSolveSplits + 1];   // later reused as the support's row offsets
   const int bh = blockIdx.x, b = bh / c.Hq, h = bh - b * c.Hq, g = h / c.G, hh = h - g * c.G;
   const int unit = b * c.Hkv + g;
@@ -637,7 +641,7 @@ __global__ __launch_bounds__(kWave) void attn_entmax_solve_kernel(
         const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
         if (keep && pos < kSolveCap) {
           cz[pos] = e[u].x;
-          cslot[pos] = __float_as_int(e[u].y);
+          crow[pos] = __float_as_uint(e[u].y);
         }
         n += __popcll(bal);
       }
@@ -668,21 +672,12 @@ __global__ __launch_bounds__(kWave) void attn_entmax_solve_kernel(
     const int i = lane + j * kWave;
     zr[j] = (in_regs && i < n) ? cz[i] : -INFINITY;
   }
-  const int L = seq_len(c, b);
-  RowMap rm{sel_idx + (size_t)unit * cap, c.bt + (size_t)b * c.maxP, gran, c.S, c.Hkv, g, D, L, num_pages(c, L)};
-  // the selection entries of the register-held survivors are read now, their block-table entries
-  // after the bisection, so that both loads wait behind the threshold arithmetic, not after it
-  int selv[ZR], tin[ZR];
+  // the V row offsets of the register-held survivors
+  long long offr[ZR];
 #pragma unroll
   for (int j = 0; j < ZR; ++j) {
     const int i = lane + j * kWave;
-    selv[j] = -1;
-    tin[j] = 0;
-    if (in_regs && i < n) {
-      const int slot = cslot[i], item = slot / rows_per_item;
-      tin[j] = slot - item * rows_per_item;
-      selv[j] = rm.sel[item];
-    }
+    offr[j] = (in_regs && i < n) ? (long long)crow[i] * D : -1;
   }
   // 3. bisection; for alpha = 1.5 and 2 it stops as soon as no survivor lies in (lo, hi]: the
   //    support {z' > tau} is then settled and the closed form below gives tau from it
@@ -749,9 +744,6 @@ __global__ __launch_bounds__(kWave) void attn_entmax_solve_kernel(
       khi = cnt;
     }
   }
-  long long offr[ZR];
-#pragma unroll
-  for (int j = 0; j < ZR; ++j) offr[j] = (in_regs && lane + j * kWave < n) ? rm.offset_of(selv[j], tin[j]) : -1;
   float tau = lo;
   if (ALPHA_KIND != 3) {
     int prev = -1;
@@ -840,8 +832,7 @@ __global__ __launch_bounds__(kWave) void attn_entmax_solve_kernel(
       if (i < n) {
         const float x = cz[i] - tau;
         if (x > 0.0f) {
-          const int slot = cslot[i], item = slot / rows_per_item;
-          off = rm.row_offset(item, slot - item * rows_per_item);
+          off = (long long)crow[i] * D;
           pv = pw(x) * norm;
         }
       }
@@ -878,9 +869,7 @@ __global__ __launch_bounds__(kWave) void attn_entmax_solve_kernel(
       const float x = e.x - tau;
       if (!(x > 0.0f)) continue;
       const float p = pw(x) * norm;
-      const int slot = __float_as_int(e.y), item = slot / rows_per_item;
-      const long long off = rm.row_offset(item, slot - item * rows_per_item);
-      if (off < 0) continue;
+      const long long off = (long long)__float_as_uint(e.y) * D;
       float vx[8];
       Elem<T>::load8(V + off + lr * 8, vx);
 #pragma unroll
