@@ -73,10 +73,13 @@ def test_pooled_key_block_sizes(dev, over):
     dict(lsh_tables=16, lsh_bits=7, Hq=64, Hkv=8, lsh_tau=0.5),               # G = 8, 16384 masses
     dict(lsh_tables=32, lsh_bits=5, dtype="f32", d=64, Hq=4, Hkv=4, S=64),    # G = 1, float32, page 64
     dict(B=4, lens=[0, 1, 17, 4097], k=100),                                  # empty, single-token, k >= L_b
+    dict(lsh_tables=48, lsh_bits=3, S=48, lsh_tau=1.0),                       # pages of 48: cut by the 4096-token blocks
+    dict(lsh_tables=16, lsh_bits=4, S=8, Hq=64, Hkv=8, lsh_tau=0.5),          # pages of 8 (513 per block), G = 8
 ])
 def test_soft_lsh_variants(dev, over):
     """Soft-LSH token scores with 16 to 64 tables of 1 to 8 bits, every group size, a float32 cache,
-    page size 64 and ragged / empty sequences: buckets, norms and keys bit-exact, selections exact."""
+    pages of 8, 48 and 64 tokens and ragged / empty sequences: buckets, norms and keys bit-exact,
+    selections exact."""
     H.log(f"[parity lsh] {over}")
     w = W.make("socket128k", device=dev, **{**SMALL["socket128k"], **over})
     st = H.gpu_step(w)
