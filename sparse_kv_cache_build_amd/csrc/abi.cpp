@@ -72,7 +72,7 @@ bool lsh_ok(int L, int P) { return (L == 16 || L == 32 || L == 48 || L == 64) &&
 // Workspace of a scoring call. LSH: the bucket masses of every unit, G * L * 2^P uint32 each
 // (`lsh_entries` per unit; the size query, which does not see L and P, assumes the maximum).
 size_t score_ws(const skv_cache *c, int kind, int r, size_t lsh_entries = skv::kLshMaxEntries) {
-  if (kind == SKV_SCORE_GAUSS || kind == SKV_SCORE_GAUSS_Q) return 0;   // the scorer stages q itself
+  if (kind == SKV_SCORE_GAUSS || kind == SKV_SCORE_GAUSS_Q || kind == SKV_SCORE_POOL) return 0;   // q staged by the scorer
   if (kind == SKV_SCORE_PROJ) return round_up(sizeof(double) * (size_t)c->batch * c->num_q_heads * r);
   if (kind == SKV_SCORE_LSH) return round_up(sizeof(uint32_t) * (size_t)c->batch * c->num_kv_heads * lsh_entries);
   return round_up(sizeof(double) * 2 * (size_t)c->batch * c->num_q_heads * c->head_dim);
@@ -385,7 +385,7 @@ skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q,
   if (kind == SKV_SCORE_BOX)
     e = skv::launch_score_box(v, c->dtype, q, m->box, out->key, ws, s, ev);
   else if (kind == SKV_SCORE_POOL)
-    e = skv::launch_score_pool(v, c->dtype, q, m->pool_block, m->pool, out->key, ws, s, ev);
+    e = skv::launch_score_pool(v, c->dtype, q, m->pool_block, m->pool, out->key, s, ev);
   else if (kind == SKV_SCORE_LSH)
     e = skv::launch_score_lsh(v, c->dtype, q, m->lsh_tables, m->lsh_bits, m->lsh_planes, sm_scale, m->lsh_bucket,
                               m->vnorm, out->key, workspace, s, ev);

@@ -60,7 +60,7 @@ hipError_t launch_score_lsh(const CacheView &c, int dtype, const void *q, int L,
 hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, const float *gauss, float scale,
                               int quantile, float *m, float *s, float *shat, hipStream_t st, const KernelEvents &ev);
 hipError_t launch_score_pool(const CacheView &c, int dtype, const void *q, int pb, const float *pool, float *key,
-                             double *ws, hipStream_t st, const KernelEvents &ev);
+                             hipStream_t st, const KernelEvents &ev);
 hipError_t launch_score_proj(const CacheView &c, int dtype, const void *q, int r, const float *proj,
                              const uint16_t *kproj, float *key, double *ws, hipStream_t st,
                              const KernelEvents &ev);

@@ -3,24 +3,23 @@
 //
 // Exactness: every score sum runs in float64 over the coordinate index in ascending order, one
 // lane per page (or token), so that the float32 key is the rounding of the same float64 value
-// a plain sequential loop produces; all products involved are exact in float64. The query terms
-// are staged once per step in a float64 workspace, read by uniform (scalar) loads.
+// a plain sequential loop produces; all products involved are exact in float64. The box and
+// projected-key query terms are staged once per step in a float64 workspace, read by uniform
+// (scalar) loads; the pooled and Gaussian scorers stage theirs in LDS from q.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace skv {
 
-// Per query head and coordinate, two float64 terms:
-//   BOX:   (max(q_j, 0), min(q_j, 0)), so that max(q kmin, q kmax) = q+ kmax + q- kmin term by term
-//   GAUSS: (q_j, q_j^2)
-// Layout [B, Hq, D, 2].
+// BOX: per query head and coordinate, the two float64 terms (max(q_j, 0), min(q_j, 0)), so that
+// max(q kmin, q kmax) = q+ kmax + q- kmin term by term. Layout [B, Hq, D, 2].
 template <typename T>
-__global__ void qprep_pair_kernel(const T *__restrict__ q, int n, int gauss, double *__restrict__ out) {
+__global__ void qprep_pair_kernel(const T *__restrict__ q, int n, double *__restrict__ out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const double x = (double)Elem<T>::get(q, i);
-  out[2 * i] = gauss ? x : fmax(x, 0.0);
-  out[2 * i + 1] = gauss ? x * x : fmin(x, 0.0);
+  out[2 * i] = fmax(x, 0.0);
+  out[2 * i + 1] = fmin(x, 0.0);
 }
 
 // PROJ: q~_h[i] = RN_f32(sum_j P[i][j] q_hj) (float64 sum, j ascending), stored as float64 values.
@@ -118,14 +117,14 @@ __global__ __launch_bounds__(256) void score_box_kernel(CacheView c, const T *__
 // than that take several tiles). Each tile is read in chunks of 32 coordinates: every lane loads
 // 16 bytes of eight rows, so one load instruction covers eight whole 128-byte lines, and the chunk
 // goes through LDS to the lane that owns the row. That lane sums q_hi pool_j[i] in float64 with i
-// ascending (the query terms come from the (q, q^2) staging), takes the largest over the heads and
+// ascending (the query terms are staged in LDS from q itself), takes the largest over the heads and
 // its valid sub-blocks (those holding a token), the page's lanes combine, and key[b][g][p] is the
 // float32 rounding of the result; -inf past the sequence. The next chunk is loaded while the current
 // one is summed. Every line is read once and whole by one instruction, so the loads are marked
 // non-temporal.
-template <int D, int G>
+template <typename QT, int D, int G>
 __global__ __launch_bounds__(256) void score_pool_kernel(CacheView c, int pb, int lw, const float *__restrict__ pool,
-                                                         const double *__restrict__ qpm, float *__restrict__ key) {
+                                                         const QT *__restrict__ q, float *__restrict__ key) {
   constexpr int CW = 32, NC = D / CW, LDR = CW + 4;   // chunk width, chunks per row, padded LDS row
   __shared__ double qs[G * D];
   __shared__ float xs[4][64 * LDR];
@@ -141,8 +140,8 @@ __global__ __launch_bounds__(256) void score_pool_kernel(CacheView c, int pb, in
     return;
   }
   const int T = (nsb + W - 1) >> lw;
-  const double *qq = qpm + (size_t)(b * c.Hq + g * G) * D * 2;
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) qs[i] = qq[(size_t)i * 2];
+  const QT *qg = q + (size_t)(b * c.Hq + g * G) * D;   // the G heads of the group are adjacent
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) qs[i] = (double)Elem<QT>::get(qg, i);
   const int *bt = c.bt + (size_t)b * c.maxP;
   // element offset of a tile row in the pool array, -1 for rows without a valid token
   auto row_off = [&](int row, int t) -> long long {
@@ -641,8 +640,8 @@ __global__ __launch_bounds__(256) void score_proj_cand_kernel(CacheView c, const
 // ---------------------------------------------------------------- launchers
 
 template <typename T>
-static hipError_t qprep_pair(const void *q, int n, int gauss, double *ws, hipStream_t st) {
-  qprep_pair_kernel<T><<<(n + 255) / 256, 256, 0, st>>>(static_cast<const T *>(q), n, gauss, ws);
+static hipError_t qprep_pair(const void *q, int n, double *ws, hipStream_t st) {
+  qprep_pair_kernel<T><<<(n + 255) / 256, 256, 0, st>>>(static_cast<const T *>(q), n, ws);
   return hipGetLastError();
 }
 
@@ -670,7 +669,7 @@ static hipError_t box_d(const CacheView &c, const void *box, const double *qpm, 
 hipError_t launch_score_box(const CacheView &c, int dtype, const void *q, const void *box, float *key, double *ws,
                             hipStream_t st, const KernelEvents &ev) {
   const int n = c.B * c.Hq * c.D;
-  hipError_t e = dtype == 0 ? qprep_pair<float>(q, n, 0, ws, st) : qprep_pair<uint16_t>(q, n, 0, ws, st);
+  hipError_t e = dtype == 0 ? qprep_pair<float>(q, n, ws, st) : qprep_pair<uint16_t>(q, n, ws, st);
   if (e != hipSuccess) return e;
   if (c.D == 64) return dtype == 0 ? box_d<float, 64>(c, box, ws, key, st, ev) : box_d<uint16_t, 64>(c, box, ws, key, st, ev);
   return dtype == 0 ? box_d<float, 128>(c, box, ws, key, st, ev) : box_d<uint16_t, 128>(c, box, ws, key, st, ev);
@@ -696,8 +695,8 @@ hipError_t launch_score_gauss(const CacheView &c, int dtype, const void *q, cons
                    : gauss_d<uint16_t, 128>(c, q, gauss, scale, quantile, m, s, shat, st, ev);
 }
 
-template <int D>
-static hipError_t pool_d(const CacheView &c, int pb, const float *pool, const double *qpm, float *key, hipStream_t st,
+template <typename T, int D>
+static hipError_t pool_d(const CacheView &c, int pb, const T *q, const float *pool, float *key, hipStream_t st,
                          const KernelEvents &ev) {
   int lw = 0;
   while ((1 << lw) < c.S / pb && lw < 6) ++lw;
@@ -705,16 +704,19 @@ static hipError_t pool_d(const CacheView &c, int pb, const float *pool, const do
   const dim3 grid((c.maxP + pages_per_block - 1) / pages_per_block, c.B * c.Hkv);
   hipError_t e0 = ev.before(st);
   if (e0 != hipSuccess) return e0;
-  SKV_DISPATCH_G(c.G, score_pool_kernel<D, GG><<<grid, 256, 0, st>>>(c, pb, lw, pool, qpm, key))
+  SKV_DISPATCH_G(c.G, score_pool_kernel<T, D, GG><<<grid, 256, 0, st>>>(c, pb, lw, pool, q, key))
   return ev.after(st);
 }
 
 hipError_t launch_score_pool(const CacheView &c, int dtype, const void *q, int pb, const float *pool, float *key,
-                             double *ws, hipStream_t st, const KernelEvents &ev) {
-  const int n = c.B * c.Hq * c.D;
-  hipError_t e = dtype == 0 ? qprep_pair<float>(q, n, 1, ws, st) : qprep_pair<uint16_t>(q, n, 1, ws, st);
-  if (e != hipSuccess) return e;
-  return c.D == 64 ? pool_d<64>(c, pb, pool, ws, key, st, ev) : pool_d<128>(c, pb, pool, ws, key, st, ev);
+                             hipStream_t st, const KernelEvents &ev) {
+  if (dtype == 0) {
+    const float *qf = static_cast<const float *>(q);
+    return c.D == 64 ? pool_d<float, 64>(c, pb, qf, pool, key, st, ev) : pool_d<float, 128>(c, pb, qf, pool, key, st, ev);
+  }
+  const uint16_t *qb = static_cast<const uint16_t *>(q);
+  return c.D == 64 ? pool_d<uint16_t, 64>(c, pb, qb, pool, key, st, ev)
+                   : pool_d<uint16_t, 128>(c, pb, qb, pool, key, st, ev);
 }
 
 template <int R>
