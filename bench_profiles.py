@@ -63,7 +63,7 @@ TRAFFIC_SOURCES = ["sparse_kv_cache_build_amd/csrc/common.hpp", "sparse_kv_cache
 
 def short(name: str) -> str:
     """Kernel name without 'void', the namespace and the argument list."""
-    n = re.sub(r"^void ", "", name)
+    n = re.sub(r"^void ", "", name).replace("(anonymous namespace)::", "")
     depth, out = 0, []
     for ch in n:   # cut at the first '(' outside template brackets
         if ch == "<":
@@ -245,15 +245,17 @@ def cmd_counters(a):
         wl = m.group(1)
         for r in counter_rows(d):
             key = (wl, short(r["Kernel_Name"]))
+            if a.by_grid:   # one row per launch configuration (workgroups of the grid)
+                key = (wl, f"{key[1]}, {int(r['Grid_Size']) // int(r['Workgroup_Size'])} WG")
             res[key][r["Counter_Name"]][(d, r["Dispatch_Id"])] = float(r["Counter_Value"])
             if m.group(2) == "A" and r["Counter_Name"] == "GRBM_GUI_ACTIVE":
                 dur[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    out = [f"# Utilisation counters of the hot kernels", "",
-           "Commands (three passes per workload, one counter set each, repository root in $R; "
-           "`--sets 1` keeps one buffer set):", ""]
+    out = [f"# Utilisation counters of {a.title}", "",
+           "Commands (three passes per workload, one counter set each, repository root in $R"
+           + ("; `--sets 1` keeps one buffer set):" if "--sets 1" in a.bench_args else "):"), ""]
     for p, ctrs in PASSES.items():
         out.append(f"    cd /tmp && rocprofv3 --pmc {ctrs} --kernel-include-regex '<kernels>' --output-format csv "
-                   f"-d <out> -o ctr -- python3 $R/bench.py --workload <W> --steps 3 --warmup 1 --no-cpu --sets 1   # pass {p}")
+                   f"-d <out> -o ctr -- python3 $R/bench.py {a.bench_args}   # pass {p}")
     out += ["", f"Kernels: `{a.regex}`.", "",
             "Per kernel and workload, means over its dispatches (busy = GRBM_GUI_ACTIVE / 8 cycles; "
             "formulas in bench_profiles.py):", "",
@@ -332,6 +334,10 @@ def main():
     c.add_argument("--out", required=True)
     c.add_argument("--regex", default="")
     c.add_argument("--notes", help="a text file appended to the summary")
+    c.add_argument("--by-grid", action="store_true", help="one row per grid size of each kernel")
+    c.add_argument("--title", default="the hot kernels")
+    c.add_argument("--bench-args", default="--workload <W> --steps 3 --warmup 1 --no-cpu --sets 1",
+                   help="the bench.py arguments of the profiled runs, as the summary states them")
     c.add_argument("dirs", nargs="+")
     r = sub.add_parser("parity")
     r.add_argument("--record", required=True)
