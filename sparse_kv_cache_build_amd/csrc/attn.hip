@@ -84,7 +84,10 @@ struct RowMap {
 
 // ---------------------------------------------------------------- softmax, split-K
 
-template <typename T, int D, int G>
+// NTL: K and V rows loaded non-temporally. Page selections read runs of S consecutive rows (4 KiB
+// at S = 16, d = 128), where the non-temporal hint pays; token selections read scattered 256-byte
+// rows, which plain loads serve better (token128k 31.7 -> 29.6 us), as for the reference gather.
+template <typename T, int D, int G, bool NTL>
 __global__ __launch_bounds__(kAttnThreads) void attn_softmax_kernel(
     CacheView c, const T *__restrict__ q, const int32_t *__restrict__ sel_idx, const int32_t *__restrict__ sel_count,
     int cap, int gran, int spi, int nsplit, float scale_log2, float *__restrict__ part, float *__restrict__ out) {
@@ -160,8 +163,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_softmax_kernel(
       const int ru = r + u * RL::RGB;
       o[u] = ru < NR ? roff[ru] : -1;
       if (o[u] >= 0) {
-        kx[u].load_once(K + o[u] + lr * 8);
-        vx[u].load_once(V + o[u] + lr * 8);
+        if constexpr (NTL) {
+          kx[u].load_once(K + o[u] + lr * 8);
+          vx[u].load_once(V + o[u] + lr * 8);
+        } else {
+          kx[u].load(K + o[u] + lr * 8);
+          vx[u].load(V + o[u] + lr * 8);
+        }
       } else {
         kx[u].zero();
       }
@@ -910,8 +918,12 @@ static hipError_t attn_typed(const AttnArgs &a, hipStream_t st) {
     const size_t lds_s = sizeof(long long) * (size_t)rps_s;
     hipError_t e0 = a.ev.before(st);
     if (e0 != hipSuccess) return e0;
-    SKV_ATTN_DISPATCH_G(c.G, attn_softmax_kernel<T, D, GG><<<grid, kAttnThreads, lds_s, st>>>(
-                                 c, q, a.sel_idx, a.sel_count, a.cap, a.gran, a.spi, a.nsplit, scale_log2, a.part, a.out))
+    if (a.gran)
+      SKV_ATTN_DISPATCH_G(c.G, attn_softmax_kernel<T, D, GG, false><<<grid, kAttnThreads, lds_s, st>>>(
+                                   c, q, a.sel_idx, a.sel_count, a.cap, a.gran, a.spi, a.nsplit, scale_log2, a.part, a.out))
+    else
+      SKV_ATTN_DISPATCH_G(c.G, attn_softmax_kernel<T, D, GG, true><<<grid, kAttnThreads, lds_s, st>>>(
+                                   c, q, a.sel_idx, a.sel_count, a.cap, a.gran, a.spi, a.nsplit, scale_log2, a.part, a.out))
     hipError_t e = a.ev.after(st);
     if (e != hipSuccess || a.nsplit == 1) return e;
     attn_combine_kernel<D><<<c.B * c.Hq, D, 0, st>>>(c, a.sel_count, a.cap, a.spi, a.nsplit, a.part, a.out);
