@@ -205,8 +205,8 @@ enum { SKV_TOKEN_PHASE_ALL = 0, SKV_TOKEN_PHASE_BOUND = 1, SKV_TOKEN_PHASE_FILTE
  *          SKV_SEL_TOKEN_TOPK (tokens = 1).
  * Entries past the sequence (p >= ceil(L_b / S), or t >= L_b) are -inf (BOX, PROJ) or NaN
  * (GAUSS). `q` is [B, Hq, d] in the cache dtype. `workspace` must hold
- * skv_workspace_bytes(c, SKV_OP_SCORE, &kind, 0) bytes (256-byte aligned; GAUSS, GAUSS_Q and POOL
- * need none and may pass NULL).
+ * skv_workspace_bytes(c, SKV_OP_SCORE, &kind, 0) bytes (256-byte aligned; GAUSS, GAUSS_Q, POOL and
+ * BOX with at most 4 query heads per KV head need none and may pass NULL).
  * Errors: SKV_ERR_INVALID_ARG (null pointers, kind not in m->kinds, bad sm_scale or temperature),
  * SKV_ERR_WORKSPACE, SKV_ERR_UNSUPPORTED, SKV_ERR_HIP. */
 skv_status skv_score_pages(const skv_cache *c, const skv_meta *m, const void *q, int32_t kind, float sm_scale,

@@ -73,6 +73,7 @@ bool lsh_ok(int L, int P) { return (L == 16 || L == 32 || L == 48 || L == 64) &&
 // (`lsh_entries` per unit; the size query, which does not see L and P, assumes the maximum).
 size_t score_ws(const skv_cache *c, int kind, int r, size_t lsh_entries = skv::kLshMaxEntries) {
   if (kind == SKV_SCORE_GAUSS || kind == SKV_SCORE_GAUSS_Q || kind == SKV_SCORE_POOL) return 0;   // q staged by the scorer
+  if (kind == SKV_SCORE_BOX && c->num_q_heads <= 4 * c->num_kv_heads) return 0;                    // likewise at G <= 4
   if (kind == SKV_SCORE_PROJ) return round_up(sizeof(double) * (size_t)c->batch * c->num_q_heads * r);
   if (kind == SKV_SCORE_LSH) return round_up(sizeof(uint32_t) * (size_t)c->batch * c->num_kv_heads * lsh_entries);
   return round_up(sizeof(double) * 2 * (size_t)c->batch * c->num_q_heads * c->head_dim);

@@ -3,9 +3,9 @@
 //
 // Exactness: every score sum runs in float64 over the coordinate index in ascending order, one
 // lane per page (or token), so that the float32 key is the rounding of the same float64 value
-// a plain sequential loop produces; all products involved are exact in float64. The box and
-// projected-key query terms are staged once per step in a float64 workspace, read by uniform
-// (scalar) loads; the pooled and Gaussian scorers stage theirs in LDS from q.
+// a plain sequential loop produces; all products involved are exact in float64. The projected-key
+// query terms, and the box terms at G = 8, are staged once per step in a float64 workspace, read by
+// uniform (scalar) loads; the other scorers stage theirs in LDS from q.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -55,12 +55,27 @@ __device__ __forceinline__ float box_elem(const uint4 (&r)[N], int jj) {
 }
 
 // BOX key: one lane per page. key[b][g][p] = RN_f32(max_h sum_j (q+_hj kmax_j + q-_hj kmin_j)).
+// The query terms q+, q- are read as block-uniform values: at G <= 4 from LDS, where the block
+// stages them from q itself (no preparation launch); at G = 8, where their LDS broadcasts would
+// saturate LDS, by scalar loads from the workspace that qprep_pair_kernel fills.
 // For each coordinate exactly one of the two products is nonzero (or both are zero), so the
 // float64 running sum equals sum_j max(q_hj kmin_j, q_hj kmax_j) accumulated in order.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void score_box_kernel(CacheView c, const T *__restrict__ box,
-                                                        const double *__restrict__ qpm, float *__restrict__ key) {
+                                                        const double *__restrict__ qpm, const T *__restrict__ qraw,
+                                                        float *__restrict__ key) {
   const int g = blockIdx.x % c.Hkv, b = blockIdx.y, unit = b * c.Hkv + g;
+  constexpr bool LQ = G <= 4;   // query terms staged in LDS from q
+  __shared__ double qsl[LQ ? G * D * 2 : 2];
+  if constexpr (LQ) {
+    const T *qg = qraw + (size_t)(b * c.Hq + g * G) * D;
+    for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+      const double x = (double)Elem<T>::get(qg, i);
+      qsl[2 * i] = fmax(x, 0.0);
+      qsl[2 * i + 1] = fmin(x, 0.0);
+    }
+    __syncthreads();
+  }
   const int p = (blockIdx.x / c.Hkv) * blockDim.x + threadIdx.x;
   if (p >= c.maxP) return;
   float *out = key + (size_t)unit * c.maxP + p;
@@ -73,7 +88,7 @@ __global__ __launch_bounds__(256) void score_box_kernel(CacheView c, const T *__
   // the page's box: 128-byte lines, each the min row's and the max row's values of the same C
   // coordinates (64 bytes each)
   const uint4 *row = reinterpret_cast<const uint4 *>(box + ((size_t)phys * c.Hkv + g) * 2 * D);
-  const double *qq = qpm + (size_t)(b * c.Hq + g * G) * D * 2;
+  const double *qq = LQ ? qsl : qpm + (size_t)(b * c.Hq + g * G) * D * 2;
   // The lines are read in groups of NL whole lines, their 16-byte loads issued together, so that
   // each line is fetched once. Left to the scheduler, the loads of a line were spread over the
   // arithmetic, and the line was often evicted in between. One line per group at G = 8, where the
@@ -655,24 +670,27 @@ static hipError_t qprep_pair(const void *q, int n, double *ws, hipStream_t st) {
   }
 
 template <typename T, int D>
-static hipError_t box_d(const CacheView &c, const void *box, const double *qpm, float *key, hipStream_t st,
+static hipError_t box_d(const CacheView &c, const void *q, const void *box, const double *qpm, float *key, hipStream_t st,
                         const KernelEvents &ev) {
   // the Hkv blocks of one page range are adjacent in launch order (page block = x / Hkv), so the
   // KV heads' boxes of a physical page (adjacent in memory) are read at about the same time
   const dim3 grid(((c.maxP + 255) / 256) * c.Hkv, c.B);
   hipError_t e0 = ev.before(st);
   if (e0 != hipSuccess) return e0;
-  SKV_DISPATCH_G(c.G, score_box_kernel<T, D, GG><<<grid, 256, 0, st>>>(c, static_cast<const T *>(box), qpm, key))
+  SKV_DISPATCH_G(c.G, score_box_kernel<T, D, GG><<<grid, 256, 0, st>>>(c, static_cast<const T *>(box), qpm,
+                                                                         static_cast<const T *>(q), key))
   return ev.after(st);
 }
 
 hipError_t launch_score_box(const CacheView &c, int dtype, const void *q, const void *box, float *key, double *ws,
                             hipStream_t st, const KernelEvents &ev) {
   const int n = c.B * c.Hq * c.D;
-  hipError_t e = dtype == 0 ? qprep_pair<float>(q, n, ws, st) : qprep_pair<uint16_t>(q, n, ws, st);
-  if (e != hipSuccess) return e;
-  if (c.D == 64) return dtype == 0 ? box_d<float, 64>(c, box, ws, key, st, ev) : box_d<uint16_t, 64>(c, box, ws, key, st, ev);
-  return dtype == 0 ? box_d<float, 128>(c, box, ws, key, st, ev) : box_d<uint16_t, 128>(c, box, ws, key, st, ev);
+  if (c.G > 4) {   // at G = 8 the terms are read by scalar loads from the workspace
+    hipError_t e = dtype == 0 ? qprep_pair<float>(q, n, ws, st) : qprep_pair<uint16_t>(q, n, ws, st);
+    if (e != hipSuccess) return e;
+  }
+  if (c.D == 64) return dtype == 0 ? box_d<float, 64>(c, q, box, ws, key, st, ev) : box_d<uint16_t, 64>(c, q, box, ws, key, st, ev);
+  return dtype == 0 ? box_d<float, 128>(c, q, box, ws, key, st, ev) : box_d<uint16_t, 128>(c, q, box, ws, key, st, ev);
 }
 
 template <typename T, int D>

@@ -149,8 +149,15 @@ def test_score_and_meta_validation(L):
     c = cache()
     m = B.Meta(B.META_BOX, FAKE, None, 0, None, None)
     out = B.Scores(FAKE, None, None, None)
-    st = L.skv_score_pages(C.byref(c), C.byref(m), C.c_void_p(FAKE), B.SCORE_BOX, 0.1, C.byref(out), None, 0, None)
+    # the box bound reads its query terms from the workspace at G = 8 and stages them itself at G <= 4
+    c8 = cache(num_q_heads=64)
+    st = L.skv_score_pages(C.byref(c8), C.byref(m), C.c_void_p(FAKE), B.SCORE_BOX, 0.1, C.byref(out), None, 0, None)
     assert st == B.SKV_ERR_WORKSPACE
+    n = C.c_size_t(1)
+    assert L.skv_workspace_bytes(C.byref(c), B.OP_SCORE, C.byref(C.c_int32(B.SCORE_BOX)), 0, C.byref(n)) == B.SKV_OK
+    assert n.value == 0
+    assert L.skv_workspace_bytes(C.byref(c8), B.OP_SCORE, C.byref(C.c_int32(B.SCORE_BOX)), 0, C.byref(n)) == B.SKV_OK
+    assert n.value == 2 * 64 * 128 * 8 * 2
     st = L.skv_score_pages(C.byref(c), C.byref(m), C.c_void_p(FAKE), B.SCORE_GAUSS, 0.1, C.byref(out),
                            C.c_void_p(FAKE), 1 << 20, None)
     assert st == B.SKV_ERR_INVALID_ARG                              # gauss metadata not present
