@@ -220,19 +220,29 @@ __global__ __launch_bounds__(256) void score_pool_kernel(CacheView c, int pb, in
   if (my_j == 0 && my_p < c.maxP) key[(size_t)unit * c.maxP + my_p] = my_p < np ? (float)best : -INFINITY;
 }
 
+constexpr int kLshPrepThreads = kLshMaxProj;   // one thread per hyperplane of the largest table set
 // Soft-LSH bucket masses of one query head, one workgroup per (b, h): z_i = w_{l,i} . q / ||q||
 // (float64 sums in coordinate order; 0 for q = 0), the two sigmoids sigma(+-2 z_i / tau) of every
 // hyperplane, then for each table l and bucket beta the product over the bits (ascending) of the
 // sigmoid the bit's sign picks, stored as the integer p * 2^24 rounded to nearest even. Layout
 // [B, Hkv, L, 2^P, G]: the G heads of one bucket are adjacent for the scorer.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void lsh_prep_kernel(CacheView c, const T *__restrict__ q, int L, int P,
+__global__ __launch_bounds__(kLshPrepThreads) void lsh_prep_kernel(CacheView c, const T *__restrict__ q, int L, int P,
                                                        const float *__restrict__ planes, double tau,
                                                        uint32_t *__restrict__ tab) {
   __shared__ double qs[D];
   __shared__ double sg[2 * kLshMaxProj];   // [l * P + i][+, -]
   __shared__ double nq;
   const int bh = blockIdx.x, b = bh / c.Hq, h = bh - b * c.Hq, g = h / c.G, hh = h - g * c.G;
+  // the hyperplane rows do not depend on q: each thread's first chunk is requested before q is
+  // staged, and ||q|| (thread 0, a sequential float64 sum) is taken while the others sum their dots
+  constexpr int CH = 8, NCH = D / 4 / CH;
+  const int m0 = threadIdx.x;   // L P <= kLshMaxProj = blockDim.x: at most one hyperplane per thread
+  const float4 *w4 = reinterpret_cast<const float4 *>(planes + (size_t)min(m0, L * P - 1) * D);
+  float4 wa[CH], wb[CH];
+  if (m0 < L * P)
+#pragma unroll
+    for (int j = 0; j < CH; ++j) wa[j] = w4[j];
   for (int j = threadIdx.x; j < D; j += blockDim.x) qs[j] = (double)Elem<T>::get(q, (size_t)bh * D + j);
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -240,17 +250,11 @@ __global__ __launch_bounds__(256) void lsh_prep_kernel(CacheView c, const T *__r
     for (int j = 0; j < D; ++j) ss = fma(qs[j], qs[j], ss);
     nq = sqrt(ss);
   }
-  __syncthreads();
-  for (int m = threadIdx.x; m < L * P; m += blockDim.x) {
-    const float4 *w4 = reinterpret_cast<const float4 *>(planes + (size_t)m * D);
+  double dot = 0.0;
+  if (m0 < L * P) {
     // the hyperplane streams in chunks of 32 coordinates, the next chunk loading while one is
     // summed; each chunk's query terms are read from LDS into registers before its sum, so the
     // sequential FMA chain never waits on LDS
-    constexpr int CH = 8, NCH = D / 4 / CH;
-    float4 wa[CH], wb[CH];
-#pragma unroll
-    for (int j = 0; j < CH; ++j) wa[j] = w4[j];
-    double dot = 0.0;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       if (k + 1 < NCH)
@@ -269,9 +273,12 @@ __global__ __launch_bounds__(256) void lsh_prep_kernel(CacheView c, const T *__r
 #pragma unroll
       for (int j = 0; j < CH; ++j) wa[j] = wb[j];
     }
+  }
+  __syncthreads();   // nq is ready
+  if (m0 < L * P) {
     const double z = nq > 0.0 ? dot / nq : 0.0;
-    sg[2 * m] = 1.0 / (1.0 + exp(-((2.0 * z) / tau)));
-    sg[2 * m + 1] = 1.0 / (1.0 + exp(-((-2.0 * z) / tau)));
+    sg[2 * m0] = 1.0 / (1.0 + exp(-((2.0 * z) / tau)));
+    sg[2 * m0 + 1] = 1.0 / (1.0 + exp(-((-2.0 * z) / tau)));
   }
   __syncthreads();
   const int nb = 1 << P;
@@ -808,9 +815,9 @@ static hipError_t lsh_d(const CacheView &c, int dtype, const void *q, int L, int
                         const uint8_t *bucket, const float *vnorm, float *key, uint32_t *tab, hipStream_t st,
                         const KernelEvents &ev) {
   if (dtype == 0)
-    lsh_prep_kernel<float, D><<<c.B * c.Hq, 256, 0, st>>>(c, static_cast<const float *>(q), L, P, planes, tau, tab);
+    lsh_prep_kernel<float, D><<<c.B * c.Hq, kLshPrepThreads, 0, st>>>(c, static_cast<const float *>(q), L, P, planes, tau, tab);
   else
-    lsh_prep_kernel<uint16_t, D><<<c.B * c.Hq, 256, 0, st>>>(c, static_cast<const uint16_t *>(q), L, P, planes, tau,
+    lsh_prep_kernel<uint16_t, D><<<c.B * c.Hq, kLshPrepThreads, 0, st>>>(c, static_cast<const uint16_t *>(q), L, P, planes, tau,
                                                              tab);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
