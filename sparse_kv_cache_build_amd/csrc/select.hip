@@ -105,7 +105,8 @@ __device__ void radix_kth_regs(const uint32_t (&u)[KPT], int n, uint32_t r, uint
 
 // Ordered take over i in [0, n): keeps keys > T and the first `need` keys == T (lowest i), and
 // writes out[rank] = idx(i) in increasing i. Each thread walks a contiguous chunk; block scans
-// give the ranks. Every thread of the block must call it.
+// give the ranks (one scan of both counts packed in a word when n < 2^15). Every thread of the
+// block must call it.
 template <int NT, typename Get, typename Idx>
 __device__ void ordered_take(Get get, Idx idx, int n, uint32_t T, uint32_t need, int32_t *out, int *scan_scratch) {
   const int per = (n + NT - 1) / NT;
@@ -116,9 +117,15 @@ __device__ void ordered_take(Get get, Idx idx, int n, uint32_t T, uint32_t need,
     ngt += u > T;
     neq += u == T;
   }
-  int tot;
-  int gt_before = block_excl_scan<NT>(ngt, scan_scratch, &tot);
-  int eq_before = block_excl_scan<NT>(neq, scan_scratch, &tot);
+  int tot, gt_before, eq_before;
+  if (n < 32768) {   // both counts in one word (each below 2^15): one scan gives both prefixes
+    const int both = block_excl_scan<NT>((ngt << 16) | neq, scan_scratch, &tot);
+    gt_before = both >> 16;
+    eq_before = both & 0xffff;
+  } else {
+    gt_before = block_excl_scan<NT>(ngt, scan_scratch, &tot);
+    eq_before = block_excl_scan<NT>(neq, scan_scratch, &tot);
+  }
   for (int i = i0; i < i1; ++i) {
     const uint32_t u = get(i);
     if (u > T || (u == T && (uint32_t)eq_before < need)) out[gt_before + min((uint32_t)eq_before, need)] = idx(i);
